@@ -1,0 +1,32 @@
+"""CPU float64 oracle for MXFP8 microscaled attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import this package. The library (``block_scaled_mxfp8_amd``) never imports it, and
+this package imports nothing from the library: the two share no code, tables or helpers.
+
+Contents
+  codec.py      E4M3 / E8M0 codec and MX group quantisation (bit-exact reference).
+  attention.py  same-scheme quantised attention forward/backward in float64 for one
+                (sequence, head), the unquantised float64 reference, and the ambiguity
+                bound that states which device results are admissible where an fp32
+                decision (an E4M3 rounding, a group exponent) sits within rounding error
+                of a threshold.
+
+Parity pins (tests/test_oracle_*.py, run with -m "not gpu") tie every function to the pages
+or to mathematics: the E4M3 format definition and torch.float8_e4m3fn, the worked examples
+of the FLAMIA notes (480 -> e = 1 and code 240; 1024 saturating to 448 and reconstructing
+1.75; the cosine example; the visible-pair counts), closed forms (Q = 0, one token),
+brute-force softmax attention on tiny inputs, finite differences, the D = G.O and
+sum_j dS_ij = 0 identities, and power-of-two / scale-doubling invariances.
+The ambiguity bound is pinned by perturbation: random device-like perturbations inside
+the stated budget never move an output outside the bound.
+"""
+from .codec import (E4M3_MAX, GROUP, e4m3_decode, e4m3_encode, e4m3_round, mx_scale_exponent,
+                    mx_quantize_groups, mx_dequantize_groups, mx_fake_quant, mx_fake_quant_blocks2d)
+from .attention import (ArithModel, head_forward, head_backward, head_reference, visible, round_to, ulp_of)
+
+__all__ = [
+    "E4M3_MAX", "GROUP", "e4m3_decode", "e4m3_encode", "e4m3_round", "mx_scale_exponent",
+    "mx_quantize_groups", "mx_dequantize_groups", "mx_fake_quant", "mx_fake_quant_blocks2d",
+    "ArithModel", "head_forward", "head_backward", "head_reference", "visible", "round_to", "ulp_of",
+]

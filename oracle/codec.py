@@ -1,0 +1,167 @@
+"""MX codec of the oracle: E4M3 element codes, E8M0 power-of-two scales, groups of 32.
+
+Test infrastructure only (see ``oracle/__init__.py``). Plain float64 numpy, written from
+the format definitions, one step per line so it can be checked by eye.
+
+Sources (the pages, by title and section):
+  * Meta "FlashAttention-4 on MXFP8" write-up (aixai.ru), section "What MXFP8 and
+    FlashAttention 4 are": a block of 32 values shares one scale stored as E8M0.
+  * FLAMIA reading notes (zhongzhuzhou.org), section 2 "two hardware formats": MXFP8 =
+    E4M3 codes, one UE8M0 power-of-two scale per 32 elements, groups along the GEMM
+    contraction axis.
+  * FLAMIA reading notes, section 4 "why E4M3 is often unaffected by scale doubling":
+    largest finite E4M3 code is 448, smallest subnormal 2^-9; the scale exponent is the
+    smallest integer e with a / 2^e <= 448, i.e. e = ceil(log2(a / 448)); an all-zero block
+    takes a conventional finite scale; worked example a = 480 -> e = 1, code 240.
+  * FA4 MXFP8 article (zdabc.icu), block-quantisation demo: amax per 32-block, scale
+    2^ceil(log2(amax/448)), clamp to +-448, cast to float8_e4m3fn (behaviour only).
+
+Readings where the pages are silent (each listed in the design doc):
+  * E4M3 is the OCP "FN" variant: bias 7, no infinities, S.1111.111 is NaN.
+  * Conversion rounds to nearest, ties to even, keeps the sign (so -0 and negative values
+    that round to zero encode as 0x80), and saturates every finite |y| > 448 (and +-inf) to
+    +-448 -- the "silent saturation" the FLAMIA notes warn about in section 5.
+  * An all-zero group (and any group whose exponent would fall below -127) takes the
+    E8M0 exponent -127 (byte 0x00), the formula's limit clamped to the E8M0 range.
+  * A group holding a NaN or an infinity gets scale byte 0xFF (E8M0 NaN) and codes 0x7F.
+"""
+import numpy as np
+
+E4M3_MAX = 448.0
+E8M0_BIAS = 127
+E8M0_MIN_EXP = -127
+E8M0_MAX_EXP = 127
+E8M0_NAN = 0xFF
+E4M3_NAN = 0x7F
+GROUP = 32
+
+
+def e4m3_decode(codes):
+    """Value of each E4M3 byte from the bit fields: sign | 4-bit exponent (bias 7) | 3-bit mantissa.
+
+    exponent field 0 -> subnormal m/8 * 2^-6; field 15 with mantissa 7 -> NaN;
+    otherwise (1 + m/8) * 2^(E-7).
+    """
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    efield = (c >> 3) & 0xF
+    mfield = c & 0x7
+    sub = mfield / 8.0 * 2.0 ** -6
+    nrm = (1.0 + mfield / 8.0) * np.exp2(efield - 7.0)
+    val = sign * np.where(efield == 0, sub, nrm)
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def e4m3_round(y):
+    """Round float64 values onto the E4M3 value grid (RNE, saturating to +-448). Returns values.
+
+    Grid: for |y| in [2^E, 2^(E+1)) with E >= -6 the spacing is 2^(E-3); below 2^-6
+    (subnormals) the spacing is 2^-9. Division by the power-of-two spacing is exact in
+    float64, so np.rint (round half to even) performs the RNE step exactly.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    with np.errstate(invalid="ignore", over="ignore"):
+        _, ex = np.frexp(a)                 # a = f * 2^ex with f in [0.5, 1)
+        binade = np.maximum(ex - 1, -6)     # a in [2^binade, 2^(binade+1)) for normals
+        step = np.ldexp(1.0, binade - 3)
+        q = np.rint(a / step) * step
+        q = np.where(q > E4M3_MAX, E4M3_MAX, q)        # saturation (also catches +inf)
+    q = np.where(np.isnan(a), np.nan, q)
+    return np.copysign(q, y)
+
+
+def e4m3_encode(y):
+    """E4M3 byte of each float64 value: RNE onto the grid, then pack the bit fields."""
+    y = np.asarray(y, dtype=np.float64)
+    q = np.abs(e4m3_round(y))
+    nan = np.isnan(q)
+    q = np.where(nan, 0.0, q)
+    _, ex = np.frexp(q)
+    e_unb = ex - 1                                   # q in [2^e_unb, 2^(e_unb+1))
+    normal = q >= 2.0 ** -6
+    efield = np.where(normal, e_unb + 7, 0)
+    mant = np.where(normal, q / np.ldexp(1.0, np.where(normal, e_unb, 0)) - 1.0, q / 2.0 ** -9)
+    mfield = np.where(normal, mant * 8.0, mant)
+    code = (efield.astype(np.int64) << 3) | np.rint(mfield).astype(np.int64)
+    code = code | (np.signbit(y).astype(np.int64) << 7)
+    code = np.where(nan, E4M3_NAN, code)
+    return code.astype(np.uint8)
+
+
+def mx_scale_exponent(amax):
+    """E8M0 exponent of each group: the smallest integer e with amax * 2^-e <= 448.
+
+    Written as the definition: start from the binade of amax and step until the
+    inequality holds and fails for e - 1. amax == 0 gives -127; results are clamped
+    to [-127, 127]. amax must be finite and >= 0 (non-finite groups are handled by
+    the caller).
+    """
+    a = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))        # a in [2^(ex-1), 2^ex)
+    e = (ex - 1) - 9                                 # a * 2^-e in [512, 1024): too big
+    for _ in range(3):                               # at most two increments are needed
+        e = np.where(np.ldexp(a, -e) > E4M3_MAX, e + 1, e)
+    assert np.all((np.ldexp(a, -e) <= E4M3_MAX) | (a == 0))
+    assert np.all((np.ldexp(a, -(e - 1)) > E4M3_MAX) | (a == 0))
+    e = np.where(a > 0, e, E8M0_MIN_EXP)
+    return np.clip(e, E8M0_MIN_EXP, E8M0_MAX_EXP).astype(np.int64)
+
+
+def mx_quantize_groups(x, axis):
+    """Quantise ``x`` in groups of 32 consecutive elements along ``axis``.
+
+    The length along ``axis`` is padded with zeros to a multiple of 32 for the group
+    statistics only (zeros never raise an amax); a short final group is a partial group.
+    Returns (codes uint8 with the shape of x, exponents int64 with the group axis of
+    length ceil(n/32), scale bytes uint8 of the same shape).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    xm = np.moveaxis(x, axis, -1)
+    n = xm.shape[-1]
+    ng = -(-n // GROUP)
+    pad = ng * GROUP - n
+    xp = np.concatenate([xm, np.zeros(xm.shape[:-1] + (pad,))], axis=-1) if pad else xm
+    blocks = xp.reshape(xm.shape[:-1] + (ng, GROUP))
+    finite = np.all(np.isfinite(blocks), axis=-1)
+    amax = np.max(np.abs(np.where(np.isfinite(blocks), blocks, 0.0)), axis=-1)
+    e = mx_scale_exponent(amax)
+    codes = e4m3_encode(np.ldexp(blocks, -e[..., None]))
+    codes = np.where(finite[..., None], codes, E4M3_NAN).astype(np.uint8)
+    sbytes = np.where(finite, e + E8M0_BIAS, E8M0_NAN).astype(np.uint8)
+    codes = codes.reshape(xp.shape)[..., :n]
+    return np.moveaxis(codes, -1, axis), np.moveaxis(e, -1, axis), np.moveaxis(sbytes, -1, axis)
+
+
+def mx_dequantize_groups(codes, exps, axis):
+    """Inverse of mx_quantize_groups: decode(code) * 2^e of the element's group."""
+    v = np.moveaxis(e4m3_decode(codes), axis, -1)
+    ee = np.repeat(np.moveaxis(np.asarray(exps), axis, -1), GROUP, axis=-1)[..., : v.shape[-1]]
+    return np.moveaxis(np.ldexp(v, ee), -1, axis)
+
+
+def mx_fake_quant(x, axis):
+    """decode(quantise(x)) along ``axis`` in one call."""
+    codes, e, _ = mx_quantize_groups(x, axis)
+    return mx_dequantize_groups(codes, e, axis)
+
+
+def mx_fake_quant_blocks2d(u):
+    """Quantise a 2-D array in 32 x 32 square blocks (one E8M0 scale per block).
+
+    This is the dS scale geometry of the Meta write-up, section "Quantising dS without a
+    transpose" (square blocks, so the scale is invariant under transposition). Rows and
+    columns are padded with zeros to multiples of 32 for the statistics only.
+    Returns (dequantised values, exponent per block).
+    """
+    u = np.asarray(u, dtype=np.float64)
+    r, c = u.shape
+    R, C = -(-r // GROUP) * GROUP, -(-c // GROUP) * GROUP
+    up = np.zeros((R, C))
+    up[:r, :c] = u
+    blk = up.reshape(R // GROUP, GROUP, C // GROUP, GROUP)
+    amax = np.max(np.abs(blk), axis=(1, 3))
+    e = mx_scale_exponent(amax)
+    q = e4m3_decode(e4m3_encode(np.ldexp(blk, -e[:, None, :, None])))
+    q = np.ldexp(q, e[:, None, :, None]).reshape(R, C)[:r, :c]
+    return q, e

@@ -1,0 +1,98 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle timing.
+
+This module holds no part of the method's arithmetic: it only draws numbers. Every tensor
+is drawn from numpy's PCG64 generator seeded with (base seed, tensor id), in logical
+row-major order ([B, H, L, d] batched, [T, H, d] packed), as float32 normals that are then
+rounded to the storage dtype (bf16 by round-to-nearest-even) by the caller's conversion.
+
+Workloads (sizes and value distributions):
+  c1  forward only, causal, B1 H1 L256 d64, fp32 N(0,1)
+  c2  fwd+bwd, causal, B2 H8 L1024 d128, bf16 N(0,1) with 2 outlier channels per
+      (tensor, head) of Q, K, V scaled x50 (same channels across batch and tokens); G ~ N(0,1)
+  c3  fwd+bwd, causal, B4 H32 L4096 d128, bf16 N(0,1); G ~ N(0,1)
+  c4  packed: 128 documents, lengths clip(round(exp(ln 384 + 1.0 z)), 32, 2048), H4 d128,
+      causal per document, bf16 N(0,1)
+  c5  non-causal, B1 H16 L16384 d128, bf16 N(0,1) * u, u ~ U(0.5, 4) per (tensor, batch,
+      token) shared across heads and channels; GQA variant with 4 KV heads
+"""
+import numpy as np
+
+TENSOR_ID = {"q": 1, "k": 2, "v": 3, "g": 4, "lengths": 5, "outliers": 6, "magnitude": 7}
+
+CONFIGS = {
+    "c1": dict(batch=1, heads=1, heads_kv=1, seqlen=256, head_dim=64, causal=True, dtype="f32", backward=False),
+    "c2": dict(batch=2, heads=8, heads_kv=8, seqlen=1024, head_dim=128, causal=True, dtype="bf16", backward=True,
+               outliers=2, outlier_scale=50.0),
+    "c3": dict(batch=4, heads=32, heads_kv=32, seqlen=4096, head_dim=128, causal=True, dtype="bf16", backward=True),
+    "c4": dict(n_docs=128, median=384, sigma=1.0, min_len=32, max_len=2048, heads=4, heads_kv=4, head_dim=128,
+               causal=True, dtype="bf16", backward=True),
+    "c5": dict(batch=1, heads=16, heads_kv=16, seqlen=16384, head_dim=128, causal=False, dtype="bf16", backward=True,
+               magnitude=(0.5, 4.0)),
+    "c5gqa": dict(batch=1, heads=16, heads_kv=4, seqlen=16384, head_dim=128, causal=False, dtype="bf16",
+                  backward=True, magnitude=(0.5, 4.0)),
+}
+SEED_BASE = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "c5gqa": 1005}
+
+
+def rng(seed, tensor):
+    return np.random.Generator(np.random.PCG64([int(seed), TENSOR_ID[tensor]]))
+
+
+def normal(seed, tensor, shape):
+    return rng(seed, tensor).standard_normal(size=shape, dtype=np.float32)
+
+
+def doc_lengths(seed, n_docs, median, sigma, min_len, max_len):
+    z = rng(seed, "lengths").standard_normal(n_docs)
+    n = np.rint(np.exp(np.log(median) + sigma * z))
+    return np.clip(n, min_len, max_len).astype(np.int64)
+
+
+def cu_seqlens_of(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+def make_inputs(cfg_name, seed=None, batch=None, heads=None, seqlen=None, tensors=("q", "k", "v", "g")):
+    """Float32 numpy arrays for one workload (the caller converts to the storage dtype).
+
+    Batched: dict(q [B,H,L,d], k/v [B,Hkv,L,d], g [B,H,L,d]); packed (c4): q [T,H,d] ... and
+    'cu_seqlens'. ``batch``/``heads``/``seqlen`` override the sizes (smaller parity cases).
+    """
+    cfg = dict(CONFIGS[cfg_name])
+    seed = SEED_BASE[cfg_name] if seed is None else seed
+    d = cfg["head_dim"]
+    out = {}
+    if "n_docs" in cfg:
+        lengths = doc_lengths(seed, cfg["n_docs"], cfg["median"], cfg["sigma"], cfg["min_len"], cfg["max_len"])
+        T = int(lengths.sum())
+        out["cu_seqlens"] = cu_seqlens_of(lengths)
+        for t in tensors:
+            h = cfg["heads_kv"] if t in ("k", "v") else cfg["heads"]
+            out[t] = normal(seed, t, (T, h, d))
+        return out
+    B = batch or cfg["batch"]
+    H = heads or cfg["heads"]
+    Hkv = cfg["heads_kv"] if heads is None else max(1, H * cfg["heads_kv"] // cfg["heads"])
+    L = seqlen or cfg["seqlen"]
+    mag = None
+    if "magnitude" in cfg:
+        lo, hi = cfg["magnitude"]
+        r = rng(seed, "magnitude")
+        mag = {t: r.uniform(lo, hi, size=(B, 1, L, 1)).astype(np.float32) for t in ("q", "k", "v")}
+    outl = None
+    if "outliers" in cfg:
+        r = rng(seed, "outliers")
+        outl = {}
+        for t in ("q", "k", "v"):
+            h = Hkv if t in ("k", "v") else H
+            outl[t] = [r.choice(d, size=cfg["outliers"], replace=False) for _ in range(h)]
+    for t in tensors:
+        h = Hkv if t in ("k", "v") else H
+        x = normal(seed, t, (B, h, L, d))
+        if mag is not None and t in mag:
+            x *= mag[t]
+        if outl is not None and t in outl:
+            for hh in range(h):
+                x[:, hh, :, outl[t][hh]] *= cfg["outlier_scale"]
+        out[t] = x
+    return out
