@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""MXFP8 flash attention benchmark on one MI355X.
+
+One step = the whole hot path on one batch of the B4 H32 L4096 d128 causal bf16 workload:
+mx_quantize of Q, K and V (ROW + SEQ views), the forward (O, LSE) and the backward (G
+views + D, main kernel, dQ finalize). Inputs are resident in HBM before the timed region.
+
+FLOPs are causal-adjusted (FLAMIA notes section 6 visible-pair count): forward 4 d per
+visible pair, backward 10 d (five GEMMs). `value` is the step's fwd+bwd FLOPs over the
+step's wall time (quantisation included). The per-kernel lines come from HIP events that
+the library records immediately around each launch of the named kernel, on its stream.
+
+    python bench.py [--steps K] [--warmup W] [--dq f32|f16] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_MXFP8_TFLOPS = 5000.0      # MI355X dense MXFP8 MFMA, AMD's published figure
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dq", choices=["f32", "f16"], default="f32", help="dQ accumulation of the timed step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=10, help="launches averaged per kernel line")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU; multi-GPU runs are not part of it (use --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F32, PROFILE_BWD_FINAL, PROFILE_BWD_MAIN,
+                                        PROFILE_BWD_PREP, PROFILE_FWD, PROFILE_QUANTIZE, load, mx_attn_bwd,
+                                        mx_attn_fwd, mx_profile_kernel, mx_quantize)
+    from block_scaled_mxfp8_amd.flops import attn_flops, visible_pairs
+
+    load()
+    cfg = synth.CONFIGS["c3"]
+    B, H, L, d = cfg["batch"], cfg["heads"], cfg["seqlen"], cfg["head_dim"]
+    dq_mode = MX_DQ_F32 if args.dq == "f32" else MX_DQ_F16_BOOST
+    print(f"[bench] generating c3 inputs B{B} H{H} L{L} d{d}", file=sys.stderr, flush=True)
+    x = synth.make_inputs("c3")
+    t = {n: torch.from_numpy(x[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v", "g")}
+    del x
+    pairs = visible_pairs(B, H, L, causal=True)
+    f_fwd = attn_flops(pairs, d)
+    f_bwd = attn_flops(pairs, d, backward=True)
+    ws = {}
+
+    def quant():
+        return mx_quantize(t["q"]), mx_quantize(t["k"]), mx_quantize(t["v"])
+
+    def step(mode=dq_mode):
+        (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
+        o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=True)
+        dq, dk, dv, w = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=True, dq_mode=mode,
+                                    workspace=ws.get(mode))
+        ws[mode] = w
+        return o, dq
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    # the timed region also feeds the roofline line: events around every launch of the
+    # backward main kernel (the step's dominant kernel)
+    ev_main = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev_main:
+        a.record()
+        b.record()
+    mx_profile_kernel(PROFILE_BWD_MAIN, ev_main)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mx_profile_kernel(0, [])
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_bwd_main = float(np.mean([a.elapsed_time(b) for a, b in ev_main]))
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # per-kernel averages outside the timed region
+    def kernel_ms(kind, fn, n=args.profile_steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record()
+            b.record()
+        mx_profile_kernel(kind, ev)
+        torch.cuda.synchronize()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        mx_profile_kernel(0, [])
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
+    o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=True)
+    ms_fwd = kernel_ms(PROFILE_FWD, lambda: mx_attn_fwd(q_row, k_row, v_seq, causal=True))
+    ms_quant = kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize(t["q"]), n=3 * args.profile_steps)
+
+    def bwd(mode):
+        return lambda: mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=True, dq_mode=mode,
+                                   workspace=ws.get(mode))
+
+    res_bwd = {}
+    for name, mode in (("f32", MX_DQ_F32), ("f16", MX_DQ_F16_BOOST)):
+        if mode not in ws:
+            _, _, _, ws[mode] = bwd(mode)()
+        main = kernel_ms(PROFILE_BWD_MAIN, bwd(mode))
+        prep = kernel_ms(PROFILE_BWD_PREP, bwd(mode))
+        fin = kernel_ms(PROFILE_BWD_FINAL, bwd(mode))
+        # whole call, events around it on the current stream
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        for _ in range(args.profile_steps):
+            bwd(mode)()
+        s1.record()
+        torch.cuda.synchronize()
+        call = s0.elapsed_time(s1) / args.profile_steps
+        res_bwd[name] = dict(main_ms=main, prep_ms=prep, finalize_ms=fin, call_ms=call)
+
+    q_elems = B * H * L * d
+    quant_bytes = q_elems * (2 + 2 * (1 + 1 / 32))          # bf16 in, two views of codes + scales out
+    tflops = lambda f, ms: f / (ms * 1e-3) / 1e12          # noqa: E731
+    kernels = {
+        "attn_fwd": dict(ms=ms_fwd, tflops=tflops(f_fwd, ms_fwd)),
+        "attn_bwd_main": dict(ms=ms_bwd_main, tflops=tflops(f_bwd, ms_bwd_main)),
+        "quantize": dict(ms=ms_quant, gbs=quant_bytes / (ms_quant * 1e-3) / 1e9),
+    }
+    bwd_f32 = res_bwd["f32"]
+    bwd_f16 = res_bwd["f16"]
+    line = {
+        "metric": "MXFP8 attn fwd/bwd TFLOP/s (causal-adj) at B4 H32 L4096 d128, % of peak",
+        "value": round(tflops(f_fwd + f_bwd, ms_step), 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8",
+        "data": "synthetic",
+        "config": {"workload": "c3: B4 H32 L4096 d128 causal, bf16 N(0,1) inputs, step = quantise Q/K/V + fwd + bwd",
+                   "batch": B, "heads": H, "seqlen": L, "head_dim": d, "causal": True, "dq": args.dq},
+        "pct_of_peak": round(100 * tflops(f_fwd + f_bwd, ms_step) / PEAK_MXFP8_TFLOPS, 2),
+        "fwd_tflops": round(tflops(f_fwd, ms_fwd), 2),
+        "fwd_pct_of_peak": round(100 * tflops(f_fwd, ms_fwd) / PEAK_MXFP8_TFLOPS, 2),
+        "bwd_tflops": round(tflops(f_bwd, bwd_f32["call_ms"]), 2),
+        "bwd_pct_of_peak": round(100 * tflops(f_bwd, bwd_f32["call_ms"]) / PEAK_MXFP8_TFLOPS, 2),
+        "bwd_f16dq_tflops": round(tflops(f_bwd, bwd_f16["call_ms"]), 2),
+        "bwd_f16dq_pct_of_peak": round(100 * tflops(f_bwd, bwd_f16["call_ms"]) / PEAK_MXFP8_TFLOPS, 2),
+        "quantize_gbs": round(kernels["quantize"]["gbs"], 1),
+        "kernels_ms": {"attn_fwd": round(ms_fwd, 4), "attn_bwd_main_f32": round(bwd_f32["main_ms"], 4),
+                       "attn_bwd_main_f16": round(bwd_f16["main_ms"], 4), "bwd_prep": round(bwd_f32["prep_ms"], 4),
+                       "dq_finalize": round(bwd_f32["finalize_ms"], 4), "quantize_one_tensor": round(ms_quant, 4)},
+        "flops": {"fwd": f_fwd, "bwd": f_bwd, "visible_pairs": pairs},
+        "pages_context": {"fa4_mx8_fwd_pflops_gb300": 2.85, "fa4_mx8_bwd_pflops_gb300_f16dq": 1.98,
+                          "fa4_mx8_bwd_pflops_gb300_f32dq": 1.82},
+        "roofline": {"kernel": "attn_bwd_kernel<128> (backward main)", "bound": "mfma",
+                     "achieved": round(kernels["attn_bwd_main"]["tflops"], 2), "peak": PEAK_MXFP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kernels["attn_bwd_main"]["tflops"] / PEAK_MXFP8_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(t)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(t):
+    """The float64 oracle (as it stands) on a bounded sample of the same workload: forward and
+    backward of one (batch, head) pair of the B4 H32 L4096 d128 causal step."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from block_scaled_mxfp8_amd.flops import attn_flops
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - only used to report the thread count
+        cores = os.cpu_count()
+    q, k, v, g = (t[n][0, 0].to(torch.float64).cpu().numpy() for n in ("q", "k", "v", "g"))
+    L, d = q.shape
+    t0 = time.perf_counter()
+    f = oracle.head_forward(q, k, v, True)
+    oracle.head_backward(q, k, v, f["O_out"], f["lse"], g, True)
+    sec = time.perf_counter() - t0
+    pairs = L * (L + 1) // 2
+    fl = attn_flops(pairs, d) + attn_flops(pairs, d, backward=True)
+    return {"value": round(fl / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fwd+bwd of 1 of 128 (batch, head) pairs (b0 h0, L{L} d{d} causal), float64 numpy, "
+                      f"{sec:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

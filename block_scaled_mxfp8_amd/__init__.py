@@ -1,6 +1,23 @@
 """libmxattn: MXFP8 microscaled flash attention for AMD MI355X (gfx950).
 
-The compute path is the HIP shared library ``libmxattn.so`` (C ABI declared in
-``include/mxattn.h``); this package only marshals arguments to it. Importing the package
-does not load the library; the first call does, and raises if it is missing.
+The compute path is the HIP shared library ``libmxattn.so`` (C ABI: ``include/mxattn.h``).
+This module only marshals torch tensors (device memory and the current stream) into those
+calls; every step of the method runs in the library's kernels. Importing the package does
+not load the library; the first call does, and raises if it has not been built
+(``python -m block_scaled_mxfp8_amd.build``).
+
+Functions mirror the C entry points:
+    mx_quantize(x, views=ROW|SEQ, cu_seqlens=None, max_seqlen=None) -> (row QView, seq QView)
+    mx_attn_fwd(q_row, k_row, v_seq, ...) -> (o, lse)
+    mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, ...) -> (dq, dk, dv)
+    mx_attn_varlen_fwd / mx_attn_varlen_bwd: the same with cu_seqlens (packed [T, H, d]).
 """
+from ._lib import (MX_VIEW_ROW, MX_VIEW_SEQ, MX_DQ_F32, MX_DQ_F16_BOOST, MXError, QView, lib_path, load,
+                   mx_abi_version, mx_attn_bwd, mx_attn_fwd, mx_attn_varlen_bwd, mx_attn_varlen_fwd, mx_quantize,
+                   mx_attn_workspace_size, mx_read_flags, mx_profile_kernel, PROFILE_FWD, PROFILE_BWD_MAIN,
+                   PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_FINAL)
+
+__all__ = ["MX_VIEW_ROW", "MX_VIEW_SEQ", "MX_DQ_F32", "MX_DQ_F16_BOOST", "MXError", "QView", "lib_path", "load",
+           "mx_abi_version", "mx_attn_bwd", "mx_attn_fwd", "mx_attn_varlen_bwd", "mx_attn_varlen_fwd", "mx_quantize",
+           "mx_attn_workspace_size", "mx_read_flags", "mx_profile_kernel", "PROFILE_FWD", "PROFILE_BWD_MAIN",
+           "PROFILE_QUANTIZE", "PROFILE_BWD_PREP", "PROFILE_BWD_FINAL"]

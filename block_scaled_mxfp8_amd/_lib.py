@@ -1,0 +1,348 @@
+"""ctypes binding of libmxattn.so: argument marshalling only.
+
+Torch supplies device memory (outputs are allocated here with torch.empty) and the current
+HIP stream; the library does all the work. Nothing here falls back to another
+implementation: a missing library or a non-zero status raises.
+"""
+import ctypes
+import os
+from typing import NamedTuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+MX_OK, MX_E_ARG, MX_E_UNSUPPORTED, MX_E_WORKSPACE, MX_E_DEVICE = range(5)
+MX_F32, MX_BF16 = 0, 1
+MX_VIEW_ROW, MX_VIEW_SEQ = 1, 2
+MX_DQ_F32, MX_DQ_F16_BOOST = 0, 1
+
+
+class MXError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: libmxattn status {status} ({_strerror(status)})")
+
+
+class _Seq(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("cu_seqlens", ctypes.c_void_p),
+                ("n_docs", ctypes.c_int32), ("max_seqlen", ctypes.c_int32), ("total_tokens", ctypes.c_int64)]
+
+
+class _QView(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("seq", _Seq), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("out_dtype", ctypes.c_int32), ("dq_mode", ctypes.c_int32), ("deterministic", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class QView(NamedTuple):
+    """One quantised view: uint8 codes and E8M0 scale bytes (layouts in include/mxattn.h)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+
+
+_LIB = None
+
+
+def lib_path():
+    return os.environ.get("MXATTN_LIB", os.path.join(HERE, "libmxattn.so"))
+
+
+def load():
+    """Load libmxattn.so once (raises if it was not built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m block_scaled_mxfp8_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.mx_quantize.argtypes = [ctypes.POINTER(_Seq), I32, I32, P, I32, I32, ctypes.POINTER(_QView),
+                                ctypes.POINTER(_QView), P]
+    lib.mx_quantize.restype = I32
+    for name in ("mx_attn_fwd", "mx_attn_varlen_fwd"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, P, P, P]
+        f.restype = I32
+    for name in ("mx_attn_bwd", "mx_attn_varlen_bwd"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, _QView, _QView, P, P, P, I32, P, P, P, P]
+        f.restype = I32
+    lib.mx_attn_workspace_size.argtypes = [ctypes.POINTER(_Desc), I32]
+    lib.mx_attn_workspace_size.restype = SZ
+    lib.mx_view_codes_bytes.argtypes = [ctypes.POINTER(_Seq), I32, I32, I32]
+    lib.mx_view_codes_bytes.restype = SZ
+    lib.mx_view_scales_bytes.argtypes = [ctypes.POINTER(_Seq), I32, I32, I32]
+    lib.mx_view_scales_bytes.restype = SZ
+    lib.mx_read_flags.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
+    lib.mx_read_flags.restype = I32
+    lib.mx_strerror.argtypes = [I32]
+    lib.mx_strerror.restype = ctypes.c_char_p
+    lib.mx_profile_kernel.argtypes = [I32, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p), I32]
+    lib.mx_profile_kernel.restype = I32
+    lib.mx_abi_version.argtypes = []
+    lib.mx_abi_version.restype = I32
+    _LIB = lib
+    return lib
+
+
+def _strerror(status):
+    try:
+        return load().mx_strerror(status).decode()
+    except Exception:  # noqa: BLE001 - only used to format an error message
+        return "?"
+
+
+def _check(status, where):
+    if status != MX_OK:
+        raise MXError(status, where)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return MX_F32
+    if dt == torch.bfloat16:
+        return MX_BF16
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _seq(shape, cu_seqlens, max_seqlen):
+    """mx_seq for a tensor of logical shape [B, H, L, d] (batched) or [T, H, d] (packed)."""
+    s = _Seq()
+    if cu_seqlens is None:
+        if len(shape) != 4:
+            raise ValueError("batched tensors are [B, H, L, d]")
+        s.batch, s.seqlen = shape[0], shape[2]
+        s.cu_seqlens, s.n_docs, s.max_seqlen, s.total_tokens = None, 0, 0, shape[0] * shape[2]
+    else:
+        if len(shape) != 3:
+            raise ValueError("packed tensors are [T, H, d]")
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+            raise ValueError("cu_seqlens must be a device int32 tensor")
+        if max_seqlen is None:
+            # host copy (synchronises); pass max_seqlen to avoid it
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
+        s.batch, s.seqlen = 1, 0
+        s.cu_seqlens = cu_seqlens.data_ptr()
+        s.n_docs = cu_seqlens.numel() - 1
+        s.max_seqlen = max(1, int(max_seqlen))
+        s.total_tokens = shape[0]
+    return s
+
+
+def _heads_dim(shape, cu_seqlens):
+    """(heads, head_dim) of a logical tensor: [B, H, L, d] batched or [T, H, d] packed."""
+    if cu_seqlens is None:
+        if len(shape) != 4:
+            raise ValueError("batched tensors are [B, H, L, d]")
+        return shape[1], shape[3]
+    if len(shape) != 3:
+        raise ValueError("packed tensors are [T, H, d]")
+    return shape[1], shape[2]
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _check_view(lib, v, seq, heads, d, view, what):
+    """The view's tensors must hold exactly what the library will address."""
+    codes, scales = _view_bytes(lib, seq, heads, d, view)
+    if v is None or _nbytes(v.codes) != codes or _nbytes(v.scales) != scales:
+        raise ValueError(f"{what}: view buffers do not match the geometry ({codes} / {scales} bytes expected)")
+    if not (v.codes.is_cuda and v.scales.is_cuda and v.codes.is_contiguous() and v.scales.is_contiguous()):
+        raise ValueError(f"{what}: views must be contiguous device tensors")
+
+
+def _check_tensor(t, seq_shape_elems, what):
+    if t.numel() != seq_shape_elems or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous device tensor of {seq_shape_elems} elements")
+
+
+def _qv(v):
+    return _QView(v.codes.data_ptr(), v.scales.data_ptr())
+
+
+def _view_bytes(lib, seq, heads, d, view):
+    return (lib.mx_view_codes_bytes(ctypes.byref(seq), heads, d, view),
+            lib.mx_view_scales_bytes(ctypes.byref(seq), heads, d, view))
+
+
+def _seq_view_shapes(shape, seq, cu_seqlens):
+    d = shape[-1]
+    if cu_seqlens is None:
+        B, H, L, _ = shape
+        G = (L + 31) // 32
+        return (B, H, G, d, 32), (B, H, G, d)
+    T, H, _ = shape
+    Gc = T // 32 + (cu_seqlens.numel() - 1)
+    return (H, Gc, d, 32), (H, Gc, d)
+
+
+def mx_quantize(x, views=MX_VIEW_ROW | MX_VIEW_SEQ, cu_seqlens=None, max_seqlen=None):
+    """Quantise x ([B,H,L,d] or packed [T,H,d], fp32/bf16) -> (row QView or None, seq QView or None)."""
+    lib = load()
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    shape = tuple(x.shape)
+    seq = _seq(shape, cu_seqlens, max_seqlen)
+    heads, d = _heads_dim(shape, cu_seqlens)
+    row = seqv = None
+    rv = _QView()
+    sv = _QView()
+    if views & MX_VIEW_ROW:
+        row = QView(torch.empty(shape, dtype=torch.uint8, device=x.device),
+                    torch.empty(shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device))
+        rv = _qv(row)
+    if views & MX_VIEW_SEQ:
+        cs, ss = _seq_view_shapes(shape, seq, cu_seqlens)
+        seqv = QView(torch.empty(cs, dtype=torch.uint8, device=x.device),
+                     torch.empty(ss, dtype=torch.uint8, device=x.device))
+        sv = _qv(seqv)
+    for v, view, what in ((row, MX_VIEW_ROW, "row view"), (seqv, MX_VIEW_SEQ, "seq view")):
+        if v is not None:
+            _check_view(lib, v, seq, heads, d, view, what)
+    st = lib.mx_quantize(ctypes.byref(seq), heads, d, x.data_ptr(), _dtype_code(x.dtype), views, ctypes.byref(rv),
+                         ctypes.byref(sv), _stream())
+    _check(st, "mx_quantize")
+    return row, seqv
+
+
+def _desc(q_shape, k_shape, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode=MX_DQ_F32):
+    d = _Desc()
+    d.seq = _seq(q_shape, cu_seqlens, max_seqlen)
+    d.heads_q, d.head_dim = _heads_dim(q_shape, cu_seqlens)
+    d.heads_kv, dk = _heads_dim(k_shape, cu_seqlens)
+    if dk != d.head_dim or k_shape[0] != q_shape[0] or (cu_seqlens is None and k_shape[2] != q_shape[2]):
+        raise ValueError("q and k/v geometries differ")
+    d.causal = 1 if causal else 0
+    d.softmax_scale = float(softmax_scale or 0.0)
+    d.out_dtype = _dtype_code(out_dtype)
+    d.dq_mode = int(dq_mode)
+    d.deterministic = 0
+    return d
+
+
+def _fwd(name, q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen):
+    lib = load()
+    qs = tuple(q_row.codes.shape)
+    desc = _desc(qs, tuple(k_row.codes.shape), cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype)
+    dev = q_row.codes.device
+    seq = desc.seq
+    _check_view(lib, q_row, seq, desc.heads_q, desc.head_dim, MX_VIEW_ROW, "q_row")
+    _check_view(lib, k_row, seq, desc.heads_kv, desc.head_dim, MX_VIEW_ROW, "k_row")
+    _check_view(lib, v_seq, seq, desc.heads_kv, desc.head_dim, MX_VIEW_SEQ, "v_seq")
+    o = torch.empty(qs, dtype=out_dtype, device=dev)
+    lse = torch.empty(qs[:-1], dtype=torch.float32, device=dev)
+    st = getattr(lib, name)(ctypes.byref(desc), _qv(q_row), _qv(k_row), _qv(v_seq), o.data_ptr(), lse.data_ptr(),
+                            _stream())
+    _check(st, name)
+    return o, lse
+
+
+def mx_attn_fwd(q_row, k_row, v_seq, causal=True, softmax_scale=0.0, out_dtype=torch.bfloat16, cu_seqlens=None,
+                max_seqlen=None):
+    """Forward attention from quantised views -> (o [like q], lse float32 [B,H,L] / [T,H])."""
+    return _fwd("mx_attn_fwd", q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen)
+
+
+def mx_attn_varlen_fwd(q_row, k_row, v_seq, cu_seqlens, max_seqlen=None, causal=True, softmax_scale=0.0,
+                       out_dtype=torch.bfloat16):
+    return _fwd("mx_attn_varlen_fwd", q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen)
+
+
+def mx_attn_workspace_size(q_shape, cu_seqlens=None, max_seqlen=None, heads_kv=None, dq_mode=MX_DQ_F32):
+    lib = load()
+    k_shape = list(q_shape)
+    if heads_kv is not None:
+        k_shape[-3 if cu_seqlens is None else -2] = heads_kv
+    desc = _desc(tuple(q_shape), tuple(k_shape), cu_seqlens, max_seqlen, True, 0.0, torch.bfloat16, dq_mode)
+    return lib.mx_attn_workspace_size(ctypes.byref(desc), 1)
+
+
+def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype, dq_mode, cu_seqlens,
+         max_seqlen, workspace):
+    lib = load()
+    qs, ks = tuple(q_row.codes.shape), tuple(k_row.codes.shape)
+    desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode)
+    dev = q_row.codes.device
+    need = lib.mx_attn_workspace_size(ctypes.byref(desc), 1)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif _nbytes(workspace) < need or not workspace.is_cuda:
+        raise ValueError(f"workspace needs {need} bytes")
+    desc.workspace = workspace.data_ptr()
+    desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    dq = torch.empty(qs, dtype=out_dtype, device=dev)
+    dk = torch.empty(ks, dtype=out_dtype, device=dev)
+    dv = torch.empty(ks, dtype=out_dtype, device=dev)
+    seq = desc.seq
+    for v, h, view, what in ((q_row, desc.heads_q, MX_VIEW_ROW, "q_row"), (q_seq, desc.heads_q, MX_VIEW_SEQ, "q_seq"),
+                             (k_row, desc.heads_kv, MX_VIEW_ROW, "k_row"), (k_seq, desc.heads_kv, MX_VIEW_SEQ, "k_seq"),
+                             (v_row, desc.heads_kv, MX_VIEW_ROW, "v_row")):
+        _check_view(lib, v, seq, h, desc.head_dim, view, what)
+    nq = q_row.codes.numel()
+    _check_tensor(o, nq, "o")
+    _check_tensor(g, nq, "g")
+    _check_tensor(lse, nq // desc.head_dim, "lse")
+    if o.dtype != out_dtype or lse.dtype != torch.float32:
+        raise ValueError("o must have out_dtype and lse float32")
+    st = getattr(lib, name)(ctypes.byref(desc), _qv(q_row), _qv(q_seq), _qv(k_row), _qv(k_seq), _qv(v_row),
+                            o.data_ptr(), lse.data_ptr(), g.data_ptr(), _dtype_code(g.dtype), dq.data_ptr(),
+                            dk.data_ptr(), dv.data_ptr(), _stream())
+    _check(st, name)
+    return dq, dk, dv, workspace
+
+
+def mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal=True, softmax_scale=0.0,
+                out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32, cu_seqlens=None, max_seqlen=None, workspace=None):
+    """Backward attention -> (dq, dk, dv, workspace). o/lse are the forward's outputs."""
+    return _bwd("mx_attn_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype,
+                dq_mode, cu_seqlens, max_seqlen, workspace)
+
+
+def mx_attn_varlen_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, cu_seqlens, max_seqlen=None, causal=True,
+                       softmax_scale=0.0, out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32, workspace=None):
+    return _bwd("mx_attn_varlen_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale,
+                out_dtype, dq_mode, cu_seqlens, max_seqlen, workspace)
+
+
+def mx_read_flags(workspace):
+    """Status word of a backward workspace (synchronous; after the stream finished)."""
+    lib = load()
+    out = ctypes.c_uint32(0)
+    _check(lib.mx_read_flags(ctypes.c_void_p(workspace.data_ptr()), ctypes.byref(out)), "mx_read_flags")
+    return out.value
+
+
+def mx_abi_version():
+    return load().mx_abi_version()
+
+
+PROFILE_FWD, PROFILE_BWD_MAIN, PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_FINAL = 1, 2, 3, 4, 5
+_PROFILE_KEEP = []
+
+
+def mx_profile_kernel(kernel, events):
+    """Register (start, stop) torch.cuda.Event pairs for every launch of one library kernel
+    (measurement only); kernel=0 or events=[] turns the hook off."""
+    lib = load()
+    if kernel == 0 or not events:
+        _PROFILE_KEEP.clear()
+        _check(lib.mx_profile_kernel(0, None, None, 0), "mx_profile_kernel")
+        return
+    n = len(events)
+    starts = (ctypes.c_void_p * n)(*[e[0].cuda_event for e in events])
+    stops = (ctypes.c_void_p * n)(*[e[1].cuda_event for e in events])
+    _PROFILE_KEEP[:] = [starts, stops, events]
+    _check(lib.mx_profile_kernel(kernel, starts, stops, n), "mx_profile_kernel")

@@ -1,0 +1,51 @@
+"""Build libmxattn.so in-tree with hipcc for gfx950.
+
+    python -m block_scaled_mxfp8_amd.build [--verbose]
+
+All HIP sources under csrc/ are compiled into one shared library next to this file. Packed
+FP32 instructions are disabled for the device code (-packed-fp32-ops); the host pass of
+hipcc warns that it does not know that target feature, which is harmless.
+"""
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libmxattn.so")
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libmxattn)")
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+
+
+def build(verbose=False, out=LIB, extra=()):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wno-unused-command-line-argument",
+           "-I", os.path.join(ROOT, "include"), *extra, *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = "\n".join(line for line in (res.stdout + res.stderr).splitlines() if noise not in line and "(ignoring feature)" not in line)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + msgs)
+    if verbose and msgs.strip():
+        print(msgs)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

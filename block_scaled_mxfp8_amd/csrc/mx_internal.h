@@ -1,0 +1,73 @@
+// Internal launcher interface between the C ABI (mxattn_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx_layout.h"
+
+namespace mx {
+
+struct QuantizeParams {
+  Geom geom;
+  int heads;
+  int head_dim;
+  bool f32;              // input dtype: fp32 (else bf16)
+  const void* x;
+  uint8_t* row_codes;    // nullptr: ROW view not wanted
+  uint8_t* row_scales;
+  uint8_t* seq_codes;    // nullptr: SEQ view not wanted
+  uint8_t* seq_scales;
+  // backward preprocessing (all nullptr for a plain quantise): with `o` set, the kernel also
+  // writes delta[token, head] = sum_c dequant(ROW code) * O and zeroes dq_acc.
+  const void* o;
+  bool o_f32;
+  float* delta;
+  void* dq_acc;
+  bool dq_f16;
+};
+
+struct AttnParams {
+  Geom geom;
+  int heads_q, heads_kv, head_dim;
+  int causal;
+  float scale;           // alpha
+  bool out_f32;          // O / dQ / dK / dV storage type (else bf16)
+  // forward operands
+  const uint8_t* q_codes; const uint8_t* q_scales;    // ROW view of Q
+  const uint8_t* k_codes; const uint8_t* k_scales;    // ROW view of K
+  const uint8_t* v_codes; const uint8_t* v_scales;    // SEQ view of V
+  void* o;
+  float* lse;
+  // work list for packed mode (device, built by the forward launcher in the workspace-free path)
+};
+
+struct BwdParams {
+  Geom geom;
+  int heads_q, heads_kv, head_dim;
+  int causal;
+  float scale;
+  bool out_f32;
+  int dq_mode;
+  const uint8_t* q_codes; const uint8_t* q_scales;      // ROW Q
+  const uint8_t* qs_codes; const uint8_t* qs_scales;    // SEQ Q
+  const uint8_t* k_codes; const uint8_t* k_scales;      // ROW K
+  const uint8_t* ks_codes; const uint8_t* ks_scales;    // SEQ K
+  const uint8_t* vr_codes; const uint8_t* vr_scales;    // ROW V
+  const void* o;
+  const float* lse;
+  const void* g;
+  bool g_f32;
+  void* dq; void* dk; void* dv;
+  // workspace pieces
+  uint8_t* gr_codes; uint8_t* gr_scales;                // ROW G
+  uint8_t* gs_codes; uint8_t* gs_scales;                // SEQ G
+  float* delta;                                         // D per (row, head)
+  void* dq_acc;                                         // FP32 or FP16 accumulator [like Q]
+  uint32_t* flags;
+};
+
+hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);
+hipError_t launch_attn_fwd(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,51 @@
+// Tensor and quantised-view addressing shared by the host launchers and the kernels.
+// The layouts are the ones declared in include/mxattn.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+constexpr int kGroup = 32;
+
+// Geometry of one call. Batched: cu == nullptr, every (b, h) is one sequence of `seqlen`
+// tokens. Packed: batch == 1, documents j = 0..n_docs-1 span tokens [cu[j], cu[j+1]).
+struct Geom {
+  int batch;
+  int seqlen;        // batched L; packed: 0
+  const int* cu;     // device cu_seqlens (packed) or nullptr
+  int n_docs;        // packed: number of documents; batched: batch
+  int max_seqlen;    // longest sequence / document
+  long long total;   // total tokens of one head: B*L (batched) or T (packed)
+  int gseq;          // SEQ-view group rows per (b, h): ceil(L/32) (batched) or T/32 + n_docs (packed)
+};
+
+__host__ __device__ inline bool packed(const Geom& g) { return g.cu != nullptr; }
+
+// Element offset of token t (index inside its sequence/document), head h, channel c.
+// `seq` is the batch index (batched) or the document's first token cu[j] (packed).
+__host__ __device__ inline long long elem_offset(const Geom& g, int heads, int d, long long seq, int h, long long t,
+                                                 int c) {
+  if (g.cu == nullptr) return (((long long)seq * heads + h) * g.seqlen + t) * d + c;
+  return ((seq + t) * heads + h) * (long long)d + c;
+}
+
+// Stride between consecutive tokens of one head, in elements.
+__host__ __device__ inline long long token_stride(const Geom& g, int heads, int d) {
+  return g.cu == nullptr ? (long long)d : (long long)heads * d;
+}
+
+// SEQ-view group row of group `grp` of sequence/document `s` (index b or j) for head h.
+// Packed documents start at row floor(cu[j]/32) + j, which never overlaps the previous
+// document's rows and needs no prefix sum.
+__host__ __device__ inline long long seq_group_row(const Geom& g, int heads, int s, int h, int doc_start, int grp) {
+  if (g.cu == nullptr) return ((long long)s * heads + h) * g.gseq + grp;
+  return (long long)h * g.gseq + (doc_start >> 5) + s + grp;
+}
+
+// Byte position of token offset t (0..31) inside a 32-byte SEQ-view group. It matches the
+// K order of the gfx950 32x32x64 MFMA operand built from an accumulator tile: lanes 0-31
+// carry tokens {0-3, 8-11, 16-19, 24-27} in bytes 0-15, lanes 32-63 the rest.
+__host__ __device__ constexpr inline int seq_pos(int t) { return 16 * ((t >> 2) & 1) + 4 * (t >> 3) + (t & 3); }
+
+}  // namespace mx

@@ -1,0 +1,274 @@
+// C ABI of libmxattn (declared in include/mxattn.h): host-side validation, sizing and
+// kernel launches. Nothing here reads device memory or synchronises, except mx_read_flags.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mxattn.h"
+#include "mx_internal.h"
+#include "mx_layout.h"
+#include "mx_profile.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool make_geom(const mx_seq* s, mx::Geom* g) {
+  if (!s) return false;
+  if (s->cu_seqlens) {
+    if (s->n_docs < 1 || s->total_tokens < 0 || s->max_seqlen < 1) return false;
+    if (s->total_tokens > (1LL << 31) - 64) return false;
+    g->cu = s->cu_seqlens;
+    g->batch = 1;
+    g->seqlen = 0;
+    g->n_docs = s->n_docs;
+    g->max_seqlen = s->max_seqlen;
+    g->total = s->total_tokens;
+    g->gseq = (int)(s->total_tokens / 32 + s->n_docs);
+  } else {
+    if (s->batch < 1 || s->seqlen < 1 || s->seqlen > (1LL << 30) || s->batch > (1LL << 20)) return false;
+    g->cu = nullptr;
+    g->batch = (int)s->batch;
+    g->seqlen = (int)s->seqlen;
+    g->n_docs = (int)s->batch;
+    g->max_seqlen = (int)s->seqlen;
+    g->total = s->batch * s->seqlen;
+    g->gseq = (int)((s->seqlen + 31) / 32);
+  }
+  return true;
+}
+
+size_t row_codes_bytes(const mx::Geom& g, int heads, int d) { return (size_t)g.total * heads * d; }
+size_t seq_codes_bytes(const mx::Geom& g, int heads, int d) {
+  const size_t rows = mx::packed(g) ? (size_t)g.gseq * heads : (size_t)g.gseq * heads * g.batch;
+  return rows * d * 32;
+}
+
+bool valid_dim(int d) { return d == 64 || d == 128; }
+
+mx_status check_view(const mx_qview& v) {
+  if (!v.codes || !v.scales) return MX_E_ARG;
+  if (!aligned(v.codes, 16) || !aligned(v.scales, 4)) return MX_E_ARG;
+  return MX_OK;
+}
+
+mx_status check_desc(const mx_attn_desc* d, mx::Geom* g) {
+  if (!d) return MX_E_ARG;
+  if (!make_geom(&d->seq, g)) return MX_E_ARG;
+  if (d->heads_q < 1 || d->heads_kv < 1 || d->heads_q % d->heads_kv != 0) return MX_E_ARG;
+  if (d->out_dtype != MX_F32 && d->out_dtype != MX_BF16) return MX_E_ARG;
+  if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale)) return MX_E_ARG;
+  if (d->dq_mode != MX_DQ_F32 && d->dq_mode != MX_DQ_F16_BOOST) return MX_E_ARG;
+  if (!valid_dim(d->head_dim)) return MX_E_UNSUPPORTED;
+  if (d->deterministic != 0) return MX_E_UNSUPPORTED;
+  return MX_OK;
+}
+
+struct BwdWorkspace {
+  size_t gr_codes, gr_scales, gs_codes, gs_scales, delta, dq_acc, flags, total;
+};
+
+BwdWorkspace bwd_layout(const mx::Geom& g, const mx_attn_desc* d) {
+  BwdWorkspace w;
+  const int hq = d->heads_q, dim = d->head_dim;
+  size_t off = 0;
+  w.flags = off; off += align_up(sizeof(uint32_t));   // status word first: mx_read_flags finds it
+  w.gr_codes = off; off += align_up(row_codes_bytes(g, hq, dim));
+  w.gr_scales = off; off += align_up(row_codes_bytes(g, hq, dim) / 32);
+  w.gs_codes = off; off += align_up(seq_codes_bytes(g, hq, dim));
+  w.gs_scales = off; off += align_up(seq_codes_bytes(g, hq, dim) / 32);
+  w.delta = off; off += align_up((size_t)g.total * hq * sizeof(float));
+  w.dq_acc = off; off += align_up(row_codes_bytes(g, hq, dim) * (d->dq_mode == MX_DQ_F16_BOOST ? 2 : 4));
+  w.total = off;
+  return w;
+}
+
+mx_status fwd_impl(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o, float* lse,
+                   void* stream, bool need_packed) {
+  mx::Geom g;
+  mx_status st = check_desc(desc, &g);
+  if (st != MX_OK) return st;
+  if (need_packed && !desc->seq.cu_seqlens) return MX_E_ARG;
+  if ((st = check_view(q_row)) != MX_OK || (st = check_view(k_row)) != MX_OK || (st = check_view(v_seq)) != MX_OK)
+    return st;
+  if (!o || !lse || !aligned(o, 16) || !aligned(lse, 4)) return MX_E_ARG;
+  mx::AttnParams p = {};
+  p.geom = g;
+  p.heads_q = desc->heads_q;
+  p.heads_kv = desc->heads_kv;
+  p.head_dim = desc->head_dim;
+  p.causal = desc->causal ? 1 : 0;
+  p.scale = desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0f / sqrtf((float)desc->head_dim);
+  p.out_f32 = desc->out_dtype == MX_F32;
+  p.q_codes = q_row.codes; p.q_scales = q_row.scales;
+  p.k_codes = k_row.codes; p.k_scales = k_row.scales;
+  p.v_codes = v_seq.codes; p.v_scales = v_seq.scales;
+  p.o = o;
+  p.lse = lse;
+  if (g.total == 0) return MX_OK;
+  return mx::launch_attn_fwd(p, (hipStream_t)stream) == hipSuccess ? MX_OK : MX_E_DEVICE;
+}
+
+mx_status bwd_impl(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row, mx_qview k_seq,
+                   mx_qview v_row, const void* o, const float* lse, const void* gptr, mx_dtype g_dtype, void* dq,
+                   void* dk, void* dv, void* stream, bool need_packed) {
+  mx::Geom g;
+  mx_status st = check_desc(desc, &g);
+  if (st != MX_OK) return st;
+  if (need_packed && !desc->seq.cu_seqlens) return MX_E_ARG;
+  const mx_qview views[5] = {q_row, q_seq, k_row, k_seq, v_row};
+  for (const auto& v : views)
+    if ((st = check_view(v)) != MX_OK) return st;
+  if (!o || !lse || !gptr || !dq || !dk || !dv) return MX_E_ARG;
+  if (!aligned(o, 16) || !aligned(gptr, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16)) return MX_E_ARG;
+  if (g_dtype != MX_F32 && g_dtype != MX_BF16) return MX_E_ARG;
+  const BwdWorkspace w = bwd_layout(g, desc);
+  if (!desc->workspace || desc->workspace_bytes < w.total || !aligned(desc->workspace, kAlign)) return MX_E_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(desc->workspace);
+  mx::BwdParams p = {};
+  p.geom = g;
+  p.heads_q = desc->heads_q;
+  p.heads_kv = desc->heads_kv;
+  p.head_dim = desc->head_dim;
+  p.causal = desc->causal ? 1 : 0;
+  p.scale = desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0f / sqrtf((float)desc->head_dim);
+  p.out_f32 = desc->out_dtype == MX_F32;
+  p.dq_mode = desc->dq_mode;
+  p.q_codes = q_row.codes; p.q_scales = q_row.scales;
+  p.qs_codes = q_seq.codes; p.qs_scales = q_seq.scales;
+  p.k_codes = k_row.codes; p.k_scales = k_row.scales;
+  p.ks_codes = k_seq.codes; p.ks_scales = k_seq.scales;
+  p.vr_codes = v_row.codes; p.vr_scales = v_row.scales;
+  p.o = o;
+  p.lse = lse;
+  p.g = gptr;
+  p.g_f32 = g_dtype == MX_F32;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.gr_codes = ws + w.gr_codes; p.gr_scales = ws + w.gr_scales;
+  p.gs_codes = ws + w.gs_codes; p.gs_scales = ws + w.gs_scales;
+  p.delta = reinterpret_cast<float*>(ws + w.delta);
+  p.dq_acc = ws + w.dq_acc;
+  p.flags = reinterpret_cast<uint32_t*>(ws + w.flags);
+  if (g.total == 0) return MX_OK;
+  return mx::launch_attn_bwd(p, (hipStream_t)stream) == hipSuccess ? MX_OK : MX_E_DEVICE;
+}
+
+}  // namespace
+
+namespace mx {
+ProfileHook& profile_hook() {
+  static ProfileHook hook;
+  return hook;
+}
+}  // namespace mx
+
+extern "C" {
+
+mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x, mx_dtype dtype, int32_t views,
+                      mx_qview* row_out, mx_qview* seq_out, void* stream) {
+  mx::Geom g;
+  if (!make_geom(seq, &g) || heads < 1 || !x) return MX_E_ARG;
+  if (dtype != MX_F32 && dtype != MX_BF16) return MX_E_ARG;
+  if (views < 1 || views > 3) return MX_E_ARG;
+  if (!valid_dim(head_dim)) return MX_E_UNSUPPORTED;
+  if (!aligned(x, 16)) return MX_E_ARG;
+  mx::QuantizeParams p = {};
+  p.geom = g;
+  p.heads = heads;
+  p.head_dim = head_dim;
+  p.f32 = dtype == MX_F32;
+  p.x = x;
+  if (views & MX_VIEW_ROW) {
+    if (!row_out || check_view(*row_out) != MX_OK) return MX_E_ARG;
+    p.row_codes = row_out->codes;
+    p.row_scales = row_out->scales;
+  }
+  if (views & MX_VIEW_SEQ) {
+    if (!seq_out || check_view(*seq_out) != MX_OK) return MX_E_ARG;
+    p.seq_codes = seq_out->codes;
+    p.seq_scales = seq_out->scales;
+  }
+  if (g.total == 0) return MX_OK;
+  const int slot = mx::profile_begin(mx::kProfQuantize, (hipStream_t)stream);
+  const hipError_t err = mx::launch_quantize(p, (hipStream_t)stream);
+  mx::profile_end(slot, (hipStream_t)stream);
+  return err == hipSuccess ? MX_OK : MX_E_DEVICE;
+}
+
+mx_status mx_attn_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o, float* lse,
+                      void* stream) {
+  return fwd_impl(desc, q_row, k_row, v_seq, o, lse, stream, false);
+}
+
+mx_status mx_attn_varlen_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o,
+                             float* lse, void* stream) {
+  return fwd_impl(desc, q_row, k_row, v_seq, o, lse, stream, true);
+}
+
+mx_status mx_attn_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row, mx_qview k_seq,
+                      mx_qview v_row, const void* o, const float* lse, const void* g, mx_dtype g_dtype, void* dq,
+                      void* dk, void* dv, void* stream) {
+  return bwd_impl(desc, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, false);
+}
+
+mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
+                             mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
+                             mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream) {
+  return bwd_impl(desc, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, true);
+}
+
+size_t mx_attn_workspace_size(const mx_attn_desc* desc, int32_t for_bwd) {
+  mx::Geom g;
+  if (!for_bwd || !desc || !make_geom(&desc->seq, &g) || desc->heads_q < 1 || !valid_dim(desc->head_dim)) return 0;
+  return bwd_layout(g, desc).total;
+}
+
+size_t mx_view_codes_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view) {
+  mx::Geom g;
+  if (!make_geom(seq, &g) || heads < 1 || !valid_dim(head_dim)) return 0;
+  if (view == MX_VIEW_ROW) return row_codes_bytes(g, heads, head_dim);
+  if (view == MX_VIEW_SEQ) return seq_codes_bytes(g, heads, head_dim);
+  return 0;
+}
+
+size_t mx_view_scales_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view) {
+  return mx_view_codes_bytes(seq, heads, head_dim, view) / 32;
+}
+
+mx_status mx_read_flags(const void* workspace, uint32_t* flags) {
+  if (!flags || !workspace) return MX_E_ARG;
+  *flags = 0;
+  return hipMemcpy(flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost) == hipSuccess ? MX_OK : MX_E_DEVICE;
+}
+
+mx_status mx_profile_kernel(int32_t kernel, void* const* start_events, void* const* stop_events, int32_t count) {
+  mx::ProfileHook& h = mx::profile_hook();
+  if (kernel == 0 || count <= 0) {
+    h = mx::ProfileHook();
+    return MX_OK;
+  }
+  if (kernel < 1 || kernel > 5 || !start_events || !stop_events) return MX_E_ARG;
+  h.kind = kernel;
+  h.start = (hipEvent_t*)start_events;
+  h.stop = (hipEvent_t*)stop_events;
+  h.n = count;
+  h.count = 0;
+  return MX_OK;
+}
+
+const char* mx_strerror(mx_status s) {
+  switch (s) {
+    case MX_OK: return "ok";
+    case MX_E_ARG: return "invalid argument";
+    case MX_E_UNSUPPORTED: return "unsupported configuration";
+    case MX_E_WORKSPACE: return "workspace missing or too small";
+    case MX_E_DEVICE: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t mx_abi_version(void) { return MXATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+// mx_quantize: one pass over x writes both MX views.
+//
+// Meta write-up (aixai.ru), "Quantisation inside the producers": the producer writes FP8 in
+// two scale layouts so no consumer re-quantises; "Why swapping the data type does not
+// work": Q/K groups run along the head dimension, V groups along the sequence. FLAMIA
+// notes section 6: in a packed row buffer the scale statistics stay inside each document.
+//
+// One workgroup owns one SEQ-view group row: 32 consecutive tokens (of one sequence or
+// document) x all d channels of one head. It reads the tile once, writes the ROW view
+// (groups of 32 channels of a token) straight from registers and the SEQ view (groups of
+// 32 tokens of a channel) after a transpose through LDS. The kernel is HBM-bound:
+// 2 B read + 2 x (1 + 1/32) B written per bf16 element.
+#include "mx_device.h"
+#include "mx_internal.h"
+#include "mx_layout.h"
+
+namespace mx {
+
+template <int D, bool kF32>
+__global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
+  constexpr int TPT = D / 16;  // threads per token (16 channels each)
+  const int tid = threadIdx.x;
+  const int tk = tid / TPT;    // token offset in the group row
+  const int cb = tid % TPT;    // channel block of 16
+  const int R = blockIdx.x;    // group row (within the sequence, or the packed buffer)
+  const int h = blockIdx.y;
+  const Geom& g = p.geom;
+
+  int s, grp, ntok;
+  long long tok0;  // first token of this group row, relative to the sequence start
+  int doc_start = 0;
+  if (!packed(g)) {
+    s = blockIdx.z;
+    grp = R;
+    tok0 = (long long)R * kGroup;
+    ntok = min(kGroup, g.seqlen - (int)tok0);
+  } else {
+    // document j owns group rows [cu[j]/32 + j, cu[j+1]/32 + j + 1); find j by bisection
+    int lo = 0, hi = g.n_docs - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if ((g.cu[mid] >> 5) + mid <= R) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+    doc_start = g.cu[s];
+    grp = R - ((doc_start >> 5) + s);
+    tok0 = (long long)grp * kGroup;
+    ntok = min(kGroup, g.cu[s + 1] - doc_start - (int)tok0);
+  }
+  if (ntok <= 0) return;  // padding row of the packed SEQ view: never read
+  const long long sbase = packed(g) ? (long long)doc_start : (long long)s;
+  const bool valid = tk < ntok;
+
+  // ---- load 16 channels of one token (zeros past the end) ----
+  float v[16];
+  const long long e0 = elem_offset(g, p.heads, D, sbase, h, tok0 + tk, cb * 16);
+  if (valid) {
+    if (kF32) {
+      const v4f* src = reinterpret_cast<const v4f*>(static_cast<const float*>(p.x) + e0);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v4f t = src[i];
+        v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
+      }
+    } else {
+      const v4i* src = reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(p.x) + e0);
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        v4i t = src[i];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          v[8 * i + 2 * j] = bf16_bits_to_float((uint32_t)t[j] & 0xFFFFu);
+          v[8 * i + 2 * j + 1] = bf16_bits_to_float((uint32_t)t[j] >> 16);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; i++) v[i] = 0.f;
+  }
+
+  // ---- ROW view: 32 channels of one token = this thread's 16 + the neighbour's 16 ----
+  if (p.row_codes) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) am = max(am, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+    const bool nonfinite = am >= kInfBits;
+    const int e = scale_exp_from_bits(nonfinite ? 0u : am);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      w[i] = nonfinite ? 0x7F7F7F7Fu
+                       : pack4_e4m3(ldexpf(v[4 * i], -e), ldexpf(v[4 * i + 1], -e), ldexpf(v[4 * i + 2], -e),
+                                    ldexpf(v[4 * i + 3], -e));
+    if (valid) {
+      v4i out = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      *reinterpret_cast<v4i*>(p.row_codes + e0) = out;
+      if ((cb & 1) == 0) p.row_scales[e0 >> 5] = nonfinite ? 0xFF : (uint8_t)(e + 127);
+    }
+    if (p.o != nullptr) {
+      // Backward preprocessing (FLAMIA notes section 5, Algorithm 1 step 09; the same G view
+      // feeds D and dP): D = sum_c G_row~ * O with O as saved, in fp32.
+      float part = 0.f;
+      float ov[16];
+      if (valid) {
+        if (p.o_f32) {
+          const v4f* src = reinterpret_cast<const v4f*>(static_cast<const float*>(p.o) + e0);
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            v4f t = src[i];
+            ov[4 * i] = t[0]; ov[4 * i + 1] = t[1]; ov[4 * i + 2] = t[2]; ov[4 * i + 3] = t[3];
+          }
+        } else {
+          const v4i* src = reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(p.o) + e0);
+#pragma unroll
+          for (int i = 0; i < 2; i++) {
+            v4i t = src[i];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+              ov[8 * i + 2 * j] = bf16_bits_to_float((uint32_t)t[j] & 0xFFFFu);
+              ov[8 * i + 2 * j + 1] = bf16_bits_to_float((uint32_t)t[j] >> 16);
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float dq4[4];
+          unpack4_e4m3(w[i], dq4);
+#pragma unroll
+          for (int j = 0; j < 4; j++) part = __builtin_fmaf(ldexpf(dq4[j], e), ov[4 * i + j], part);
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < TPT; m <<= 1) part += __shfl_xor(part, m);
+      if (valid && cb == 0) {
+        const long long ti = packed(g) ? ((long long)(doc_start + tok0 + tk) * p.heads + h)
+                                       : (((long long)s * p.heads + h) * g.seqlen + tok0 + tk);
+        p.delta[ti] = part;
+      }
+      if (valid) {
+        if (p.dq_f16) {
+          v4i* dst = reinterpret_cast<v4i*>(static_cast<uint16_t*>(p.dq_acc) + e0);
+          dst[0] = v4i{0, 0, 0, 0};
+          dst[1] = v4i{0, 0, 0, 0};
+        } else {
+          v4i* dst = reinterpret_cast<v4i*>(static_cast<float*>(p.dq_acc) + e0);
+#pragma unroll
+          for (int i = 0; i < 4; i++) dst[i] = v4i{0, 0, 0, 0};
+        }
+      }
+    }
+  }
+  if (!p.seq_codes) return;
+
+  // ---- SEQ view: 32 tokens of one channel, through LDS ----
+  __shared__ float tile[kGroup][D + 1];
+#pragma unroll
+  for (int i = 0; i < 16; i++) tile[tk][cb * 16 + i] = v[i];
+  __syncthreads();
+  const int c = tid >> 1;   // channel (2 threads per channel, 16 tokens each)
+  const int hf = tid & 1;   // token half
+  // run A (bytes 8hf..8hf+7) holds tokens 16hf + {0..3, 8..11}; run B (bytes 16+8hf..) tokens 16hf + {4..7, 12..15}
+  float a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    a[i] = tile[16 * hf + i][c];
+    a[4 + i] = tile[16 * hf + 8 + i][c];
+    b[i] = tile[16 * hf + 4 + i][c];
+    b[4 + i] = tile[16 * hf + 12 + i][c];
+  }
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) am = max(am, max(__float_as_uint(a[i]) & 0x7FFFFFFFu, __float_as_uint(b[i]) & 0x7FFFFFFFu));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+  const bool nonfinite = am >= kInfBits;
+  const int e = scale_exp_from_bits(nonfinite ? 0u : am);
+  uint32_t wa0, wa1, wb0, wb1;
+  if (nonfinite) {
+    wa0 = wa1 = wb0 = wb1 = 0x7F7F7F7Fu;
+  } else {
+    wa0 = pack4_e4m3(ldexpf(a[0], -e), ldexpf(a[1], -e), ldexpf(a[2], -e), ldexpf(a[3], -e));
+    wa1 = pack4_e4m3(ldexpf(a[4], -e), ldexpf(a[5], -e), ldexpf(a[6], -e), ldexpf(a[7], -e));
+    wb0 = pack4_e4m3(ldexpf(b[0], -e), ldexpf(b[1], -e), ldexpf(b[2], -e), ldexpf(b[3], -e));
+    wb1 = pack4_e4m3(ldexpf(b[4], -e), ldexpf(b[5], -e), ldexpf(b[6], -e), ldexpf(b[7], -e));
+    // padding tokens of a partial group are exact zeros -> code 0
+  }
+  const long long grow = seq_group_row(g, p.heads, s, h, doc_start, grp);
+  uint8_t* dst = p.seq_codes + (grow * D + c) * kGroup;
+  *reinterpret_cast<v2i*>(dst + 8 * hf) = v2i{(int)wa0, (int)wa1};
+  *reinterpret_cast<v2i*>(dst + 16 + 8 * hf) = v2i{(int)wb0, (int)wb1};
+  if (hf == 0) p.seq_scales[grow * D + c] = nonfinite ? 0xFF : (uint8_t)(e + 127);
+}
+
+hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream) {
+  const Geom& g = p.geom;
+  dim3 grid(g.gseq, p.heads, packed(g) ? 1 : g.batch);
+  if (p.head_dim == 128) {
+    if (p.f32) hipLaunchKernelGGL((quantize_kernel<128, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((quantize_kernel<128, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (p.f32) hipLaunchKernelGGL((quantize_kernel<64, true>), grid, dim3(128), 0, stream, p);
+    else hipLaunchKernelGGL((quantize_kernel<64, false>), grid, dim3(128), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mx

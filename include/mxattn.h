@@ -1,0 +1,166 @@
+/*
+ * libmxattn — MXFP8 microscaled flash attention for AMD MI355X (gfx950). C ABI.
+ *
+ * Method (the pages, by title and section):
+ *   - Meta "FlashAttention-4 on MXFP8" write-up (aixai.ru), "Why swapping the data type
+ *     does not work": MXFP8 = E4M3 codes, one E8M0 scale per 32 elements; Q/K scale groups
+ *     run along the head dimension, V groups along the sequence; P and dS are quantised
+ *     online inside the kernels. "Quantising dS without a transpose": dS in square 32x32
+ *     blocks. Same section: dQ accumulated in FP32 or in FP16 with a 2^9 boost.
+ *   - FLAMIA reading notes (zhongzhuzhou.org), section 2: S = alpha Q K^T, P = softmax over
+ *     the visible keys, O = P V; dV = P^T G, E = G V^T, U = P (E - D) with D = G . O,
+ *     dQ = alpha U K, dK = alpha U^T Q; online softmax state (max, sum, LSE). Section 4:
+ *     scale exponent e = ceil(log2(amax / 448)). Section 5 Algorithm 1: the forward saves O
+ *     and the row LSE; the backward rebuilds S and P from the same score operands and the
+ *     saved LSE. Section 6: packed documents in one row buffer, scale groups inside each
+ *     document, +inf LSE for rows without visible keys, outputs at the packed offsets.
+ *
+ * Conventions
+ *   - Every pointer argument of a compute call is DEVICE memory owned by the caller (for
+ *     example a torch tensor). The library never allocates, frees or keeps a pointer past
+ *     the call; the backward's scratch space is the caller's workspace buffer.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls enqueue
+ *     kernels and return; they never synchronise and never read device memory on the host,
+ *     so they can be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is launched. A failed validation
+ *     launches nothing and returns MX_E_ARG / MX_E_UNSUPPORTED / MX_E_WORKSPACE. A launch
+ *     error returns MX_E_DEVICE. Faults inside kernels surface at the caller's next
+ *     synchronisation. Nothing throws or aborts across this boundary.
+ *   - Element layouts (d = head_dim, contiguous):
+ *       batched (seq.cu_seqlens == NULL): [B, H, L, d]
+ *       packed  (seq.cu_seqlens != NULL): [T, H, d], documents back to back
+ *   - Quantised views. A group is 32 elements with one E8M0 scale byte (exponent + 127).
+ *       ROW view  (groups of 32 channels of one token): codes in the element layout above
+ *                 ([B,H,L,d] / [T,H,d], uint8); scales [B,H,L,d/32] / [T,H,d/32] (uint8),
+ *                 i.e. the scale of code index i is scales[i / 32].
+ *       SEQ view  (groups of 32 consecutive tokens of one channel, starting at the sequence
+ *                 or document start; the last group of a sequence may be partial):
+ *                 codes  [B, H, G, d, 32]      scales [B, H, G, d]     (batched, G = ceil(L/32))
+ *                 codes  [H, Gc, d, 32]        scales [H, Gc, d]       (packed, Gc = T/32 + n_docs)
+ *                 In packed mode document j's group g sits at group row floor(cu[j]/32) + j + g;
+ *                 rows not covered by any document are padding (never read).
+ *                 Inside each 32-byte group the token at offset t (0..31) is stored at byte
+ *                 position MX_SEQ_POS(t) = 16*((t>>2)&1) + 4*(t>>3) + (t&3); padding tokens
+ *                 of a partial group hold code 0.
+ */
+#ifndef MXATTN_H
+#define MXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXATTN_ABI_VERSION 1
+
+#define MX_SEQ_POS(t) (16 * (((t) >> 2) & 1) + 4 * ((t) >> 3) + ((t) & 3))
+
+typedef enum {
+  MX_OK = 0,
+  MX_E_ARG = 1,          /* null pointer, bad size, inconsistent geometry */
+  MX_E_UNSUPPORTED = 2,  /* valid but not implemented here (e.g. head_dim not in {64, 128}) */
+  MX_E_WORKSPACE = 3,    /* workspace missing or smaller than mx_attn_workspace_size() */
+  MX_E_DEVICE = 4        /* a kernel launch failed */
+} mx_status;
+
+typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
+
+enum { MX_VIEW_ROW = 1, MX_VIEW_SEQ = 2 };
+enum { MX_DQ_F32 = 0, MX_DQ_F16_BOOST = 1 };
+
+/* Bits of the device status word (see mx_read_flags). */
+enum { MX_FLAG_DQ_OVERFLOW = 1u, MX_FLAG_NONFINITE = 2u };
+
+/* Sequence geometry.
+ *   batched: cu_seqlens = NULL; batch = B, seqlen = L (>= 1).
+ *   packed:  cu_seqlens = device int32[n_docs + 1], cu[0] = 0, non-decreasing, cu[n_docs] = T;
+ *            total_tokens = T and max_seqlen >= every document length must be given on the
+ *            host (the library never reads cu_seqlens on the host). batch/seqlen ignored. */
+typedef struct {
+  int64_t batch;
+  int64_t seqlen;
+  const int32_t* cu_seqlens;
+  int32_t n_docs;
+  int32_t max_seqlen;
+  int64_t total_tokens;
+} mx_seq;
+
+/* One quantised view: codes and E8M0 scale bytes (layouts above). */
+typedef struct {
+  uint8_t* codes;
+  uint8_t* scales;
+} mx_qview;
+
+typedef struct {
+  mx_seq seq;
+  int32_t heads_q;        /* H (query heads) */
+  int32_t heads_kv;       /* key/value heads; heads_q % heads_kv == 0 (GQA groups are contiguous) */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t causal;         /* 1: key j visible to query i iff j <= i inside the sequence/document */
+  float softmax_scale;    /* alpha; 0 -> head_dim^-1/2 */
+  mx_dtype out_dtype;     /* storage type of O, dQ, dK, dV */
+  int32_t dq_mode;        /* MX_DQ_F32 or MX_DQ_F16_BOOST (FP16 partial sums x 2^9) */
+  int32_t deterministic;  /* reserved: must be 0 here */
+  void* workspace;        /* device scratch for mx_attn_bwd (see mx_attn_workspace_size) */
+  size_t workspace_bytes;
+} mx_attn_desc;
+
+/* Quantise one tensor x (layout above, dtype MX_F32 or MX_BF16) into the ROW and/or SEQ view
+ * in a single pass over x. views = MX_VIEW_ROW | MX_VIEW_SEQ; the unused output may be NULL.
+ * Group exponent: the smallest e with amax * 2^-e <= 448 (amax 0 -> -127), clamped to
+ * [-127, 127]; codes = E4M3 round-to-nearest-even of x * 2^-e. A group holding a NaN or an
+ * infinity gets scale 0xFF and codes 0x7F. */
+mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x, mx_dtype dtype,
+                      int32_t views, mx_qview* row_out, mx_qview* seq_out, void* stream);
+
+/* Forward: O [layout above, out_dtype] and LSE float32 [B,H,L] / [T,H] (natural log,
+ * +inf for a row without visible keys). q_row / k_row: ROW views of Q and K (heads_q and
+ * heads_kv heads); v_seq: SEQ view of V. */
+mx_status mx_attn_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o,
+                      float* lse, void* stream);
+
+/* Backward: given G = dL/dO (g_dtype), the saved O and LSE of the forward, and the views of
+ * Q, K, V, writes dQ [like Q], dK and dV [like K] in out_dtype. G is quantised internally
+ * (ROW and SEQ views) into the workspace, D = rowsum(G_row o O) is formed there, and dQ is
+ * accumulated there (FP32, or FP16 x 2^9 for dq_mode = MX_DQ_F16_BOOST). */
+mx_status mx_attn_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
+                      mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
+                      mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
+
+/* Packed (jagged) entry points: identical to mx_attn_fwd / mx_attn_bwd and the same kernels,
+ * but desc->seq.cu_seqlens is required (MX_E_ARG otherwise). */
+mx_status mx_attn_varlen_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq,
+                             void* o, float* lse, void* stream);
+mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
+                             mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
+                             mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
+
+/* Bytes of device workspace mx_attn_bwd needs for this descriptor (0 for the forward). */
+size_t mx_attn_workspace_size(const mx_attn_desc* desc, int32_t for_bwd);
+
+/* Byte sizes of the quantised views of a tensor with `heads` heads (codes, scales). */
+size_t mx_view_codes_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view);
+size_t mx_view_scales_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view);
+
+/* Copy the device status word of a backward workspace to *flags (synchronous; call after the
+ * stream has finished). Bits: MX_FLAG_DQ_OVERFLOW, MX_FLAG_NONFINITE. */
+mx_status mx_read_flags(const void* workspace, uint32_t* flags);
+
+/* Measurement hook (not part of the compute path). Registers `count` pairs of HIP events
+ * (hipEvent_t passed as void*, created by the caller): every following launch of the selected
+ * kernel records start[i % count] just before and stop[i % count] just after it, on the stream
+ * it is launched on, i = launch index since registration. kernel: 1 forward attention kernel,
+ * 2 backward main kernel, 3 mx_quantize, 4 backward G preprocessing, 5 dQ finalize; 0 (or
+ * count <= 0) turns the hook off. The event arrays must stay valid while registered. One
+ * hook per process; not thread-safe. */
+mx_status mx_profile_kernel(int32_t kernel, void* const* start_events, void* const* stop_events, int32_t count);
+
+const char* mx_strerror(mx_status s);
+int32_t mx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXATTN_H */

@@ -123,13 +123,17 @@ def _mx_dev(y, e, dy_rel, group_axis):
 
 
 def head_forward(q, k, v, causal, softmax_scale=None, quantized=True, out_dtype="bf16",
-                 bounds=False, arith=None, perturb=None):
+                 bounds=False, arith=None, perturb=None, rows=None):
     """Forward pass for one head: returns dict(O (float64, unrounded), O_out (rounded), lse,
     ell, and when bounds=True: B (ambiguity bound on O), eta (accumulation allowance)).
 
     ``perturb`` is a test hook: perturb(name, value, raw_budget) -> value, applied to the
     base-2 exponent argument x = S' - M before exp2, so tests can emulate device rounding
-    inside the stated budget and check that the result stays within the bound."""
+    inside the stated budget and check that the result stays within the bound.
+
+    ``rows`` (optional, sorted query indices) evaluates only those query rows -- each row is
+    independent in the forward, and its P groups run along keys -- and returns arrays with one
+    entry per selected row; Q is still quantised whole so the row-view groups are unchanged."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -143,24 +147,27 @@ def head_forward(q, k, v, causal, softmax_scale=None, quantized=True, out_dtype=
         Vt = mx_fake_quant(v, axis=0)      # seq view: 32 tokens of one channel
     else:
         Qt, Kt, Vt = q, k, v
-    O = np.zeros((n, d))
-    lse = np.full(n, np.inf)
-    ell_all = np.zeros(n)
-    B = np.zeros((n, d)) if bounds else None
-    eta = np.zeros((n, d)) if bounds else None
-    dmax = np.zeros(n) if bounds else None
+    sel = np.arange(n) if rows is None else np.asarray(rows)
+    n_out = len(sel)
+    O = np.zeros((n_out, d))
+    lse = np.full(n_out, np.inf)
+    ell_all = np.zeros(n_out)
+    B = np.zeros((n_out, d)) if bounds else None
+    eta = np.zeros((n_out, d)) if bounds else None
+    dmax = np.zeros(n_out) if bounds else None
     absV = np.abs(Vt)
     c = alpha * LOG2E
-    for r0 in range(0, n, ROW_CHUNK):
-        r1 = min(n, r0 + ROW_CHUNK)
-        mask = visible(r1 - r0, nk, causal, r0)
-        Sraw = Qt[r0:r1] @ Kt.T
+    for r0 in range(0, n_out, ROW_CHUNK):
+        r1 = min(n_out, r0 + ROW_CHUNK)
+        qi = sel[r0:r1]
+        mask = (np.arange(nk)[None, :] <= qi[:, None]) if causal else np.ones((r1 - r0, nk), dtype=bool)
+        Sraw = Qt[qi] @ Kt.T
         Sp = np.where(mask, Sraw * c, -np.inf)            # base-2 logits S' = S log2 e
         has = mask.any(axis=1)
         M = np.where(has, np.ceil(np.max(Sp, axis=1)), 0.0)
         x = Sp - M[:, None]
         if bounds or perturb:
-            absS = np.abs(Qt[r0:r1]) @ np.abs(Kt).T
+            absS = np.abs(Qt[qi]) @ np.abs(Kt).T
             dx = c * (A.mfma_rel * absS + np.abs(Sraw) * 2 * U32) + np.abs(np.where(mask, x, 0.0)) * U32
         if perturb:
             x = np.where(mask, perturb("x", np.where(mask, x, 0.0), dx), -np.inf)
@@ -210,7 +217,8 @@ def _pad_groups(a):
 
 
 def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantized=True,
-                  out_dtype="bf16", bounds=False, arith=None, fwd=None, dq_mode="f32", perturb=None):
+                  out_dtype="bf16", bounds=False, arith=None, fwd=None, dq_mode="f32", perturb=None,
+                  dq_blocks=None):
     """Backward pass for one head (Algorithm 1 steps 09-16 of the FLAMIA notes).
 
     o_saved: O as stored by the forward (output dtype); lse: the forward's row LSE (natural
@@ -219,6 +227,10 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
     (the device backward is given the same values); passing ``fwd`` (a head_forward result
     with bounds) instead adds the uncertainty of a device forward's own O and LSE. ``perturb`` is the
     test hook of head_forward, applied to x = (S - LSE) log2 e, to E and to D.
+
+    ``dq_blocks`` (optional) lists 32-row query blocks (block index b = rows 32b..32b+31): only
+    dQ of those rows is evaluated (a dS scale block is 32 queries x 32 keys, so a whole query
+    block determines its rows' dQ); dK and dV are then returned as NaN.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -261,8 +273,11 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
     if perturb:
         D = perturb("D", D, dD)
     c = alpha * LOG2E
-    for r0 in range(0, n, ROW_CHUNK):
-        r1 = min(n, r0 + ROW_CHUNK)
+    if dq_blocks is None:
+        chunks = [(r0, min(n, r0 + ROW_CHUNK)) for r0 in range(0, n, ROW_CHUNK)]
+    else:
+        chunks = [(32 * int(b), min(n, 32 * int(b) + 32)) for b in sorted(set(dq_blocks))]
+    for r0, r1 in chunks:
         rows = r1 - r0
         mask = visible(rows, nk, causal, r0)
         Sraw = Qr[r0:r1] @ Kr.T
@@ -302,6 +317,9 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
             edK += (A.mfma_rel + n_steps * U32) * alpha * (np.abs(Uh).T @ np.abs(Qs[r0:r1]))
             acc_rel = n_steps * U32 if dq_mode == "f32" else 2 * (nk / 64 + 2) * 2.0 ** -11
             edQ[r0:r1] = (A.mfma_rel + acc_rel) * alpha * (np.abs(Uh) @ np.abs(Ks))
+    if dq_blocks is not None:
+        dK[:] = np.nan
+        dV[:] = np.nan
     out = dict(dQ=dQ, dK=dK, dV=dV, D=D, dQ_out=round_to(dQ, out_dtype), dK_out=round_to(dK, out_dtype),
                dV_out=round_to(dV, out_dtype))
     if bounds:

@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports every function include/mxattn.h
+declares, and host-side validation rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_mxfp8_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mxattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:mx_status|size_t|const char\*|int32_t)\s+(mx_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.lib_path()):
+        pytest.fail("libmxattn.so is not built (python -m block_scaled_mxfp8_amd.build)")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("mx_quantize", "mx_attn_fwd", "mx_attn_bwd", "mx_attn_varlen_fwd", "mx_attn_varlen_bwd",
+                     "mx_attn_workspace_size", "mx_read_flags", "mx_strerror", "mx_abi_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.mx_abi_version() == 1
+    assert lib.mx_strerror(0) == b"ok"
+
+
+def _seq(batch=1, seqlen=64):
+    s = _lib._Seq()
+    s.batch, s.seqlen = batch, seqlen
+    return s
+
+
+FAKE = 0x10000   # a non-null, 256-aligned address that validation never dereferences
+
+
+def test_quantize_validation_errors(lib):
+    s = _seq()
+    v = _lib._QView(FAKE, FAKE)
+    assert lib.mx_quantize(None, 1, 128, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert lib.mx_quantize(ctypes.byref(s), 1, 128, None, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert lib.mx_quantize(ctypes.byref(s), 1, 96, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_UNSUPPORTED
+    assert lib.mx_quantize(ctypes.byref(s), 0, 128, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert lib.mx_quantize(ctypes.byref(s), 1, 128, FAKE, 7, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert lib.mx_quantize(ctypes.byref(s), 1, 128, FAKE + 2, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    bad = _seq(batch=0)
+    assert lib.mx_quantize(ctypes.byref(bad), 1, 128, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    # packed geometry without documents
+    p = _lib._Seq()
+    p.cu_seqlens, p.n_docs, p.max_seqlen, p.total_tokens = FAKE, 0, 10, 10
+    assert lib.mx_quantize(ctypes.byref(p), 1, 128, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+
+
+def _desc(**kw):
+    d = _lib._Desc()
+    d.seq = _seq()
+    d.heads_q, d.heads_kv, d.head_dim, d.causal = 4, 2, 128, 1
+    d.out_dtype = _lib.MX_BF16
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_attention_validation_errors(lib):
+    v = _lib._QView(FAKE, FAKE)
+    f = lib.mx_attn_fwd
+    assert f(None, v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(_desc(heads_kv=3)), v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(_desc(head_dim=80)), v, v, v, FAKE, FAKE, None) == _lib.MX_E_UNSUPPORTED
+    assert f(ctypes.byref(_desc(deterministic=1)), v, v, v, FAKE, FAKE, None) == _lib.MX_E_UNSUPPORTED
+    assert f(ctypes.byref(_desc(softmax_scale=float("nan"))), v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(_desc()), _lib._QView(0, FAKE), v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(_desc()), v, v, v, None, FAKE, None) == _lib.MX_E_ARG
+    # varlen entry points require cu_seqlens
+    assert lib.mx_attn_varlen_fwd(ctypes.byref(_desc()), v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    b = lib.mx_attn_bwd
+    d = _desc()
+    assert b(ctypes.byref(d), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None) == _lib.MX_E_WORKSPACE
+    need = lib.mx_attn_workspace_size(ctypes.byref(d), 1)
+    assert need > 0 and lib.mx_attn_workspace_size(ctypes.byref(d), 0) == 0
+    d.workspace, d.workspace_bytes = FAKE, need - 1
+    assert b(ctypes.byref(d), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None) == _lib.MX_E_WORKSPACE
+    assert b(ctypes.byref(d), v, v, v, v, v, FAKE, FAKE, FAKE, 9, FAKE, FAKE, FAKE, None) == _lib.MX_E_ARG
+    assert lib.mx_attn_varlen_bwd(ctypes.byref(d), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None) == _lib.MX_E_ARG
+
+
+def test_view_sizes(lib):
+    s = _seq(batch=2, seqlen=70)
+    assert lib.mx_view_codes_bytes(ctypes.byref(s), 3, 128, 1) == 2 * 3 * 70 * 128
+    assert lib.mx_view_scales_bytes(ctypes.byref(s), 3, 128, 1) == 2 * 3 * 70 * 4
+    assert lib.mx_view_codes_bytes(ctypes.byref(s), 3, 128, 2) == 2 * 3 * 3 * 128 * 32
+    assert lib.mx_view_scales_bytes(ctypes.byref(s), 3, 128, 2) == 2 * 3 * 3 * 128
+    p = _lib._Seq()
+    p.cu_seqlens, p.n_docs, p.max_seqlen, p.total_tokens = FAKE, 5, 100, 300
+    assert lib.mx_view_codes_bytes(ctypes.byref(p), 2, 64, 2) == 2 * (300 // 32 + 5) * 64 * 32
+
+
+def test_binding_geometry_and_allocation_sizes_agree_with_library(lib):
+    # heads/head_dim come from the layout: [B, H, L, d] batched, [T, H, d] packed
+    assert _lib._heads_dim((2, 3, 70, 128), None) == (3, 128)
+    assert _lib._heads_dim((300, 2, 64), object()) == (2, 64)
+    with pytest.raises(ValueError):
+        _lib._heads_dim((3, 70, 128), None)
+    # the shapes the binding allocates hold exactly the bytes the library addresses
+    import math
+    for shape in ((1, 1, 256, 64), (2, 3, 70, 128), (1, 2, 1, 128), (4, 32, 4096, 128)):
+        s = _lib._Seq()
+        s.batch, s.seqlen, s.total_tokens = shape[0], shape[2], shape[0] * shape[2]
+        h, d = _lib._heads_dim(shape, None)
+        cs, ss = _lib._seq_view_shapes(shape, s, None)
+        assert math.prod(shape) == lib.mx_view_codes_bytes(ctypes.byref(s), h, d, 1)
+        assert math.prod(shape[:-1]) * (d // 32) == lib.mx_view_scales_bytes(ctypes.byref(s), h, d, 1)
+        assert math.prod(cs) == lib.mx_view_codes_bytes(ctypes.byref(s), h, d, 2)
+        assert math.prod(ss) == lib.mx_view_scales_bytes(ctypes.byref(s), h, d, 2)

@@ -1,0 +1,169 @@
+"""Packed (jagged) attention: the varlen entry points vs the oracle run document by document,
+and document isolation (FLAMIA notes section 6: scale groups never straddle documents, so
+changing another document changes nothing in this one)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from block_scaled_mxfp8_amd import (MX_DQ_F32, mx_attn_varlen_bwd, mx_attn_varlen_fwd, mx_quantize)
+from tests.layouts import as_f64, to_device
+from tests.metrics import cosine, gate, rms
+
+pytestmark = pytest.mark.gpu
+REL = 2e-2
+
+
+def _packed(lengths, H, Hkv, d, seed=11, scale_docs=None):
+    cu = synth.cu_seqlens_of(np.array(lengths))
+    T = int(cu[-1])
+    rng = np.random.default_rng(seed)
+    x = {n: rng.standard_normal((T, H if n in ("q", "g") else Hkv, d)).astype(np.float32) for n in ("q", "k", "v", "g")}
+    return x, cu
+
+
+def _dev(x, cu):
+    t = {n: to_device(x[n], torch.bfloat16) for n in x}
+    return t, torch.from_numpy(cu).cuda()
+
+
+def _fwd(t, cud, maxlen, causal=True):
+    q_row, _ = mx_quantize(t["q"], views=1, cu_seqlens=cud, max_seqlen=maxlen)
+    k_row, _ = mx_quantize(t["k"], views=1, cu_seqlens=cud, max_seqlen=maxlen)
+    _, v_seq = mx_quantize(t["v"], views=2, cu_seqlens=cud, max_seqlen=maxlen)
+    return mx_attn_varlen_fwd(q_row, k_row, v_seq, cud, max_seqlen=maxlen, causal=causal)
+
+
+def _bwd(t, o, lse, cud, maxlen, causal=True, dq_mode=MX_DQ_F32):
+    q_row, q_seq = mx_quantize(t["q"], cu_seqlens=cud, max_seqlen=maxlen)
+    k_row, k_seq = mx_quantize(t["k"], cu_seqlens=cud, max_seqlen=maxlen)
+    v_row, _ = mx_quantize(t["v"], views=1, cu_seqlens=cud, max_seqlen=maxlen)
+    return mx_attn_varlen_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], cud, max_seqlen=maxlen,
+                              causal=causal, dq_mode=dq_mode)
+
+
+LENGTHS = [1, 31, 32, 33, 100, 7, 300, 129, 64]
+
+
+@pytest.mark.parametrize("H,Hkv,d", [(2, 2, 128), (4, 2, 64)])
+def test_varlen_forward_matches_oracle(H, Hkv, d):
+    print(f"[varlen fwd] H{H} kv{Hkv} d{d}", flush=True)
+    x, cu = _packed(LENGTHS, H, Hkv, d)
+    t, cud = _dev(x, cu)
+    o, lse = _fwd(t, cud, max(LENGTHS))
+    torch.cuda.synchronize()
+    o, lse = as_f64(o), as_f64(lse)
+    q, k, v = (as_f64(t[n]) for n in ("q", "k", "v"))
+    devs, refs, allows = [], [], []
+    for j in range(len(LENGTHS)):
+        a, b = cu[j], cu[j + 1]
+        for h in range(H):
+            hk = h // (H // Hkv)
+            f = oracle.head_forward(q[a:b, h], k[a:b, hk], v[a:b, hk], True, bounds=True)
+            devs.append(o[a:b, h])
+            refs.append(f["O"])
+            allows.append(f["B"] + f["eta"] + oracle.ulp_of(o[a:b, h], "bf16") / 2)
+            assert np.all(np.abs(lse[a:b, h] - f["lse"]) <= 2e-5 + 4 * f["drel_max"] + 1e-6 * np.abs(f["lse"]))
+    ok, worst, plain, namb = gate(np.concatenate(devs), np.concatenate(refs), np.concatenate(allows), REL)
+    print(f"  O: plain max|d|/rms {plain:.3e}, worst excess {worst:.3e}, B>0: {namb}", flush=True)
+    assert ok
+
+
+@pytest.mark.parametrize("H,Hkv,d", [(2, 2, 128), (4, 2, 64)])
+def test_varlen_backward_matches_oracle(H, Hkv, d):
+    print(f"[varlen bwd] H{H} kv{Hkv} d{d}", flush=True)
+    x, cu = _packed(LENGTHS, H, Hkv, d)
+    t, cud = _dev(x, cu)
+    q, k, v, g = (as_f64(t[n]) for n in ("q", "k", "v", "g"))
+    T = q.shape[0]
+    O = np.zeros(q.shape)
+    LSE = np.zeros((T, H), np.float32)
+    for j in range(len(LENGTHS)):
+        a, b = cu[j], cu[j + 1]
+        for h in range(H):
+            hk = h // (H // Hkv)
+            f = oracle.head_forward(q[a:b, h], k[a:b, hk], v[a:b, hk], True)
+            O[a:b, h], LSE[a:b, h] = f["O_out"], f["lse"]
+    dq, dk, dv, ws = _bwd(t, torch.from_numpy(O).to(torch.bfloat16).cuda(), torch.from_numpy(LSE).cuda(), cud,
+                          max(LENGTHS))
+    torch.cuda.synchronize()
+    dev = {"dQ": as_f64(dq), "dK": as_f64(dk), "dV": as_f64(dv)}
+    ref = {"dQ": np.zeros(q.shape), "dK": np.zeros(k.shape), "dV": np.zeros(k.shape)}
+    allow = {n: np.zeros_like(ref[n]) for n in ref}
+    for j in range(len(LENGTHS)):
+        a, b = cu[j], cu[j + 1]
+        for h in range(H):
+            hk = h // (H // Hkv)
+            r = oracle.head_backward(q[a:b, h], k[a:b, hk], v[a:b, hk], O[a:b, h], LSE[a:b, h].astype(np.float64),
+                                     g[a:b, h], True, bounds=True)
+            ref["dQ"][a:b, h] = r["dQ"]
+            allow["dQ"][a:b, h] = r["B_dQ"] + r["eta_dQ"]
+            for n in ("dK", "dV"):
+                ref[n][a:b, hk] += r[n]
+                allow[n][a:b, hk] += r["B_" + n] + r["eta_" + n]
+    for n in ("dQ", "dK", "dV"):
+        ok, worst, plain, namb = gate(dev[n], ref[n], allow[n] + oracle.ulp_of(dev[n], "bf16") / 2, REL)
+        print(f"  {n}: plain max|d|/rms {plain:.3e}, worst excess {worst:.3e}, B>0: {namb}", flush=True)
+        assert ok, n
+
+
+def test_varlen_document_isolation_is_bitwise():
+    # Perturb every other document (x1000 and sign flips): O, LSE, dK, dV of document j are
+    # bit-identical. dQ of a document longer than one 128-key tile sums atomics from several
+    # workgroups in no fixed order, so it is compared to float32 rounding instead.
+    lengths = [40, 200, 13, 96]
+    H, d = 2, 128
+    x, cu = _packed(lengths, H, H, d, seed=5)
+    y = {n: x[n].copy() for n in x}
+    j = 1
+    for n in y:
+        y[n][:cu[j]] *= -1000.0
+        y[n][cu[j + 1]:] *= 1e-3
+    outs = []
+    for inp in (x, y):
+        t, cud = _dev(inp, cu)
+        o, lse = _fwd(t, cud, 200)
+        dq, dk, dv, ws = _bwd(t, o, lse, cud, 200)
+        torch.cuda.synchronize()
+        a, b = cu[j], cu[j + 1]
+        outs.append([z[a:b].cpu() for z in (o, lse, dq, dk, dv)])
+    for name, u, v in zip(("O", "LSE", "dQ", "dK", "dV"), outs[0], outs[1]):
+        if name == "dQ":
+            assert torch.allclose(u.float(), v.float(), rtol=1e-2, atol=1e-3 * float(u.float().abs().max())), name
+        else:
+            assert torch.equal(u, v), name
+
+
+def test_c4_packed_workload_sampled_documents():
+    # The full c4 workload (128 documents, log-normal lengths 32..2048, H4 d128, causal per
+    # document) on the GPU; the oracle checks a sample of documents (shortest, longest, median).
+    x = synth.make_inputs("c4")
+    cu = x.pop("cu_seqlens")
+    lengths = np.diff(cu)
+    maxlen = int(lengths.max())
+    print(f"[c4] T={cu[-1]} docs={len(lengths)} max={maxlen}", flush=True)
+    t = {n: to_device(x[n], torch.bfloat16) for n in x}
+    cud = torch.from_numpy(cu).cuda()
+    o, lse = _fwd(t, cud, maxlen)
+    dq, dk, dv, ws = _bwd(t, o, lse, cud, maxlen)
+    torch.cuda.synchronize()
+    q, k, v, g = (as_f64(t[n]) for n in ("q", "k", "v", "g"))
+    o, dq, dk, dv = (as_f64(z) for z in (o, dq, dk, dv))
+    order = np.argsort(lengths)
+    sample = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1]), 3})
+    devs, refs, allows = [], [], []
+    for j in sample:
+        a, b = cu[j], cu[j + 1]
+        for h in range(q.shape[1]):
+            f = oracle.head_forward(q[a:b, h], k[a:b, h], v[a:b, h], True, bounds=True)
+            devs.append(o[a:b, h])
+            refs.append(f["O"])
+            allows.append(f["B"] + f["eta"] + oracle.ulp_of(o[a:b, h], "bf16") / 2)
+            r = oracle.head_reference(q[a:b, h], k[a:b, h], v[a:b, h], g[a:b, h], True)
+            for n, z in (("O", o), ("dQ", dq), ("dK", dk), ("dV", dv)):
+                cs = cosine(z[a:b, h], r[n])
+                assert cs >= 0.995, (j, h, n, cs)
+    ok, worst, plain, namb = gate(np.concatenate(devs), np.concatenate(refs), np.concatenate(allows), REL)
+    print(f"  O sampled docs {sample}: plain max|d|/rms {plain:.3e}, worst excess {worst:.3e}", flush=True)
+    assert ok

@@ -263,3 +263,29 @@ def test_round_to_bf16_is_rne():
     y = np.random.default_rng(13).standard_normal(10000) * 100
     t = torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(round_to(y.astype(np.float32).astype(np.float64), "bf16"), t)
+
+
+def test_forward_row_subset_equals_full_rows():
+    rng = np.random.default_rng(14)
+    n, d = 200, 64
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    rows = np.array([0, 5, 31, 32, 150, 199])
+    for causal in (True, False):
+        full = head_forward(q, k, v, causal, bounds=True)
+        sub = head_forward(q, k, v, causal, bounds=True, rows=rows)
+        for key in ("O", "lse", "B", "eta"):
+            assert np.array_equal(sub[key], full[key][rows]), key
+
+
+def test_backward_dq_blocks_equal_full_rows():
+    rng = np.random.default_rng(15)
+    n, d = 160, 64
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    for causal in (True, False):
+        f = head_forward(q, k, v, causal)
+        full = head_backward(q, k, v, f["O_out"], f["lse"], g, causal, bounds=True)
+        part = head_backward(q, k, v, f["O_out"], f["lse"], g, causal, bounds=True, dq_blocks=[0, 3])
+        rows = np.r_[0:32, 96:128]
+        for key in ("dQ", "B_dQ", "eta_dQ"):
+            assert np.array_equal(part[key][rows], full[key][rows]), key
+        assert np.all(np.isnan(part["dK"]))
