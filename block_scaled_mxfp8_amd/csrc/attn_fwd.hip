@@ -38,20 +38,26 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBlockM = 32 * kWaves;  // queries per workgroup
 constexpr int kBlockN = 64;           // keys per tile
+constexpr int kStages = 3;            // LDS tile buffers: V(j), K(j+1) in use while tile j+2 lands
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_448 = 8.807354922057604f;
 
+// LDS tiles, written by LDS-DMA loads (lane i of a load lands at base + i * size).
+//  k:  K ROW codes [64 keys][d]; the 16-byte chunk c of key row r sits at chunk c ^ (r & 7)
+//      so the 32 rows an operand read touches spread over all banks.
+//  v:  V SEQ codes [2 groups][d channels][32 tokens]; the two 16-byte halves of channel ch
+//      are swapped when (ch >> 2) & 1, for the same reason.
+//  ks: K ROW scales [64 keys][d / 32];  vs: V SEQ scales [2 groups][d].
 template <int D>
 struct FwdSmem {
-  alignas(16) uint8_t k[2][kBlockN * D];             // K ROW codes, 16-byte chunks XOR-swizzled by key row
-  alignas(16) uint8_t v[2][2 * D * 32];              // V SEQ codes [group][channel][32], halves swizzled
-  alignas(16) uint8_t ks[2][kBlockN * (D / 32)];     // K ROW scales [key][d/32]
-  alignas(16) uint8_t vs[2][2 * D];                  // V SEQ scales [group][channel]
+  alignas(16) uint8_t k[kStages][kBlockN * D];
+  alignas(16) uint8_t v[kStages][2 * D * 32];
+  alignas(16) uint8_t ks[kStages][kBlockN * (D / 32)];
+  alignas(16) uint8_t vs[kStages][2 * D];
 };
 
 __device__ __forceinline__ int k_swz(int row, int chunk, int nchunk) { return chunk ^ (row & (nchunk - 1) & 7); }
-
 __device__ __forceinline__ int v_half_swz(int c, int half) { return half ^ ((c >> 2) & 1); }
 
 // Work decode: which (sequence, head, query tile) this workgroup computes.
@@ -95,90 +101,97 @@ __device__ __forceinline__ Work decode_work(const AttnParams& p) {
   return w;
 }
 
-template <int D>
-struct TileRegs {
-  v4i k[D / 64];
-  v4i v[D / 64];
-  uint32_t ks;
-  uint32_t vs;
-};
+__device__ __forceinline__ void dma(const void* src, void* lds, int size) {
+  // LDS-DMA load: each lane's `size` (16 or 4) bytes land at lds + lane * size (lds is wave-uniform).
+  if (size == 16)
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
 
-// Global -> registers for key tile kt (zeros past the end of the sequence/document).
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Issue the LDS-DMA loads of key tile kt into stage st. Rows past the end of the sequence /
+// document are clamped to its last row (and its last SEQ group): they are finite, and their
+// scores are masked, so their P is 0. LDS-DMA writes at least one dword per lane, so the
+// 2-byte K scales of d = 64 take an ordinary load instead: returned here, stored by
+// put_kscale before the barrier that publishes the tile.
 template <int D>
-__device__ __forceinline__ void load_tile(const AttnParams& p, const Work& w, int hkv, int kt, TileRegs<D>& r) {
+__device__ __forceinline__ uint32_t issue_tile(const AttnParams& p, const Work& w, int hkv, int kt, FwdSmem<D>& sm,
+                                               int st) {
   const Geom& g = p.geom;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const long long sbase = packed(g) ? (long long)w.doc_start : (long long)w.s;
-  constexpr int NCH = D / 16;  // 16-byte chunks per key row
+  constexpr int NCH = D / 16;               // 16-byte chunks per key row
+  const int nlast = w.n - 1;
+  const int glast = ((w.n + 31) >> 5) - 1;
 #pragma unroll
-  for (int i = 0; i < D / 64; i++) {
-    const int ch = tid + i * 256;
-    const int row = ch / NCH, cc = ch % NCH;
-    const int key = kt * kBlockN + row;
-    if (key < w.n) {
-      const long long off = elem_offset(g, p.heads_kv, D, sbase, hkv, key, cc * 16);
-      r.k[i] = *reinterpret_cast<const v4i*>(p.k_codes + off);
-    } else {
-      r.k[i] = v4i{0, 0, 0, 0};
-    }
-    // V: two consecutive SEQ group rows of 32 tokens (D x 32 bytes each)
-    const int grp = ch / (2 * D);
-    const int gi = 2 * kt + grp;
-    const int ngroups = (w.n + 31) >> 5;
-    if (gi < ngroups) {
-      const long long row0 = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
-      r.v[i] = *reinterpret_cast<const v4i*>(p.v_codes + row0 * D * 32 + (ch % (2 * D)) * 16);
-    } else {
-      r.v[i] = v4i{0, 0, 0, 0};
-    }
+  for (int j = wave; j < kBlockN * NCH / 64; j += kWaves) {     // K codes
+    const int pch = j * 64 + lane;
+    const int r = pch / NCH;
+    const int c = k_swz(r, pch % NCH, NCH);
+    const int key = min(kt * kBlockN + r, nlast);
+    dma(p.k_codes + elem_offset(g, p.heads_kv, D, sbase, hkv, key, c * 16), &sm.k[st][j * 1024], 16);
   }
-  r.ks = 0;
-  r.vs = 0;
-  if (tid < kBlockN) {
-    const int key = kt * kBlockN + tid;
-    if (key < w.n) {
-      const long long off = elem_offset(g, p.heads_kv, D, sbase, hkv, key, 0) >> 5;
-      r.ks = (D == 128) ? *reinterpret_cast<const uint32_t*>(p.k_scales + off)
-                        : (uint32_t)*reinterpret_cast<const uint16_t*>(p.k_scales + off);
-    }
-  } else if (tid < kBlockN + D / 2) {
-    const int word = tid - kBlockN;          // dword of the [2][D] scale block
-    const int grp = (word * 4) / D;
-    const int gi = 2 * kt + grp;
-    const int ngroups = (w.n + 31) >> 5;
-    if (gi < ngroups) {
-      const long long row0 = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
-      r.vs = *reinterpret_cast<const uint32_t*>(p.v_scales + row0 * D + (word * 4) % D);
-    }
+#pragma unroll
+  for (int j = wave; j < 4 * D / 64; j += kWaves) {             // V codes (2 groups x D x 2 halves)
+    const int pch = j * 64 + lane;
+    const int grp = pch / (2 * D);
+    const int ch = (pch % (2 * D)) >> 1;
+    const int half = v_half_swz(ch, pch & 1);
+    const int gi = min(2 * kt + grp, glast);
+    const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
+    dma(p.v_codes + (row * D + ch) * 32 + half * 16, &sm.v[st][j * 1024], 16);
   }
+  uint32_t kscale = 0;
+  if (wave == 0) {                                               // K scales, one key per lane
+    const int key = min(kt * kBlockN + lane, nlast);
+    const uint8_t* src = p.k_scales + (elem_offset(g, p.heads_kv, D, sbase, hkv, key, 0) >> 5);
+    if (D == 128) dma(src, sm.ks[st], 4);
+    else kscale = *reinterpret_cast<const uint16_t*>(src);
+  } else if (wave == 1 && lane < D / 2) {                        // V scales, one dword per lane
+    const int gi = min(2 * kt + (lane * 4) / D, glast);
+    const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
+    dma(p.v_scales + row * D + (lane * 4) % D, sm.vs[st], 4);
+  }
+  return kscale;
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(FwdSmem<D>& sm, int buf, const TileRegs<D>& r) {
-  const int tid = threadIdx.x;
-  constexpr int NCH = D / 16;
-#pragma unroll
-  for (int i = 0; i < D / 64; i++) {
-    const int ch = tid + i * 256;
-    const int row = ch / NCH, cc = ch % NCH;
-    *reinterpret_cast<v4i*>(&sm.k[buf][row * D + (k_swz(row, cc, NCH) << 4)]) = r.k[i];
-    const int grp = ch / (2 * D);
-    const int c = (ch / 2) % D;
-    const int half = ch & 1;
-    *reinterpret_cast<v4i*>(&sm.v[buf][(grp * D + c) * 32 + (v_half_swz(c, half) << 4)]) = r.v[i];
-  }
-  if (tid < kBlockN) {
-    if (D == 128) *reinterpret_cast<uint32_t*>(&sm.ks[buf][tid * 4]) = r.ks;
-    else *reinterpret_cast<uint16_t*>(&sm.ks[buf][tid * 2]) = (uint16_t)r.ks;
-  } else if (tid < kBlockN + D / 2) {
-    *reinterpret_cast<uint32_t*>(&sm.vs[buf][(tid - kBlockN) * 4]) = r.vs;
-  }
+__device__ __forceinline__ void put_kscale(FwdSmem<D>& sm, int st, uint32_t kscale) {
+  if (D == 64 && threadIdx.x < 64) *reinterpret_cast<uint16_t*>(&sm.ks[st][threadIdx.x * 2]) = (uint16_t)kscale;
 }
 
 __device__ __forceinline__ v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 
+// S^T for the two 32-key half tiles of stage st: keys are MFMA rows, the wave's 32 queries columns.
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
+__device__ __forceinline__ void scores(const FwdSmem<D>& sm, int st, const v8i* qop, const int* qsc, v16f* sacc) {
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5, l32 = lane & 31;
+  constexpr int NS = D / 64;
+  constexpr int NCH = D / 16;
+#pragma unroll
+  for (int T = 0; T < 2; T++) {
+    const int row = T * 32 + l32;
+    const uint32_t ksw = (D == 128) ? *reinterpret_cast<const uint32_t*>(&sm.ks[st][row * 4])
+                                    : (uint32_t)*reinterpret_cast<const uint16_t*>(&sm.ks[st][row * 2]);
+    sacc[T] = v16f{};
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+      const v4i a = *reinterpret_cast<const v4i*>(&sm.k[st][row * D + (k_swz(row, 4 * s + hh, NCH) << 4)]);
+      const v4i b = *reinterpret_cast<const v4i*>(&sm.k[st][row * D + (k_swz(row, 4 * s + 2 + hh, NCH) << 4)]);
+      const int ksc = (ksw >> (8 * (2 * s + hh))) & 0xFF;
+      sacc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), qop[s], sacc[T], 0, 0, 0, ksc, 0, qsc[s]);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<D> sm;
   const Work w = decode_work(p);
   if (!w.valid) return;
@@ -193,6 +206,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
   const int qw = q0 + wave * 32;             // first query of this wave
   const int qi = qw + l32;                   // this lane's query
   const bool qvalid = qi < w.n;
+  const int kend = p.causal ? min(w.n, q0 + kBlockM) : w.n;  // keys this workgroup needs
+  const int nkt = (kend + kBlockN - 1) / kBlockN;
+
+  put_kscale<D>(sm, 0, issue_tile<D>(p, w, hkv, 0, sm, 0));
+  if (nkt > 1) put_kscale<D>(sm, 1, issue_tile<D>(p, w, hkv, 1, sm, 1));
 
   // ---- Q operand (B of S^T = K Q^T), kept in registers ----
   constexpr int NS = D / 64;  // contraction steps of 64 over d
@@ -202,19 +220,17 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
   for (int s = 0; s < NS; s++) {
     if (qvalid) {
       const long long off = elem_offset(g, p.heads_q, D, sbase, w.h, qi, 64 * s);
-      v4i a = *reinterpret_cast<const v4i*>(p.q_codes + off + 16 * hh);
-      v4i b = *reinterpret_cast<const v4i*>(p.q_codes + off + 32 + 16 * hh);
-      qop[s] = cat(a, b);
+      qop[s] = cat(*reinterpret_cast<const v4i*>(p.q_codes + off + 16 * hh),
+                   *reinterpret_cast<const v4i*>(p.q_codes + off + 32 + 16 * hh));
       qsc[s] = p.q_scales[(off >> 5) + hh];
     } else {
       qop[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
       qsc[s] = 127;
     }
   }
-
-  const int kend = p.causal ? min(w.n, q0 + kBlockM) : w.n;  // keys this workgroup needs
-  const int nkt = (kend + kBlockN - 1) / kBlockN;
   const float c = p.scale * kLog2e;   // S' = acc * c (base-2 logits)
+  // a wave is idle for key tile j when all its keys follow all its queries (causal) or it has no queries
+  auto active = [&](int j) { return qw < w.n && !(p.causal && j * kBlockN > qw + 31); };
 
   v16f oacc[D / 32];
 #pragma unroll
@@ -222,34 +238,19 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
   float M = -INFINITY;  // integer running max (base 2)
   float lsum = 0.f;     // this lane's share of l (its 16 keys of every half tile)
 
-  TileRegs<D> tr;
-  load_tile<D>(p, w, hkv, 0, tr);
-  store_tile<D>(sm, 0, tr);
+  wait_dma();
   __syncthreads();
+  v16f sacc[2], snext[2];
+  if (active(0)) scores<D>(sm, 0, qop, qsc, sacc);
 
   for (int kt = 0; kt < nkt; kt++) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) load_tile<D>(p, w, hkv, kt + 1, tr);
+    const int st = kt % kStages;
+    uint32_t kscale = 0;
+    if (kt + 2 < nkt) kscale = issue_tile<D>(p, w, hkv, kt + 2, sm, (kt + 2) % kStages);
+    // scores of the next tile go to the matrix cores while this tile's softmax runs on the VALU
+    if (kt + 1 < nkt && active(kt + 1)) scores<D>(sm, (kt + 1) % kStages, qop, qsc, snext);
     const int kbase = kt * kBlockN;
-    // skip tiles entirely above this wave's diagonal
-    const bool active = !(p.causal && kbase > qw + 31) && qw < w.n;
-    if (active) {
-      // ---- S^T for two 32-key half tiles ----
-      v16f sacc[2];
-#pragma unroll
-      for (int T = 0; T < 2; T++) {
-        sacc[T] = v16f{};
-        const int row = T * 32 + l32;
-#pragma unroll
-        for (int s = 0; s < NS; s++) {
-          constexpr int NCH = D / 16;
-          v4i a = *reinterpret_cast<const v4i*>(&sm.k[buf][row * D + (k_swz(row, 4 * s + hh, NCH) << 4)]);
-          v4i b = *reinterpret_cast<const v4i*>(&sm.k[buf][row * D + (k_swz(row, 4 * s + 2 + hh, NCH) << 4)]);
-          const int ksc = sm.ks[buf][row * (D / 32) + 2 * s + hh];
-          sacc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), qop[s], sacc[T], 0, 0, 0, ksc, 0,
-                                                                    qsc[s]);
-        }
-      }
+    if (active(kt)) {
       // ---- mask (diagonal / tail tiles only) ----
       const bool need_mask = (p.causal && kbase + kBlockN - 1 > qw) || kbase + kBlockN > w.n;
       if (need_mask) {
@@ -259,62 +260,65 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
           for (int i = 0; i < 16; i++) {
             const int key = kbase + T * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
             const bool vis = key < w.n && (!p.causal || key <= qi);
-            if (!vis) sacc[T][i] = -INFINITY;
+            sacc[T][i] = vis ? sacc[T][i] : -INFINITY;
           }
       }
       // ---- row / group maxima (raw accumulator units; c > 0) ----
-      float gm0 = sacc[0][0], gm1 = sacc[1][0];
+      float gm0 = fmaxf(sacc[0][0], sacc[0][1]), gm1 = fmaxf(sacc[1][0], sacc[1][1]);
 #pragma unroll
-      for (int i = 1; i < 16; i++) {
-        gm0 = fmaxf(gm0, sacc[0][i]);
-        gm1 = fmaxf(gm1, sacc[1][i]);
+      for (int i = 2; i < 16; i += 2) {
+        gm0 = fmaxf(fmaxf(gm0, sacc[0][i]), sacc[0][i + 1]);
+        gm1 = fmaxf(fmaxf(gm1, sacc[1][i]), sacc[1][i + 1]);
       }
       gm0 = fmaxf(gm0, swap32(gm0));
       gm1 = fmaxf(gm1, swap32(gm1));
-      const float tmax = fmaxf(gm0, gm1) * c;
-      const float Mnew = fmaxf(M, ceilf(tmax));
+      const float Mnew = fmaxf(M, ceilf(fmaxf(gm0, gm1) * c));
       if (__builtin_amdgcn_ballot_w64(Mnew > M)) {
-        const float f = (Mnew > M) ? exp2f(M - Mnew) : 1.f;   // exact power of two (0 when M = -inf)
+        const float f = (Mnew > M) ? __builtin_amdgcn_exp2f(M - Mnew) : 1.f;   // power of two (0 when M = -inf)
         lsum *= f;
 #pragma unroll
         for (int t = 0; t < D / 32; t++) oacc[t] *= f;
         M = Mnew;
       }
-      // ---- group exponents and P codes ----
+      // ---- group exponents and P codes: y = 2^(S' - M - e), e = ceil(max S' - M - log2 448) ----
       const bool rowlive = M > -INFINITY;
       const float e0 = fminf(fmaxf(ceilf(gm0 * c - M - kLog2_448), -127.f), 127.f);
       const float e1 = fminf(fmaxf(ceilf(gm1 * c - M - kLog2_448), -127.f), 127.f);
       const float off0 = rowlive ? M + e0 : 0.f;
       const float off1 = rowlive ? M + e1 : 0.f;
-      float y0[16], y1[16];
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; i++) {
-        y0[i] = exp2f(__builtin_fmaf(sacc[0][i], c, -off0));
-        y1[i] = exp2f(__builtin_fmaf(sacc[1][i], c, -off1));
-        s0 += y0[i];
-        s1 += y1[i];
+        sacc[0][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][i], c, -off0));
+        sacc[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][i], c, -off1));
+        s0 += sacc[0][i];
+        s1 += sacc[1][i];
       }
       lsum += ldexpf(s0, (int)e0) + ldexpf(s1, (int)e1);
       v8i pop;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        pop[j] = (int)pack4_e4m3(y0[4 * j], y0[4 * j + 1], y0[4 * j + 2], y0[4 * j + 3]);
-        pop[4 + j] = (int)pack4_e4m3(y1[4 * j], y1[4 * j + 1], y1[4 * j + 2], y1[4 * j + 3]);
+        pop[j] = (int)pack4_e4m3(sacc[0][4 * j], sacc[0][4 * j + 1], sacc[0][4 * j + 2], sacc[0][4 * j + 3]);
+        pop[4 + j] = (int)pack4_e4m3(sacc[1][4 * j], sacc[1][4 * j + 1], sacc[1][4 * j + 2], sacc[1][4 * j + 3]);
       }
       const int psc = (int)(hh ? e1 : e0) + 127;
       // ---- O^T += V^T P^T ----
 #pragma unroll
       for (int t = 0; t < D / 32; t++) {
         const int ch = t * 32 + l32;
-        v4i a = *reinterpret_cast<const v4i*>(&sm.v[buf][(0 * D + ch) * 32 + (v_half_swz(ch, hh) << 4)]);
-        v4i b = *reinterpret_cast<const v4i*>(&sm.v[buf][(1 * D + ch) * 32 + (v_half_swz(ch, hh) << 4)]);
-        const int vsc = sm.vs[buf][hh * D + ch];
+        const v4i a = *reinterpret_cast<const v4i*>(&sm.v[st][(0 * D + ch) * 32 + (v_half_swz(ch, hh) << 4)]);
+        const v4i b = *reinterpret_cast<const v4i*>(&sm.v[st][(1 * D + ch) * 32 + (v_half_swz(ch, hh) << 4)]);
+        const int vsc = sm.vs[st][hh * D + ch];
         oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), pop, oacc[t], 0, 0, 0, vsc, 0, psc);
       }
     }
-    if (kt + 1 < nkt) store_tile<D>(sm, buf ^ 1, tr);
-    __syncthreads();
+    sacc[0] = snext[0];
+    sacc[1] = snext[1];
+    if (kt + 2 < nkt) put_kscale<D>(sm, (kt + 2) % kStages, kscale);
+    if (kt + 1 < nkt) {
+      wait_dma();
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O = a / l, LSE = (M + log2 l) ln 2 ----
