@@ -3,7 +3,7 @@
 
 One step = the whole hot path on one batch of the B4 H32 L4096 d128 causal bf16 workload:
 mx_quantize of Q, K and V (ROW + SEQ views), the forward (O, LSE) and the backward (G
-views + D, main kernel, dQ finalize). Inputs are resident in HBM before the timed region.
+views + D, the dK/dV kernel, the dQ kernel). Inputs are resident in HBM before the timed region.
 
 FLOPs are causal-adjusted (FLAMIA notes section 6 visible-pair count): forward 4 d per
 visible pair, backward 10 d (five GEMMs). `value` is the step's fwd+bwd FLOPs over the
@@ -43,7 +43,7 @@ def main():
     import torch
 
     import synth
-    from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F32, PROFILE_BWD_FINAL, PROFILE_BWD_MAIN,
+    from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F32, PROFILE_BWD_DKDV, PROFILE_BWD_DQ,
                                         PROFILE_BWD_PREP, PROFILE_FWD, PROFILE_QUANTIZE, load, mx_attn_bwd,
                                         mx_attn_fwd, mx_profile_kernel, mx_quantize)
     from block_scaled_mxfp8_amd.flops import attn_flops, visible_pairs
@@ -76,12 +76,12 @@ def main():
     for _ in range(args.warmup):
         step()
     # the timed region also feeds the roofline line: events around every launch of the
-    # backward main kernel (the step's dominant kernel)
+    # backward dK/dV kernel (the step's dominant kernel)
     ev_main = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in ev_main:
         a.record()
         b.record()
-    mx_profile_kernel(PROFILE_BWD_MAIN, ev_main)
+    mx_profile_kernel(PROFILE_BWD_DKDV, ev_main)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -120,9 +120,9 @@ def main():
     for name, mode in (("f32", MX_DQ_F32), ("f16", MX_DQ_F16_BOOST)):
         if mode not in ws:
             _, _, _, ws[mode] = bwd(mode)()
-        main = kernel_ms(PROFILE_BWD_MAIN, bwd(mode))
+        main = kernel_ms(PROFILE_BWD_DKDV, bwd(mode))
         prep = kernel_ms(PROFILE_BWD_PREP, bwd(mode))
-        fin = kernel_ms(PROFILE_BWD_FINAL, bwd(mode))
+        fin = kernel_ms(PROFILE_BWD_DQ, bwd(mode))
         # whole call, events around it on the current stream
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -132,14 +132,18 @@ def main():
         s1.record()
         torch.cuda.synchronize()
         call = s0.elapsed_time(s1) / args.profile_steps
-        res_bwd[name] = dict(main_ms=main, prep_ms=prep, finalize_ms=fin, call_ms=call)
+        res_bwd[name] = dict(dkdv_ms=main, prep_ms=prep, dq_ms=fin, call_ms=call)
 
     q_elems = B * H * L * d
     quant_bytes = q_elems * (2 + 2 * (1 + 1 / 32))          # bf16 in, two views of codes + scales out
     tflops = lambda f, ms: f / (ms * 1e-3) / 1e12          # noqa: E731
+    # algorithmic FLOPs per kernel: dK/dV kernel S, E, dV, dK (4 of the 5 products, 8 d per
+    # visible pair); dQ kernel dQ (2 d) plus the S and E it rebuilds (4 d, not counted in the
+    # step's FLOPs, which follow the method's 10 d per pair)
+    f_dkdv = f_bwd * 4 // 5
     kernels = {
         "attn_fwd": dict(ms=ms_fwd, tflops=tflops(f_fwd, ms_fwd)),
-        "attn_bwd_main": dict(ms=ms_bwd_main, tflops=tflops(f_bwd, ms_bwd_main)),
+        "attn_bwd_dkdv": dict(ms=ms_bwd_main, tflops=tflops(f_dkdv, ms_bwd_main)),
         "quantize": dict(ms=ms_quant, gbs=quant_bytes / (ms_quant * 1e-3) / 1e9),
     }
     bwd_f32 = res_bwd["f32"]
@@ -167,15 +171,15 @@ def main():
         "bwd_f16dq_tflops": round(tflops(f_bwd, bwd_f16["call_ms"]), 2),
         "bwd_f16dq_pct_of_peak": round(100 * tflops(f_bwd, bwd_f16["call_ms"]) / PEAK_MXFP8_TFLOPS, 2),
         "quantize_gbs": round(kernels["quantize"]["gbs"], 1),
-        "kernels_ms": {"attn_fwd": round(ms_fwd, 4), "attn_bwd_main_f32": round(bwd_f32["main_ms"], 4),
-                       "attn_bwd_main_f16": round(bwd_f16["main_ms"], 4), "bwd_prep": round(bwd_f32["prep_ms"], 4),
-                       "dq_finalize": round(bwd_f32["finalize_ms"], 4), "quantize_one_tensor": round(ms_quant, 4)},
+        "kernels_ms": {"attn_fwd": round(ms_fwd, 4), "attn_bwd_dkdv": round(bwd_f32["dkdv_ms"], 4),
+                       "attn_bwd_dq_f32": round(bwd_f32["dq_ms"], 4), "attn_bwd_dq_f16": round(bwd_f16["dq_ms"], 4),
+                       "bwd_prep": round(bwd_f32["prep_ms"], 4), "quantize_one_tensor": round(ms_quant, 4)},
         "flops": {"fwd": f_fwd, "bwd": f_bwd, "visible_pairs": pairs},
         "pages_context": {"fa4_mx8_fwd_pflops_gb300": 2.85, "fa4_mx8_bwd_pflops_gb300_f16dq": 1.98,
                           "fa4_mx8_bwd_pflops_gb300_f32dq": 1.82},
-        "roofline": {"kernel": "attn_bwd_kernel<128> (backward main)", "bound": "mfma",
-                     "achieved": round(kernels["attn_bwd_main"]["tflops"], 2), "peak": PEAK_MXFP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(kernels["attn_bwd_main"]["tflops"] / PEAK_MXFP8_TFLOPS, 4),
+        "roofline": {"kernel": "attn_bwd_dkdv_kernel<128> (backward dK/dV)", "bound": "mfma",
+                     "achieved": round(kernels["attn_bwd_dkdv"]["tflops"], 2), "peak": PEAK_MXFP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kernels["attn_bwd_dkdv"]["tflops"] / PEAK_MXFP8_TFLOPS, 4),
                      "traffic": None},
     }
     if not args.no_cpu_baseline:

@@ -14,10 +14,10 @@ Functions mirror the C entry points:
 """
 from ._lib import (MX_VIEW_ROW, MX_VIEW_SEQ, MX_DQ_F32, MX_DQ_F16_BOOST, MXError, QView, lib_path, load,
                    mx_abi_version, mx_attn_bwd, mx_attn_fwd, mx_attn_varlen_bwd, mx_attn_varlen_fwd, mx_quantize,
-                   mx_attn_workspace_size, mx_read_flags, mx_profile_kernel, PROFILE_FWD, PROFILE_BWD_MAIN,
-                   PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_FINAL)
+                   mx_attn_workspace_size, mx_read_flags, mx_profile_kernel, PROFILE_FWD, PROFILE_BWD_DKDV,
+                   PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_DQ)
 
 __all__ = ["MX_VIEW_ROW", "MX_VIEW_SEQ", "MX_DQ_F32", "MX_DQ_F16_BOOST", "MXError", "QView", "lib_path", "load",
            "mx_abi_version", "mx_attn_bwd", "mx_attn_fwd", "mx_attn_varlen_bwd", "mx_attn_varlen_fwd", "mx_quantize",
-           "mx_attn_workspace_size", "mx_read_flags", "mx_profile_kernel", "PROFILE_FWD", "PROFILE_BWD_MAIN",
-           "PROFILE_QUANTIZE", "PROFILE_BWD_PREP", "PROFILE_BWD_FINAL"]
+           "mx_attn_workspace_size", "mx_read_flags", "mx_profile_kernel", "PROFILE_FWD", "PROFILE_BWD_DKDV",
+           "PROFILE_QUANTIZE", "PROFILE_BWD_PREP", "PROFILE_BWD_DQ"]

@@ -329,7 +329,7 @@ def mx_abi_version():
     return load().mx_abi_version()
 
 
-PROFILE_FWD, PROFILE_BWD_MAIN, PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_FINAL = 1, 2, 3, 4, 5
+PROFILE_FWD, PROFILE_BWD_DKDV, PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_DQ = 1, 2, 3, 4, 5
 _PROFILE_KEEP = []
 
 

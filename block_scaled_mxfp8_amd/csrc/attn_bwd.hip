@@ -3,27 +3,39 @@
 // Method: FLAMIA notes (zhongzhuzhou.org) section 2 (dV = P^T G, E = G V^T, U = P (E - D),
 // D = G . O, dQ = alpha U K, dK = alpha U^T Q) and section 5 Algorithm 1 steps 09-16 (encode
 // G and form D from its matching view; rebuild S and P from the same score operands and the
-// saved LSE; quantise U inside the tile; accumulate dV, dK and boosted FP16 dQ partials;
-// undo the boost at the end). Meta write-up (aixai.ru), "Quantising dS without a transpose":
-// dS is quantised in 32x32 blocks whose max-abs is reduced in the register layout; dQ is
-// accumulated in FP32 or in FP16 with a fixed 2^9 boost.
+// saved LSE; quantise U inside the tile; accumulate dV, dK and dQ; FP16 dQ partial sums carry
+// a fixed 2^9 boost that is undone at the end). Meta write-up (aixai.ru), "Quantising dS
+// without a transpose": dS is quantised in 32 x 32 blocks whose max-abs is reduced in the
+// register layout.
 //
 // Passes (all on the caller's stream):
-//   1. prep (quantize.hip with `o` set): G -> ROW and SEQ views, D = sum_c G_row~ O, dQ acc = 0.
-//   2. main (this file): one workgroup per (sequence or document, KV head, 128-key tile);
-//      wave w owns keys [32w, 32w+32) of the tile and keeps their dK, dV in registers; the
-//      workgroup walks 64-query steps (and, for GQA, every query head of the group).
-//   3. finalize (this file): dQ = acc * alpha (FP32) or acc * 2^-9 (FP16), flags.
+//   1. prep (quantize.hip with `o` set): G -> ROW and SEQ views, D = sum_c G_row~ O.
+//   2. dK/dV: one workgroup per (sequence or document, KV head, 128-key block); wave w owns
+//      keys [32w, 32w + 32) and keeps their dK, dV in registers while the workgroup streams
+//      64-query steps (of every query head of a GQA group) through LDS.
+//   3. dQ: one workgroup per (sequence or document, query head, 128-query block); wave w owns
+//      queries [32w, 32w + 32) and keeps their dQ in registers while the workgroup streams
+//      64-key tiles through LDS, rebuilding S, E, P and dS for its own queries.
+// dQ is not reduced with atomics: gfx950's L2 performs about one atomic dword per clock per
+// channel (~1.4 TB/s over the chip, FP16 pairs included), while one 64 x 128 dQ partial per
+// 64 x 128 (query x key) step of a single-pass backward moves ~4.4 GB at B4 H32 L4096 d128.
+// Rebuilding S and E in pass 3 costs two extra MFMA products per (query, key) pair and no
+// memory beyond O(L); both passes produce identical dS blocks (same 32 x 32 block grid, same
+// products, same rounding).
 //
-// gfx950 mapping. S = Q K^T and E = G V^T use V_MFMA_SCALE_F32_32X32X64_F8F6F4 with queries
-// as rows and the wave's 32 keys as columns, so a lane holds 16 queries of ONE key per
-// 32-query tile and the other 16 sit in lane ^ 32. That is the contraction order of the
-// same MFMA's A operand for the products that contract over queries: P_b^T G_seq (dV) and
-// dS^T Q_seq (dK) take the lane's own codes (P_b groups = 32 queries of one key, E8M0 from
-// a lane-pair max; dS blocks = 32 queries x the wave's 32 keys, E8M0 from a wave max-abs).
-// dQ = dS K_seq contracts over keys: the dS codes go to LDS once and come back transposed
-// with ds_read_b64_tr_b8 (8x8 byte transposes), so the quantisation itself never needs a
-// transposed layout.
+// gfx950 mapping (V_MFMA_SCALE_F32_32X32X64_F8F6F4; a lane's accumulator holds column l % 32
+// and rows 8(i/4) + 4h + i%4, h = l / 32; operand byte j of lane half h is contraction index
+// 16h + j%16 + 32(j/16)). The accumulator's row split equals the operand's contraction
+// split, so a tile's codes feed the next product from the lane's own registers:
+//   dK/dV pass: S = Q K^T and E = G V^T with queries as rows and the wave's keys as columns;
+//     the lane's 16 + 16 query values of its key are the A operand (rows = keys) of
+//     dV += P_b^T G_seq and dK += dS^T Q_seq, contracting over the 64 queries of the step.
+//   dQ pass: S^T = K Q^T and E^T = V G^T with keys as rows and the wave's queries as columns;
+//     the lane's 16 + 16 key values of its query are the B operand of dQ^T += K_seq^T dS^T,
+//     contracting over the 64 keys of the tile.
+// The SEQ views store each 32-token group in that contraction order (mx_layout.h seq_pos).
+// E8M0 group exponents are exact functions of the group max-abs bits; codes come from
+// v_cvt_scalef32_pk_fp8_f32 (x / 2^e, RNE). Group maxima use DPP and lane permutes, no LDS.
 #include "mx_device.h"
 #include "mx_internal.h"
 #include "mx_layout.h"
@@ -34,439 +46,323 @@ namespace mx {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kBlockN = 32 * kWaves;  // keys per workgroup
-constexpr int kStepM = 64;            // queries per step
+constexpr int kBlockK = 32 * kWaves;   // keys per dK/dV workgroup
+constexpr int kStepQ = 64;             // queries per dK/dV step
+constexpr int kBlockQ = 32 * kWaves;   // queries per dQ workgroup
+constexpr int kStepK = 64;             // keys per dQ step
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kBoost = 512.f;       // 2^9 (FP16 dQ mode)
+constexpr float kBoost = 512.f;        // 2^9 (FP16 dQ partial sums)
 
+__device__ __forceinline__ float max_abs16(const float* x) {
+  float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fabsf(x[2]));
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) m = fmaxf(fmaxf(m, fabsf(x[i])), fabsf(x[i + 1]));
+  return fmaxf(m, fabsf(x[15]));
+}
+
+// ROW scale word of one token: its d/32 E8M0 bytes (group 0 in the low byte). `base` points at
+// the scales of a token of the same head and `rel_elems` is the element distance to this one.
 template <int D>
-struct BwdSmem {
-  alignas(16) uint8_t qr[2][kStepM * D];       // Q ROW codes, 16-byte chunks XOR-swizzled by row
-  alignas(16) uint8_t gr[2][kStepM * D];       // G ROW codes
-  alignas(16) uint8_t qs[2][2 * D * 32];       // Q SEQ codes [group][channel][32]
-  alignas(16) uint8_t gs[2][2 * D * 32];       // G SEQ codes
-  alignas(16) uint8_t qrs[2][kStepM * (D / 32)];
-  alignas(16) uint8_t grs[2][kStepM * (D / 32)];
-  alignas(16) uint8_t qss[2][2 * D];
-  alignas(16) uint8_t gss[2][2 * D];
-  alignas(16) float lse2[2][kStepM];           // LSE * log2 e (+inf for rows past the end)
-  alignas(16) float dlt[2][kStepM];            // D
-  alignas(16) uint8_t ds[2][kBlockN * 32];     // dS codes [query tile][key][32 query positions]
-  alignas(16) int dse[2][kWaves];              // dS block scale bytes [query tile][wave]
+__device__ __forceinline__ uint32_t load_row_scales(const uint8_t* base, uint32_t rel_elems) {
+  const uint8_t* src = base + (rel_elems >> 5);
+  return D == 128 ? *reinterpret_cast<const uint32_t*>(src) : (uint32_t)*reinterpret_cast<const uint16_t*>(src);
+}
+
+// Wave index as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+__device__ __forceinline__ long long token_index(const Geom& g, int heads, int s, int doc_start, int h, int t) {
+  return packed(g) ? ((long long)(doc_start + t) * heads + h) : (((long long)s * heads + h) * g.seqlen + t);
+}
+
+// LDS-DMA of a 64-row ROW-view tile ([row][d] codes, row_swz chunks) and of a two-group
+// SEQ-view tile ([group][channel][32], half_swz halves). One DMA instruction moves 64 x 16
+// bytes. With NCH = d/16 chunks per row, instruction j covers rows j*64/NCH + lane/NCH, and
+// the swizzled chunk of a lane does not depend on j (64/NCH is a multiple of NCH); likewise
+// in a SEQ tile the half of a lane does not depend on the instruction. So each lane keeps
+// one 32-bit offset per tile kind and the rest is a wave-uniform base.
+template <int D>
+__device__ __forceinline__ int row_tile_lane_off(int lane) {
+  constexpr int NCH = D / 16;
+  const int lr = lane / NCH;
+  return row_swz(lr, lane % NCH, NCH) * 16;
+}
+__device__ __forceinline__ int seq_tile_lane_off(int lane) {
+  return (lane >> 1) * 32 + (half_swz(lane >> 1, lane & 1) << 4);
+}
+
+// rows r0.. of a ROW tile; rows past `rmax` (relative to r0) are clamped to it.
+template <int D>
+__device__ __forceinline__ void dma_row_tile(const uint8_t* base, long long tstride, int rmax, int lane, int loff,
+                                             uint8_t* lds) {
+  constexpr int NCH = D / 16;
+#pragma unroll
+  for (int j = 0; j < 64 * NCH / 64; j++) {
+    const int r = min(j * (64 / NCH) + lane / NCH, rmax);
+    lds_dma(base + (uint32_t)(r * tstride + loff), lds + j * 1024, 16);
+  }
+}
+
+// groups g0, g0+1 of a SEQ view (rows row0, row1 of the [rows][D][32] layout); instructions
+// [jbeg, 4D/64) with stride jstep.
+template <int D>
+__device__ __forceinline__ void dma_seq_tile(const uint8_t* codes, long long row0, long long row1, int loff,
+                                             uint8_t* lds, int jbeg, int jstep) {
+  constexpr int PER = D / 32;             // instructions per group
+#pragma unroll
+  for (int j = 0; j < 2 * PER; j++) {
+    if (j % jstep != jbeg) continue;
+    const uint8_t* gbase = codes + (j < PER ? row0 : row1) * (D * 32) + (j % PER) * 1024;
+    lds_dma(gbase + (uint32_t)loff, lds + j * 1024, 16);
+  }
+}
+
+// ============================== dK / dV pass ==============================
+
+// One 64-query step in LDS. Code tiles are written by LDS-DMA; the small items by ordinary
+// loads (issued with the DMA, stored before the barrier that publishes the step).
+template <int D>
+struct DkvStage {
+  alignas(16) uint8_t qr[kStepQ * D];   // Q ROW codes [query][d], row_swz chunks
+  alignas(16) uint8_t gr[kStepQ * D];   // G ROW codes
+  alignas(16) uint8_t qs[2 * D * 32];   // Q SEQ codes [group][channel][32], half_swz halves
+  alignas(16) uint8_t gs[2 * D * 32];   // G SEQ codes
+  alignas(16) uint32_t qrs[kStepQ];     // Q ROW scale word per query
+  alignas(16) uint32_t grs[kStepQ];     // G ROW scale word per query
+  alignas(16) uint8_t qss[2 * D];       // Q SEQ scales [group][channel]
+  alignas(16) uint8_t gss[2 * D];       // G SEQ scales
+  alignas(16) float lse2[kStepQ];       // LSE * log2 e (+inf past the end)
+  alignas(16) float dlt[kStepQ];        // D (0 past the end)
 };
 
-__device__ __forceinline__ int r_swz(int row, int chunk, int nchunk) { return chunk ^ (row & (nchunk - 1) & 7); }
-__device__ __forceinline__ int h_swz(int c, int half) { return half ^ ((c >> 2) & 1); }
-// token offset (0..31) held at byte position o of a SEQ group: inverse of seq_pos
-__device__ __forceinline__ int seq_tok(int o) { return 8 * ((o & 15) >> 2) + 4 * (o >> 4) + (o & 3); }
-__device__ __forceinline__ v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
-
-struct BWork {
-  int s, doc_start, n, hkv, kt;
+struct KvWork {
+  int s, doc_start, n, hkv, kb;
   bool valid;
 };
 
-__device__ __forceinline__ BWork decode_bwork(const BwdParams& p) {
+__device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
   const Geom& g = p.geom;
-  BWork w;
+  KvWork w;
   w.valid = true;
   if (!packed(g)) {
-    const int nkt = (g.seqlen + kBlockN - 1) / kBlockN;
-    const long long total = (long long)nkt * p.heads_kv * g.batch;
+    const int nkb = (g.seqlen + kBlockK - 1) / kBlockK;
+    const long long total = (long long)nkb * p.heads_kv * g.batch;
     long long bid = blockIdx.x;
+    // a contiguous range of work items per XCD (workgroups go round-robin over the 8 XCDs),
+    // so the key blocks of a head share one L2; causal: small kb = most queries, first
     if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int bh = (int)(bid / nkt);
-    w.kt = (int)(bid % nkt);   // causal: small kt = most queries, dispatched first
+    const int bh = (int)(bid / nkb);
+    w.kb = (int)(bid % nkb);
     w.s = bh / p.heads_kv;
     w.hkv = bh % p.heads_kv;
     w.doc_start = 0;
     w.n = g.seqlen;
   } else {
-    w.kt = blockIdx.x;
+    w.kb = blockIdx.x;
     w.hkv = blockIdx.y;
     w.s = blockIdx.z;
     w.doc_start = g.cu[w.s];
     w.n = g.cu[w.s + 1] - w.doc_start;
-    w.valid = w.kt * kBlockN < w.n;
+    w.valid = w.kb * kBlockK < w.n;
   }
   return w;
 }
 
+// Issue the loads of the step (query head hq, queries q0..q0+63) into stage `st`; `sv` gets
+// this thread's small items. Rows past the end are clamped to the last row (finite codes;
+// their LSE is +inf, so their P and U are 0).
 template <int D>
-struct StepRegs {
-  v4i qr[D / 64], gr[D / 64], qs[D / 64], gs[D / 64];
-  uint32_t sc;   // one scale word (which one depends on the thread)
-  float f;       // lse2 or D
-};
-
-// Global -> registers for the 64-query step starting at q0 of query head hq.
-template <int D>
-__device__ __forceinline__ void load_step(const BwdParams& p, const BWork& w, int hq, int q0, StepRegs<D>& r) {
+__device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
+                                          uint32_t (&sv)[2], int roff, int soff) {
   const Geom& g = p.geom;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
   const long long sbase = packed(g) ? (long long)w.doc_start : (long long)w.s;
-  constexpr int NCH = D / 16;
-  const int ngroups = (w.n + 31) >> 5;
-#pragma unroll
-  for (int i = 0; i < D / 64; i++) {
-    const int ch = tid + i * 256;
-    const int row = ch / NCH, cc = ch % NCH;
-    const int q = q0 + row;
-    if (q < w.n) {
-      const long long off = elem_offset(g, p.heads_q, D, sbase, hq, q, cc * 16);
-      r.qr[i] = *reinterpret_cast<const v4i*>(p.q_codes + off);
-      r.gr[i] = *reinterpret_cast<const v4i*>(p.gr_codes + off);
-    } else {
-      r.qr[i] = v4i{0, 0, 0, 0};
-      r.gr[i] = v4i{0, 0, 0, 0};
-    }
-    const int gi = (q0 >> 5) + ch / (2 * D);
-    if (gi < ngroups) {
-      const long long row0 = seq_group_row(g, p.heads_q, w.s, hq, w.doc_start, gi);
-      const long long off = row0 * D * 32 + (ch % (2 * D)) * 16;
-      r.qs[i] = *reinterpret_cast<const v4i*>(p.qs_codes + off);
-      r.gs[i] = *reinterpret_cast<const v4i*>(p.gs_codes + off);
-    } else {
-      r.qs[i] = v4i{0, 0, 0, 0};
-      r.gs[i] = v4i{0, 0, 0, 0};
-    }
+  const int nlast = w.n - 1;
+  const int glast = ((w.n + 31) >> 5) - 1;
+  if (wave < 2) {                                     // wave 0: Q ROW, wave 1: G ROW
+    const long long tok0 = elem_offset(g, p.heads_q, D, sbase, hq, q0, 0);
+    dma_row_tile<D>((wave == 0 ? p.q_codes : p.gr_codes) + tok0, token_stride(g, p.heads_q, D), nlast - q0, lane,
+                    roff, wave == 0 ? st.qr : st.gr);
+  } else {                                            // wave 2: Q SEQ, wave 3: G SEQ
+    const int g0 = q0 >> 5;
+    const long long row0 = seq_group_row(g, p.heads_q, w.s, hq, w.doc_start, min(g0, glast));
+    const long long row1 = seq_group_row(g, p.heads_q, w.s, hq, w.doc_start, min(g0 + 1, glast));
+    dma_seq_tile<D>(wave == 2 ? p.qs_codes : p.gs_codes, row0, row1, soff, wave == 2 ? st.qs : st.gs, 0, 1);
   }
-  // scales: [0,64) Q ROW, [64,128) G ROW, [128,128+D/2) Q SEQ, [128+D/2, 128+D) G SEQ
-  r.sc = 0;
-  if (tid < 128) {
-    const int q = q0 + (tid & 63);
-    if (q < w.n) {
-      const long long off = elem_offset(g, p.heads_q, D, sbase, hq, q, 0) >> 5;
-      const uint8_t* src = (tid < 64 ? p.q_scales : p.gr_scales) + off;
-      r.sc = (D == 128) ? *reinterpret_cast<const uint32_t*>(src) : (uint32_t)*reinterpret_cast<const uint16_t*>(src);
-    }
-  } else if (tid < 128 + D) {
-    const int word = (tid - 128) % (D / 2);
-    const bool isg = tid - 128 >= D / 2;
-    const int gi = (q0 >> 5) + (word * 4) / D;
-    if (gi < ngroups) {
-      const long long row0 = seq_group_row(g, p.heads_q, w.s, hq, w.doc_start, gi);
-      r.sc = *reinterpret_cast<const uint32_t*>((isg ? p.gs_scales : p.qs_scales) + row0 * D + (word * 4) % D);
-    }
-  }
-  // per-query scalars: threads [0,64) LSE * log2 e, [64,128) D
-  r.f = 0.f;
-  if (tid < 128) {
-    const int q = q0 + (tid & 63);
-    if (q < w.n) {
-      const long long li = packed(g) ? ((long long)(w.doc_start + q) * p.heads_q + hq)
-                                     : (((long long)w.s * p.heads_q + hq) * g.seqlen + q);
-      r.f = tid < 64 ? p.lse[li] * kLog2e : p.delta[li];
-    } else {
-      r.f = tid < 64 ? INFINITY : 0.f;
-    }
+  sv[0] = sv[1] = 0;
+  if (wave < 2) {                                     // ROW scale word + LSE (wave 0) / D (wave 1)
+    const int q = min(q0 + lane, nlast);
+    const long long tok = elem_offset(g, p.heads_q, D, sbase, hq, q0, 0);
+    const uint32_t rel = (uint32_t)((q - q0) * token_stride(g, p.heads_q, D));
+    sv[0] = load_row_scales<D>((wave == 0 ? p.q_scales : p.gr_scales) + (tok >> 5), rel);
+    const float* f = (wave == 0 ? p.lse : p.delta) + token_index(g, p.heads_q, w.s, w.doc_start, hq, q0);
+    const float x = f[(uint32_t)((q - q0) * (packed(g) ? p.heads_q : 1))];
+    const bool live = q0 + lane < w.n;
+    sv[1] = __float_as_uint(wave == 0 ? (live ? x * kLog2e : INFINITY) : (live ? x : 0.f));
+  } else if (lane < D / 2) {                          // SEQ scales (wave 2: Q, wave 3: G), a dword per lane
+    const int gi = min((q0 >> 5) + (lane * 4) / D, glast);
+    const long long row = seq_group_row(g, p.heads_q, w.s, hq, w.doc_start, gi);
+    sv[0] = *reinterpret_cast<const uint32_t*>((wave == 2 ? p.qs_scales : p.gs_scales) + row * D + (lane * 4) % D);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void store_step(BwdSmem<D>& sm, int buf, const StepRegs<D>& r) {
-  const int tid = threadIdx.x;
-  constexpr int NCH = D / 16;
-#pragma unroll
-  for (int i = 0; i < D / 64; i++) {
-    const int ch = tid + i * 256;
-    const int row = ch / NCH, cc = ch % NCH;
-    const int ro = row * D + (r_swz(row, cc, NCH) << 4);
-    *reinterpret_cast<v4i*>(&sm.qr[buf][ro]) = r.qr[i];
-    *reinterpret_cast<v4i*>(&sm.gr[buf][ro]) = r.gr[i];
-    const int grp = ch / (2 * D);
-    const int c = (ch / 2) % D;
-    const int so = (grp * D + c) * 32 + (h_swz(c, ch & 1) << 4);
-    *reinterpret_cast<v4i*>(&sm.qs[buf][so]) = r.qs[i];
-    *reinterpret_cast<v4i*>(&sm.gs[buf][so]) = r.gs[i];
-  }
-  if (tid < 128) {
-    uint8_t* dst = (tid < 64 ? sm.qrs[buf] : sm.grs[buf]) + (tid & 63) * (D / 32);
-    if (D == 128) *reinterpret_cast<uint32_t*>(dst) = r.sc;
-    else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)r.sc;
-    if (tid < 64) sm.lse2[buf][tid] = r.f;
-    else sm.dlt[buf][tid - 64] = r.f;
-  } else if (tid < 128 + D) {
-    const int word = (tid - 128) % (D / 2);
-    const bool isg = tid - 128 >= D / 2;
-    *reinterpret_cast<uint32_t*>((isg ? sm.gss[buf] : sm.qss[buf]) + word * 4) = r.sc;
+__device__ __forceinline__ void dkv_put(DkvStage<D>& st, const uint32_t (&sv)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  if (wave < 2) {
+    (wave == 0 ? st.qrs : st.grs)[lane] = sv[0];
+    (wave == 0 ? st.lse2 : st.dlt)[lane] = __uint_as_float(sv[1]);
+  } else if (lane < D / 2) {
+    reinterpret_cast<uint32_t*>(wave == 2 ? st.qss : st.gss)[lane] = sv[0];
   }
 }
 
-// Max of |x| over the whole wave (for the 32x32 dS block scale).
-__device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 1));
-  x = fmaxf(x, __shfl_xor(x, 2));
-  x = fmaxf(x, __shfl_xor(x, 4));
-  x = fmaxf(x, __shfl_xor(x, 8));
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, swap32(x));
-}
-
+// d = 128 needs ~400 registers per lane (dK and dV accumulators alone take 128): one wave per
+// SIMD, accumulators in AGPRs. d = 64 fits two workgroups per CU.
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdParams p) {
-  __shared__ BwdSmem<D> sm;
-  const BWork w = decode_bwork(p);
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(BwdParams p) {
+  __shared__ DkvStage<D> sm[2];
+  const KvWork w = decode_kv(p);
   if (!w.valid) return;
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int hh = lane >> 5;
   const int l32 = lane & 31;
   const long long sbase = packed(g) ? (long long)w.doc_start : (long long)w.s;
-  const int k0 = w.kt * kBlockN;          // first key of the workgroup
+  const int k0 = w.kb * kBlockK;
   const int kw = k0 + wave * 32;          // first key of this wave
-  const int key = kw + l32;               // this lane's key (S / E column)
+  const int key = kw + l32;               // this lane's key (column of S and E)
   const bool kvalid = key < w.n;
   const float c = p.scale * kLog2e;
   constexpr int NS = D / 64;              // contraction steps over d
   constexpr int NCT = D / 32;             // 32-channel tiles
-  const int ngroups = (w.n + 31) >> 5;
 
-  // ---- per-wave key operands (B of S and E), kept in registers ----
+  const int group = p.heads_q / p.heads_kv;
+  const int qfirst = p.causal ? (k0 / kStepQ) * kStepQ : 0;
+  const int nsteps_h = (w.n - qfirst + kStepQ - 1) / kStepQ;
+  const int nsteps = nsteps_h * group;
+  const int roff = row_tile_lane_off<D>(lane), soff = seq_tile_lane_off(lane);
+  uint32_t sv[2];
+  dkv_issue<D>(p, w, w.hkv * group, qfirst, sm[0], sv, roff, soff);
+
+  // K and V of the lane's key: B operands of S and E, kept in registers
+  // kvsc: byte s = K scale of contraction step s, byte 2 + s = V scale (groups 2s + hh)
   v8i kop[NS], vop[NS];
-  int ksc[NS], vsc[NS];
+  uint32_t kvsc = 0;
 #pragma unroll
   for (int s = 0; s < NS; s++) {
-    if (kvalid) {
-      const long long off = elem_offset(g, p.heads_kv, D, sbase, w.hkv, key, 64 * s);
-      kop[s] = cat(*reinterpret_cast<const v4i*>(p.k_codes + off + 16 * hh),
-                   *reinterpret_cast<const v4i*>(p.k_codes + off + 32 + 16 * hh));
-      vop[s] = cat(*reinterpret_cast<const v4i*>(p.vr_codes + off + 16 * hh),
-                   *reinterpret_cast<const v4i*>(p.vr_codes + off + 32 + 16 * hh));
-      ksc[s] = p.k_scales[(off >> 5) + hh];
-      vsc[s] = p.vr_scales[(off >> 5) + hh];
-    } else {
-      kop[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      vop[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      ksc[s] = 0;
-      vsc[s] = 0;
-    }
+    const long long off = elem_offset(g, p.heads_kv, D, sbase, w.hkv, min(key, w.n - 1), 64 * s);
+    kop[s] = cat(*reinterpret_cast<const v4i*>(p.k_codes + off + 16 * hh),
+                 *reinterpret_cast<const v4i*>(p.k_codes + off + 32 + 16 * hh));
+    vop[s] = cat(*reinterpret_cast<const v4i*>(p.vr_codes + off + 16 * hh),
+                 *reinterpret_cast<const v4i*>(p.vr_codes + off + 32 + 16 * hh));
+    kvsc |= ((uint32_t)p.k_scales[(off >> 5) + hh] << (8 * s)) | ((uint32_t)p.vr_scales[(off >> 5) + hh] << (16 + 8 * s));
   }
-  // ---- K SEQ operand for dQ (B: channels x keys): wave handles channel tile(s) ----
-  // D = 128: wave w -> channel tile w, both query tiles. D = 64: wave w -> channel tile w & 1,
-  // query tile w >> 1.
-  const int dq_ct = (D == 128) ? wave : (wave & 1);
-  v8i ksop[2];
-  int kssc[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ks++) {
-    const int ch = dq_ct * 32 + l32;
-    const int g0 = (k0 >> 5) + 2 * ks;
-    v4i a = v4i{0, 0, 0, 0}, b = v4i{0, 0, 0, 0};
-    int sa = 0, sb = 0;
-    if (g0 < ngroups) {
-      const long long row = seq_group_row(g, p.heads_kv, w.s, w.hkv, w.doc_start, g0);
-      a = *reinterpret_cast<const v4i*>(p.ks_codes + (row * D + ch) * 32 + 16 * hh);
-      sa = p.ks_scales[row * D + ch];
-    }
-    if (g0 + 1 < ngroups) {
-      const long long row = seq_group_row(g, p.heads_kv, w.s, w.hkv, w.doc_start, g0 + 1);
-      b = *reinterpret_cast<const v4i*>(p.ks_codes + (row * D + ch) * 32 + 16 * hh);
-      sb = p.ks_scales[row * D + ch];
-    }
-    ksop[ks] = cat(a, b);
-    kssc[ks] = hh ? sb : sa;
-  }
-
   v16f dk[NCT], dv[NCT];
 #pragma unroll
   for (int t = 0; t < NCT; t++) {
     dk[t] = v16f{};
     dv[t] = v16f{};
   }
-
-  const int group = p.heads_q / p.heads_kv;
-  const int qfirst = p.causal ? (k0 / kStepM) * kStepM : 0;
-  const int nsteps_h = (w.n - qfirst + kStepM - 1) / kStepM;
-  const int nsteps = nsteps_h * group;
-
-  StepRegs<D> sr;
-  load_step<D>(p, w, w.hkv * group, qfirst, sr);
-  store_step<D>(sm, 0, sr);
+  // lane-constant LDS byte offsets; tile, step and group displacements are immediates
+  int roff_ab[2 * NS];                    // ROW tile, row l32: chunks 4s + hh and 4s + 2 + hh
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    roff_ab[2 * s] = l32 * D + (row_swz(l32, 4 * s + hh, D / 16) << 4);
+    roff_ab[2 * s + 1] = l32 * D + (row_swz(l32, 4 * s + 2 + hh, D / 16) << 4);
+  }
+  const int soff_c = l32 * 32 + (half_swz(l32, hh) << 4);   // SEQ tile, channel l32 of group 0
+  const int scoff = hh * D + l32;                            // SEQ scale of channel l32, group hh
+  const int fidx = 4 * hh;                                   // LSE / D index of the lane's rows
+  dkv_put<D>(sm[0], sv);
+  wait_vmem();
   __syncthreads();
 
   for (int st = 0; st < nsteps; st++) {
     const int buf = st & 1;
-    const int hq = w.hkv * group + st / nsteps_h;
-    const int q0 = qfirst + (st % nsteps_h) * kStepM;
+    const int q0 = qfirst + (st % nsteps_h) * kStepQ;
     if (st + 1 < nsteps) {
-      const int st2 = st + 1;
-      load_step<D>(p, w, w.hkv * group + st2 / nsteps_h, qfirst + (st2 % nsteps_h) * kStepM, sr);
+      const int s2 = st + 1;
+      dkv_issue<D>(p, w, w.hkv * group + s2 / nsteps_h, qfirst + (s2 % nsteps_h) * kStepQ, sm[buf ^ 1], sv, roff,
+                   soff);
     }
-    // waves whose keys are all after the step's last query (causal) see nothing
-    const bool active = !(p.causal && kw > q0 + kStepM - 1) && kw < w.n;
-    uint32_t dsw[2][4];   // dS codes of this lane, per query tile
-    int dsbyte[2] = {0, 0};
-    if (active) {
-      v16f sacc[2], eacc[2];
+    const DkvStage<D>& S = sm[buf];
+    // waves whose keys all follow the step's last query (causal) see nothing
+    if (kw < w.n && !(p.causal && kw > q0 + kStepQ - 1)) {
+      const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.n;
+      v8i pbop, dsop;
+      int pbe[2], dse[2];
 #pragma unroll
       for (int qt = 0; qt < 2; qt++) {
-        sacc[qt] = v16f{};
-        eacc[qt] = v16f{};
         const int row = qt * 32 + l32;
+        const uint32_t qsw = S.qrs[row] >> (8 * hh);
+        const uint32_t gsw = S.grs[row] >> (8 * hh);
+        v16f sacc = v16f{}, eacc = v16f{};
 #pragma unroll
         for (int s = 0; s < NS; s++) {
-          constexpr int NCH = D / 16;
-          const int o0 = row * D + (r_swz(row, 4 * s + hh, NCH) << 4);
-          const int o1 = row * D + (r_swz(row, 4 * s + 2 + hh, NCH) << 4);
-          const v8i qa = cat(*reinterpret_cast<const v4i*>(&sm.qr[buf][o0]), *reinterpret_cast<const v4i*>(&sm.qr[buf][o1]));
-          const v8i ga = cat(*reinterpret_cast<const v4i*>(&sm.gr[buf][o0]), *reinterpret_cast<const v4i*>(&sm.gr[buf][o1]));
-          const int qsc = sm.qrs[buf][row * (D / 32) + 2 * s + hh];
-          const int gsc = sm.grs[buf][row * (D / 32) + 2 * s + hh];
-          sacc[qt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kop[s], sacc[qt], 0, 0, 0, qsc, 0, ksc[s]);
-          eacc[qt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga, vop[s], eacc[qt], 0, 0, 0, gsc, 0, vsc[s]);
+          const int o0 = qt * 32 * D + roff_ab[2 * s], o1 = qt * 32 * D + roff_ab[2 * s + 1];
+          const v8i qa = cat(*reinterpret_cast<const v4i*>(&S.qr[o0]), *reinterpret_cast<const v4i*>(&S.qr[o1]));
+          const v8i ga = cat(*reinterpret_cast<const v4i*>(&S.gr[o0]), *reinterpret_cast<const v4i*>(&S.gr[o1]));
+          sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kop[s], sacc, 0, 0, 0, (int)(qsw >> (16 * s)), 0,
+                                                                 (int)(kvsc >> (8 * s)));
+          eacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga, vop[s], eacc, 0, 0, 0, (int)(gsw >> (16 * s)), 0,
+                                                                 (int)(kvsc >> (16 + 8 * s)));
         }
-      }
-      // ---- P = 2^(S' - LSE'), masked; P_b codes (32 queries of this key per group) ----
-      const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepM > w.n || !kvalid || kw + 32 > w.n;
-      float P[2][16];
-#pragma unroll
-      for (int qt = 0; qt < 2; qt++) {
+        // P = 2^(S' - LSE') for the lane's 16 queries (rows 8j + 4hh + u of the tile)
+        float P[16], U[16];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const int r0 = qt * 32 + 8 * j + 4 * hh;   // 4 consecutive queries of this lane
-          const v4f l4 = *reinterpret_cast<const v4f*>(&sm.lse2[buf][r0]);
+          const v4f l4 = *reinterpret_cast<const v4f*>(&S.lse2[qt * 32 + 8 * j + fidx]);
+          const v4f d4 = *reinterpret_cast<const v4f*>(&S.dlt[qt * 32 + 8 * j + fidx]);
 #pragma unroll
           for (int u = 0; u < 4; u++) {
-            float x = __builtin_fmaf(sacc[qt][4 * j + u], c, -l4[u]);
+            float x = __builtin_fmaf(sacc[4 * j + u], c, -l4[u]);
             if (need_mask) {
-              const int q = q0 + r0 + u;
-              const bool vis = kvalid && q < w.n && (!p.causal || key <= q);
-              if (!vis) x = -INFINITY;
+              const int q = q0 + qt * 32 + 8 * j + 4 * hh + u;
+              if (!(kvalid && q < w.n && (!p.causal || key <= q))) x = -INFINITY;
             }
-            P[qt][4 * j + u] = __builtin_amdgcn_exp2f(x);
+            P[4 * j + u] = __builtin_amdgcn_exp2f(x);
+            U[4 * j + u] = P[4 * j + u] * (eacc[4 * j + u] - d4[u]);
           }
         }
-      }
-      v8i pbop;
-      int pbe[2];
+        // P_b: 32 queries of this key per group (this lane and lane ^ 32)
+        float pm = max_abs16(P);
+        pm = fmaxf(pm, swap32(pm));
+        pbe[qt] = scale_exp_from_bits(__float_as_uint(pm));
+        const float psc = exp2_scale(pbe[qt]);
+        // dS: the 32 x 32 block (this wave's keys x the tile's queries)
+        const float um = wave_max(max_abs16(U));
+        dse[qt] = scale_exp_from_bits(__float_as_uint(um));
+        const float usc = exp2_scale(dse[qt]);
 #pragma unroll
-      for (int qt = 0; qt < 2; qt++) {
-        float am = P[qt][0];
-#pragma unroll
-        for (int i = 1; i < 16; i++) am = fmaxf(am, P[qt][i]);
-        am = fmaxf(am, swap32(am));
-        const int e = scale_exp_from_bits(__float_as_uint(am));
-        pbe[qt] = e;
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-          pbop[4 * qt + j] = (int)pack4_e4m3(ldexpf(P[qt][4 * j], -e), ldexpf(P[qt][4 * j + 1], -e),
-                                             ldexpf(P[qt][4 * j + 2], -e), ldexpf(P[qt][4 * j + 3], -e));
+        for (int j = 0; j < 4; j++) {
+          pbop[4 * qt + j] = (int)pack4_e4m3_scaled(P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3], psc);
+          dsop[4 * qt + j] = (int)pack4_e4m3_scaled(U[4 * j], U[4 * j + 1], U[4 * j + 2], U[4 * j + 3], usc);
+        }
       }
       const int pbsc = (hh ? pbe[1] : pbe[0]) + 127;
-      // ---- dV += P_b^T G_seq ----
+      const int dssc = (hh ? dse[1] : dse[0]) + 127;
+      // dV += P_b^T G_seq, dK += dS^T Q_seq (rows = the wave's keys, columns = channels)
 #pragma unroll
       for (int t = 0; t < NCT; t++) {
-        const int ch = t * 32 + l32;
-        const v8i gb = cat(*reinterpret_cast<const v4i*>(&sm.gs[buf][(0 * D + ch) * 32 + (h_swz(ch, hh) << 4)]),
-                           *reinterpret_cast<const v4i*>(&sm.gs[buf][(1 * D + ch) * 32 + (h_swz(ch, hh) << 4)]));
-        const int gsc = sm.gss[buf][hh * D + ch];
-        dv[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pbop, gb, dv[t], 0, 0, 0, pbsc, 0, gsc);
-      }
-      // ---- U = P (E - D); 32x32 block scale from a wave max-abs; dS codes ----
-      v8i dsop;
-#pragma unroll
-      for (int qt = 0; qt < 2; qt++) {
-        float U[16];
-        float am = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const v4f d4 = *reinterpret_cast<const v4f*>(&sm.dlt[buf][qt * 32 + 8 * j + 4 * hh]);
-#pragma unroll
-          for (int u = 0; u < 4; u++) {
-            U[4 * j + u] = P[qt][4 * j + u] * (eacc[qt][4 * j + u] - d4[u]);
-            am = fmaxf(am, fabsf(U[4 * j + u]));
-          }
-        }
-        am = wave_max(am);
-        const int e = scale_exp_from_bits(__float_as_uint(am));
-        dsbyte[qt] = e + 127;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          dsw[qt][j] = pack4_e4m3(ldexpf(U[4 * j], -e), ldexpf(U[4 * j + 1], -e), ldexpf(U[4 * j + 2], -e),
-                                  ldexpf(U[4 * j + 3], -e));
-          dsop[4 * qt + j] = (int)dsw[qt][j];
-        }
-      }
-      const int dssc = hh ? dsbyte[1] : dsbyte[0];
-      // ---- dK += dS^T Q_seq ----
-#pragma unroll
-      for (int t = 0; t < NCT; t++) {
-        const int ch = t * 32 + l32;
-        const v8i qb = cat(*reinterpret_cast<const v4i*>(&sm.qs[buf][(0 * D + ch) * 32 + (h_swz(ch, hh) << 4)]),
-                           *reinterpret_cast<const v4i*>(&sm.qs[buf][(1 * D + ch) * 32 + (h_swz(ch, hh) << 4)]));
-        const int qsc = sm.qss[buf][hh * D + ch];
-        dk[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsop, qb, dk[t], 0, 0, 0, dssc, 0, qsc);
-      }
-    } else {
-#pragma unroll
-      for (int qt = 0; qt < 2; qt++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) dsw[qt][j] = 0;
-      dsbyte[0] = dsbyte[1] = 0;
-    }
-    // ---- dS codes to LDS: row = key of the workgroup, 32 query positions per tile ----
-#pragma unroll
-    for (int qt = 0; qt < 2; qt++) {
-      v4i wv = {(int)dsw[qt][0], (int)dsw[qt][1], (int)dsw[qt][2], (int)dsw[qt][3]};
-      *reinterpret_cast<v4i*>(&sm.ds[qt][(wave * 32 + l32) * 32 + 16 * hh]) = wv;
-    }
-    if (lane == 0) {
-      sm.dse[0][wave] = dsbyte[0];
-      sm.dse[1][wave] = dsbyte[1];
-    }
-    __syncthreads();
-    // ---- dQ partial = dS K_seq over the workgroup's 128 keys ----
-    {
-      const int G16 = lane >> 4;          // 16-lane group of ds_read_b64_tr_b8
-      const int li = lane & 15;
-      const int b = li >> 1, a = li & 1;  // this lane supplies row b of half a
-#pragma unroll
-      for (int qt = 0; qt < 2; qt++) {
-        if (D == 64 && qt != (wave >> 1)) continue;
-        v16f dq = v16f{};
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) {
-          v8i aop;
-#pragma unroll
-          for (int rho = 0; rho < 4; rho++) {
-            const int kb = rho >> 1;
-            const int krow = 32 * (2 * ks + kb) + seq_tok(16 * (G16 >> 1) + 8 * (rho & 1) + b);
-            const int col = 16 * (G16 & 1) + 8 * a;
-            const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) v2i*)((__attribute__((address_space(3))) uint8_t*)&sm.ds[qt][krow * 32 + col]));
-            aop[2 * rho] = t[0];
-            aop[2 * rho + 1] = t[1];
-          }
-          const int asc = sm.dse[qt][2 * ks + hh];
-          dq = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, ksop[ks], dq, 0, 0, 0, asc, 0, kssc[ks]);
-        }
-        // atomics: M row r = 8(i/4) + 4hh + i%4 holds query seq_tok(r) of the tile
-        const int ch = dq_ct * 32 + l32;
-        const float mul = p.dq_mode == 1 ? p.scale * kBoost : 1.f;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int r = 8 * (i >> 2) + 4 * hh + (i & 3);
-          const int q = q0 + qt * 32 + seq_tok(r);
-          if (q < w.n) {
-            const long long off = elem_offset(g, p.heads_q, D, sbase, hq, q, ch);
-            if (p.dq_mode == 1) {
-              __hip_atomic_fetch_add(static_cast<_Float16*>(p.dq_acc) + off, (_Float16)(dq[i] * mul),
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-              __hip_atomic_fetch_add(static_cast<float*>(p.dq_acc) + off, dq[i], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-            }
-          }
-        }
+        const int h0 = t * 1024 + soff_c, h1 = D * 32 + t * 1024 + soff_c;   // channel t*32 + l32, groups 0 / 1
+        const v8i gb = cat(*reinterpret_cast<const v4i*>(&S.gs[h0]), *reinterpret_cast<const v4i*>(&S.gs[h1]));
+        const v8i qb = cat(*reinterpret_cast<const v4i*>(&S.qs[h0]), *reinterpret_cast<const v4i*>(&S.qs[h1]));
+        dv[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pbop, gb, dv[t], 0, 0, 0, pbsc, 0, S.gss[scoff + t * 32]);
+        dk[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsop, qb, dk[t], 0, 0, 0, dssc, 0, S.qss[scoff + t * 32]);
       }
     }
-    if (st + 1 < nsteps) store_step<D>(sm, buf ^ 1, sr);
-    __syncthreads();
+    if (st + 1 < nsteps) {
+      dkv_put<D>(sm[buf ^ 1], sv);
+      wait_vmem();
+      __syncthreads();
+    }
   }
 
-  // ---- epilogue: dK = alpha * acc, dV = acc; C rows = keys, columns = channels ----
+  // ---- epilogue: dK = alpha * acc, dV = acc; accumulator rows = keys, columns = channels ----
 #pragma unroll
   for (int t = 0; t < NCT; t++) {
     const int ch = t * 32 + l32;
@@ -488,38 +384,293 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdParams p) {
   }
 }
 
-// dQ = acc * alpha (FP32 accumulation) or acc * 2^-9 (FP16, boosted); flags.
-template <bool kF16>
-__global__ __launch_bounds__(256) void dq_finalize_kernel(const void* acc, void* dq, long long n, float mul, bool out_f32,
-                                                         uint32_t* flags) {
-  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= n) return;
-  float v[4];
-  uint32_t bad = 0;
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    float a = kF16 ? (float)static_cast<const _Float16*>(acc)[i + j] : static_cast<const float*>(acc)[i + j];
-    if (__builtin_isnan(a)) bad |= 2u;
-    else if (__builtin_isinf(a)) bad |= kF16 ? 1u : 2u;
-    v[j] = a * mul;
-  }
-  if (out_f32) {
-    *reinterpret_cast<v4f*>(static_cast<float*>(dq) + i) = v4f{v[0], v[1], v[2], v[3]};
+// ================================ dQ pass =================================
+
+// One 64-key tile in LDS (code tiles by LDS-DMA, small items by ordinary loads).
+template <int D>
+struct DqStage {
+  alignas(16) uint8_t kr[kStepK * D];   // K ROW codes [key][d], row_swz chunks
+  alignas(16) uint8_t vr[kStepK * D];   // V ROW codes
+  alignas(16) uint8_t ks[2 * D * 32];   // K SEQ codes [group][channel][32], half_swz halves
+  alignas(16) uint32_t krs[kStepK];     // K ROW scale word per key
+  alignas(16) uint32_t vrs[kStepK];     // V ROW scale word per key
+  alignas(16) uint8_t kss[2 * D];       // K SEQ scales [group][channel]
+};
+
+struct QWork {
+  int s, doc_start, n, h, qb;
+  bool valid;
+};
+
+__device__ __forceinline__ QWork decode_q(const BwdParams& p) {
+  const Geom& g = p.geom;
+  QWork w;
+  w.valid = true;
+  if (!packed(g)) {
+    const int nqb = (g.seqlen + kBlockQ - 1) / kBlockQ;
+    const long long total = (long long)nqb * p.heads_q * g.batch;
+    long long bid = blockIdx.x;
+    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int bh = (int)(bid / nqb);
+    int qb = (int)(bid % nqb);
+    if (p.causal) qb = nqb - 1 - qb;     // most keys first
+    w.s = bh / p.heads_q;
+    w.h = bh % p.heads_q;
+    w.qb = qb;
+    w.doc_start = 0;
+    w.n = g.seqlen;
   } else {
-    const uint32_t w0 = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
-    const uint32_t w1 = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
-    *reinterpret_cast<v2i*>(static_cast<uint16_t*>(dq) + i) = v2i{(int)w0, (int)w1};
+    w.qb = blockIdx.x;
+    w.h = blockIdx.y;
+    w.s = blockIdx.z;
+    w.doc_start = g.cu[w.s];
+    w.n = g.cu[w.s + 1] - w.doc_start;
+    if (p.causal) w.qb = (w.n + kBlockQ - 1) / kBlockQ - 1 - w.qb;
+    w.valid = w.qb >= 0 && w.qb * kBlockQ < w.n;
   }
-  if (bad) __hip_atomic_fetch_or(flags, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return w;
+}
+
+// Issue the loads of key tile kt (keys 64kt..64kt+63 of KV head hkv) into stage `st`.
+template <int D>
+__device__ __forceinline__ void dq_issue(const BwdParams& p, const QWork& w, int hkv, int kt, DqStage<D>& st,
+                                         uint32_t& sv, int roff, int soff) {
+  const Geom& g = p.geom;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const long long sbase = packed(g) ? (long long)w.doc_start : (long long)w.s;
+  const int nlast = w.n - 1;
+  const int glast = ((w.n + 31) >> 5) - 1;
+  const int k0 = kt * kStepK;
+  if (wave < 2) {                                     // wave 0: K ROW, wave 1: V ROW
+    const long long tok0 = elem_offset(g, p.heads_kv, D, sbase, hkv, k0, 0);
+    dma_row_tile<D>((wave == 0 ? p.k_codes : p.vr_codes) + tok0, token_stride(g, p.heads_kv, D), nlast - k0, lane,
+                    roff, wave == 0 ? st.kr : st.vr);
+  } else {                                            // waves 2-3: K SEQ, alternate instructions
+    const int g0 = k0 >> 5;
+    const long long row0 = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, min(g0, glast));
+    const long long row1 = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, min(g0 + 1, glast));
+    dma_seq_tile<D>(p.ks_codes, row0, row1, soff, st.ks, wave - 2, 2);
+  }
+  sv = 0;
+  if (wave < 2) {                                     // ROW scale words (wave 0: K, wave 1: V)
+    const int k = min(k0 + lane, nlast);
+    const long long tok = elem_offset(g, p.heads_kv, D, sbase, hkv, k0, 0);
+    const uint32_t rel = (uint32_t)((k - k0) * token_stride(g, p.heads_kv, D));
+    sv = load_row_scales<D>((wave == 0 ? p.k_scales : p.vr_scales) + (tok >> 5), rel);
+  } else if (wave == 2 && lane < D / 2) {             // K SEQ scales, a dword per lane
+    const int gi = min((k0 >> 5) + (lane * 4) / D, glast);
+    const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
+    sv = *reinterpret_cast<const uint32_t*>(p.ks_scales + row * D + (lane * 4) % D);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dq_put(DqStage<D>& st, uint32_t sv) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  if (wave < 2) (wave == 0 ? st.krs : st.vrs)[lane] = sv;
+  else if (wave == 2 && lane < D / 2) reinterpret_cast<uint32_t*>(st.kss)[lane] = sv;
+}
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// kF16: dQ partial sums of 128 keys (two tiles) are multiplied by alpha 2^9, rounded to FP16
+// and summed in FP16; the result is scaled by 2^-9.
+template <int D, bool kF16>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
+  __shared__ DqStage<D> sm[2];
+  const QWork w = decode_q(p);
+  if (!w.valid) return;
+  const Geom& g = p.geom;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  const int hkv = w.h / (p.heads_q / p.heads_kv);
+  const long long sbase = packed(g) ? (long long)w.doc_start : (long long)w.s;
+  const int q0 = w.qb * kBlockQ;
+  const int qw = q0 + wave * 32;          // first query of this wave
+  const int qi = qw + l32;                // this lane's query (column of S^T and E^T)
+  const bool qvalid = qi < w.n;
+  const float c = p.scale * kLog2e;
+  constexpr int NS = D / 64;
+  constexpr int NCT = D / 32;
+  const int kend = p.causal ? min(w.n, q0 + kBlockQ) : w.n;
+  const int nkt = (kend + kStepK - 1) / kStepK;
+
+  const int roff = row_tile_lane_off<D>(lane), soff = seq_tile_lane_off(lane);
+  uint32_t sv;
+  dq_issue<D>(p, w, hkv, 0, sm[0], sv, roff, soff);
+
+  // Q and G of the lane's query: B operands of S^T and E^T, kept in registers
+  v8i qop[NS], gop[NS];
+  int qsc[NS], gsc[NS];
+  const int qc = min(qi, w.n - 1);
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    const long long off = elem_offset(g, p.heads_q, D, sbase, w.h, qc, 64 * s);
+    qop[s] = cat(*reinterpret_cast<const v4i*>(p.q_codes + off + 16 * hh),
+                 *reinterpret_cast<const v4i*>(p.q_codes + off + 32 + 16 * hh));
+    gop[s] = cat(*reinterpret_cast<const v4i*>(p.gr_codes + off + 16 * hh),
+                 *reinterpret_cast<const v4i*>(p.gr_codes + off + 32 + 16 * hh));
+    qsc[s] = p.q_scales[(off >> 5) + hh];
+    gsc[s] = p.gr_scales[(off >> 5) + hh];
+  }
+  const long long li = token_index(g, p.heads_q, w.s, w.doc_start, w.h, qc);
+  const float lse2 = qvalid ? p.lse[li] * kLog2e : INFINITY;
+  const float dl = qvalid ? p.delta[li] : 0.f;
+
+  v16f dq[NCT];
+  h2 acc16[NCT][8];
+#pragma unroll
+  for (int t = 0; t < NCT; t++) {
+    dq[t] = v16f{};
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc16[t][i] = h2{(_Float16)0.f, (_Float16)0.f};
+  }
+  const float fmul = p.scale * kBoost;
+  auto fold = [&]() {
+#pragma unroll
+    for (int t = 0; t < NCT; t++) {
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        acc16[t][i] += h2{(_Float16)(dq[t][2 * i] * fmul), (_Float16)(dq[t][2 * i + 1] * fmul)};
+      dq[t] = v16f{};
+    }
+  };
+  int roff_ab[2 * NS];                    // ROW tile, row l32: chunks 4s + hh and 4s + 2 + hh
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    roff_ab[2 * s] = l32 * D + (row_swz(l32, 4 * s + hh, D / 16) << 4);
+    roff_ab[2 * s + 1] = l32 * D + (row_swz(l32, 4 * s + 2 + hh, D / 16) << 4);
+  }
+  const int soff_c = l32 * 32 + (half_swz(l32, hh) << 4);   // SEQ tile, channel l32 of group 0
+  const int scoff = hh * D + l32;                            // SEQ scale of channel l32, group hh
+  dq_put<D>(sm[0], sv);
+  wait_vmem();
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; kt++) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) dq_issue<D>(p, w, hkv, kt + 1, sm[buf ^ 1], sv, roff, soff);
+    const DqStage<D>& S = sm[buf];
+    const int kbase = kt * kStepK;
+    if (qw < w.n && !(p.causal && kbase > qw + 31)) {
+      const bool need_mask = (p.causal && kbase + kStepK - 1 > qw) || kbase + kStepK > w.n || qw + 32 > w.n;
+      v8i dsop;
+      int dse[2];
+#pragma unroll
+      for (int T = 0; T < 2; T++) {
+        const int row = T * 32 + l32;
+        const uint32_t ksw = S.krs[row] >> (8 * hh);
+        const uint32_t vsw = S.vrs[row] >> (8 * hh);
+        v16f sacc = v16f{}, eacc = v16f{};
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+          const int o0 = T * 32 * D + roff_ab[2 * s], o1 = T * 32 * D + roff_ab[2 * s + 1];
+          const v8i ka = cat(*reinterpret_cast<const v4i*>(&S.kr[o0]), *reinterpret_cast<const v4i*>(&S.kr[o1]));
+          const v8i va = cat(*reinterpret_cast<const v4i*>(&S.vr[o0]), *reinterpret_cast<const v4i*>(&S.vr[o1]));
+          sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qop[s], sacc, 0, 0, 0, (int)(ksw >> (16 * s)), 0,
+                                                                 qsc[s]);
+          eacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, gop[s], eacc, 0, 0, 0, (int)(vsw >> (16 * s)), 0,
+                                                                 gsc[s]);
+        }
+        float U[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          float x = __builtin_fmaf(sacc[i], c, -lse2);
+          if (need_mask) {
+            const int k = kbase + T * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if (!(qvalid && k < w.n && (!p.causal || k <= qi))) x = -INFINITY;
+          }
+          U[i] = __builtin_amdgcn_exp2f(x) * (eacc[i] - dl);
+        }
+        const float um = wave_max(max_abs16(U));
+        dse[T] = scale_exp_from_bits(__float_as_uint(um));
+        const float usc = exp2_scale(dse[T]);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          dsop[4 * T + j] = (int)pack4_e4m3_scaled(U[4 * j], U[4 * j + 1], U[4 * j + 2], U[4 * j + 3], usc);
+      }
+      const int dssc = (hh ? dse[1] : dse[0]) + 127;
+      // dQ^T += K_seq^T dS^T (rows = channels, columns = the wave's queries)
+#pragma unroll
+      for (int t = 0; t < NCT; t++) {
+        const v8i ka = cat(*reinterpret_cast<const v4i*>(&S.ks[t * 1024 + soff_c]),
+                           *reinterpret_cast<const v4i*>(&S.ks[D * 32 + t * 1024 + soff_c]));
+        dq[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, dsop, dq[t], 0, 0, 0, S.kss[scoff + t * 32], 0, dssc);
+      }
+    }
+    if (kF16 && ((kt & 1) || kt + 1 == nkt)) fold();
+    if (kt + 1 < nkt) {
+      dq_put<D>(sm[buf ^ 1], sv);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: dQ = alpha * acc (FP32) or acc16 * 2^-9; lane writes 4 channels at a time ----
+  uint32_t bad = 0;
+  if (qvalid) {
+    const long long obase = elem_offset(g, p.heads_q, D, sbase, w.h, qi, 0);
+#pragma unroll
+    for (int t = 0; t < NCT; t++) {
+#pragma unroll
+      for (int b4 = 0; b4 < 4; b4++) {
+        const int ch = t * 32 + 8 * b4 + 4 * hh;
+        float o[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const int i = 4 * b4 + u;
+          const float a = kF16 ? (float)acc16[t][i >> 1][i & 1] : dq[t][i];
+          if (__builtin_isnan(a)) bad |= 2u;
+          else if (__builtin_isinf(a)) bad |= kF16 ? 1u : 2u;
+          o[u] = kF16 ? a * (1.f / kBoost) : a * p.scale;
+        }
+        if (p.out_f32) {
+          *reinterpret_cast<v4f*>(static_cast<float*>(p.dq) + obase + ch) = v4f{o[0], o[1], o[2], o[3]};
+        } else {
+          const uint32_t w0 = float_to_bf16_bits(o[0]) | (float_to_bf16_bits(o[1]) << 16);
+          const uint32_t w1 = float_to_bf16_bits(o[2]) | (float_to_bf16_bits(o[3]) << 16);
+          *reinterpret_cast<v2i*>(static_cast<uint16_t*>(p.dq) + obase + ch) = v2i{(int)w0, (int)w1};
+        }
+      }
+    }
+  }
+  if (bad) __hip_atomic_fetch_or(p.flags, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void clear_flags_kernel(uint32_t* flags) { *flags = 0u; }
+
+template <int D>
+hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
+  const Geom& g = p.geom;
+  dim3 gkv, gq;
+  if (!packed(g)) {
+    gkv = dim3((unsigned)((long long)((g.seqlen + kBlockK - 1) / kBlockK) * p.heads_kv * g.batch), 1, 1);
+    gq = dim3((unsigned)((long long)((g.seqlen + kBlockQ - 1) / kBlockQ) * p.heads_q * g.batch), 1, 1);
+  } else {
+    gkv = dim3((unsigned)((g.max_seqlen + kBlockK - 1) / kBlockK), (unsigned)p.heads_kv, (unsigned)g.n_docs);
+    gq = dim3((unsigned)((g.max_seqlen + kBlockQ - 1) / kBlockQ), (unsigned)p.heads_q, (unsigned)g.n_docs);
+  }
+  int slot = profile_begin(kProfBwdKV, stream);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), gkv, dim3(256), 0, stream, p);
+  profile_end(slot, stream);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  slot = profile_begin(kProfBwdQ, stream);
+  if (p.dq_mode == 1) hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), gq, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), gq, dim3(256), 0, stream, p);
+  profile_end(slot, stream);
+  return hipGetLastError();
+}
 
 }  // namespace
 
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
   const Geom& g = p.geom;
-  // 1. prep: G views, D, zeroed dQ accumulator
+  // 1. prep: G views and D
   QuantizeParams qp = {};
   qp.geom = g;
   qp.heads = p.heads_q;
@@ -533,38 +684,13 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
   qp.o = p.o;
   qp.o_f32 = p.out_f32;
   qp.delta = p.delta;
-  qp.dq_acc = p.dq_acc;
-  qp.dq_f16 = p.dq_mode == 1;
   hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(1), 0, stream, p.flags);
-  int slot = profile_begin(kProfBwdPrep, stream);
+  const int slot = profile_begin(kProfBwdPrep, stream);
   hipError_t err = launch_quantize(qp, stream);
   profile_end(slot, stream);
   if (err != hipSuccess) return err;
-  // 2. main
-  dim3 grid;
-  if (!packed(g)) {
-    const int nkt = (g.seqlen + kBlockN - 1) / kBlockN;
-    grid = dim3((unsigned)((long long)nkt * p.heads_kv * g.batch), 1, 1);
-  } else {
-    grid = dim3((unsigned)((g.max_seqlen + kBlockN - 1) / kBlockN), (unsigned)p.heads_kv, (unsigned)g.n_docs);
-  }
-  slot = profile_begin(kProfBwdMain, stream);
-  if (p.head_dim == 128) hipLaunchKernelGGL((attn_bwd_kernel<128>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((attn_bwd_kernel<64>), grid, dim3(256), 0, stream, p);
-  profile_end(slot, stream);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  // 3. finalize dQ
-  const long long n = g.total * (long long)p.heads_q * p.head_dim;
-  const unsigned blocks = (unsigned)((n / 4 + 255) / 256);
-  slot = profile_begin(kProfBwdFinal, stream);
-  if (p.dq_mode == 1)
-    hipLaunchKernelGGL((dq_finalize_kernel<true>), dim3(blocks), dim3(256), 0, stream, p.dq_acc, p.dq, n, 1.f / kBoost,
-                       p.out_f32, p.flags);
-  else
-    hipLaunchKernelGGL((dq_finalize_kernel<false>), dim3(blocks), dim3(256), 0, stream, p.dq_acc, p.dq, n, p.scale,
-                       p.out_f32, p.flags);
-  profile_end(slot, stream);
-  return hipGetLastError();
+  // 2. dK / dV, 3. dQ
+  return p.head_dim == 128 ? launch_main<128>(p, stream) : launch_main<64>(p, stream);
 }
 
 }  // namespace mx

@@ -57,9 +57,6 @@ struct FwdSmem {
   alignas(16) uint8_t vs[kStages][2 * D];
 };
 
-__device__ __forceinline__ int k_swz(int row, int chunk, int nchunk) { return chunk ^ (row & (nchunk - 1) & 7); }
-__device__ __forceinline__ int v_half_swz(int c, int half) { return half ^ ((c >> 2) & 1); }
-
 // Work decode: which (sequence, head, query tile) this workgroup computes.
 struct Work {
   int s;          // batch index or document index
@@ -101,18 +98,6 @@ __device__ __forceinline__ Work decode_work(const AttnParams& p) {
   return w;
 }
 
-__device__ __forceinline__ void dma(const void* src, void* lds, int size) {
-  // LDS-DMA load: each lane's `size` (16 or 4) bytes land at lds + lane * size (lds is wave-uniform).
-  if (size == 16)
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-  else
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
-}
-
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Issue the LDS-DMA loads of key tile kt into stage st. Rows past the end of the sequence /
 // document are clamped to its last row (and its last SEQ group): they are finite, and their
 // scores are masked, so their P is 0. LDS-DMA writes at least one dword per lane, so the
@@ -132,30 +117,30 @@ __device__ __forceinline__ uint32_t issue_tile(const AttnParams& p, const Work& 
   for (int j = wave; j < kBlockN * NCH / 64; j += kWaves) {     // K codes
     const int pch = j * 64 + lane;
     const int r = pch / NCH;
-    const int c = k_swz(r, pch % NCH, NCH);
+    const int c = row_swz(r, pch % NCH, NCH);
     const int key = min(kt * kBlockN + r, nlast);
-    dma(p.k_codes + elem_offset(g, p.heads_kv, D, sbase, hkv, key, c * 16), &sm.k[st][j * 1024], 16);
+    lds_dma(p.k_codes + elem_offset(g, p.heads_kv, D, sbase, hkv, key, c * 16), &sm.k[st][j * 1024], 16);
   }
 #pragma unroll
   for (int j = wave; j < 4 * D / 64; j += kWaves) {             // V codes (2 groups x D x 2 halves)
     const int pch = j * 64 + lane;
     const int grp = pch / (2 * D);
     const int ch = (pch % (2 * D)) >> 1;
-    const int half = v_half_swz(ch, pch & 1);
+    const int half = half_swz(ch, pch & 1);
     const int gi = min(2 * kt + grp, glast);
     const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
-    dma(p.v_codes + (row * D + ch) * 32 + half * 16, &sm.v[st][j * 1024], 16);
+    lds_dma(p.v_codes + (row * D + ch) * 32 + half * 16, &sm.v[st][j * 1024], 16);
   }
   uint32_t kscale = 0;
   if (wave == 0) {                                               // K scales, one key per lane
     const int key = min(kt * kBlockN + lane, nlast);
     const uint8_t* src = p.k_scales + (elem_offset(g, p.heads_kv, D, sbase, hkv, key, 0) >> 5);
-    if (D == 128) dma(src, sm.ks[st], 4);
+    if (D == 128) lds_dma(src, sm.ks[st], 4);
     else kscale = *reinterpret_cast<const uint16_t*>(src);
   } else if (wave == 1 && lane < D / 2) {                        // V scales, one dword per lane
     const int gi = min(2 * kt + (lane * 4) / D, glast);
     const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
-    dma(p.v_scales + row * D + (lane * 4) % D, sm.vs[st], 4);
+    lds_dma(p.v_scales + row * D + (lane * 4) % D, sm.vs[st], 4);
   }
   return kscale;
 }
@@ -164,8 +149,6 @@ template <int D>
 __device__ __forceinline__ void put_kscale(FwdSmem<D>& sm, int st, uint32_t kscale) {
   if (D == 64 && threadIdx.x < 64) *reinterpret_cast<uint16_t*>(&sm.ks[st][threadIdx.x * 2]) = (uint16_t)kscale;
 }
-
-__device__ __forceinline__ v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 
 // S^T for the two 32-key half tiles of stage st: keys are MFMA rows, the wave's 32 queries columns.
 template <int D>
@@ -182,8 +165,8 @@ __device__ __forceinline__ void scores(const FwdSmem<D>& sm, int st, const v8i* 
     sacc[T] = v16f{};
 #pragma unroll
     for (int s = 0; s < NS; s++) {
-      const v4i a = *reinterpret_cast<const v4i*>(&sm.k[st][row * D + (k_swz(row, 4 * s + hh, NCH) << 4)]);
-      const v4i b = *reinterpret_cast<const v4i*>(&sm.k[st][row * D + (k_swz(row, 4 * s + 2 + hh, NCH) << 4)]);
+      const v4i a = *reinterpret_cast<const v4i*>(&sm.k[st][row * D + (row_swz(row, 4 * s + hh, NCH) << 4)]);
+      const v4i b = *reinterpret_cast<const v4i*>(&sm.k[st][row * D + (row_swz(row, 4 * s + 2 + hh, NCH) << 4)]);
       const int ksc = (ksw >> (8 * (2 * s + hh))) & 0xFF;
       sacc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), qop[s], sacc[T], 0, 0, 0, ksc, 0, qsc[s]);
     }
@@ -238,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   float M = -INFINITY;  // integer running max (base 2)
   float lsum = 0.f;     // this lane's share of l (its 16 keys of every half tile)
 
-  wait_dma();
+  wait_vmem();
   __syncthreads();
   v16f sacc[2], snext[2];
   if (active(0)) scores<D>(sm, 0, qop, qsc, sacc);
@@ -306,8 +289,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int t = 0; t < D / 32; t++) {
         const int ch = t * 32 + l32;
-        const v4i a = *reinterpret_cast<const v4i*>(&sm.v[st][(0 * D + ch) * 32 + (v_half_swz(ch, hh) << 4)]);
-        const v4i b = *reinterpret_cast<const v4i*>(&sm.v[st][(1 * D + ch) * 32 + (v_half_swz(ch, hh) << 4)]);
+        const v4i a = *reinterpret_cast<const v4i*>(&sm.v[st][(0 * D + ch) * 32 + (half_swz(ch, hh) << 4)]);
+        const v4i b = *reinterpret_cast<const v4i*>(&sm.v[st][(1 * D + ch) * 32 + (half_swz(ch, hh) << 4)]);
         const int vsc = sm.vs[st][hh * D + ch];
         oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), pop, oacc[t], 0, 0, 0, vsc, 0, psc);
       }
@@ -316,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     sacc[1] = snext[1];
     if (kt + 2 < nkt) put_kscale<D>(sm, (kt + 2) % kStages, kscale);
     if (kt + 1 < nkt) {
-      wait_dma();
+      wait_vmem();
       __syncthreads();
     }
   }

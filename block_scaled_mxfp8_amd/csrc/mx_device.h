@@ -63,6 +63,21 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// 2^e for an E8M0 exponent e in [-127, 127] as an fp32 scale operand (2^-127 is the
+// subnormal 0x00400000; the kernels run with IEEE denormals).
+__device__ __forceinline__ float exp2_scale(int e) {
+  return __uint_as_float(e > -127 ? (uint32_t)(e + 127) << 23 : 0x00400000u);
+}
+
+// Four E4M3 codes of x / s (RNE, v_cvt_scalef32_pk_fp8_f32; s a power of two), packed
+// little-endian. Equal to pack4_e4m3 of the values times 1/s, without the multiplies.
+__device__ __forceinline__ uint32_t pack4_e4m3_scaled(float a, float b, float c, float d, float s) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, s, false);
+  const v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c, d, s, true);
+  return __builtin_bit_cast(uint32_t, w);
+}
+
 // Exchange with the lane 32 positions away (lane ^ 32) via v_permlane32_swap.
 __device__ __forceinline__ float swap32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -70,5 +85,40 @@ __device__ __forceinline__ float swap32(float x) {
   // lanes >= 32 read the lower half from r[0].
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
+
+// Maximum over all 64 lanes, without LDS: DPP within rows of 16, then the row pairs
+// (v_permlane16_swap) and the halves (v_permlane32_swap). Every lane gets the result.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));   // quad 1,0,3,2
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));   // quad 2,3,0,1
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));  // half mirror
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));  // mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(x, fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1])));
+}
+
+__device__ __forceinline__ v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
+
+// LDS tile swizzles. Row-major code tiles ([rows][d]): 16-byte chunk c of row r sits at chunk
+// c ^ (r & 7), so the 32 rows an MFMA operand read touches spread over all banks. SEQ-view
+// tiles ([group][channel][32]): the two 16-byte halves of channel ch swap when (ch >> 2) & 1.
+__device__ __forceinline__ int row_swz(int row, int chunk, int nchunk) { return chunk ^ (row & (nchunk - 1) & 7); }
+__device__ __forceinline__ int half_swz(int c, int half) { return half ^ ((c >> 2) & 1); }
+
+// LDS-DMA load (global_load_lds): lane i's `size` bytes (16 or 4) land at lds + i * size;
+// `lds` must be the same for the whole wave. Completion is counted by vmcnt.
+__device__ __forceinline__ void lds_dma(const void* src, void* lds, int size) {
+  if (size == 16)
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// Wait for every outstanding vector-memory operation of this wave (loads, LDS-DMA).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace mx

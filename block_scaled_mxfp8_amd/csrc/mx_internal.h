@@ -18,12 +18,10 @@ struct QuantizeParams {
   uint8_t* seq_codes;    // nullptr: SEQ view not wanted
   uint8_t* seq_scales;
   // backward preprocessing (all nullptr for a plain quantise): with `o` set, the kernel also
-  // writes delta[token, head] = sum_c dequant(ROW code) * O and zeroes dq_acc.
+  // writes delta[token, head] = sum_c dequant(ROW code) * O.
   const void* o;
   bool o_f32;
   float* delta;
-  void* dq_acc;
-  bool dq_f16;
 };
 
 struct AttnParams {
@@ -62,7 +60,6 @@ struct BwdParams {
   uint8_t* gr_codes; uint8_t* gr_scales;                // ROW G
   uint8_t* gs_codes; uint8_t* gs_scales;                // SEQ G
   float* delta;                                         // D per (row, head)
-  void* dq_acc;                                         // FP32 or FP16 accumulator [like Q]
   uint32_t* flags;
 };
 

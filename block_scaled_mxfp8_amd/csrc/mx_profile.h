@@ -7,8 +7,7 @@
 
 namespace mx {
 
-enum ProfileKind { kProfNone = 0, kProfFwd = 1, kProfBwdMain = 2, kProfQuantize = 3, kProfBwdPrep = 4,
-                   kProfBwdFinal = 5 };
+enum ProfileKind { kProfNone = 0, kProfFwd = 1, kProfBwdKV = 2, kProfQuantize = 3, kProfBwdPrep = 4, kProfBwdQ = 5 };
 
 struct ProfileHook {
   int kind = kProfNone;
@@ -24,13 +23,13 @@ inline int profile_begin(int kind, hipStream_t stream) {
   ProfileHook& h = profile_hook();
   if (h.kind != kind || h.n <= 0) return -1;
   const int slot = (int)(h.count++ % h.n);
-  hipEventRecord(h.start[slot], stream);
+  (void)hipEventRecord(h.start[slot], stream);
   return slot;
 }
 
 inline void profile_end(int slot, hipStream_t stream) {
   if (slot < 0) return;
-  hipEventRecord(profile_hook().stop[slot], stream);
+  (void)hipEventRecord(profile_hook().stop[slot], stream);
 }
 
 }  // namespace mx

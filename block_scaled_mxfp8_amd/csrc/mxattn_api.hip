@@ -67,7 +67,7 @@ mx_status check_desc(const mx_attn_desc* d, mx::Geom* g) {
 }
 
 struct BwdWorkspace {
-  size_t gr_codes, gr_scales, gs_codes, gs_scales, delta, dq_acc, flags, total;
+  size_t gr_codes, gr_scales, gs_codes, gs_scales, delta, flags, total;
 };
 
 BwdWorkspace bwd_layout(const mx::Geom& g, const mx_attn_desc* d) {
@@ -80,7 +80,6 @@ BwdWorkspace bwd_layout(const mx::Geom& g, const mx_attn_desc* d) {
   w.gs_codes = off; off += align_up(seq_codes_bytes(g, hq, dim));
   w.gs_scales = off; off += align_up(seq_codes_bytes(g, hq, dim) / 32);
   w.delta = off; off += align_up((size_t)g.total * hq * sizeof(float));
-  w.dq_acc = off; off += align_up(row_codes_bytes(g, hq, dim) * (d->dq_mode == MX_DQ_F16_BOOST ? 2 : 4));
   w.total = off;
   return w;
 }
@@ -149,7 +148,6 @@ mx_status bwd_impl(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_
   p.gr_codes = ws + w.gr_codes; p.gr_scales = ws + w.gr_scales;
   p.gs_codes = ws + w.gs_codes; p.gs_scales = ws + w.gs_scales;
   p.delta = reinterpret_cast<float*>(ws + w.delta);
-  p.dq_acc = ws + w.dq_acc;
   p.flags = reinterpret_cast<uint32_t*>(ws + w.flags);
   if (g.total == 0) return MX_OK;
   return mx::launch_attn_bwd(p, (hipStream_t)stream) == hipSuccess ? MX_OK : MX_E_DEVICE;

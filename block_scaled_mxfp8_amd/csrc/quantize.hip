@@ -138,17 +138,6 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
                                        : (((long long)s * p.heads + h) * g.seqlen + tok0 + tk);
         p.delta[ti] = part;
       }
-      if (valid) {
-        if (p.dq_f16) {
-          v4i* dst = reinterpret_cast<v4i*>(static_cast<uint16_t*>(p.dq_acc) + e0);
-          dst[0] = v4i{0, 0, 0, 0};
-          dst[1] = v4i{0, 0, 0, 0};
-        } else {
-          v4i* dst = reinterpret_cast<v4i*>(static_cast<float*>(p.dq_acc) + e0);
-#pragma unroll
-          for (int i = 0; i < 4; i++) dst[i] = v4i{0, 0, 0, 0};
-        }
-      }
     }
   }
   if (!p.seq_codes) return;

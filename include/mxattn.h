@@ -123,8 +123,9 @@ mx_status mx_attn_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, 
 
 /* Backward: given G = dL/dO (g_dtype), the saved O and LSE of the forward, and the views of
  * Q, K, V, writes dQ [like Q], dK and dV [like K] in out_dtype. G is quantised internally
- * (ROW and SEQ views) into the workspace, D = rowsum(G_row o O) is formed there, and dQ is
- * accumulated there (FP32, or FP16 x 2^9 for dq_mode = MX_DQ_F16_BOOST). */
+ * (ROW and SEQ views) into the workspace and D = rowsum(G_row o O) is formed there. dQ is
+ * accumulated in FP32, or (dq_mode = MX_DQ_F16_BOOST) as FP16 sums of FP32 partials over
+ * 128-key blocks, each multiplied by 2^9 before rounding; the boost is removed at the end. */
 mx_status mx_attn_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
                       mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                       mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
@@ -152,7 +153,7 @@ mx_status mx_read_flags(const void* workspace, uint32_t* flags);
  * (hipEvent_t passed as void*, created by the caller): every following launch of the selected
  * kernel records start[i % count] just before and stop[i % count] just after it, on the stream
  * it is launched on, i = launch index since registration. kernel: 1 forward attention kernel,
- * 2 backward main kernel, 3 mx_quantize, 4 backward G preprocessing, 5 dQ finalize; 0 (or
+ * 2 backward dK/dV kernel, 3 mx_quantize, 4 backward G preprocessing, 5 backward dQ kernel; 0 (or
  * count <= 0) turns the hook off. The event arrays must stay valid while registered. One
  * hook per process; not thread-safe. */
 mx_status mx_profile_kernel(int32_t kernel, void* const* start_events, void* const* stop_events, int32_t count);
