@@ -4,7 +4,10 @@
 
 All HIP sources under csrc/ are compiled into one shared library next to this file. Packed
 FP32 instructions are disabled for the device code (-packed-fp32-ops); the host pass of
-hipcc warns that it does not know that target feature, which is harmless.
+hipcc warns that it does not know that target feature, which is harmless. MFMA accumulators
+are kept in the VGPR form (-amdgpu-mfma-vgpr-form): left to its heuristic, the backend put the
+backward's dK/dV accumulators in AGPRs and copied them to VGPRs and back around every MFMA
+(~450 v_accvgpr moves per 64-query step).
 """
 import glob
 import os
@@ -31,7 +34,7 @@ def sources():
 def build(verbose=False, out=LIB, extra=()):
     tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wno-unused-command-line-argument",
            "-I", os.path.join(ROOT, "include"), *extra, *sources(), "-o", tmp]
     if verbose:

@@ -77,29 +77,30 @@ __device__ __forceinline__ long long token_index(const Geom& g, int heads, int s
 
 // LDS-DMA of a 64-row ROW-view tile ([row][d] codes, row_swz chunks) and of a two-group
 // SEQ-view tile ([group][channel][32], half_swz halves). One DMA instruction moves 64 x 16
-// bytes. With NCH = d/16 chunks per row, instruction j covers rows j*64/NCH + lane/NCH, and
-// the swizzled chunk of a lane does not depend on j (64/NCH is a multiple of NCH); likewise
-// in a SEQ tile the half of a lane does not depend on the instruction. So each lane keeps
-// one 32-bit offset per tile kind and the rest is a wave-uniform base.
+// bytes. With NCH = d/16 chunks per row, instruction j covers rows j*64/NCH + lane/NCH; the
+// swizzled chunk of a lane depends only on the parity of j (d = 128) or not at all (d = 64),
+// and in a SEQ tile the half of a lane does not depend on the instruction. So each lane keeps
+// one or two 32-bit offsets and the rest is a wave-uniform base.
 template <int D>
-__device__ __forceinline__ int row_tile_lane_off(int lane) {
+__device__ __forceinline__ int row_tile_lane_off(int lane, int jpar) {
   constexpr int NCH = D / 16;
-  const int lr = lane / NCH;
-  return row_swz(lr, lane % NCH, NCH) * 16;
+  const int r = jpar * (64 / NCH) + lane / NCH;
+  return row_swz(r, lane % NCH, NCH) * 16;
 }
 __device__ __forceinline__ int seq_tile_lane_off(int lane) {
   return (lane >> 1) * 32 + (half_swz(lane >> 1, lane & 1) << 4);
 }
 
-// rows r0.. of a ROW tile; rows past `rmax` (relative to r0) are clamped to it.
+// rows r0.. of a ROW tile; rows past `rmax` (relative to r0) are clamped to it. loff[p] is
+// row_tile_lane_off for instruction parity p.
 template <int D>
-__device__ __forceinline__ void dma_row_tile(const uint8_t* base, long long tstride, int rmax, int lane, int loff,
-                                             uint8_t* lds) {
+__device__ __forceinline__ void dma_row_tile(const uint8_t* base, long long tstride, int rmax, int lane,
+                                             const int (&loff)[2], uint8_t* lds) {
   constexpr int NCH = D / 16;
 #pragma unroll
   for (int j = 0; j < 64 * NCH / 64; j++) {
     const int r = min(j * (64 / NCH) + lane / NCH, rmax);
-    lds_dma(base + (uint32_t)(r * tstride + loff), lds + j * 1024, 16);
+    lds_dma(base + (uint32_t)(r * tstride + loff[j & 1]), lds + j * 1024, 16);
   }
 }
 
@@ -173,7 +174,7 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
 // their LSE is +inf, so their P and U are 0).
 template <int D>
 __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
-                                          uint32_t (&sv)[2], int roff, int soff) {
+                                          uint32_t (&sv)[2], const int (&roff)[2], int soff) {
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -244,7 +245,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
   const int qfirst = p.causal ? (k0 / kStepQ) * kStepQ : 0;
   const int nsteps_h = (w.n - qfirst + kStepQ - 1) / kStepQ;
   const int nsteps = nsteps_h * group;
-  const int roff = row_tile_lane_off<D>(lane), soff = seq_tile_lane_off(lane);
+  const int roff[2] = {row_tile_lane_off<D>(lane, 0), row_tile_lane_off<D>(lane, 1)};
+  const int soff = seq_tile_lane_off(lane);
   uint32_t sv[2];
   dkv_issue<D>(p, w, w.hkv * group, qfirst, sm[0], sv, roff, soff);
 
@@ -434,7 +436,7 @@ __device__ __forceinline__ QWork decode_q(const BwdParams& p) {
 // Issue the loads of key tile kt (keys 64kt..64kt+63 of KV head hkv) into stage `st`.
 template <int D>
 __device__ __forceinline__ void dq_issue(const BwdParams& p, const QWork& w, int hkv, int kt, DqStage<D>& st,
-                                         uint32_t& sv, int roff, int soff) {
+                                         uint32_t& sv, const int (&roff)[2], int soff) {
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -499,7 +501,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const int kend = p.causal ? min(w.n, q0 + kBlockQ) : w.n;
   const int nkt = (kend + kStepK - 1) / kStepK;
 
-  const int roff = row_tile_lane_off<D>(lane), soff = seq_tile_lane_off(lane);
+  const int roff[2] = {row_tile_lane_off<D>(lane, 0), row_tile_lane_off<D>(lane, 1)};
+  const int soff = seq_tile_lane_off(lane);
   uint32_t sv;
   dq_issue<D>(p, w, hkv, 0, sm[0], sv, roff, soff);
 

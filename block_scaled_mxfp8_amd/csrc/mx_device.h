@@ -101,11 +101,17 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 
-// LDS tile swizzles. Row-major code tiles ([rows][d]): 16-byte chunk c of row r sits at chunk
-// c ^ (r & 7), so the 32 rows an MFMA operand read touches spread over all banks. SEQ-view
-// tiles ([group][channel][32]): the two 16-byte halves of channel ch swap when (ch >> 2) & 1.
-__device__ __forceinline__ int row_swz(int row, int chunk, int nchunk) { return chunk ^ (row & (nchunk - 1) & 7); }
-__device__ __forceinline__ int half_swz(int c, int half) { return half ^ ((c >> 2) & 1); }
+// LDS tile swizzles. A 16-byte-per-lane LDS read is served 16 lanes (256 bytes, every bank
+// once) at a time, so the 16 rows (channels) such a group touches must land on distinct
+// 16-byte bank groups.
+//  Row-major code tiles ([rows][d], nchunk = d/16 chunks of 16 bytes per row; 16/nchunk rows
+//  fill the 256 bytes): chunk c of row r sits at c ^ ((r / (16/nchunk)) mod nchunk).
+//  SEQ-view tiles ([group][channel][32]): the two 16-byte halves of channel ch swap when
+//  (ch >> 3) & 1.
+__device__ __forceinline__ int row_swz(int row, int chunk, int nchunk) {
+  return chunk ^ ((nchunk == 8 ? row >> 1 : row >> 2) & (nchunk - 1));
+}
+__device__ __forceinline__ int half_swz(int c, int half) { return half ^ ((c >> 3) & 1); }
 
 // LDS-DMA load (global_load_lds): lane i's `size` bytes (16 or 4) land at lds + i * size;
 // `lds` must be the same for the whole wave. Completion is counted by vmcnt.
