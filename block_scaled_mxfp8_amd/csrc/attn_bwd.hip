@@ -141,11 +141,12 @@ struct KvWork {
   bool valid;
 };
 
+template <bool kPacked>
 __device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
   const Geom& g = p.geom;
   KvWork w;
   w.valid = true;
-  if (!packed(g)) {
+  if (!kPacked) {
     const int nkb = (g.seqlen + kBlockK - 1) / kBlockK;
     const long long total = (long long)nkb * p.heads_kv * g.batch;
     long long bid = blockIdx.x;
@@ -169,42 +170,95 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
   return w;
 }
 
+// Lane-invariant DMA offsets of the dK/dV stage loads. A ROW tile takes NCH = d/16 chunk
+// loads per row, 64/NCH rows per instruction and NCH instructions; wave w issues
+// instructions NJ*w .. NJ*w + NJ - 1 (NJ = NCH/4) of each ROW tile and D/64 of each SEQ tile.
+template <int D>
+struct DkvLane {
+  int cz[D / 64];    // swizzled chunk byte offset of this lane, per instruction of the wave
+  int rlo[D / 64];   // row offset (bytes) inside the wave's rows + cz, for a full tile
+  int lrow;          // row of this lane inside an instruction
+  int soff;          // SEQ tile lane offset
+};
+
+template <int D, bool kPacked>
+__device__ __forceinline__ DkvLane<D> dkv_lane(const BwdParams& p, int lane) {
+  constexpr int NCH = D / 16, NJ = NCH / 4, RPI = 64 / NCH;
+  DkvLane<D> L;
+  L.lrow = lane / NCH;
+  const int ts = (int)token_stride_k<kPacked>(p.heads_q, D);
+#pragma unroll
+  for (int jj = 0; jj < NJ; jj++) {
+    // row of instruction j = NJ*w + jj is j*RPI + lrow; its swizzle depends on j only
+    // through jj (NJ*RPI is a multiple of the swizzle period)
+    L.cz[jj] = row_swz(jj * RPI + L.lrow, lane % NCH, NCH) * 16;
+    L.rlo[jj] = (jj * RPI + L.lrow) * ts + L.cz[jj];
+  }
+  L.soff = seq_tile_lane_off(lane);
+  return L;
+}
+
 // Issue the loads of the step (query head hq, queries q0..q0+63) into stage `st`; `sv` gets
 // this thread's small items. Rows past the end are clamped to the last row (finite codes;
 // their LSE is +inf, so their P and U are 0).
-template <int D>
+template <int D, bool kPacked>
 __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
-                                          uint32_t (&sv)[2], const int (&roff)[2], int soff) {
+                                          uint32_t (&sv)[2], const DkvLane<D>& L) {
+  constexpr int NCH = D / 16, NJ = NCH / 4, RPI = 64 / NCH, PER = D / 32, NSJ = D / 64;
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const long long sbase = packed(g) ? (long long)w.doc_start : (long long)w.s;
-  const int nlast = w.n - 1;
-  const int glast = ((w.n + 31) >> 5) - 1;
-  if (wave < 2) {                                     // wave 0: Q ROW, wave 1: G ROW
-    const long long tok0 = elem_offset(g, p.heads_q, D, sbase, hq, q0, 0);
-    dma_row_tile<D>((wave == 0 ? p.q_codes : p.gr_codes) + tok0, token_stride(g, p.heads_q, D), nlast - q0, lane,
-                    roff, wave == 0 ? st.qr : st.gr);
-  } else {                                            // wave 2: Q SEQ, wave 3: G SEQ
-    const int g0 = q0 >> 5;
-    const long long row0 = seq_group_row(g, p.heads_q, w.s, hq, w.doc_start, min(g0, glast));
-    const long long row1 = seq_group_row(g, p.heads_q, w.s, hq, w.doc_start, min(g0 + 1, glast));
-    dma_seq_tile<D>(wave == 2 ? p.qs_codes : p.gs_codes, row0, row1, soff, wave == 2 ? st.qs : st.gs, 0, 1);
+  const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
+  const long long ts = token_stride_k<kPacked>(p.heads_q, D);
+  const long long off0 = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, hq, q0, 0);
+  const int rmax = w.n - 1 - q0;
+  // ROW tiles
+  if (rmax >= kStepQ - 1) {
+    const long long wb = off0 + (long long)(NJ * wave * RPI) * ts;
+#pragma unroll
+    for (int jj = 0; jj < NJ; jj++) {
+      const int j = NJ * wave + jj;
+      lds_dma(p.q_codes + wb + (uint32_t)L.rlo[jj], st.qr + j * 1024, 16);
+      lds_dma(p.gr_codes + wb + (uint32_t)L.rlo[jj], st.gr + j * 1024, 16);
+    }
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < NJ; jj++) {
+      const int j = NJ * wave + jj;
+      const uint32_t vo = (uint32_t)(min(j * RPI + L.lrow, rmax) * (int)ts + L.cz[jj]);
+      lds_dma(p.q_codes + off0 + vo, st.qr + j * 1024, 16);
+      lds_dma(p.gr_codes + off0 + vo, st.gr + j * 1024, 16);
+    }
   }
-  sv[0] = sv[1] = 0;
-  if (wave < 2) {                                     // ROW scale word + LSE (wave 0) / D (wave 1)
-    const int q = min(q0 + lane, nlast);
-    const long long tok = elem_offset(g, p.heads_q, D, sbase, hq, q0, 0);
-    const uint32_t rel = (uint32_t)((q - q0) * token_stride(g, p.heads_q, D));
-    sv[0] = load_row_scales<D>((wave == 0 ? p.q_scales : p.gr_scales) + (tok >> 5), rel);
-    const float* f = (wave == 0 ? p.lse : p.delta) + token_index(g, p.heads_q, w.s, w.doc_start, hq, q0);
-    const float x = f[(uint32_t)((q - q0) * (packed(g) ? p.heads_q : 1))];
-    const bool live = q0 + lane < w.n;
-    sv[1] = __float_as_uint(wave == 0 ? (live ? x * kLog2e : INFINITY) : (live ? x : 0.f));
-  } else if (lane < D / 2) {                          // SEQ scales (wave 2: Q, wave 3: G), a dword per lane
-    const int gi = min((q0 >> 5) + (lane * 4) / D, glast);
-    const long long row = seq_group_row(g, p.heads_q, w.s, hq, w.doc_start, gi);
-    sv[0] = *reinterpret_cast<const uint32_t*>((wave == 2 ? p.qs_scales : p.gs_scales) + row * D + (lane * 4) % D);
+  // SEQ tiles (groups q0/32 and q0/32 + 1, the latter clamped to the last group)
+  const int glast = ((w.n + 31) >> 5) - 1;
+#pragma unroll
+  for (int jj = 0; jj < NSJ; jj++) {
+    const int j = NSJ * wave + jj;
+    const int grp = min((q0 >> 5) + j / PER, glast);
+    const long long row = seq_group_row_k<kPacked>(g, p.heads_q, w.s, hq, w.doc_start, grp);
+    const long long o = row * (D * 32) + (j % PER) * 1024;
+    lds_dma(p.qs_codes + o + (uint32_t)L.soff, st.qs + j * 1024, 16);
+    lds_dma(p.gs_codes + o + (uint32_t)L.soff, st.gs + j * 1024, 16);
+  }
+  // small items: wave 0 Q ROW scales, wave 1 G ROW scales, wave 2 LSE + Q SEQ scales,
+  // wave 3 D + G SEQ scales
+  const int r = min(lane, rmax);
+  if (wave < 2) {
+    const uint8_t* base = (wave == 0 ? p.q_scales : p.gr_scales) + (off0 >> 5);
+    sv[0] = load_row_scales<D>(base, (uint32_t)(r * (int)ts));
+    sv[1] = 0;
+  } else {
+    const float* f = (wave == 2 ? p.lse : p.delta) + token_index_k<kPacked>(g, p.heads_q, w.s, w.doc_start, hq, q0);
+    const float x = f[(uint32_t)(r * (kPacked ? p.heads_q : 1))];
+    const bool live = lane <= rmax;
+    sv[0] = __float_as_uint(wave == 2 ? (live ? x * kLog2e : INFINITY) : (live ? x : 0.f));
+    sv[1] = 0;
+    if (lane < D / 2) {
+      const int gi = min((q0 >> 5) + (lane * 4) / D, glast);
+      const long long row = seq_group_row_k<kPacked>(g, p.heads_q, w.s, hq, w.doc_start, gi);
+      sv[1] = *reinterpret_cast<const uint32_t*>((wave == 2 ? p.qs_scales : p.gs_scales) + row * D + (lane * 4) % D);
+    }
   }
 }
 
@@ -214,25 +268,32 @@ __device__ __forceinline__ void dkv_put(DkvStage<D>& st, const uint32_t (&sv)[2]
   const int wave = wave_id();
   if (wave < 2) {
     (wave == 0 ? st.qrs : st.grs)[lane] = sv[0];
-    (wave == 0 ? st.lse2 : st.dlt)[lane] = __uint_as_float(sv[1]);
-  } else if (lane < D / 2) {
-    reinterpret_cast<uint32_t*>(wave == 2 ? st.qss : st.gss)[lane] = sv[0];
+  } else {
+    (wave == 2 ? st.lse2 : st.dlt)[lane] = __uint_as_float(sv[0]);
+    if (lane < D / 2) reinterpret_cast<uint32_t*>(wave == 2 ? st.qss : st.gss)[lane] = sv[1];
   }
 }
 
-// d = 128 needs ~400 registers per lane (dK and dV accumulators alone take 128): one wave per
-// SIMD, accumulators in AGPRs. d = 64 fits two workgroups per CU.
-template <int D>
+// E8M0 exponent of a P group: P is 0 or a normal number <= 1 (v_exp_f32 flushes results
+// below 2^-126), so the subnormal branch of scale_exp_from_bits is not needed.
+__device__ __forceinline__ int p_scale_exp(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  return max((int)(b >> 23) - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0), -127);
+}
+
+// d = 128 needs ~300 registers per lane (dK and dV accumulators alone take 128): one wave
+// per SIMD. d = 64 fits two workgroups per CU.
+template <int D, bool kPacked>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ DkvStage<D> sm[2];
-  const KvWork w = decode_kv(p);
+  const KvWork w = decode_kv<kPacked>(p);
   if (!w.valid) return;
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int hh = lane >> 5;
   const int l32 = lane & 31;
-  const long long sbase = packed(g) ? (long long)w.doc_start : (long long)w.s;
+  const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
   const int k0 = w.kb * kBlockK;
   const int kw = k0 + wave * 32;          // first key of this wave
   const int key = kw + l32;               // this lane's key (column of S and E)
@@ -243,12 +304,11 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
 
   const int group = p.heads_q / p.heads_kv;
   const int qfirst = p.causal ? (k0 / kStepQ) * kStepQ : 0;
-  const int nsteps_h = (w.n - qfirst + kStepQ - 1) / kStepQ;
-  const int nsteps = nsteps_h * group;
-  const int roff[2] = {row_tile_lane_off<D>(lane, 0), row_tile_lane_off<D>(lane, 1)};
-  const int soff = seq_tile_lane_off(lane);
+  const int nsteps = ((w.n - qfirst + kStepQ - 1) / kStepQ) * group;
+  const DkvLane<D> L = dkv_lane<D, kPacked>(p, lane);
+  int hq = w.hkv * group, q0 = qfirst;    // the step in LDS buffer st & 1
   uint32_t sv[2];
-  dkv_issue<D>(p, w, w.hkv * group, qfirst, sm[0], sv, roff, soff);
+  dkv_issue<D, kPacked>(p, w, hq, q0, sm[0], sv, L);
 
   // K and V of the lane's key: B operands of S and E, kept in registers
   // kvsc: byte s = K scale of contraction step s, byte 2 + s = V scale (groups 2s + hh)
@@ -256,7 +316,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
   uint32_t kvsc = 0;
 #pragma unroll
   for (int s = 0; s < NS; s++) {
-    const long long off = elem_offset(g, p.heads_kv, D, sbase, w.hkv, min(key, w.n - 1), 64 * s);
+    const long long off = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, w.hkv, min(key, w.n - 1), 64 * s);
     kop[s] = cat(*reinterpret_cast<const v4i*>(p.k_codes + off + 16 * hh),
                  *reinterpret_cast<const v4i*>(p.k_codes + off + 32 + 16 * hh));
     vop[s] = cat(*reinterpret_cast<const v4i*>(p.vr_codes + off + 16 * hh),
@@ -285,12 +345,13 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
 
   for (int st = 0; st < nsteps; st++) {
     const int buf = st & 1;
-    const int q0 = qfirst + (st % nsteps_h) * kStepQ;
-    if (st + 1 < nsteps) {
-      const int s2 = st + 1;
-      dkv_issue<D>(p, w, w.hkv * group + s2 / nsteps_h, qfirst + (s2 % nsteps_h) * kStepQ, sm[buf ^ 1], sv, roff,
-                   soff);
+    int hq_n = hq, q0_n = q0 + kStepQ;
+    if (q0_n >= w.n) {
+      q0_n = qfirst;
+      hq_n++;
     }
+    const bool more = st + 1 < nsteps;
+    if (more) dkv_issue<D, kPacked>(p, w, hq_n, q0_n, sm[buf ^ 1], sv, L);
     const DkvStage<D>& S = sm[buf];
     // waves whose keys all follow the step's last query (causal) see nothing
     if (kw < w.n && !(p.causal && kw > q0 + kStepQ - 1)) {
@@ -333,7 +394,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
         // P_b: 32 queries of this key per group (this lane and lane ^ 32)
         float pm = max_abs16(P);
         pm = fmaxf(pm, swap32(pm));
-        pbe[qt] = scale_exp_from_bits(__float_as_uint(pm));
+        pbe[qt] = p_scale_exp(pm);
         const float psc = exp2_scale(pbe[qt]);
         // dS: the 32 x 32 block (this wave's keys x the tile's queries)
         const float um = wave_max(max_abs16(U));
@@ -357,11 +418,13 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
         dk[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsop, qb, dk[t], 0, 0, 0, dssc, 0, S.qss[scoff + t * 32]);
       }
     }
-    if (st + 1 < nsteps) {
+    if (more) {
       dkv_put<D>(sm[buf ^ 1], sv);
       wait_vmem();
       __syncthreads();
     }
+    hq = hq_n;
+    q0 = q0_n;
   }
 
   // ---- epilogue: dK = alpha * acc, dV = acc; accumulator rows = keys, columns = channels ----
@@ -372,7 +435,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
     for (int i = 0; i < 16; i++) {
       const int kk = kw + 8 * (i >> 2) + 4 * hh + (i & 3);
       if (kk < w.n) {
-        const long long off = elem_offset(g, p.heads_kv, D, sbase, w.hkv, kk, ch);
+        const long long off = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, w.hkv, kk, ch);
         const float vk = dk[t][i] * p.scale, vv = dv[t][i];
         if (p.out_f32) {
           static_cast<float*>(p.dk)[off] = vk;
@@ -658,7 +721,8 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
     gq = dim3((unsigned)((g.max_seqlen + kBlockQ - 1) / kBlockQ), (unsigned)p.heads_q, (unsigned)g.n_docs);
   }
   int slot = profile_begin(kProfBwdKV, stream);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), gkv, dim3(256), 0, stream, p);
+  if (packed(g)) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), gkv, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), gkv, dim3(256), 0, stream, p);
   profile_end(slot, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -43,6 +43,27 @@ __host__ __device__ inline long long seq_group_row(const Geom& g, int heads, int
   return (long long)h * g.gseq + (doc_start >> 5) + s + grp;
 }
 
+// The same three maps with the layout fixed at compile time (kernels are instantiated for
+// batched and packed geometry, so no runtime layout branch sits in their loops).
+template <bool kPacked>
+__host__ __device__ inline long long elem_offset_k(const Geom& g, int heads, int d, long long seq, int h, long long t,
+                                                   int c) {
+  if (kPacked) return ((seq + t) * heads + h) * (long long)d + c;
+  return (((long long)seq * heads + h) * g.seqlen + t) * d + c;
+}
+template <bool kPacked>
+__host__ __device__ inline long long token_stride_k(int heads, int d) { return kPacked ? (long long)heads * d : d; }
+template <bool kPacked>
+__host__ __device__ inline long long seq_group_row_k(const Geom& g, int heads, int s, int h, int doc_start, int grp) {
+  if (!kPacked) return ((long long)s * heads + h) * g.gseq + grp;
+  return (long long)h * g.gseq + (doc_start >> 5) + s + grp;
+}
+// Index of (token t, head h) in a [B, H, L] / [T, H] per-row array (LSE, D).
+template <bool kPacked>
+__host__ __device__ inline long long token_index_k(const Geom& g, int heads, int s, int doc_start, int h, long long t) {
+  return kPacked ? ((long long)(doc_start + t) * heads + h) : (((long long)s * heads + h) * g.seqlen + t);
+}
+
 // Byte position of token offset t (0..31) inside a 32-byte SEQ-view group. It matches the
 // K order of the gfx950 32x32x64 MFMA operand built from an accumulator tile: lanes 0-31
 // carry tokens {0-3, 8-11, 16-19, 24-27} in bytes 0-15, lanes 32-63 the rest.
