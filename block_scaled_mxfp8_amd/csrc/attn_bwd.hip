@@ -212,6 +212,26 @@ __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, i
   const long long ts = token_stride_k<kPacked>(p.heads_q, D);
   const long long off0 = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, hq, q0, 0);
   const int rmax = w.n - 1 - q0;
+  const int glast = ((w.n + 31) >> 5) - 1;
+  // Small items first, as raw bits (dkv_put converts them): their loads then precede the
+  // DMA in the wave's in-order vector-memory queue, so waiting for them (at dkv_put) does
+  // not wait for this step's DMA. Wave 0: Q ROW scales, wave 1: G ROW scales, wave 2: LSE +
+  // Q SEQ scales, wave 3: D + G SEQ scales.
+  const int r = min(lane, rmax);
+  if (wave < 2) {
+    const uint8_t* base = (wave == 0 ? p.q_scales : p.gr_scales) + (off0 >> 5);
+    sv[0] = load_row_scales<D>(base, (uint32_t)(r * (int)ts));
+    sv[1] = 0;
+  } else {
+    const float* f = (wave == 2 ? p.lse : p.delta) + token_index_k<kPacked>(g, p.heads_q, w.s, w.doc_start, hq, q0);
+    sv[0] = __float_as_uint(f[(uint32_t)(r * (kPacked ? p.heads_q : 1))]);
+    // every lane loads (lanes >= d/2 repeat a dword of the lower half and are not stored), so
+    // the load is not divergent and needs no wait before the branches reconverge
+    const int word = lane % (D / 2);
+    const int gi = min((q0 >> 5) + (word * 4) / D, glast);
+    const long long row = seq_group_row_k<kPacked>(g, p.heads_q, w.s, hq, w.doc_start, gi);
+    sv[1] = *reinterpret_cast<const uint32_t*>((wave == 2 ? p.qs_scales : p.gs_scales) + row * D + (word * 4) % D);
+  }
   // ROW tiles
   if (rmax >= kStepQ - 1) {
     const long long wb = off0 + (long long)(NJ * wave * RPI) * ts;
@@ -231,7 +251,6 @@ __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, i
     }
   }
   // SEQ tiles (groups q0/32 and q0/32 + 1, the latter clamped to the last group)
-  const int glast = ((w.n + 31) >> 5) - 1;
 #pragma unroll
   for (int jj = 0; jj < NSJ; jj++) {
     const int j = NSJ * wave + jj;
@@ -241,35 +260,19 @@ __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, i
     lds_dma(p.qs_codes + o + (uint32_t)L.soff, st.qs + j * 1024, 16);
     lds_dma(p.gs_codes + o + (uint32_t)L.soff, st.gs + j * 1024, 16);
   }
-  // small items: wave 0 Q ROW scales, wave 1 G ROW scales, wave 2 LSE + Q SEQ scales,
-  // wave 3 D + G SEQ scales
-  const int r = min(lane, rmax);
-  if (wave < 2) {
-    const uint8_t* base = (wave == 0 ? p.q_scales : p.gr_scales) + (off0 >> 5);
-    sv[0] = load_row_scales<D>(base, (uint32_t)(r * (int)ts));
-    sv[1] = 0;
-  } else {
-    const float* f = (wave == 2 ? p.lse : p.delta) + token_index_k<kPacked>(g, p.heads_q, w.s, w.doc_start, hq, q0);
-    const float x = f[(uint32_t)(r * (kPacked ? p.heads_q : 1))];
-    const bool live = lane <= rmax;
-    sv[0] = __float_as_uint(wave == 2 ? (live ? x * kLog2e : INFINITY) : (live ? x : 0.f));
-    sv[1] = 0;
-    if (lane < D / 2) {
-      const int gi = min((q0 >> 5) + (lane * 4) / D, glast);
-      const long long row = seq_group_row_k<kPacked>(g, p.heads_q, w.s, hq, w.doc_start, gi);
-      sv[1] = *reinterpret_cast<const uint32_t*>((wave == 2 ? p.qs_scales : p.gs_scales) + row * D + (lane * 4) % D);
-    }
-  }
 }
 
+// Store the small items of a step; rows past the end (lane > rmax) get LSE' = +inf, D = 0.
 template <int D>
-__device__ __forceinline__ void dkv_put(DkvStage<D>& st, const uint32_t (&sv)[2]) {
+__device__ __forceinline__ void dkv_put(DkvStage<D>& st, const uint32_t (&sv)[2], int rmax) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   if (wave < 2) {
     (wave == 0 ? st.qrs : st.grs)[lane] = sv[0];
   } else {
-    (wave == 2 ? st.lse2 : st.dlt)[lane] = __uint_as_float(sv[0]);
+    const float x = __uint_as_float(sv[0]);
+    const bool live = lane <= rmax;
+    (wave == 2 ? st.lse2 : st.dlt)[lane] = wave == 2 ? (live ? x * kLog2e : INFINITY) : (live ? x : 0.f);
     if (lane < D / 2) reinterpret_cast<uint32_t*>(wave == 2 ? st.qss : st.gss)[lane] = sv[1];
   }
 }
@@ -279,6 +282,81 @@ __device__ __forceinline__ void dkv_put(DkvStage<D>& st, const uint32_t (&sv)[2]
 __device__ __forceinline__ int p_scale_exp(float amax) {
   const uint32_t b = __float_as_uint(amax);
   return max((int)(b >> 23) - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0), -127);
+}
+
+// Codes of one 64-query step of one wave: P_b (A operand of dV += P_b^T G_seq) and dS (A
+// operand of dK += dS^T Q_seq) with their E8M0 scale operands.
+struct StepCodes {
+  v8i pb, ds;
+  int pbsc, dssc;
+};
+
+// S, E for the two 32-query tiles, P, P_b and dS codes. kMask applies visibility (diagonal
+// and tail steps only, so the common path is straight-line code): element (row r of the
+// step, this lane's key) is visible when r < lim and, under causal, r + rel >= 0, with
+// rel = q0 + 4hh - key and lim = n - q0 - 4hh (the lane's rows are r = 32 qt + 8j + u,
+// u = 0..3, offset by 4hh). The dK/dV accumulators are not touched here, so the masked and
+// unmasked variants merge with only the codes live.
+template <int D, bool kMask>
+__device__ __forceinline__ StepCodes dkv_codes(const DkvStage<D>& S, const v8i* kop, const v8i* vop, uint32_t kvsc,
+                                               const int* roff_ab, int fidx, float c, int rel, int lim, bool kvalid,
+                                               bool causal) {
+  constexpr int NS = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+  StepCodes out;
+  int pbe[2], dse[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++) {
+    const uint32_t qsw = S.qrs[qt * 32 + l32] >> (8 * hh);
+    const uint32_t gsw = S.grs[qt * 32 + l32] >> (8 * hh);
+    v16f sacc = v16f{}, eacc = v16f{};
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+      const int o0 = qt * 32 * D + roff_ab[2 * s], o1 = qt * 32 * D + roff_ab[2 * s + 1];
+      const v8i qa = cat(*reinterpret_cast<const v4i*>(&S.qr[o0]), *reinterpret_cast<const v4i*>(&S.qr[o1]));
+      const v8i ga = cat(*reinterpret_cast<const v4i*>(&S.gr[o0]), *reinterpret_cast<const v4i*>(&S.gr[o1]));
+      sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kop[s], sacc, 0, 0, 0, (int)(qsw >> (16 * s)), 0,
+                                                             (int)(kvsc >> (8 * s)));
+      eacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga, vop[s], eacc, 0, 0, 0, (int)(gsw >> (16 * s)), 0,
+                                                             (int)(kvsc >> (16 + 8 * s)));
+    }
+    // P = 2^(S' - LSE') for the lane's 16 queries (rows 8j + 4hh + u of the tile)
+    float P[16], U[16];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const v4f l4 = *reinterpret_cast<const v4f*>(&S.lse2[qt * 32 + 8 * j + fidx]);
+      const v4f d4 = *reinterpret_cast<const v4f*>(&S.dlt[qt * 32 + 8 * j + fidx]);
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        float x = __builtin_fmaf(sacc[4 * j + u], c, -l4[u]);
+        if (kMask) {
+          const int r = 32 * qt + 8 * j + u;
+          if (!(kvalid && r < lim && (!causal || r + rel >= 0))) x = -INFINITY;
+        }
+        P[4 * j + u] = __builtin_amdgcn_exp2f(x);
+        U[4 * j + u] = P[4 * j + u] * (eacc[4 * j + u] - d4[u]);
+      }
+    }
+    // P_b: 32 queries of this key per group (this lane and lane ^ 32)
+    float pm = max_abs16(P);
+    pm = fmaxf(pm, swap32(pm));
+    pbe[qt] = p_scale_exp(pm);
+    const float psc = exp2_scale(pbe[qt]);
+    // dS: the 32 x 32 block (this wave's keys x the tile's queries)
+    const float um = wave_max(max_abs16(U));
+    dse[qt] = scale_exp_from_bits(__float_as_uint(um));
+    const float usc = exp2_scale(dse[qt]);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      out.pb[4 * qt + j] = (int)pack4_e4m3_scaled(P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3], psc);
+      out.ds[4 * qt + j] = (int)pack4_e4m3_scaled(U[4 * j], U[4 * j + 1], U[4 * j + 2], U[4 * j + 3], usc);
+    }
+  }
+  out.pbsc = (hh ? pbe[1] : pbe[0]) + 127;
+  out.dssc = (hh ? dse[1] : dse[0]) + 127;
+  return out;
 }
 
 // d = 128 needs ~300 registers per lane (dK and dV accumulators alone take 128): one wave
@@ -339,7 +417,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
   const int soff_c = l32 * 32 + (half_swz(l32, hh) << 4);   // SEQ tile, channel l32 of group 0
   const int scoff = hh * D + l32;                            // SEQ scale of channel l32, group hh
   const int fidx = 4 * hh;                                   // LSE / D index of the lane's rows
-  dkv_put<D>(sm[0], sv);
+  dkv_put<D>(sm[0], sv, w.n - 1 - q0);
   wait_vmem();
   __syncthreads();
 
@@ -356,70 +434,24 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(Bw
     // waves whose keys all follow the step's last query (causal) see nothing
     if (kw < w.n && !(p.causal && kw > q0 + kStepQ - 1)) {
       const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.n;
-      v8i pbop, dsop;
-      int pbe[2], dse[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; qt++) {
-        const int row = qt * 32 + l32;
-        const uint32_t qsw = S.qrs[row] >> (8 * hh);
-        const uint32_t gsw = S.grs[row] >> (8 * hh);
-        v16f sacc = v16f{}, eacc = v16f{};
-#pragma unroll
-        for (int s = 0; s < NS; s++) {
-          const int o0 = qt * 32 * D + roff_ab[2 * s], o1 = qt * 32 * D + roff_ab[2 * s + 1];
-          const v8i qa = cat(*reinterpret_cast<const v4i*>(&S.qr[o0]), *reinterpret_cast<const v4i*>(&S.qr[o1]));
-          const v8i ga = cat(*reinterpret_cast<const v4i*>(&S.gr[o0]), *reinterpret_cast<const v4i*>(&S.gr[o1]));
-          sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kop[s], sacc, 0, 0, 0, (int)(qsw >> (16 * s)), 0,
-                                                                 (int)(kvsc >> (8 * s)));
-          eacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga, vop[s], eacc, 0, 0, 0, (int)(gsw >> (16 * s)), 0,
-                                                                 (int)(kvsc >> (16 + 8 * s)));
-        }
-        // P = 2^(S' - LSE') for the lane's 16 queries (rows 8j + 4hh + u of the tile)
-        float P[16], U[16];
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const v4f l4 = *reinterpret_cast<const v4f*>(&S.lse2[qt * 32 + 8 * j + fidx]);
-          const v4f d4 = *reinterpret_cast<const v4f*>(&S.dlt[qt * 32 + 8 * j + fidx]);
-#pragma unroll
-          for (int u = 0; u < 4; u++) {
-            float x = __builtin_fmaf(sacc[4 * j + u], c, -l4[u]);
-            if (need_mask) {
-              const int q = q0 + qt * 32 + 8 * j + 4 * hh + u;
-              if (!(kvalid && q < w.n && (!p.causal || key <= q))) x = -INFINITY;
-            }
-            P[4 * j + u] = __builtin_amdgcn_exp2f(x);
-            U[4 * j + u] = P[4 * j + u] * (eacc[4 * j + u] - d4[u]);
-          }
-        }
-        // P_b: 32 queries of this key per group (this lane and lane ^ 32)
-        float pm = max_abs16(P);
-        pm = fmaxf(pm, swap32(pm));
-        pbe[qt] = p_scale_exp(pm);
-        const float psc = exp2_scale(pbe[qt]);
-        // dS: the 32 x 32 block (this wave's keys x the tile's queries)
-        const float um = wave_max(max_abs16(U));
-        dse[qt] = scale_exp_from_bits(__float_as_uint(um));
-        const float usc = exp2_scale(dse[qt]);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          pbop[4 * qt + j] = (int)pack4_e4m3_scaled(P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3], psc);
-          dsop[4 * qt + j] = (int)pack4_e4m3_scaled(U[4 * j], U[4 * j + 1], U[4 * j + 2], U[4 * j + 3], usc);
-        }
-      }
-      const int pbsc = (hh ? pbe[1] : pbe[0]) + 127;
-      const int dssc = (hh ? dse[1] : dse[0]) + 127;
+      const StepCodes cd =
+          need_mask ? dkv_codes<D, true>(S, kop, vop, kvsc, roff_ab, fidx, c, q0 + 4 * hh - key, w.n - q0 - 4 * hh,
+                                         kvalid, p.causal)
+                    : dkv_codes<D, false>(S, kop, vop, kvsc, roff_ab, fidx, c, 0, 0, true, false);
       // dV += P_b^T G_seq, dK += dS^T Q_seq (rows = the wave's keys, columns = channels)
 #pragma unroll
       for (int t = 0; t < NCT; t++) {
         const int h0 = t * 1024 + soff_c, h1 = D * 32 + t * 1024 + soff_c;   // channel t*32 + l32, groups 0 / 1
         const v8i gb = cat(*reinterpret_cast<const v4i*>(&S.gs[h0]), *reinterpret_cast<const v4i*>(&S.gs[h1]));
         const v8i qb = cat(*reinterpret_cast<const v4i*>(&S.qs[h0]), *reinterpret_cast<const v4i*>(&S.qs[h1]));
-        dv[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pbop, gb, dv[t], 0, 0, 0, pbsc, 0, S.gss[scoff + t * 32]);
-        dk[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(dsop, qb, dk[t], 0, 0, 0, dssc, 0, S.qss[scoff + t * 32]);
+        dv[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cd.pb, gb, dv[t], 0, 0, 0, cd.pbsc, 0,
+                                                                S.gss[scoff + t * 32]);
+        dk[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cd.ds, qb, dk[t], 0, 0, 0, cd.dssc, 0,
+                                                                S.qss[scoff + t * 32]);
       }
     }
     if (more) {
-      dkv_put<D>(sm[buf ^ 1], sv);
+      dkv_put<D>(sm[buf ^ 1], sv, w.n - 1 - q0_n);
       wait_vmem();
       __syncthreads();
     }
