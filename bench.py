@@ -11,12 +11,46 @@ step's wall time (quantisation included). The per-kernel lines come from HIP eve
 the library records immediately around each launch of the named kernel, on its stream.
 
     python bench.py [--steps K] [--warmup W] [--dq f32|f16] [--no-cpu-baseline]
+    python bench.py --pmc-run      # one untimed step + a 1 GiB device copy, for counter runs
+
+`roofline.traffic` is the dK/dV kernel's HBM bytes per launch from rocprofv3 counters
+(FETCH_SIZE and WRITE_SIZE, each scaled by its reading for the 1 GiB copy of --pmc-run),
+stored in profiles/ with the hash of the kernel sources it was measured on; it is reported
+only while those sources are unchanged, else null.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_attn_bwd_dkdv_c3.json")
+# sources that determine the dK/dV kernel's code (hashed to validate recorded counters)
+KERNEL_SOURCES = ["block_scaled_mxfp8_amd/csrc/attn_bwd.hip", "block_scaled_mxfp8_amd/csrc/mx_device.h",
+                  "block_scaled_mxfp8_amd/csrc/mx_layout.h", "block_scaled_mxfp8_amd/csrc/mx_internal.h",
+                  "block_scaled_mxfp8_amd/build.py"]
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per dK/dV launch from the counter record, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return int(rec["fetch_kib"] * rec["fetch_scale"] * 1024 + rec["write_kib"] * rec["write_scale"] * 1024)
 
 PEAK_MXFP8_TFLOPS = 5000.0      # MI355X dense MXFP8 MFMA, AMD's published figure
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
@@ -30,6 +64,7 @@ def parse():
     ap.add_argument("--dq", choices=["f32", "f16"], default="f32", help="dQ accumulation of the timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=10, help="launches averaged per kernel line")
+    ap.add_argument("--pmc-run", action="store_true", help="one untimed step + a 1 GiB copy (counter collection)")
     return ap.parse_args()
 
 
@@ -72,6 +107,16 @@ def main():
         ws[mode] = w
         return o, dq
 
+    if args.pmc_run:
+        step()
+        step()
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        b.copy_(a)          # calibration: 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        print("[bench] pmc run done", file=sys.stderr, flush=True)
+        return
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -180,7 +225,7 @@ def main():
         "roofline": {"kernel": "attn_bwd_dkdv_kernel<128> (backward dK/dV)", "bound": "mfma",
                      "achieved": round(kernels["attn_bwd_dkdv"]["tflops"], 2), "peak": PEAK_MXFP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kernels["attn_bwd_dkdv"]["tflops"] / PEAK_MXFP8_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic()},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(t)

@@ -218,7 +218,8 @@ def mx_quantize(x, views=MX_VIEW_ROW | MX_VIEW_SEQ, cu_seqlens=None, max_seqlen=
     return row, seqv
 
 
-def _desc(q_shape, k_shape, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode=MX_DQ_F32):
+def _desc(q_shape, k_shape, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode=MX_DQ_F32,
+          deterministic=False):
     d = _Desc()
     d.seq = _seq(q_shape, cu_seqlens, max_seqlen)
     d.heads_q, d.head_dim = _heads_dim(q_shape, cu_seqlens)
@@ -229,7 +230,7 @@ def _desc(q_shape, k_shape, cu_seqlens, max_seqlen, causal, softmax_scale, out_d
     d.softmax_scale = float(softmax_scale or 0.0)
     d.out_dtype = _dtype_code(out_dtype)
     d.dq_mode = int(dq_mode)
-    d.deterministic = 0
+    d.deterministic = 1 if deterministic else 0
     return d
 
 
@@ -271,10 +272,10 @@ def mx_attn_workspace_size(q_shape, cu_seqlens=None, max_seqlen=None, heads_kv=N
 
 
 def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype, dq_mode, cu_seqlens,
-         max_seqlen, workspace):
+         max_seqlen, workspace, deterministic=False):
     lib = load()
     qs, ks = tuple(q_row.codes.shape), tuple(k_row.codes.shape)
-    desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode)
+    desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode, deterministic)
     dev = q_row.codes.device
     need = lib.mx_attn_workspace_size(ctypes.byref(desc), 1)
     if workspace is None:
@@ -305,16 +306,19 @@ def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_sca
 
 
 def mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal=True, softmax_scale=0.0,
-                out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32, cu_seqlens=None, max_seqlen=None, workspace=None):
-    """Backward attention -> (dq, dk, dv, workspace). o/lse are the forward's outputs."""
+                out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32, cu_seqlens=None, max_seqlen=None, workspace=None,
+                deterministic=False):
+    """Backward attention -> (dq, dk, dv, workspace). o/lse are the forward's outputs. Results are
+    bitwise reproducible whether or not `deterministic` is set."""
     return _bwd("mx_attn_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype,
-                dq_mode, cu_seqlens, max_seqlen, workspace)
+                dq_mode, cu_seqlens, max_seqlen, workspace, deterministic)
 
 
 def mx_attn_varlen_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, cu_seqlens, max_seqlen=None, causal=True,
-                       softmax_scale=0.0, out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32, workspace=None):
+                       softmax_scale=0.0, out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32, workspace=None,
+                       deterministic=False):
     return _bwd("mx_attn_varlen_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale,
-                out_dtype, dq_mode, cu_seqlens, max_seqlen, workspace)
+                out_dtype, dq_mode, cu_seqlens, max_seqlen, workspace, deterministic)
 
 
 def mx_read_flags(workspace):

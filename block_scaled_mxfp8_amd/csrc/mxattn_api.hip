@@ -62,7 +62,7 @@ mx_status check_desc(const mx_attn_desc* d, mx::Geom* g) {
   if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale)) return MX_E_ARG;
   if (d->dq_mode != MX_DQ_F32 && d->dq_mode != MX_DQ_F16_BOOST) return MX_E_ARG;
   if (!valid_dim(d->head_dim)) return MX_E_UNSUPPORTED;
-  if (d->deterministic != 0) return MX_E_UNSUPPORTED;
+  if (d->deterministic != 0 && d->deterministic != 1) return MX_E_ARG;
   return MX_OK;
 }
 

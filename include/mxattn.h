@@ -102,7 +102,8 @@ typedef struct {
   float softmax_scale;    /* alpha; 0 -> head_dim^-1/2 */
   mx_dtype out_dtype;     /* storage type of O, dQ, dK, dV */
   int32_t dq_mode;        /* MX_DQ_F32 or MX_DQ_F16_BOOST (FP16 partial sums x 2^9) */
-  int32_t deterministic;  /* reserved: must be 0 here */
+  int32_t deterministic;  /* 0 or 1; every call is bitwise reproducible (fixed reduction order, no
+                             atomics), so 1 costs nothing; other values: MX_E_ARG */
   void* workspace;        /* device scratch for mx_attn_bwd (see mx_attn_workspace_size) */
   size_t workspace_bytes;
 } mx_attn_desc;

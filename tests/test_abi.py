@@ -80,7 +80,9 @@ def test_attention_validation_errors(lib):
     assert f(None, v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
     assert f(ctypes.byref(_desc(heads_kv=3)), v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
     assert f(ctypes.byref(_desc(head_dim=80)), v, v, v, FAKE, FAKE, None) == _lib.MX_E_UNSUPPORTED
-    assert f(ctypes.byref(_desc(deterministic=1)), v, v, v, FAKE, FAKE, None) == _lib.MX_E_UNSUPPORTED
+    assert f(ctypes.byref(_desc(deterministic=2)), v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    # deterministic = 1 is accepted: validation proceeds to the next check (null output)
+    assert f(ctypes.byref(_desc(deterministic=1)), v, v, v, None, FAKE, None) == _lib.MX_E_ARG
     assert f(ctypes.byref(_desc(softmax_scale=float("nan"))), v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
     assert f(ctypes.byref(_desc()), _lib._QView(0, FAKE), v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
     assert f(ctypes.byref(_desc()), v, v, v, None, FAKE, None) == _lib.MX_E_ARG
