@@ -199,15 +199,14 @@ __device__ __forceinline__ DkvLane<D> dkv_lane(const BwdParams& p, int lane) {
 }
 
 // Issue the loads of the step (query head hq, queries q0..q0+63) into stage `st`; `sv` gets
-// this thread's small items. Rows past the end are clamped to the last row (finite codes;
-// their LSE is +inf, so their P and U are 0).
+// this thread's small items; `wave` (0..3) is the loading wave's index. Rows past the end are
+// clamped to the last row (finite codes; their LSE is +inf, so their P and U are 0).
 template <int D, bool kPacked>
 __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
-                                          uint32_t (&sv)[2], const DkvLane<D>& L) {
+                                          uint32_t (&sv)[2], const DkvLane<D>& L, int wave) {
   constexpr int NCH = D / 16, NJ = NCH / 4, RPI = 64 / NCH, PER = D / 32, NSJ = D / 64;
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
   const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
   const long long ts = token_stride_k<kPacked>(p.heads_q, D);
   const long long off0 = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, hq, q0, 0);
@@ -215,8 +214,8 @@ __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, i
   const int glast = ((w.n + 31) >> 5) - 1;
   // Small items first, as raw bits (dkv_put converts them): their loads then precede the
   // DMA in the wave's in-order vector-memory queue, so waiting for them (at dkv_put) does
-  // not wait for this step's DMA. Wave 0: Q ROW scales, wave 1: G ROW scales, wave 2: LSE +
-  // Q SEQ scales, wave 3: D + G SEQ scales.
+  // not wait for this step's DMA. Loader 0: Q ROW scales, 1: G ROW scales, 2: LSE + Q SEQ
+  // scales, 3: D + G SEQ scales.
   const int r = min(lane, rmax);
   if (wave < 2) {
     const uint8_t* base = (wave == 0 ? p.q_scales : p.gr_scales) + (off0 >> 5);
@@ -264,9 +263,8 @@ __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, i
 
 // Store the small items of a step; rows past the end (lane > rmax) get LSE' = +inf, D = 0.
 template <int D>
-__device__ __forceinline__ void dkv_put(DkvStage<D>& st, const uint32_t (&sv)[2], int rmax) {
+__device__ __forceinline__ void dkv_put(DkvStage<D>& st, const uint32_t (&sv)[2], int rmax, int wave) {
   const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
   if (wave < 2) {
     (wave == 0 ? st.qrs : st.grs)[lane] = sv[0];
   } else {
@@ -359,104 +357,164 @@ __device__ __forceinline__ StepCodes dkv_codes(const DkvStage<D>& S, const v8i* 
   return out;
 }
 
-// d = 128 needs ~300 registers per lane (dK and dV accumulators alone take 128): one wave
-// per SIMD. d = 64 fits two workgroups per CU.
+// Producer / accumulator split. Waves 0-3 (producers) own keys [32w, 32w + 32) for the S, E,
+// P, U and code work (VALU-heavy, holding the keys' K and V operands); waves 4-7
+// (accumulators) own the same keys' dK and dV and do the dV/dK products and all stage
+// loading. On gfx950 the four waves of a workgroup half map to the four SIMDs, so each SIMD
+// runs one producer and one accumulator over the same keys: one wave's VALU work overlaps
+// the other's MFMAs, and neither needs the registers of both roles (dK + dV alone are 128
+// per lane at d = 128). Codes reach the accumulators through LDS one step later.
+//
+// Iteration j (j = 0..nsteps): accumulators issue the loads of step j + 1 into stage
+// (j+1) % 3; producers turn stage j % 3 into codes in exchange buffer j % 2; accumulators
+// apply the codes of step j - 1 (stage (j-1) % 3, buffer (j-1) % 2); one barrier ends it.
+constexpr int kCodeDw = 18 * 64;            // exchange dwords per key group: 16 code + 2 scale per lane
+
+template <int D>
+struct DkvShared {
+  DkvStage<D> st[3];
+  alignas(16) uint32_t cx[2][kWaves][kCodeDw];
+};
+
+// Exchange layout (per key group): dwords [k*256 + lane*4, +4) hold code chunk k (k = 0, 1:
+// P_b bytes 0-15 / 16-31; k = 2, 3: dS), then [1024 + 2 lane] = P_b scale, [+1] = dS scale.
+__device__ __forceinline__ void put_codes(uint32_t* cx, const StepCodes& c) {
+  const int lane = threadIdx.x & 63;
+  reinterpret_cast<v4i*>(cx)[lane] = v4i{c.pb[0], c.pb[1], c.pb[2], c.pb[3]};
+  reinterpret_cast<v4i*>(cx)[64 + lane] = v4i{c.pb[4], c.pb[5], c.pb[6], c.pb[7]};
+  reinterpret_cast<v4i*>(cx)[128 + lane] = v4i{c.ds[0], c.ds[1], c.ds[2], c.ds[3]};
+  reinterpret_cast<v4i*>(cx)[192 + lane] = v4i{c.ds[4], c.ds[5], c.ds[6], c.ds[7]};
+  reinterpret_cast<v2i*>(cx + 1024)[lane] = v2i{c.pbsc, c.dssc};
+}
+
+__device__ __forceinline__ StepCodes get_codes(const uint32_t* cx) {
+  const int lane = threadIdx.x & 63;
+  StepCodes c;
+  c.pb = cat(reinterpret_cast<const v4i*>(cx)[lane], reinterpret_cast<const v4i*>(cx)[64 + lane]);
+  c.ds = cat(reinterpret_cast<const v4i*>(cx)[128 + lane], reinterpret_cast<const v4i*>(cx)[192 + lane]);
+  const v2i sc = reinterpret_cast<const v2i*>(cx + 1024)[lane];
+  c.pbsc = sc[0];
+  c.dssc = sc[1];
+  return c;
+}
+
+// (head, first query) of step s + 1, given step s
+__device__ __forceinline__ void next_step(int& hq, int& q0, int qfirst, int n) {
+  q0 += kStepQ;
+  if (q0 >= n) {
+    q0 = qfirst;
+    hq++;
+  }
+}
+
 template <int D, bool kPacked>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(BwdParams p) {
-  __shared__ DkvStage<D> sm[2];
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+  __shared__ DkvShared<D> sm;
   const KvWork w = decode_kv<kPacked>(p);
   if (!w.valid) return;
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
+  const int kg = wave & 3;                // key group
   const int hh = lane >> 5;
   const int l32 = lane & 31;
   const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
   const int k0 = w.kb * kBlockK;
-  const int kw = k0 + wave * 32;          // first key of this wave
+  const int kw = k0 + kg * 32;            // first key of this key group
   const int key = kw + l32;               // this lane's key (column of S and E)
-  const bool kvalid = key < w.n;
-  const float c = p.scale * kLog2e;
   constexpr int NS = D / 64;              // contraction steps over d
   constexpr int NCT = D / 32;             // 32-channel tiles
-
   const int group = p.heads_q / p.heads_kv;
   const int qfirst = p.causal ? (k0 / kStepQ) * kStepQ : 0;
   const int nsteps = ((w.n - qfirst + kStepQ - 1) / kStepQ) * group;
-  const DkvLane<D> L = dkv_lane<D, kPacked>(p, lane);
-  int hq = w.hkv * group, q0 = qfirst;    // the step in LDS buffer st & 1
-  uint32_t sv[2];
-  dkv_issue<D, kPacked>(p, w, hq, q0, sm[0], sv, L);
+  // a key group sees nothing in a step whose queries all precede its keys (causal)
+  auto active = [&](int q0) { return kw < w.n && !(p.causal && kw > q0 + kStepQ - 1); };
 
-  // K and V of the lane's key: B operands of S and E, kept in registers
-  // kvsc: byte s = K scale of contraction step s, byte 2 + s = V scale (groups 2s + hh)
-  v8i kop[NS], vop[NS];
-  uint32_t kvsc = 0;
+  if (wave < kWaves) {
+    // ---------------- producer ----------------
+    const bool kvalid = key < w.n;
+    const float c = p.scale * kLog2e;
+    v8i kop[NS], vop[NS];
+    uint32_t kvsc = 0;   // byte s = K scale of contraction step s, byte 2 + s = V scale (groups 2s + hh)
 #pragma unroll
-  for (int s = 0; s < NS; s++) {
-    const long long off = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, w.hkv, min(key, w.n - 1), 64 * s);
-    kop[s] = cat(*reinterpret_cast<const v4i*>(p.k_codes + off + 16 * hh),
-                 *reinterpret_cast<const v4i*>(p.k_codes + off + 32 + 16 * hh));
-    vop[s] = cat(*reinterpret_cast<const v4i*>(p.vr_codes + off + 16 * hh),
-                 *reinterpret_cast<const v4i*>(p.vr_codes + off + 32 + 16 * hh));
-    kvsc |= ((uint32_t)p.k_scales[(off >> 5) + hh] << (8 * s)) | ((uint32_t)p.vr_scales[(off >> 5) + hh] << (16 + 8 * s));
+    for (int s = 0; s < NS; s++) {
+      const long long off = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, w.hkv, min(key, w.n - 1), 64 * s);
+      kop[s] = cat(*reinterpret_cast<const v4i*>(p.k_codes + off + 16 * hh),
+                   *reinterpret_cast<const v4i*>(p.k_codes + off + 32 + 16 * hh));
+      vop[s] = cat(*reinterpret_cast<const v4i*>(p.vr_codes + off + 16 * hh),
+                   *reinterpret_cast<const v4i*>(p.vr_codes + off + 32 + 16 * hh));
+      kvsc |= ((uint32_t)p.k_scales[(off >> 5) + hh] << (8 * s)) |
+              ((uint32_t)p.vr_scales[(off >> 5) + hh] << (16 + 8 * s));
+    }
+    int roff_ab[2 * NS];                  // ROW tile, row l32: chunks 4s + hh and 4s + 2 + hh
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+      roff_ab[2 * s] = l32 * D + (row_swz(l32, 4 * s + hh, D / 16) << 4);
+      roff_ab[2 * s + 1] = l32 * D + (row_swz(l32, 4 * s + 2 + hh, D / 16) << 4);
+    }
+    const int fidx = 4 * hh;              // LSE / D index of the lane's rows
+    __syncthreads();                      // stage 0 loaded
+    int hq = w.hkv * group, q0 = qfirst;
+    for (int j = 0; j <= nsteps; j++) {
+      if (j < nsteps && active(q0)) {
+        const DkvStage<D>& S = sm.st[j % 3];
+        const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.n;
+        const StepCodes cd =
+            need_mask ? dkv_codes<D, true>(S, kop, vop, kvsc, roff_ab, fidx, c, q0 + 4 * hh - key, w.n - q0 - 4 * hh,
+                                           kvalid, p.causal)
+                      : dkv_codes<D, false>(S, kop, vop, kvsc, roff_ab, fidx, c, 0, 0, true, false);
+        put_codes(sm.cx[j & 1][kg], cd);
+      }
+      next_step(hq, q0, qfirst, w.n);
+      __syncthreads();
+    }
+    return;
   }
+
+  // ---------------- accumulator + loader ----------------
+  const int lw = kg;                      // loader index
+  const DkvLane<D> L = dkv_lane<D, kPacked>(p, lane);
+  int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
+  uint32_t sv[2];
+  dkv_issue<D, kPacked>(p, w, hq_l, q0_l, sm.st[0], sv, L, lw);
+  dkv_put<D>(sm.st[0], sv, w.n - 1 - q0_l, lw);
   v16f dk[NCT], dv[NCT];
 #pragma unroll
   for (int t = 0; t < NCT; t++) {
     dk[t] = v16f{};
     dv[t] = v16f{};
   }
-  // lane-constant LDS byte offsets; tile, step and group displacements are immediates
-  int roff_ab[2 * NS];                    // ROW tile, row l32: chunks 4s + hh and 4s + 2 + hh
-#pragma unroll
-  for (int s = 0; s < NS; s++) {
-    roff_ab[2 * s] = l32 * D + (row_swz(l32, 4 * s + hh, D / 16) << 4);
-    roff_ab[2 * s + 1] = l32 * D + (row_swz(l32, 4 * s + 2 + hh, D / 16) << 4);
-  }
   const int soff_c = l32 * 32 + (half_swz(l32, hh) << 4);   // SEQ tile, channel l32 of group 0
   const int scoff = hh * D + l32;                            // SEQ scale of channel l32, group hh
-  const int fidx = 4 * hh;                                   // LSE / D index of the lane's rows
-  dkv_put<D>(sm[0], sv, w.n - 1 - q0);
   wait_vmem();
-  __syncthreads();
-
-  for (int st = 0; st < nsteps; st++) {
-    const int buf = st & 1;
-    int hq_n = hq, q0_n = q0 + kStepQ;
-    if (q0_n >= w.n) {
-      q0_n = qfirst;
-      hq_n++;
-    }
-    const bool more = st + 1 < nsteps;
-    if (more) dkv_issue<D, kPacked>(p, w, hq_n, q0_n, sm[buf ^ 1], sv, L);
-    const DkvStage<D>& S = sm[buf];
-    // waves whose keys all follow the step's last query (causal) see nothing
-    if (kw < w.n && !(p.causal && kw > q0 + kStepQ - 1)) {
-      const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.n;
-      const StepCodes cd =
-          need_mask ? dkv_codes<D, true>(S, kop, vop, kvsc, roff_ab, fidx, c, q0 + 4 * hh - key, w.n - q0 - 4 * hh,
-                                         kvalid, p.causal)
-                    : dkv_codes<D, false>(S, kop, vop, kvsc, roff_ab, fidx, c, 0, 0, true, false);
-      // dV += P_b^T G_seq, dK += dS^T Q_seq (rows = the wave's keys, columns = channels)
+  __syncthreads();                        // stage 0 loaded
+  int q0_a = qfirst;                      // step whose codes are applied (j - 1)
+  for (int j = 0; j <= nsteps; j++) {
+    next_step(hq_l, q0_l, qfirst, w.n);   // step j + 1
+    const bool load = j + 1 < nsteps;
+    if (load) dkv_issue<D, kPacked>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], sv, L, lw);
+    if (j >= 1) {
+      if (active(q0_a)) {
+        const DkvStage<D>& S = sm.st[(j - 1) % 3];
+        const StepCodes cd = get_codes(sm.cx[(j - 1) & 1][kg]);
+        // dV += P_b^T G_seq, dK += dS^T Q_seq (rows = the group's keys, columns = channels)
 #pragma unroll
-      for (int t = 0; t < NCT; t++) {
-        const int h0 = t * 1024 + soff_c, h1 = D * 32 + t * 1024 + soff_c;   // channel t*32 + l32, groups 0 / 1
-        const v8i gb = cat(*reinterpret_cast<const v4i*>(&S.gs[h0]), *reinterpret_cast<const v4i*>(&S.gs[h1]));
-        const v8i qb = cat(*reinterpret_cast<const v4i*>(&S.qs[h0]), *reinterpret_cast<const v4i*>(&S.qs[h1]));
-        dv[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cd.pb, gb, dv[t], 0, 0, 0, cd.pbsc, 0,
-                                                                S.gss[scoff + t * 32]);
-        dk[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cd.ds, qb, dk[t], 0, 0, 0, cd.dssc, 0,
-                                                                S.qss[scoff + t * 32]);
+        for (int t = 0; t < NCT; t++) {
+          const int h0 = t * 1024 + soff_c, h1 = D * 32 + t * 1024 + soff_c;   // channel t*32 + l32
+          const v8i gb = cat(*reinterpret_cast<const v4i*>(&S.gs[h0]), *reinterpret_cast<const v4i*>(&S.gs[h1]));
+          const v8i qb = cat(*reinterpret_cast<const v4i*>(&S.qs[h0]), *reinterpret_cast<const v4i*>(&S.qs[h1]));
+          dv[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cd.pb, gb, dv[t], 0, 0, 0, cd.pbsc, 0,
+                                                                  S.gss[scoff + t * 32]);
+          dk[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cd.ds, qb, dk[t], 0, 0, 0, cd.dssc, 0,
+                                                                  S.qss[scoff + t * 32]);
+        }
       }
+      q0_a += kStepQ;
+      if (q0_a >= w.n) q0_a = qfirst;
     }
-    if (more) {
-      dkv_put<D>(sm[buf ^ 1], sv, w.n - 1 - q0_n);
-      wait_vmem();
-      __syncthreads();
-    }
-    hq = hq_n;
-    q0 = q0_n;
+    if (load) dkv_put<D>(sm.st[(j + 1) % 3], sv, w.n - 1 - q0_l, lw);
+    wait_vmem();
+    __syncthreads();
   }
 
   // ---- epilogue: dK = alpha * acc, dV = acc; accumulator rows = keys, columns = channels ----
@@ -753,8 +811,8 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
     gq = dim3((unsigned)((g.max_seqlen + kBlockQ - 1) / kBlockQ), (unsigned)p.heads_q, (unsigned)g.n_docs);
   }
   int slot = profile_begin(kProfBwdKV, stream);
-  if (packed(g)) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), gkv, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), gkv, dim3(256), 0, stream, p);
+  if (packed(g)) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), gkv, dim3(512), 0, stream, p);
+  else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), gkv, dim3(512), 0, stream, p);
   profile_end(slot, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
