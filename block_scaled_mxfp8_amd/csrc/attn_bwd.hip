@@ -170,45 +170,19 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
   return w;
 }
 
-// Lane-invariant DMA offsets of the dK/dV stage loads. A ROW tile takes NCH = d/16 chunk
-// loads per row, 64/NCH rows per instruction and NCH instructions; wave w issues
-// instructions NJ*w .. NJ*w + NJ - 1 (NJ = NCH/4) of each ROW tile and D/64 of each SEQ tile.
-template <int D>
-struct DkvLane {
-  int cz[D / 64];    // swizzled chunk byte offset of this lane, per instruction of the wave
-  int rlo[D / 64];   // row offset (bytes) inside the wave's rows + cz, for a full tile
-  int lrow;          // row of this lane inside an instruction
-  int soff;          // SEQ tile lane offset
-};
-
-template <int D, bool kPacked>
-__device__ __forceinline__ DkvLane<D> dkv_lane(const BwdParams& p, int lane) {
-  constexpr int NCH = D / 16, NJ = NCH / 4, RPI = 64 / NCH;
-  DkvLane<D> L;
-  L.lrow = lane / NCH;
-  const int ts = (int)token_stride_k<kPacked>(p.heads_q, D);
-#pragma unroll
-  for (int jj = 0; jj < NJ; jj++) {
-    // row of instruction j = NJ*w + jj is j*RPI + lrow; its swizzle depends on j only
-    // through jj (NJ*RPI is a multiple of the swizzle period)
-    L.cz[jj] = row_swz(jj * RPI + L.lrow, lane % NCH, NCH) * 16;
-    L.rlo[jj] = (jj * RPI + L.lrow) * ts + L.cz[jj];
-  }
-  L.soff = seq_tile_lane_off(lane);
-  return L;
-}
-
-// Issue the loads of the step (query head hq, queries q0..q0+63) into stage `st`; `sv` gets
-// this thread's small items; `wave` (0..3) is the loading wave's index. Rows past the end are
-// clamped to the last row (finite codes; their LSE is +inf, so their P and U are 0).
-template <int D, bool kPacked>
+// Issue the loads of the step (query head hq, queries q0..q0+63) into stage `st`, as loader
+// `lw` of NL: ROW-tile and SEQ-tile DMA instructions j = lw, lw + NL, ... (each moves 64 x 16
+// bytes: 64/NCH rows of NCH = d/16 chunks, or 32 channels of one SEQ group), and for loaders
+// 0-3 one small item set in `sv`. Rows past the end are clamped to the last row (finite
+// codes; their LSE is +inf, so their P and U are 0).
+template <int D, bool kPacked, int NL>
 __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
-                                          uint32_t (&sv)[2], const DkvLane<D>& L, int wave) {
-  constexpr int NCH = D / 16, NJ = NCH / 4, RPI = 64 / NCH, PER = D / 32, NSJ = D / 64;
+                                          uint32_t (&sv)[2], int lw) {
+  constexpr int NCH = D / 16, RPI = 64 / NCH, PER = D / 32, NSEQ = 4 * D / 64;
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
   const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
-  const long long ts = token_stride_k<kPacked>(p.heads_q, D);
+  const int ts = (int)token_stride_k<kPacked>(p.heads_q, D);
   const long long off0 = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, hq, q0, 0);
   const int rmax = w.n - 1 - q0;
   const int glast = ((w.n + 31) >> 5) - 1;
@@ -217,61 +191,59 @@ __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, i
   // not wait for this step's DMA. Loader 0: Q ROW scales, 1: G ROW scales, 2: LSE + Q SEQ
   // scales, 3: D + G SEQ scales.
   const int r = min(lane, rmax);
-  if (wave < 2) {
-    const uint8_t* base = (wave == 0 ? p.q_scales : p.gr_scales) + (off0 >> 5);
-    sv[0] = load_row_scales<D>(base, (uint32_t)(r * (int)ts));
+  if (lw < 2) {
+    const uint8_t* base = (lw == 0 ? p.q_scales : p.gr_scales) + (off0 >> 5);
+    sv[0] = load_row_scales<D>(base, (uint32_t)(r * ts));
     sv[1] = 0;
-  } else {
-    const float* f = (wave == 2 ? p.lse : p.delta) + token_index_k<kPacked>(g, p.heads_q, w.s, w.doc_start, hq, q0);
+  } else if (lw < 4) {
+    const float* f = (lw == 2 ? p.lse : p.delta) + token_index_k<kPacked>(g, p.heads_q, w.s, w.doc_start, hq, q0);
     sv[0] = __float_as_uint(f[(uint32_t)(r * (kPacked ? p.heads_q : 1))]);
     // every lane loads (lanes >= d/2 repeat a dword of the lower half and are not stored), so
     // the load is not divergent and needs no wait before the branches reconverge
     const int word = lane % (D / 2);
     const int gi = min((q0 >> 5) + (word * 4) / D, glast);
     const long long row = seq_group_row_k<kPacked>(g, p.heads_q, w.s, hq, w.doc_start, gi);
-    sv[1] = *reinterpret_cast<const uint32_t*>((wave == 2 ? p.qs_scales : p.gs_scales) + row * D + (word * 4) % D);
+    sv[1] = *reinterpret_cast<const uint32_t*>((lw == 2 ? p.qs_scales : p.gs_scales) + row * D + (word * 4) % D);
   }
-  // ROW tiles
-  if (rmax >= kStepQ - 1) {
-    const long long wb = off0 + (long long)(NJ * wave * RPI) * ts;
+  // ROW tiles (Q, G)
+  const int lrow = lane / NCH;
+  const bool full = rmax >= kStepQ - 1;
 #pragma unroll
-    for (int jj = 0; jj < NJ; jj++) {
-      const int j = NJ * wave + jj;
-      lds_dma(p.q_codes + wb + (uint32_t)L.rlo[jj], st.qr + j * 1024, 16);
-      lds_dma(p.gr_codes + wb + (uint32_t)L.rlo[jj], st.gr + j * 1024, 16);
-    }
-  } else {
-#pragma unroll
-    for (int jj = 0; jj < NJ; jj++) {
-      const int j = NJ * wave + jj;
-      const uint32_t vo = (uint32_t)(min(j * RPI + L.lrow, rmax) * (int)ts + L.cz[jj]);
-      lds_dma(p.q_codes + off0 + vo, st.qr + j * 1024, 16);
-      lds_dma(p.gr_codes + off0 + vo, st.gr + j * 1024, 16);
+  for (int j0 = 0; j0 < NCH; j0 += NL) {
+    const int j = j0 + lw;
+    if (NCH % NL == 0 || j < NCH) {
+      const int row = j * RPI + lrow;
+      const int vo = (full ? row : min(row, rmax)) * ts + row_swz(row, lane % NCH, NCH) * 16;
+      lds_dma(p.q_codes + off0 + (uint32_t)vo, st.qr + j * 1024, 16);
+      lds_dma(p.gr_codes + off0 + (uint32_t)vo, st.gr + j * 1024, 16);
     }
   }
   // SEQ tiles (groups q0/32 and q0/32 + 1, the latter clamped to the last group)
+  const int soff = seq_tile_lane_off(lane);
 #pragma unroll
-  for (int jj = 0; jj < NSJ; jj++) {
-    const int j = NSJ * wave + jj;
-    const int grp = min((q0 >> 5) + j / PER, glast);
-    const long long row = seq_group_row_k<kPacked>(g, p.heads_q, w.s, hq, w.doc_start, grp);
-    const long long o = row * (D * 32) + (j % PER) * 1024;
-    lds_dma(p.qs_codes + o + (uint32_t)L.soff, st.qs + j * 1024, 16);
-    lds_dma(p.gs_codes + o + (uint32_t)L.soff, st.gs + j * 1024, 16);
+  for (int j0 = 0; j0 < NSEQ; j0 += NL) {
+    const int j = j0 + lw;
+    if (NSEQ % NL == 0 || j < NSEQ) {
+      const int grp = min((q0 >> 5) + j / PER, glast);
+      const long long row = seq_group_row_k<kPacked>(g, p.heads_q, w.s, hq, w.doc_start, grp);
+      const long long o = row * (D * 32) + (j % PER) * 1024;
+      lds_dma(p.qs_codes + o + (uint32_t)soff, st.qs + j * 1024, 16);
+      lds_dma(p.gs_codes + o + (uint32_t)soff, st.gs + j * 1024, 16);
+    }
   }
 }
 
 // Store the small items of a step; rows past the end (lane > rmax) get LSE' = +inf, D = 0.
 template <int D>
-__device__ __forceinline__ void dkv_put(DkvStage<D>& st, const uint32_t (&sv)[2], int rmax, int wave) {
+__device__ __forceinline__ void dkv_put(DkvStage<D>& st, const uint32_t (&sv)[2], int rmax, int lw) {
   const int lane = threadIdx.x & 63;
-  if (wave < 2) {
-    (wave == 0 ? st.qrs : st.grs)[lane] = sv[0];
-  } else {
+  if (lw < 2) {
+    (lw == 0 ? st.qrs : st.grs)[lane] = sv[0];
+  } else if (lw < 4) {
     const float x = __uint_as_float(sv[0]);
     const bool live = lane <= rmax;
-    (wave == 2 ? st.lse2 : st.dlt)[lane] = wave == 2 ? (live ? x * kLog2e : INFINITY) : (live ? x : 0.f);
-    if (lane < D / 2) reinterpret_cast<uint32_t*>(wave == 2 ? st.qss : st.gss)[lane] = sv[1];
+    (lw == 2 ? st.lse2 : st.dlt)[lane] = lw == 2 ? (live ? x * kLog2e : INFINITY) : (live ? x : 0.f);
+    if (lane < D / 2) reinterpret_cast<uint32_t*>(lw == 2 ? st.qss : st.gss)[lane] = sv[1];
   }
 }
 
@@ -282,121 +254,92 @@ __device__ __forceinline__ int p_scale_exp(float amax) {
   return max((int)(b >> 23) - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0), -127);
 }
 
-// Codes of one 64-query step of one wave: P_b (A operand of dV += P_b^T G_seq) and dS (A
-// operand of dK += dS^T Q_seq) with their E8M0 scale operands.
-struct StepCodes {
-  v8i pb, ds;
-  int pbsc, dssc;
-};
-
-// S, E for the two 32-query tiles, P, P_b and dS codes. kMask applies visibility (diagonal
-// and tail steps only, so the common path is straight-line code): element (row r of the
-// step, this lane's key) is visible when r < lim and, under causal, r + rel >= 0, with
-// rel = q0 + 4hh - key and lim = n - q0 - 4hh (the lane's rows are r = 32 qt + 8j + u,
-// u = 0..3, offset by 4hh). The dK/dV accumulators are not touched here, so the masked and
-// unmasked variants merge with only the codes live.
+// Codes of one 32-query tile qt of a 64-query step for one key group, written to the group's
+// exchange area `cx`: S and E (queries as MFMA rows, the group's 32 keys as columns),
+// P = 2^(S' - LSE'), U = P (E - D), P_b codes (the 32 queries of each key: this lane and lane
+// ^ 32) and dS codes (the 32 x 32 block). kMask applies visibility (diagonal and tail steps
+// only): element (row r of the step, this lane's key) is visible when r < lim and, under
+// causal, r + rel >= 0, with rel = q0 + 4hh - key and lim = n - q0 - 4hh (the lane's rows
+// are r = 32 qt + 8j + u, u = 0..3, offset by 4hh).
+//
+// Exchange layout per key group (dwords): chunk k at [64 k + lane] (v4 units): k = qt holds
+// the P_b codes of tile qt (operand bytes 16 qt .. 16 qt + 15), k = 2 + qt the dS codes; at
+// 1024 + 128 qt + 2 lane: the P_b exponent of the lane's key for tile qt, then the tile's dS
+// exponent.
 template <int D, bool kMask>
-__device__ __forceinline__ StepCodes dkv_codes(const DkvStage<D>& S, const v8i* kop, const v8i* vop, uint32_t kvsc,
-                                               const int* roff_ab, int fidx, float c, int rel, int lim, bool kvalid,
-                                               bool causal) {
+__device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, const v8i* kop, const v8i* vop,
+                                               uint32_t kvsc, const int* roff_ab, int fidx, float c, int rel, int lim,
+                                               bool kvalid, bool causal, uint32_t* cx) {
   constexpr int NS = D / 64;
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
   const int l32 = lane & 31;
-  StepCodes out;
-  int pbe[2], dse[2];
+  const uint32_t qsw = S.qrs[qt * 32 + l32] >> (8 * hh);
+  const uint32_t gsw = S.grs[qt * 32 + l32] >> (8 * hh);
+  v16f sacc = v16f{}, eacc = v16f{};
 #pragma unroll
-  for (int qt = 0; qt < 2; qt++) {
-    const uint32_t qsw = S.qrs[qt * 32 + l32] >> (8 * hh);
-    const uint32_t gsw = S.grs[qt * 32 + l32] >> (8 * hh);
-    v16f sacc = v16f{}, eacc = v16f{};
+  for (int s = 0; s < NS; s++) {
+    const int o0 = qt * 32 * D + roff_ab[2 * s], o1 = qt * 32 * D + roff_ab[2 * s + 1];
+    const v8i qa = cat(*reinterpret_cast<const v4i*>(&S.qr[o0]), *reinterpret_cast<const v4i*>(&S.qr[o1]));
+    const v8i ga = cat(*reinterpret_cast<const v4i*>(&S.gr[o0]), *reinterpret_cast<const v4i*>(&S.gr[o1]));
+    sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kop[s], sacc, 0, 0, 0, (int)(qsw >> (16 * s)), 0,
+                                                           (int)(kvsc >> (8 * s)));
+    eacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga, vop[s], eacc, 0, 0, 0, (int)(gsw >> (16 * s)), 0,
+                                                           (int)(kvsc >> (16 + 8 * s)));
+  }
+  float P[16], U[16];
 #pragma unroll
-    for (int s = 0; s < NS; s++) {
-      const int o0 = qt * 32 * D + roff_ab[2 * s], o1 = qt * 32 * D + roff_ab[2 * s + 1];
-      const v8i qa = cat(*reinterpret_cast<const v4i*>(&S.qr[o0]), *reinterpret_cast<const v4i*>(&S.qr[o1]));
-      const v8i ga = cat(*reinterpret_cast<const v4i*>(&S.gr[o0]), *reinterpret_cast<const v4i*>(&S.gr[o1]));
-      sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kop[s], sacc, 0, 0, 0, (int)(qsw >> (16 * s)), 0,
-                                                             (int)(kvsc >> (8 * s)));
-      eacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga, vop[s], eacc, 0, 0, 0, (int)(gsw >> (16 * s)), 0,
-                                                             (int)(kvsc >> (16 + 8 * s)));
-    }
-    // P = 2^(S' - LSE') for the lane's 16 queries (rows 8j + 4hh + u of the tile)
-    float P[16], U[16];
+  for (int j = 0; j < 4; j++) {
+    const v4f l4 = *reinterpret_cast<const v4f*>(&S.lse2[qt * 32 + 8 * j + fidx]);
+    const v4f d4 = *reinterpret_cast<const v4f*>(&S.dlt[qt * 32 + 8 * j + fidx]);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const v4f l4 = *reinterpret_cast<const v4f*>(&S.lse2[qt * 32 + 8 * j + fidx]);
-      const v4f d4 = *reinterpret_cast<const v4f*>(&S.dlt[qt * 32 + 8 * j + fidx]);
-#pragma unroll
-      for (int u = 0; u < 4; u++) {
-        float x = __builtin_fmaf(sacc[4 * j + u], c, -l4[u]);
-        if (kMask) {
-          const int r = 32 * qt + 8 * j + u;
-          if (!(kvalid && r < lim && (!causal || r + rel >= 0))) x = -INFINITY;
-        }
-        P[4 * j + u] = __builtin_amdgcn_exp2f(x);
-        U[4 * j + u] = P[4 * j + u] * (eacc[4 * j + u] - d4[u]);
+    for (int u = 0; u < 4; u++) {
+      float x = __builtin_fmaf(sacc[4 * j + u], c, -l4[u]);
+      if (kMask) {
+        const int r = 32 * qt + 8 * j + u;
+        if (!(kvalid && r < lim && (!causal || r + rel >= 0))) x = -INFINITY;
       }
-    }
-    // P_b: 32 queries of this key per group (this lane and lane ^ 32)
-    float pm = max_abs16(P);
-    pm = fmaxf(pm, swap32(pm));
-    pbe[qt] = p_scale_exp(pm);
-    const float psc = exp2_scale(pbe[qt]);
-    // dS: the 32 x 32 block (this wave's keys x the tile's queries)
-    const float um = wave_max(max_abs16(U));
-    dse[qt] = scale_exp_from_bits(__float_as_uint(um));
-    const float usc = exp2_scale(dse[qt]);
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      out.pb[4 * qt + j] = (int)pack4_e4m3_scaled(P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3], psc);
-      out.ds[4 * qt + j] = (int)pack4_e4m3_scaled(U[4 * j], U[4 * j + 1], U[4 * j + 2], U[4 * j + 3], usc);
+      P[4 * j + u] = __builtin_amdgcn_exp2f(x);
+      U[4 * j + u] = P[4 * j + u] * (eacc[4 * j + u] - d4[u]);
     }
   }
-  out.pbsc = (hh ? pbe[1] : pbe[0]) + 127;
-  out.dssc = (hh ? dse[1] : dse[0]) + 127;
-  return out;
+  float pm = max_abs16(P);
+  pm = fmaxf(pm, swap32(pm));
+  const int pbe = p_scale_exp(pm);
+  const float psc = exp2_scale(pbe);
+  const int dse = scale_exp_from_bits(__float_as_uint(wave_max(max_abs16(U))));
+  const float usc = exp2_scale(dse);
+  v4i pb, ds;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    pb[j] = (int)pack4_e4m3_scaled(P[4 * j], P[4 * j + 1], P[4 * j + 2], P[4 * j + 3], psc);
+    ds[j] = (int)pack4_e4m3_scaled(U[4 * j], U[4 * j + 1], U[4 * j + 2], U[4 * j + 3], usc);
+  }
+  reinterpret_cast<v4i*>(cx)[qt * 64 + lane] = pb;
+  reinterpret_cast<v4i*>(cx)[(2 + qt) * 64 + lane] = ds;
+  reinterpret_cast<v2i*>(cx + 1024 + 128 * qt)[lane] = v2i{pbe, dse};
 }
 
-// Producer / accumulator split. Waves 0-3 (producers) own keys [32w, 32w + 32) for the S, E,
-// P, U and code work (VALU-heavy, holding the keys' K and V operands); waves 4-7
-// (accumulators) own the same keys' dK and dV and do the dV/dK products and all stage
-// loading. On gfx950 the four waves of a workgroup half map to the four SIMDs, so each SIMD
-// runs one producer and one accumulator over the same keys: one wave's VALU work overlaps
-// the other's MFMAs, and neither needs the registers of both roles (dK + dV alone are 128
-// per lane at d = 128). Codes reach the accumulators through LDS one step later.
+// Producer / accumulator split, 12 waves. Waves 0-7 are producers: wave w computes the codes
+// of query tile w >> 2 for key group w & 3 (VALU-heavy, holding the group's K and V
+// operands) and loads stages; waves 8-11 are accumulators: wave 8 + k holds key group k's dK
+// and dV and applies the codes one step later (codes pass through an LDS exchange buffer).
+// The waves of a workgroup go round-robin to the four SIMDs, so each SIMD runs two producers
+// and one accumulator of the same key group: the producers' VALU work overlaps each other's
+// latencies and the accumulator's MFMAs, and each role fits three waves per SIMD.
 //
-// Iteration j (j = 0..nsteps): accumulators issue the loads of step j + 1 into stage
-// (j+1) % 3; producers turn stage j % 3 into codes in exchange buffer j % 2; accumulators
-// apply the codes of step j - 1 (stage (j-1) % 3, buffer (j-1) % 2); one barrier ends it.
-constexpr int kCodeDw = 18 * 64;            // exchange dwords per key group: 16 code + 2 scale per lane
+// Iteration j (j = 0..nsteps): producers issue the loads of step j + 1 into stage (j+1) % 3
+// and turn stage j % 3 into codes in exchange buffer j % 2; accumulators apply the codes of
+// step j - 1 (stage (j-1) % 3, buffer (j-1) % 2); one barrier ends the iteration.
+constexpr int kDkvProducers = 2 * kWaves;
+constexpr int kDkvThreads = 64 * (kDkvProducers + kWaves);
+constexpr int kCodeDw = 1280;               // exchange dwords per key group
 
 template <int D>
 struct DkvShared {
   DkvStage<D> st[3];
   alignas(16) uint32_t cx[2][kWaves][kCodeDw];
 };
-
-// Exchange layout (per key group): dwords [k*256 + lane*4, +4) hold code chunk k (k = 0, 1:
-// P_b bytes 0-15 / 16-31; k = 2, 3: dS), then [1024 + 2 lane] = P_b scale, [+1] = dS scale.
-__device__ __forceinline__ void put_codes(uint32_t* cx, const StepCodes& c) {
-  const int lane = threadIdx.x & 63;
-  reinterpret_cast<v4i*>(cx)[lane] = v4i{c.pb[0], c.pb[1], c.pb[2], c.pb[3]};
-  reinterpret_cast<v4i*>(cx)[64 + lane] = v4i{c.pb[4], c.pb[5], c.pb[6], c.pb[7]};
-  reinterpret_cast<v4i*>(cx)[128 + lane] = v4i{c.ds[0], c.ds[1], c.ds[2], c.ds[3]};
-  reinterpret_cast<v4i*>(cx)[192 + lane] = v4i{c.ds[4], c.ds[5], c.ds[6], c.ds[7]};
-  reinterpret_cast<v2i*>(cx + 1024)[lane] = v2i{c.pbsc, c.dssc};
-}
-
-__device__ __forceinline__ StepCodes get_codes(const uint32_t* cx) {
-  const int lane = threadIdx.x & 63;
-  StepCodes c;
-  c.pb = cat(reinterpret_cast<const v4i*>(cx)[lane], reinterpret_cast<const v4i*>(cx)[64 + lane]);
-  c.ds = cat(reinterpret_cast<const v4i*>(cx)[128 + lane], reinterpret_cast<const v4i*>(cx)[192 + lane]);
-  const v2i sc = reinterpret_cast<const v2i*>(cx + 1024)[lane];
-  c.pbsc = sc[0];
-  c.dssc = sc[1];
-  return c;
-}
 
 // (head, first query) of step s + 1, given step s
 __device__ __forceinline__ void next_step(int& hq, int& q0, int qfirst, int n) {
@@ -408,7 +351,7 @@ __device__ __forceinline__ void next_step(int& hq, int& q0, int qfirst, int n) {
 }
 
 template <int D, bool kPacked>
-__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ DkvShared<D> sm;
   const KvWork w = decode_kv<kPacked>(p);
   if (!w.valid) return;
@@ -430,8 +373,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   // a key group sees nothing in a step whose queries all precede its keys (causal)
   auto active = [&](int q0) { return kw < w.n && !(p.causal && kw > q0 + kStepQ - 1); };
 
-  if (wave < kWaves) {
-    // ---------------- producer ----------------
+  if (wave < kDkvProducers) {
+    // ---------------- producer + loader ----------------
+    const int qt = wave >> 2;
+    const int lw = wave;                  // loader index
     const bool kvalid = key < w.n;
     const float c = p.scale * kLog2e;
     v8i kop[NS], vop[NS];
@@ -453,31 +398,40 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       roff_ab[2 * s + 1] = l32 * D + (row_swz(l32, 4 * s + 2 + hh, D / 16) << 4);
     }
     const int fidx = 4 * hh;              // LSE / D index of the lane's rows
+    int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
+    uint32_t sv[2] = {0, 0};
+    dkv_issue<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[0], sv, lw);
+    dkv_put<D>(sm.st[0], sv, w.n - 1 - q0_l, lw);
+    wait_vmem();
     __syncthreads();                      // stage 0 loaded
-    int hq = w.hkv * group, q0 = qfirst;
+    int q0 = qfirst;                      // step whose codes are computed (j)
     for (int j = 0; j <= nsteps; j++) {
+      next_step(hq_l, q0_l, qfirst, w.n);  // step j + 1
+      const bool load = j + 1 < nsteps;
+      if (load) dkv_issue<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], sv, lw);
       if (j < nsteps && active(q0)) {
         const DkvStage<D>& S = sm.st[j % 3];
+        uint32_t* cx = sm.cx[j & 1][kg];
         const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.n;
-        const StepCodes cd =
-            need_mask ? dkv_codes<D, true>(S, kop, vop, kvsc, roff_ab, fidx, c, q0 + 4 * hh - key, w.n - q0 - 4 * hh,
-                                           kvalid, p.causal)
-                      : dkv_codes<D, false>(S, kop, vop, kvsc, roff_ab, fidx, c, 0, 0, true, false);
-        put_codes(sm.cx[j & 1][kg], cd);
+        if (need_mask)
+          dkv_codes_tile<D, true>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, q0 + 4 * hh - key, w.n - q0 - 4 * hh,
+                                  kvalid, p.causal, cx);
+        else
+          dkv_codes_tile<D, false>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, 0, 0, true, false, cx);
       }
-      next_step(hq, q0, qfirst, w.n);
+      if (load) dkv_put<D>(sm.st[(j + 1) % 3], sv, w.n - 1 - q0_l, lw);
+      q0 += kStepQ;
+      if (q0 >= w.n) q0 = qfirst;
+      wait_vmem();
       __syncthreads();
     }
     return;
   }
 
-  // ---------------- accumulator + loader ----------------
-  const int lw = kg;                      // loader index
-  const DkvLane<D> L = dkv_lane<D, kPacked>(p, lane);
-  int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
-  uint32_t sv[2];
-  dkv_issue<D, kPacked>(p, w, hq_l, q0_l, sm.st[0], sv, L, lw);
-  dkv_put<D>(sm.st[0], sv, w.n - 1 - q0_l, lw);
+  // ---------------- accumulator ----------------
+  // dV^T += G_seq^T P_b and dK^T += Q_seq^T dS: channels are MFMA rows (A = the SEQ tile), the
+  // group's keys columns (B = the codes), so each lane ends with 4 consecutive channels per
+  // accumulator quad of its key, stored as one 8- or 16-byte write.
   v16f dk[NCT], dv[NCT];
 #pragma unroll
   for (int t = 0; t < NCT; t++) {
@@ -486,53 +440,54 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   }
   const int soff_c = l32 * 32 + (half_swz(l32, hh) << 4);   // SEQ tile, channel l32 of group 0
   const int scoff = hh * D + l32;                            // SEQ scale of channel l32, group hh
-  wait_vmem();
   __syncthreads();                        // stage 0 loaded
   int q0_a = qfirst;                      // step whose codes are applied (j - 1)
   for (int j = 0; j <= nsteps; j++) {
-    next_step(hq_l, q0_l, qfirst, w.n);   // step j + 1
-    const bool load = j + 1 < nsteps;
-    if (load) dkv_issue<D, kPacked>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], sv, L, lw);
     if (j >= 1) {
       if (active(q0_a)) {
         const DkvStage<D>& S = sm.st[(j - 1) % 3];
-        const StepCodes cd = get_codes(sm.cx[(j - 1) & 1][kg]);
-        // dV += P_b^T G_seq, dK += dS^T Q_seq (rows = the group's keys, columns = channels)
+        const uint32_t* cx = sm.cx[(j - 1) & 1][kg];
+        const v8i pb = cat(reinterpret_cast<const v4i*>(cx)[lane], reinterpret_cast<const v4i*>(cx)[64 + lane]);
+        const v8i ds = cat(reinterpret_cast<const v4i*>(cx)[128 + lane], reinterpret_cast<const v4i*>(cx)[192 + lane]);
+        const v2i e = reinterpret_cast<const v2i*>(cx + 1024 + 128 * hh)[lane];   // exponents of tile hh
+        const int pbsc = e[0] + 127, dssc = e[1] + 127;
 #pragma unroll
         for (int t = 0; t < NCT; t++) {
           const int h0 = t * 1024 + soff_c, h1 = D * 32 + t * 1024 + soff_c;   // channel t*32 + l32
-          const v8i gb = cat(*reinterpret_cast<const v4i*>(&S.gs[h0]), *reinterpret_cast<const v4i*>(&S.gs[h1]));
-          const v8i qb = cat(*reinterpret_cast<const v4i*>(&S.qs[h0]), *reinterpret_cast<const v4i*>(&S.qs[h1]));
-          dv[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cd.pb, gb, dv[t], 0, 0, 0, cd.pbsc, 0,
-                                                                  S.gss[scoff + t * 32]);
-          dk[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cd.ds, qb, dk[t], 0, 0, 0, cd.dssc, 0,
-                                                                  S.qss[scoff + t * 32]);
+          const v8i ga = cat(*reinterpret_cast<const v4i*>(&S.gs[h0]), *reinterpret_cast<const v4i*>(&S.gs[h1]));
+          const v8i qa = cat(*reinterpret_cast<const v4i*>(&S.qs[h0]), *reinterpret_cast<const v4i*>(&S.qs[h1]));
+          dv[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga, pb, dv[t], 0, 0, 0, S.gss[scoff + t * 32], 0,
+                                                                  pbsc);
+          dk[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, ds, dk[t], 0, 0, 0, S.qss[scoff + t * 32], 0,
+                                                                  dssc);
         }
       }
       q0_a += kStepQ;
       if (q0_a >= w.n) q0_a = qfirst;
     }
-    if (load) dkv_put<D>(sm.st[(j + 1) % 3], sv, w.n - 1 - q0_l, lw);
-    wait_vmem();
     __syncthreads();
   }
 
-  // ---- epilogue: dK = alpha * acc, dV = acc; accumulator rows = keys, columns = channels ----
+  // ---- epilogue: dK = alpha * acc, dV = acc; lane = key kw + l32, quad b4 of tile t = channels
+  //      t*32 + 8 b4 + 4 hh .. +3 ----
+  if (key < w.n) {
+    const long long base = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, w.hkv, key, 0) + 4 * hh;
 #pragma unroll
-  for (int t = 0; t < NCT; t++) {
-    const int ch = t * 32 + l32;
+    for (int t = 0; t < NCT; t++) {
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int kk = kw + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (kk < w.n) {
-        const long long off = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, w.hkv, kk, ch);
-        const float vk = dk[t][i] * p.scale, vv = dv[t][i];
+      for (int b4 = 0; b4 < 4; b4++) {
+        const long long off = base + t * 32 + 8 * b4;
+        const float k0v = dk[t][4 * b4] * p.scale, k1v = dk[t][4 * b4 + 1] * p.scale;
+        const float k2v = dk[t][4 * b4 + 2] * p.scale, k3v = dk[t][4 * b4 + 3] * p.scale;
         if (p.out_f32) {
-          static_cast<float*>(p.dk)[off] = vk;
-          static_cast<float*>(p.dv)[off] = vv;
+          *reinterpret_cast<v4f*>(static_cast<float*>(p.dk) + off) = v4f{k0v, k1v, k2v, k3v};
+          *reinterpret_cast<v4f*>(static_cast<float*>(p.dv) + off) =
+              v4f{dv[t][4 * b4], dv[t][4 * b4 + 1], dv[t][4 * b4 + 2], dv[t][4 * b4 + 3]};
         } else {
-          static_cast<uint16_t*>(p.dk)[off] = (uint16_t)float_to_bf16_bits(vk);
-          static_cast<uint16_t*>(p.dv)[off] = (uint16_t)float_to_bf16_bits(vv);
+          *reinterpret_cast<v2i*>(static_cast<uint16_t*>(p.dk) + off) =
+              v2i{(int)pack2_bf16(k0v, k1v), (int)pack2_bf16(k2v, k3v)};
+          *reinterpret_cast<v2i*>(static_cast<uint16_t*>(p.dv) + off) =
+              v2i{(int)pack2_bf16(dv[t][4 * b4], dv[t][4 * b4 + 1]), (int)pack2_bf16(dv[t][4 * b4 + 2], dv[t][4 * b4 + 3])};
         }
       }
     }
@@ -811,8 +766,8 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
     gq = dim3((unsigned)((g.max_seqlen + kBlockQ - 1) / kBlockQ), (unsigned)p.heads_q, (unsigned)g.n_docs);
   }
   int slot = profile_begin(kProfBwdKV, stream);
-  if (packed(g)) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), gkv, dim3(512), 0, stream, p);
-  else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), gkv, dim3(512), 0, stream, p);
+  if (packed(g)) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+  else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), gkv, dim3(kDkvThreads), 0, stream, p);
   profile_end(slot, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

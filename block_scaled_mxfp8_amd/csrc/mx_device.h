@@ -78,6 +78,13 @@ __device__ __forceinline__ uint32_t pack4_e4m3_scaled(float a, float b, float c,
   return __builtin_bit_cast(uint32_t, w);
 }
 
+// Two floats -> packed bf16 pair (low half = a), RNE (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, bf2));
+}
+
 // Exchange with the lane 32 positions away (lane ^ 32) via v_permlane32_swap.
 __device__ __forceinline__ float swap32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
