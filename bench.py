@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=10, help="launches averaged per kernel line")
     ap.add_argument("--pmc-run", action="store_true", help="one untimed step + a 1 GiB copy (counter collection)")
+    ap.add_argument("--recompute-dq", action="store_true",
+                    help="minimal workspace: the dQ pass rebuilds dS instead of reading the stored codes")
     return ap.parse_args()
 
 
@@ -99,11 +101,13 @@ def main():
     def quant():
         return mx_quantize(t["q"]), mx_quantize(t["k"]), mx_quantize(t["v"])
 
+    ds_store = not args.recompute_dq
+
     def step(mode=dq_mode):
         (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
         o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=True)
         dq, dk, dv, w = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=True, dq_mode=mode,
-                                    workspace=ws.get(mode))
+                                    workspace=ws.get(mode), ds_store=ds_store)
         ws[mode] = w
         return o, dq
 
@@ -159,7 +163,7 @@ def main():
 
     def bwd(mode):
         return lambda: mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=True, dq_mode=mode,
-                                   workspace=ws.get(mode))
+                                   workspace=ws.get(mode), ds_store=ds_store)
 
     res_bwd = {}
     for name, mode in (("f32", MX_DQ_F32), ("f16", MX_DQ_F16_BOOST)):
@@ -183,9 +187,12 @@ def main():
     quant_bytes = q_elems * (2 + 2 * (1 + 1 / 32))          # bf16 in, two views of codes + scales out
     tflops = lambda f, ms: f / (ms * 1e-3) / 1e12          # noqa: E731
     # algorithmic FLOPs per kernel: dK/dV kernel S, E, dV, dK (4 of the 5 products, 8 d per
-    # visible pair); dQ kernel dQ (2 d) plus the S and E it rebuilds (4 d, not counted in the
-    # step's FLOPs, which follow the method's 10 d per pair)
+    # visible pair); dQ kernel dQ (2 d; the recomputing variant also rebuilds S and E, 4 d more,
+    # not counted in the step's FLOPs, which follow the method's 10 d per pair)
     f_dkdv = f_bwd * 4 // 5
+    # dQ from the store reads the stored 32 x 32 blocks once (1024 code bytes + 1 exponent each)
+    nb = (L + 31) // 32
+    ds_bytes = B * H * nb * (nb + 1) // 2 * 1025
     kernels = {
         "attn_fwd": dict(ms=ms_fwd, tflops=tflops(f_fwd, ms_fwd)),
         "attn_bwd_dkdv": dict(ms=ms_bwd_main, tflops=tflops(f_dkdv, ms_bwd_main)),
@@ -207,7 +214,8 @@ def main():
         "dtype": "mxfp8",
         "data": "synthetic",
         "config": {"workload": "c3: B4 H32 L4096 d128 causal, bf16 N(0,1) inputs, step = quantise Q/K/V + fwd + bwd",
-                   "batch": B, "heads": H, "seqlen": L, "head_dim": d, "causal": True, "dq": args.dq},
+                   "batch": B, "heads": H, "seqlen": L, "head_dim": d, "causal": True, "dq": args.dq,
+                   "dq_pass": "rebuilds dS" if args.recompute_dq else "reads stored dS codes"},
         "pct_of_peak": round(100 * tflops(f_fwd + f_bwd, ms_step) / PEAK_MXFP8_TFLOPS, 2),
         "fwd_tflops": round(tflops(f_fwd, ms_fwd), 2),
         "fwd_pct_of_peak": round(100 * tflops(f_fwd, ms_fwd) / PEAK_MXFP8_TFLOPS, 2),
@@ -216,6 +224,7 @@ def main():
         "bwd_f16dq_tflops": round(tflops(f_bwd, bwd_f16["call_ms"]), 2),
         "bwd_f16dq_pct_of_peak": round(100 * tflops(f_bwd, bwd_f16["call_ms"]) / PEAK_MXFP8_TFLOPS, 2),
         "quantize_gbs": round(kernels["quantize"]["gbs"], 1),
+        "dq_store_read_gbs": None if args.recompute_dq else round(ds_bytes / (bwd_f32["dq_ms"] * 1e-3) / 1e9, 1),
         "kernels_ms": {"attn_fwd": round(ms_fwd, 4), "attn_bwd_dkdv": round(bwd_f32["dkdv_ms"], 4),
                        "attn_bwd_dq_f32": round(bwd_f32["dq_ms"], 4), "attn_bwd_dq_f16": round(bwd_f16["dq_ms"], 4),
                        "bwd_prep": round(bwd_f32["prep_ms"], 4), "quantize_one_tensor": round(ms_quant, 4)},

@@ -262,24 +262,27 @@ def mx_attn_varlen_fwd(q_row, k_row, v_seq, cu_seqlens, max_seqlen=None, causal=
     return _fwd("mx_attn_varlen_fwd", q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen)
 
 
-def mx_attn_workspace_size(q_shape, cu_seqlens=None, max_seqlen=None, heads_kv=None, dq_mode=MX_DQ_F32):
+def mx_attn_workspace_size(q_shape, cu_seqlens=None, max_seqlen=None, heads_kv=None, dq_mode=MX_DQ_F32,
+                           causal=True, ds_store=True):
+    """Backward workspace bytes; ds_store=True includes the dS code store (O(L^2) bytes)."""
     lib = load()
     k_shape = list(q_shape)
     if heads_kv is not None:
         k_shape[-3 if cu_seqlens is None else -2] = heads_kv
-    desc = _desc(tuple(q_shape), tuple(k_shape), cu_seqlens, max_seqlen, True, 0.0, torch.bfloat16, dq_mode)
-    return lib.mx_attn_workspace_size(ctypes.byref(desc), 1)
+    desc = _desc(tuple(q_shape), tuple(k_shape), cu_seqlens, max_seqlen, causal, 0.0, torch.bfloat16, dq_mode)
+    return lib.mx_attn_workspace_size(ctypes.byref(desc), 2 if ds_store else 1)
 
 
 def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype, dq_mode, cu_seqlens,
-         max_seqlen, workspace, deterministic=False):
+         max_seqlen, workspace, deterministic=False, ds_store=True):
     lib = load()
     qs, ks = tuple(q_row.codes.shape), tuple(k_row.codes.shape)
     desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode, deterministic)
     dev = q_row.codes.device
     need = lib.mx_attn_workspace_size(ctypes.byref(desc), 1)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        size = lib.mx_attn_workspace_size(ctypes.byref(desc), 2) if ds_store else need
+        workspace = torch.empty(size, dtype=torch.uint8, device=dev)
     elif _nbytes(workspace) < need or not workspace.is_cuda:
         raise ValueError(f"workspace needs {need} bytes")
     desc.workspace = workspace.data_ptr()
@@ -307,18 +310,20 @@ def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_sca
 
 def mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal=True, softmax_scale=0.0,
                 out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32, cu_seqlens=None, max_seqlen=None, workspace=None,
-                deterministic=False):
+                deterministic=False, ds_store=True):
     """Backward attention -> (dq, dk, dv, workspace). o/lse are the forward's outputs. Results are
-    bitwise reproducible whether or not `deterministic` is set."""
+    bitwise reproducible whether or not `deterministic` is set. Without a `workspace` one is
+    allocated: with the dS code store (faster dQ pass, O(L^2) bytes) when ds_store is true, else
+    the minimum. A given workspace selects the store by its size (mx_attn_workspace_size)."""
     return _bwd("mx_attn_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype,
-                dq_mode, cu_seqlens, max_seqlen, workspace, deterministic)
+                dq_mode, cu_seqlens, max_seqlen, workspace, deterministic, ds_store)
 
 
 def mx_attn_varlen_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, cu_seqlens, max_seqlen=None, causal=True,
                        softmax_scale=0.0, out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32, workspace=None,
-                       deterministic=False):
+                       deterministic=False, ds_store=True):
     return _bwd("mx_attn_varlen_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale,
-                out_dtype, dq_mode, cu_seqlens, max_seqlen, workspace, deterministic)
+                out_dtype, dq_mode, cu_seqlens, max_seqlen, workspace, deterministic, ds_store)
 
 
 def mx_read_flags(workspace):

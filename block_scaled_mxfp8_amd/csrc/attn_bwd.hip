@@ -263,13 +263,13 @@ __device__ __forceinline__ int p_scale_exp(float amax) {
 // are r = 32 qt + 8j + u, u = 0..3, offset by 4hh).
 //
 // Exchange layout per key group (dwords): chunk k at [64 k + lane] (v4 units): k = qt holds
-// the P_b codes of tile qt (operand bytes 16 qt .. 16 qt + 15), k = 2 + qt the dS codes; at
-// 1024 + 128 qt + 2 lane: the P_b exponent of the lane's key for tile qt, then the tile's dS
-// exponent.
+// the P_b codes of tile qt (operand bytes 16 qt .. 16 qt + 15); k = 2 + qt holds the dS codes
+// of tile qt, the lane's 16 bytes at the swizzled slot ds_slot_off(lane); at 1024 + 128 qt +
+// 2 lane: the P_b exponent of the lane's key for tile qt, then the tile's dS exponent.
 template <int D, bool kMask>
 __device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, const v8i* kop, const v8i* vop,
                                                uint32_t kvsc, const int* roff_ab, int fidx, float c, int rel, int lim,
-                                               bool kvalid, bool causal, uint32_t* cx) {
+                                               bool kvalid, bool causal, uint32_t* cx, int slot_off) {
   constexpr int NS = D / 64;
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
@@ -316,7 +316,7 @@ __device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, con
     ds[j] = (int)pack4_e4m3_scaled(U[4 * j], U[4 * j + 1], U[4 * j + 2], U[4 * j + 3], usc);
   }
   reinterpret_cast<v4i*>(cx)[qt * 64 + lane] = pb;
-  reinterpret_cast<v4i*>(cx)[(2 + qt) * 64 + lane] = ds;
+  *reinterpret_cast<v4i*>(reinterpret_cast<uint8_t*>(cx) + (2 + qt) * 1024 + slot_off) = ds;
   reinterpret_cast<v2i*>(cx + 1024 + 128 * qt)[lane] = v2i{pbe, dse};
 }
 
@@ -350,7 +350,52 @@ __device__ __forceinline__ void next_step(int& hq, int& q0, int qfirst, int n) {
   }
 }
 
-template <int D, bool kPacked>
+// dS block (qb, kb) of query head h in the code store (layout in mx_layout.h DsStore): index of
+// its 1024-byte code block and of its exponent byte.
+template <bool kPacked>
+__device__ __forceinline__ void ds_block(const BwdParams& p, int s, int h, int doc_start, int qb, int kb,
+                                         long long& code_blk, long long& exp_idx) {
+  const long long row = seq_group_row_k<kPacked>(p.geom, p.heads_q, s, h, doc_start, qb);
+  exp_idx = row * p.ds.ecols + kb;
+  if (!kPacked && p.ds.tri)
+    code_blk = ((long long)s * p.heads_q + h) * p.ds.head_blocks + (long long)qb * (qb + 1) / 2 + kb;
+  else
+    code_blk = row * p.ds.cols + kb;
+}
+
+// Byte offset of a producer lane's 16 dS codes inside a 32 x 32 block in LDS. Lane (key
+// k = l % 32, h = l / 32) holds the codes of queries 8j + 4h + u (j, u = 0..3, in that order);
+// its 16-byte slot is 32h + (k ^ 4h), so that both the lane's own read and the transposed
+// read (ds_tr_offsets) touch every LDS bank once per 16-lane group.
+__device__ __forceinline__ int ds_slot_off(int lane) {
+  const int hh = lane >> 5, l32 = lane & 31;
+  return 16 * (32 * hh + (l32 ^ (4 * hh)));
+}
+
+// Transposed read of such a block with ds_read_b64_tr_b8 (in each 16-lane group, output lane
+// 8a + t receives byte t of the 8-byte rows supplied by lanes 2b + a, b = 0..7). Supplier lane
+// (b, a) of group G reads, for register pair r, the 8 bytes of key seq_tok(16 (G >> 1) + 8 r
+// + b) and queries {16 (G & 1) + 8 (t >> 2) + 4a + (t & 3)}. Output lane l then holds the 16
+// keys 16 (l / 32) .. + 15 of the block in SEQ contraction order (the dQ product's operand
+// bytes 0-15, or 16-31 for the second key block), for query sigma(l % 32): the lane index
+// with bits 2 and 3 swapped. The key of pair r = 1 is that of r = 0 plus 16, so its offset is
+// the returned offset (pair 0) plus 256.
+__device__ __forceinline__ int ds_tr_offset(int lane) {
+  const int G = lane >> 4, tb = (lane & 15) >> 1, ta = lane & 1;
+  const int key = seq_tok(16 * (G >> 1) + tb);
+  return 16 * (32 * ta + (key ^ (4 * ta))) + 8 * (G & 1);
+}
+__device__ __forceinline__ int sigma_q(int l32) { return (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1); }
+
+__device__ __forceinline__ v2i ds_read_tr8(const uint8_t* lds) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) v2i*)((__attribute__((address_space(3))) const uint8_t*)lds));
+}
+
+// kStore: the accumulator waves also write each dS block to the code store, transposed into
+// the dQ product's operand order: lane l's 16 bytes at 16 l of the block's 1024 bytes (read
+// back by the dQ pass instead of rebuilding dS).
+template <int D, bool kPacked, bool kStore>
 __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ DkvShared<D> sm;
   const KvWork w = decode_kv<kPacked>(p);
@@ -398,12 +443,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
       roff_ab[2 * s + 1] = l32 * D + (row_swz(l32, 4 * s + 2 + hh, D / 16) << 4);
     }
     const int fidx = 4 * hh;              // LSE / D index of the lane's rows
+    const int slot_off = ds_slot_off(lane);
     int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
     uint32_t sv[2] = {0, 0};
     dkv_issue<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[0], sv, lw);
     dkv_put<D>(sm.st[0], sv, w.n - 1 - q0_l, lw);
     wait_vmem();
-    __syncthreads();                      // stage 0 loaded
+    wg_barrier();                         // stage 0 loaded
     int q0 = qfirst;                      // step whose codes are computed (j)
     for (int j = 0; j <= nsteps; j++) {
       next_step(hq_l, q0_l, qfirst, w.n);  // step j + 1
@@ -415,15 +461,15 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.n;
         if (need_mask)
           dkv_codes_tile<D, true>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, q0 + 4 * hh - key, w.n - q0 - 4 * hh,
-                                  kvalid, p.causal, cx);
+                                  kvalid, p.causal, cx, slot_off);
         else
-          dkv_codes_tile<D, false>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, 0, 0, true, false, cx);
+          dkv_codes_tile<D, false>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, 0, 0, true, false, cx, slot_off);
       }
       if (load) dkv_put<D>(sm.st[(j + 1) % 3], sv, w.n - 1 - q0_l, lw);
       q0 += kStepQ;
       if (q0 >= w.n) q0 = qfirst;
       wait_vmem();
-      __syncthreads();
+      wg_barrier();
     }
     return;
   }
@@ -440,17 +486,41 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   }
   const int soff_c = l32 * 32 + (half_swz(l32, hh) << 4);   // SEQ tile, channel l32 of group 0
   const int scoff = hh * D + l32;                            // SEQ scale of channel l32, group hh
-  __syncthreads();                        // stage 0 loaded
+  const int slot_off = ds_slot_off(lane);
+  const int troff = ds_tr_offset(lane);
+  wg_barrier();                           // stage 0 loaded
   int q0_a = qfirst;                      // step whose codes are applied (j - 1)
+  int hq_a = w.hkv * group;               // its query head
   for (int j = 0; j <= nsteps; j++) {
     if (j >= 1) {
       if (active(q0_a)) {
         const DkvStage<D>& S = sm.st[(j - 1) % 3];
         const uint32_t* cx = sm.cx[(j - 1) & 1][kg];
+        const uint8_t* cxb = reinterpret_cast<const uint8_t*>(cx);
         const v8i pb = cat(reinterpret_cast<const v4i*>(cx)[lane], reinterpret_cast<const v4i*>(cx)[64 + lane]);
-        const v8i ds = cat(reinterpret_cast<const v4i*>(cx)[128 + lane], reinterpret_cast<const v4i*>(cx)[192 + lane]);
+        const v8i ds = cat(*reinterpret_cast<const v4i*>(cxb + 2048 + slot_off),
+                           *reinterpret_cast<const v4i*>(cxb + 3072 + slot_off));
         const v2i e = reinterpret_cast<const v2i*>(cx + 1024 + 128 * hh)[lane];   // exponents of tile hh
         const int pbsc = e[0] + 127, dssc = e[1] + 127;
+        if (kStore) {
+          // blocks (query group qb = q0/32 + qt, key group kb); under causal only kb <= qb
+          const int kb = kw >> 5;
+#pragma unroll
+          for (int qt = 0; qt < 2; qt++) {
+            const int qb = (q0_a >> 5) + qt;
+            if ((qb << 5) < w.n && (!p.causal || kb <= qb)) {
+              const v2i x0 = ds_read_tr8(cxb + (2 + qt) * 1024 + troff);
+              const v2i x1 = ds_read_tr8(cxb + (2 + qt) * 1024 + 256 + troff);
+              long long blk, ei;
+              ds_block<kPacked>(p, w.s, hq_a, w.doc_start, qb, kb, blk, ei);
+              __builtin_nontemporal_store(
+                  v4i{x0[0], x0[1], x1[0], x1[1]},
+                  reinterpret_cast<__attribute__((address_space(1))) v4i*>(scalar_ptr(p.ds_codes + blk * 1024) +
+                                                                          (uint32_t)(lane * 16)));
+              if (lane == 32 * qt) p.ds_exps[ei] = (uint8_t)(dssc);   // lane 32 qt holds tile qt's exponent
+            }
+          }
+        }
 #pragma unroll
         for (int t = 0; t < NCT; t++) {
           const int h0 = t * 1024 + soff_c, h1 = D * 32 + t * 1024 + soff_c;   // channel t*32 + l32
@@ -463,15 +533,20 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         }
       }
       q0_a += kStepQ;
-      if (q0_a >= w.n) q0_a = qfirst;
+      if (q0_a >= w.n) {
+        q0_a = qfirst;
+        hq_a++;
+      }
     }
-    __syncthreads();
+    wg_barrier();
   }
 
   // ---- epilogue: dK = alpha * acc, dV = acc; lane = key kw + l32, quad b4 of tile t = channels
-  //      t*32 + 8 b4 + 4 hh .. +3 ----
-  if (key < w.n) {
-    const long long base = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, w.hkv, key, 0) + 4 * hh;
+  //      t*32 + 8 b4 + 4 hh .. +3 (the key is recomputed from the lane id here rather than kept
+  //      live through the loop) ----
+  const int key_e = kw + (__lane_id() & 31);
+  if (key_e < w.n) {
+    const long long base = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, w.hkv, key_e, 0) + 4 * (__lane_id() >> 5);
 #pragma unroll
     for (int t = 0; t < NCT; t++) {
 #pragma unroll
@@ -752,6 +827,199 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   if (bad) __hip_atomic_fetch_or(p.flags, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ========================== dQ pass from stored dS ==========================
+//
+// dQ^T += K_seq^T dS^T over 64-key tiles, with the dS blocks the dK/dV pass stored (the same
+// 32 x 32 blocks, codes and exponents the rebuilding pass produces). One workgroup per
+// (sequence or document, query head, 128-query block); wave w owns query block qb, the 32
+// queries [32w, 32w + 32) of it. The stored blocks are already in the operand's register order
+// (lane l: 16 key bytes for query sigma(l % 32)), so each wave loads its two blocks per tile
+// straight into registers, kPre tiles ahead; the K SEQ tile (shared by the four waves) goes
+// through LDS by DMA, two tiles ahead. The pass reads 1 byte per visible (query, key) pair
+// from HBM and moves no other per-pair data: it is bound by HBM bandwidth.
+template <int D>
+struct DqdsStage {
+  alignas(16) uint8_t ks[2 * D * 32];       // K SEQ codes [group][channel][32], half_swz halves
+  alignas(16) uint8_t kss[kWaves][256];     // K SEQ scales [group][channel], one copy per wave
+};
+
+constexpr int kPre = 4;                     // dS tiles in flight per wave (register ring)
+
+// Per-wave constants of the dQ-from-store pass.
+struct DqdsCtx {
+  int lane, wave, hh, hkv, glast;
+  int kb_end;                 // the wave's key blocks: kb < kb_end
+  long long blk0, ex0;        // code block and exponent index of (qb, kb = 0)
+  int soff, soff_c, scoff;    // K SEQ DMA lane offset, operand offset, scale offset
+};
+
+// K SEQ tile kt into stage st; tiles past the end reload the last groups (never read).
+template <int D, bool kPacked>
+__device__ __forceinline__ void dqds_issue_k(const BwdParams& p, const QWork& w, const DqdsCtx& c, int kt,
+                                             DqdsStage<D>* __restrict__ st) {
+  constexpr int PER = D / 32, NSEQ = 2 * PER;
+  const Geom& g = p.geom;
+  const int g0 = 2 * kt;
+#pragma unroll
+  for (int jj = 0; jj < NSEQ / kWaves; jj++) {
+    const int j = c.wave + kWaves * jj;
+    const int grp = min(g0 + j / PER, c.glast);
+    const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, c.hkv, w.doc_start, grp);
+    lds_dma(p.ks_codes + row * (D * 32) + (j % PER) * 1024 + c.soff, st->ks + j * 1024, 16);
+  }
+  const int i = c.lane % (D / 2);             // dword i of [group g0 | group g0 + 1]; d = 64: lanes 32+ repeat
+  const int grp = min(g0 + (i * 4) / D, c.glast);
+  const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, c.hkv, w.doc_start, grp);
+  lds_dma(p.ks_scales + row * D + (i * 4) % D, st->kss[c.wave], 4);
+}
+
+// dS blocks kb = 2kt, 2kt + 1 and the exponent of block 2kt + hh; absent blocks load block 0 of
+// the store (never used).
+__device__ __forceinline__ void dqds_load_ds(const BwdParams& p, const DqdsCtx& c, int kt, v4i (&r)[2], int& e) {
+  const int g0 = 2 * kt;
+#pragma unroll
+  for (int b = 0; b < 2; b++) {
+    const long long blk = g0 + b < c.kb_end ? c.blk0 + g0 + b : 0;
+    r[b] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) v4i*>(
+        scalar_ptr(p.ds_codes + blk * 1024) + (uint32_t)(c.lane * 16)));
+  }
+  const long long ei = g0 + c.hh < c.kb_end ? c.ex0 + g0 + c.hh : 0;
+  e = p.ds_exps[ei];
+}
+
+// One tile: start the K tile kt + 2 into `nxt`, dQ^T += K_seq^T dS^T for tile kt (K from `cur`,
+// dS from the registers r, e; kt < 0 only issues), then reload r, e with tile kt + kPre. The
+// stages never overlap; the restrict qualifiers tell the compiler so, which keeps it from
+// waiting for the new LDS-DMA before reading `cur` (every LDS-DMA of the kernel is issued from
+// this one call site, so all of them carry that information).
+template <int D, bool kPacked>
+__device__ __forceinline__ void dqds_tile(const BwdParams& p, const QWork& w, const DqdsCtx& c, int kt,
+                                          const DqdsStage<D>* __restrict__ cur, DqdsStage<D>* __restrict__ nxt,
+                                          v4i (&r)[2], int& e, v16f* dq) {
+  constexpr int NCT = D / 32;
+  dqds_issue_k<D, kPacked>(p, w, c, kt + 2, nxt);
+  const int g0 = 2 * kt;
+  if (kt >= 0 && g0 < c.kb_end) {
+    const bool two = g0 + 1 < c.kb_end;
+    const v8i dsop = cat(r[0], two ? r[1] : v4i{0, 0, 0, 0});
+    const int dssc = g0 + c.hh < c.kb_end ? e : 127;
+#pragma unroll
+    for (int t = 0; t < NCT; t++) {
+      const v8i ka = cat(*reinterpret_cast<const v4i*>(&cur->ks[t * 1024 + c.soff_c]),
+                         *reinterpret_cast<const v4i*>(&cur->ks[D * 32 + t * 1024 + c.soff_c]));
+      dq[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, dsop, dq[t], 0, 0, 0,
+                                                              cur->kss[c.wave][c.scoff + t * 32], 0, dssc);
+    }
+  }
+  dqds_load_ds(p, c, kt + kPre, r, e);
+}
+
+template <int D, bool kF16, bool kPacked>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(BwdParams p) {
+  __shared__ DqdsStage<D> sm[3];
+  const QWork w = decode_q(p);
+  if (!w.valid) return;
+  const Geom& g = p.geom;
+  constexpr int NCT = D / 32;
+  constexpr int NK = 2 * (D / 32) / kWaves + 1;   // K-tile instructions per wave and tile
+  // Vector-memory instructions per wave and tile: NK (K tile, LDS-DMA) then 3 (two dS blocks
+  // and the exponent byte). At the top of iteration kt, K tile kt and dS tile kt have landed
+  // once at most [dS kt-2+P] [K kt+1] [dS kt-1+P] = NK + 6 younger instructions remain.
+  constexpr int NW = NK + 6;
+  static_assert(kPre >= 3, "dS tile kt must be issued before K tile kt");
+  DqdsCtx c;
+  c.lane = threadIdx.x & 63;
+  c.wave = wave_id();
+  c.hh = c.lane >> 5;
+  const int l32 = c.lane & 31;
+  c.hkv = w.h / (p.heads_q / p.heads_kv);
+  const int q0 = w.qb * kBlockQ;
+  const int qw = q0 + c.wave * 32;            // first query of this wave = 32 qb
+  const int qb = qw >> 5;
+  const int kend = p.causal ? min(w.n, q0 + kBlockQ) : w.n;
+  const int nkt = (kend + kStepK - 1) / kStepK;
+  c.glast = ((w.n + 31) >> 5) - 1;
+  c.kb_end = qw >= w.n ? 0 : (p.causal ? qb + 1 : c.glast + 1);
+  c.blk0 = 0;
+  c.ex0 = 0;
+  if (c.kb_end > 0) ds_block<kPacked>(p, w.s, w.h, w.doc_start, qb, 0, c.blk0, c.ex0);
+  c.soff = seq_tile_lane_off(c.lane);
+  c.soff_c = l32 * 32 + (half_swz(l32, c.hh) << 4);   // SEQ tile, channel l32 of group 0
+  c.scoff = c.hh * D + l32;                            // SEQ scale of channel l32, group hh
+
+  v16f dq[NCT];
+  h2 acc16[NCT][8];
+#pragma unroll
+  for (int t = 0; t < NCT; t++) {
+    dq[t] = v16f{};
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc16[t][i] = h2{(_Float16)0.f, (_Float16)0.f};
+  }
+  const float fmul = p.scale * kBoost;
+
+  // Ring slot of tile kt: kt mod kPre. Tiles 0 .. P-3 load here; iterations kt = -2, -1 only
+  // issue (K 0, dS P-2, K 1, dS P-1), giving the steady-state order from the first real tile.
+  v4i dsr[kPre][2];
+  int exr[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre - 2; u++) dqds_load_ds(p, c, u, dsr[u], exr[u]);
+
+  // kPre tiles per trip (the register ring is indexed by a compile-time slot); trips run whole,
+  // the tiles past nkt have no blocks and only keep the issue pattern uniform
+  for (int kt0 = -2; kt0 < nkt; kt0 += kPre) {
+#pragma unroll
+    for (int u = 0; u < kPre; u++) {
+      const int kt = kt0 + u;
+      const int slot = (u + kPre - 2) % kPre;
+      wait_vmem_n<NW>();
+      wg_barrier();                        // K tile kt visible; every wave is done with tile kt - 1
+      dqds_tile<D, kPacked>(p, w, c, kt, &sm[(kt + 3) % 3], &sm[(kt + 2) % 3], dsr[slot], exr[slot], dq);
+      if (kF16 && kt >= 0 && ((kt & 1) || kt + 1 == nkt)) {
+#pragma unroll
+        for (int t = 0; t < NCT; t++) {
+#pragma unroll
+          for (int i = 0; i < 8; i++)
+            acc16[t][i] += h2{(_Float16)(dq[t][2 * i] * fmul), (_Float16)(dq[t][2 * i + 1] * fmul)};
+          dq[t] = v16f{};
+        }
+      }
+    }
+  }
+  wait_vmem();                             // no LDS-DMA may be in flight when the wave ends
+
+  // ---- epilogue: column l32 = query qw + sigma(l32); 4 channels per store ----
+  const int hh = c.hh;
+  const int qi = qw + sigma_q(l32);
+  uint32_t bad = 0;
+  if (qi < w.n) {
+    const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
+    const long long obase = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, w.h, qi, 0);
+#pragma unroll
+    for (int t = 0; t < NCT; t++) {
+#pragma unroll
+      for (int b4 = 0; b4 < 4; b4++) {
+        const int ch = t * 32 + 8 * b4 + 4 * hh;
+        float o[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const int i = 4 * b4 + u;
+          const float a = kF16 ? (float)acc16[t][i >> 1][i & 1] : dq[t][i];
+          if (__builtin_isnan(a)) bad |= 2u;
+          else if (__builtin_isinf(a)) bad |= kF16 ? 1u : 2u;
+          o[u] = kF16 ? a * (1.f / kBoost) : a * p.scale;
+        }
+        if (p.out_f32) {
+          *reinterpret_cast<v4f*>(static_cast<float*>(p.dq) + obase + ch) = v4f{o[0], o[1], o[2], o[3]};
+        } else {
+          *reinterpret_cast<v2i*>(static_cast<uint16_t*>(p.dq) + obase + ch) =
+              v2i{(int)pack2_bf16(o[0], o[1]), (int)pack2_bf16(o[2], o[3])};
+        }
+      }
+    }
+  }
+  if (bad) __hip_atomic_fetch_or(p.flags, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ void clear_flags_kernel(uint32_t* flags) { *flags = 0u; }
 
 template <int D>
@@ -765,15 +1033,30 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
     gkv = dim3((unsigned)((g.max_seqlen + kBlockK - 1) / kBlockK), (unsigned)p.heads_kv, (unsigned)g.n_docs);
     gq = dim3((unsigned)((g.max_seqlen + kBlockQ - 1) / kBlockQ), (unsigned)p.heads_q, (unsigned)g.n_docs);
   }
+  const bool store = p.ds_codes != nullptr;
   int slot = profile_begin(kProfBwdKV, stream);
-  if (packed(g)) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), gkv, dim3(kDkvThreads), 0, stream, p);
-  else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), gkv, dim3(kDkvThreads), 0, stream, p);
+  if (packed(g)) {
+    if (store) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, false>), gkv, dim3(kDkvThreads), 0, stream, p);
+  } else {
+    if (store) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, false>), gkv, dim3(kDkvThreads), 0, stream, p);
+  }
   profile_end(slot, stream);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   slot = profile_begin(kProfBwdQ, stream);
-  if (p.dq_mode == 1) hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), gq, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), gq, dim3(256), 0, stream, p);
+  const bool f16 = p.dq_mode == 1;
+  if (!store) {
+    if (f16) hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), gq, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), gq, dim3(256), 0, stream, p);
+  } else if (packed(g)) {
+    if (f16) hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D, true, true>), gq, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D, false, true>), gq, dim3(256), 0, stream, p);
+  } else {
+    if (f16) hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D, true, false>), gq, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D, false, false>), gq, dim3(256), 0, stream, p);
+  }
   profile_end(slot, stream);
   return hipGetLastError();
 }

@@ -131,7 +131,34 @@ __device__ __forceinline__ void lds_dma(const void* src, void* lds, int size) {
                                      (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
 }
 
+// A wave-uniform pointer held in scalar registers. Adding a 32-bit lane offset to it gives
+// scalar-base + vector-offset addressing; it also keeps the compiler from folding a
+// loop-invariant lane offset into a 64-bit per-lane address kept live across a loop.
+// The result is a global-address-space pointer, so accesses through it stay global (not flat)
+// instructions.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* scalar_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<__attribute__((address_space(1))) T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Wait for every outstanding vector-memory operation of this wave (loads, LDS-DMA).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory operations of this wave are outstanding (they complete
+// in issue order, so this waits for all but the N most recent).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Workgroup barrier that completes this wave's LDS operations first (so its LDS writes are
+// visible after the barrier) but does not wait for global loads, stores or LDS-DMA: the
+// caller orders its LDS-DMA with wait_vmem / wait_vmem_n, and global stores drain on their
+// own. The asm statements also keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 }  // namespace mx

@@ -61,6 +61,9 @@ struct BwdParams {
   uint8_t* gs_codes; uint8_t* gs_scales;                // SEQ G
   float* delta;                                         // D per (row, head)
   uint32_t* flags;
+  // dS code store (nullptr: dQ recomputes dS instead); layout in mx_layout.h DsStore
+  uint8_t* ds_codes; uint8_t* ds_exps;
+  DsStore ds;
 };
 
 hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);

@@ -68,5 +68,29 @@ __host__ __device__ inline long long token_index_k(const Geom& g, int heads, int
 // K order of the gfx950 32x32x64 MFMA operand built from an accumulator tile: lanes 0-31
 // carry tokens {0-3, 8-11, 16-19, 24-27} in bytes 0-15, lanes 32-63 the rest.
 __host__ __device__ constexpr inline int seq_pos(int t) { return 16 * ((t >> 2) & 1) + 4 * (t >> 3) + (t & 3); }
+// Its inverse: the token offset stored at byte position p of a group.
+__host__ __device__ constexpr inline int seq_tok(int p) { return 8 * ((p >> 2) & 3) + 4 * ((p >> 4) & 1) + (p & 3); }
+
+// dS code store of the backward (an optional part of its workspace). Each 32-query x 32-key
+// block (qb, kb) of a query head holds 1024 E4M3 codes and one E8M0 byte.
+//   block rows: row(qb) = seq_group_row of query group qb (the SEQ-view row numbering)
+//   code blocks: batched causal: (b * H + h) * nb(nb+1)/2 + qb(qb+1)/2 + kb (kb <= qb only);
+//                otherwise row(qb) * cols + kb, cols = ceil(L / 32) or ceil(max_seqlen / 32)
+//   exponents:   row(qb) * ecols + kb, ecols = cols rounded up to a multiple of 4
+struct DsStore {
+  long long head_blocks;   // batched causal: code blocks per (b, h)
+  int cols, ecols;
+  bool tri;                // batched causal (triangular code rows)
+};
+
+__host__ __device__ inline DsStore ds_store_geom(const Geom& g, bool causal) {
+  DsStore s;
+  const long long nb = packed(g) ? (g.max_seqlen + 31) / 32 : (g.seqlen + 31) / 32;
+  s.cols = (int)nb;
+  s.ecols = (int)((nb + 3) / 4 * 4);
+  s.tri = !packed(g) && causal;
+  s.head_blocks = s.tri ? nb * (nb + 1) / 2 : (long long)g.gseq * nb;
+  return s;
+}
 
 }  // namespace mx

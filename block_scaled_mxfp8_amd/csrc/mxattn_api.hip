@@ -66,8 +66,12 @@ mx_status check_desc(const mx_attn_desc* d, mx::Geom* g) {
   return MX_OK;
 }
 
+// Backward workspace: the status word, G's views and D (always), then the optional dS code
+// store (total_store - total bytes; with it the dQ pass reads dS instead of rebuilding it).
 struct BwdWorkspace {
   size_t gr_codes, gr_scales, gs_codes, gs_scales, delta, flags, total;
+  size_t ds_codes, ds_exps, total_store;
+  mx::DsStore ds;
 };
 
 BwdWorkspace bwd_layout(const mx::Geom& g, const mx_attn_desc* d) {
@@ -81,6 +85,12 @@ BwdWorkspace bwd_layout(const mx::Geom& g, const mx_attn_desc* d) {
   w.gs_scales = off; off += align_up(seq_codes_bytes(g, hq, dim) / 32);
   w.delta = off; off += align_up((size_t)g.total * hq * sizeof(float));
   w.total = off;
+  w.ds = mx::ds_store_geom(g, d->causal != 0);
+  const size_t rows = (size_t)g.gseq * hq * (mx::packed(g) ? 1 : (size_t)g.batch);   // query groups
+  const size_t blocks = w.ds.tri ? (size_t)g.batch * hq * (size_t)w.ds.head_blocks : rows * (size_t)w.ds.cols;
+  w.ds_codes = off; off += align_up(blocks * 1024);
+  w.ds_exps = off; off += align_up(rows * (size_t)w.ds.ecols);
+  w.total_store = off;
   return w;
 }
 
@@ -149,6 +159,11 @@ mx_status bwd_impl(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_
   p.gs_codes = ws + w.gs_codes; p.gs_scales = ws + w.gs_scales;
   p.delta = reinterpret_cast<float*>(ws + w.delta);
   p.flags = reinterpret_cast<uint32_t*>(ws + w.flags);
+  if (desc->workspace_bytes >= w.total_store) {
+    p.ds_codes = ws + w.ds_codes;
+    p.ds_exps = ws + w.ds_exps;
+    p.ds = w.ds;
+  }
   if (g.total == 0) return MX_OK;
   return mx::launch_attn_bwd(p, (hipStream_t)stream) == hipSuccess ? MX_OK : MX_E_DEVICE;
 }
@@ -219,8 +234,10 @@ mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
 
 size_t mx_attn_workspace_size(const mx_attn_desc* desc, int32_t for_bwd) {
   mx::Geom g;
-  if (!for_bwd || !desc || !make_geom(&desc->seq, &g) || desc->heads_q < 1 || !valid_dim(desc->head_dim)) return 0;
-  return bwd_layout(g, desc).total;
+  if (for_bwd != 1 && for_bwd != 2) return 0;
+  if (!desc || !make_geom(&desc->seq, &g) || desc->heads_q < 1 || !valid_dim(desc->head_dim)) return 0;
+  const BwdWorkspace w = bwd_layout(g, desc);
+  return for_bwd == 2 ? w.total_store : w.total;
 }
 
 size_t mx_view_codes_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view) {

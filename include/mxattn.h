@@ -104,7 +104,8 @@ typedef struct {
   int32_t dq_mode;        /* MX_DQ_F32 or MX_DQ_F16_BOOST (FP16 partial sums x 2^9) */
   int32_t deterministic;  /* 0 or 1; every call is bitwise reproducible (fixed reduction order, no
                              atomics), so 1 costs nothing; other values: MX_E_ARG */
-  void* workspace;        /* device scratch for mx_attn_bwd (see mx_attn_workspace_size) */
+  void* workspace;        /* device scratch for mx_attn_bwd (see mx_attn_workspace_size); with at
+                             least the for_bwd = 2 size the backward keeps the dS codes there */
   size_t workspace_bytes;
 } mx_attn_desc;
 
@@ -139,7 +140,15 @@ mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
                              mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                              mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
 
-/* Bytes of device workspace mx_attn_bwd needs for this descriptor (0 for the forward). */
+/* Bytes of device workspace for mx_attn_bwd with this descriptor.
+ *   for_bwd = 1: the minimum (G's views, D, the status word; O(tokens x heads x head_dim)).
+ *     The dQ pass then rebuilds S, P and dS itself (two more score-sized products per pair).
+ *   for_bwd = 2: the minimum plus a store of the quantised dS blocks (one byte per visible
+ *     (query, key) pair of every query head, plus one scale byte per 32 x 32 block; for a
+ *     causal batch about B * H * L^2 / 2 bytes). The dK/dV pass writes the dS codes there and
+ *     the dQ pass reads them instead of rebuilding them. The results are the same either way.
+ * mx_attn_bwd uses the store whenever desc->workspace_bytes >= the for_bwd = 2 size.
+ * Other for_bwd values (0 = forward, which needs none) return 0. */
 size_t mx_attn_workspace_size(const mx_attn_desc* desc, int32_t for_bwd);
 
 /* Byte sizes of the quantised views of a tensor with `heads` heads (codes, scales). */

@@ -127,3 +127,42 @@ def test_binding_geometry_and_allocation_sizes_agree_with_library(lib):
         assert math.prod(shape[:-1]) * (d // 32) == lib.mx_view_scales_bytes(ctypes.byref(s), h, d, 1)
         assert math.prod(cs) == lib.mx_view_codes_bytes(ctypes.byref(s), h, d, 2)
         assert math.prod(ss) == lib.mx_view_scales_bytes(ctypes.byref(s), h, d, 2)
+
+
+def _bwd_desc(seq, heads, d, causal):
+    desc = _lib._Desc()
+    desc.seq = seq
+    desc.heads_q = desc.heads_kv = heads
+    desc.head_dim = d
+    desc.causal = causal
+    return desc
+
+
+def _up(x, a=256):
+    return (x + a - 1) // a * a
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_workspace_sizes_with_and_without_the_ds_store(lib, causal):
+    # batched B2 H3 L100 d128: G ROW + SEQ views, D and the status word; the dS store adds one
+    # 1024-byte block per visible 32 x 32 (query, key) block (triangular under causal) and one
+    # exponent byte per block of a row padded to a multiple of 4
+    B, H, L, d = 2, 3, 100, 128
+    s = _seq(batch=B, seqlen=L)
+    desc = _bwd_desc(s, H, d, causal)
+    nb = (L + 31) // 32
+    base = (_up(4) + _up(B * H * L * d) + _up(B * H * L * d // 32) + _up(B * H * nb * d * 32)
+            + _up(B * H * nb * d) + _up(B * H * L * 4))
+    assert lib.mx_attn_workspace_size(ctypes.byref(desc), 1) == base
+    blocks = B * H * (nb * (nb + 1) // 2 if causal else nb * nb)
+    exps = B * H * nb * ((nb + 3) // 4 * 4)
+    assert lib.mx_attn_workspace_size(ctypes.byref(desc), 2) == base + _up(blocks * 1024) + _up(exps)
+    assert lib.mx_attn_workspace_size(ctypes.byref(desc), 0) == 0
+    assert lib.mx_attn_workspace_size(ctypes.byref(desc), 3) == 0
+    # packed T = 300 in 5 documents, max length 100: rectangular rows of ceil(100/32) blocks
+    p = _lib._Seq()
+    p.cu_seqlens, p.n_docs, p.max_seqlen, p.total_tokens = FAKE, 5, 100, 300
+    desc = _bwd_desc(p, 2, 64, causal)
+    small = lib.mx_attn_workspace_size(ctypes.byref(desc), 1)
+    rows = 2 * (300 // 32 + 5)
+    assert lib.mx_attn_workspace_size(ctypes.byref(desc), 2) == small + _up(rows * 4 * 1024) + _up(rows * 4)

@@ -40,12 +40,12 @@ def _fwd_dev(t, causal, out_dtype):
     return o, lse
 
 
-def _bwd_dev(t, o, lse, causal, out_dtype, dq_mode):
+def _bwd_dev(t, o, lse, causal, out_dtype, dq_mode, ds_store=True):
     q_row, q_seq = mx_quantize(t["q"])
     k_row, k_seq = mx_quantize(t["k"])
     v_row, _ = mx_quantize(t["v"], views=1)
     dq, dk, dv, ws = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=causal,
-                                 out_dtype=out_dtype, dq_mode=dq_mode)
+                                 out_dtype=out_dtype, dq_mode=dq_mode, ds_store=ds_store)
     return dq, dk, dv, ws
 
 
@@ -127,31 +127,36 @@ def test_backward_matches_oracle(case):
             LSE[b, h] = f["lse"]
     o_dev = torch.from_numpy(O_saved).to(dtype).cuda()
     lse_dev = torch.from_numpy(LSE).cuda()
-    dq, dk, dv, ws = _bwd_dev(t, o_dev, lse_dev, causal, dtype, dq_mode)
-    torch.cuda.synchronize()
-    dq, dk, dv = as_f64(dq), as_f64(dk), as_f64(dv)
-    res = {n: ([], [], []) for n in ("dQ", "dK", "dV")}
-    ref_kv = {n: np.zeros((B, Hkv) + k.shape[2:]) for n in ("dK", "dV")}
-    allow_kv = {n: np.zeros((B, Hkv) + k.shape[2:]) for n in ("dK", "dV")}
+    ref = {"dQ": np.zeros(q.shape), "dK": np.zeros(k.shape), "dV": np.zeros(k.shape)}
+    allow = {n: np.zeros_like(ref[n]) for n in ref}
     for b in range(B):
         for h in range(H):
             hk = h // (H // Hkv)
             r = oracle.head_backward(q[b, h], k[b, hk], v[b, hk], O_saved[b, h], LSE[b, h].astype(np.float64),
                                      g[b, h], causal, out_dtype=odt, bounds=True, dq_mode="f32" if dq_mode == 0 else "f16")
-            res["dQ"][0].append(dq[b, h])
-            res["dQ"][1].append(r["dQ"])
-            res["dQ"][2].append(r["B_dQ"] + r["eta_dQ"] + oracle.ulp_of(dq[b, h], odt) / 2)
+            ref["dQ"][b, h] = r["dQ"]
+            allow["dQ"][b, h] = r["B_dQ"] + r["eta_dQ"]
             for n in ("dK", "dV"):
-                ref_kv[n][b, hk] += r[n]
-                allow_kv[n][b, hk] += r["B_" + n] + r["eta_" + n]
-    for n, dev in (("dK", dk), ("dV", dv)):
-        res[n] = (list(dev.reshape((-1,) + dev.shape[2:])), list(ref_kv[n].reshape((-1,) + dev.shape[2:])),
-                  list((allow_kv[n] + oracle.ulp_of(dev, odt) / 2).reshape((-1,) + dev.shape[2:])))
-    for n in ("dQ", "dK", "dV"):
-        ok, worst, plain, namb = gate(np.stack(res[n][0]), np.stack(res[n][1]), np.stack(res[n][2]), REL)
-        print(f"  {n}: plain max|d|/rms {plain:.3e}, worst excess {worst:.3e}, B>0: {namb}", flush=True)
-        _where(n, np.stack(res[n][0]), np.stack(res[n][1]), np.stack(res[n][2]))
-        assert ok, n
+                ref[n][b, hk] += r[n]
+                allow[n][b, hk] += r["B_" + n] + r["eta_" + n]
+    # both backward variants: dS codes kept in the workspace store, or rebuilt by the dQ pass
+    outs = {}
+    for ds_store in (True, False):
+        print(f"  ds_store={ds_store}", flush=True)
+        dq, dk, dv, ws = _bwd_dev(t, o_dev, lse_dev, causal, dtype, dq_mode, ds_store=ds_store)
+        torch.cuda.synchronize()
+        outs[ds_store] = (dq, dk, dv)
+        dev = {"dQ": as_f64(dq), "dK": as_f64(dk), "dV": as_f64(dv)}
+        for n in ("dQ", "dK", "dV"):
+            al = allow[n] + oracle.ulp_of(dev[n], odt) / 2
+            ok, worst, plain, namb = gate(dev[n], ref[n], al, REL)
+            print(f"  {n}: plain max|d|/rms {plain:.3e}, worst excess {worst:.3e}, B>0: {namb}", flush=True)
+            _where(n, dev[n], ref[n], al)
+            assert ok, n
+    # the two variants quantise the same dS blocks the same way
+    for n, a, b in zip(("dQ", "dK", "dV"), outs[True], outs[False]):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)) if a.dtype == torch.bfloat16 \
+            else torch.equal(a, b), n
 
 
 @pytest.mark.parametrize("cfg,B,H,L,d,causal", [("c3", 1, 2, 512, 128, True), ("c3", 1, 2, 384, 128, False),
