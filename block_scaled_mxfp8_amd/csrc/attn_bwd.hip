@@ -68,6 +68,15 @@ __device__ __forceinline__ uint32_t load_row_scales(const uint8_t* base, uint32_
   return D == 128 ? *reinterpret_cast<const uint32_t*>(src) : (uint32_t)*reinterpret_cast<const uint16_t*>(src);
 }
 
+// Lane index as a value the compiler cannot hoist out of a loop (an empty volatile asm
+// produces it), so that per-lane offsets derived from it are recomputed where they are used
+// instead of being kept live in registers across the loop.
+__device__ __forceinline__ int fresh_lane() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 // Wave index as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
@@ -170,15 +179,19 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
   return w;
 }
 
-// Issue the loads of the step (query head hq, queries q0..q0+63) into stage `st`, as loader
-// `lw` of NL: ROW-tile and SEQ-tile DMA instructions j = lw, lw + NL, ... (each moves 64 x 16
-// bytes: 64/NCH rows of NCH = d/16 chunks, or 32 channels of one SEQ group), and for loaders
-// 0-3 one small item set in `sv`. Rows past the end are clamped to the last row (finite
-// codes; their LSE is +inf, so their P and U are 0).
+// Issue the producers' loads of the step (query head hq, queries q0..q0+63) into stage `st`,
+// as loader `lw` of NL (NL >= 6): ROW-tile DMA instructions j = lw, lw + NL, ... (each moves
+// 64 x 16 bytes: 64/NCH rows of NCH = d/16 chunks) and one small-item dword per lane into `sv`: loader 0 the Q ROW scale word of row `lane`, 1 the G
+// ROW scale word, 2 LSE, 3 D, 4 the Q SEQ scales, 5 the G SEQ scales (dword lane % (d/2) of
+// the step's two groups); loaders 6+ repeat loader 0's load and store nothing. Every loader
+// loads on every path, so the register is only ever written by loads (no write-after-load
+// wait). Rows past the end are clamped to the last row (finite codes; their LSE becomes +inf
+// in dkv_put, so their P and U are 0).
 template <int D, bool kPacked, int NL>
-__device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
-                                          uint32_t (&sv)[2], int lw) {
-  constexpr int NCH = D / 16, RPI = 64 / NCH, PER = D / 32, NSEQ = 4 * D / 64;
+__device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
+                                              uint32_t& sv, int lw) {
+  static_assert(NL >= 6, "six small-item loaders");
+  constexpr int NCH = D / 16, RPI = 64 / NCH;
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
   const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
@@ -186,24 +199,20 @@ __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, i
   const long long off0 = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, hq, q0, 0);
   const int rmax = w.n - 1 - q0;
   const int glast = ((w.n + 31) >> 5) - 1;
-  // Small items first, as raw bits (dkv_put converts them): their loads then precede the
-  // DMA in the wave's in-order vector-memory queue, so waiting for them (at dkv_put) does
-  // not wait for this step's DMA. Loader 0: Q ROW scales, 1: G ROW scales, 2: LSE + Q SEQ
-  // scales, 3: D + G SEQ scales.
+  // small item first: its load then precedes the DMA in the wave's in-order vector-memory
+  // queue, so waiting for it (at dkv_put) does not wait for this step's DMA
   const int r = min(lane, rmax);
-  if (lw < 2) {
-    const uint8_t* base = (lw == 0 ? p.q_scales : p.gr_scales) + (off0 >> 5);
-    sv[0] = load_row_scales<D>(base, (uint32_t)(r * ts));
-    sv[1] = 0;
-  } else if (lw < 4) {
+  if (lw == 2 || lw == 3) {
     const float* f = (lw == 2 ? p.lse : p.delta) + token_index_k<kPacked>(g, p.heads_q, w.s, w.doc_start, hq, q0);
-    sv[0] = __float_as_uint(f[(uint32_t)(r * (kPacked ? p.heads_q : 1))]);
-    // every lane loads (lanes >= d/2 repeat a dword of the lower half and are not stored), so
-    // the load is not divergent and needs no wait before the branches reconverge
-    const int word = lane % (D / 2);
+    sv = __float_as_uint(f[(uint32_t)(r * (kPacked ? p.heads_q : 1))]);
+  } else if (lw == 4 || lw == 5) {
+    const int word = lane % (D / 2);       // lanes >= d/2 repeat a dword of the lower half
     const int gi = min((q0 >> 5) + (word * 4) / D, glast);
     const long long row = seq_group_row_k<kPacked>(g, p.heads_q, w.s, hq, w.doc_start, gi);
-    sv[1] = *reinterpret_cast<const uint32_t*>((lw == 2 ? p.qs_scales : p.gs_scales) + row * D + (word * 4) % D);
+    sv = *reinterpret_cast<const uint32_t*>((lw == 4 ? p.qs_scales : p.gs_scales) + row * D + (word * 4) % D);
+  } else {
+    const uint8_t* base = (lw == 1 ? p.gr_scales : p.q_scales) + (off0 >> 5);
+    sv = load_row_scales<D>(base, (uint32_t)(r * ts));
   }
   // ROW tiles (Q, G)
   const int lrow = lane / NCH;
@@ -218,8 +227,19 @@ __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, i
       lds_dma(p.gr_codes + off0 + (uint32_t)vo, st.gr + j * 1024, 16);
     }
   }
-  // SEQ tiles (groups q0/32 and q0/32 + 1, the latter clamped to the last group)
-  const int soff = seq_tile_lane_off(lane);
+}
+
+// Issue the accumulators' loads of the step into stage `st`: the SEQ tiles of Q and G (groups
+// q0/32 and q0/32 + 1, the latter clamped to the last group), instructions j = lw, lw + NL, ...
+// (each moves the 32 channels of one group). The lane offset is recomputed here (registers are
+// short in this role).
+template <int D, bool kPacked, int NL>
+__device__ __forceinline__ void dkv_issue_seq(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
+                                              int lw) {
+  constexpr int PER = D / 32, NSEQ = 4 * D / 64;
+  const Geom& g = p.geom;
+  const int glast = ((w.n + 31) >> 5) - 1;
+  const int soff = seq_tile_lane_off(fresh_lane());
 #pragma unroll
   for (int j0 = 0; j0 < NSEQ; j0 += NL) {
     const int j = j0 + lw;
@@ -233,17 +253,18 @@ __device__ __forceinline__ void dkv_issue(const BwdParams& p, const KvWork& w, i
   }
 }
 
-// Store the small items of a step; rows past the end (lane > rmax) get LSE' = +inf, D = 0.
+// Store the small item of a step; rows past the end (lane > rmax) get LSE' = +inf, D = 0.
 template <int D>
-__device__ __forceinline__ void dkv_put(DkvStage<D>& st, const uint32_t (&sv)[2], int rmax, int lw) {
+__device__ __forceinline__ void dkv_put(DkvStage<D>& st, uint32_t sv, int rmax, int lw) {
   const int lane = threadIdx.x & 63;
-  if (lw < 2) {
-    (lw == 0 ? st.qrs : st.grs)[lane] = sv[0];
-  } else if (lw < 4) {
-    const float x = __uint_as_float(sv[0]);
-    const bool live = lane <= rmax;
-    (lw == 2 ? st.lse2 : st.dlt)[lane] = lw == 2 ? (live ? x * kLog2e : INFINITY) : (live ? x : 0.f);
-    if (lane < D / 2) reinterpret_cast<uint32_t*>(lw == 2 ? st.qss : st.gss)[lane] = sv[1];
+  const bool live = lane <= rmax;
+  const float x = __uint_as_float(sv);
+  if (lw == 0) st.qrs[lane] = sv;
+  else if (lw == 1) st.grs[lane] = sv;
+  else if (lw == 2) st.lse2[lane] = live ? x * kLog2e : INFINITY;
+  else if (lw == 3) st.dlt[lane] = live ? x : 0.f;
+  else if (lw == 4 || lw == 5) {
+    if (lane < D / 2) reinterpret_cast<uint32_t*>(lw == 4 ? st.qss : st.gss)[lane] = sv;
   }
 }
 
@@ -303,11 +324,14 @@ __device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, con
       U[4 * j + u] = P[4 * j + u] * (eacc[4 * j + u] - d4[u]);
     }
   }
-  float pm = max_abs16(P);
+  // P_b exponent per key (the lane's 16 queries and lane ^ 32's); dS exponent per block (whole
+  // wave), computed once in scalar registers
+  float pm = max16_tree(P);
   pm = fmaxf(pm, swap32(pm));
   const int pbe = p_scale_exp(pm);
   const float psc = exp2_scale(pbe);
-  const int dse = scale_exp_from_bits(__float_as_uint(wave_max(max_abs16(U))));
+  const uint32_t ub = __builtin_amdgcn_readfirstlane(wave_max_bits(__float_as_uint(max_abs16_tree(U))));
+  const int dse = scale_exp_from_bits(ub);
   const float usc = exp2_scale(dse);
   v4i pb, ds;
 #pragma unroll
@@ -328,9 +352,12 @@ __device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, con
 // and one accumulator of the same key group: the producers' VALU work overlaps each other's
 // latencies and the accumulator's MFMAs, and each role fits three waves per SIMD.
 //
-// Iteration j (j = 0..nsteps): producers issue the loads of step j + 1 into stage (j+1) % 3
-// and turn stage j % 3 into codes in exchange buffer j % 2; accumulators apply the codes of
-// step j - 1 (stage (j-1) % 3, buffer (j-1) % 2); one barrier ends the iteration.
+// Iteration j (j = 0..nsteps): producers issue the ROW-tile and small-item loads of step
+// j + 1 into stage (j+1) % 3 and turn stage j % 3 into codes in exchange buffer j % 2;
+// accumulators issue the SEQ-tile loads of step j + 1 and apply the codes of step j - 1
+// (stage (j-1) % 3, buffer (j-1) % 2); one barrier ends the iteration. (The loads of a step
+// pass through the CU's vector-memory path at about 64 bytes per clock; splitting them keeps
+// the producers from queueing behind all of them.)
 constexpr int kDkvProducers = 2 * kWaves;
 constexpr int kDkvThreads = 64 * (kDkvProducers + kWaves);
 constexpr int kCodeDw = 1280;               // exchange dwords per key group
@@ -445,8 +472,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     const int fidx = 4 * hh;              // LSE / D index of the lane's rows
     const int slot_off = ds_slot_off(lane);
     int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
-    uint32_t sv[2] = {0, 0};
-    dkv_issue<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[0], sv, lw);
+    uint32_t sv = 0;
+    dkv_issue_row<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[0], sv, lw);
     dkv_put<D>(sm.st[0], sv, w.n - 1 - q0_l, lw);
     wait_vmem();
     wg_barrier();                         // stage 0 loaded
@@ -454,7 +481,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     for (int j = 0; j <= nsteps; j++) {
       next_step(hq_l, q0_l, qfirst, w.n);  // step j + 1
       const bool load = j + 1 < nsteps;
-      if (load) dkv_issue<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], sv, lw);
+      if (load) dkv_issue_row<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], sv, lw);
       if (j < nsteps && active(q0)) {
         const DkvStage<D>& S = sm.st[j % 3];
         uint32_t* cx = sm.cx[j & 1][kg];
@@ -484,16 +511,26 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     dk[t] = v16f{};
     dv[t] = v16f{};
   }
-  const int soff_c = l32 * 32 + (half_swz(l32, hh) << 4);   // SEQ tile, channel l32 of group 0
-  const int scoff = hh * D + l32;                            // SEQ scale of channel l32, group hh
-  const int slot_off = ds_slot_off(lane);
-  const int troff = ds_tr_offset(lane);
+  const int lw = wave - kDkvProducers;    // SEQ-tile loader index
+  int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
+  dkv_issue_seq<D, kPacked, kWaves>(p, w, hq_l, q0_l, sm.st[0], lw);
+  wait_vmem();
   wg_barrier();                           // stage 0 loaded
   int q0_a = qfirst;                      // step whose codes are applied (j - 1)
   int hq_a = w.hkv * group;               // its query head
   for (int j = 0; j <= nsteps; j++) {
+    next_step(hq_l, q0_l, qfirst, w.n);  // step j + 1
+    const bool load = j + 1 < nsteps;
+    if (load) dkv_issue_seq<D, kPacked, kWaves>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], lw);
+    int nst = 0;                          // global stores issued after the loads
     if (j >= 1) {
       if (active(q0_a)) {
+        // per-lane offsets, recomputed here (registers are short in this role)
+        const int ln = fresh_lane(), l32a = ln & 31, hha = ln >> 5;
+        const int soff_c = l32a * 32 + (half_swz(l32a, hha) << 4);   // SEQ tile, channel l32 of group 0
+        const int scoff = hha * D + l32a;                             // SEQ scale of channel l32, group hh
+        const int slot_off = ds_slot_off(ln);
+        const int troff = ds_tr_offset(ln);
         const DkvStage<D>& S = sm.st[(j - 1) % 3];
         const uint32_t* cx = sm.cx[(j - 1) & 1][kg];
         const uint8_t* cxb = reinterpret_cast<const uint8_t*>(cx);
@@ -518,6 +555,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
                   reinterpret_cast<__attribute__((address_space(1))) v4i*>(scalar_ptr(p.ds_codes + blk * 1024) +
                                                                           (uint32_t)(lane * 16)));
               if (lane == 32 * qt) p.ds_exps[ei] = (uint8_t)(dssc);   // lane 32 qt holds tile qt's exponent
+              nst += 2;
             }
           }
         }
@@ -538,6 +576,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         hq_a++;
       }
     }
+    // the SEQ tiles of step j + 1 have landed once at most the nst younger stores are outstanding
+    if (nst == 4) wait_vmem_n<4>();
+    else if (nst == 2) wait_vmem_n<2>();
+    else wait_vmem();
     wg_barrier();
   }
 

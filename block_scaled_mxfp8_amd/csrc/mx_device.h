@@ -106,6 +106,34 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(x, fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1])));
 }
 
+// Largest of 16 non-negative floats (e.g. |x| or P), as a depth-3 tree of three-input maxima.
+__device__ __forceinline__ float max16_tree(const float* x) {
+  const float m0 = fmaxf(fmaxf(x[0], x[1]), x[2]), m1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+  const float m2 = fmaxf(fmaxf(x[6], x[7]), x[8]), m3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+  const float m4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+  return fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), x[15]));
+}
+__device__ __forceinline__ float max_abs16_tree(const float* x) {
+  float a[16];
+#pragma unroll
+  for (int i = 0; i < 16; i++) a[i] = fabsf(x[i]);
+  return max16_tree(a);
+}
+
+// Maximum over all 64 lanes of non-negative float bit patterns (unsigned order = float order;
+// a NaN ranks above +inf): DPP within rows of 16, then v_permlane16_swap and
+// v_permlane32_swap. Integer maxima take the DPP operand directly. Every lane gets the result.
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // quad 1,0,3,2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // quad 2,3,0,1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // half mirror
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));  // mirror
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max(x, max((uint32_t)r[0], (uint32_t)r[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(x, max((uint32_t)q[0], (uint32_t)q[1]));
+}
+
 __device__ __forceinline__ v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 
 // LDS tile swizzles. A 16-byte-per-lane LDS read is served 16 lanes (256 bytes, every bank
