@@ -419,6 +419,23 @@ __device__ __forceinline__ v2i ds_read_tr8(const uint8_t* lds) {
       (__attribute__((address_space(3))) v2i*)((__attribute__((address_space(3))) const uint8_t*)lds));
 }
 
+// The 16 bytes a lane takes from one stored dS block: two transposed reads at `lds` and
+// `lds` + 256, complete when the statement ends. Written as one asm statement that waits for
+// its own LDS results: the compiler treats the builtin read as possibly aliasing the wave's
+// LDS-DMA in flight and would wait for all of that first.
+__device__ __forceinline__ v4i ds_read_tr8_pair(const uint8_t* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)lds;
+  v2i x0, x1;
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %2\n\t"
+      "ds_read_b64_tr_b8 %1, %2 offset:256\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1)
+      : "v"(a)
+      : "memory");
+  return v4i{x0[0], x0[1], x1[0], x1[1]};
+}
+
 // kStore: the accumulator waves also write each dS block to the code store, transposed into
 // the dQ product's operand order: lane l's 16 bytes at 16 l of the block's 1024 bytes (read
 // back by the dQ pass instead of rebuilding dS).
@@ -546,14 +563,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
           for (int qt = 0; qt < 2; qt++) {
             const int qb = (q0_a >> 5) + qt;
             if ((qb << 5) < w.n && (!p.causal || kb <= qb)) {
-              const v2i x0 = ds_read_tr8(cxb + (2 + qt) * 1024 + troff);
-              const v2i x1 = ds_read_tr8(cxb + (2 + qt) * 1024 + 256 + troff);
+              const v4i x = ds_read_tr8_pair(cxb + (2 + qt) * 1024 + troff);
               long long blk, ei;
               ds_block<kPacked>(p, w.s, hq_a, w.doc_start, qb, kb, blk, ei);
               __builtin_nontemporal_store(
-                  v4i{x0[0], x0[1], x1[0], x1[1]},
-                  reinterpret_cast<__attribute__((address_space(1))) v4i*>(scalar_ptr(p.ds_codes + blk * 1024) +
-                                                                          (uint32_t)(lane * 16)));
+                  x, reinterpret_cast<__attribute__((address_space(1))) v4i*>(scalar_ptr(p.ds_codes + blk * 1024) +
+                                                                             (uint32_t)(lane * 16)));
               if (lane == 32 * qt) p.ds_exps[ei] = (uint8_t)(dssc);   // lane 32 qt holds tile qt's exponent
               nst += 2;
             }
