@@ -142,7 +142,7 @@ struct DkvStage {
   alignas(16) uint8_t qss[2 * D];       // Q SEQ scales [group][channel]
   alignas(16) uint8_t gss[2 * D];       // G SEQ scales
   alignas(16) float lse2[kStepQ];       // LSE * log2 e (+inf past the end)
-  alignas(16) float dlt[kStepQ];        // D (0 past the end)
+  alignas(16) float ndlt[kStepQ];       // -D (0 past the end): the E product's initial value
 };
 
 struct KvWork {
@@ -254,6 +254,7 @@ __device__ __forceinline__ void dkv_issue_seq(const BwdParams& p, const KvWork& 
 }
 
 // Store the small item of a step; rows past the end (lane > rmax) get LSE' = +inf, D = 0.
+// D is stored negated: it is the initial accumulator of E, so the product yields E - D.
 template <int D>
 __device__ __forceinline__ void dkv_put(DkvStage<D>& st, uint32_t sv, int rmax, int lw) {
   const int lane = threadIdx.x & 63;
@@ -262,7 +263,7 @@ __device__ __forceinline__ void dkv_put(DkvStage<D>& st, uint32_t sv, int rmax, 
   if (lw == 0) st.qrs[lane] = sv;
   else if (lw == 1) st.grs[lane] = sv;
   else if (lw == 2) st.lse2[lane] = live ? x * kLog2e : INFINITY;
-  else if (lw == 3) st.dlt[lane] = live ? x : 0.f;
+  else if (lw == 3) st.ndlt[lane] = live ? -x : 0.f;
   else if (lw == 4 || lw == 5) {
     if (lane < D / 2) reinterpret_cast<uint32_t*>(lw == 4 ? st.qss : st.gss)[lane] = sv;
   }
@@ -297,7 +298,14 @@ __device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, con
   const int l32 = lane & 31;
   const uint32_t qsw = S.qrs[qt * 32 + l32] >> (8 * hh);
   const uint32_t gsw = S.grs[qt * 32 + l32] >> (8 * hh);
-  v16f sacc = v16f{}, eacc = v16f{};
+  // E starts from -D of the lane's rows (8j + 4hh + u), so the product gives E - D
+  v16f sacc = v16f{}, eacc;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const v4f d4 = *reinterpret_cast<const v4f*>(&S.ndlt[qt * 32 + 8 * j + fidx]);
+#pragma unroll
+    for (int u = 0; u < 4; u++) eacc[4 * j + u] = d4[u];
+  }
 #pragma unroll
   for (int s = 0; s < NS; s++) {
     const int o0 = qt * 32 * D + roff_ab[2 * s], o1 = qt * 32 * D + roff_ab[2 * s + 1];
@@ -312,7 +320,6 @@ __device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, con
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const v4f l4 = *reinterpret_cast<const v4f*>(&S.lse2[qt * 32 + 8 * j + fidx]);
-    const v4f d4 = *reinterpret_cast<const v4f*>(&S.dlt[qt * 32 + 8 * j + fidx]);
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       float x = __builtin_fmaf(sacc[4 * j + u], c, -l4[u]);
@@ -321,14 +328,14 @@ __device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, con
         if (!(kvalid && r < lim && (!causal || r + rel >= 0))) x = -INFINITY;
       }
       P[4 * j + u] = __builtin_amdgcn_exp2f(x);
-      U[4 * j + u] = P[4 * j + u] * (eacc[4 * j + u] - d4[u]);
+      U[4 * j + u] = P[4 * j + u] * eacc[4 * j + u];
     }
   }
-  // P_b exponent per key (the lane's 16 queries and lane ^ 32's); dS exponent per block (whole
-  // wave), computed once in scalar registers
-  float pm = max16_tree(P);
-  pm = fmaxf(pm, swap32(pm));
-  const int pbe = p_scale_exp(pm);
+  // P_b exponent per key (the lane's 16 queries and lane ^ 32's; P >= 0, so its bit patterns
+  // order like the values); dS exponent per block (whole wave), computed once in scalar registers
+  uint32_t pmb = __float_as_uint(max16_tree(P));
+  pmb = max(pmb, __float_as_uint(swap32(__uint_as_float(pmb))));
+  const int pbe = p_scale_exp(__uint_as_float(pmb));
   const float psc = exp2_scale(pbe);
   const uint32_t ub = __builtin_amdgcn_readfirstlane(wave_max_bits(__float_as_uint(max_abs16_tree(U))));
   const int dse = scale_exp_from_bits(ub);
@@ -808,7 +815,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
         const int row = T * 32 + l32;
         const uint32_t ksw = S.krs[row] >> (8 * hh);
         const uint32_t vsw = S.vrs[row] >> (8 * hh);
-        v16f sacc = v16f{}, eacc = v16f{};
+        // E^T starts from -D of the lane's query (as in the dK/dV pass), so it gives E - D
+        v16f sacc = v16f{}, eacc;
+#pragma unroll
+        for (int i = 0; i < 16; i++) eacc[i] = -dl;
 #pragma unroll
         for (int s = 0; s < NS; s++) {
           const int o0 = T * 32 * D + roff_ab[2 * s], o1 = T * 32 * D + roff_ab[2 * s + 1];
@@ -827,7 +837,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
             const int k = kbase + T * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
             if (!(qvalid && k < w.n && (!p.causal || k <= qi))) x = -INFINITY;
           }
-          U[i] = __builtin_amdgcn_exp2f(x) * (eacc[i] - dl);
+          U[i] = __builtin_amdgcn_exp2f(x) * eacc[i];
         }
         const float um = wave_max(max_abs16(U));
         dse[T] = scale_exp_from_bits(__float_as_uint(um));

@@ -70,10 +70,13 @@ __device__ __forceinline__ float exp2_scale(int e) {
 }
 
 // Four E4M3 codes of x / s (RNE, v_cvt_scalef32_pk_fp8_f32; s a power of two), packed
-// little-endian. Equal to pack4_e4m3 of the values times 1/s, without the multiplies.
+// little-endian. Equal to pack4_e4m3 of the values times 1/s, without the multiplies. The
+// instruction writes one half of its destination and keeps the other; the first one starts
+// from a's own bits (its other half is overwritten by the second), so no register has to be
+// cleared first.
 __device__ __forceinline__ uint32_t pack4_e4m3_scaled(float a, float b, float c, float d, float s) {
   typedef short v2s __attribute__((ext_vector_type(2)));
-  const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, s, false);
+  const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, a), a, b, s, false);
   const v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c, d, s, true);
   return __builtin_bit_cast(uint32_t, w);
 }
