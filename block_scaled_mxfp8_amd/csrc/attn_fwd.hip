@@ -10,14 +10,19 @@
 //
 // gfx950 mapping.
 //  * One workgroup = 4 waves = 128 queries of one (batch, head) or (document, head); each
-//    wave owns 32 queries. Keys advance in tiles of 64, staged (codes + E8M0 scales) in LDS,
-//    double-buffered.
+//    wave owns 32 queries. Keys advance in tiles of 64, staged (codes + E8M0 scales) in LDS
+//    in three stages (the loop is unrolled twice so the score registers alternate).
 //  * Scores are computed transposed, S^T = K Q^T, with V_MFMA_SCALE_F32_32X32X64_F8F6F4:
 //    keys are MFMA rows, queries columns, so every lane holds 16 scores of ONE query for each
 //    32-key half tile, and the query's other 16 keys sit in lane ^ 32. Row and group maxima
 //    need one v_permlane32_swap.
-//  * The running max M is an integer (base 2), so 2^(S' - M) and every rescale are exact
-//    powers of two, and the P codes do not depend on M. A 32-key group of one query spans
+//  * The reference max M is an integer (base 2), so 2^(S' - M) and every rescale are exact
+//    powers of two, and the P codes do not depend on M. M may lag the running max by up to
+//    tau = 8 (FLAMIA notes, section 5, the paragraph on the two parameters that bound the
+//    probabilities): the accumulators are rescaled only when a row's tile max exceeds M + tau,
+//    instead of at almost every tile. P's E8M0 group exponents are taken relative to M, so the
+//    lag only multiplies the O accumulator and l by one common power of two (at most 2^8),
+//    which cancels in O = a / l and LSE = M + log2 l. A 32-key group of one query spans
 //    lanes l and l^32; its exponent is ceil(max S' - M - log2 448) and the codes are
 //    RNE_E4M3(2^(S' - M - e)) by one FMA + one v_exp_f32 + the hardware converter.
 //  * The P codes of a lane (16 keys of half tile 0 in bytes 0-15, 16 keys of half tile 1 in
@@ -42,12 +47,13 @@ constexpr int kStages = 3;            // LDS tile buffers: V(j), K(j+1) in use w
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_448 = 8.807354922057604f;
+constexpr float kTau = 8.f;           // largest lag of the reference max behind the running max
 
 // LDS tiles, written by LDS-DMA loads (lane i of a load lands at base + i * size).
-//  k:  K ROW codes [64 keys][d]; the 16-byte chunk c of key row r sits at chunk c ^ (r & 7)
-//      so the 32 rows an operand read touches spread over all banks.
+//  k:  K ROW codes [64 keys][d]; 16-byte chunks swizzled by row (mx_device.h row_swz) so
+//      the rows an operand read touches spread over all banks.
 //  v:  V SEQ codes [2 groups][d channels][32 tokens]; the two 16-byte halves of channel ch
-//      are swapped when (ch >> 2) & 1, for the same reason.
+//      are swapped when (ch >> 3) & 1 (half_swz), for the same reason.
 //  ks: K ROW scales [64 keys][d / 32];  vs: V SEQ scales [2 groups][d].
 template <int D>
 struct FwdSmem {
@@ -67,11 +73,12 @@ struct Work {
   bool valid;
 };
 
+template <bool kPacked>
 __device__ __forceinline__ Work decode_work(const AttnParams& p) {
   const Geom& g = p.geom;
   Work w;
   w.valid = true;
-  if (!packed(g)) {
+  if (!kPacked) {
     const int nqt = (g.seqlen + kBlockM - 1) / kBlockM;
     const long long total = (long long)nqt * p.heads_q * g.batch;
     long long bid = blockIdx.x;
@@ -98,49 +105,81 @@ __device__ __forceinline__ Work decode_work(const AttnParams& p) {
   return w;
 }
 
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Tile loads. Wave w issues the K-code DMA instructions j = w, w + 4, ... (64/NCH key rows
+// of NCH = d/16 chunks each) and the V-code instructions j = w, w + 4, ... (64 x 16 bytes of
+// the [group][channel][32] tile); wave 0 also loads the K scales and wave 1 the V scales. The
+// lane's part of a K-code address, (lane / NCH) * token stride + swizzled chunk * 16, is the
+// same for all of a wave's instructions (the swizzle depends on the row only through the
+// parity of j, which is the wave's), and so is its part of a V-code address (channel lane / 2,
+// logical half (lane & 1) ^ bit 4 of the lane); each is computed once (kl, vl) and added to a
+// wave-uniform base.
+template <int D, bool kPacked>
+__device__ __forceinline__ uint32_t k_lane_off(const AttnParams& p, int wave) {
+  constexpr int NCH = D / 16, RPI = 64 / NCH;
+  const int lane = threadIdx.x & 63;
+  const int row = (wave & 1) * RPI + lane / NCH;   // row of instruction j = wave, mod the swizzle period
+  return (uint32_t)((lane / NCH) * (int)token_stride_k<kPacked>(p.heads_kv, D) + row_swz(row, lane % NCH, NCH) * 16);
+}
+__device__ __forceinline__ uint32_t v_lane_off() {
+  const int lane = threadIdx.x & 63;
+  return (uint32_t)((lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 4) & 1)) << 4));
+}
+
 // Issue the LDS-DMA loads of key tile kt into stage st. Rows past the end of the sequence /
 // document are clamped to its last row (and its last SEQ group): they are finite, and their
 // scores are masked, so their P is 0. LDS-DMA writes at least one dword per lane, so the
 // 2-byte K scales of d = 64 take an ordinary load instead: returned here, stored by
 // put_kscale before the barrier that publishes the tile.
-template <int D>
+template <int D, bool kPacked>
 __device__ __forceinline__ uint32_t issue_tile(const AttnParams& p, const Work& w, int hkv, int kt, FwdSmem<D>& sm,
-                                               int st) {
+                                               int st, uint32_t kl, uint32_t vl) {
+  constexpr int NCH = D / 16, RPI = 64 / NCH;
+  constexpr int NJ = NCH / kWaves;          // K-code (and V-code) instructions per wave
   const Geom& g = p.geom;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const long long sbase = packed(g) ? (long long)w.doc_start : (long long)w.s;
-  constexpr int NCH = D / 16;               // 16-byte chunks per key row
-  const int nlast = w.n - 1;
+  const int wave = wave_id();
+  const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
+  const int k0 = kt * kBlockN;
+  const int rmax = w.n - 1 - k0;            // last row of the tile inside the sequence
+  const int ts = (int)token_stride_k<kPacked>(p.heads_kv, D);
+  const uint8_t* kb = p.k_codes + elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, hkv, k0, 0);
+  if (rmax >= kBlockN - 1) {
+#pragma unroll
+    for (int jj = 0; jj < NJ; jj++) {
+      const int j = wave + jj * kWaves;
+      lds_dma(kb + (uint32_t)(j * RPI * ts) + kl, &sm.k[st][j * 1024], 16);
+    }
+  } else {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int jj = 0; jj < NJ; jj++) {
+      const int j = wave + jj * kWaves;
+      const int r = j * RPI + lane / NCH;
+      const int o = min(r, rmax) * ts + row_swz(r, lane % NCH, NCH) * 16;
+      lds_dma(kb + (uint32_t)o, &sm.k[st][j * 1024], 16);
+    }
+  }
   const int glast = ((w.n + 31) >> 5) - 1;
 #pragma unroll
-  for (int j = wave; j < kBlockN * NCH / 64; j += kWaves) {     // K codes
-    const int pch = j * 64 + lane;
-    const int r = pch / NCH;
-    const int c = row_swz(r, pch % NCH, NCH);
-    const int key = min(kt * kBlockN + r, nlast);
-    lds_dma(p.k_codes + elem_offset(g, p.heads_kv, D, sbase, hkv, key, c * 16), &sm.k[st][j * 1024], 16);
-  }
-#pragma unroll
-  for (int j = wave; j < 4 * D / 64; j += kWaves) {             // V codes (2 groups x D x 2 halves)
-    const int pch = j * 64 + lane;
-    const int grp = pch / (2 * D);
-    const int ch = (pch % (2 * D)) >> 1;
-    const int half = half_swz(ch, pch & 1);
-    const int gi = min(2 * kt + grp, glast);
-    const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
-    lds_dma(p.v_codes + (row * D + ch) * 32 + half * 16, &sm.v[st][j * 1024], 16);
+  for (int jj = 0; jj < NJ; jj++) {         // V codes (2 groups x D channels x 2 halves)
+    const int j = wave + jj * kWaves;
+    const int gi = min(2 * kt + (j * 64) / (2 * D), glast);
+    const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
+    lds_dma(p.v_codes + row * (D * 32) + ((j * 64) % (2 * D)) * 16 + vl, &sm.v[st][j * 1024], 16);
   }
   uint32_t kscale = 0;
-  if (wave == 0) {                                               // K scales, one key per lane
-    const int key = min(kt * kBlockN + lane, nlast);
-    const uint8_t* src = p.k_scales + (elem_offset(g, p.heads_kv, D, sbase, hkv, key, 0) >> 5);
+  const int lane = threadIdx.x & 63;
+  if (wave == 0) {                          // K scales, one key per lane
+    const uint8_t* src = p.k_scales + (elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, hkv, k0, 0) >> 5) +
+                         ((uint32_t)(min(lane, rmax) * ts) >> 5);
     if (D == 128) lds_dma(src, sm.ks[st], 4);
     else kscale = *reinterpret_cast<const uint16_t*>(src);
-  } else if (wave == 1 && lane < D / 2) {                        // V scales, one dword per lane
-    const int gi = min(2 * kt + (lane * 4) / D, glast);
-    const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
-    lds_dma(p.v_scales + row * D + (lane * 4) % D, sm.vs[st], 4);
+  } else if (wave == 1 && lane < D / 2) {   // V scales: lane's dword of the groups 2kt, 2kt + 1
+    // (adjacent rows); past the last group the second half repeats the first
+    const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, hkv, w.doc_start, 2 * kt);
+    const uint32_t o = (uint32_t)(2 * kt + 1 <= glast ? lane * 4 : (lane * 4) % D);
+    lds_dma(p.v_scales + row * D + o, sm.vs[st], 4);
   }
   return kscale;
 }
@@ -173,27 +212,36 @@ __device__ __forceinline__ void scores(const FwdSmem<D>& sm, int st, const v8i* 
   }
 }
 
-template <int D>
+// Largest of the 16 accumulator values of a lane (depth-3 tree of three-input maxima).
+__device__ __forceinline__ float vmax16(const v16f& x) {
+  const float m0 = fmaxf(fmaxf(x[0], x[1]), x[2]), m1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+  const float m2 = fmaxf(fmaxf(x[6], x[7]), x[8]), m3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+  const float m4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+  return fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), x[15]));
+}
+
+template <int D, bool kPacked>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<D> sm;
-  const Work w = decode_work(p);
+  const Work w = decode_work<kPacked>(p);
   if (!w.valid) return;
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int hh = lane >> 5;     // lane half
   const int l32 = lane & 31;
   const int hkv = w.h / (p.heads_q / p.heads_kv);
-  const long long sbase = packed(g) ? (long long)w.doc_start : (long long)w.s;
+  const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
   const int q0 = w.qt * kBlockM;             // first query of the workgroup
   const int qw = q0 + wave * 32;             // first query of this wave
   const int qi = qw + l32;                   // this lane's query
   const bool qvalid = qi < w.n;
   const int kend = p.causal ? min(w.n, q0 + kBlockM) : w.n;  // keys this workgroup needs
   const int nkt = (kend + kBlockN - 1) / kBlockN;
+  const uint32_t kl = k_lane_off<D, kPacked>(p, wave), vl = v_lane_off();
 
-  put_kscale<D>(sm, 0, issue_tile<D>(p, w, hkv, 0, sm, 0));
-  if (nkt > 1) put_kscale<D>(sm, 1, issue_tile<D>(p, w, hkv, 1, sm, 1));
+  put_kscale<D>(sm, 0, issue_tile<D, kPacked>(p, w, hkv, 0, sm, 0, kl, vl));
+  if (nkt > 1) put_kscale<D>(sm, 1, issue_tile<D, kPacked>(p, w, hkv, 1, sm, 1, kl, vl));
 
   // ---- Q operand (B of S^T = K Q^T), kept in registers ----
   constexpr int NS = D / 64;  // contraction steps of 64 over d
@@ -202,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
   for (int s = 0; s < NS; s++) {
     if (qvalid) {
-      const long long off = elem_offset(g, p.heads_q, D, sbase, w.h, qi, 64 * s);
+      const long long off = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, w.h, qi, 64 * s);
       qop[s] = cat(*reinterpret_cast<const v4i*>(p.q_codes + off + 16 * hh),
                    *reinterpret_cast<const v4i*>(p.q_codes + off + 32 + 16 * hh));
       qsc[s] = p.q_scales[(off >> 5) + hh];
@@ -214,54 +262,54 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   const float c = p.scale * kLog2e;   // S' = acc * c (base-2 logits)
   // a wave is idle for key tile j when all its keys follow all its queries (causal) or it has no queries
   auto active = [&](int j) { return qw < w.n && !(p.causal && j * kBlockN > qw + 31); };
+  // keys visible to this lane's query: [0, vis_end)
+  const int vis_end = p.causal ? min(w.n, qi + 1) : w.n;
 
   v16f oacc[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; t++) oacc[t] = v16f{};
-  float M = -INFINITY;  // integer running max (base 2)
+  float M = -INFINITY;  // reference max (an integer, base 2), at most kTau below the running max
   float lsum = 0.f;     // this lane's share of l (its 16 keys of every half tile)
 
   wait_vmem();
   __syncthreads();
-  v16f sacc[2], snext[2];
-  if (active(0)) scores<D>(sm, 0, qop, qsc, sacc);
+  v16f sa[2], sb[2];
+  if (active(0)) scores<D>(sm, 0, qop, qsc, sa);
 
-  for (int kt = 0; kt < nkt; kt++) {
+  // One key tile: issue the loads of tile kt + 2, put the scores of tile kt + 1 on the matrix
+  // cores (into nxt) while this tile's softmax (on cur) runs on the VALU, then P V.
+  auto tile = [&](int kt, v16f(&cur)[2], v16f(&nxt)[2]) __attribute__((always_inline)) {
     const int st = kt % kStages;
     uint32_t kscale = 0;
-    if (kt + 2 < nkt) kscale = issue_tile<D>(p, w, hkv, kt + 2, sm, (kt + 2) % kStages);
-    // scores of the next tile go to the matrix cores while this tile's softmax runs on the VALU
-    if (kt + 1 < nkt && active(kt + 1)) scores<D>(sm, (kt + 1) % kStages, qop, qsc, snext);
+    if (kt + 2 < nkt) kscale = issue_tile<D, kPacked>(p, w, hkv, kt + 2, sm, (kt + 2) % kStages, kl, vl);
+    if (kt + 1 < nkt && active(kt + 1)) scores<D>(sm, (kt + 1) % kStages, qop, qsc, nxt);
     const int kbase = kt * kBlockN;
     if (active(kt)) {
-      // ---- mask (diagonal / tail tiles only) ----
+      // ---- mask (diagonal / tail tiles only): the lane's key T*32 + 8(i>>2) + 4hh + (i&3)
+      //      of the tile is visible when it is below vis_end ----
       const bool need_mask = (p.causal && kbase + kBlockN - 1 > qw) || kbase + kBlockN > w.n;
       if (need_mask) {
+        const int lim = vis_end - kbase - 4 * hh;
 #pragma unroll
         for (int T = 0; T < 2; T++)
 #pragma unroll
-          for (int i = 0; i < 16; i++) {
-            const int key = kbase + T * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            const bool vis = key < w.n && (!p.causal || key <= qi);
-            sacc[T][i] = vis ? sacc[T][i] : -INFINITY;
-          }
+          for (int i = 0; i < 16; i++)
+            if (T * 32 + 8 * (i >> 2) + (i & 3) >= lim) cur[T][i] = -INFINITY;
       }
       // ---- row / group maxima (raw accumulator units; c > 0) ----
-      float gm0 = fmaxf(sacc[0][0], sacc[0][1]), gm1 = fmaxf(sacc[1][0], sacc[1][1]);
-#pragma unroll
-      for (int i = 2; i < 16; i += 2) {
-        gm0 = fmaxf(fmaxf(gm0, sacc[0][i]), sacc[0][i + 1]);
-        gm1 = fmaxf(fmaxf(gm1, sacc[1][i]), sacc[1][i + 1]);
-      }
+      float gm0 = vmax16(cur[0]), gm1 = vmax16(cur[1]);
       gm0 = fmaxf(gm0, swap32(gm0));
       gm1 = fmaxf(gm1, swap32(gm1));
-      const float Mnew = fmaxf(M, ceilf(fmaxf(gm0, gm1) * c));
-      if (__builtin_amdgcn_ballot_w64(Mnew > M)) {
-        const float f = (Mnew > M) ? __builtin_amdgcn_exp2f(M - Mnew) : 1.f;   // power of two (0 when M = -inf)
+      // ---- reference max: moves (rescaling the accumulators) only when the tile's row max
+      //      exceeds it by more than kTau ----
+      const float mt = ceilf(fmaxf(gm0, gm1) * c);
+      const bool up = mt > M + kTau;
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float f = up ? __builtin_amdgcn_exp2f(M - mt) : 1.f;   // power of two (0 when M = -inf)
         lsum *= f;
 #pragma unroll
         for (int t = 0; t < D / 32; t++) oacc[t] *= f;
-        M = Mnew;
+        M = up ? mt : M;
       }
       // ---- group exponents and P codes: y = 2^(S' - M - e), e = ceil(max S' - M - log2 448) ----
       const bool rowlive = M > -INFINITY;
@@ -269,20 +317,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       const float e1 = fminf(fmaxf(ceilf(gm1 * c - M - kLog2_448), -127.f), 127.f);
       const float off0 = rowlive ? M + e0 : 0.f;
       const float off1 = rowlive ? M + e1 : 0.f;
-      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; i++) {
-        sacc[0][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[0][i], c, -off0));
-        sacc[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[1][i], c, -off1));
-        s0 += sacc[0][i];
-        s1 += sacc[1][i];
+        cur[0][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[0][i], c, -off0));
+        cur[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[1][i], c, -off1));
+      }
+      float s0 = cur[0][0], s1 = cur[1][0];
+#pragma unroll
+      for (int i = 1; i < 16; i++) {
+        s0 += cur[0][i];
+        s1 += cur[1][i];
       }
       lsum += ldexpf(s0, (int)e0) + ldexpf(s1, (int)e1);
       v8i pop;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        pop[j] = (int)pack4_e4m3(sacc[0][4 * j], sacc[0][4 * j + 1], sacc[0][4 * j + 2], sacc[0][4 * j + 3]);
-        pop[4 + j] = (int)pack4_e4m3(sacc[1][4 * j], sacc[1][4 * j + 1], sacc[1][4 * j + 2], sacc[1][4 * j + 3]);
+        pop[j] = (int)pack4_e4m3(cur[0][4 * j], cur[0][4 * j + 1], cur[0][4 * j + 2], cur[0][4 * j + 3]);
+        pop[4 + j] = (int)pack4_e4m3(cur[1][4 * j], cur[1][4 * j + 1], cur[1][4 * j + 2], cur[1][4 * j + 3]);
       }
       const int psc = (int)(hh ? e1 : e0) + 127;
       // ---- O^T += V^T P^T ----
@@ -295,13 +346,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
         oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), pop, oacc[t], 0, 0, 0, vsc, 0, psc);
       }
     }
-    sacc[0] = snext[0];
-    sacc[1] = snext[1];
     if (kt + 2 < nkt) put_kscale<D>(sm, (kt + 2) % kStages, kscale);
     if (kt + 1 < nkt) {
       wait_vmem();
       __syncthreads();
     }
+  };
+  // two tiles per iteration, so the score registers alternate without copies
+  for (int kt = 0; kt < nkt; kt += 2) {
+    tile(kt, sa, sb);
+    if (kt + 1 < nkt) tile(kt + 1, sb, sa);
   }
 
   // ---- epilogue: O = a / l, LSE = (M + log2 l) ln 2 ----
@@ -309,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   if (!qvalid) return;
   const bool any = l > 0.f;
   const float inv = any ? 1.f / l : 0.f;
-  const long long obase = elem_offset(g, p.heads_q, D, sbase, w.h, qi, 0);
+  const long long obase = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, w.h, qi, 0);
 #pragma unroll
   for (int t = 0; t < D / 32; t++) {
 #pragma unroll
@@ -327,8 +381,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     }
   }
   if (hh == 0) {
-    const long long li = packed(g) ? ((long long)(w.doc_start + qi) * p.heads_q + w.h)
-                                   : (((long long)w.s * p.heads_q + w.h) * g.seqlen + qi);
+    const long long li = token_index_k<kPacked>(g, p.heads_q, w.s, w.doc_start, w.h, qi);
     p.lse[li] = any ? (M + __log2f(l)) * kLn2 : INFINITY;
   }
 }
@@ -346,8 +399,13 @@ hipError_t launch_attn_fwd(const AttnParams& p, hipStream_t stream) {
   }
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
   const int slot = profile_begin(kProfFwd, stream);
-  if (p.head_dim == 128) hipLaunchKernelGGL((attn_fwd_kernel<128>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((attn_fwd_kernel<64>), grid, dim3(256), 0, stream, p);
+  if (packed(g)) {
+    if (p.head_dim == 128) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (p.head_dim == 128) hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, dim3(256), 0, stream, p);
+  }
   profile_end(slot, stream);
   return hipGetLastError();
 }

@@ -40,9 +40,11 @@ __device__ __forceinline__ int scale_exp_from_bits(uint32_t abits) {
   return e < kExpMin ? kExpMin : (e > kExpMax ? kExpMax : e);
 }
 
-// Four E4M3 codes (RNE) packed little-endian into one dword.
+// Four E4M3 codes (RNE) packed little-endian into one dword. Each conversion writes one half
+// of its destination and keeps the other; the first starts from a's own bits (its other half
+// is overwritten by the second), so no register has to be cleared first.
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
