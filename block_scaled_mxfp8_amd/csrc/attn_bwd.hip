@@ -157,13 +157,9 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
   w.valid = true;
   if (!kPacked) {
     const int nkb = (g.seqlen + kBlockK - 1) / kBlockK;
-    const long long total = (long long)nkb * p.heads_kv * g.batch;
-    long long bid = blockIdx.x;
-    // a contiguous range of work items per XCD (workgroups go round-robin over the 8 XCDs),
-    // so the key blocks of a head share one L2; causal: small kb = most queries, first
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int bh = (int)(bid / nkb);
-    w.kb = (int)(bid % nkb);
+    int bh, rank;
+    lpt_order(blockIdx.x, p.heads_kv * g.batch, nkb, bh, rank);
+    w.kb = rank;                          // causal: the first key block sees the most queries
     w.s = bh / p.heads_kv;
     w.hkv = bh % p.heads_kv;
     w.doc_start = 0;
@@ -657,12 +653,9 @@ __device__ __forceinline__ QWork decode_q(const BwdParams& p) {
   w.valid = true;
   if (!packed(g)) {
     const int nqb = (g.seqlen + kBlockQ - 1) / kBlockQ;
-    const long long total = (long long)nqb * p.heads_q * g.batch;
-    long long bid = blockIdx.x;
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int bh = (int)(bid / nqb);
-    int qb = (int)(bid % nqb);
-    if (p.causal) qb = nqb - 1 - qb;     // most keys first
+    int bh, rank;
+    lpt_order(blockIdx.x, p.heads_q * g.batch, nqb, bh, rank);
+    const int qb = p.causal ? nqb - 1 - rank : rank;   // causal: the last query block sees the most keys
     w.s = bh / p.heads_q;
     w.h = bh % p.heads_q;
     w.qb = qb;

@@ -54,12 +54,13 @@ constexpr float kTau = 8.f;           // largest lag of the reference max behind
 //      the rows an operand read touches spread over all banks.
 //  v:  V SEQ codes [2 groups][d channels][32 tokens]; the two 16-byte halves of channel ch
 //      are swapped when (ch >> 3) & 1 (half_swz), for the same reason.
-//  ks: K ROW scales [64 keys][d / 32];  vs: V SEQ scales [2 groups][d].
+//  ks: K ROW scales, one dword per key (its d/32 bytes; at d = 64 the upper half is unused);
+//  vs: V SEQ scales [2 groups][d].
 template <int D>
 struct FwdSmem {
   alignas(16) uint8_t k[kStages][kBlockN * D];
   alignas(16) uint8_t v[kStages][2 * D * 32];
-  alignas(16) uint8_t ks[kStages][kBlockN * (D / 32)];
+  alignas(16) uint32_t ks[kStages][kBlockN];
   alignas(16) uint8_t vs[kStages][2 * D];
 };
 
@@ -80,17 +81,11 @@ __device__ __forceinline__ Work decode_work(const AttnParams& p) {
   w.valid = true;
   if (!kPacked) {
     const int nqt = (g.seqlen + kBlockM - 1) / kBlockM;
-    const long long total = (long long)nqt * p.heads_q * g.batch;
-    long long bid = blockIdx.x;
-    // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2): give
-    // each XCD a contiguous range of work items so a head's K/V tiles stay in one L2.
-    if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-    const int bh = (int)(bid / nqt);
-    int qt = (int)(bid % nqt);
-    if (p.causal) qt = nqt - 1 - qt;  // longest rows first
+    int bh, rank;
+    lpt_order(blockIdx.x, p.heads_q * g.batch, nqt, bh, rank);
     w.s = bh / p.heads_q;
     w.h = bh % p.heads_q;
-    w.qt = qt;
+    w.qt = p.causal ? nqt - 1 - rank : rank;  // causal: the last query tile sees the most keys
     w.doc_start = 0;
     w.n = g.seqlen;
   } else {
@@ -127,16 +122,19 @@ __device__ __forceinline__ uint32_t v_lane_off() {
   return (uint32_t)((lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 4) & 1)) << 4));
 }
 
-// Issue the LDS-DMA loads of key tile kt into stage st. Rows past the end of the sequence /
-// document are clamped to its last row (and its last SEQ group): they are finite, and their
-// scores are masked, so their P is 0. LDS-DMA writes at least one dword per lane, so the
-// 2-byte K scales of d = 64 take an ordinary load instead: returned here, stored by
-// put_kscale before the barrier that publishes the tile.
+// Issue the LDS-DMA loads of key tile kt into stage st: kNj K-code and kNj V-code
+// instructions per wave, plus one scale load on waves 0 and 1. Rows past the end
+// of the sequence / document are clamped to its last row (and its last SEQ group): they are
+// finite, and their scores are masked, so their P is 0. At d = 64 the K scales are a 2-byte
+// DMA per key, which lands in the low half of the key's dword.
+template <int D>
+constexpr int kNj = D / 16 / kWaves;
+
 template <int D, bool kPacked>
-__device__ __forceinline__ uint32_t issue_tile(const AttnParams& p, const Work& w, int hkv, int kt, FwdSmem<D>& sm,
+__device__ __forceinline__ void issue_tile(const AttnParams& p, const Work& w, int hkv, int kt, FwdSmem<D>& sm,
                                                int st, uint32_t kl, uint32_t vl) {
   constexpr int NCH = D / 16, RPI = 64 / NCH;
-  constexpr int NJ = NCH / kWaves;          // K-code (and V-code) instructions per wave
+  constexpr int NJ = kNj<D>;                // K-code (and V-code) instructions per wave
   const Geom& g = p.geom;
   const int wave = wave_id();
   const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
@@ -168,26 +166,19 @@ __device__ __forceinline__ uint32_t issue_tile(const AttnParams& p, const Work& 
     const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
     lds_dma(p.v_codes + row * (D * 32) + ((j * 64) % (2 * D)) * 16 + vl, &sm.v[st][j * 1024], 16);
   }
-  uint32_t kscale = 0;
   const int lane = threadIdx.x & 63;
   if (wave == 0) {                          // K scales, one key per lane
     const uint8_t* src = p.k_scales + (elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, hkv, k0, 0) >> 5) +
                          ((uint32_t)(min(lane, rmax) * ts) >> 5);
-    if (D == 128) lds_dma(src, sm.ks[st], 4);
-    else kscale = *reinterpret_cast<const uint16_t*>(src);
+    lds_dma(src, sm.ks[st], D / 32);
   } else if (wave == 1 && lane < D / 2) {   // V scales: lane's dword of the groups 2kt, 2kt + 1
     // (adjacent rows); past the last group the second half repeats the first
     const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, hkv, w.doc_start, 2 * kt);
     const uint32_t o = (uint32_t)(2 * kt + 1 <= glast ? lane * 4 : (lane * 4) % D);
     lds_dma(p.v_scales + row * D + o, sm.vs[st], 4);
   }
-  return kscale;
 }
 
-template <int D>
-__device__ __forceinline__ void put_kscale(FwdSmem<D>& sm, int st, uint32_t kscale) {
-  if (D == 64 && threadIdx.x < 64) *reinterpret_cast<uint16_t*>(&sm.ks[st][threadIdx.x * 2]) = (uint16_t)kscale;
-}
 
 // S^T for the two 32-key half tiles of stage st: keys are MFMA rows, the wave's 32 queries columns.
 template <int D>
@@ -196,17 +187,21 @@ __device__ __forceinline__ void scores(const FwdSmem<D>& sm, int st, const v8i* 
   const int hh = lane >> 5, l32 = lane & 31;
   constexpr int NS = D / 64;
   constexpr int NCH = D / 16;
+  uint32_t ksw[2];
 #pragma unroll
   for (int T = 0; T < 2; T++) {
-    const int row = T * 32 + l32;
-    const uint32_t ksw = (D == 128) ? *reinterpret_cast<const uint32_t*>(&sm.ks[st][row * 4])
-                                    : (uint32_t)*reinterpret_cast<const uint16_t*>(&sm.ks[st][row * 2]);
+    ksw[T] = sm.ks[st][T * 32 + l32];
     sacc[T] = v16f{};
+  }
+  // the two half tiles' products alternate, so consecutive MFMAs are independent
 #pragma unroll
-    for (int s = 0; s < NS; s++) {
+  for (int s = 0; s < NS; s++) {
+#pragma unroll
+    for (int T = 0; T < 2; T++) {
+      const int row = T * 32 + l32;
       const v4i a = *reinterpret_cast<const v4i*>(&sm.k[st][row * D + (row_swz(row, 4 * s + hh, NCH) << 4)]);
       const v4i b = *reinterpret_cast<const v4i*>(&sm.k[st][row * D + (row_swz(row, 4 * s + 2 + hh, NCH) << 4)]);
-      const int ksc = (ksw >> (8 * (2 * s + hh))) & 0xFF;
+      const int ksc = (ksw[T] >> (8 * (2 * s + hh))) & 0xFF;
       sacc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), qop[s], sacc[T], 0, 0, 0, ksc, 0, qsc[s]);
     }
   }
@@ -240,8 +235,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   const int nkt = (kend + kBlockN - 1) / kBlockN;
   const uint32_t kl = k_lane_off<D, kPacked>(p, wave), vl = v_lane_off();
 
-  put_kscale<D>(sm, 0, issue_tile<D, kPacked>(p, w, hkv, 0, sm, 0, kl, vl));
-  if (nkt > 1) put_kscale<D>(sm, 1, issue_tile<D, kPacked>(p, w, hkv, 1, sm, 1, kl, vl));
+  issue_tile<D, kPacked>(p, w, hkv, 0, sm, 0, kl, vl);
+  if (nkt > 1) issue_tile<D, kPacked>(p, w, hkv, 1, sm, 1, kl, vl);
 
   // ---- Q operand (B of S^T = K Q^T), kept in registers ----
   constexpr int NS = D / 64;  // contraction steps of 64 over d
@@ -280,8 +275,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   // cores (into nxt) while this tile's softmax (on cur) runs on the VALU, then P V.
   auto tile = [&](int kt, v16f(&cur)[2], v16f(&nxt)[2]) __attribute__((always_inline)) {
     const int st = kt % kStages;
-    uint32_t kscale = 0;
-    if (kt + 2 < nkt) kscale = issue_tile<D, kPacked>(p, w, hkv, kt + 2, sm, (kt + 2) % kStages, kl, vl);
+    if (kt + 2 < nkt) issue_tile<D, kPacked>(p, w, hkv, kt + 2, sm, (kt + 2) % kStages, kl, vl);
     if (kt + 1 < nkt && active(kt + 1)) scores<D>(sm, (kt + 1) % kStages, qop, qsc, nxt);
     const int kbase = kt * kBlockN;
     if (active(kt)) {
@@ -346,10 +340,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
         oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), pop, oacc[t], 0, 0, 0, vsc, 0, psc);
       }
     }
-    if (kt + 2 < nkt) put_kscale<D>(sm, (kt + 2) % kStages, kscale);
+    // publish tile kt + 1. (Waiting here also for tile kt + 2's loads, issued at the top of
+    // this iteration, measured slightly faster than leaving them in flight.)
     if (kt + 1 < nkt) {
       wait_vmem();
-      __syncthreads();
+      wg_barrier();
     }
   };
   // two tiles per iteration, so the score registers alternate without copies

@@ -154,14 +154,18 @@ __device__ __forceinline__ int row_swz(int row, int chunk, int nchunk) {
 __device__ __forceinline__ int half_swz(int c, int half) { return half ^ ((c >> 3) & 1); }
 
 // LDS-DMA load (global_load_lds): lane i's `size` bytes (16 or 4) land at lds + i * size;
-// `lds` must be the same for the whole wave. Completion is counted by vmcnt.
+// with size 2 they land in the low half of the dword at lds + 4 i. `lds` must be the same for
+// the whole wave. Completion is counted by vmcnt.
 __device__ __forceinline__ void lds_dma(const void* src, void* lds, int size) {
   if (size == 16)
     __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-  else
+  else if (size == 4)
     __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds, 2, 0, 0);
 }
 
 // A wave-uniform pointer held in scalar registers. Adding a 32-bit lane offset to it gives

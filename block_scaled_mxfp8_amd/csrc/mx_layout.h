@@ -64,6 +64,32 @@ __host__ __device__ inline long long token_index_k(const Geom& g, int heads, int
   return kPacked ? ((long long)(doc_start + t) * heads + h) : (((long long)s * heads + h) * g.seqlen + t);
 }
 
+// Work order of a batched launch over nbh (sequence, head) pairs x nt tiles per pair, one
+// workgroup per (pair, tile); rank 0 is the most expensive tile of a pair. Workgroups go
+// round-robin to the 8 XCDs (each with its own L2), so XCD x receives workgroups x, x + 8, ...
+// and dispatches them in that order as slots free up. Each XCD gets a contiguous range of
+// pairs (when nbh is a multiple of 8); inside it, chunks of 4 pairs are dispatched with the
+// ranks in increasing order and the pairs inner. So the costliest tiles of the last pairs do
+// not start last (a pair-by-pair order leaves them running alone at the end of the launch),
+// and the pairs in flight, whose K and V share the L2, stay few.
+__device__ inline void lpt_order(long long bid, int nbh, int nt, int& pair, int& rank) {
+  constexpr int kChunk = 4;
+  long long j = bid;
+  int p0 = 0, np = nbh;
+  if ((nbh & 7) == 0) {
+    np = nbh >> 3;
+    p0 = (int)(bid & 7) * np;
+    j = bid >> 3;
+  }
+  const long long cj = (long long)kChunk * nt;
+  const int chunk = (int)(j / cj);
+  const int c0 = chunk * kChunk;
+  const int cc = min(kChunk, np - c0);
+  const int r = (int)(j - chunk * cj);
+  rank = r / cc;
+  pair = p0 + c0 + r % cc;
+}
+
 // Byte position of token offset t (0..31) inside a 32-byte SEQ-view group. It matches the
 // K order of the gfx950 32x32x64 MFMA operand built from an accumulator tile: lanes 0-31
 // carry tokens {0-3, 8-11, 16-19, 24-27} in bytes 0-15, lanes 32-63 the rest.
