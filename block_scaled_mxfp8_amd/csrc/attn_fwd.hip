@@ -10,8 +10,9 @@
 //
 // gfx950 mapping.
 //  * One workgroup = 4 waves = 128 queries of one (batch, head) or (document, head); each
-//    wave owns 32 queries. Keys advance in tiles of 64, staged (codes + E8M0 scales) in LDS
-//    in three stages (the loop is unrolled twice so the score registers alternate).
+//    wave owns 32 queries. Keys advance in tiles of 64, staged (codes + E8M0 scales) in LDS,
+//    K two tiles ahead and V one tile ahead, two slots each; the loop is unrolled twice, so
+//    slot indices are constants and the score registers alternate without copies.
 //  * Scores are computed transposed, S^T = K Q^T, with V_MFMA_SCALE_F32_32X32X64_F8F6F4:
 //    keys are MFMA rows, queries columns, so every lane holds 16 scores of ONE query for each
 //    32-key half tile, and the query's other 16 keys sit in lane ^ 32. Row and group maxima
@@ -36,6 +37,8 @@
 #include "mx_layout.h"
 #include "mx_profile.h"
 
+#include <type_traits>
+
 namespace mx {
 
 namespace {
@@ -43,7 +46,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBlockM = 32 * kWaves;  // queries per workgroup
 constexpr int kBlockN = 64;           // keys per tile
-constexpr int kStages = 3;            // LDS tile buffers: V(j), K(j+1) in use while tile j+2 lands
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_448 = 8.807354922057604f;
@@ -56,12 +58,14 @@ constexpr float kTau = 8.f;           // largest lag of the reference max behind
 //      are swapped when (ch >> 3) & 1 (half_swz), for the same reason.
 //  ks: K ROW scales, one dword per key (its d/32 bytes; at d = 64 the upper half is unused);
 //  vs: V SEQ scales [2 groups][d].
+// K and V tiles have two slots each: K(j) sits in slot j % 2 and is loaded two tiles ahead
+// (the scores of tile j + 1 are computed during tile j), V(j) in slot j % 2, one tile ahead.
 template <int D>
 struct FwdSmem {
-  alignas(16) uint8_t k[kStages][kBlockN * D];
-  alignas(16) uint8_t v[kStages][2 * D * 32];
-  alignas(16) uint32_t ks[kStages][kBlockN];
-  alignas(16) uint8_t vs[kStages][2 * D];
+  alignas(16) uint8_t k[2][kBlockN * D];
+  alignas(16) uint8_t v[2][2 * D * 32];
+  alignas(16) uint32_t ks[2][kBlockN];
+  alignas(16) uint8_t vs[2][2 * D];
 };
 
 // Work decode: which (sequence, head, query tile) this workgroup computes.
@@ -122,65 +126,92 @@ __device__ __forceinline__ uint32_t v_lane_off() {
   return (uint32_t)((lane >> 1) * 32 + (((lane & 1) ^ ((lane >> 4) & 1)) << 4));
 }
 
-// Issue the LDS-DMA loads of key tile kt into stage st: kNj K-code and kNj V-code
-// instructions per wave, plus one scale load on waves 0 and 1. Rows past the end
-// of the sequence / document are clamped to its last row (and its last SEQ group): they are
-// finite, and their scores are masked, so their P is 0. At d = 64 the K scales are a 2-byte
-// DMA per key, which lands in the low half of the key's dword.
+// Wave-uniform bases of the K and V streams of one (sequence or document, KV head).
+struct KvBase {
+  const uint8_t* k;    // K ROW codes of key 0
+  const uint8_t* ks;   // K ROW scales of key 0
+  const uint8_t* v;    // V SEQ codes of group 0 (the groups of a sequence are consecutive rows)
+  const uint8_t* vs;   // V SEQ scales of group 0
+  int ts;              // token stride of K, in elements (= bytes of codes)
+  int n;               // tokens
+};
+
+template <int D, bool kPacked>
+__device__ __forceinline__ KvBase kv_base(const AttnParams& p, const Work& w, int hkv) {
+  const Geom& g = p.geom;
+  const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
+  const long long k0 = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, hkv, 0, 0);
+  const long long row0 = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, hkv, w.doc_start, 0);
+  KvBase b;
+  b.k = p.k_codes + k0;
+  b.ks = p.k_scales + (k0 >> 5);
+  b.v = p.v_codes + row0 * (D * 32);
+  b.vs = p.v_scales + row0 * D;
+  b.ts = (int)token_stride_k<kPacked>(p.heads_kv, D);
+  b.n = w.n;
+  return b;
+}
+
+// Issue the LDS-DMA loads of K tile kt into `kt_lds` / `ks_lds`: kNj code instructions per
+// wave, and on wave 0 the scales (one key per lane; at d = 64 a 2-byte DMA, which lands in
+// the low half of the key's dword). Rows past the end of the sequence / document are clamped
+// to its last row: they are finite, and their scores are masked, so their P is 0.
 template <int D>
 constexpr int kNj = D / 16 / kWaves;
 
-template <int D, bool kPacked>
-__device__ __forceinline__ void issue_tile(const AttnParams& p, const Work& w, int hkv, int kt, FwdSmem<D>& sm,
-                                               int st, uint32_t kl, uint32_t vl) {
+template <int D>
+__device__ __forceinline__ void issue_k(const KvBase& b, int kt, int wave, uint8_t* kt_lds, uint32_t* ks_lds,
+                                        uint32_t kl, uint32_t ksl) {
   constexpr int NCH = D / 16, RPI = 64 / NCH;
-  constexpr int NJ = kNj<D>;                // K-code (and V-code) instructions per wave
-  const Geom& g = p.geom;
-  const int wave = wave_id();
-  const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
   const int k0 = kt * kBlockN;
-  const int rmax = w.n - 1 - k0;            // last row of the tile inside the sequence
-  const int ts = (int)token_stride_k<kPacked>(p.heads_kv, D);
-  const uint8_t* kb = p.k_codes + elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, hkv, k0, 0);
+  const int rmax = b.n - 1 - k0;            // last row of the tile inside the sequence
+  const uint8_t* kb = b.k + (long long)k0 * b.ts;
+  const uint8_t* ksb = b.ks + (((long long)k0 * b.ts) >> 5);
   if (rmax >= kBlockN - 1) {
 #pragma unroll
-    for (int jj = 0; jj < NJ; jj++) {
+    for (int jj = 0; jj < kNj<D>; jj++) {
       const int j = wave + jj * kWaves;
-      lds_dma(kb + (uint32_t)(j * RPI * ts) + kl, &sm.k[st][j * 1024], 16);
+      lds_dma_so(kb + (long long)j * RPI * b.ts, kl, kt_lds + j * 1024, 16);
     }
+    if (wave == 0) lds_dma_so(ksb, ksl, ks_lds, D / 32);
+    asm volatile("" ::: "memory");        // keeps the clamped path's loads separate
   } else {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int jj = 0; jj < NJ; jj++) {
+    for (int jj = 0; jj < kNj<D>; jj++) {
       const int j = wave + jj * kWaves;
       const int r = j * RPI + lane / NCH;
-      const int o = min(r, rmax) * ts + row_swz(r, lane % NCH, NCH) * 16;
-      lds_dma(kb + (uint32_t)o, &sm.k[st][j * 1024], 16);
+      const int o = min(r, rmax) * b.ts + row_swz(r, lane % NCH, NCH) * 16;
+      lds_dma(kb + (uint32_t)o, kt_lds + j * 1024, 16);
     }
-  }
-  const int glast = ((w.n + 31) >> 5) - 1;
-#pragma unroll
-  for (int jj = 0; jj < NJ; jj++) {         // V codes (2 groups x D channels x 2 halves)
-    const int j = wave + jj * kWaves;
-    const int gi = min(2 * kt + (j * 64) / (2 * D), glast);
-    const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
-    lds_dma(p.v_codes + row * (D * 32) + ((j * 64) % (2 * D)) * 16 + vl, &sm.v[st][j * 1024], 16);
-  }
-  const int lane = threadIdx.x & 63;
-  if (wave == 0) {                          // K scales, one key per lane
-    const uint8_t* src = p.k_scales + (elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, hkv, k0, 0) >> 5) +
-                         ((uint32_t)(min(lane, rmax) * ts) >> 5);
-    lds_dma(src, sm.ks[st], D / 32);
-  } else if (wave == 1 && lane < D / 2) {   // V scales: lane's dword of the groups 2kt, 2kt + 1
-    // (adjacent rows); past the last group the second half repeats the first
-    const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, hkv, w.doc_start, 2 * kt);
-    const uint32_t o = (uint32_t)(2 * kt + 1 <= glast ? lane * 4 : (lane * 4) % D);
-    lds_dma(p.v_scales + row * D + o, sm.vs[st], 4);
+    if (wave == 0) lds_dma(ksb + ((uint32_t)(min(lane, rmax) * b.ts) >> 5), ks_lds, D / 32);
+    asm volatile("" ::: "memory");
   }
 }
 
+// Issue the LDS-DMA loads of V tile kt (SEQ groups 2kt and 2kt + 1, the second clamped to the
+// last group) into `vt_lds` / `vs_lds`: kNj code instructions per wave (64 x 16 bytes of the
+// [group][channel][32] tile each: at d = 128 instruction jj of wave w covers group jj,
+// channels 32w.., at d = 64 group w / 2, channels 32(w % 2)..), and on wave 1 the scales (the
+// lane's dword of the two groups' [2][d] bytes; vsl = 4 lane for lanes < d/2).
+template <int D>
+__device__ __forceinline__ void issue_v(const KvBase& b, int kt, int wave, uint8_t* vt_lds, uint8_t* vs_lds,
+                                        uint32_t vl, uint32_t vsl) {
+  const bool two = 2 * kt + 1 <= ((b.n + 31) >> 5) - 1;   // the tile's second group exists
+  const uint8_t* g0 = b.v + (long long)(2 * kt) * (D * 32);
+  const uint8_t* g1 = two ? g0 + D * 32 : g0;
+#pragma unroll
+  for (int jj = 0; jj < kNj<D>; jj++) {
+    const int j = wave + jj * kWaves;
+    const uint8_t* gb = D == 128 ? (jj ? g1 : g0) : ((wave >> 1) ? g1 : g0);
+    const int cw = D == 128 ? wave : (wave & 1);           // 32-channel block (x 1024 bytes)
+    lds_dma_so(gb + cw * 1024, vl, vt_lds + j * 1024, 16);
+  }
+  if (wave == 1 && (threadIdx.x & 63) < D / 2)
+    lds_dma_so(b.vs + (long long)(2 * kt) * D, two ? vsl : vsl % D, vs_lds, 4);
+}
 
-// S^T for the two 32-key half tiles of stage st: keys are MFMA rows, the wave's 32 queries columns.
+// S^T for the two 32-key half tiles of K slot st: keys are MFMA rows, the wave's 32 queries columns.
 template <int D>
 __device__ __forceinline__ void scores(const FwdSmem<D>& sm, int st, const v8i* qop, const int* qsc, v16f* sacc) {
   const int lane = threadIdx.x & 63;
@@ -205,6 +236,27 @@ __device__ __forceinline__ void scores(const FwdSmem<D>& sm, int st, const v8i* 
       sacc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), qop[s], sacc[T], 0, 0, 0, ksc, 0, qsc[s]);
     }
   }
+}
+
+// x = -inf unless OFF < lim. One compare and select through VCC: written out so that the 32
+// compares of a tile do not each hold a scalar register pair until their selects.
+// (`ninf` holds -inf in a vector register: the select cannot read a literal and VCC at once.)
+template <int OFF>
+__device__ __forceinline__ float mask_below(float x, int lim, float ninf) {
+  asm volatile(
+      "v_cmp_lt_i32_e32 vcc, %1, %2\n\t"
+      "v_cndmask_b32_e32 %0, %3, %0, vcc"
+      : "+v"(x)
+      : "n"(OFF), "v"(lim), "v"(ninf)
+      : "vcc");
+  return x;
+}
+// The 16 accumulator values of a half tile: value i holds tile key T0 + 8(i >> 2) + (i & 3)
+// (plus 4 for the upper lane half, folded into lim).
+template <int T0, int... I>
+__device__ __forceinline__ void mask_tile(v16f& x, int lim, std::integer_sequence<int, I...>) {
+  const float ninf = -INFINITY;
+  ((x[I] = mask_below<T0 + 8 * (I >> 2) + (I & 3)>(x[I], lim, ninf)), ...);
 }
 
 // Largest of the 16 accumulator values of a lane (depth-3 tree of three-input maxima).
@@ -234,9 +286,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   const int kend = p.causal ? min(w.n, q0 + kBlockM) : w.n;  // keys this workgroup needs
   const int nkt = (kend + kBlockN - 1) / kBlockN;
   const uint32_t kl = k_lane_off<D, kPacked>(p, wave), vl = v_lane_off();
+  const uint32_t ksl = (uint32_t)(lane * (int)token_stride_k<kPacked>(p.heads_kv, D)) >> 5;   // K scales of key `lane`
+  const uint32_t vsl = (uint32_t)(lane * 4);
 
-  issue_tile<D, kPacked>(p, w, hkv, 0, sm, 0, kl, vl);
-  if (nkt > 1) issue_tile<D, kPacked>(p, w, hkv, 1, sm, 1, kl, vl);
+  const KvBase kvb = kv_base<D, kPacked>(p, w, hkv);
+  issue_k<D>(kvb, 0, wave, sm.k[0], sm.ks[0], kl, ksl);
+  if (nkt > 1) issue_k<D>(kvb, 1, wave, sm.k[1], sm.ks[1], kl, ksl);
+  issue_v<D>(kvb, 0, wave, sm.v[0], sm.vs[0], vl, vsl);
 
   // ---- Q operand (B of S^T = K Q^T), kept in registers ----
   constexpr int NS = D / 64;  // contraction steps of 64 over d
@@ -271,12 +327,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   v16f sa[2], sb[2];
   if (active(0)) scores<D>(sm, 0, qop, qsc, sa);
 
-  // One key tile: issue the loads of tile kt + 2, put the scores of tile kt + 1 on the matrix
-  // cores (into nxt) while this tile's softmax (on cur) runs on the VALU, then P V.
-  auto tile = [&](int kt, v16f(&cur)[2], v16f(&nxt)[2]) __attribute__((always_inline)) {
-    const int st = kt % kStages;
-    if (kt + 2 < nkt) issue_tile<D, kPacked>(p, w, hkv, kt + 2, sm, (kt + 2) % kStages, kl, vl);
-    if (kt + 1 < nkt && active(kt + 1)) scores<D>(sm, (kt + 1) % kStages, qop, qsc, nxt);
+  // One key tile kt (slot st = kt % 2, a constant in each unrolled copy): issue the loads of K
+  // tile kt + 2 and V tile kt + 1, put the scores of tile kt + 1 on the matrix cores (into nxt)
+  // while this tile's softmax (on cur) runs on the VALU, then P V.
+  auto tile = [&](auto slot, int kt, v16f(&cur)[2], v16f(&nxt)[2]) __attribute__((always_inline)) {
+    constexpr int st = decltype(slot)::value;
+    if (kt + 2 < nkt) issue_k<D>(kvb, kt + 2, wave, sm.k[st], sm.ks[st], kl, ksl);
+    if (kt + 1 < nkt) issue_v<D>(kvb, kt + 1, wave, sm.v[st ^ 1], sm.vs[st ^ 1], vl, vsl);
+    if (kt + 1 < nkt && active(kt + 1)) scores<D>(sm, st ^ 1, qop, qsc, nxt);
     const int kbase = kt * kBlockN;
     if (active(kt)) {
       // ---- mask (diagonal / tail tiles only): the lane's key T*32 + 8(i>>2) + 4hh + (i&3)
@@ -284,11 +342,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       const bool need_mask = (p.causal && kbase + kBlockN - 1 > qw) || kbase + kBlockN > w.n;
       if (need_mask) {
         const int lim = vis_end - kbase - 4 * hh;
-#pragma unroll
-        for (int T = 0; T < 2; T++)
-#pragma unroll
-          for (int i = 0; i < 16; i++)
-            if (T * 32 + 8 * (i >> 2) + (i & 3) >= lim) cur[T][i] = -INFINITY;
+        mask_tile<0>(cur[0], lim, std::make_integer_sequence<int, 16>{});
+        mask_tile<32>(cur[1], lim, std::make_integer_sequence<int, 16>{});
       }
       // ---- row / group maxima (raw accumulator units; c > 0) ----
       float gm0 = vmax16(cur[0]), gm1 = vmax16(cur[1]);
@@ -340,8 +395,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
         oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), pop, oacc[t], 0, 0, 0, vsc, 0, psc);
       }
     }
-    // publish tile kt + 1. (Waiting here also for tile kt + 2's loads, issued at the top of
-    // this iteration, measured slightly faster than leaving them in flight.)
+    // publish K tile kt + 2 and V tile kt + 1
     if (kt + 1 < nkt) {
       wait_vmem();
       wg_barrier();
@@ -349,8 +403,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   };
   // two tiles per iteration, so the score registers alternate without copies
   for (int kt = 0; kt < nkt; kt += 2) {
-    tile(kt, sa, sb);
-    if (kt + 1 < nkt) tile(kt + 1, sb, sa);
+    tile(std::integral_constant<int, 0>{}, kt, sa, sb);
+    if (kt + 1 < nkt) tile(std::integral_constant<int, 1>{}, kt + 1, sb, sa);
   }
 
   // ---- epilogue: O = a / l, LSE = (M + log2 l) ln 2 ----

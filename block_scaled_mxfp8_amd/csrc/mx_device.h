@@ -181,6 +181,20 @@ __device__ __forceinline__ __attribute__((address_space(1))) T* scalar_ptr(T* p)
   return reinterpret_cast<__attribute__((address_space(1))) T*>(((uint64_t)hi << 32) | lo);
 }
 
+// LDS-DMA from a wave-uniform address `base` plus a 32-bit lane offset `off`, kept in the
+// scalar-base + vector-offset form: the base is made scalar explicitly (a no-op when it already
+// is) and the offset is hidden from loop-invariant hoisting, which would otherwise widen it to
+// a 64-bit vector address computed with 64-bit vector adds.
+__device__ __forceinline__ void lds_dma_so(const void* base, uint32_t off, void* lds, int size) {
+  asm volatile("" : "+v"(off));
+  const __attribute__((address_space(1))) uint8_t* g = scalar_ptr(reinterpret_cast<const uint8_t*>(base));
+  auto src = (__attribute__((address_space(1))) void*)(g + off);
+  auto dst = (__attribute__((address_space(3))) void*)lds;
+  if (size == 16) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+  else if (size == 4) __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+  else __builtin_amdgcn_global_load_lds(src, dst, 2, 0, 0);
+}
+
 // Wait for every outstanding vector-memory operation of this wave (loads, LDS-DMA).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N vector-memory operations of this wave are outstanding (they complete
