@@ -326,6 +326,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   __syncthreads();
   v16f sa[2], sb[2];
   if (active(0)) scores<D>(sm, 0, qop, qsc, sa);
+  wg_barrier();   // every wave has read K slot 0 before the first tile loads K(2) into it
 
   // One key tile kt (slot st = kt % 2, a constant in each unrolled copy): issue the loads of K
   // tile kt + 2 and V tile kt + 1, put the scores of tile kt + 1 on the matrix cores (into nxt)

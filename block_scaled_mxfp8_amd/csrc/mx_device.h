@@ -189,7 +189,8 @@ __device__ __forceinline__ void lds_dma_so(const void* base, uint32_t off, void*
   asm volatile("" : "+v"(off));
   const __attribute__((address_space(1))) uint8_t* g = scalar_ptr(reinterpret_cast<const uint8_t*>(base));
   auto src = (__attribute__((address_space(1))) void*)(g + off);
-  auto dst = (__attribute__((address_space(3))) void*)lds;
+  // the LDS address is the low half of the generic address (a plain cast adds a null check)
+  auto dst = (__attribute__((address_space(3))) void*)(uint32_t)reinterpret_cast<uintptr_t>(lds);
   if (size == 16) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
   else if (size == 4) __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
   else __builtin_amdgcn_global_load_lds(src, dst, 2, 0, 0);
