@@ -129,20 +129,21 @@ __device__ __forceinline__ void dma_seq_tile(const uint8_t* codes, long long row
 
 // ============================== dK / dV pass ==============================
 
-// One 64-query step in LDS. Code tiles are written by LDS-DMA; the small items by ordinary
-// loads (issued with the DMA, stored before the barrier that publishes the step).
+// One 64-query step in LDS, written entirely by LDS-DMA.
 template <int D>
 struct DkvStage {
   alignas(16) uint8_t qr[kStepQ * D];   // Q ROW codes [query][d], row_swz chunks
   alignas(16) uint8_t gr[kStepQ * D];   // G ROW codes
   alignas(16) uint8_t qs[2 * D * 32];   // Q SEQ codes [group][channel][32], half_swz halves
   alignas(16) uint8_t gs[2 * D * 32];   // G SEQ codes
-  alignas(16) uint32_t qrs[kStepQ];     // Q ROW scale word per query
+  alignas(16) uint32_t qrs[kStepQ];     // Q ROW scale word per query (d = 64: low half only)
   alignas(16) uint32_t grs[kStepQ];     // G ROW scale word per query
-  alignas(16) uint8_t qss[2 * D];       // Q SEQ scales [group][channel]
-  alignas(16) uint8_t gss[2 * D];       // G SEQ scales
-  alignas(16) float lse2[kStepQ];       // LSE * log2 e (+inf past the end)
-  alignas(16) float ndlt[kStepQ];       // -D (0 past the end): the E product's initial value
+  // SEQ scales [group][channel]; one dword per lane of the DMA, so 256 bytes also at d = 64
+  // (where lanes 32-63 repeat lanes 0-31)
+  alignas(16) uint8_t qss[2 * D < 256 ? 256 : 2 * D];
+  alignas(16) uint8_t gss[2 * D < 256 ? 256 : 2 * D];
+  alignas(16) float lse2[kStepQ];       // LSE * log2 e
+  alignas(16) float ndlt[kStepQ];       // -D: the E product's initial value
 };
 
 struct KvWork {
@@ -175,17 +176,17 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
   return w;
 }
 
-// Issue the producers' loads of the step (query head hq, queries q0..q0+63) into stage `st`,
-// as loader `lw` of NL (NL >= 6): ROW-tile DMA instructions j = lw, lw + NL, ... (each moves
-// 64 x 16 bytes: 64/NCH rows of NCH = d/16 chunks) and one small-item dword per lane into `sv`: loader 0 the Q ROW scale word of row `lane`, 1 the G
-// ROW scale word, 2 LSE, 3 D, 4 the Q SEQ scales, 5 the G SEQ scales (dword lane % (d/2) of
-// the step's two groups); loaders 6+ repeat loader 0's load and store nothing. Every loader
-// loads on every path, so the register is only ever written by loads (no write-after-load
-// wait). Rows past the end are clamped to the last row (finite codes; their LSE becomes +inf
-// in dkv_put, so their P and U are 0).
+// Issue the producers' loads of the step (query head hq, queries q0..q0+63) into stage `st`, as
+// loader `lw` of NL (NL >= 6), all LDS-DMA: ROW-tile instructions j = lw, lw + NL, ... (each
+// moves 64 x 16 bytes: 64/NCH rows of NCH = d/16 chunks) and, for lw < 6, one per-query item
+// (64 lanes x 4 bytes; the ROW scale words are 2 bytes at d = 64, landing in the low half of
+// the lane's dword): 0 the Q ROW scale words, 1 the G ROW scale words, 2 LSE * log2 e, 3 -D,
+// 4 the Q SEQ scales, 5 the G SEQ scales (dword lane % (d/2) of the step's two groups, the
+// second clamped to the last group). Rows past the end are clamped to the last row (finite
+// codes and values); the masked tile code gives them P = 0 and U = 0.
 template <int D, bool kPacked, int NL>
 __device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
-                                              uint32_t& sv, int lw) {
+                                              int lw) {
   static_assert(NL >= 6, "six small-item loaders");
   constexpr int NCH = D / 16, RPI = 64 / NCH;
   const Geom& g = p.geom;
@@ -194,21 +195,20 @@ __device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& 
   const int ts = (int)token_stride_k<kPacked>(p.heads_q, D);
   const long long off0 = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, hq, q0, 0);
   const int rmax = w.n - 1 - q0;
-  const int glast = ((w.n + 31) >> 5) - 1;
-  // small item first: its load then precedes the DMA in the wave's in-order vector-memory
-  // queue, so waiting for it (at dkv_put) does not wait for this step's DMA
   const int r = min(lane, rmax);
-  if (lw == 2 || lw == 3) {
-    const float* f = (lw == 2 ? p.lse : p.delta) + token_index_k<kPacked>(g, p.heads_q, w.s, w.doc_start, hq, q0);
-    sv = __float_as_uint(f[(uint32_t)(r * (kPacked ? p.heads_q : 1))]);
+  if (lw == 0 || lw == 1) {
+    lds_dma((lw == 0 ? p.q_scales : p.gr_scales) + (off0 >> 5) + ((uint32_t)(r * ts) >> 5), lw == 0 ? st.qrs : st.grs,
+            D / 32);
+  } else if (lw == 2 || lw == 3) {
+    const float* src = (lw == 2 ? p.lse2 : p.ndelta) + token_index_k<kPacked>(g, p.heads_q, w.s, w.doc_start, hq, q0) +
+                       (uint32_t)(r * (kPacked ? p.heads_q : 1));
+    lds_dma(src, lw == 2 ? st.lse2 : st.ndlt, 4);
   } else if (lw == 4 || lw == 5) {
+    const int glast = ((w.n + 31) >> 5) - 1;
     const int word = lane % (D / 2);       // lanes >= d/2 repeat a dword of the lower half
     const int gi = min((q0 >> 5) + (word * 4) / D, glast);
     const long long row = seq_group_row_k<kPacked>(g, p.heads_q, w.s, hq, w.doc_start, gi);
-    sv = *reinterpret_cast<const uint32_t*>((lw == 4 ? p.qs_scales : p.gs_scales) + row * D + (word * 4) % D);
-  } else {
-    const uint8_t* base = (lw == 1 ? p.gr_scales : p.q_scales) + (off0 >> 5);
-    sv = load_row_scales<D>(base, (uint32_t)(r * ts));
+    lds_dma((lw == 4 ? p.qs_scales : p.gs_scales) + row * D + (word * 4) % D, lw == 4 ? st.qss : st.gss, 4);
   }
   // ROW tiles (Q, G)
   const int lrow = lane / NCH;
@@ -249,22 +249,6 @@ __device__ __forceinline__ void dkv_issue_seq(const BwdParams& p, const KvWork& 
   }
 }
 
-// Store the small item of a step; rows past the end (lane > rmax) get LSE' = +inf, D = 0.
-// D is stored negated: it is the initial accumulator of E, so the product yields E - D.
-template <int D>
-__device__ __forceinline__ void dkv_put(DkvStage<D>& st, uint32_t sv, int rmax, int lw) {
-  const int lane = threadIdx.x & 63;
-  const bool live = lane <= rmax;
-  const float x = __uint_as_float(sv);
-  if (lw == 0) st.qrs[lane] = sv;
-  else if (lw == 1) st.grs[lane] = sv;
-  else if (lw == 2) st.lse2[lane] = live ? x * kLog2e : INFINITY;
-  else if (lw == 3) st.ndlt[lane] = live ? -x : 0.f;
-  else if (lw == 4 || lw == 5) {
-    if (lane < D / 2) reinterpret_cast<uint32_t*>(lw == 4 ? st.qss : st.gss)[lane] = sv;
-  }
-}
-
 // E8M0 exponent of a P group: P is 0 or a normal number <= 1 (v_exp_f32 flushes results
 // below 2^-126), so the subnormal branch of scale_exp_from_bits is not needed.
 __device__ __forceinline__ int p_scale_exp(float amax) {
@@ -284,10 +268,13 @@ __device__ __forceinline__ int p_scale_exp(float amax) {
 // the P_b codes of tile qt (operand bytes 16 qt .. 16 qt + 15); k = 2 + qt holds the dS codes
 // of tile qt, the lane's 16 bytes at the swizzled slot ds_slot_off(lane); at 1024 + 128 qt +
 // 2 lane: the P_b exponent of the lane's key for tile qt, then the tile's dS exponent.
-template <int D, bool kMask>
-__device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, const v8i* kop, const v8i* vop,
+//
+// `mid` runs after the S and E products are issued, while the matrix cores work on them (the
+// producers issue the next step's loads there).
+template <int D, bool kMask, class Mid>
+__device__ __forceinline__ int dkv_codes_tile(const DkvStage<D>& S, int qt, const v8i* kop, const v8i* vop,
                                                uint32_t kvsc, const int* roff_ab, int fidx, float c, int rel, int lim,
-                                               bool kvalid, bool causal, uint32_t* cx, int slot_off) {
+                                               bool kvalid, bool causal, uint32_t* cx, int slot_off, Mid&& mid) {
   constexpr int NS = D / 64;
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
@@ -312,6 +299,7 @@ __device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, con
     eacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga, vop[s], eacc, 0, 0, 0, (int)(gsw >> (16 * s)), 0,
                                                            (int)(kvsc >> (16 + 8 * s)));
   }
+  mid();
   float P[16], U[16];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
@@ -345,22 +333,24 @@ __device__ __forceinline__ void dkv_codes_tile(const DkvStage<D>& S, int qt, con
   reinterpret_cast<v4i*>(cx)[qt * 64 + lane] = pb;
   *reinterpret_cast<v4i*>(reinterpret_cast<uint8_t*>(cx) + (2 + qt) * 1024 + slot_off) = ds;
   reinterpret_cast<v2i*>(cx + 1024 + 128 * qt)[lane] = v2i{pbe, dse};
+  return dse;
 }
 
 // Producer / accumulator split, 12 waves. Waves 0-7 are producers: wave w computes the codes
 // of query tile w >> 2 for key group w & 3 (VALU-heavy, holding the group's K and V
-// operands) and loads stages; waves 8-11 are accumulators: wave 8 + k holds key group k's dK
-// and dV and applies the codes one step later (codes pass through an LDS exchange buffer).
-// The waves of a workgroup go round-robin to the four SIMDs, so each SIMD runs two producers
-// and one accumulator of the same key group: the producers' VALU work overlaps each other's
-// latencies and the accumulator's MFMAs, and each role fits three waves per SIMD.
+// operands), loads stages and (kStore) writes its 32 x 32 dS block to the code store; waves
+// 8-11 are accumulators: wave 8 + k holds key group k's dK and dV and applies the codes one
+// step later (codes pass through an LDS exchange buffer). The waves of a workgroup go
+// round-robin to the four SIMDs, so each SIMD runs two producers and one accumulator of the
+// same key group: the producers' VALU work overlaps each other's latencies and the
+// accumulator's MFMAs, and each role fits three waves per SIMD.
 //
-// Iteration j (j = 0..nsteps): producers issue the ROW-tile and small-item loads of step
-// j + 1 into stage (j+1) % 3 and turn stage j % 3 into codes in exchange buffer j % 2;
-// accumulators issue the SEQ-tile loads of step j + 1 and apply the codes of step j - 1
-// (stage (j-1) % 3, buffer (j-1) % 2); one barrier ends the iteration. (The loads of a step
-// pass through the CU's vector-memory path at about 64 bytes per clock; splitting them keeps
-// the producers from queueing behind all of them.)
+// Iteration j (j = 0..nsteps): producers issue the S and E products of step j, then the
+// ROW-tile and small-item loads of step j + 1 into stage (j+1) % 3, then turn stage j % 3
+// into codes in exchange buffer j % 2; accumulators issue the SEQ-tile loads of step j + 1 and
+// apply the codes of step j - 1 (stage (j-1) % 3, buffer (j-1) % 2); one barrier ends the
+// iteration. The accumulators set the pace (eight products per step each, against four
+// per producer), so the dS stores sit with the producers.
 constexpr int kDkvProducers = 2 * kWaves;
 constexpr int kDkvThreads = 64 * (kDkvProducers + kWaves);
 constexpr int kCodeDw = 1280;               // exchange dwords per key group
@@ -381,16 +371,19 @@ __device__ __forceinline__ void next_step(int& hq, int& q0, int qfirst, int n) {
 }
 
 // dS block (qb, kb) of query head h in the code store (layout in mx_layout.h DsStore): index of
-// its 1024-byte code block and of its exponent byte.
+// its 1024-byte code block and of its exponent byte. The host enables the store only when
+// both counts fit 32 bits, so the arithmetic is 32-bit (it is scalar code on the hot path).
 template <bool kPacked>
 __device__ __forceinline__ void ds_block(const BwdParams& p, int s, int h, int doc_start, int qb, int kb,
-                                         long long& code_blk, long long& exp_idx) {
-  const long long row = seq_group_row_k<kPacked>(p.geom, p.heads_q, s, h, doc_start, qb);
-  exp_idx = row * p.ds.ecols + kb;
+                                         uint32_t& code_blk, uint32_t& exp_idx) {
+  const Geom& g = p.geom;
+  const uint32_t row = kPacked ? (uint32_t)h * g.gseq + (uint32_t)((doc_start >> 5) + s + qb)
+                               : ((uint32_t)s * p.heads_q + h) * g.gseq + qb;
+  exp_idx = row * (uint32_t)p.ds.ecols + kb;
   if (!kPacked && p.ds.tri)
-    code_blk = ((long long)s * p.heads_q + h) * p.ds.head_blocks + (long long)qb * (qb + 1) / 2 + kb;
+    code_blk = ((uint32_t)s * p.heads_q + h) * (uint32_t)p.ds.head_blocks + (uint32_t)(qb * (qb + 1) / 2 + kb);
   else
-    code_blk = row * p.ds.cols + kb;
+    code_blk = row * (uint32_t)p.ds.cols + kb;
 }
 
 // Byte offset of a producer lane's 16 dS codes inside a 32 x 32 block in LDS. Lane (key
@@ -439,9 +432,9 @@ __device__ __forceinline__ v4i ds_read_tr8_pair(const uint8_t* lds) {
   return v4i{x0[0], x0[1], x1[0], x1[1]};
 }
 
-// kStore: the accumulator waves also write each dS block to the code store, transposed into
-// the dQ product's operand order: lane l's 16 bytes at 16 l of the block's 1024 bytes (read
-// back by the dQ pass instead of rebuilding dS).
+// kStore: the producer waves also write each dS block to the code store, transposed into the
+// dQ product's operand order: lane l's 16 bytes at 16 l of the block's 1024 bytes (read back
+// by the dQ pass instead of rebuilding dS).
 template <int D, bool kPacked, bool kStore>
 __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ DkvShared<D> sm;
@@ -491,31 +484,62 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     }
     const int fidx = 4 * hh;              // LSE / D index of the lane's rows
     const int slot_off = ds_slot_off(lane);
+    const int kb = kw >> 5;               // key group of the dS blocks
+    int hq = w.hkv * group;               // head of step j
     int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
-    uint32_t sv = 0;
-    dkv_issue_row<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[0], sv, lw);
-    dkv_put<D>(sm.st[0], sv, w.n - 1 - q0_l, lw);
+    dkv_issue_row<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[0], lw);
     wait_vmem();
     wg_barrier();                         // stage 0 loaded
     int q0 = qfirst;                      // step whose codes are computed (j)
     for (int j = 0; j <= nsteps; j++) {
       next_step(hq_l, q0_l, qfirst, w.n);  // step j + 1
       const bool load = j + 1 < nsteps;
-      if (load) dkv_issue_row<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], sv, lw);
+      // the next step's loads are issued while this step's S and E products run. They are
+      // issued on every iteration (no branch for the compiler to sink the products past): past
+      // the last step they reload the first step, whose addresses are valid, into stage
+      // (j + 1) % 3, which nobody reads then.
+      auto issue = [&]() __attribute__((always_inline)) {
+        dkv_issue_row<D, kPacked, kDkvProducers>(p, w, load ? hq_l : w.hkv * group, load ? q0_l : qfirst,
+                                                 sm.st[(j + 1) % 3], lw);
+      };
+      bool stored = false;
       if (j < nsteps && active(q0)) {
         const DkvStage<D>& S = sm.st[j % 3];
         uint32_t* cx = sm.cx[j & 1][kg];
         const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.n;
+        int dse;
         if (need_mask)
-          dkv_codes_tile<D, true>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, q0 + 4 * hh - key, w.n - q0 - 4 * hh,
-                                  kvalid, p.causal, cx, slot_off);
+          dse = dkv_codes_tile<D, true>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, q0 + 4 * hh - key,
+                                        w.n - q0 - 4 * hh, kvalid, p.causal, cx, slot_off, issue);
         else
-          dkv_codes_tile<D, false>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, 0, 0, true, false, cx, slot_off);
+          dse = dkv_codes_tile<D, false>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, 0, 0, true, false, cx, slot_off,
+                                         issue);
+        // kStore: this wave's dS block (query group qb, key group kb; under causal only kb <= qb),
+        // read back transposed from the exchange buffer (the wave's own LDS writes, in order)
+        const int qb = (q0 >> 5) + qt;
+        if (kStore && (qb << 5) < w.n && (!p.causal || kb <= qb)) {
+          const v4i x = ds_read_tr8_pair(reinterpret_cast<const uint8_t*>(cx) + (2 + qt) * 1024 + ds_tr_offset(fresh_lane()));
+          uint32_t blk, ei;
+          ds_block<kPacked>(p, w.s, hq, w.doc_start, qb, kb, blk, ei);
+          uint32_t lo = (uint32_t)(lane * 16);
+          asm volatile("" : "+v"(lo));     // keeps the scalar-base + 32-bit-offset store form
+          __builtin_nontemporal_store(
+              x, reinterpret_cast<__attribute__((address_space(1))) v4i*>(
+                     scalar_ptr(p.ds_codes + ((uint64_t)blk << 10)) + lo));
+          if (lane == 0) p.ds_exps[ei] = (uint8_t)(dse + 127);
+          stored = true;
+        }
+      } else {
+        issue();
       }
-      if (load) dkv_put<D>(sm.st[(j + 1) % 3], sv, w.n - 1 - q0_l, lw);
       q0 += kStepQ;
-      if (q0 >= w.n) q0 = qfirst;
-      wait_vmem();
+      if (q0 >= w.n) {
+        q0 = qfirst;
+        hq++;
+      }
+      // this step's loads have landed once at most the two younger stores are outstanding
+      if (stored) wait_vmem_n<2>();
+      else wait_vmem();
       wg_barrier();
     }
     return;
@@ -537,12 +561,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   wait_vmem();
   wg_barrier();                           // stage 0 loaded
   int q0_a = qfirst;                      // step whose codes are applied (j - 1)
-  int hq_a = w.hkv * group;               // its query head
   for (int j = 0; j <= nsteps; j++) {
     next_step(hq_l, q0_l, qfirst, w.n);  // step j + 1
     const bool load = j + 1 < nsteps;
     if (load) dkv_issue_seq<D, kPacked, kWaves>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], lw);
-    int nst = 0;                          // global stores issued after the loads
     if (j >= 1) {
       if (active(q0_a)) {
         // per-lane offsets, recomputed here (registers are short in this role)
@@ -550,7 +572,6 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         const int soff_c = l32a * 32 + (half_swz(l32a, hha) << 4);   // SEQ tile, channel l32 of group 0
         const int scoff = hha * D + l32a;                             // SEQ scale of channel l32, group hh
         const int slot_off = ds_slot_off(ln);
-        const int troff = ds_tr_offset(ln);
         const DkvStage<D>& S = sm.st[(j - 1) % 3];
         const uint32_t* cx = sm.cx[(j - 1) & 1][kg];
         const uint8_t* cxb = reinterpret_cast<const uint8_t*>(cx);
@@ -559,24 +580,6 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
                            *reinterpret_cast<const v4i*>(cxb + 3072 + slot_off));
         const v2i e = reinterpret_cast<const v2i*>(cx + 1024 + 128 * hh)[lane];   // exponents of tile hh
         const int pbsc = e[0] + 127, dssc = e[1] + 127;
-        if (kStore) {
-          // blocks (query group qb = q0/32 + qt, key group kb); under causal only kb <= qb
-          const int kb = kw >> 5;
-#pragma unroll
-          for (int qt = 0; qt < 2; qt++) {
-            const int qb = (q0_a >> 5) + qt;
-            if ((qb << 5) < w.n && (!p.causal || kb <= qb)) {
-              const v4i x = ds_read_tr8_pair(cxb + (2 + qt) * 1024 + troff);
-              long long blk, ei;
-              ds_block<kPacked>(p, w.s, hq_a, w.doc_start, qb, kb, blk, ei);
-              __builtin_nontemporal_store(
-                  x, reinterpret_cast<__attribute__((address_space(1))) v4i*>(scalar_ptr(p.ds_codes + blk * 1024) +
-                                                                             (uint32_t)(lane * 16)));
-              if (lane == 32 * qt) p.ds_exps[ei] = (uint8_t)(dssc);   // lane 32 qt holds tile qt's exponent
-              nst += 2;
-            }
-          }
-        }
 #pragma unroll
         for (int t = 0; t < NCT; t++) {
           const int h0 = t * 1024 + soff_c, h1 = D * 32 + t * 1024 + soff_c;   // channel t*32 + l32
@@ -589,15 +592,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         }
       }
       q0_a += kStepQ;
-      if (q0_a >= w.n) {
-        q0_a = qfirst;
-        hq_a++;
-      }
+      if (q0_a >= w.n) q0_a = qfirst;
     }
-    // the SEQ tiles of step j + 1 have landed once at most the nst younger stores are outstanding
-    if (nst == 4) wait_vmem_n<4>();
-    else if (nst == 2) wait_vmem_n<2>();
-    else wait_vmem();
+    wait_vmem();
     wg_barrier();
   }
 
@@ -761,8 +758,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
     gsc[s] = p.gr_scales[(off >> 5) + hh];
   }
   const long long li = token_index(g, p.heads_q, w.s, w.doc_start, w.h, qc);
-  const float lse2 = qvalid ? p.lse[li] * kLog2e : INFINITY;
-  const float dl = qvalid ? p.delta[li] : 0.f;
+  const float lse2 = qvalid ? p.lse2[li] : INFINITY;
+  const float ndl = qvalid ? p.ndelta[li] : 0.f;
 
   v16f dq[NCT];
   h2 acc16[NCT][8];
@@ -811,7 +808,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
         // E^T starts from -D of the lane's query (as in the dK/dV pass), so it gives E - D
         v16f sacc = v16f{}, eacc;
 #pragma unroll
-        for (int i = 0; i < 16; i++) eacc[i] = -dl;
+        for (int i = 0; i < 16; i++) eacc[i] = ndl;
 #pragma unroll
         for (int s = 0; s < NS; s++) {
           const int o0 = T * 32 * D + roff_ab[2 * s], o1 = T * 32 * D + roff_ab[2 * s + 1];
@@ -909,7 +906,7 @@ constexpr int kPre = 4;                     // dS tiles in flight per wave (regi
 struct DqdsCtx {
   int lane, wave, hh, hkv, glast;
   int kb_end;                 // the wave's key blocks: kb < kb_end
-  long long blk0, ex0;        // code block and exponent index of (qb, kb = 0)
+  uint32_t blk0, ex0;         // code block and exponent index of (qb, kb = 0)
   int soff, soff_c, scoff;    // K SEQ DMA lane offset, operand offset, scale offset
 };
 
@@ -939,11 +936,11 @@ __device__ __forceinline__ void dqds_load_ds(const BwdParams& p, const DqdsCtx& 
   const int g0 = 2 * kt;
 #pragma unroll
   for (int b = 0; b < 2; b++) {
-    const long long blk = g0 + b < c.kb_end ? c.blk0 + g0 + b : 0;
+    const uint32_t blk = g0 + b < c.kb_end ? c.blk0 + g0 + b : 0;
     r[b] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) v4i*>(
-        scalar_ptr(p.ds_codes + blk * 1024) + (uint32_t)(c.lane * 16)));
+        scalar_ptr(p.ds_codes + ((uint64_t)blk << 10)) + (uint32_t)(c.lane * 16)));
   }
-  const long long ei = g0 + c.hh < c.kb_end ? c.ex0 + g0 + c.hh : 0;
+  const uint32_t ei = g0 + c.hh < c.kb_end ? c.ex0 + g0 + c.hh : 0;
   e = p.ds_exps[ei];
 }
 
@@ -1138,7 +1135,9 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
   qp.seq_scales = p.gs_scales;
   qp.o = p.o;
   qp.o_f32 = p.out_f32;
-  qp.delta = p.delta;
+  qp.ndelta = p.ndelta;
+  qp.lse = p.lse;
+  qp.lse2 = p.lse2;
   hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(1), 0, stream, p.flags);
   const int slot = profile_begin(kProfBwdPrep, stream);
   hipError_t err = launch_quantize(qp, stream);

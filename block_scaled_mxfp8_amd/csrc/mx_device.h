@@ -197,11 +197,25 @@ __device__ __forceinline__ void lds_dma_so(const void* base, uint32_t off, void*
 }
 
 // Wait for every outstanding vector-memory operation of this wave (loads, LDS-DMA).
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt through the builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; the other counters left at their maxima), so that the compiler's own wait
+// insertion knows what has completed (it cannot see into inline asm and would add waits of
+// its own before later LDS accesses). The empty asm statements keep memory accesses from
+// moving across the wait.
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
 // Wait until at most N vector-memory operations of this wave are outstanding (they complete
 // in issue order, so this waits for all but the N most recent).
 template <int N>
-__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
 
 // Workgroup barrier that completes this wave's LDS operations first (so its LDS writes are
 // visible after the barrier) but does not wait for global loads, stores or LDS-DMA: the

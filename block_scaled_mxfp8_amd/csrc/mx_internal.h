@@ -18,10 +18,13 @@ struct QuantizeParams {
   uint8_t* seq_codes;    // nullptr: SEQ view not wanted
   uint8_t* seq_scales;
   // backward preprocessing (all nullptr for a plain quantise): with `o` set, the kernel also
-  // writes delta[token, head] = sum_c dequant(ROW code) * O.
+  // writes ndelta[token, head] = -sum_c dequant(ROW code) * O (that is -D) and
+  // lse2[token, head] = lse * log2 e, the forms the backward kernels consume.
   const void* o;
   bool o_f32;
-  float* delta;
+  float* ndelta;
+  const float* lse;
+  float* lse2;
 };
 
 struct AttnParams {
@@ -59,7 +62,8 @@ struct BwdParams {
   // workspace pieces
   uint8_t* gr_codes; uint8_t* gr_scales;                // ROW G
   uint8_t* gs_codes; uint8_t* gs_scales;                // SEQ G
-  float* delta;                                         // D per (row, head)
+  float* ndelta;                                        // -D per (row, head)
+  float* lse2;                                          // LSE * log2 e per (row, head)
   uint32_t* flags;
   // dS code store (nullptr: dQ recomputes dS instead); layout in mx_layout.h DsStore
   uint8_t* ds_codes; uint8_t* ds_exps;

@@ -66,11 +66,14 @@ mx_status check_desc(const mx_attn_desc* d, mx::Geom* g) {
   return MX_OK;
 }
 
-// Backward workspace: the status word, G's views and D (always), then the optional dS code
+// Backward workspace: the status word, G's views, -D and LSE * log2 e (always), then the optional dS code
 // store (total_store - total bytes; with it the dQ pass reads dS instead of rebuilding it).
+// The kernels index the store's blocks and exponents with 32-bit integers; a geometry whose
+// store would need more has no store (store_ok false, total_store = total).
 struct BwdWorkspace {
-  size_t gr_codes, gr_scales, gs_codes, gs_scales, delta, flags, total;
+  size_t gr_codes, gr_scales, gs_codes, gs_scales, ndelta, lse2, flags, total;
   size_t ds_codes, ds_exps, total_store;
+  bool store_ok;
   mx::DsStore ds;
 };
 
@@ -83,14 +86,16 @@ BwdWorkspace bwd_layout(const mx::Geom& g, const mx_attn_desc* d) {
   w.gr_scales = off; off += align_up(row_codes_bytes(g, hq, dim) / 32);
   w.gs_codes = off; off += align_up(seq_codes_bytes(g, hq, dim));
   w.gs_scales = off; off += align_up(seq_codes_bytes(g, hq, dim) / 32);
-  w.delta = off; off += align_up((size_t)g.total * hq * sizeof(float));
+  w.ndelta = off; off += align_up((size_t)g.total * hq * sizeof(float));
+  w.lse2 = off; off += align_up((size_t)g.total * hq * sizeof(float));
   w.total = off;
   w.ds = mx::ds_store_geom(g, d->causal != 0);
   const size_t rows = (size_t)g.gseq * hq * (mx::packed(g) ? 1 : (size_t)g.batch);   // query groups
   const size_t blocks = w.ds.tri ? (size_t)g.batch * hq * (size_t)w.ds.head_blocks : rows * (size_t)w.ds.cols;
+  w.store_ok = blocks <= UINT32_MAX && rows * (size_t)w.ds.ecols <= UINT32_MAX;
   w.ds_codes = off; off += align_up(blocks * 1024);
   w.ds_exps = off; off += align_up(rows * (size_t)w.ds.ecols);
-  w.total_store = off;
+  w.total_store = w.store_ok ? off : w.total;
   return w;
 }
 
@@ -157,9 +162,10 @@ mx_status bwd_impl(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.gr_codes = ws + w.gr_codes; p.gr_scales = ws + w.gr_scales;
   p.gs_codes = ws + w.gs_codes; p.gs_scales = ws + w.gs_scales;
-  p.delta = reinterpret_cast<float*>(ws + w.delta);
+  p.ndelta = reinterpret_cast<float*>(ws + w.ndelta);
+  p.lse2 = reinterpret_cast<float*>(ws + w.lse2);
   p.flags = reinterpret_cast<uint32_t*>(ws + w.flags);
-  if (desc->workspace_bytes >= w.total_store) {
+  if (w.store_ok && desc->workspace_bytes >= w.total_store) {
     p.ds_codes = ws + w.ds_codes;
     p.ds_exps = ws + w.ds_exps;
     p.ds = w.ds;

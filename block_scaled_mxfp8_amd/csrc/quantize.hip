@@ -136,7 +136,8 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
       if (valid && cb == 0) {
         const long long ti = packed(g) ? ((long long)(doc_start + tok0 + tk) * p.heads + h)
                                        : (((long long)s * p.heads + h) * g.seqlen + tok0 + tk);
-        p.delta[ti] = part;
+        p.ndelta[ti] = -part;
+        p.lse2[ti] = p.lse[ti] * 1.4426950408889634f;
       }
     }
   }

@@ -141,13 +141,16 @@ mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
                              mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
 
 /* Bytes of device workspace for mx_attn_bwd with this descriptor.
- *   for_bwd = 1: the minimum (G's views, D, the status word; O(tokens x heads x head_dim)).
+ *   for_bwd = 1: the minimum (G's views, -D and LSE log2 e per row, the status word;
+ *     O(tokens x heads x head_dim)).
  *     The dQ pass then rebuilds S, P and dS itself (two more score-sized products per pair).
  *   for_bwd = 2: the minimum plus a store of the quantised dS blocks (one byte per visible
  *     (query, key) pair of every query head, plus one scale byte per 32 x 32 block; for a
  *     causal batch about B * H * L^2 / 2 bytes). The dK/dV pass writes the dS codes there and
  *     the dQ pass reads them instead of rebuilding them. The results are the same either way.
- * mx_attn_bwd uses the store whenever desc->workspace_bytes >= the for_bwd = 2 size.
+ * mx_attn_bwd uses the store whenever desc->workspace_bytes >= the for_bwd = 2 size. A geometry
+ * whose store would hold 2^32 or more blocks or exponent bytes has none: for_bwd = 2 then
+ * returns the for_bwd = 1 size.
  * Other for_bwd values (0 = forward, which needs none) return 0. */
 size_t mx_attn_workspace_size(const mx_attn_desc* desc, int32_t for_bwd);
 

@@ -152,7 +152,7 @@ def test_workspace_sizes_with_and_without_the_ds_store(lib, causal):
     desc = _bwd_desc(s, H, d, causal)
     nb = (L + 31) // 32
     base = (_up(4) + _up(B * H * L * d) + _up(B * H * L * d // 32) + _up(B * H * nb * d * 32)
-            + _up(B * H * nb * d) + _up(B * H * L * 4))
+            + _up(B * H * nb * d) + 2 * _up(B * H * L * 4))
     assert lib.mx_attn_workspace_size(ctypes.byref(desc), 1) == base
     blocks = B * H * (nb * (nb + 1) // 2 if causal else nb * nb)
     exps = B * H * nb * ((nb + 3) // 4 * 4)
