@@ -74,8 +74,15 @@ def load():
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, _QView, _QView, P, P, P, I32, P, P, P, P]
         f.restype = I32
+    lib.mx_attn_cross_fwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Seq), _QView, _QView, _QView, P, P, P]
+    lib.mx_attn_cross_fwd.restype = I32
+    lib.mx_attn_cross_bwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Seq), _QView, _QView, _QView, _QView,
+                                      _QView, P, P, P, I32, P, P, P, P]
+    lib.mx_attn_cross_bwd.restype = I32
     lib.mx_attn_workspace_size.argtypes = [ctypes.POINTER(_Desc), I32]
     lib.mx_attn_workspace_size.restype = SZ
+    lib.mx_attn_cross_workspace_size.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Seq), I32]
+    lib.mx_attn_cross_workspace_size.restype = SZ
     lib.mx_view_codes_bytes.argtypes = [ctypes.POINTER(_Seq), I32, I32, I32]
     lib.mx_view_codes_bytes.restype = SZ
     lib.mx_view_scales_bytes.argtypes = [ctypes.POINTER(_Seq), I32, I32, I32]
@@ -219,12 +226,16 @@ def mx_quantize(x, views=MX_VIEW_ROW | MX_VIEW_SEQ, cu_seqlens=None, max_seqlen=
 
 
 def _desc(q_shape, k_shape, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode=MX_DQ_F32,
-          deterministic=False):
+          deterministic=False, cross=None):
+    """cross = (cu_seqlens_k, max_seqlen_k) for cross-attention (k/v with their own lengths)."""
     d = _Desc()
     d.seq = _seq(q_shape, cu_seqlens, max_seqlen)
     d.heads_q, d.head_dim = _heads_dim(q_shape, cu_seqlens)
     d.heads_kv, dk = _heads_dim(k_shape, cu_seqlens)
-    if dk != d.head_dim or k_shape[0] != q_shape[0] or (cu_seqlens is None and k_shape[2] != q_shape[2]):
+    if cross is None:
+        if dk != d.head_dim or k_shape[0] != q_shape[0] or (cu_seqlens is None and k_shape[2] != q_shape[2]):
+            raise ValueError("q and k/v geometries differ")
+    elif dk != d.head_dim or (cu_seqlens is None and k_shape[0] != q_shape[0]):
         raise ValueError("q and k/v geometries differ")
     d.causal = 1 if causal else 0
     d.softmax_scale = float(softmax_scale or 0.0)
@@ -234,19 +245,33 @@ def _desc(q_shape, k_shape, cu_seqlens, max_seqlen, causal, softmax_scale, out_d
     return d
 
 
-def _fwd(name, q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen):
+def _key_seq(k_shape, cross):
+    """mx_seq of the keys for cross-attention (None: self-attention)."""
+    if cross is None:
+        return None
+    cu_k, max_k = cross
+    return _seq(k_shape, cu_k, max_k)
+
+
+def _fwd(name, q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen, cross=None):
     lib = load()
-    qs = tuple(q_row.codes.shape)
-    desc = _desc(qs, tuple(k_row.codes.shape), cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype)
+    qs, ks = tuple(q_row.codes.shape), tuple(k_row.codes.shape)
+    desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, cross=cross)
     dev = q_row.codes.device
     seq = desc.seq
+    seq_k = _key_seq(ks, cross)
+    kseq = seq if seq_k is None else seq_k
     _check_view(lib, q_row, seq, desc.heads_q, desc.head_dim, MX_VIEW_ROW, "q_row")
-    _check_view(lib, k_row, seq, desc.heads_kv, desc.head_dim, MX_VIEW_ROW, "k_row")
-    _check_view(lib, v_seq, seq, desc.heads_kv, desc.head_dim, MX_VIEW_SEQ, "v_seq")
+    _check_view(lib, k_row, kseq, desc.heads_kv, desc.head_dim, MX_VIEW_ROW, "k_row")
+    _check_view(lib, v_seq, kseq, desc.heads_kv, desc.head_dim, MX_VIEW_SEQ, "v_seq")
     o = torch.empty(qs, dtype=out_dtype, device=dev)
     lse = torch.empty(qs[:-1], dtype=torch.float32, device=dev)
-    st = getattr(lib, name)(ctypes.byref(desc), _qv(q_row), _qv(k_row), _qv(v_seq), o.data_ptr(), lse.data_ptr(),
-                            _stream())
+    if seq_k is None:
+        st = getattr(lib, name)(ctypes.byref(desc), _qv(q_row), _qv(k_row), _qv(v_seq), o.data_ptr(),
+                                lse.data_ptr(), _stream())
+    else:
+        st = lib.mx_attn_cross_fwd(ctypes.byref(desc), ctypes.byref(seq_k), _qv(q_row), _qv(k_row), _qv(v_seq),
+                                   o.data_ptr(), lse.data_ptr(), _stream())
     _check(st, name)
     return o, lse
 
@@ -274,14 +299,18 @@ def mx_attn_workspace_size(q_shape, cu_seqlens=None, max_seqlen=None, heads_kv=N
 
 
 def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype, dq_mode, cu_seqlens,
-         max_seqlen, workspace, deterministic=False, ds_store=True):
+         max_seqlen, workspace, deterministic=False, ds_store=True, cross=None):
     lib = load()
     qs, ks = tuple(q_row.codes.shape), tuple(k_row.codes.shape)
-    desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode, deterministic)
+    desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode, deterministic, cross)
+    seq_k = _key_seq(ks, cross)
+    kseq_p = None if seq_k is None else ctypes.byref(seq_k)
     dev = q_row.codes.device
-    need = lib.mx_attn_workspace_size(ctypes.byref(desc), 1)
+    need = lib.mx_attn_cross_workspace_size(ctypes.byref(desc), kseq_p, 1)
+    if need == 0:
+        raise ValueError("invalid geometry for the backward")
     if workspace is None:
-        size = lib.mx_attn_workspace_size(ctypes.byref(desc), 2) if ds_store else need
+        size = lib.mx_attn_cross_workspace_size(ctypes.byref(desc), kseq_p, 2) if ds_store else need
         workspace = torch.empty(size, dtype=torch.uint8, device=dev)
     elif _nbytes(workspace) < need or not workspace.is_cuda:
         raise ValueError(f"workspace needs {need} bytes")
@@ -291,19 +320,25 @@ def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_sca
     dk = torch.empty(ks, dtype=out_dtype, device=dev)
     dv = torch.empty(ks, dtype=out_dtype, device=dev)
     seq = desc.seq
-    for v, h, view, what in ((q_row, desc.heads_q, MX_VIEW_ROW, "q_row"), (q_seq, desc.heads_q, MX_VIEW_SEQ, "q_seq"),
-                             (k_row, desc.heads_kv, MX_VIEW_ROW, "k_row"), (k_seq, desc.heads_kv, MX_VIEW_SEQ, "k_seq"),
-                             (v_row, desc.heads_kv, MX_VIEW_ROW, "v_row")):
-        _check_view(lib, v, seq, h, desc.head_dim, view, what)
+    kseq = seq if seq_k is None else seq_k
+    for v, sq, h, view, what in ((q_row, seq, desc.heads_q, MX_VIEW_ROW, "q_row"),
+                                 (q_seq, seq, desc.heads_q, MX_VIEW_SEQ, "q_seq"),
+                                 (k_row, kseq, desc.heads_kv, MX_VIEW_ROW, "k_row"),
+                                 (k_seq, kseq, desc.heads_kv, MX_VIEW_SEQ, "k_seq"),
+                                 (v_row, kseq, desc.heads_kv, MX_VIEW_ROW, "v_row")):
+        _check_view(lib, v, sq, h, desc.head_dim, view, what)
     nq = q_row.codes.numel()
     _check_tensor(o, nq, "o")
     _check_tensor(g, nq, "g")
     _check_tensor(lse, nq // desc.head_dim, "lse")
     if o.dtype != out_dtype or lse.dtype != torch.float32:
         raise ValueError("o must have out_dtype and lse float32")
-    st = getattr(lib, name)(ctypes.byref(desc), _qv(q_row), _qv(q_seq), _qv(k_row), _qv(k_seq), _qv(v_row),
-                            o.data_ptr(), lse.data_ptr(), g.data_ptr(), _dtype_code(g.dtype), dq.data_ptr(),
-                            dk.data_ptr(), dv.data_ptr(), _stream())
+    args = (_qv(q_row), _qv(q_seq), _qv(k_row), _qv(k_seq), _qv(v_row), o.data_ptr(), lse.data_ptr(), g.data_ptr(),
+            _dtype_code(g.dtype), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream())
+    if seq_k is None:
+        st = getattr(lib, name)(ctypes.byref(desc), *args)
+    else:
+        st = lib.mx_attn_cross_bwd(ctypes.byref(desc), ctypes.byref(seq_k), *args)
     _check(st, name)
     return dq, dk, dv, workspace
 
@@ -324,6 +359,36 @@ def mx_attn_varlen_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, cu_seqlens,
                        deterministic=False, ds_store=True):
     return _bwd("mx_attn_varlen_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale,
                 out_dtype, dq_mode, cu_seqlens, max_seqlen, workspace, deterministic, ds_store)
+
+
+def mx_attn_cross_fwd(q_row, k_row, v_seq, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                      max_seqlen_k=None, softmax_scale=0.0, out_dtype=torch.bfloat16):
+    """Non-causal cross-attention: queries [B,H,Lq,d] / [Tq,H,d] against keys and values with their
+    own lengths ([B,Hkv,Lk,d] / [Tk,Hkv,d]); packed inputs need both cu_seqlens (same number of
+    documents). -> (o [like q], lse)."""
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens or neither")
+    return _fwd("mx_attn_cross_fwd", q_row, k_row, v_seq, False, softmax_scale, out_dtype, cu_seqlens_q,
+                max_seqlen_q, cross=(cu_seqlens_k, max_seqlen_k))
+
+
+def mx_attn_cross_workspace_size(q_shape, k_shape, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                                 max_seqlen_k=None, dq_mode=MX_DQ_F32, ds_store=True):
+    lib = load()
+    desc = _desc(tuple(q_shape), tuple(k_shape), cu_seqlens_q, max_seqlen_q, False, 0.0, torch.bfloat16, dq_mode,
+                 cross=(cu_seqlens_k, max_seqlen_k))
+    seq_k = _key_seq(tuple(k_shape), (cu_seqlens_k, max_seqlen_k))
+    return lib.mx_attn_cross_workspace_size(ctypes.byref(desc), ctypes.byref(seq_k), 2 if ds_store else 1)
+
+
+def mx_attn_cross_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, cu_seqlens_q=None, cu_seqlens_k=None,
+                      max_seqlen_q=None, max_seqlen_k=None, softmax_scale=0.0, out_dtype=torch.bfloat16,
+                      dq_mode=MX_DQ_F32, workspace=None, ds_store=True):
+    """Backward of mx_attn_cross_fwd -> (dq [like q], dk, dv [like k], workspace)."""
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens or neither")
+    return _bwd("mx_attn_cross_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, False, softmax_scale, out_dtype,
+                dq_mode, cu_seqlens_q, max_seqlen_q, workspace, False, ds_store, cross=(cu_seqlens_k, max_seqlen_k))
 
 
 def mx_read_flags(workspace):

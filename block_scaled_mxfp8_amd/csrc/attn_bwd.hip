@@ -146,8 +146,10 @@ struct DkvStage {
   alignas(16) float ndlt[kStepQ];       // -D: the E product's initial value
 };
 
+// doc_start / n: the queries of the sequence or document; doc_k / nk: its keys (the same for
+// self-attention).
 struct KvWork {
-  int s, doc_start, n, hkv, kb;
+  int s, doc_start, n, doc_k, nk, hkv, kb;
   bool valid;
 };
 
@@ -157,7 +159,7 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
   KvWork w;
   w.valid = true;
   if (!kPacked) {
-    const int nkb = (g.seqlen + kBlockK - 1) / kBlockK;
+    const int nkb = (p.geom_k.seqlen + kBlockK - 1) / kBlockK;
     int bh, rank;
     lpt_order(blockIdx.x, p.heads_kv * g.batch, nkb, bh, rank);
     w.kb = rank;                          // causal: the first key block sees the most queries
@@ -165,13 +167,17 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
     w.hkv = bh % p.heads_kv;
     w.doc_start = 0;
     w.n = g.seqlen;
+    w.doc_k = 0;
+    w.nk = p.geom_k.seqlen;
   } else {
     w.kb = blockIdx.x;
     w.hkv = blockIdx.y;
     w.s = blockIdx.z;
     w.doc_start = g.cu[w.s];
     w.n = g.cu[w.s + 1] - w.doc_start;
-    w.valid = w.kb * kBlockK < w.n;
+    w.doc_k = p.geom_k.cu[w.s];
+    w.nk = p.geom_k.cu[w.s + 1] - w.doc_k;
+    w.valid = w.kb * kBlockK < w.nk;
   }
   return w;
 }
@@ -440,13 +446,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   __shared__ DkvShared<D> sm;
   const KvWork w = decode_kv<kPacked>(p);
   if (!w.valid) return;
-  const Geom& g = p.geom;
+  const Geom& gk = p.geom_k;              // keys, values, dK, dV
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int kg = wave & 3;                // key group
   const int hh = lane >> 5;
   const int l32 = lane & 31;
-  const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
+  const long long sbase_k = kPacked ? (long long)w.doc_k : (long long)w.s;
   const int k0 = w.kb * kBlockK;
   const int kw = k0 + kg * 32;            // first key of this key group
   const int key = kw + l32;               // this lane's key (column of S and E)
@@ -454,21 +460,22 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   constexpr int NCT = D / 32;             // 32-channel tiles
   const int group = p.heads_q / p.heads_kv;
   const int qfirst = p.causal ? (k0 / kStepQ) * kStepQ : 0;
-  const int nsteps = ((w.n - qfirst + kStepQ - 1) / kStepQ) * group;
+  const int nsteps = ((w.n - qfirst + kStepQ - 1) / kStepQ) * group;   // 0: no queries (dK = dV = 0)
   // a key group sees nothing in a step whose queries all precede its keys (causal)
-  auto active = [&](int q0) { return kw < w.n && !(p.causal && kw > q0 + kStepQ - 1); };
+  auto active = [&](int q0) { return kw < w.nk && !(p.causal && kw > q0 + kStepQ - 1); };
 
   if (wave < kDkvProducers) {
     // ---------------- producer + loader ----------------
+    if (nsteps == 0) return;              // (uniform: no wave of the workgroup reaches a barrier)
     const int qt = wave >> 2;
     const int lw = wave;                  // loader index
-    const bool kvalid = key < w.n;
+    const bool kvalid = key < w.nk;
     const float c = p.scale * kLog2e;
     v8i kop[NS], vop[NS];
     uint32_t kvsc = 0;   // byte s = K scale of contraction step s, byte 2 + s = V scale (groups 2s + hh)
 #pragma unroll
     for (int s = 0; s < NS; s++) {
-      const long long off = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, w.hkv, min(key, w.n - 1), 64 * s);
+      const long long off = elem_offset_k<kPacked>(gk, p.heads_kv, D, sbase_k, w.hkv, min(key, w.nk - 1), 64 * s);
       kop[s] = cat(*reinterpret_cast<const v4i*>(p.k_codes + off + 16 * hh),
                    *reinterpret_cast<const v4i*>(p.k_codes + off + 32 + 16 * hh));
       vop[s] = cat(*reinterpret_cast<const v4i*>(p.vr_codes + off + 16 * hh),
@@ -506,7 +513,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
       if (j < nsteps && active(q0)) {
         const DkvStage<D>& S = sm.st[j % 3];
         uint32_t* cx = sm.cx[j & 1][kg];
-        const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.n;
+        const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.nk;
         int dse;
         if (need_mask)
           dse = dkv_codes_tile<D, true>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, q0 + 4 * hh - key,
@@ -557,11 +564,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   }
   const int lw = wave - kDkvProducers;    // SEQ-tile loader index
   int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
-  dkv_issue_seq<D, kPacked, kWaves>(p, w, hq_l, q0_l, sm.st[0], lw);
-  wait_vmem();
-  wg_barrier();                           // stage 0 loaded
+  if (nsteps > 0) {
+    dkv_issue_seq<D, kPacked, kWaves>(p, w, hq_l, q0_l, sm.st[0], lw);
+    wait_vmem();
+    wg_barrier();                         // stage 0 loaded
+  }
   int q0_a = qfirst;                      // step whose codes are applied (j - 1)
-  for (int j = 0; j <= nsteps; j++) {
+  for (int j = 0; nsteps > 0 && j <= nsteps; j++) {
     next_step(hq_l, q0_l, qfirst, w.n);  // step j + 1
     const bool load = j + 1 < nsteps;
     if (load) dkv_issue_seq<D, kPacked, kWaves>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], lw);
@@ -602,8 +611,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   //      t*32 + 8 b4 + 4 hh .. +3 (the key is recomputed from the lane id here rather than kept
   //      live through the loop) ----
   const int key_e = kw + (__lane_id() & 31);
-  if (key_e < w.n) {
-    const long long base = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, w.hkv, key_e, 0) + 4 * (__lane_id() >> 5);
+  if (key_e < w.nk) {
+    const long long base = elem_offset_k<kPacked>(gk, p.heads_kv, D, sbase_k, w.hkv, key_e, 0) + 4 * (__lane_id() >> 5);
 #pragma unroll
     for (int t = 0; t < NCT; t++) {
 #pragma unroll
@@ -639,8 +648,9 @@ struct DqStage {
   alignas(16) uint8_t kss[2 * D];       // K SEQ scales [group][channel]
 };
 
+// doc_start / n: the queries of the sequence or document; doc_k / nk: its keys.
 struct QWork {
-  int s, doc_start, n, h, qb;
+  int s, doc_start, n, doc_k, nk, h, qb;
   bool valid;
 };
 
@@ -658,12 +668,16 @@ __device__ __forceinline__ QWork decode_q(const BwdParams& p) {
     w.qb = qb;
     w.doc_start = 0;
     w.n = g.seqlen;
+    w.doc_k = 0;
+    w.nk = p.geom_k.seqlen;
   } else {
     w.qb = blockIdx.x;
     w.h = blockIdx.y;
     w.s = blockIdx.z;
     w.doc_start = g.cu[w.s];
     w.n = g.cu[w.s + 1] - w.doc_start;
+    w.doc_k = p.geom_k.cu[w.s];
+    w.nk = p.geom_k.cu[w.s + 1] - w.doc_k;
     if (p.causal) w.qb = (w.n + kBlockQ - 1) / kBlockQ - 1 - w.qb;
     w.valid = w.qb >= 0 && w.qb * kBlockQ < w.n;
   }
@@ -674,12 +688,12 @@ __device__ __forceinline__ QWork decode_q(const BwdParams& p) {
 template <int D>
 __device__ __forceinline__ void dq_issue(const BwdParams& p, const QWork& w, int hkv, int kt, DqStage<D>& st,
                                          uint32_t& sv, const int (&roff)[2], int soff) {
-  const Geom& g = p.geom;
+  const Geom& g = p.geom_k;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const long long sbase = packed(g) ? (long long)w.doc_start : (long long)w.s;
-  const int nlast = w.n - 1;
-  const int glast = ((w.n + 31) >> 5) - 1;
+  const long long sbase = packed(g) ? (long long)w.doc_k : (long long)w.s;
+  const int nlast = w.nk - 1;
+  const int glast = ((w.nk + 31) >> 5) - 1;
   const int k0 = kt * kStepK;
   if (wave < 2) {                                     // wave 0: K ROW, wave 1: V ROW
     const long long tok0 = elem_offset(g, p.heads_kv, D, sbase, hkv, k0, 0);
@@ -687,8 +701,8 @@ __device__ __forceinline__ void dq_issue(const BwdParams& p, const QWork& w, int
                     roff, wave == 0 ? st.kr : st.vr);
   } else {                                            // waves 2-3: K SEQ, alternate instructions
     const int g0 = k0 >> 5;
-    const long long row0 = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, min(g0, glast));
-    const long long row1 = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, min(g0 + 1, glast));
+    const long long row0 = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_k, min(g0, glast));
+    const long long row1 = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_k, min(g0 + 1, glast));
     dma_seq_tile<D>(p.ks_codes, row0, row1, soff, st.ks, wave - 2, 2);
   }
   sv = 0;
@@ -699,7 +713,7 @@ __device__ __forceinline__ void dq_issue(const BwdParams& p, const QWork& w, int
     sv = load_row_scales<D>((wave == 0 ? p.k_scales : p.vr_scales) + (tok >> 5), rel);
   } else if (wave == 2 && lane < D / 2) {             // K SEQ scales, a dword per lane
     const int gi = min((k0 >> 5) + (lane * 4) / D, glast);
-    const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_start, gi);
+    const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_k, gi);
     sv = *reinterpret_cast<const uint32_t*>(p.ks_scales + row * D + (lane * 4) % D);
   }
 }
@@ -735,13 +749,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const float c = p.scale * kLog2e;
   constexpr int NS = D / 64;
   constexpr int NCT = D / 32;
-  const int kend = p.causal ? min(w.n, q0 + kBlockQ) : w.n;
-  const int nkt = (kend + kStepK - 1) / kStepK;
+  const int kend = p.causal ? min(w.n, q0 + kBlockQ) : w.nk;
+  const int nkt = (kend + kStepK - 1) / kStepK;   // 0: no keys (dQ = 0)
 
   const int roff[2] = {row_tile_lane_off<D>(lane, 0), row_tile_lane_off<D>(lane, 1)};
   const int soff = seq_tile_lane_off(lane);
-  uint32_t sv;
-  dq_issue<D>(p, w, hkv, 0, sm[0], sv, roff, soff);
+  uint32_t sv = 0;
+  if (nkt > 0) dq_issue<D>(p, w, hkv, 0, sm[0], sv, roff, soff);
 
   // Q and G of the lane's query: B operands of S^T and E^T, kept in registers
   v8i qop[NS], gop[NS];
@@ -787,7 +801,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   }
   const int soff_c = l32 * 32 + (half_swz(l32, hh) << 4);   // SEQ tile, channel l32 of group 0
   const int scoff = hh * D + l32;                            // SEQ scale of channel l32, group hh
-  dq_put<D>(sm[0], sv);
+  if (nkt > 0) dq_put<D>(sm[0], sv);
   wait_vmem();
   __syncthreads();
 
@@ -797,7 +811,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
     const DqStage<D>& S = sm[buf];
     const int kbase = kt * kStepK;
     if (qw < w.n && !(p.causal && kbase > qw + 31)) {
-      const bool need_mask = (p.causal && kbase + kStepK - 1 > qw) || kbase + kStepK > w.n || qw + 32 > w.n;
+      const bool need_mask = (p.causal && kbase + kStepK - 1 > qw) || kbase + kStepK > w.nk || qw + 32 > w.n;
       v8i dsop;
       int dse[2];
 #pragma unroll
@@ -825,7 +839,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
           float x = __builtin_fmaf(sacc[i], c, -lse2);
           if (need_mask) {
             const int k = kbase + T * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (!(qvalid && k < w.n && (!p.causal || k <= qi))) x = -INFINITY;
+            if (!(qvalid && k < w.nk && (!p.causal || k <= qi))) x = -INFINITY;
           }
           U[i] = __builtin_amdgcn_exp2f(x) * eacc[i];
         }
@@ -915,18 +929,18 @@ template <int D, bool kPacked>
 __device__ __forceinline__ void dqds_issue_k(const BwdParams& p, const QWork& w, const DqdsCtx& c, int kt,
                                              DqdsStage<D>* __restrict__ st) {
   constexpr int PER = D / 32, NSEQ = 2 * PER;
-  const Geom& g = p.geom;
+  const Geom& g = p.geom_k;
   const int g0 = 2 * kt;
 #pragma unroll
   for (int jj = 0; jj < NSEQ / kWaves; jj++) {
     const int j = c.wave + kWaves * jj;
     const int grp = min(g0 + j / PER, c.glast);
-    const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, c.hkv, w.doc_start, grp);
+    const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, c.hkv, w.doc_k, grp);
     lds_dma(p.ks_codes + row * (D * 32) + (j % PER) * 1024 + c.soff, st->ks + j * 1024, 16);
   }
   const int i = c.lane % (D / 2);             // dword i of [group g0 | group g0 + 1]; d = 64: lanes 32+ repeat
   const int grp = min(g0 + (i * 4) / D, c.glast);
-  const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, c.hkv, w.doc_start, grp);
+  const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, c.hkv, w.doc_k, grp);
   lds_dma(p.ks_scales + row * D + (i * 4) % D, st->kss[c.wave], 4);
 }
 
@@ -993,9 +1007,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(BwdParams p) {
   const int q0 = w.qb * kBlockQ;
   const int qw = q0 + c.wave * 32;            // first query of this wave = 32 qb
   const int qb = qw >> 5;
-  const int kend = p.causal ? min(w.n, q0 + kBlockQ) : w.n;
-  const int nkt = (kend + kStepK - 1) / kStepK;
-  c.glast = ((w.n + 31) >> 5) - 1;
+  const int kend = p.causal ? min(w.n, q0 + kBlockQ) : w.nk;
+  const int nkt = (kend + kStepK - 1) / kStepK;   // 0: no keys (dQ = 0; nothing is loaded)
+  c.glast = ((w.nk + 31) >> 5) - 1;            // last key group
   c.kb_end = qw >= w.n ? 0 : (p.causal ? qb + 1 : c.glast + 1);
   c.blk0 = 0;
   c.ex0 = 0;
@@ -1018,12 +1032,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(BwdParams p) {
   // issue (K 0, dS P-2, K 1, dS P-1), giving the steady-state order from the first real tile.
   v4i dsr[kPre][2];
   int exr[kPre];
+  if (nkt > 0) {
 #pragma unroll
-  for (int u = 0; u < kPre - 2; u++) dqds_load_ds(p, c, u, dsr[u], exr[u]);
+    for (int u = 0; u < kPre - 2; u++) dqds_load_ds(p, c, u, dsr[u], exr[u]);
+  }
 
   // kPre tiles per trip (the register ring is indexed by a compile-time slot); trips run whole,
   // the tiles past nkt have no blocks and only keep the issue pattern uniform
-  for (int kt0 = -2; kt0 < nkt; kt0 += kPre) {
+  for (int kt0 = -2; nkt > 0 && kt0 < nkt; kt0 += kPre) {
 #pragma unroll
     for (int u = 0; u < kPre; u++) {
       const int kt = kt0 + u;
@@ -1084,10 +1100,10 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
   const Geom& g = p.geom;
   dim3 gkv, gq;
   if (!packed(g)) {
-    gkv = dim3((unsigned)((long long)((g.seqlen + kBlockK - 1) / kBlockK) * p.heads_kv * g.batch), 1, 1);
+    gkv = dim3((unsigned)((long long)((p.geom_k.seqlen + kBlockK - 1) / kBlockK) * p.heads_kv * g.batch), 1, 1);
     gq = dim3((unsigned)((long long)((g.seqlen + kBlockQ - 1) / kBlockQ) * p.heads_q * g.batch), 1, 1);
   } else {
-    gkv = dim3((unsigned)((g.max_seqlen + kBlockK - 1) / kBlockK), (unsigned)p.heads_kv, (unsigned)g.n_docs);
+    gkv = dim3((unsigned)((p.geom_k.max_seqlen + kBlockK - 1) / kBlockK), (unsigned)p.heads_kv, (unsigned)g.n_docs);
     gq = dim3((unsigned)((g.max_seqlen + kBlockQ - 1) / kBlockQ), (unsigned)p.heads_q, (unsigned)g.n_docs);
   }
   const bool store = p.ds_codes != nullptr;

@@ -71,8 +71,10 @@ struct FwdSmem {
 // Work decode: which (sequence, head, query tile) this workgroup computes.
 struct Work {
   int s;          // batch index or document index
-  int doc_start;  // packed: first token of the document
-  int n;          // tokens in the sequence / document
+  int doc_start;  // packed: first query token of the document
+  int n;          // query tokens in the sequence / document
+  int doc_k;      // packed: first key token of the document
+  int nk;         // key tokens (= n for self-attention)
   int h;          // query head
   int qt;         // query tile
   bool valid;
@@ -92,12 +94,16 @@ __device__ __forceinline__ Work decode_work(const AttnParams& p) {
     w.qt = p.causal ? nqt - 1 - rank : rank;  // causal: the last query tile sees the most keys
     w.doc_start = 0;
     w.n = g.seqlen;
+    w.doc_k = 0;
+    w.nk = p.geom_k.seqlen;
   } else {
     w.qt = blockIdx.x;
     w.h = blockIdx.y;
     w.s = blockIdx.z;
     w.doc_start = g.cu[w.s];
     w.n = g.cu[w.s + 1] - w.doc_start;
+    w.doc_k = p.geom_k.cu[w.s];
+    w.nk = p.geom_k.cu[w.s + 1] - w.doc_k;
     if (p.causal) w.qt = (w.n + kBlockM - 1) / kBlockM - 1 - w.qt;
     w.valid = w.qt >= 0 && w.qt * kBlockM < w.n;
   }
@@ -138,17 +144,17 @@ struct KvBase {
 
 template <int D, bool kPacked>
 __device__ __forceinline__ KvBase kv_base(const AttnParams& p, const Work& w, int hkv) {
-  const Geom& g = p.geom;
-  const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
+  const Geom& g = p.geom_k;
+  const long long sbase = kPacked ? (long long)w.doc_k : (long long)w.s;
   const long long k0 = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, hkv, 0, 0);
-  const long long row0 = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, hkv, w.doc_start, 0);
+  const long long row0 = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, hkv, w.doc_k, 0);
   KvBase b;
   b.k = p.k_codes + k0;
   b.ks = p.k_scales + (k0 >> 5);
   b.v = p.v_codes + row0 * (D * 32);
   b.vs = p.v_scales + row0 * D;
   b.ts = (int)token_stride_k<kPacked>(p.heads_kv, D);
-  b.n = w.n;
+  b.n = w.nk;
   return b;
 }
 
@@ -283,16 +289,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   const int qw = q0 + wave * 32;             // first query of this wave
   const int qi = qw + l32;                   // this lane's query
   const bool qvalid = qi < w.n;
-  const int kend = p.causal ? min(w.n, q0 + kBlockM) : w.n;  // keys this workgroup needs
+  const int kend = p.causal ? min(w.n, q0 + kBlockM) : w.nk;  // keys this workgroup needs (may be 0)
   const int nkt = (kend + kBlockN - 1) / kBlockN;
   const uint32_t kl = k_lane_off<D, kPacked>(p, wave), vl = v_lane_off();
   const uint32_t ksl = (uint32_t)(lane * (int)token_stride_k<kPacked>(p.heads_kv, D)) >> 5;   // K scales of key `lane`
   const uint32_t vsl = (uint32_t)(lane * 4);
 
   const KvBase kvb = kv_base<D, kPacked>(p, w, hkv);
-  issue_k<D>(kvb, 0, wave, sm.k[0], sm.ks[0], kl, ksl);
+  if (nkt > 0) {
+    issue_k<D>(kvb, 0, wave, sm.k[0], sm.ks[0], kl, ksl);
+    issue_v<D>(kvb, 0, wave, sm.v[0], sm.vs[0], vl, vsl);
+  }
   if (nkt > 1) issue_k<D>(kvb, 1, wave, sm.k[1], sm.ks[1], kl, ksl);
-  issue_v<D>(kvb, 0, wave, sm.v[0], sm.vs[0], vl, vsl);
 
   // ---- Q operand (B of S^T = K Q^T), kept in registers ----
   constexpr int NS = D / 64;  // contraction steps of 64 over d
@@ -314,7 +322,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   // a wave is idle for key tile j when all its keys follow all its queries (causal) or it has no queries
   auto active = [&](int j) { return qw < w.n && !(p.causal && j * kBlockN > qw + 31); };
   // keys visible to this lane's query: [0, vis_end)
-  const int vis_end = p.causal ? min(w.n, qi + 1) : w.n;
+  const int vis_end = p.causal ? min(w.n, qi + 1) : w.nk;
 
   v16f oacc[D / 32];
 #pragma unroll
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   wait_vmem();
   __syncthreads();
   v16f sa[2], sb[2];
-  if (active(0)) scores<D>(sm, 0, qop, qsc, sa);
+  if (nkt > 0 && active(0)) scores<D>(sm, 0, qop, qsc, sa);
   wg_barrier();   // every wave has read K slot 0 before the first tile loads K(2) into it
 
   // One key tile kt (slot st = kt % 2, a constant in each unrolled copy): issue the loads of K
@@ -340,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     if (active(kt)) {
       // ---- mask (diagonal / tail tiles only): the lane's key T*32 + 8(i>>2) + 4hh + (i&3)
       //      of the tile is visible when it is below vis_end ----
-      const bool need_mask = (p.causal && kbase + kBlockN - 1 > qw) || kbase + kBlockN > w.n;
+      const bool need_mask = (p.causal && kbase + kBlockN - 1 > qw) || kbase + kBlockN > w.nk;
       if (need_mask) {
         const int lim = vis_end - kbase - 4 * hh;
         mask_tile<0>(cur[0], lim, std::make_integer_sequence<int, 16>{});

@@ -28,7 +28,8 @@ struct QuantizeParams {
 };
 
 struct AttnParams {
-  Geom geom;
+  Geom geom;             // queries (and O, LSE)
+  Geom geom_k;           // keys and values: the same as geom for self-attention
   int heads_q, heads_kv, head_dim;
   int causal;
   float scale;           // alpha
@@ -39,11 +40,11 @@ struct AttnParams {
   const uint8_t* v_codes; const uint8_t* v_scales;    // SEQ view of V
   void* o;
   float* lse;
-  // work list for packed mode (device, built by the forward launcher in the workspace-free path)
 };
 
 struct BwdParams {
-  Geom geom;
+  Geom geom;             // queries (and G, O, LSE, dQ)
+  Geom geom_k;           // keys and values (and dK, dV): the same as geom for self-attention
   int heads_q, heads_kv, head_dim;
   int causal;
   float scale;

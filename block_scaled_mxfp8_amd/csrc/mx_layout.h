@@ -101,7 +101,8 @@ __host__ __device__ constexpr inline int seq_tok(int p) { return 8 * ((p >> 2) &
 // block (qb, kb) of a query head holds 1024 E4M3 codes and one E8M0 byte.
 //   block rows: row(qb) = seq_group_row of query group qb (the SEQ-view row numbering)
 //   code blocks: batched causal: (b * H + h) * nb(nb+1)/2 + qb(qb+1)/2 + kb (kb <= qb only);
-//                otherwise row(qb) * cols + kb, cols = ceil(L / 32) or ceil(max_seqlen / 32)
+//                otherwise row(qb) * cols + kb, cols = ceil(L / 32) or ceil(max_seqlen / 32) of
+//                the keys (cross-attention: the key sequences' lengths)
 //   exponents:   row(qb) * ecols + kb, ecols = cols rounded up to a multiple of 4
 struct DsStore {
   long long head_blocks;   // batched causal: code blocks per (b, h)
@@ -109,12 +110,13 @@ struct DsStore {
   bool tri;                // batched causal (triangular code rows)
 };
 
-__host__ __device__ inline DsStore ds_store_geom(const Geom& g, bool causal) {
+// g: the queries' geometry (block rows), gk: the keys' (block columns).
+__host__ __device__ inline DsStore ds_store_geom(const Geom& g, const Geom& gk, bool causal) {
   DsStore s;
-  const long long nb = packed(g) ? (g.max_seqlen + 31) / 32 : (g.seqlen + 31) / 32;
+  const long long nb = packed(gk) ? (gk.max_seqlen + 31) / 32 : (gk.seqlen + 31) / 32;
   s.cols = (int)nb;
   s.ecols = (int)((nb + 3) / 4 * 4);
-  s.tri = !packed(g) && causal;
+  s.tri = !packed(g) && causal;           // causal is self-attention only (same rows and columns)
   s.head_blocks = s.tri ? nb * (nb + 1) / 2 : (long long)g.gseq * nb;
   return s;
 }

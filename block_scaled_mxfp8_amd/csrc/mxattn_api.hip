@@ -77,7 +77,7 @@ struct BwdWorkspace {
   mx::DsStore ds;
 };
 
-BwdWorkspace bwd_layout(const mx::Geom& g, const mx_attn_desc* d) {
+BwdWorkspace bwd_layout(const mx::Geom& g, const mx::Geom& gk, const mx_attn_desc* d) {
   BwdWorkspace w;
   const int hq = d->heads_q, dim = d->head_dim;
   size_t off = 0;
@@ -89,7 +89,7 @@ BwdWorkspace bwd_layout(const mx::Geom& g, const mx_attn_desc* d) {
   w.ndelta = off; off += align_up((size_t)g.total * hq * sizeof(float));
   w.lse2 = off; off += align_up((size_t)g.total * hq * sizeof(float));
   w.total = off;
-  w.ds = mx::ds_store_geom(g, d->causal != 0);
+  w.ds = mx::ds_store_geom(g, gk, d->causal != 0);
   const size_t rows = (size_t)g.gseq * hq * (mx::packed(g) ? 1 : (size_t)g.batch);   // query groups
   const size_t blocks = w.ds.tri ? (size_t)g.batch * hq * (size_t)w.ds.head_blocks : rows * (size_t)w.ds.cols;
   w.store_ok = blocks <= UINT32_MAX && rows * (size_t)w.ds.ecols <= UINT32_MAX;
@@ -99,17 +99,35 @@ BwdWorkspace bwd_layout(const mx::Geom& g, const mx_attn_desc* d) {
   return w;
 }
 
-mx_status fwd_impl(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o, float* lse,
-                   void* stream, bool need_packed) {
-  mx::Geom g;
+// Key geometry of a call: the queries' own for self-attention (seq_k == nullptr); for
+// cross-attention *seq_k, which must use the same layout (batched with the same batch, or
+// packed with the same number of documents: document j's queries attend to document j's
+// keys). Cross-attention is non-causal.
+mx_status key_geom(const mx_attn_desc* d, const mx::Geom& g, const mx_seq* seq_k, mx::Geom* gk) {
+  if (!seq_k) {
+    *gk = g;
+    return MX_OK;
+  }
+  if (!make_geom(seq_k, gk)) return MX_E_ARG;
+  if (mx::packed(g) != mx::packed(*gk)) return MX_E_ARG;
+  if (mx::packed(g) ? gk->n_docs != g.n_docs : gk->batch != g.batch) return MX_E_ARG;
+  if (d->causal) return MX_E_UNSUPPORTED;
+  return MX_OK;
+}
+
+mx_status fwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview k_row, mx_qview v_seq,
+                   void* o, float* lse, void* stream, bool need_packed) {
+  mx::Geom g, gk;
   mx_status st = check_desc(desc, &g);
   if (st != MX_OK) return st;
   if (need_packed && !desc->seq.cu_seqlens) return MX_E_ARG;
+  if ((st = key_geom(desc, g, seq_k, &gk)) != MX_OK) return st;
   if ((st = check_view(q_row)) != MX_OK || (st = check_view(k_row)) != MX_OK || (st = check_view(v_seq)) != MX_OK)
     return st;
   if (!o || !lse || !aligned(o, 16) || !aligned(lse, 4)) return MX_E_ARG;
   mx::AttnParams p = {};
   p.geom = g;
+  p.geom_k = gk;
   p.heads_q = desc->heads_q;
   p.heads_kv = desc->heads_kv;
   p.head_dim = desc->head_dim;
@@ -125,24 +143,26 @@ mx_status fwd_impl(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_
   return mx::launch_attn_fwd(p, (hipStream_t)stream) == hipSuccess ? MX_OK : MX_E_DEVICE;
 }
 
-mx_status bwd_impl(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row, mx_qview k_seq,
-                   mx_qview v_row, const void* o, const float* lse, const void* gptr, mx_dtype g_dtype, void* dq,
-                   void* dk, void* dv, void* stream, bool need_packed) {
-  mx::Geom g;
+mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
+                   mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* gptr, mx_dtype g_dtype,
+                   void* dq, void* dk, void* dv, void* stream, bool need_packed) {
+  mx::Geom g, gk;
   mx_status st = check_desc(desc, &g);
   if (st != MX_OK) return st;
   if (need_packed && !desc->seq.cu_seqlens) return MX_E_ARG;
+  if ((st = key_geom(desc, g, seq_k, &gk)) != MX_OK) return st;
   const mx_qview views[5] = {q_row, q_seq, k_row, k_seq, v_row};
   for (const auto& v : views)
     if ((st = check_view(v)) != MX_OK) return st;
   if (!o || !lse || !gptr || !dq || !dk || !dv) return MX_E_ARG;
   if (!aligned(o, 16) || !aligned(gptr, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16)) return MX_E_ARG;
   if (g_dtype != MX_F32 && g_dtype != MX_BF16) return MX_E_ARG;
-  const BwdWorkspace w = bwd_layout(g, desc);
+  const BwdWorkspace w = bwd_layout(g, gk, desc);
   if (!desc->workspace || desc->workspace_bytes < w.total || !aligned(desc->workspace, kAlign)) return MX_E_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(desc->workspace);
   mx::BwdParams p = {};
   p.geom = g;
+  p.geom_k = gk;
   p.heads_q = desc->heads_q;
   p.heads_kv = desc->heads_kv;
   p.head_dim = desc->head_dim;
@@ -218,32 +238,50 @@ mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const 
 
 mx_status mx_attn_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o, float* lse,
                       void* stream) {
-  return fwd_impl(desc, q_row, k_row, v_seq, o, lse, stream, false);
+  return fwd_impl(desc, nullptr, q_row, k_row, v_seq, o, lse, stream, false);
 }
 
 mx_status mx_attn_varlen_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o,
                              float* lse, void* stream) {
-  return fwd_impl(desc, q_row, k_row, v_seq, o, lse, stream, true);
+  return fwd_impl(desc, nullptr, q_row, k_row, v_seq, o, lse, stream, true);
+}
+
+mx_status mx_attn_cross_fwd(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview k_row,
+                            mx_qview v_seq, void* o, float* lse, void* stream) {
+  if (!seq_k) return MX_E_ARG;
+  return fwd_impl(desc, seq_k, q_row, k_row, v_seq, o, lse, stream, false);
 }
 
 mx_status mx_attn_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row, mx_qview k_seq,
                       mx_qview v_row, const void* o, const float* lse, const void* g, mx_dtype g_dtype, void* dq,
                       void* dk, void* dv, void* stream) {
-  return bwd_impl(desc, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, false);
+  return bwd_impl(desc, nullptr, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, false);
 }
 
 mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
                              mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                              mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream) {
-  return bwd_impl(desc, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, true);
+  return bwd_impl(desc, nullptr, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, true);
+}
+
+mx_status mx_attn_cross_bwd(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview q_seq,
+                            mx_qview k_row, mx_qview k_seq, mx_qview v_row, const void* o, const float* lse,
+                            const void* g, mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream) {
+  if (!seq_k) return MX_E_ARG;
+  return bwd_impl(desc, seq_k, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, false);
+}
+
+size_t mx_attn_cross_workspace_size(const mx_attn_desc* desc, const mx_seq* seq_k, int32_t for_bwd) {
+  mx::Geom g, gk;
+  if (for_bwd != 1 && for_bwd != 2) return 0;
+  if (!desc || !make_geom(&desc->seq, &g) || desc->heads_q < 1 || !valid_dim(desc->head_dim)) return 0;
+  if (key_geom(desc, g, seq_k, &gk) != MX_OK) return 0;
+  const BwdWorkspace w = bwd_layout(g, gk, desc);
+  return for_bwd == 2 ? w.total_store : w.total;
 }
 
 size_t mx_attn_workspace_size(const mx_attn_desc* desc, int32_t for_bwd) {
-  mx::Geom g;
-  if (for_bwd != 1 && for_bwd != 2) return 0;
-  if (!desc || !make_geom(&desc->seq, &g) || desc->heads_q < 1 || !valid_dim(desc->head_dim)) return 0;
-  const BwdWorkspace w = bwd_layout(g, desc);
-  return for_bwd == 2 ? w.total_store : w.total;
+  return mx_attn_cross_workspace_size(desc, nullptr, for_bwd);
 }
 
 size_t mx_view_codes_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view) {

@@ -140,6 +140,26 @@ mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
                              mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                              mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
 
+/* Cross-attention (jagged or batched): the queries follow desc->seq, the keys and values the
+ * geometry *seq_k (the pages' production shape: a fixed number of seed queries per document
+ * against jagged key/value sequences; Meta write-up, "what the production model looks like",
+ * and FLAMIA notes section 6 for the jagged layout). Query sequence or document j attends to
+ * key sequence or document j: both geometries batched with the same batch (lengths L_q and
+ * L_k), or both packed with the same n_docs (documents of different lengths on each side;
+ * a document may have no keys: its queries get O = 0 and LSE = +inf, and dQ = 0). Non-causal
+ * only (desc->causal != 0: MX_E_UNSUPPORTED). K and V (views, dK, dV) use seq_k's layout and
+ * token count; Q, O, LSE, G and dQ use desc->seq's. Otherwise identical to mx_attn_fwd /
+ * mx_attn_bwd (same kernels); the workspace comes from mx_attn_cross_workspace_size. */
+mx_status mx_attn_cross_fwd(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview k_row,
+                            mx_qview v_seq, void* o, float* lse, void* stream);
+mx_status mx_attn_cross_bwd(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview q_seq,
+                            mx_qview k_row, mx_qview k_seq, mx_qview v_row, const void* o, const float* lse,
+                            const void* g, mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
+/* Workspace bytes for mx_attn_cross_bwd (for_bwd as for mx_attn_workspace_size; the dS store
+ * has one column of blocks per 32 keys of the longest key sequence). 0 for an invalid pair of
+ * geometries. */
+size_t mx_attn_cross_workspace_size(const mx_attn_desc* desc, const mx_seq* seq_k, int32_t for_bwd);
+
 /* Bytes of device workspace for mx_attn_bwd with this descriptor.
  *   for_bwd = 1: the minimum (G's views, -D and LSE log2 e per row, the status word;
  *     O(tokens x heads x head_dim)).

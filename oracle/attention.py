@@ -164,7 +164,7 @@ def head_forward(q, k, v, causal, softmax_scale=None, quantized=True, out_dtype=
         Sraw = Qt[qi] @ Kt.T
         Sp = np.where(mask, Sraw * c, -np.inf)            # base-2 logits S' = S log2 e
         has = mask.any(axis=1)
-        M = np.where(has, np.ceil(np.max(Sp, axis=1)), 0.0)
+        M = np.where(has, np.ceil(np.max(Sp, axis=1, initial=-np.inf)), 0.0)   # (no keys at all: no row is live)
         x = Sp - M[:, None]
         if bounds or perturb:
             absS = np.abs(Qt[qi]) @ np.abs(Kt).T

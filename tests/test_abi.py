@@ -166,3 +166,35 @@ def test_workspace_sizes_with_and_without_the_ds_store(lib, causal):
     small = lib.mx_attn_workspace_size(ctypes.byref(desc), 1)
     rows = 2 * (300 // 32 + 5)
     assert lib.mx_attn_workspace_size(ctypes.byref(desc), 2) == small + _up(rows * 4 * 1024) + _up(rows * 4)
+
+
+def test_cross_attention_validation_and_workspace(lib):
+    # keys with their own geometry: same layout kind and batch / document count, non-causal
+    v = _lib._QView(FAKE, FAKE)
+    desc = _bwd_desc(_seq(batch=2, seqlen=100), 3, 128, 0)
+    sk = _seq(batch=2, seqlen=300)
+    f, b = lib.mx_attn_cross_fwd, lib.mx_attn_cross_bwd
+    assert f(ctypes.byref(desc), None, v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(desc), ctypes.byref(_seq(batch=3, seqlen=300)), v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    p = _lib._Seq()
+    p.cu_seqlens, p.n_docs, p.max_seqlen, p.total_tokens = FAKE, 2, 300, 400
+    assert f(ctypes.byref(desc), ctypes.byref(p), v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    causal = _bwd_desc(_seq(batch=2, seqlen=100), 3, 128, 1)
+    assert f(ctypes.byref(causal), ctypes.byref(sk), v, v, v, FAKE, FAKE, None) == _lib.MX_E_UNSUPPORTED
+    assert lib.mx_attn_cross_workspace_size(ctypes.byref(causal), ctypes.byref(sk), 1) == 0
+    # validation passes the geometry and reaches the null output / missing workspace
+    assert f(ctypes.byref(desc), ctypes.byref(sk), v, v, v, None, FAKE, None) == _lib.MX_E_ARG
+    assert b(ctypes.byref(desc), ctypes.byref(sk), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE,
+             None) == _lib.MX_E_WORKSPACE
+    # workspace: the query side as for self-attention; the dS store has ceil(Lk / 32) block
+    # columns per query group row (rectangular: non-causal)
+    B, H, L, d, Lk = 2, 3, 100, 128, 300
+    nb, nbk = (L + 31) // 32, (Lk + 31) // 32
+    base = (_up(4) + _up(B * H * L * d) + _up(B * H * L * d // 32) + _up(B * H * nb * d * 32)
+            + _up(B * H * nb * d) + 2 * _up(B * H * L * 4))
+    assert lib.mx_attn_cross_workspace_size(ctypes.byref(desc), ctypes.byref(sk), 1) == base
+    assert lib.mx_attn_cross_workspace_size(ctypes.byref(desc), ctypes.byref(sk), 2) == (
+        base + _up(B * H * nb * nbk * 1024) + _up(B * H * nb * ((nbk + 3) // 4 * 4)))
+    # with the queries' own geometry it is the self-attention size
+    assert (lib.mx_attn_cross_workspace_size(ctypes.byref(desc), ctypes.byref(_seq(batch=2, seqlen=100)), 2)
+            == lib.mx_attn_workspace_size(ctypes.byref(desc), 2))

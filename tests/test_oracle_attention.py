@@ -289,3 +289,88 @@ def test_backward_dq_blocks_equal_full_rows():
         for key in ("dQ", "B_dQ", "eta_dQ"):
             assert np.array_equal(part[key][rows], full[key][rows]), key
         assert np.all(np.isnan(part["dK"]))
+
+
+# ---- cross-attention shapes (queries and keys of different lengths, non-causal) ----
+
+@pytest.mark.parametrize("nq,nk", [(7, 11), (11, 5), (1, 9)])
+def test_cross_reference_matches_brute_force(nq, nk):
+    rng = np.random.default_rng(21)
+    d = 6
+    q = rng.standard_normal((nq, d))
+    k, v = rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    ref = head_reference(q, k, v, np.zeros((nq, d)), False)
+    O, lse = brute_forward(q, k, v, False, d ** -0.5)
+    assert ref["O"].shape == (nq, d)
+    assert np.allclose(ref["O"], O, rtol=0, atol=1e-13)
+    assert np.allclose(ref["lse"], lse, rtol=0, atol=1e-13)
+
+
+def test_cross_reference_gradients_match_finite_differences():
+    rng = np.random.default_rng(22)
+    nq, nk, d = 5, 8, 4
+    q, g = rng.standard_normal((nq, d)), rng.standard_normal((nq, d))
+    k, v = rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    ref = head_reference(q, k, v, g, False)
+    h = 1e-6
+
+    def loss(qq, kk, vv):
+        return float(np.sum(g * head_reference(qq, kk, vv, g, False)["O"]))
+
+    for name, grad, x in (("q", ref["dQ"], q), ("k", ref["dK"], k), ("v", ref["dV"], v)):
+        num = np.zeros(x.shape)
+        for i in range(x.shape[0]):
+            for c in range(d):
+                args = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+                args[name][i, c] += h
+                up = loss(args["q"], args["k"], args["v"])
+                args[name][i, c] -= 2 * h
+                dn = loss(args["q"], args["k"], args["v"])
+                num[i, c] = (up - dn) / (2 * h)
+        assert np.allclose(grad, num, rtol=0, atol=2e-8), name
+
+
+def test_cross_quantisers_off_reduces_to_reference():
+    rng = np.random.default_rng(23)
+    nq, nk, d = 40, 70, 64
+    q, g = rng.standard_normal((nq, d)), rng.standard_normal((nq, d))
+    k, v = rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    ref = head_reference(q, k, v, g, False)
+    f = head_forward(q, k, v, False, quantized=False)
+    assert np.allclose(f["O"], ref["O"], rtol=0, atol=1e-12)
+    b = head_backward(q, k, v, f["O"], f["lse"], g, False, quantized=False)
+    for name in ("dQ", "dK", "dV"):
+        assert b[name].shape == ref[name].shape
+        assert np.allclose(b[name], ref[name], rtol=0, atol=1e-11), name
+
+
+def test_cross_query_rows_are_independent_of_the_query_count():
+    # Q is quantised per token (groups along d) and V along the keys, so one query row's output
+    # does not depend on how many other queries there are; P groups run over the row's keys
+    # (here 45 = one full group and a partial one).
+    rng = np.random.default_rng(24)
+    nq, nk, d = 37, 45, 64
+    q = rng.standard_normal((nq, d))
+    k, v = rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    full = head_forward(q, k, v, False)
+    for i in (0, 17, nq - 1):
+        one = head_forward(q[i:i + 1], k, v, False)
+        assert np.array_equal(one["O"][0], full["O"][i])
+        assert one["lse"][0] == full["lse"][i]
+
+
+def test_cross_document_without_keys_or_queries():
+    # FLAMIA notes section 6: a query row that sees no key gets O = 0 and LSE = +inf; so dQ = 0.
+    # A document without queries contributes nothing to dK and dV.
+    rng = np.random.default_rng(25)
+    d = 64
+    q, g = rng.standard_normal((5, d)), rng.standard_normal((5, d))
+    empty = np.zeros((0, d))
+    f = head_forward(q, empty, empty, False)
+    assert np.all(f["O"] == 0) and np.all(np.isinf(f["lse"]))
+    b = head_backward(q, empty, empty, f["O_out"], f["lse"], g, False)
+    assert np.all(b["dQ"] == 0) and b["dK"].shape == (0, d)
+    k, v = rng.standard_normal((17, d)), rng.standard_normal((17, d))
+    f = head_forward(empty, k, v, False)
+    b = head_backward(empty, k, v, f["O_out"], f["lse"], empty, False)
+    assert np.all(b["dK"] == 0) and np.all(b["dV"] == 0)
