@@ -12,6 +12,8 @@ the library records immediately around each launch of the named kernel, on its s
 
     python bench.py [--steps K] [--warmup W] [--dq f32|f16] [--no-cpu-baseline]
     python bench.py --pmc-run      # one untimed step + a 1 GiB device copy, for counter runs
+    python bench.py --workload x1  # cross-attention: 768 documents x 512 queries against
+                                   # jagged keys/values (<= 14980), H3 d128, non-causal
 
 `roofline.traffic` is the dK/dV kernel's HBM bytes per launch from rocprofv3 counters
 (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for the 1 GiB copy of --pmc-run),
@@ -67,6 +69,8 @@ def parse():
     ap.add_argument("--pmc-run", action="store_true", help="one untimed step + a 1 GiB copy (counter collection)")
     ap.add_argument("--recompute-dq", action="store_true",
                     help="minimal workspace: the dQ pass rebuilds dS instead of reading the stored codes")
+    ap.add_argument("--workload", choices=["c3", "x1"], default="c3",
+                    help="c3: the headline causal self-attention step; x1: the jagged cross-attention step")
     return ap.parse_args()
 
 
@@ -76,6 +80,9 @@ def main():
         print("bench.py: this build measures one GPU; multi-GPU runs are not part of it (use --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "x1":
+        run_cross(args)
+        return
     import numpy as np
     import torch
 
@@ -238,6 +245,107 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(t)
+    print(json.dumps(line), flush=True)
+
+
+def run_cross(args):
+    """x1: one step = mx_quantize of Q (per query document) and K, V (per key document) + the
+    cross-attention forward and backward. FLOPs: 4 d (forward) and 10 d (backward) per
+    (query, key) pair of every document and head."""
+    import numpy as np
+    import torch
+
+    import synth
+    from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F32, PROFILE_BWD_DKDV, PROFILE_BWD_DQ,
+                                        PROFILE_BWD_PREP, PROFILE_FWD, PROFILE_QUANTIZE, load, mx_attn_cross_bwd,
+                                        mx_attn_cross_fwd, mx_profile_kernel, mx_quantize)
+    from block_scaled_mxfp8_amd.flops import attn_flops
+
+    load()
+    cfg = synth.CONFIGS["x1"]
+    H, d = cfg["heads"], cfg["head_dim"]
+    dq_mode = MX_DQ_F32 if args.dq == "f32" else MX_DQ_F16_BOOST
+    print("[bench] generating x1 inputs on the device", file=sys.stderr, flush=True)
+    x = synth.make_cross_inputs_device()
+    nq, nk = np.diff(x["cu_q"]), np.diff(x["cu_k"])
+    cq, ck = torch.from_numpy(x["cu_q"]).cuda(), torch.from_numpy(x["cu_k"]).cuda()
+    mq, mk = int(nq.max()), int(nk.max())
+    pairs = H * int(np.sum(nq * nk))
+    f_fwd, f_bwd = attn_flops(pairs, d), attn_flops(pairs, d, backward=True)
+    ws = {}
+
+    def quant():
+        return (mx_quantize(x["q"], cu_seqlens=cq, max_seqlen=mq), mx_quantize(x["k"], cu_seqlens=ck, max_seqlen=mk),
+                mx_quantize(x["v"], cu_seqlens=ck, max_seqlen=mk))
+
+    def step(mode=dq_mode):
+        (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
+        o, lse = mx_attn_cross_fwd(q_row, k_row, v_seq, cq, ck, mq, mk)
+        dq, dk, dv, w = mx_attn_cross_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, x["g"], cq, ck, mq, mk,
+                                          dq_mode=mode, workspace=ws.get(mode))
+        ws[mode] = w
+        return o, dq
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    print(f"[bench] timed {steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    def kernel_ms(kind, fn, n=3):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record()
+            b.record()
+        mx_profile_kernel(kind, ev)
+        torch.cuda.synchronize()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        mx_profile_kernel(0, [])
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
+    o, lse = mx_attn_cross_fwd(q_row, k_row, v_seq, cq, ck, mq, mk)
+    fwd = lambda: mx_attn_cross_fwd(q_row, k_row, v_seq, cq, ck, mq, mk)  # noqa: E731
+    bwd = lambda: mx_attn_cross_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, x["g"], cq, ck, mq, mk,  # noqa: E731
+                                    dq_mode=dq_mode, workspace=ws[dq_mode])
+    ms = {"attn_fwd": kernel_ms(PROFILE_FWD, fwd), "attn_bwd_dkdv": kernel_ms(PROFILE_BWD_DKDV, bwd),
+          "attn_bwd_dq": kernel_ms(PROFILE_BWD_DQ, bwd), "bwd_prep": kernel_ms(PROFILE_BWD_PREP, bwd),
+          "quantize_kv": kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize(x["k"], cu_seqlens=ck, max_seqlen=mk))}
+    tflops = lambda f, t: f / (t * 1e-3) / 1e12  # noqa: E731
+    f_dkdv = f_bwd * 4 // 5
+    line = {
+        "metric": "MXFP8 cross-attn fwd/bwd TFLOP/s, 768 docs x 512 queries vs jagged KV (<= 14980), H3 d128",
+        "value": round(tflops(f_fwd + f_bwd, ms_step), 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8",
+        "data": "synthetic",
+        "config": {"workload": "x1: cross-attention, 768 documents x 512 queries, key/value lengths U[1, 14980] "
+                               f"(total {int(nk.sum())}, max {mk}), H3 d128, non-causal, bf16 N(0,1); step = "
+                               "quantise Q/K/V + fwd + bwd", "dq": args.dq},
+        "pct_of_peak": round(100 * tflops(f_fwd + f_bwd, ms_step) / PEAK_MXFP8_TFLOPS, 2),
+        "fwd_tflops": round(tflops(f_fwd, ms["attn_fwd"]), 2),
+        "kernels_ms": {k: round(v, 4) for k, v in ms.items()},
+        "flops": {"fwd": f_fwd, "bwd": f_bwd, "pairs": pairs},
+        "roofline": {"kernel": "attn_bwd_dkdv_kernel<128> (backward dK/dV)", "bound": "mfma",
+                     "achieved": round(tflops(f_dkdv, ms["attn_bwd_dkdv"]), 2), "peak": PEAK_MXFP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops(f_dkdv, ms["attn_bwd_dkdv"]) / PEAK_MXFP8_TFLOPS, 4),
+                     "traffic": None},
+    }
     print(json.dumps(line), flush=True)
 
 

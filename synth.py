@@ -14,6 +14,12 @@ Workloads (sizes and value distributions):
       causal per document, bf16 N(0,1)
   c5  non-causal, B1 H16 L16384 d128, bf16 N(0,1) * u, u ~ U(0.5, 4) per (tensor, batch,
       token) shared across heads and channels; GQA variant with 4 KV heads
+  x1  cross-attention, the production shape of the Meta write-up: 768 documents of 512
+      queries each against key/value documents of lengths drawn uniformly from [1, 14980]
+      (the pages give the count, the total 5,856,019 and the maximum 14,980; a uniform draw's
+      mean, 7490, is within 2 % of the stated mean 7625), H3 (model width 384) d128,
+      non-causal, bf16 N(0,1). At this size the values come from torch's generator on the
+      device (seeded per tensor); the lengths from numpy as above.
 """
 import numpy as np
 
@@ -31,7 +37,9 @@ CONFIGS = {
     "c5gqa": dict(batch=1, heads=16, heads_kv=4, seqlen=16384, head_dim=128, causal=False, dtype="bf16",
                   backward=True, magnitude=(0.5, 4.0)),
 }
-SEED_BASE = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "c5gqa": 1005}
+CONFIGS["x1"] = dict(n_docs=768, queries=512, max_keys=14980, heads=3, heads_kv=3, head_dim=128, causal=False,
+                     dtype="bf16", backward=True)
+SEED_BASE = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "c5gqa": 1005, "x1": 1101}
 
 
 def rng(seed, tensor):
@@ -95,4 +103,34 @@ def make_inputs(cfg_name, seed=None, batch=None, heads=None, seqlen=None, tensor
             for hh in range(h):
                 x[:, hh, :, outl[t][hh]] *= cfg["outlier_scale"]
         out[t] = x
+    return out
+
+
+def cross_lengths(seed=None, n_docs=None):
+    """(query lengths, key lengths) of the x1 cross-attention workload (numpy int64)."""
+    cfg = CONFIGS["x1"]
+    seed = SEED_BASE["x1"] if seed is None else seed
+    n = cfg["n_docs"] if n_docs is None else n_docs
+    nk = rng(seed, "lengths").integers(1, cfg["max_keys"] + 1, size=n)
+    return np.full(n, cfg["queries"], dtype=np.int64), nk.astype(np.int64)
+
+
+def make_cross_inputs_device(seed=None, n_docs=None, dtype=None, device="cuda"):
+    """x1 inputs drawn on the device: dict(q, g [Tq,H,d], k, v [Tk,Hkv,d] in `dtype` (default
+    bf16), cu_q, cu_k (numpy int32)). torch's generator on `device`, seeded with
+    (base seed * 16 + tensor id) per tensor."""
+    import torch
+    cfg = CONFIGS["x1"]
+    seed = SEED_BASE["x1"] if seed is None else seed
+    nq, nk = cross_lengths(seed, n_docs)
+    cu_q, cu_k = cu_seqlens_of(nq), cu_seqlens_of(nk)
+    out = {"cu_q": cu_q, "cu_k": cu_k}
+    for t in ("q", "k", "v", "g"):
+        rows = int(cu_k[-1]) if t in ("k", "v") else int(cu_q[-1])
+        h = cfg["heads_kv"] if t in ("k", "v") else cfg["heads"]
+        gen = torch.Generator(device=device)
+        gen.manual_seed(int(seed) * 16 + TENSOR_ID[t])
+        x = torch.randn((rows, h, cfg["head_dim"]), generator=gen, device=device, dtype=torch.float32)
+        out[t] = x.to(dtype or torch.bfloat16)
+        del x
     return out

@@ -125,3 +125,51 @@ def test_packed_cross_attention_matches_oracle(H, Hkv, d):
     x = {"q": rng.standard_normal((Tq, H, d)), "g": rng.standard_normal((Tq, H, d)),
          "k": rng.standard_normal((Tk, Hkv, d)), "v": rng.standard_normal((Tk, Hkv, d))}
     _check_cross({n: a.astype(np.float32) for n, a in x.items()}, cu_q, cu_k, H, Hkv, d)
+
+
+def test_x1_production_shape_sampled_documents():
+    # The x1 workload at full size, in the benchmark's launch configuration (768 documents x 512
+    # queries vs jagged keys, H3 d128): the oracle checks head 0 of two documents, forward, then
+    # their backward given the oracle's own saved O and LSE for those documents.
+    import synth
+    print("[x1 full] inputs + quantise + forward", flush=True)
+    x = synth.make_cross_inputs_device()
+    cu_q, cu_k = x["cu_q"], x["cu_k"]
+    nk = np.diff(cu_k)
+    cq, ck = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    mq, mk = int(np.diff(cu_q).max()), int(nk.max())
+    q_row, q_seq, k_row, k_seq, v_row, v_seq = _views(x, cq, ck, mq, mk)
+    o, lse = mx_attn_cross_fwd(q_row, k_row, v_seq, cq, ck, mq, mk)
+    torch.cuda.synchronize()
+    # two documents with modest key counts (the oracle's cost grows with 512 x n_k)
+    docs = [int(np.argmin(np.abs(nk - 700))), int(np.argmin(np.abs(nk - 2100)))]
+    h = 0
+    sl = {j: (slice(int(cu_q[j]), int(cu_q[j + 1])), slice(int(cu_k[j]), int(cu_k[j + 1]))) for j in docs}
+    ref = {}
+    o2, lse2 = o.clone(), lse.clone()
+    for j in docs:
+        qs, ks = sl[j]
+        q, g = as_f64(x["q"][qs, h]), as_f64(x["g"][qs, h])
+        k, v = as_f64(x["k"][ks, h]), as_f64(x["v"][ks, h])
+        print(f"  oracle forward doc {j} (n_k {nk[j]})", flush=True)
+        f = oracle.head_forward(q, k, v, False, bounds=True)
+        od, ld = as_f64(o[qs, h]), as_f64(lse[qs, h])
+        ok, worst, plain, _ = gate(od, f["O"], f["B"] + f["eta"] + oracle.ulp_of(od, "bf16") / 2, REL)
+        print(f"  O doc {j}: plain max|d|/rms {plain:.3e} worst excess {worst:.3e}", flush=True)
+        assert ok
+        assert np.all(np.abs(ld - f["lse"]) <= 2e-5 + 4 * f["drel_max"] + 1e-6 * np.abs(f["lse"]))
+        o2[qs, h] = torch.from_numpy(f["O_out"]).to(torch.bfloat16).cuda()
+        lse2[qs, h] = torch.from_numpy(f["lse"].astype(np.float32)).cuda()
+        ref[j] = (q, k, v, g, f)
+    print("[x1 full] backward", flush=True)
+    dq, dk, dv, ws = mx_attn_cross_bwd(q_row, q_seq, k_row, k_seq, v_row, o2, lse2, x["g"], cq, ck, mq, mk)
+    torch.cuda.synchronize()
+    for j in docs:
+        qs, ks = sl[j]
+        q, k, v, g, f = ref[j]
+        r = oracle.head_backward(q, k, v, f["O_out"], f["lse"], g, False, bounds=True)
+        for n, dev in (("dQ", dq[qs, h]), ("dK", dk[ks, h]), ("dV", dv[ks, h])):
+            xd = as_f64(dev)
+            ok, worst, plain, _ = gate(xd, r[n], r["B_" + n] + r["eta_" + n] + oracle.ulp_of(xd, "bf16") / 2, REL)
+            print(f"  {n} doc {j}: plain max|d|/rms {plain:.3e} worst excess {worst:.3e}", flush=True)
+            assert ok, n
