@@ -52,6 +52,7 @@ constexpr int kBlockQ = 32 * kWaves;   // queries per dQ workgroup
 constexpr int kStepK = 64;             // keys per dQ step
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kBoost = 512.f;        // 2^9 (FP16 dQ partial sums)
+constexpr int kDkvChunk = 2;           // (sequence, head) pairs per longest-first chunk (mx_layout.h lpt_order)
 
 __device__ __forceinline__ float max_abs16(const float* x) {
   float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fabsf(x[2]));
@@ -161,7 +162,7 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
   if (!kPacked) {
     const int nkb = (p.geom_k.seqlen + kBlockK - 1) / kBlockK;
     int bh, rank;
-    lpt_order(blockIdx.x, p.heads_kv * g.batch, nkb, bh, rank);
+    lpt_order<kDkvChunk>(blockIdx.x, p.heads_kv * g.batch, nkb, bh, rank);
     w.kb = rank;                          // causal: the first key block sees the most queries
     w.s = bh / p.heads_kv;
     w.hkv = bh % p.heads_kv;
@@ -661,7 +662,7 @@ __device__ __forceinline__ QWork decode_q(const BwdParams& p) {
   if (!packed(g)) {
     const int nqb = (g.seqlen + kBlockQ - 1) / kBlockQ;
     int bh, rank;
-    lpt_order(blockIdx.x, p.heads_q * g.batch, nqb, bh, rank);
+    lpt_order<4>(blockIdx.x, p.heads_q * g.batch, nqb, bh, rank);
     const int qb = p.causal ? nqb - 1 - rank : rank;   // causal: the last query block sees the most keys
     w.s = bh / p.heads_q;
     w.h = bh % p.heads_q;

@@ -88,7 +88,7 @@ __device__ __forceinline__ Work decode_work(const AttnParams& p) {
   if (!kPacked) {
     const int nqt = (g.seqlen + kBlockM - 1) / kBlockM;
     int bh, rank;
-    lpt_order(blockIdx.x, p.heads_q * g.batch, nqt, bh, rank);
+    lpt_order<4>(blockIdx.x, p.heads_q * g.batch, nqt, bh, rank);
     w.s = bh / p.heads_q;
     w.h = bh % p.heads_q;
     w.qt = p.causal ? nqt - 1 - rank : rank;  // causal: the last query tile sees the most keys

@@ -68,12 +68,12 @@ __host__ __device__ inline long long token_index_k(const Geom& g, int heads, int
 // workgroup per (pair, tile); rank 0 is the most expensive tile of a pair. Workgroups go
 // round-robin to the 8 XCDs (each with its own L2), so XCD x receives workgroups x, x + 8, ...
 // and dispatches them in that order as slots free up. Each XCD gets a contiguous range of
-// pairs (when nbh is a multiple of 8); inside it, chunks of 4 pairs are dispatched with the
-// ranks in increasing order and the pairs inner. So the costliest tiles of the last pairs do
-// not start last (a pair-by-pair order leaves them running alone at the end of the launch),
-// and the pairs in flight, whose K and V share the L2, stay few.
+// pairs (when nbh is a multiple of 8); inside it, chunks of kChunk pairs are dispatched with
+// the ranks in increasing order and the pairs inner. So the costliest tiles of the last pairs
+// do not start last (a pair-by-pair order leaves them running alone at the end of the launch),
+// and the pairs in flight, whose operands share the L2, stay few.
+template <int kChunk>
 __device__ inline void lpt_order(long long bid, int nbh, int nt, int& pair, int& rank) {
-  constexpr int kChunk = 4;
   long long j = bid;
   int p0 = 0, np = nbh;
   if ((nbh & 7) == 0) {
