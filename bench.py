@@ -14,8 +14,9 @@ the library records immediately around each launch of the named kernel, on its s
     python bench.py --pmc-run      # one untimed step + a 1 GiB device copy, for counter runs
     python bench.py --workload x1  # cross-attention: 768 documents x 512 queries against
                                    # jagged keys/values (<= 14980), H3 d128, non-causal
+    python bench.py --workload n1  # fused RMSNorm + quantise producer, x [262144, 512] bf16
 
-`roofline.traffic` is the dK/dV kernel's HBM bytes per launch from rocprofv3 counters
+`roofline.traffic` is the roofline kernel's HBM bytes per launch from rocprofv3 counters
 (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for the 1 GiB copy of --pmc-run),
 stored in profiles/ with the hash of the kernel sources it was measured on; it is reported
 only while those sources are unchanged, else null.
@@ -35,22 +36,30 @@ KERNEL_SOURCES = ["block_scaled_mxfp8_amd/csrc/attn_bwd.hip", "block_scaled_mxfp
                   "block_scaled_mxfp8_amd/build.py"]
 
 
-def kernel_sources_sha256():
+# the fused RMSNorm + quantise kernel (n1 workload)
+NORM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_rmsnorm_quantize_n1.json")
+NORM_KERNEL_SOURCES = ["block_scaled_mxfp8_amd/csrc/rmsnorm_quantize.hip", "block_scaled_mxfp8_amd/csrc/mx_device.h",
+                       "block_scaled_mxfp8_amd/csrc/mx_layout.h", "block_scaled_mxfp8_amd/csrc/mx_norm.h",
+                       "block_scaled_mxfp8_amd/build.py"]
+
+
+def kernel_sources_sha256(sources=None):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """Bytes per dK/dV launch from the counter record, or None if absent or stale."""
+def recorded_traffic(path=None, sources=None):
+    """Bytes per launch of the recorded kernel (default: dK/dV) from its counter record, or
+    None if absent or stale."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE if path is None else path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("sources_sha256") != kernel_sources_sha256():
+    if rec.get("sources_sha256") != kernel_sources_sha256(sources):
         return None
     return int(rec["fetch_kib"] * rec["fetch_scale"] * 1024 + rec["write_kib"] * rec["write_scale"] * 1024)
 
@@ -69,8 +78,9 @@ def parse():
     ap.add_argument("--pmc-run", action="store_true", help="one untimed step + a 1 GiB copy (counter collection)")
     ap.add_argument("--recompute-dq", action="store_true",
                     help="minimal workspace: the dQ pass rebuilds dS instead of reading the stored codes")
-    ap.add_argument("--workload", choices=["c3", "x1"], default="c3",
-                    help="c3: the headline causal self-attention step; x1: the jagged cross-attention step")
+    ap.add_argument("--workload", choices=["c3", "x1", "n1"], default="c3",
+                    help="c3: the headline causal self-attention step; x1: the jagged cross-attention step; "
+                         "n1: the fused RMSNorm + quantise producer")
     return ap.parse_args()
 
 
@@ -82,6 +92,9 @@ def main():
         sys.exit(2)
     if args.workload == "x1":
         run_cross(args)
+        return
+    if args.workload == "n1":
+        run_norm(args)
         return
     import numpy as np
     import torch
@@ -347,6 +360,108 @@ def run_cross(args):
                      "traffic": None},
     }
     print(json.dumps(line), flush=True)
+
+
+def run_norm(args):
+    """n1: one step = mx_rmsnorm_quantize of x [262144, 512] bf16 into both MX views.
+    Algorithmic bytes: x read once (2 B/elem), gamma (2 B/column), both views written
+    (2 x (1 + 1/32) B/elem)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from block_scaled_mxfp8_amd import PROFILE_RMSNORM, load, mx_profile_kernel, mx_rmsnorm_quantize
+
+    load()
+    cfg = synth.CONFIGS["n1"]
+    rows, n = cfg["rows"], cfg["n"]
+    eps = 1e-6
+    print("[bench] generating n1 inputs on the device", file=sys.stderr, flush=True)
+    x, gamma = synth.make_norm_inputs_device()
+    nbytes = rows * n * 2 + n * 2 + 2 * (rows * n + rows * n // 32)
+    step = lambda: mx_rmsnorm_quantize(x, gamma, eps)  # noqa: E731
+    if args.pmc_run:
+        step()
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        buf2 = torch.empty_like(buf)
+        buf2.copy_(buf)
+        torch.cuda.synchronize()
+        print("[bench] pmc run done", file=sys.stderr, flush=True)
+        return
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    print(f"[bench] timed {steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    # the kernel alone, from HIP events the library records around it on its launch stream
+    nev = max(1, args.profile_steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    mx_profile_kernel(PROFILE_RMSNORM, ev)
+    torch.cuda.synchronize()
+    for _ in range(nev):
+        step()
+    torch.cuda.synchronize()
+    mx_profile_kernel(0, [])
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gbs = lambda t: nbytes / (t * 1e-3) / 1e9  # noqa: E731
+    line = {
+        "metric": "fused RMSNorm + MXFP8 quantise (both scale layouts) effective throughput at N=512",
+        "value": round(gbs(ms_step) / 1e3, 3),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->mxfp8",
+        "data": "synthetic",
+        "config": {"workload": f"n1: x [{rows}, {n}] bf16 (N(0,1) x per-row 2^U(-3,3), 4 outlier channels x20), "
+                               "gamma 1 + 0.25 N(0,1), eps 1e-6; step = RMSNorm + ROW and SEQ MX views",
+                   "rows": rows, "n": n},
+        "bytes_per_step": nbytes,
+        "kernel_ms": round(k_ms, 5),
+        "pages_context": {"fused_rmsnorm_quantize_tbs_blackwell_n512": [2.6, 4.0],
+                          "unfused_tbs_blackwell_n512": [0.75, 0.87]},
+        "roofline": {"kernel": "rmsnorm_quantize_kernel<bf16, n <= 512>", "bound": "hbm",
+                     "achieved": round(gbs(k_ms), 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs(k_ms) / PEAK_HBM_GBS, 4),
+                     "traffic": recorded_traffic(NORM_TRAFFIC_FILE, NORM_KERNEL_SOURCES)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_norm(x, gamma, eps)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_norm(x, gamma, eps, rows=32768):
+    """The float64 oracle (as it stands) on the first `rows` rows of the n1 input."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - only used to report the thread count
+        cores = os.cpu_count()
+    xs = x[:rows].float().cpu().numpy().astype(np.float64)
+    g = gamma.float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.rmsnorm_quantize(xs, g, float(np.float32(eps)))
+    sec = time.perf_counter() - t0
+    n = xs.shape[1]
+    nbytes = rows * n * 2 + n * 2 + 2 * (rows * n + rows * n // 32)
+    return {"value": round(nbytes / sec / 1e12, 6), "unit": "TB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {rows} of {x.shape[0]} rows (n {n}), float64 numpy, {sec:.1f} s"}
 
 
 def cpu_baseline(t):

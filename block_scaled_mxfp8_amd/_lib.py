@@ -66,6 +66,9 @@ def load():
     lib.mx_quantize.argtypes = [ctypes.POINTER(_Seq), I32, I32, P, I32, I32, ctypes.POINTER(_QView),
                                 ctypes.POINTER(_QView), P]
     lib.mx_quantize.restype = I32
+    lib.mx_rmsnorm_quantize.argtypes = [P, P, I32, I64, I32, ctypes.c_float, I32, ctypes.POINTER(_QView),
+                                        ctypes.POINTER(_QView), P]
+    lib.mx_rmsnorm_quantize.restype = I32
     for name in ("mx_attn_fwd", "mx_attn_varlen_fwd"):
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, P, P, P]
@@ -222,6 +225,33 @@ def mx_quantize(x, views=MX_VIEW_ROW | MX_VIEW_SEQ, cu_seqlens=None, max_seqlen=
     st = lib.mx_quantize(ctypes.byref(seq), heads, d, x.data_ptr(), _dtype_code(x.dtype), views, ctypes.byref(rv),
                          ctypes.byref(sv), _stream())
     _check(st, "mx_quantize")
+    return row, seqv
+
+
+def mx_rmsnorm_quantize(x, gamma, eps=1e-6, views=MX_VIEW_ROW | MX_VIEW_SEQ):
+    """RMSNorm of x [rows, n] (fp32/bf16) with weight gamma [n] (same dtype), written only as MX
+    views of the result -> (row QView: codes [rows, n], scales [rows, n/32]; seq QView: codes
+    [ceil(rows/32), n, 32], scales [ceil(rows/32), n]); a view not asked for is None."""
+    lib = load()
+    if not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
+        raise ValueError("x must be a contiguous 2-D device tensor [rows, n]")
+    rows, n = x.shape
+    if not gamma.is_cuda or not gamma.is_contiguous() or tuple(gamma.shape) != (n,) or gamma.dtype != x.dtype:
+        raise ValueError("gamma must be a contiguous device tensor [n] of x's dtype")
+    row = seqv = None
+    rv, sv = _QView(), _QView()
+    if views & MX_VIEW_ROW:
+        row = QView(torch.empty((rows, n), dtype=torch.uint8, device=x.device),
+                    torch.empty((rows, max(n // 32, 1)), dtype=torch.uint8, device=x.device))
+        rv = _qv(row)
+    if views & MX_VIEW_SEQ:
+        g = -(-rows // 32)
+        seqv = QView(torch.empty((g, n, 32), dtype=torch.uint8, device=x.device),
+                     torch.empty((g, n), dtype=torch.uint8, device=x.device))
+        sv = _qv(seqv)
+    st = lib.mx_rmsnorm_quantize(x.data_ptr(), gamma.data_ptr(), _dtype_code(x.dtype), rows, n, float(eps), views,
+                                 ctypes.byref(rv), ctypes.byref(sv), _stream())
+    _check(st, "mx_rmsnorm_quantize")
     return row, seqv
 
 
@@ -403,7 +433,7 @@ def mx_abi_version():
     return load().mx_abi_version()
 
 
-PROFILE_FWD, PROFILE_BWD_DKDV, PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_DQ = 1, 2, 3, 4, 5
+PROFILE_FWD, PROFILE_BWD_DKDV, PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_DQ, PROFILE_RMSNORM = 1, 2, 3, 4, 5, 6
 _PROFILE_KEEP = []
 
 

@@ -7,7 +7,9 @@
 
 namespace mx {
 
-enum ProfileKind { kProfNone = 0, kProfFwd = 1, kProfBwdKV = 2, kProfQuantize = 3, kProfBwdPrep = 4, kProfBwdQ = 5 };
+enum ProfileKind {
+  kProfNone = 0, kProfFwd = 1, kProfBwdKV = 2, kProfQuantize = 3, kProfBwdPrep = 4, kProfBwdQ = 5, kProfRmsNorm = 6
+};
 
 struct ProfileHook {
   int kind = kProfNone;

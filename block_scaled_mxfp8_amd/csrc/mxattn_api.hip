@@ -5,6 +5,7 @@
 
 #include "../../include/mxattn.h"
 #include "mx_internal.h"
+#include "mx_norm.h"
 #include "mx_layout.h"
 #include "mx_profile.h"
 
@@ -236,6 +237,38 @@ mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const 
   return err == hipSuccess ? MX_OK : MX_E_DEVICE;
 }
 
+mx_status mx_rmsnorm_quantize(const void* x, const void* gamma, mx_dtype dtype, int64_t rows, int32_t n, float eps,
+                              int32_t views, mx_qview* row_out, mx_qview* seq_out, void* stream) {
+  if (rows < 0 || n < 32 || n % 32 != 0) return MX_E_ARG;
+  if (dtype != MX_F32 && dtype != MX_BF16) return MX_E_ARG;
+  if (views < 1 || views > 3) return MX_E_ARG;
+  if (!(eps >= 0.f) || !(eps <= 3.4e38f)) return MX_E_ARG;   // NaN fails both
+  if (n > 65536 || rows > (int64_t)0x7FFFFFFF * 32) return MX_E_UNSUPPORTED;
+  if (rows == 0) return MX_OK;          // nothing is read or written: every pointer may be NULL
+  if (!x || !gamma || !aligned(x, 16) || !aligned(gamma, 16)) return MX_E_ARG;
+  mx::RmsNormParams p = {};
+  p.x = x;
+  p.gamma = gamma;
+  p.f32 = dtype == MX_F32;
+  p.rows = rows;
+  p.n = n;
+  p.eps = eps;
+  if (views & MX_VIEW_ROW) {
+    if (!row_out || check_view(*row_out) != MX_OK) return MX_E_ARG;
+    p.row_codes = row_out->codes;
+    p.row_scales = row_out->scales;
+  }
+  if (views & MX_VIEW_SEQ) {
+    if (!seq_out || check_view(*seq_out) != MX_OK) return MX_E_ARG;
+    p.seq_codes = seq_out->codes;
+    p.seq_scales = seq_out->scales;
+  }
+  const int slot = mx::profile_begin(mx::kProfRmsNorm, (hipStream_t)stream);
+  const hipError_t err = mx::launch_rmsnorm_quantize(p, (hipStream_t)stream);
+  mx::profile_end(slot, (hipStream_t)stream);
+  return err == hipSuccess ? MX_OK : MX_E_DEVICE;
+}
+
 mx_status mx_attn_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o, float* lse,
                       void* stream) {
   return fwd_impl(desc, nullptr, q_row, k_row, v_seq, o, lse, stream, false);
@@ -308,7 +341,7 @@ mx_status mx_profile_kernel(int32_t kernel, void* const* start_events, void* con
     h = mx::ProfileHook();
     return MX_OK;
   }
-  if (kernel < 1 || kernel > 5 || !start_events || !stop_events) return MX_E_ARG;
+  if (kernel < 1 || kernel > 6 || !start_events || !stop_events) return MX_E_ARG;
   h.kind = kernel;
   h.start = (hipEvent_t*)start_events;
   h.stop = (hipEvent_t*)stop_events;

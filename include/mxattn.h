@@ -117,6 +117,26 @@ typedef struct {
 mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x, mx_dtype dtype,
                       int32_t views, mx_qview* row_out, mx_qview* seq_out, void* stream);
 
+/* Fused RMSNorm + quantise, the normalisation producer of Meta's MXFP8 write-up (section
+ * "Quantisation inside the producers": the kernel that reads the activations writes them as
+ * FP8 in both scale layouts, so no consumer quantises again). For each row m of x
+ * [rows, n] (contiguous, dtype MX_F32 or MX_BF16; gamma: n values of the same dtype):
+ *   y[m, c] = (x[m, c] * gamma[c]) * r_m,  r_m = 1 / sqrt(sum_c x[m, c]^2 / n + eps),
+ * in FP32 (FMA sums of squares), written only as MX views of y with the group rule of
+ * mx_quantize:
+ *   ROW view (groups of 32 columns of a row): codes [rows, n], scales [rows, n/32];
+ *   SEQ view (groups of 32 rows of a column): codes [ceil(rows/32), n, 32] with row offset t
+ *            of group g at byte MX_SEQ_POS(t), scales [ceil(rows/32), n]; the rows past the
+ *            end of a partial last group count as zeros and hold code 0.
+ * i.e. the views mx_quantize gives for an [1, 1, rows, n] tensor. views = MX_VIEW_ROW |
+ * MX_VIEW_SEQ; the unused output may be NULL. n: a multiple of 32, 32..65536 (larger:
+ * MX_E_UNSUPPORTED); rows >= 0 (0 launches nothing and reads no pointer); eps finite, >= 0;
+ * x and gamma 16-byte aligned. FP32 limits of the plain formula: a row whose sum of squares
+ * overflows FP32 gets r = 0 (y = +-0, or NaN where x is infinite); an all-zero row with
+ * eps = 0 gets y = NaN; groups holding NaN take scale 0xFF and codes 0x7F. */
+mx_status mx_rmsnorm_quantize(const void* x, const void* gamma, mx_dtype dtype, int64_t rows, int32_t n, float eps,
+                              int32_t views, mx_qview* row_out, mx_qview* seq_out, void* stream);
+
 /* Forward: O [layout above, out_dtype] and LSE float32 [B,H,L] / [T,H] (natural log,
  * +inf for a row without visible keys). q_row / k_row: ROW views of Q and K (heads_q and
  * heads_kv heads); v_seq: SEQ view of V. */
@@ -186,7 +206,8 @@ mx_status mx_read_flags(const void* workspace, uint32_t* flags);
  * (hipEvent_t passed as void*, created by the caller): every following launch of the selected
  * kernel records start[i % count] just before and stop[i % count] just after it, on the stream
  * it is launched on, i = launch index since registration. kernel: 1 forward attention kernel,
- * 2 backward dK/dV kernel, 3 mx_quantize, 4 backward G preprocessing, 5 backward dQ kernel; 0 (or
+ * 2 backward dK/dV kernel, 3 mx_quantize, 4 backward G preprocessing, 5 backward dQ kernel,
+ * 6 mx_rmsnorm_quantize; 0 (or
  * count <= 0) turns the hook off. The event arrays must stay valid while registered. One
  * hook per process; not thread-safe. */
 mx_status mx_profile_kernel(int32_t kernel, void* const* start_events, void* const* stop_events, int32_t count);

@@ -20,10 +20,15 @@ Workloads (sizes and value distributions):
       mean, 7490, is within 2 % of the stated mean 7625), H3 (model width 384) d128,
       non-causal, bf16 N(0,1). At this size the values come from torch's generator on the
       device (seeded per tensor); the lengths from numpy as above.
+  n1  fused RMSNorm + quantise producer: x [262144, 512] (64 sequences x 4096 tokens; the
+      pages quote N = 512), bf16 x[m, c] = z * 2^u_m * o_c with z ~ N(0,1), a per-row
+      magnitude u_m ~ U(-3, 3) and o_c = 20 on 4 fixed outlier channels (else 1);
+      gamma = 1 + 0.25 N(0,1). Small test cases draw the same recipe with numpy; the full
+      size draws it with torch's generator on the device.
 """
 import numpy as np
 
-TENSOR_ID = {"q": 1, "k": 2, "v": 3, "g": 4, "lengths": 5, "outliers": 6, "magnitude": 7}
+TENSOR_ID = {"q": 1, "k": 2, "v": 3, "g": 4, "lengths": 5, "outliers": 6, "magnitude": 7, "x": 8, "gamma": 9}
 
 CONFIGS = {
     "c1": dict(batch=1, heads=1, heads_kv=1, seqlen=256, head_dim=64, causal=True, dtype="f32", backward=False),
@@ -39,7 +44,8 @@ CONFIGS = {
 }
 CONFIGS["x1"] = dict(n_docs=768, queries=512, max_keys=14980, heads=3, heads_kv=3, head_dim=128, causal=False,
                      dtype="bf16", backward=True)
-SEED_BASE = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "c5gqa": 1005, "x1": 1101}
+CONFIGS["n1"] = dict(rows=262144, n=512, dtype="bf16", outlier_channels=(3, 100, 257, 511), outlier=20.0)
+SEED_BASE = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "c5gqa": 1005, "x1": 1101, "n1": 1201}
 
 
 def rng(seed, tensor):
@@ -134,3 +140,42 @@ def make_cross_inputs_device(seed=None, n_docs=None, dtype=None, device="cuda"):
         out[t] = x.to(dtype or torch.bfloat16)
         del x
     return out
+
+
+def _norm_channel_scale(n):
+    cfg = CONFIGS["n1"]
+    o = np.ones(n, dtype=np.float32)
+    for c in cfg["outlier_channels"]:
+        if c < n:
+            o[c] = cfg["outlier"]
+    return o
+
+
+def make_norm_inputs(rows, n, seed=None):
+    """n1 recipe at any size with numpy: (x [rows, n], gamma [n]) float32."""
+    seed = SEED_BASE["n1"] if seed is None else seed
+    z = normal(seed, "x", (rows, n))
+    u = rng(seed, "magnitude").uniform(-3.0, 3.0, size=(rows, 1)).astype(np.float32)
+    x = z * np.exp2(u) * _norm_channel_scale(n)[None, :]
+    gamma = (1.0 + 0.25 * normal(seed, "gamma", (n,))).astype(np.float32)
+    return x.astype(np.float32), gamma
+
+
+def make_norm_inputs_device(rows=None, n=None, seed=None, dtype=None, device="cuda"):
+    """n1 recipe drawn on the device: (x [rows, n], gamma [n]) in `dtype` (default bf16).
+    torch's generator on `device`, seeded with (base seed * 16 + tensor id)."""
+    import torch
+    cfg = CONFIGS["n1"]
+    seed = SEED_BASE["n1"] if seed is None else seed
+    rows = cfg["rows"] if rows is None else rows
+    n = cfg["n"] if n is None else n
+    dtype = dtype or torch.bfloat16
+    gens = {}
+    for t in ("x", "magnitude", "gamma"):
+        gens[t] = torch.Generator(device=device)
+        gens[t].manual_seed(int(seed) * 16 + TENSOR_ID[t])
+    o = torch.from_numpy(_norm_channel_scale(n)).to(device)
+    u = torch.rand((rows, 1), generator=gens["magnitude"], device=device) * 6.0 - 3.0
+    x = torch.randn((rows, n), generator=gens["x"], device=device) * torch.exp2(u) * o
+    gamma = 1.0 + 0.25 * torch.randn((n,), generator=gens["gamma"], device=device)
+    return x.to(dtype), gamma.to(dtype)

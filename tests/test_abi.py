@@ -27,7 +27,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("mx_quantize", "mx_attn_fwd", "mx_attn_bwd", "mx_attn_varlen_fwd", "mx_attn_varlen_bwd",
-                     "mx_attn_workspace_size", "mx_read_flags", "mx_strerror", "mx_abi_version"):
+                     "mx_attn_workspace_size", "mx_read_flags", "mx_strerror", "mx_abi_version",
+                     "mx_attn_cross_fwd", "mx_attn_cross_bwd", "mx_rmsnorm_quantize"):
         assert required in names
 
 
@@ -198,3 +199,36 @@ def test_cross_attention_validation_and_workspace(lib):
     # with the queries' own geometry it is the self-attention size
     assert (lib.mx_attn_cross_workspace_size(ctypes.byref(desc), ctypes.byref(_seq(batch=2, seqlen=100)), 2)
             == lib.mx_attn_workspace_size(ctypes.byref(desc), 2))
+
+
+def test_rmsnorm_quantize_validation(lib):
+    # every failure is caught on the host before a launch; rows = 0 launches nothing
+    f = lib.mx_rmsnorm_quantize
+    v = _lib._QView(FAKE, FAKE)
+    BF16, F32 = 1, 0
+    ok_args = (FAKE, FAKE, BF16, 64, 512, 1e-6, 3, ctypes.byref(v), ctypes.byref(v), None)
+
+    def call(**kw):
+        names = ("x", "gamma", "dtype", "rows", "n", "eps", "views", "row", "seq", "stream")
+        a = dict(zip(names, ok_args))
+        a.update(kw)
+        return f(*(a[k] for k in names))
+
+    assert call(x=None) == _lib.MX_E_ARG
+    assert call(gamma=None) == _lib.MX_E_ARG
+    assert call(dtype=7) == _lib.MX_E_ARG
+    assert call(rows=-1) == _lib.MX_E_ARG
+    for n in (0, 16, 48, 100):
+        assert call(n=n) == _lib.MX_E_ARG, n
+    assert call(n=1 << 17) == _lib.MX_E_UNSUPPORTED
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert call(eps=eps) == _lib.MX_E_ARG, eps
+    for views in (0, 4):
+        assert call(views=views) == _lib.MX_E_ARG, views
+    assert call(x=FAKE + 8) == _lib.MX_E_ARG            # misaligned
+    assert call(row=None) == _lib.MX_E_ARG               # ROW view asked for, none given
+    assert call(views=2, seq=ctypes.byref(_lib._QView(None, FAKE))) == _lib.MX_E_ARG
+    assert call(rows=0, row=None, seq=None) == _lib.MX_OK
+    assert call(rows=0, x=None, gamma=None, row=None, seq=None) == _lib.MX_OK
+    assert call(rows=0, n=48) == _lib.MX_E_ARG          # the scalars are still checked
+    assert call(rows=0, dtype=F32, views=1, row=None) == _lib.MX_OK
