@@ -9,6 +9,8 @@ Contents
   norm.py       RMSNorm over the last axis followed by both MX views of its output (the
                 fused normalisation producer), and the rule stating which device codes are
                 consistent with an fp32 evaluation of it.
+  gemm.py       MXFP8 GEMM (float64 product of two ROW views) followed by both MX views of its
+                output (the fused GEMM producer), and the FP32 accumulation bound.
   attention.py  same-scheme quantised attention forward/backward in float64 for one
                 (sequence, head), the unquantised float64 reference, and the ambiguity
                 bound that states which device results are admissible where an fp32
@@ -28,10 +30,11 @@ from .codec import (E4M3_MAX, GROUP, e4m3_decode, e4m3_encode, e4m3_round, mx_sc
                     mx_quantize_groups, mx_dequantize_groups, mx_fake_quant, mx_fake_quant_blocks2d)
 from .attention import (ArithModel, head_forward, head_backward, head_reference, visible, round_to, ulp_of)
 from .norm import rmsnorm, rmsnorm_quantize, fp32_rel_bound, admissible
+from .gemm import gemm_quantize, accumulation_bound, dequant_rows
 
 __all__ = [
     "E4M3_MAX", "GROUP", "e4m3_decode", "e4m3_encode", "e4m3_round", "mx_scale_exponent",
     "mx_quantize_groups", "mx_dequantize_groups", "mx_fake_quant", "mx_fake_quant_blocks2d",
     "ArithModel", "head_forward", "head_backward", "head_reference", "visible", "round_to", "ulp_of",
-    "rmsnorm", "rmsnorm_quantize", "fp32_rel_bound", "admissible",
+    "rmsnorm", "rmsnorm_quantize", "fp32_rel_bound", "admissible", "gemm_quantize", "accumulation_bound", "dequant_rows",
 ]
