@@ -50,20 +50,28 @@ def fp32_rel_bound(n):
     return 2.0 * (n + 8) * 2.0 ** -24
 
 
-def admissible(y, axis, dev_sbytes, dev_codes, rel):
-    """Which device results are consistent with y known to relative accuracy ``rel``.
+def admissible(y, axis, dev_sbytes, dev_codes, rel, err=None):
+    """Which device results are consistent with y known to within rel |y| + err.
 
     y: float64 values ([rows, n]); axis: the group axis (1 ROW, 0 SEQ); dev_sbytes: device
     scale bytes (group axis of length ceil(len/32)); dev_codes: device codes with the shape
-    of y in natural order. A group's device exponent is admissible when it is the codec's
-    exponent of some amax in [amax (1 - rel), amax (1 + rel)]; given an admissible exponent e,
-    an element's code is admissible when it is the code of some value in y 2^-e [1 - rel,
-    1 + rel] (E4M3 rounding is monotone, so the ends of the interval give the extreme codes).
+    of y in natural order; rel: relative error; err: optional absolute error per element
+    (shape of y; e.g. a matrix product's accumulation bound). Each element's value lies in
+    [y - t, y + t] with t = rel |y| + err. A group's device exponent is admissible when it is
+    the codec's exponent of some amax between the largest max(|y| - t, 0) and the largest
+    |y| + t of the group; given an admissible exponent e, an element's code is admissible when
+    it is the code of some value in [y - t, y + t] 2^-e (E4M3 rounding is monotone, so the
+    ends of the interval give the extreme codes). With err = None this is the relative
+    interval amax [1 - rel, 1 + rel], y [1 - rel, 1 + rel].
     Groups holding a non-finite value must carry scale 0xFF and codes 0x7F.
     Returns (groups_ok, codes_ok) boolean arrays (group shape, element shape).
     """
     y = np.asarray(y, dtype=np.float64)
+    t = rel * np.abs(np.where(np.isfinite(y), y, 0.0))
+    if err is not None:
+        t = t + np.broadcast_to(np.asarray(err, dtype=np.float64), y.shape)
     ym = np.moveaxis(y, axis, -1)
+    tm = np.moveaxis(t, axis, -1)
     cm = np.moveaxis(np.asarray(dev_codes), axis, -1)
     sb = np.moveaxis(np.asarray(dev_sbytes).astype(np.int64), axis, -1)
     n = ym.shape[-1]
@@ -71,19 +79,21 @@ def admissible(y, axis, dev_sbytes, dev_codes, rel):
     pad = ng * GROUP - n
     if pad:
         ym = np.concatenate([ym, np.zeros(ym.shape[:-1] + (pad,))], axis=-1)
+        tm = np.concatenate([tm, np.zeros(tm.shape[:-1] + (pad,))], axis=-1)
         cm = np.concatenate([cm, np.zeros(cm.shape[:-1] + (pad,), dtype=cm.dtype)], axis=-1)
     blocks = ym.reshape(ym.shape[:-1] + (ng, GROUP))
+    tol = tm.reshape(tm.shape[:-1] + (ng, GROUP))
     cblk = cm.reshape(cm.shape[:-1] + (ng, GROUP))
     finite = np.all(np.isfinite(blocks), axis=-1)
-    amax = np.max(np.abs(np.where(np.isfinite(blocks), blocks, 0.0)), axis=-1)
-    e_lo = mx_scale_exponent(amax * (1.0 - rel))
-    e_hi = mx_scale_exponent(amax * (1.0 + rel))
+    ab = np.abs(np.where(np.isfinite(blocks), blocks, 0.0))
+    e_lo = mx_scale_exponent(np.max(np.maximum(ab - tol, 0.0), axis=-1))
+    e_hi = mx_scale_exponent(np.max(ab + tol, axis=-1))
     e_dev = sb - E8M0_BIAS
     groups_ok = np.where(finite, (e_dev >= e_lo) & (e_dev <= e_hi), sb == E8M0_NAN)
     e_use = np.where(groups_ok & finite, e_dev, 0)[..., None]
     with np.errstate(invalid="ignore"):
-        c1 = e4m3_encode(np.ldexp(blocks * (1.0 - rel), -e_use)).astype(np.int64)
-        c2 = e4m3_encode(np.ldexp(blocks * (1.0 + rel), -e_use)).astype(np.int64)
+        c1 = e4m3_encode(np.ldexp(blocks - tol, -e_use)).astype(np.int64)
+        c2 = e4m3_encode(np.ldexp(blocks + tol, -e_use)).astype(np.int64)
     # order codes by value: sign-magnitude byte -> signed integer rank
     rank = lambda c: np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
     r1, r2, rd = rank(c1), rank(c2), rank(cblk.astype(np.int64))

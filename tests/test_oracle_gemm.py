@@ -107,3 +107,70 @@ def test_fp32_accumulations_stay_inside_the_bound(order):
     assert np.all(np.abs(c32 - c) <= bound)
     # and the bound is not vacuous: it stays below 2^-9 of the absolute-product sum
     assert np.all(bound <= 2.0 ** -9 * np.abs(G.dequant_rows(a, sa)) @ np.abs(G.dequant_rows(b, sb)).T)
+
+
+def _views_of(c):
+    rc, _, rs = oracle.mx_quantize_groups(c, axis=1)
+    sc, _, ss = oracle.mx_quantize_groups(c, axis=0)
+    return rc, rs, sc, ss
+
+
+@pytest.mark.parametrize("order", ["blas", "sequential"])
+def test_views_of_fp32_accumulations_are_admitted(order):
+    # a device that accumulates in FP32 in any order and then quantises its own C must pass
+    rng = np.random.default_rng(7)
+    a, sa = _operand(rng, 70, 256)       # 70 rows: a partial SEQ group of 6 rows
+    b, sb = _operand(rng, 96, 256)
+    ref = G.gemm_quantize(a, sa, b, sb)
+    bound = G.accumulation_bound(a, sa, b, sb)
+    da, db = G.dequant_rows(a, sa).astype(np.float32), G.dequant_rows(b, sb).astype(np.float32)
+    if order == "blas":
+        c32 = (da @ db.T).astype(np.float64)
+    else:
+        acc = np.zeros((70, 96), np.float32)
+        for k in range(255, -1, -1):
+            acc = (acc + np.outer(da[:, k], db[:, k]).astype(np.float32)).astype(np.float32)
+        c32 = acc.astype(np.float64)
+    rc, rs, sc, ss = _views_of(c32)
+    for axis, codes, sbytes in ((1, rc, rs), (0, sc, ss)):
+        gok, cok = oracle.admissible(ref["c"], axis, sbytes, codes, 0.0, err=bound)
+        assert gok.all() and cok.all()
+
+
+def test_admissible_rejects_wrong_codes_scales_and_axes():
+    rng = np.random.default_rng(8)
+    a, sa = _operand(rng, 64, 128)
+    b, sb = _operand(rng, 64, 128)
+    ref = G.gemm_quantize(a, sa, b, sb)
+    bound = G.accumulation_bound(a, sa, b, sb)
+    for axis, v in ((1, "row"), (0, "seq")):
+        codes, sbytes = ref[v + "_codes"].copy(), ref[v + "_sbytes"].copy()
+        gok, cok = oracle.admissible(ref["c"], axis, sbytes, codes, 0.0, err=bound)
+        assert gok.all() and cok.all()
+        # a code two E4M3 steps off (same sign, away from zero) is not admitted
+        i, j = 5, 9
+        bad = codes.copy()
+        bad[i, j] = (bad[i, j] & 0x80) | min((bad[i, j] & 0x7F) + 2, 0x7E)
+        if bad[i, j] != codes[i, j]:
+            assert not oracle.admissible(ref["c"], axis, sbytes, bad, 0.0, err=bound)[1][i, j]
+        # a scale byte one off is not admitted (these groups are far from a scale boundary)
+        sbad = sbytes.copy()
+        sbad[1, 1] += 1
+        assert not oracle.admissible(ref["c"], axis, sbad, codes, 0.0, err=bound)[0][1, 1]
+    # the views of the transposed product (axes swapped by mistake) are not admitted
+    tr = G.gemm_quantize(b, sb, a, sa)
+    gok, cok = oracle.admissible(ref["c"], 1, tr["row_sbytes"], tr["row_codes"], 0.0, err=bound)
+    assert not (gok.all() and cok.all())
+
+
+def test_admissible_with_zero_error_is_the_exact_decision():
+    rng = np.random.default_rng(9)
+    a, sa = _operand(rng, 32, 64)
+    b, sb = _operand(rng, 32, 64)
+    ref = G.gemm_quantize(a, sa, b, sb)
+    codes = ref["row_codes"]
+    for flip in range(1, 4):
+        bad = codes.copy()
+        bad[3, 4] ^= flip                # a different mantissa, same scale
+        gok, cok = oracle.admissible(ref["c"], 1, ref["row_sbytes"], bad, 0.0, err=np.zeros_like(ref["c"]))
+        assert gok.all() and not cok[3, 4] and cok.sum() == cok.size - 1
