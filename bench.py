@@ -15,6 +15,7 @@ the library records immediately around each launch of the named kernel, on its s
     python bench.py --workload x1  # cross-attention: 768 documents x 512 queries against
                                    # jagged keys/values (<= 14980), H3 d128, non-causal
     python bench.py --workload n1  # fused RMSNorm + quantise producer, x [262144, 512] bf16
+    python bench.py --workload g1  # fused MXFP8 GEMM + quantise producer, 16384 x 12288 x 4096
 
 `roofline.traffic` is the roofline kernel's HBM bytes per launch from rocprofv3 counters
 (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for the 1 GiB copy of --pmc-run),
@@ -35,6 +36,12 @@ KERNEL_SOURCES = ["block_scaled_mxfp8_amd/csrc/attn_bwd.hip", "block_scaled_mxfp
                   "block_scaled_mxfp8_amd/csrc/mx_layout.h", "block_scaled_mxfp8_amd/csrc/mx_internal.h",
                   "block_scaled_mxfp8_amd/build.py"]
 
+
+# the fused GEMM + quantise kernel (g1 workload)
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_gemm_quantize_g1.json")
+GEMM_KERNEL_SOURCES = ["block_scaled_mxfp8_amd/csrc/gemm_quantize.hip", "block_scaled_mxfp8_amd/csrc/mx_device.h",
+                       "block_scaled_mxfp8_amd/csrc/mx_layout.h", "block_scaled_mxfp8_amd/csrc/mx_gemm.h",
+                       "block_scaled_mxfp8_amd/build.py"]
 
 # the fused RMSNorm + quantise kernel (n1 workload)
 NORM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_rmsnorm_quantize_n1.json")
@@ -78,9 +85,9 @@ def parse():
     ap.add_argument("--pmc-run", action="store_true", help="one untimed step + a 1 GiB copy (counter collection)")
     ap.add_argument("--recompute-dq", action="store_true",
                     help="minimal workspace: the dQ pass rebuilds dS instead of reading the stored codes")
-    ap.add_argument("--workload", choices=["c3", "x1", "n1"], default="c3",
+    ap.add_argument("--workload", choices=["c3", "x1", "n1", "g1"], default="c3",
                     help="c3: the headline causal self-attention step; x1: the jagged cross-attention step; "
-                         "n1: the fused RMSNorm + quantise producer")
+                         "n1: the fused RMSNorm + quantise producer; g1: the fused GEMM + quantise producer")
     return ap.parse_args()
 
 
@@ -95,6 +102,9 @@ def main():
         return
     if args.workload == "n1":
         run_norm(args)
+        return
+    if args.workload == "g1":
+        run_gemm(args)
         return
     import numpy as np
     import torch
@@ -441,6 +451,109 @@ def run_norm(args):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_norm(x, gamma, eps)
     print(json.dumps(line), flush=True)
+
+
+def run_gemm(args):
+    """g1: one step = mx_gemm_quantize of A [16384, 4096] and B [12288, 4096] (ROW views) into
+    both MX views of C = A B^T. FLOPs 2 m n k; algorithmic bytes: both operands read once
+    ((1 + 1/32) B per element) and both views of C written (2 x (1 + 1/32) B per element)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from block_scaled_mxfp8_amd import PROFILE_GEMM, QView, load, mx_gemm_quantize, mx_profile_kernel
+
+    load()
+    cfg = synth.CONFIGS["g1"]
+    m, n, k = cfg["m"], cfg["n"], cfg["k"]
+    print("[bench] generating g1 operands on the device", file=sys.stderr, flush=True)
+    a = QView(*synth.make_gemm_operand_device(m, k, "a"))
+    b = QView(*synth.make_gemm_operand_device(n, k, "b"))
+    torch.cuda.synchronize()
+    flops = 2.0 * m * n * k
+    nbytes = (m + n) * k * 33 // 32 + 2 * (m * n * 33 // 32)
+    step = lambda: mx_gemm_quantize(a, b)  # noqa: E731
+    if args.pmc_run:
+        step()
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        buf2 = torch.empty_like(buf)
+        buf2.copy_(buf)
+        torch.cuda.synchronize()
+        print("[bench] pmc run done", file=sys.stderr, flush=True)
+        return
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    print(f"[bench] timed {steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    # the kernel alone, from HIP events the library records around it on its launch stream
+    nev = max(1, args.profile_steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
+    for e0, e1 in ev:
+        e0.record()
+        e1.record()
+    mx_profile_kernel(PROFILE_GEMM, ev)
+    torch.cuda.synchronize()
+    for _ in range(nev):
+        step()
+    torch.cuda.synchronize()
+    mx_profile_kernel(0, [])
+    k_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    tflops = lambda t: flops / (t * 1e-3) / 1e12  # noqa: E731
+    line = {
+        "metric": "fused MXFP8 GEMM + quantise (both scale layouts of the output) TFLOP/s",
+        "value": round(tflops(ms_step), 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8",
+        "data": "synthetic",
+        "config": {"workload": f"g1: C [{m}, {n}] = A [{m}, {k}] B^T, B [{n}, {k}], MXFP8 ROW-view operands "
+                               "(log-normal E4M3 codes, E8M0 scales U[123,131] / U[118,126]); step = GEMM + "
+                               "ROW and SEQ MX views of C",
+                   "m": m, "n": n, "k": k},
+        "pct_of_peak": round(100 * tflops(ms_step) / PEAK_MXFP8_TFLOPS, 2),
+        "bytes_per_step": nbytes,
+        "kernel_ms": round(k_ms, 5),
+        "pages_context": {"fused_gemm_quantize_pflops_b200": [0.91, 0.98], "separate_gemm_then_quantize_pflops_b200": 0.20},
+        "roofline": {"kernel": "gemm_quantize_kernel", "bound": "mfma",
+                     "achieved": round(tflops(k_ms), 1), "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops(k_ms) / PEAK_MXFP8_TFLOPS, 4),
+                     "traffic": recorded_traffic(GEMM_TRAFFIC_FILE, GEMM_KERNEL_SOURCES)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_gemm(a, b)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_gemm(a, b, rows=4096):
+    """The float64 oracle (as it stands) on the first `rows` rows of A against the whole of B."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - only used to report the thread count
+        cores = os.cpu_count()
+    ac, asc = a.codes[:rows].cpu().numpy(), a.scales[:rows].cpu().numpy()
+    bc, bsc = b.codes.cpu().numpy(), b.scales.cpu().numpy()
+    n, k = bc.shape
+    t0 = time.perf_counter()
+    oracle.gemm_quantize(ac, asc, bc, bsc)
+    sec = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * n * k / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "sample": f"first {rows} of {a.codes.shape[0]} rows of A against all of B "
+                                        f"({n} x {k}), float64 numpy, {sec:.1f} s"}
 
 
 def cpu_baseline_norm(x, gamma, eps, rows=32768):

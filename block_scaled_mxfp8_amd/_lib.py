@@ -69,6 +69,9 @@ def load():
     lib.mx_rmsnorm_quantize.argtypes = [P, P, I32, I64, I32, ctypes.c_float, I32, ctypes.POINTER(_QView),
                                         ctypes.POINTER(_QView), P]
     lib.mx_rmsnorm_quantize.restype = I32
+    lib.mx_gemm_quantize.argtypes = [_QView, _QView, I64, I32, I32, I32, ctypes.POINTER(_QView),
+                                     ctypes.POINTER(_QView), P]
+    lib.mx_gemm_quantize.restype = I32
     for name in ("mx_attn_fwd", "mx_attn_varlen_fwd"):
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, P, P, P]
@@ -255,6 +258,41 @@ def mx_rmsnorm_quantize(x, gamma, eps=1e-6, views=MX_VIEW_ROW | MX_VIEW_SEQ):
     return row, seqv
 
 
+def mx_gemm_quantize(a_row, b_row, views=MX_VIEW_ROW | MX_VIEW_SEQ):
+    """C = A B^T from two ROW views (a_row: codes [m, k], scales [m, k/32]; b_row: codes [n, k],
+    scales [n, k/32]), written only as MX views of C -> (row QView: codes [m, n], scales
+    [m, n/32]; seq QView: codes [ceil(m/32), n, 32], scales [ceil(m/32), n]); a view not asked
+    for is None."""
+    lib = load()
+    for name, v in (("a_row", a_row), ("b_row", b_row)):
+        if not (v.codes.is_cuda and v.scales.is_cuda and v.codes.is_contiguous() and v.scales.is_contiguous()):
+            raise ValueError(f"{name}: views must be contiguous device tensors")
+        if v.codes.dim() != 2 or v.codes.dtype != torch.uint8 or v.scales.dtype != torch.uint8:
+            raise ValueError(f"{name}: codes must be uint8 [rows, k]")
+    m, k = a_row.codes.shape
+    n, kb = b_row.codes.shape
+    if kb != k:
+        raise ValueError("a_row and b_row contract over different lengths")
+    for name, v, rows in (("a_row", a_row, m), ("b_row", b_row, n)):
+        if tuple(v.scales.shape) != (rows, k // 32):
+            raise ValueError(f"{name}: scales must be [rows, k/32]")
+    dev = a_row.codes.device
+    row = seqv = None
+    rv, sv = _QView(), _QView()
+    if views & MX_VIEW_ROW:
+        row = QView(torch.empty((m, n), dtype=torch.uint8, device=dev),
+                    torch.empty((m, max(n // 32, 1)), dtype=torch.uint8, device=dev))
+        rv = _qv(row)
+    if views & MX_VIEW_SEQ:
+        g = -(-m // 32)
+        seqv = QView(torch.empty((g, n, 32), dtype=torch.uint8, device=dev),
+                     torch.empty((g, n), dtype=torch.uint8, device=dev))
+        sv = _qv(seqv)
+    st = lib.mx_gemm_quantize(_qv(a_row), _qv(b_row), m, n, k, views, ctypes.byref(rv), ctypes.byref(sv), _stream())
+    _check(st, "mx_gemm_quantize")
+    return row, seqv
+
+
 def _desc(q_shape, k_shape, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode=MX_DQ_F32,
           deterministic=False, cross=None):
     """cross = (cu_seqlens_k, max_seqlen_k) for cross-attention (k/v with their own lengths)."""
@@ -434,6 +472,7 @@ def mx_abi_version():
 
 
 PROFILE_FWD, PROFILE_BWD_DKDV, PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_DQ, PROFILE_RMSNORM = 1, 2, 3, 4, 5, 6
+PROFILE_GEMM = 7
 _PROFILE_KEEP = []
 
 

@@ -8,7 +8,7 @@
 namespace mx {
 
 enum ProfileKind {
-  kProfNone = 0, kProfFwd = 1, kProfBwdKV = 2, kProfQuantize = 3, kProfBwdPrep = 4, kProfBwdQ = 5, kProfRmsNorm = 6
+  kProfNone = 0, kProfFwd = 1, kProfBwdKV = 2, kProfQuantize = 3, kProfBwdPrep = 4, kProfBwdQ = 5, kProfRmsNorm = 6, kProfGemm = 7
 };
 
 struct ProfileHook {

@@ -5,6 +5,7 @@
 
 #include "../../include/mxattn.h"
 #include "mx_internal.h"
+#include "mx_gemm.h"
 #include "mx_norm.h"
 #include "mx_layout.h"
 #include "mx_profile.h"
@@ -269,6 +270,37 @@ mx_status mx_rmsnorm_quantize(const void* x, const void* gamma, mx_dtype dtype, 
   return err == hipSuccess ? MX_OK : MX_E_DEVICE;
 }
 
+mx_status mx_gemm_quantize(mx_qview a_row, mx_qview b_row, int64_t m, int32_t n, int32_t k, int32_t views,
+                           mx_qview* row_out, mx_qview* seq_out, void* stream) {
+  if (m < 0 || n < 32 || n % 32 != 0 || k < 64 || k % 64 != 0) return MX_E_ARG;
+  if (views < 1 || views > 3) return MX_E_ARG;
+  if (m > 0x7FFFFFFF || n > (1 << 24) || k > (1 << 23)) return MX_E_UNSUPPORTED;
+  if (m == 0) return MX_OK;             // nothing is read or written: every pointer may be NULL
+  if (check_view(a_row) != MX_OK || check_view(b_row) != MX_OK) return MX_E_ARG;
+  mx::GemmQuantParams p = {};
+  p.a_codes = a_row.codes;
+  p.a_scales = a_row.scales;
+  p.b_codes = b_row.codes;
+  p.b_scales = b_row.scales;
+  p.m = (int)m;
+  p.n = n;
+  p.k = k;
+  if (views & MX_VIEW_ROW) {
+    if (!row_out || check_view(*row_out) != MX_OK) return MX_E_ARG;
+    p.row_codes = row_out->codes;
+    p.row_scales = row_out->scales;
+  }
+  if (views & MX_VIEW_SEQ) {
+    if (!seq_out || check_view(*seq_out) != MX_OK) return MX_E_ARG;
+    p.seq_codes = seq_out->codes;
+    p.seq_scales = seq_out->scales;
+  }
+  const int slot = mx::profile_begin(mx::kProfGemm, (hipStream_t)stream);
+  const hipError_t err = mx::launch_gemm_quantize(p, (hipStream_t)stream);
+  mx::profile_end(slot, (hipStream_t)stream);
+  return err == hipSuccess ? MX_OK : MX_E_DEVICE;
+}
+
 mx_status mx_attn_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o, float* lse,
                       void* stream) {
   return fwd_impl(desc, nullptr, q_row, k_row, v_seq, o, lse, stream, false);
@@ -341,7 +373,7 @@ mx_status mx_profile_kernel(int32_t kernel, void* const* start_events, void* con
     h = mx::ProfileHook();
     return MX_OK;
   }
-  if (kernel < 1 || kernel > 6 || !start_events || !stop_events) return MX_E_ARG;
+  if (kernel < 1 || kernel > 7 || !start_events || !stop_events) return MX_E_ARG;
   h.kind = kernel;
   h.start = (hipEvent_t*)start_events;
   h.stop = (hipEvent_t*)stop_events;

@@ -137,6 +137,26 @@ mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const 
 mx_status mx_rmsnorm_quantize(const void* x, const void* gamma, mx_dtype dtype, int64_t rows, int32_t n, float eps,
                               int32_t views, mx_qview* row_out, mx_qview* seq_out, void* stream);
 
+/* Fused MXFP8 GEMM + quantise, the GEMM producer of Meta's MXFP8 write-up (section
+ * "Quantisation inside the producers": the GEMM writes its FP8 output in both scale layouts at
+ * once, so that its consumer never quantises again). Computes C = A B^T, A [m, k] and B [n, k]
+ * given as ROW views (codes row-major [rows, k], one E8M0 byte per 32 consecutive k:
+ * scales [rows, k/32]; e.g. activations from mx_rmsnorm_quantize and a weight), accumulated in
+ * FP32 by the block-scaled matrix cores, and writes C only as MX views with the group rule of
+ * mx_quantize:
+ *   ROW view (groups of 32 columns of a row): codes [m, n], scales [m, n/32];
+ *   SEQ view (groups of 32 rows of a column): codes [ceil(m/32), n, 32] with row offset t of
+ *            group g at byte MX_SEQ_POS(t), scales [ceil(m/32), n]; the rows past the end of a
+ *            partial last group count as zeros and hold code 0.
+ * i.e. the views mx_quantize gives for an [1, 1, m, n] tensor. views = MX_VIEW_ROW |
+ * MX_VIEW_SEQ; the unused output may be NULL. k: a multiple of 64, 64..2^23; n: a multiple of
+ * 32, 32..2^24; m: 0..2^31 - 1 (0 launches nothing and reads no pointer). Code pointers 16-byte
+ * aligned, scale pointers 4-byte aligned (MX_E_ARG otherwise). A group whose FP32 sum is not
+ * finite (an overflow of the accumulation) gets scale 0xFF and codes 0x7F. The result depends
+ * only on the operands (fixed accumulation order; no atomics). */
+mx_status mx_gemm_quantize(mx_qview a_row, mx_qview b_row, int64_t m, int32_t n, int32_t k, int32_t views,
+                           mx_qview* row_out, mx_qview* seq_out, void* stream);
+
 /* Forward: O [layout above, out_dtype] and LSE float32 [B,H,L] / [T,H] (natural log,
  * +inf for a row without visible keys). q_row / k_row: ROW views of Q and K (heads_q and
  * heads_kv heads); v_seq: SEQ view of V. */
@@ -207,7 +227,7 @@ mx_status mx_read_flags(const void* workspace, uint32_t* flags);
  * kernel records start[i % count] just before and stop[i % count] just after it, on the stream
  * it is launched on, i = launch index since registration. kernel: 1 forward attention kernel,
  * 2 backward dK/dV kernel, 3 mx_quantize, 4 backward G preprocessing, 5 backward dQ kernel,
- * 6 mx_rmsnorm_quantize; 0 (or
+ * 6 mx_rmsnorm_quantize, 7 mx_gemm_quantize; 0 (or
  * count <= 0) turns the hook off. The event arrays must stay valid while registered. One
  * hook per process; not thread-safe. */
 mx_status mx_profile_kernel(int32_t kernel, void* const* start_events, void* const* stop_events, int32_t count);

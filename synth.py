@@ -25,10 +25,19 @@ Workloads (sizes and value distributions):
       magnitude u_m ~ U(-3, 3) and o_c = 20 on 4 fixed outlier channels (else 1);
       gamma = 1 + 0.25 N(0,1). Small test cases draw the same recipe with numpy; the full
       size draws it with torch's generator on the device.
+  g1  fused MXFP8 GEMM + quantise producer: C = A B^T with A [16384, 4096] (4 sequences x
+      4096 tokens at model width 4096 = 32 heads x 128, the c3 shape) and B [12288, 4096]
+      (a fused Q, K, V projection weight), written as both MX views of C [16384, 12288]. The
+      operands are ROW views drawn bit by bit: E4M3 codes with a uniform sign, exponent field
+      clip(round(7 + 2 z), 0, 15) (z ~ N(0,1): magnitudes log-normal around 1), uniform
+      mantissa, the NaN pattern S.1111.111 replaced by S.1111.110; E8M0 scale bytes uniform in
+      [123, 131] for A and [118, 126] for B. Small test cases draw the recipe with numpy; the
+      full size with torch's generator on the device.
 """
 import numpy as np
 
-TENSOR_ID = {"q": 1, "k": 2, "v": 3, "g": 4, "lengths": 5, "outliers": 6, "magnitude": 7, "x": 8, "gamma": 9}
+TENSOR_ID = {"q": 1, "k": 2, "v": 3, "g": 4, "lengths": 5, "outliers": 6, "magnitude": 7, "x": 8, "gamma": 9,
+             "a": 10, "b": 11, "a_scales": 12, "b_scales": 13}
 
 CONFIGS = {
     "c1": dict(batch=1, heads=1, heads_kv=1, seqlen=256, head_dim=64, causal=True, dtype="f32", backward=False),
@@ -45,7 +54,9 @@ CONFIGS = {
 CONFIGS["x1"] = dict(n_docs=768, queries=512, max_keys=14980, heads=3, heads_kv=3, head_dim=128, causal=False,
                      dtype="bf16", backward=True)
 CONFIGS["n1"] = dict(rows=262144, n=512, dtype="bf16", outlier_channels=(3, 100, 257, 511), outlier=20.0)
-SEED_BASE = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "c5gqa": 1005, "x1": 1101, "n1": 1201}
+CONFIGS["g1"] = dict(m=16384, n=12288, k=4096, a_scales=(123, 131), b_scales=(118, 126))
+SEED_BASE = {"c1": 1001, "c2": 1002, "c3": 1003, "c4": 1004, "c5": 1005, "c5gqa": 1005, "x1": 1101, "n1": 1201,
+             "g1": 1301}
 
 
 def rng(seed, tensor):
@@ -179,3 +190,48 @@ def make_norm_inputs_device(rows=None, n=None, seed=None, dtype=None, device="cu
     x = torch.randn((rows, n), generator=gens["x"], device=device) * torch.exp2(u) * o
     gamma = 1.0 + 0.25 * torch.randn((n,), generator=gens["gamma"], device=device)
     return x.to(dtype), gamma.to(dtype)
+
+
+def _code_bits(sign, expo, mant):
+    """Assemble E4M3 bit patterns; the NaN pattern (exponent 15, mantissa 7) becomes mantissa 6."""
+    code = sign * 128 + expo * 8 + mant
+    return code - ((code & 0x7F) == 0x7F)
+
+
+def gemm_operand(rows, k, tensor, seed=None, scale_range=None):
+    """g1 recipe at any size with numpy: one ROW-view operand (codes uint8 [rows, k], scale
+    bytes uint8 [rows, k/32]). tensor: "a" or "b"."""
+    cfg = CONFIGS["g1"]
+    seed = SEED_BASE["g1"] if seed is None else seed
+    lo, hi = cfg[tensor + "_scales"] if scale_range is None else scale_range
+    r = rng(seed, tensor)
+    sign = r.integers(0, 2, size=(rows, k))
+    expo = np.clip(np.rint(7.0 + 2.0 * r.standard_normal(size=(rows, k))), 0, 15).astype(np.int64)
+    mant = r.integers(0, 8, size=(rows, k))
+    codes = _code_bits(sign, expo, mant).astype(np.uint8)
+    scales = rng(seed, tensor + "_scales").integers(lo, hi + 1, size=(rows, k // 32)).astype(np.uint8)
+    return codes, scales
+
+
+def make_gemm_operand_device(rows, k, tensor, seed=None, device="cuda"):
+    """g1 recipe drawn on the device with torch's generator (seeded base seed * 16 + tensor id):
+    (codes uint8 [rows, k], scale bytes uint8 [rows, k/32])."""
+    import torch
+    cfg = CONFIGS["g1"]
+    seed = SEED_BASE["g1"] if seed is None else seed
+    lo, hi = cfg[tensor + "_scales"]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 16 + TENSOR_ID[tensor])
+    codes = torch.empty((rows, k), dtype=torch.uint8, device=device)
+    step = max(1, (1 << 26) // k)   # draw in slices of about 64 M elements to bound temporaries
+    for r0 in range(0, rows, step):
+        n = min(step, rows - r0)
+        sign = torch.randint(0, 2, (n, k), generator=gen, device=device, dtype=torch.int32)
+        expo = torch.clamp(torch.round(7.0 + 2.0 * torch.randn((n, k), generator=gen, device=device)), 0, 15)
+        mant = torch.randint(0, 8, (n, k), generator=gen, device=device, dtype=torch.int32)
+        code = sign * 128 + expo.to(torch.int32) * 8 + mant
+        codes[r0:r0 + n] = (code - ((code & 0x7F) == 0x7F).to(torch.int32)).to(torch.uint8)
+    gs = torch.Generator(device=device)
+    gs.manual_seed(int(seed) * 16 + TENSOR_ID[tensor + "_scales"])
+    scales = torch.randint(lo, hi + 1, (rows, k // 32), generator=gs, device=device, dtype=torch.int32).to(torch.uint8)
+    return codes, scales

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("mx_quantize", "mx_attn_fwd", "mx_attn_bwd", "mx_attn_varlen_fwd", "mx_attn_varlen_bwd",
                      "mx_attn_workspace_size", "mx_read_flags", "mx_strerror", "mx_abi_version",
-                     "mx_attn_cross_fwd", "mx_attn_cross_bwd", "mx_rmsnorm_quantize"):
+                     "mx_attn_cross_fwd", "mx_attn_cross_bwd", "mx_rmsnorm_quantize", "mx_gemm_quantize"):
         assert required in names
 
 
@@ -232,3 +232,36 @@ def test_rmsnorm_quantize_validation(lib):
     assert call(rows=0, x=None, gamma=None, row=None, seq=None) == _lib.MX_OK
     assert call(rows=0, n=48) == _lib.MX_E_ARG          # the scalars are still checked
     assert call(rows=0, dtype=F32, views=1, row=None) == _lib.MX_OK
+
+
+def test_gemm_quantize_validation(lib):
+    # every failure is caught on the host before a launch; m = 0 launches nothing
+    f = lib.mx_gemm_quantize
+    v = _lib._QView(FAKE, FAKE)
+    ok_args = (v, v, 256, 512, 1024, 3, ctypes.byref(v), ctypes.byref(v), None)
+
+    def call(**kw):
+        names = ("a", "b", "m", "n", "k", "views", "row", "seq", "stream")
+        a = dict(zip(names, ok_args))
+        a.update(kw)
+        return f(*(a[k] for k in names))
+
+    assert call(a=_lib._QView(None, FAKE)) == _lib.MX_E_ARG
+    assert call(b=_lib._QView(FAKE, None)) == _lib.MX_E_ARG
+    assert call(a=_lib._QView(FAKE + 8, FAKE)) == _lib.MX_E_ARG      # codes not 16-byte aligned
+    assert call(b=_lib._QView(FAKE, FAKE + 2)) == _lib.MX_E_ARG      # scales not 4-byte aligned
+    assert call(m=-1) == _lib.MX_E_ARG
+    for n in (0, 16, 48, 100):
+        assert call(n=n) == _lib.MX_E_ARG, n
+    for k in (0, 32, 96, 100):
+        assert call(k=k) == _lib.MX_E_ARG, k
+    for views in (0, 4):
+        assert call(views=views) == _lib.MX_E_ARG, views
+    assert call(k=1 << 24) == _lib.MX_E_UNSUPPORTED
+    assert call(n=1 << 25) == _lib.MX_E_UNSUPPORTED
+    assert call(m=1 << 31) == _lib.MX_E_UNSUPPORTED
+    assert call(row=None) == _lib.MX_E_ARG                           # ROW view asked for, none given
+    assert call(views=2, seq=ctypes.byref(_lib._QView(None, FAKE))) == _lib.MX_E_ARG
+    nul = _lib._QView(None, None)
+    assert call(m=0, a=nul, b=nul, row=None, seq=None) == _lib.MX_OK
+    assert call(m=0, k=96) == _lib.MX_E_ARG                          # the scalars are still checked
