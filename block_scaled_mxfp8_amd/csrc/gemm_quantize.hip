@@ -13,9 +13,11 @@
 //    columns 128 (w >> 2) .. + 128, i.e. 2 x 4 accumulator tiles of 32 x 32 (128 VGPRs).
 //    One workgroup per CU (136 KB of LDS), two waves per SIMD.
 //  * The contraction advances 64 at a time through four LDS stages filled by LDS-DMA
-//    (global_load_lds) three stages ahead: A and B codes [256 rows][64 bytes], 16-byte chunks
-//    swizzled by row (row_swz) so that every 16-lane operand read touches each bank once, and
-//    the two E8M0 bytes of each row in a dword slot. One barrier per stage.
+//    (global_load_lds): A and B codes [256 rows][64 bytes], 16-byte chunks swizzled by row
+//    (row_swz) so that every 16-lane operand read touches each bank once, and the two E8M0
+//    bytes of each row in a dword slot. Stages are loaded in pairs, two and three stages
+//    ahead, so that both 64-byte halves of each 128-byte row segment are requested together.
+//    One barrier per stage.
 //  * Products by V_MFMA_SCALE_F32_32X32X64_F8F6F4 with the operands' own E8M0 bytes: A rows
 //    are the MFMA rows, B rows its columns, so lane (c, h) of an accumulator holds column c,
 //    rows 8j + 4h + i (j, i = 0..3).
@@ -40,7 +42,6 @@ constexpr int kBM = 256;          // rows of C per workgroup
 constexpr int kBN = 256;          // columns of C per workgroup
 constexpr int kBK = 64;           // contraction per stage
 constexpr int kStages = 4;
-constexpr int kAhead = kStages - 1;
 constexpr int kThreads = 512;
 constexpr int kDmaPerStage = 5;   // LDS-DMA instructions per wave per stage
 constexpr int kScr = 36;          // row stride (floats) of the epilogue's transpose tile
@@ -67,23 +68,26 @@ struct StageLoads {
   int sc_row0;           // first tile row of this wave's scale load (64 per wave)
 };
 
-__device__ __forceinline__ void issue_stage(GemmSmem& sm, const StageLoads& L, int slot, int stage) {
+// Loads of stages `stage` and `stage + 1` (if any), interleaved so that the two 64-byte halves
+// of each 128-byte row segment are requested back to back; the two scale loads come last.
+__device__ __forceinline__ void issue_pair(GemmSmem& sm, const StageLoads& L, int stage, int nk) {
+  const bool two = stage + 1 < nk;
+  const int s0 = stage % kStages, s1 = (stage + 1) % kStages;
   const uint32_t k0 = (uint32_t)stage * kBK;
 #pragma unroll
   for (int q = 0; q < 2; q++) {
     const int r0 = L.code_row0 + 16 * q;
-    lds_dma_so(L.a + k0, L.code_off[q], &sm.a[slot][r0 * kBK], 16);
-    lds_dma_so(L.b + k0, L.b_off[q], &sm.b[slot][r0 * kBK], 16);
+    lds_dma_so(L.a + k0, L.code_off[q], &sm.a[s0][r0 * kBK], 16);
+    if (two) lds_dma_so(L.a + k0 + kBK, L.code_off[q], &sm.a[s1][r0 * kBK], 16);
+    lds_dma_so(L.b + k0, L.b_off[q], &sm.b[s0][r0 * kBK], 16);
+    if (two) lds_dma_so(L.b + k0 + kBK, L.b_off[q], &sm.b[s1][r0 * kBK], 16);
   }
-  uint32_t* dst = L.sc_is_a ? &sm.as[slot][L.sc_row0] : &sm.bs[slot][L.sc_row0];
-  lds_dma_so(L.sc + 2 * stage, L.sc_off, dst, 2);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_stage(int ahead) {
-  if (ahead >= 2) wait_vmem_n<2 * N>();
-  else if (ahead == 1) wait_vmem_n<N>();
-  else wait_vmem();
+  uint32_t* d0 = L.sc_is_a ? &sm.as[s0][L.sc_row0] : &sm.bs[s0][L.sc_row0];
+  lds_dma_so(L.sc + 2 * stage, L.sc_off, d0, 2);
+  if (two) {
+    uint32_t* d1 = L.sc_is_a ? &sm.as[s1][L.sc_row0] : &sm.bs[s1][L.sc_row0];
+    lds_dma_so(L.sc + 2 * stage + 2, L.sc_off, d1, 2);
+  }
 }
 
 // 16 E4M3 codes of x / 2^e (or the non-finite pattern) as one 16-byte vector.
@@ -155,9 +159,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_quantize_kernel(GemmQuantPar
   }
 
   const int nk = p.k / kBK;
-#pragma unroll
-  for (int s = 0; s < kAhead; s++)
-    if (s < nk) issue_stage(sm, L, s, s);
+  issue_pair(sm, L, 0, nk);
 
   // operand read offsets (loop-invariant): row R's chunk c sits at R * 64 + 16 row_swz(R, c)
   uint32_t a_lo[2], a_hi[2], a_sc[2], b_lo[4], b_hi[4], b_sc[4];
@@ -183,9 +185,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_quantize_kernel(GemmQuantPar
     for (int tn = 0; tn < 4; tn++) acc[tm][tn] = v16f{};
 
   for (int i = 0; i < nk; i++) {
-    wait_stage<kDmaPerStage>(min(nk - 1 - i, kAhead - 1));
+    // loads issued after stage i's last one (pairs interleave their two stages, the scale
+    // loads come last): i even -> the pair's second scale load; i odd -> the next pair
+    if (!(i & 1)) {
+      if (i + 1 < nk) wait_vmem_n<1>();
+      else wait_vmem();
+    } else {
+      if (i + 2 < nk) wait_vmem_n<2 * kDmaPerStage>();
+      else if (i + 1 < nk) wait_vmem_n<kDmaPerStage>();
+      else wait_vmem();
+    }
     wg_barrier();   // stage i is in LDS for every wave; every wave has finished stage i - 1
-    if (i + kAhead < nk) issue_stage(sm, L, (i + kAhead) % kStages, i + kAhead);
+    if (!(i & 1) && i + 2 < nk) issue_pair(sm, L, i + 2, nk);
     const int slot = i % kStages;
     const uint8_t* A = sm.a[slot];
     const uint8_t* B = sm.b[slot];
