@@ -5,7 +5,8 @@ may import this package. The library (``block_scaled_mxfp8_amd``) never imports 
 this package imports nothing from the library: the two share no code, tables or helpers.
 
 Contents
-  codec.py      E4M3 / E8M0 codec and MX group quantisation (bit-exact reference).
+  codec.py      E4M3 / E8M0 codec and MX group quantisation (bit-exact reference), including
+                FLAMIA's token-block scales (one exponent per 32-token block, all channels).
   norm.py       RMSNorm over the last axis followed by both MX views of its output (the
                 fused normalisation producer), and the rule stating which device codes are
                 consistent with an fp32 evaluation of it.
@@ -27,7 +28,8 @@ The ambiguity bound is pinned by perturbation: random device-like perturbations 
 the stated budget never move an output outside the bound.
 """
 from .codec import (E4M3_MAX, GROUP, e4m3_decode, e4m3_encode, e4m3_round, mx_scale_exponent,
-                    mx_quantize_groups, mx_dequantize_groups, mx_fake_quant, mx_fake_quant_blocks2d)
+                    mx_quantize_groups, mx_dequantize_groups, mx_fake_quant, mx_fake_quant_blocks2d,
+                    mx_quantize_token_blocks, mx_fake_quant_token_blocks)
 from .attention import (ArithModel, head_forward, head_backward, head_reference, visible, round_to, ulp_of)
 from .norm import rmsnorm, rmsnorm_quantize, fp32_rel_bound, admissible
 from .gemm import gemm_quantize, accumulation_bound, dequant_rows
@@ -35,6 +37,7 @@ from .gemm import gemm_quantize, accumulation_bound, dequant_rows
 __all__ = [
     "E4M3_MAX", "GROUP", "e4m3_decode", "e4m3_encode", "e4m3_round", "mx_scale_exponent",
     "mx_quantize_groups", "mx_dequantize_groups", "mx_fake_quant", "mx_fake_quant_blocks2d",
+    "mx_quantize_token_blocks", "mx_fake_quant_token_blocks",
     "ArithModel", "head_forward", "head_backward", "head_reference", "visible", "round_to", "ulp_of",
     "rmsnorm", "rmsnorm_quantize", "fp32_rel_bound", "admissible", "gemm_quantize", "accumulation_bound", "dequant_rows",
 ]

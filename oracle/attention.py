@@ -36,7 +36,8 @@ dQ = U K_seq; D uses G_row and the saved (output-dtype) O.
 import math
 import numpy as np
 
-from .codec import (GROUP, e4m3_round, mx_fake_quant, mx_fake_quant_blocks2d, mx_scale_exponent)
+from .codec import (GROUP, e4m3_round, mx_fake_quant, mx_fake_quant_blocks2d, mx_fake_quant_token_blocks,
+                    mx_scale_exponent)
 
 LN2 = math.log(2.0)
 LOG2E = 1.0 / LN2
@@ -123,7 +124,7 @@ def _mx_dev(y, e, dy_rel, group_axis):
 
 
 def head_forward(q, k, v, causal, softmax_scale=None, quantized=True, out_dtype="bf16",
-                 bounds=False, arith=None, perturb=None, rows=None):
+                 bounds=False, arith=None, perturb=None, rows=None, scales="axis"):
     """Forward pass for one head: returns dict(O (float64, unrounded), O_out (rounded), lse,
     ell, and when bounds=True: B (ambiguity bound on O), eta (accumulation allowance)).
 
@@ -133,7 +134,12 @@ def head_forward(q, k, v, causal, softmax_scale=None, quantized=True, out_dtype=
 
     ``rows`` (optional, sorted query indices) evaluates only those query rows -- each row is
     independent in the forward, and its P groups run along keys -- and returns arrays with one
-    entry per selected row; Q is still quantised whole so the row-view groups are unchanged."""
+    entry per selected row; Q is still quantised whole so the row-view groups are unchanged.
+
+    ``scales``: "axis" (groups of 32 along the contraction: Q and K along d, V along the
+    sequence) or "token_block" (FLAMIA notes, section 3: one exponent per 32-token block of
+    the sequence shared by all channels, for Q, K and V alike). P is quantised the same way
+    in both."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -141,7 +147,10 @@ def head_forward(q, k, v, causal, softmax_scale=None, quantized=True, out_dtype=
     nk = k.shape[0]
     alpha = float(softmax_scale) if softmax_scale else d ** -0.5
     A = arith or ArithModel()
-    if quantized:
+    if quantized and scales == "token_block":
+        Qt, Kt, Vt = (mx_fake_quant_token_blocks(x) for x in (q, k, v))
+    elif quantized:
+        assert scales == "axis", scales
         Qt = mx_fake_quant(q, axis=1)      # row view: 32 channels of one token
         Kt = mx_fake_quant(k, axis=1)
         Vt = mx_fake_quant(v, axis=0)      # seq view: 32 tokens of one channel
@@ -218,7 +227,7 @@ def _pad_groups(a):
 
 def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantized=True,
                   out_dtype="bf16", bounds=False, arith=None, fwd=None, dq_mode="f32", perturb=None,
-                  dq_blocks=None):
+                  dq_blocks=None, scales="axis"):
     """Backward pass for one head (Algorithm 1 steps 09-16 of the FLAMIA notes).
 
     o_saved: O as stored by the forward (output dtype); lse: the forward's row LSE (natural
@@ -231,6 +240,10 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
     ``dq_blocks`` (optional) lists 32-row query blocks (block index b = rows 32b..32b+31): only
     dQ of those rows is evaluated (a dS scale block is 32 queries x 32 keys, so a whole query
     block determines its rows' dQ); dK and dV are then returned as NaN.
+
+    ``scales``: the geometry of Q's, K's and V's scales, as in head_forward ("token_block":
+    one exponent per 32-token block, so each tensor's ROW and SEQ views hold the same values).
+    G is quantised inside the backward with per-axis groups either way.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -241,7 +254,13 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
     nk = k.shape[0]
     alpha = float(softmax_scale) if softmax_scale else d ** -0.5
     A = arith or ArithModel()
-    if quantized:
+    if quantized and scales == "token_block":
+        Qr = Qs = mx_fake_quant_token_blocks(q)
+        Kr = Ks = mx_fake_quant_token_blocks(k)
+        Vr = mx_fake_quant_token_blocks(v)
+        Gr, Gs = mx_fake_quant(g, 1), mx_fake_quant(g, 0)
+    elif quantized:
+        assert scales == "axis", scales
         Qr, Kr = mx_fake_quant(q, 1), mx_fake_quant(k, 1)
         Qs, Ks = mx_fake_quant(q, 0), mx_fake_quant(k, 0)
         Vr = mx_fake_quant(v, 1)

@@ -165,3 +165,36 @@ def mx_fake_quant_blocks2d(u):
     q = e4m3_decode(e4m3_encode(np.ldexp(blk, -e[:, None, :, None])))
     q = np.ldexp(q, e[:, None, :, None]).reshape(R, C)[:r, :c]
     return q, e
+
+
+def mx_quantize_token_blocks(x):
+    """Token-block scales (FLAMIA notes, section 3, why the scale is made a token block): one
+    E8M0 exponent for each block of 32 consecutive tokens of one sequence or document, shared
+    by every channel, so that the groups of 32 channels of a token and the groups of 32 tokens
+    of a channel inside the block all carry the same exponent and the same codes serve both
+    contraction axes.
+
+    x: [n, d] (the tokens of one sequence or document of one head, in order). The last block
+    may be partial. The exponent is the group rule (mx_scale_exponent) applied to the block's
+    largest |x|; a block holding a NaN or an infinity gets scale byte 0xFF and codes 0x7F.
+    Returns (codes uint8 [n, d], exponents int64 [ceil(n/32)], scale bytes uint8 [ceil(n/32)]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    nb = -(-n // GROUP)
+    xp = np.zeros((nb * GROUP, d))
+    xp[:n] = x
+    blk = xp.reshape(nb, GROUP * d)
+    finite = np.all(np.isfinite(blk), axis=1)
+    amax = np.max(np.abs(np.where(np.isfinite(blk), blk, 0.0)), axis=1)
+    e = mx_scale_exponent(amax)
+    codes = e4m3_encode(np.ldexp(blk, -e[:, None]))
+    codes = np.where(finite[:, None], codes, E4M3_NAN).astype(np.uint8).reshape(nb * GROUP, d)[:n]
+    sbytes = np.where(finite, e + E8M0_BIAS, E8M0_NAN).astype(np.uint8)
+    return codes, e, sbytes
+
+
+def mx_fake_quant_token_blocks(x):
+    """decode(quantise(x)) with token-block scales (mx_quantize_token_blocks)."""
+    codes, e, _ = mx_quantize_token_blocks(x)
+    return np.ldexp(e4m3_decode(codes), np.repeat(e, GROUP)[: codes.shape[0], None])
