@@ -112,7 +112,7 @@ def main():
     import synth
     from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F32, PROFILE_BWD_DKDV, PROFILE_BWD_DQ,
                                         PROFILE_BWD_PREP, PROFILE_FWD, PROFILE_QUANTIZE, load, mx_attn_bwd,
-                                        mx_attn_fwd, mx_profile_kernel, mx_quantize)
+                                        mx_attn_fwd, mx_profile_kernel, mx_quantize, mx_quantize_token_block)
     from block_scaled_mxfp8_amd.flops import attn_flops, visible_pairs
 
     load()
@@ -190,6 +190,8 @@ def main():
     o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=True)
     ms_fwd = kernel_ms(PROFILE_FWD, lambda: mx_attn_fwd(q_row, k_row, v_seq, causal=True))
     ms_quant = kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize(t["q"]), n=3 * args.profile_steps)
+    # the token-block variant of the quantiser (same bytes; one exponent per 32 tokens x d)
+    ms_quant_tb = kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize_token_block(t["q"]), n=3 * args.profile_steps)
 
     def bwd(mode):
         return lambda: mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=True, dq_mode=mode,
@@ -254,6 +256,7 @@ def main():
         "bwd_f16dq_tflops": round(tflops(f_bwd, bwd_f16["call_ms"]), 2),
         "bwd_f16dq_pct_of_peak": round(100 * tflops(f_bwd, bwd_f16["call_ms"]) / PEAK_MXFP8_TFLOPS, 2),
         "quantize_gbs": round(kernels["quantize"]["gbs"], 1),
+        "quantize_token_block_gbs": round(quant_bytes / (ms_quant_tb * 1e-3) / 1e9, 1),
         "dq_store_read_gbs": None if args.recompute_dq else round(ds_bytes / (bwd_f32["dq_ms"] * 1e-3) / 1e9, 1),
         "kernels_ms": {"attn_fwd": round(ms_fwd, 4), "attn_bwd_dkdv": round(bwd_f32["dkdv_ms"], 4),
                        "attn_bwd_dq_f32": round(bwd_f32["dq_ms"], 4), "attn_bwd_dq_f16": round(bwd_f16["dq_ms"], 4),

@@ -8,6 +8,7 @@ not load the library; the first call does, and raises if it has not been built
 
 Functions mirror the C entry points:
     mx_quantize(x, views=ROW|SEQ, cu_seqlens=None, max_seqlen=None) -> (row QView, seq QView)
+    mx_quantize_token_block(...): the same with one exponent per 32-token block (shared codes).
     mx_attn_fwd(q_row, k_row, v_seq, ...) -> (o, lse)
     mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, ...) -> (dq, dk, dv)
     mx_attn_varlen_fwd / mx_attn_varlen_bwd: the same with cu_seqlens (packed [T, H, d]).
@@ -21,11 +22,11 @@ from ._lib import (MX_VIEW_ROW, MX_VIEW_SEQ, MX_DQ_F32, MX_DQ_F16_BOOST, MXError
                    mx_attn_workspace_size, mx_read_flags, mx_profile_kernel, PROFILE_FWD, PROFILE_BWD_DKDV,
                    PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_DQ, mx_attn_cross_fwd, mx_attn_cross_bwd,
                    mx_attn_cross_workspace_size, mx_rmsnorm_quantize, PROFILE_RMSNORM, mx_gemm_quantize,
-                   PROFILE_GEMM)
+                   PROFILE_GEMM, mx_quantize_token_block)
 
 __all__ = ["MX_VIEW_ROW", "MX_VIEW_SEQ", "MX_DQ_F32", "MX_DQ_F16_BOOST", "MXError", "QView", "lib_path", "load",
            "mx_abi_version", "mx_attn_bwd", "mx_attn_fwd", "mx_attn_varlen_bwd", "mx_attn_varlen_fwd", "mx_quantize",
            "mx_attn_workspace_size", "mx_read_flags", "mx_profile_kernel", "PROFILE_FWD", "PROFILE_BWD_DKDV",
            "PROFILE_QUANTIZE", "PROFILE_BWD_PREP", "PROFILE_BWD_DQ", "mx_attn_cross_fwd", "mx_attn_cross_bwd",
            "mx_attn_cross_workspace_size", "mx_rmsnorm_quantize", "PROFILE_RMSNORM", "mx_gemm_quantize",
-           "PROFILE_GEMM"]
+           "PROFILE_GEMM", "mx_quantize_token_block"]

@@ -66,6 +66,8 @@ def load():
     lib.mx_quantize.argtypes = [ctypes.POINTER(_Seq), I32, I32, P, I32, I32, ctypes.POINTER(_QView),
                                 ctypes.POINTER(_QView), P]
     lib.mx_quantize.restype = I32
+    lib.mx_quantize_token_block.argtypes = lib.mx_quantize.argtypes
+    lib.mx_quantize_token_block.restype = I32
     lib.mx_rmsnorm_quantize.argtypes = [P, P, I32, I64, I32, ctypes.c_float, I32, ctypes.POINTER(_QView),
                                         ctypes.POINTER(_QView), P]
     lib.mx_rmsnorm_quantize.restype = I32
@@ -204,6 +206,16 @@ def _seq_view_shapes(shape, seq, cu_seqlens):
 
 def mx_quantize(x, views=MX_VIEW_ROW | MX_VIEW_SEQ, cu_seqlens=None, max_seqlen=None):
     """Quantise x ([B,H,L,d] or packed [T,H,d], fp32/bf16) -> (row QView or None, seq QView or None)."""
+    return _quantize(x, views, cu_seqlens, max_seqlen, "mx_quantize")
+
+
+def mx_quantize_token_block(x, views=MX_VIEW_ROW | MX_VIEW_SEQ, cu_seqlens=None, max_seqlen=None):
+    """mx_quantize with one exponent per 32-token block x all channels of a head (the views then
+    share every code) -> (row QView or None, seq QView or None)."""
+    return _quantize(x, views, cu_seqlens, max_seqlen, "mx_quantize_token_block")
+
+
+def _quantize(x, views, cu_seqlens, max_seqlen, name):
     lib = load()
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous device tensor")
@@ -225,9 +237,9 @@ def mx_quantize(x, views=MX_VIEW_ROW | MX_VIEW_SEQ, cu_seqlens=None, max_seqlen=
     for v, view, what in ((row, MX_VIEW_ROW, "row view"), (seqv, MX_VIEW_SEQ, "seq view")):
         if v is not None:
             _check_view(lib, v, seq, heads, d, view, what)
-    st = lib.mx_quantize(ctypes.byref(seq), heads, d, x.data_ptr(), _dtype_code(x.dtype), views, ctypes.byref(rv),
-                         ctypes.byref(sv), _stream())
-    _check(st, "mx_quantize")
+    st = getattr(lib, name)(ctypes.byref(seq), heads, d, x.data_ptr(), _dtype_code(x.dtype), views, ctypes.byref(rv),
+                            ctypes.byref(sv), _stream())
+    _check(st, name)
     return row, seqv
 
 

@@ -12,6 +12,7 @@ struct QuantizeParams {
   int heads;
   int head_dim;
   bool f32;              // input dtype: fp32 (else bf16)
+  bool token_block;      // one exponent per 32-token block x all channels (else per-axis groups)
   const void* x;
   uint8_t* row_codes;    // nullptr: ROW view not wanted
   uint8_t* row_scales;

@@ -207,8 +207,8 @@ ProfileHook& profile_hook() {
 
 extern "C" {
 
-mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x, mx_dtype dtype, int32_t views,
-                      mx_qview* row_out, mx_qview* seq_out, void* stream) {
+static mx_status quantize_impl(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x, mx_dtype dtype,
+                               int32_t views, mx_qview* row_out, mx_qview* seq_out, void* stream, bool token_block) {
   mx::Geom g;
   if (!make_geom(seq, &g) || heads < 1 || !x) return MX_E_ARG;
   if (dtype != MX_F32 && dtype != MX_BF16) return MX_E_ARG;
@@ -220,6 +220,7 @@ mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const 
   p.heads = heads;
   p.head_dim = head_dim;
   p.f32 = dtype == MX_F32;
+  p.token_block = token_block;
   p.x = x;
   if (views & MX_VIEW_ROW) {
     if (!row_out || check_view(*row_out) != MX_OK) return MX_E_ARG;
@@ -236,6 +237,16 @@ mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const 
   const hipError_t err = mx::launch_quantize(p, (hipStream_t)stream);
   mx::profile_end(slot, (hipStream_t)stream);
   return err == hipSuccess ? MX_OK : MX_E_DEVICE;
+}
+
+mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x, mx_dtype dtype, int32_t views,
+                      mx_qview* row_out, mx_qview* seq_out, void* stream) {
+  return quantize_impl(seq, heads, head_dim, x, dtype, views, row_out, seq_out, stream, false);
+}
+
+mx_status mx_quantize_token_block(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x, mx_dtype dtype,
+                                  int32_t views, mx_qview* row_out, mx_qview* seq_out, void* stream) {
+  return quantize_impl(seq, heads, head_dim, x, dtype, views, row_out, seq_out, stream, true);
 }
 
 mx_status mx_rmsnorm_quantize(const void* x, const void* gamma, mx_dtype dtype, int64_t rows, int32_t n, float eps,

@@ -10,13 +10,19 @@
 // (groups of 32 channels of a token) straight from registers and the SEQ view (groups of
 // 32 tokens of a channel) after a transpose through LDS. The kernel is HBM-bound:
 // 2 B read + 2 x (1 + 1/32) B written per bf16 element.
+//
+// Token-block scales (kBlock; FLAMIA notes, section 3): the workgroup's tile IS one token
+// block (32 consecutive tokens of a sequence or document x all d channels of a head), so its
+// single exponent comes from a workgroup max-abs (a wave max, then the waves' maxima through
+// LDS) and both views use it for every group of the block: the two views then hold the same
+// code for every element.
 #include "mx_device.h"
 #include "mx_internal.h"
 #include "mx_layout.h"
 
 namespace mx {
 
-template <int D, bool kF32>
+template <int D, bool kF32, bool kBlock>
 __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
   constexpr int TPT = D / 16;  // threads per token (16 channels each)
   const int tid = threadIdx.x;
@@ -79,12 +85,29 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
     for (int i = 0; i < 16; i++) v[i] = 0.f;
   }
 
+  // ---- token block: the largest magnitude bits of the whole tile (NaN/inf rank highest) ----
+  uint32_t blk_am = 0;
+  if (kBlock) {
+    __shared__ uint32_t red[2 * D / 64];
+#pragma unroll
+    for (int i = 0; i < 16; i++) blk_am = max(blk_am, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    blk_am = wave_max_bits(blk_am);
+    if ((tid & 63) == 0) red[tid >> 6] = blk_am;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 2 * D / 64; w++) blk_am = max(blk_am, red[w]);
+  }
+
   // ---- ROW view: 32 channels of one token = this thread's 16 + the neighbour's 16 ----
   if (p.row_codes) {
     uint32_t am = 0;
+    if (kBlock) {
+      am = blk_am;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 16; i++) am = max(am, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+      for (int i = 0; i < 16; i++) am = max(am, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+      am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+    }
     const bool nonfinite = am >= kInfBits;
     const int e = scale_exp_from_bits(nonfinite ? 0u : am);
     uint32_t w[4];
@@ -98,7 +121,7 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
       *reinterpret_cast<v4i*>(p.row_codes + e0) = out;
       if ((cb & 1) == 0) p.row_scales[e0 >> 5] = nonfinite ? 0xFF : (uint8_t)(e + 127);
     }
-    if (p.o != nullptr) {
+    if (!kBlock && p.o != nullptr) {
       // Backward preprocessing (FLAMIA notes section 5, Algorithm 1 step 09; the same G view
       // feeds D and dP): D = sum_c G_row~ * O with O as saved, in fp32.
       float part = 0.f;
@@ -160,9 +183,13 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
     b[4 + i] = tile[16 * hf + 12 + i][c];
   }
   uint32_t am = 0;
+  if (kBlock) {
+    am = blk_am;
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; i++) am = max(am, max(__float_as_uint(a[i]) & 0x7FFFFFFFu, __float_as_uint(b[i]) & 0x7FFFFFFFu));
-  am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+    for (int i = 0; i < 8; i++) am = max(am, max(__float_as_uint(a[i]) & 0x7FFFFFFFu, __float_as_uint(b[i]) & 0x7FFFFFFFu));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+  }
   const bool nonfinite = am >= kInfBits;
   const int e = scale_exp_from_bits(nonfinite ? 0u : am);
   uint32_t wa0, wa1, wb0, wb1;
@@ -182,16 +209,22 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
   if (hf == 0) p.seq_scales[grow * D + c] = nonfinite ? 0xFF : (uint8_t)(e + 127);
 }
 
+template <bool kBlock>
+static void launch_quantize_t(const QuantizeParams& p, dim3 grid, hipStream_t stream) {
+  if (p.head_dim == 128) {
+    if (p.f32) hipLaunchKernelGGL((quantize_kernel<128, true, kBlock>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((quantize_kernel<128, false, kBlock>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (p.f32) hipLaunchKernelGGL((quantize_kernel<64, true, kBlock>), grid, dim3(128), 0, stream, p);
+    else hipLaunchKernelGGL((quantize_kernel<64, false, kBlock>), grid, dim3(128), 0, stream, p);
+  }
+}
+
 hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream) {
   const Geom& g = p.geom;
   dim3 grid(g.gseq, p.heads, packed(g) ? 1 : g.batch);
-  if (p.head_dim == 128) {
-    if (p.f32) hipLaunchKernelGGL((quantize_kernel<128, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((quantize_kernel<128, false>), grid, dim3(256), 0, stream, p);
-  } else {
-    if (p.f32) hipLaunchKernelGGL((quantize_kernel<64, true>), grid, dim3(128), 0, stream, p);
-    else hipLaunchKernelGGL((quantize_kernel<64, false>), grid, dim3(128), 0, stream, p);
-  }
+  if (p.token_block) launch_quantize_t<true>(p, grid, stream);
+  else launch_quantize_t<false>(p, grid, stream);
   return hipGetLastError();
 }
 

@@ -117,6 +117,19 @@ typedef struct {
 mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x, mx_dtype dtype,
                       int32_t views, mx_qview* row_out, mx_qview* seq_out, void* stream);
 
+/* Token-block variant of mx_quantize (FLAMIA notes, section 3: the scale is made a token
+ * block so that one code set serves both contraction axes). Same arguments, layouts and
+ * errors as mx_quantize, but one exponent per token block: 32 consecutive tokens of a
+ * sequence or document (blocks start at each sequence or document start; the last may be
+ * partial) x all head_dim channels of one head, the smallest e with amax * 2^-e <= 448 over
+ * the whole block. Every ROW and SEQ group of the block carries that exponent, so both views
+ * hold the same code for every element. A block holding a NaN or an infinity gets scale 0xFF
+ * and codes 0x7F throughout. The views feed mx_attn_fwd / mx_attn_bwd (and their varlen and
+ * cross forms) unchanged. */
+mx_status mx_quantize_token_block(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x,
+                                  mx_dtype dtype, int32_t views, mx_qview* row_out, mx_qview* seq_out,
+                                  void* stream);
+
 /* Fused RMSNorm + quantise, the normalisation producer of Meta's MXFP8 write-up (section
  * "Quantisation inside the producers": the kernel that reads the activations writes them as
  * FP8 in both scale layouts, so no consumer quantises again). For each row m of x

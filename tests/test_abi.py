@@ -265,3 +265,17 @@ def test_gemm_quantize_validation(lib):
     nul = _lib._QView(None, None)
     assert call(m=0, a=nul, b=nul, row=None, seq=None) == _lib.MX_OK
     assert call(m=0, k=96) == _lib.MX_E_ARG                          # the scalars are still checked
+
+
+def test_token_block_quantize_validation(lib):
+    # the token-block entry point validates exactly like mx_quantize
+    s, v = _seq(), _lib._QView(FAKE, FAKE)
+    f = lib.mx_quantize_token_block
+    assert f(None, 1, 128, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(s), 1, 128, None, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(s), 0, 128, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(s), 1, 128, FAKE, 7, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(s), 1, 128, FAKE + 2, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(s), 1, 96, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_UNSUPPORTED
+    assert f(ctypes.byref(s), 1, 128, FAKE, 1, 4, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(s), 1, 128, FAKE, 1, 1, None, ctypes.byref(v), None) == _lib.MX_E_ARG
