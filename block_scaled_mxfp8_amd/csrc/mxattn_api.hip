@@ -286,6 +286,9 @@ mx_status mx_gemm_quantize(mx_qview a_row, mx_qview b_row, int64_t m, int32_t n,
   if (m < 0 || n < 32 || n % 32 != 0 || k < 64 || k % 64 != 0) return MX_E_ARG;
   if (views < 1 || views > 3) return MX_E_ARG;
   if (m > 0x7FFFFFFF || n > (1 << 24) || k > (1 << 23)) return MX_E_UNSUPPORTED;
+  // one 512-thread workgroup per 256 x 256 tile: the grid's work-items must stay below 2^32
+  // (this also keeps m + 255 and the tile count inside 32-bit arithmetic in the kernel)
+  if (((m + 255) / 256) * (int64_t)((n + 255) / 256) * 512 >= ((int64_t)1 << 32)) return MX_E_UNSUPPORTED;
   if (m == 0) return MX_OK;             // nothing is read or written: every pointer may be NULL
   if (check_view(a_row) != MX_OK || check_view(b_row) != MX_OK) return MX_E_ARG;
   mx::GemmQuantParams p = {};

@@ -163,7 +163,8 @@ mx_status mx_rmsnorm_quantize(const void* x, const void* gamma, mx_dtype dtype, 
  *            partial last group count as zeros and hold code 0.
  * i.e. the views mx_quantize gives for an [1, 1, m, n] tensor. views = MX_VIEW_ROW |
  * MX_VIEW_SEQ; the unused output may be NULL. k: a multiple of 64, 64..2^23; n: a multiple of
- * 32, 32..2^24; m: 0..2^31 - 1 (0 launches nothing and reads no pointer). Code pointers 16-byte
+ * 32, 32..2^24; m: 0..2^31 - 1 (0 launches nothing and reads no pointer); and at most 2^23 - 1
+ * tiles of 256 x 256 (ceil(m/256) * ceil(n/256)), else MX_E_UNSUPPORTED. Code pointers 16-byte
  * aligned, scale pointers 4-byte aligned (MX_E_ARG otherwise). A group whose FP32 sum is not
  * finite (an overflow of the accumulation) gets scale 0xFF and codes 0x7F. The result depends
  * only on the operands (fixed accumulation order; no atomics). */

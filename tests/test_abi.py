@@ -260,6 +260,8 @@ def test_gemm_quantize_validation(lib):
     assert call(k=1 << 24) == _lib.MX_E_UNSUPPORTED
     assert call(n=1 << 25) == _lib.MX_E_UNSUPPORTED
     assert call(m=1 << 31) == _lib.MX_E_UNSUPPORTED
+    assert call(m=(1 << 31) - 1, n=32) == _lib.MX_E_UNSUPPORTED      # 2^23 tiles: grid too large
+    assert call(m=(1 << 23) * 256 - 256, n=32, a=_lib._QView(None, None)) == _lib.MX_E_ARG   # largest grid passes the size check
     assert call(row=None) == _lib.MX_E_ARG                           # ROW view asked for, none given
     assert call(views=2, seq=ctypes.byref(_lib._QView(None, FAKE))) == _lib.MX_E_ARG
     nul = _lib._QView(None, None)
