@@ -82,6 +82,10 @@ def load():
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, _QView, _QView, P, P, P, I32, P, P, P, P]
         f.restype = I32
+    lib.mx_attn_bwd_mx.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, _QView, _QView, P, P, P, I32, P,
+                                   P, P, ctypes.POINTER(_QView), ctypes.POINTER(_QView), ctypes.POINTER(_QView),
+                                   ctypes.POINTER(_QView), P]
+    lib.mx_attn_bwd_mx.restype = I32
     lib.mx_attn_cross_fwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Seq), _QView, _QView, _QView, P, P, P]
     lib.mx_attn_cross_fwd.restype = I32
     lib.mx_attn_cross_bwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Seq), _QView, _QView, _QView, _QView,
@@ -379,7 +383,7 @@ def mx_attn_workspace_size(q_shape, cu_seqlens=None, max_seqlen=None, heads_kv=N
 
 
 def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype, dq_mode, cu_seqlens,
-         max_seqlen, workspace, deterministic=False, ds_store=True, cross=None):
+         max_seqlen, workspace, deterministic=False, ds_store=True, cross=None, mx_views=0):
     lib = load()
     qs, ks = tuple(q_row.codes.shape), tuple(k_row.codes.shape)
     desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode, deterministic, cross)
@@ -415,6 +419,21 @@ def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_sca
         raise ValueError("o must have out_dtype and lse float32")
     args = (_qv(q_row), _qv(q_seq), _qv(k_row), _qv(k_seq), _qv(v_row), o.data_ptr(), lse.data_ptr(), g.data_ptr(),
             _dtype_code(g.dtype), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream())
+    if name == "mx_attn_bwd_mx":
+        views = []
+        for tensor_views in range(2):   # dK, dV
+            row = seqv = None
+            if mx_views & MX_VIEW_ROW:
+                row = QView(torch.empty(ks, dtype=torch.uint8, device=dev),
+                            torch.empty(ks[:-1] + (desc.head_dim // 32,), dtype=torch.uint8, device=dev))
+            if mx_views & MX_VIEW_SEQ:
+                cs, ss = _seq_view_shapes(ks, kseq, cu_seqlens)
+                seqv = QView(torch.empty(cs, dtype=torch.uint8, device=dev), torch.empty(ss, dtype=torch.uint8, device=dev))
+            views += [row, seqv]
+        ptrs = [ctypes.byref(_qv(v)) if v is not None else None for v in views]
+        st = lib.mx_attn_bwd_mx(ctypes.byref(desc), *args[:-1], *ptrs, args[-1])
+        _check(st, name)
+        return dq, dk, dv, workspace, (views[0], views[1]), (views[2], views[3])
     if seq_k is None:
         st = getattr(lib, name)(ctypes.byref(desc), *args)
     else:
@@ -432,6 +451,16 @@ def mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal=True, softm
     the minimum. A given workspace selects the store by its size (mx_attn_workspace_size)."""
     return _bwd("mx_attn_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype,
                 dq_mode, cu_seqlens, max_seqlen, workspace, deterministic, ds_store)
+
+
+def mx_attn_bwd_mx(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, views=MX_VIEW_ROW | MX_VIEW_SEQ, causal=True,
+                   softmax_scale=0.0, out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32, cu_seqlens=None, max_seqlen=None,
+                   workspace=None, ds_store=True):
+    """mx_attn_bwd that also returns dK and dV as MX views formed from their FP32 values ->
+    (dq, dk, dv, workspace, (dk_row, dk_seq), (dv_row, dv_seq)); a view not asked for is None.
+    Batched, or packed with cu_seqlens."""
+    return _bwd("mx_attn_bwd_mx", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype,
+                dq_mode, cu_seqlens, max_seqlen, workspace, False, ds_store, mx_views=views)
 
 
 def mx_attn_varlen_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, cu_seqlens, max_seqlen=None, causal=True,

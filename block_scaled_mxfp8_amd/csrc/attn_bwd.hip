@@ -442,7 +442,80 @@ __device__ __forceinline__ v4i ds_read_tr8_pair(const uint8_t* lds) {
 // kStore: the producer waves also write each dS block to the code store, transposed into the
 // dQ product's operand order: lane l's 16 bytes at 16 l of the block's 1024 bytes (read back
 // by the dQ pass instead of rebuilding dS).
-template <int D, bool kPacked, bool kStore>
+// The ROW and SEQ MX views of one key group's dK or dV (Meta write-up, "Quantisation inside
+// the producers": the backward hands the next GEMMs FP8 gradients in both scale layouts), from
+// the accumulator wave's FP32 values acc * mul: lane (key kw + l32, hh) holds channels
+// 32 t + 8 b4 + 4 hh + i. ROW groups (32 channels of a key) are this lane and lane ^ 32; the
+// SEQ groups (32 keys of a channel) go through the wave-private LDS tile T [32 keys][D + 4]
+// (the pad spreads a column's reads over all banks): lane c reads channel c (and c + 64). Keys
+// past the end count as zeros and are not stored; a group holding a non-finite value gets
+// scale 0xFF and codes 0x7F, as in mx_quantize.
+template <int D, bool kPacked>
+__device__ __forceinline__ void dkv_mx_views(const BwdParams& p, const KvWork& w, int kw, const v16f* acc, float mul,
+                                             float* T, uint8_t* rc, uint8_t* rs, uint8_t* sc, uint8_t* ss) {
+  constexpr int NCT = D / 32, TP = D + 4;
+  const Geom& gk = p.geom_k;
+  const int lane = __lane_id();
+  const int hh = lane >> 5, l32 = lane & 31;
+  const bool kvalid = kw + l32 < w.nk;
+  const long long sbase_k = kPacked ? (long long)w.doc_k : (long long)w.s;
+  const long long base = elem_offset_k<kPacked>(gk, p.heads_kv, D, sbase_k, w.hkv, kw + l32, 0);
+#pragma unroll
+  for (int t = 0; t < NCT; t++) {
+    float x[16];
+#pragma unroll
+    for (int v = 0; v < 16; v++) x[v] = kvalid ? acc[t][v] * mul : 0.f;
+    if (rc) {
+      uint32_t am = 0;
+#pragma unroll
+      for (int v = 0; v < 16; v++) am = max(am, __float_as_uint(x[v]) & 0x7FFFFFFFu);
+      am = max(am, __float_as_uint(swap32(__uint_as_float(am))));
+      const bool nf = am >= kInfBits;
+      const int e = scale_exp_from_bits(nf ? 0u : am);
+      const float s = exp2_scale(e);
+      if (kvalid) {
+#pragma unroll
+        for (int b4 = 0; b4 < 4; b4++)
+          *reinterpret_cast<uint32_t*>(rc + base + 32 * t + 8 * b4 + 4 * hh) =
+              nf ? 0x7F7F7F7Fu : pack4_e4m3_scaled(x[4 * b4], x[4 * b4 + 1], x[4 * b4 + 2], x[4 * b4 + 3], s);
+        if (hh == 0) rs[(base + 32 * t) >> 5] = nf ? 0xFF : (uint8_t)(e + 127);
+      }
+    }
+    if (sc) {
+#pragma unroll
+      for (int b4 = 0; b4 < 4; b4++)
+        *reinterpret_cast<v4f*>(&T[l32 * TP + 32 * t + 8 * b4 + 4 * hh]) =
+            v4f{x[4 * b4], x[4 * b4 + 1], x[4 * b4 + 2], x[4 * b4 + 3]};
+    }
+  }
+  if (!sc) return;
+  const long long grow = seq_group_row_k<kPacked>(gk, p.heads_kv, w.s, w.hkv, w.doc_k, kw >> 5);
+#pragma unroll
+  for (int c = lane; c < D; c += 64) {
+    float y[32];
+    uint32_t am = 0;
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
+      y[k] = T[k * TP + c];
+      am = max(am, __float_as_uint(y[k]) & 0x7FFFFFFFu);
+    }
+    const bool nf = am >= kInfBits;
+    const int e = scale_exp_from_bits(nf ? 0u : am);
+    const float s = exp2_scale(e);
+    uint32_t wd[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++)   // byte 4q + j of the group holds key seq_tok(4q + j)
+      wd[q] = nf ? 0x7F7F7F7Fu
+                 : pack4_e4m3_scaled(y[seq_tok(4 * q)], y[seq_tok(4 * q + 1)], y[seq_tok(4 * q + 2)],
+                                     y[seq_tok(4 * q + 3)], s);
+    uint8_t* dst = sc + (grow * D + c) * 32;
+    *reinterpret_cast<v4i*>(dst) = v4i{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+    *reinterpret_cast<v4i*>(dst + 16) = v4i{(int)wd[4], (int)wd[5], (int)wd[6], (int)wd[7]};
+    ss[grow * D + c] = nf ? 0xFF : (uint8_t)(e + 127);
+  }
+}
+
+template <int D, bool kPacked, bool kStore, bool kMxOut = false>
 __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ DkvShared<D> sm;
   const KvWork w = decode_kv<kPacked>(p);
@@ -633,6 +706,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         }
       }
     }
+  }
+  if (kMxOut && kw < w.nk) {
+    // MX views of dK and dV; every barrier has passed, so the shared memory is this wave's
+    static_assert(kWaves * 32 * (D + 4) * 4 <= sizeof(DkvShared<D>), "transpose tiles fit");
+    float* T = reinterpret_cast<float*>(&sm) + (wave - kDkvProducers) * 32 * (D + 4);
+    dkv_mx_views<D, kPacked>(p, w, kw, dk, p.scale, T, p.dkr_codes, p.dkr_scales, p.dks_codes, p.dks_scales);
+    dkv_mx_views<D, kPacked>(p, w, kw, dv, 1.f, T, p.dvr_codes, p.dvr_scales, p.dvs_codes, p.dvs_scales);
   }
 }
 
@@ -1108,8 +1188,17 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
     gq = dim3((unsigned)((g.max_seqlen + kBlockQ - 1) / kBlockQ), (unsigned)p.heads_q, (unsigned)g.n_docs);
   }
   const bool store = p.ds_codes != nullptr;
+  const bool mx = p.dkr_codes || p.dks_codes || p.dvr_codes || p.dvs_codes;
   int slot = profile_begin(kProfBwdKV, stream);
-  if (packed(g)) {
+  if (mx) {
+    if (packed(g)) {
+      if (store) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, true, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, false, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+    } else {
+      if (store) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, true, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, false, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+    }
+  } else if (packed(g)) {
     if (store) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, true>), gkv, dim3(kDkvThreads), 0, stream, p);
     else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, false>), gkv, dim3(kDkvThreads), 0, stream, p);
   } else {

@@ -70,6 +70,10 @@ struct BwdParams {
   // dS code store (nullptr: dQ recomputes dS instead); layout in mx_layout.h DsStore
   uint8_t* ds_codes; uint8_t* ds_exps;
   DsStore ds;
+  // optional MX views of dK and dV (the keys' geometry, layouts of mx_quantize), formed from
+  // the FP32 accumulators; all nullptr: none
+  uint8_t* dkr_codes; uint8_t* dkr_scales; uint8_t* dks_codes; uint8_t* dks_scales;
+  uint8_t* dvr_codes; uint8_t* dvr_scales; uint8_t* dvs_codes; uint8_t* dvs_scales;
 };
 
 hipError_t launch_quantize(const QuantizeParams& p, hipStream_t stream);

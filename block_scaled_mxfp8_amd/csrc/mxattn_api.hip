@@ -147,7 +147,7 @@ mx_status fwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
 
 mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
                    mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* gptr, mx_dtype g_dtype,
-                   void* dq, void* dk, void* dv, void* stream, bool need_packed) {
+                   void* dq, void* dk, void* dv, void* stream, bool need_packed, const mx_qview* mx_out = nullptr) {
   mx::Geom g, gk;
   mx_status st = check_desc(desc, &g);
   if (st != MX_OK) return st;
@@ -191,6 +191,18 @@ mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
     p.ds_codes = ws + w.ds_codes;
     p.ds_exps = ws + w.ds_exps;
     p.ds = w.ds;
+  }
+  if (mx_out) {   // dK ROW, dK SEQ, dV ROW, dV SEQ; a view with null codes is not wanted
+    const mx_qview& a = mx_out[0];
+    const mx_qview& b = mx_out[1];
+    const mx_qview& c = mx_out[2];
+    const mx_qview& d = mx_out[3];
+    for (int i = 0; i < 4; i++)
+      if (mx_out[i].codes && check_view(mx_out[i]) != MX_OK) return MX_E_ARG;
+    p.dkr_codes = a.codes; p.dkr_scales = a.codes ? a.scales : nullptr;
+    p.dks_codes = b.codes; p.dks_scales = b.codes ? b.scales : nullptr;
+    p.dvr_codes = c.codes; p.dvr_scales = c.codes ? c.scales : nullptr;
+    p.dvs_codes = d.codes; p.dvs_scales = d.codes ? d.scales : nullptr;
   }
   if (g.total == 0) return MX_OK;
   return mx::launch_attn_bwd(p, (hipStream_t)stream) == hipSuccess ? MX_OK : MX_E_DEVICE;
@@ -341,6 +353,17 @@ mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
                              mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                              mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream) {
   return bwd_impl(desc, nullptr, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, true);
+}
+
+mx_status mx_attn_bwd_mx(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row, mx_qview k_seq,
+                         mx_qview v_row, const void* o, const float* lse, const void* g, mx_dtype g_dtype, void* dq,
+                         void* dk, void* dv, const mx_qview* dk_row, const mx_qview* dk_seq, const mx_qview* dv_row,
+                         const mx_qview* dv_seq, void* stream) {
+  const mx_qview none = {nullptr, nullptr};
+  const mx_qview out[4] = {dk_row ? *dk_row : none, dk_seq ? *dk_seq : none, dv_row ? *dv_row : none,
+                           dv_seq ? *dv_seq : none};
+  return bwd_impl(desc, nullptr, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, false,
+                  out);
 }
 
 mx_status mx_attn_cross_bwd(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview q_seq,

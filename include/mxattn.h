@@ -194,6 +194,21 @@ mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
                              mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                              mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
 
+/* mx_attn_bwd (batched, or packed when desc->seq.cu_seqlens is set: one entry point for both)
+ * that also hands out dK and dV as MX views, formed inside the dK/dV kernel from its FP32
+ * results (dK = alpha * accumulator, dV = accumulator) before they are rounded to out_dtype:
+ * the quantised gradients of Meta's write-up ("Quantisation inside the producers") that feed
+ * the next GEMMs. Each of dk_row, dk_seq, dv_row, dv_seq is NULL, or a view (codes NULL: not
+ * wanted) with the layout mx_quantize gives for a tensor of K's geometry (ROW: codes like K,
+ * scales [..., d/32]; SEQ: groups of 32 keys of a sequence or document). The group rule is
+ * mx_quantize's, so each view equals mx_quantize of the FP32 dK / dV (what out_dtype = MX_F32
+ * stores) bit for bit. dQ, dK, dV and every other argument and error as in mx_attn_bwd.
+ * Self-attention only (no separate key geometry). */
+mx_status mx_attn_bwd_mx(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row, mx_qview k_seq,
+                         mx_qview v_row, const void* o, const float* lse, const void* g, mx_dtype g_dtype, void* dq,
+                         void* dk, void* dv, const mx_qview* dk_row, const mx_qview* dk_seq, const mx_qview* dv_row,
+                         const mx_qview* dv_seq, void* stream);
+
 /* Cross-attention (jagged or batched): the queries follow desc->seq, the keys and values the
  * geometry *seq_k (the pages' production shape: a fixed number of seed queries per document
  * against jagged key/value sequences; Meta write-up, "what the production model looks like",

@@ -281,3 +281,14 @@ def test_token_block_quantize_validation(lib):
     assert f(ctypes.byref(s), 1, 96, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_UNSUPPORTED
     assert f(ctypes.byref(s), 1, 128, FAKE, 1, 4, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
     assert f(ctypes.byref(s), 1, 128, FAKE, 1, 1, None, ctypes.byref(v), None) == _lib.MX_E_ARG
+
+
+def test_bwd_mx_validation(lib):
+    # the gradient views are validated like every other view before any launch
+    f = lib.mx_attn_bwd_mx
+    v = _lib._QView(FAKE, FAKE)
+    d = _desc()
+    bad = _lib._QView(FAKE, FAKE + 2)            # scales not 4-byte aligned
+    assert f(ctypes.byref(d), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, ctypes.byref(bad), None, None,
+             None, None) != _lib.MX_OK
+    assert f(None, v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, None, None, None, None) == _lib.MX_E_ARG
