@@ -21,7 +21,7 @@ def _same(a, b, what):
     assert torch.equal(a.scales, b.scales), f"{what}: scales differ"
 
 
-def _run(t, causal, cu=None, maxlen=None, views=MX_VIEW_ROW | MX_VIEW_SEQ, out_dtype=torch.float32):
+def _run(t, causal, cu=None, maxlen=None, views=MX_VIEW_ROW | MX_VIEW_SEQ, out_dtype=torch.float32, ds_store=True):
     kw = dict(cu_seqlens=cu, max_seqlen=maxlen)
     q_row, q_seq = mx_quantize(t["q"], **kw)
     k_row, k_seq = mx_quantize(t["k"], **kw)
@@ -31,15 +31,16 @@ def _run(t, causal, cu=None, maxlen=None, views=MX_VIEW_ROW | MX_VIEW_SEQ, out_d
     else:
         o, lse = mx_attn_varlen_fwd(q_row, k_row, v_seq, cu_seqlens=cu, max_seqlen=maxlen, causal=causal,
                                     out_dtype=out_dtype)
-    ref = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=causal, out_dtype=out_dtype, **kw)
+    ref = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=causal, out_dtype=out_dtype,
+                      ds_store=ds_store, **kw)
     got = mx_attn_bwd_mx(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], views=views, causal=causal,
-                         out_dtype=out_dtype, **kw)
+                         out_dtype=out_dtype, ds_store=ds_store, **kw)
     torch.cuda.synchronize()
     return ref, got
 
 
-def _check(t, causal, cu=None, maxlen=None):
-    ref, got = _run(t, causal, cu, maxlen)
+def _check(t, causal, cu=None, maxlen=None, ds_store=True):
+    ref, got = _run(t, causal, cu, maxlen, ds_store=ds_store)
     dq, dk, dv, _, dkv, dvv = got
     for name, a, b in (("dQ", ref[0], dq), ("dK", ref[1], dk), ("dV", ref[2], dv)):
         assert torch.equal(a, b), f"{name} differs from mx_attn_bwd"
@@ -90,6 +91,13 @@ def test_gradient_views_packed_documents():
     t = {n: to_device(rng.standard_normal((T, H, d)).astype(np.float32), torch.bfloat16) for n in ("q", "k", "v", "g")}
     cud = torch.from_numpy(cu.astype(np.int32)).cuda()
     _check(t, True, cud, max(lengths))
+    _check(t, True, cud, max(lengths), ds_store=False)
+
+
+def test_gradient_views_with_the_minimal_workspace():
+    # the dQ pass rebuilds dS instead of reading stored codes: the other dK/dV kernel instance
+    print("[bwd-mx] minimal workspace", flush=True)
+    _check(_inputs(1, 2, 2, 130, 128, seed=31), True, ds_store=False)
 
 
 def test_single_views():
