@@ -74,3 +74,46 @@ def test_graph_capture_replays_match_eager():
         assert float(junk) == float(junk)
         for name in eager:
             assert _same(eager[name], captured[name]), f"replay {rep}: {name}"
+
+
+def test_graph_capture_of_the_producers_and_gradient_views():
+    # the other entry points are capturable too: RMSNorm + quantise, GEMM + quantise,
+    # token-block quantise and the backward with MX gradient views, replayed against eager
+    from block_scaled_mxfp8_amd import QView, mx_attn_bwd_mx, mx_gemm_quantize, mx_quantize_token_block, \
+        mx_rmsnorm_quantize
+    print("[graph] producers + token-block quantise + backward with gradient views, replay 3x", flush=True)
+    x, gamma = synth.make_norm_inputs(96, 512)
+    xd, gd = to_device(x, torch.bfloat16), to_device(gamma, torch.bfloat16)
+    bc, bs = synth.gemm_operand(288, 512, "b", seed=3)
+    b_row = QView(torch.from_numpy(bc).cuda(), torch.from_numpy(bs).cuda())
+    t = _inputs(1, 2, 2, 300, 128, seed=13)
+
+    def run():
+        a_row, a_seq = mx_rmsnorm_quantize(xd, gd, 1e-6)
+        c_row, c_seq = mx_gemm_quantize(a_row, b_row)
+        q_row, q_seq = mx_quantize_token_block(t["q"])
+        k_row, k_seq = mx_quantize_token_block(t["k"])
+        v_row, v_seq = mx_quantize_token_block(t["v"])
+        o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=True)
+        dq, dk, dv, _, dkv, dvv = mx_attn_bwd_mx(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=True)
+        out = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+        for name, v in (("a_row", a_row), ("a_seq", a_seq), ("c_row", c_row), ("c_seq", c_seq),
+                        ("dk_row", dkv[0]), ("dk_seq", dkv[1]), ("dv_row", dvv[0]), ("dv_seq", dvv[1])):
+            out[name + "_codes"], out[name + "_scales"] = v.codes, v.scales
+        return out
+
+    eager = run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = run()
+    for rep in range(3):
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        for v in captured.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        for name in eager:
+            assert _same(eager[name], captured[name]), f"replay {rep}: {name}"
