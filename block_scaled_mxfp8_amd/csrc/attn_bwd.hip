@@ -1050,6 +1050,10 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const QWork& w, co
                                           v4i (&r)[2], int& e, v16f* dq) {
   constexpr int NCT = D / 32;
   dqds_issue_k<D, kPacked>(p, w, c, kt + 2, nxt);
+  // The kernel's vmcnt wait counts this tile's dS loads as younger than the K tile's LDS-DMA.
+  // Both only read global memory, so without this compiler barrier a scheduler may hoist the
+  // loads above the DMA, and the wait would then pass with the K tile still in flight.
+  asm volatile("" ::: "memory");
   const int g0 = 2 * kt;
   if (kt >= 0 && g0 < c.kb_end) {
     const bool two = g0 + 1 < c.kb_end;
