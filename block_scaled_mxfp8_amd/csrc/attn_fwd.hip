@@ -11,8 +11,12 @@
 // gfx950 mapping.
 //  * One workgroup = 4 waves = 128 queries of one (batch, head) or (document, head); each
 //    wave owns 32 queries. Keys advance in tiles of 64, staged (codes + E8M0 scales) in LDS,
-//    K two tiles ahead and V one tile ahead, two slots each; the loop is unrolled twice, so
-//    slot indices are constants and the score registers alternate without copies.
+//    two slots each; the loop is unrolled twice, so slot indices are constants and the score
+//    and code registers alternate without copies.
+//  * Software pipeline over key tiles: while the softmax of tile j runs on the vector ALU, the
+//    matrix cores compute the scores of tile j + 1 and P V of tile j - 1; the eight products of
+//    a tile are spread through its softmax instructions, because a wave issues in order and a
+//    product occupies the matrix core for 64 cycles.
 //  * Scores are computed transposed, S^T = K Q^T, with V_MFMA_SCALE_F32_32X32X64_F8F6F4:
 //    keys are MFMA rows, queries columns, so every lane holds 16 scores of ONE query for each
 //    32-key half tile, and the query's other 16 keys sit in lane ^ 32. Row and group maxima
@@ -25,7 +29,7 @@
 //    lag only multiplies the O accumulator and l by one common power of two (at most 2^8),
 //    which cancels in O = a / l and LSE = M + log2 l. A 32-key group of one query spans
 //    lanes l and l^32; its exponent is ceil(max S' - M - log2 448) and the codes are
-//    RNE_E4M3(2^(S' - M - e)) by one FMA + one v_exp_f32 + the hardware converter.
+//    RNE_E4M3(p / 2^e), p = 2^(S' - M), by one FMA + one v_exp_f32 + the scaled converter.
 //  * The P codes of a lane (16 keys of half tile 0 in bytes 0-15, 16 keys of half tile 1 in
 //    bytes 16-31) ARE the B operand of O^T += V^T P^T for the same MFMA shape: operand byte j
 //    of lane half h has contraction index 16h + j%16 + 32(j/16), which is exactly how the
@@ -58,8 +62,9 @@ constexpr float kTau = 8.f;           // largest lag of the reference max behind
 //      are swapped when (ch >> 3) & 1 (half_swz), for the same reason.
 //  ks: K ROW scales, one dword per key (its d/32 bytes; at d = 64 the upper half is unused);
 //  vs: V SEQ scales [2 groups][d].
-// K and V tiles have two slots each: K(j) sits in slot j % 2 and is loaded two tiles ahead
-// (the scores of tile j + 1 are computed during tile j), V(j) in slot j % 2, one tile ahead.
+// K and V tiles have two slots each: K(j) sits in slot j % 2 and is loaded during tile j - 2
+// (its scores are computed during tile j - 1), V(j) in slot j % 2, loaded during tile j (P V
+// of tile j runs during tile j + 1).
 template <int D>
 struct FwdSmem {
   alignas(16) uint8_t k[2][kBlockN * D];
@@ -265,15 +270,221 @@ __device__ __forceinline__ void mask_tile(v16f& x, int lim, std::integer_sequenc
   ((x[I] = mask_below<T0 + 8 * (I >> 2) + (I & 3)>(x[I], lim, ninf)), ...);
 }
 
-// Largest of the 16 accumulator values of a lane (depth-3 tree of three-input maxima).
-__device__ __forceinline__ float vmax16(const v16f& x) {
-  const float m0 = fmaxf(fmaxf(x[0], x[1]), x[2]), m1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
-  const float m2 = fmaxf(fmaxf(x[6], x[7]), x[8]), m3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
-  const float m4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
-  return fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), x[15]));
+// Sum of the 16 values of a lane as a depth-4 tree (independent adds for the issue slots
+// between matrix-core instructions).
+__device__ __forceinline__ float vsum16(const v16f& x) {
+  const float a0 = x[0] + x[1], a1 = x[2] + x[3], a2 = x[4] + x[5], a3 = x[6] + x[7];
+  const float a4 = x[8] + x[9], a5 = x[10] + x[11], a6 = x[12] + x[13], a7 = x[14] + x[15];
+  return ((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7));
 }
 
-template <int D, bool kPacked>
+// O^T += V^T P^T for the V tile in slot st: channels are MFMA rows, the wave's 32 queries
+// columns, the 64 keys of the tile the contraction (pop: the lane's 32 P codes, psc: their
+// E8M0 byte).
+template <int D>
+__device__ __forceinline__ void pv(const FwdSmem<D>& sm, int st, const v8i& pop, int psc, v16f* oacc) {
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int t = 0; t < D / 32; t++) {
+    const int ch = t * 32 + l32;
+    const v4i a = *reinterpret_cast<const v4i*>(&sm.v[st][(0 * D + ch) * 32 + (half_swz(ch, hh) << 4)]);
+    const v4i b = *reinterpret_cast<const v4i*>(&sm.v[st][(1 * D + ch) * 32 + (half_swz(ch, hh) << 4)]);
+    const int vsc = sm.vs[st][hh * D + ch];
+    oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), pop, oacc[t], 0, 0, 0, vsc, 0, psc);
+  }
+}
+
+// c = alpha log2 e for the default alpha = d^-1/2, as a compile-time constant: the exponent
+// argument S' - M is then one multiply-add with a literal operand (a two-source instruction,
+// which issues faster than a three-register FMA on gfx950).
+template <int D>
+constexpr float default_c() { return (D == 128 ? 0.08838834764831845f : 0.125f) * kLog2e; }
+
+// Online softmax of one key tile for the lane's query: scores cur (raw accumulator units,
+// 16 keys of each 32-key half tile), reference max M and sum l updated, P codes and their
+// E8M0 byte out. Returns the factor 2^(M_old - M_new) the O accumulator must be scaled by
+// (1 unless the reference max moved).
+//  * M is an integer (base 2) and moves only when the tile's row max exceeds it by more than
+//    kTau; p = 2^(S' - M) <= 2^kTau.
+//  * The P group of a query is 32 consecutive keys: this lane's 16 and lane ^ 32's 16. Its
+//    exponent is ceil(max S' - M - log2 448) (the E8M0 rule applied to max p = 2^(max S' - M),
+//    FLAMIA notes section 7), and the codes are RNE(p / 2^e) by the scaled converter.
+//  * l is summed from the unquantised p.
+template <bool kMask, bool kLit, int D>
+__device__ __forceinline__ float softmax_tile(v16f (&cur)[2], float c_rt, int lim, float& M, float& lsum, v8i& pop,
+                                              int& psc) {
+  const float c = kLit ? default_c<D>() : c_rt;
+  if (kMask) {
+    mask_tile<0>(cur[0], lim, std::make_integer_sequence<int, 16>{});
+    mask_tile<32>(cur[1], lim, std::make_integer_sequence<int, 16>{});
+  }
+  const float gm0 = max_halves(max16_raw(cur[0])), gm1 = max_halves(max16_raw(cur[1]));
+  const float mt = ceilf(fmaxf(gm0, gm1) * c);
+  const bool up = mt > M + kTau;
+  const float f = up ? __builtin_amdgcn_exp2f(M - mt) : 1.f;   // power of two (0 when M = -inf)
+  M = up ? mt : M;
+  // a row without any visible key so far keeps M = -inf: its p are 0 (S' = -inf)
+  const float nm = kMask ? (M > -INFINITY ? -M : 0.f) : -M;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    cur[0][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[0][i], c, nm));
+    cur[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[1][i], c, nm));
+  }
+  lsum = __builtin_fmaf(lsum, f, vsum16(cur[0]) + vsum16(cur[1]));
+  const float nmq = nm - kLog2_448;
+  const float e0 = fminf(fmaxf(ceilf(__builtin_fmaf(gm0, c, nmq)), -127.f), 127.f);
+  const float e1 = fminf(fmaxf(ceilf(__builtin_fmaf(gm1, c, nmq)), -127.f), 127.f);
+  const int i0 = (int)e0, i1 = (int)e1;
+  const float s0 = exp2_scale(i0), s1 = exp2_scale(i1);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    pop[j] = (int)pack4_e4m3_scaled(cur[0][4 * j], cur[0][4 * j + 1], cur[0][4 * j + 2], cur[0][4 * j + 3], s0);
+    pop[4 + j] = (int)pack4_e4m3_scaled(cur[1][4 * j], cur[1][4 * j + 1], cur[1][4 * j + 2], cur[1][4 * j + 3], s1);
+  }
+  psc = ((threadIdx.x & 32) ? i1 : i0) + 127;
+  return f;
+}
+
+// The interleaved tile of the common case (every lane sees all keys of the tile): the tile's
+// matrix-core products -- P V of the previous tile (d/32 of them), then the scores of the next
+// tile (2 per 64 channels) -- are placed one by one between eight chunks of this tile's softmax,
+// with scheduling fences between the chunks so that the compiler keeps that order: a product
+// occupies the matrix core for 64 cycles and the wave issues in order, so each product is
+// followed by a chunk of vector work long enough to hide it. A product's LDS operand reads are
+// issued right after the previous product, a chunk ahead of their use.
+// Chunks: 0 the two groups' max trees; 1 the lane exchange, reference max, rescale factor;
+// 2-5 eight exponent arguments and exp2 each; 6 the sums and the group exponents; 7 the codes.
+template <int D, bool kLit>
+__device__ __forceinline__ float whole_tile(const FwdSmem<D>& sm, int kst, int vst, const v8i* qop, const int* qsc,
+                                            v16f (&cur)[2], v16f (&nxt)[2], const v8i& pprev, int pscprev, v16f* oacc,
+                                            float c_rt, float& M, float& lsum, v8i& pop, int& psc) {
+  constexpr int NPV = D / 32, NS = D / 64, NP = NPV + 2 * NS;
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5, l32 = lane & 31;
+  constexpr int NCH = D / 16;
+  const float c = kLit ? default_c<D>() : c_rt;
+  // operands of product i: P V of channel block i (i < NPV), else the scores of half tile
+  // T = (i - NPV) % 2 over channel step s = (i - NPV) / 2
+  uint32_t ksw0 = 0, ksw1 = 0;
+  auto read_op = [&](int i, v8i& A, int& sc) __attribute__((always_inline)) {
+    if (i < NPV) {
+      const int ch = i * 32 + l32;
+      const v4i a = *reinterpret_cast<const v4i*>(&sm.v[vst][(0 * D + ch) * 32 + (half_swz(ch, hh) << 4)]);
+      const v4i b = *reinterpret_cast<const v4i*>(&sm.v[vst][(1 * D + ch) * 32 + (half_swz(ch, hh) << 4)]);
+      A = cat(a, b);
+      sc = sm.vs[vst][hh * D + ch];
+    } else {
+      const int T = (i - NPV) & 1, s = (i - NPV) >> 1;
+      if (i == NPV) {
+        ksw0 = sm.ks[kst][l32];
+        ksw1 = sm.ks[kst][32 + l32];
+      }
+      const int row = T * 32 + l32;
+      const v4i a = *reinterpret_cast<const v4i*>(&sm.k[kst][row * D + (row_swz(row, 4 * s + hh, NCH) << 4)]);
+      const v4i b = *reinterpret_cast<const v4i*>(&sm.k[kst][row * D + (row_swz(row, 4 * s + 2 + hh, NCH) << 4)]);
+      A = cat(a, b);
+      sc = (int)(((T ? ksw1 : ksw0) >> (8 * (2 * s + hh))) & 0xFF);
+    }
+  };
+  auto product = [&](int i, const v8i& A, int sc) __attribute__((always_inline)) {
+    if (i < NPV) {
+      oacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, pprev, oacc[i], 0, 0, 0, sc, 0, pscprev);
+    } else {
+      const int T = (i - NPV) & 1, s = (i - NPV) >> 1;
+      nxt[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, qop[s], s == 0 ? v16f{} : nxt[T], 0, 0, 0, sc, 0,
+                                                               qsc[s]);
+    }
+  };
+  v8i opa[2];
+  int osc[2];
+  float gm0 = 0.f, gm1 = 0.f, f = 1.f, nm = 0.f, e0 = 0.f, e1 = 0.f;
+  auto chunk = [&](int k) __attribute__((always_inline)) {
+    if (k == 0) {
+      gm0 = max16_raw(cur[0]);
+      gm1 = max16_raw(cur[1]);
+    } else if (k == 1) {
+      gm0 = max_halves(gm0);
+      gm1 = max_halves(gm1);
+      const float mt = ceilf(fmaxf(gm0, gm1) * c);
+      const bool up = mt > M + kTau;
+      f = up ? __builtin_amdgcn_exp2f(M - mt) : 1.f;   // power of two (0 when M = -inf)
+      M = up ? mt : M;
+      nm = -M;
+      // kept opaque so that the exponent arguments stay two-operand multiply-adds with the
+      // literal c (a negated operand would need the three-operand encoding)
+      asm volatile("" : "+v"(nm));
+    } else if (k <= 5) {
+      const int T = (k - 2) >> 1, i0 = ((k - 2) & 1) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; i++) cur[T][i0 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[T][i0 + i], c, nm));
+    } else if (k == 6) {
+      lsum = __builtin_fmaf(lsum, f, vsum16(cur[0]) + vsum16(cur[1]));
+      const float nmq = nm - kLog2_448;
+      e0 = fminf(fmaxf(ceilf(__builtin_fmaf(gm0, c, nmq)), -127.f), 127.f);
+      e1 = fminf(fmaxf(ceilf(__builtin_fmaf(gm1, c, nmq)), -127.f), 127.f);
+    } else {
+      const int i0 = (int)e0, i1 = (int)e1;
+      const float s0 = __builtin_ldexpf(1.f, i0), s1 = __builtin_ldexpf(1.f, i1);   // 2^e (2^-127 subnormal)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        pop[j] = (int)pack4_e4m3_scaled(cur[0][4 * j], cur[0][4 * j + 1], cur[0][4 * j + 2], cur[0][4 * j + 3], s0);
+        pop[4 + j] = (int)pack4_e4m3_scaled(cur[1][4 * j], cur[1][4 * j + 1], cur[1][4 * j + 2], cur[1][4 * j + 3], s1);
+      }
+      psc = (hh ? i1 : i0) + 127;
+    }
+  };
+  read_op(0, opa[0], osc[0]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    // product i goes before chunk (i * 8) / NP
+#pragma unroll
+    for (int i = 0; i < NP; i++) {
+      if ((i * 8) / NP == k) {
+        product(i, opa[i & 1], osc[i & 1]);
+        if (i + 1 < NP) read_op(i + 1, opa[(i + 1) & 1], osc[(i + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    chunk(k);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return f;
+}
+
+// Instruction order of a tile: the eight matrix-core products that do not depend on this
+// tile's softmax (P V of the previous tile first, then the scores of the next one) are spread
+// through its vector arithmetic, so each product's 64 cycles on the matrix core overlap the
+// softmax instead of stalling the wave's in-order issue. The LDS operand reads of a product
+// are issued right after the previous product, a group of vector instructions ahead of their
+// use, so the LDS wait before a product finds them complete.
+__device__ __forceinline__ void interleave_tile() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);     // LDS reads: operands of product 0
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one product
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads for the next product
+    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);  // vector arithmetic
+  }
+}
+
+// Marks the results of a tile as used at this point (an empty asm reading them), then ends the
+// scheduling region, so the tile's arithmetic and products are issued before the barrier that
+// follows instead of being moved down to where the next tile first needs them. (Device pass
+// only: the vector register constraints have no meaning for the host compiler.)
+template <int D>
+__device__ __forceinline__ void pin_tile_results(const v8i& pcur, int psc, float lsum, float M, float f, const v16f (&nxt)[2],
+                                                 const v16f* oacc) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(pcur), "v"(psc), "v"(lsum), "v"(M), "v"(f), "v"(nxt[0]), "v"(nxt[1]));
+#pragma unroll
+  for (int t = 0; t < D / 32; t++) asm volatile("" ::"v"(oacc[t]));
+#endif
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, bool kPacked, bool kLit>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<D> sm;
   const Work w = decode_work<kPacked>(p);
@@ -296,10 +507,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   const uint32_t vsl = (uint32_t)(lane * 4);
 
   const KvBase kvb = kv_base<D, kPacked>(p, w, hkv);
-  if (nkt > 0) {
-    issue_k<D>(kvb, 0, wave, sm.k[0], sm.ks[0], kl, ksl);
-    issue_v<D>(kvb, 0, wave, sm.v[0], sm.vs[0], vl, vsl);
-  }
+  if (nkt > 0) issue_k<D>(kvb, 0, wave, sm.k[0], sm.ks[0], kl, ksl);
   if (nkt > 1) issue_k<D>(kvb, 1, wave, sm.k[1], sm.ks[1], kl, ksl);
 
   // ---- Q operand (B of S^T = K Q^T), kept in registers ----
@@ -319,8 +527,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     }
   }
   const float c = p.scale * kLog2e;   // S' = acc * c (base-2 logits)
-  // a wave is idle for key tile j when all its keys follow all its queries (causal) or it has no queries
-  auto active = [&](int j) { return qw < w.n && !(p.causal && j * kBlockN > qw + 31); };
   // keys visible to this lane's query: [0, vis_end)
   const int vis_end = p.causal ? min(w.n, qi + 1) : w.nk;
 
@@ -330,91 +536,84 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   float M = -INFINITY;  // reference max (an integer, base 2), at most kTau below the running max
   float lsum = 0.f;     // this lane's share of l (its 16 keys of every half tile)
 
+  // V slot 1 starts as zero codes: the first tile's P V step reads it with zero P codes
+  // (an uninitialised slot could hold NaN codes, and 0 * NaN is NaN)
+  for (int i = threadIdx.x; i < 2 * D * 32 / 16; i += 256) reinterpret_cast<v4i*>(sm.v[1])[i] = v4i{0, 0, 0, 0};
+  if (threadIdx.x < 2 * D / 4) reinterpret_cast<uint32_t*>(sm.vs[1])[threadIdx.x] = 0;
   wait_vmem();
   __syncthreads();
   v16f sa[2], sb[2];
-  if (nkt > 0 && active(0)) scores<D>(sm, 0, qop, qsc, sa);
+  scores<D>(sm, 0, qop, qsc, sa);
   wg_barrier();   // every wave has read K slot 0 before the first tile loads K(2) into it
+  v8i pa = v8i{0, 0, 0, 0, 0, 0, 0, 0}, pb = v8i{0, 0, 0, 0, 0, 0, 0, 0};   // P codes of even / odd tiles
+  int psa = 127, psb = 127;
 
-  // One key tile kt (slot st = kt % 2, a constant in each unrolled copy): issue the loads of K
-  // tile kt + 2 and V tile kt + 1, put the scores of tile kt + 1 on the matrix cores (into nxt)
-  // while this tile's softmax (on cur) runs on the VALU, then P V.
-  auto tile = [&](auto slot, int kt, v16f(&cur)[2], v16f(&nxt)[2]) __attribute__((always_inline)) {
-    constexpr int st = decltype(slot)::value;
-    if (kt + 2 < nkt) issue_k<D>(kvb, kt + 2, wave, sm.k[st], sm.ks[st], kl, ksl);
-    if (kt + 1 < nkt) issue_v<D>(kvb, kt + 1, wave, sm.v[st ^ 1], sm.vs[st ^ 1], vl, vsl);
-    if (kt + 1 < nkt && active(kt + 1)) scores<D>(sm, st ^ 1, qop, qsc, nxt);
-    const int kbase = kt * kBlockN;
-    if (active(kt)) {
-      // ---- mask (diagonal / tail tiles only): the lane's key T*32 + 8(i>>2) + 4hh + (i&3)
-      //      of the tile is visible when it is below vis_end ----
-      const bool need_mask = (p.causal && kbase + kBlockN - 1 > qw) || kbase + kBlockN > w.nk;
-      if (need_mask) {
-        const int lim = vis_end - kbase - 4 * hh;
-        mask_tile<0>(cur[0], lim, std::make_integer_sequence<int, 16>{});
-        mask_tile<32>(cur[1], lim, std::make_integer_sequence<int, 16>{});
-      }
-      // ---- row / group maxima (raw accumulator units; c > 0) ----
-      float gm0 = vmax16(cur[0]), gm1 = vmax16(cur[1]);
-      gm0 = fmaxf(gm0, swap32(gm0));
-      gm1 = fmaxf(gm1, swap32(gm1));
-      // ---- reference max: moves (rescaling the accumulators) only when the tile's row max
-      //      exceeds it by more than kTau ----
-      const float mt = ceilf(fmaxf(gm0, gm1) * c);
-      const bool up = mt > M + kTau;
-      if (__builtin_amdgcn_ballot_w64(up)) {
-        const float f = up ? __builtin_amdgcn_exp2f(M - mt) : 1.f;   // power of two (0 when M = -inf)
-        lsum *= f;
-#pragma unroll
-        for (int t = 0; t < D / 32; t++) oacc[t] *= f;
-        M = up ? mt : M;
-      }
-      // ---- group exponents and P codes: y = 2^(S' - M - e), e = ceil(max S' - M - log2 448) ----
-      const bool rowlive = M > -INFINITY;
-      const float e0 = fminf(fmaxf(ceilf(gm0 * c - M - kLog2_448), -127.f), 127.f);
-      const float e1 = fminf(fmaxf(ceilf(gm1 * c - M - kLog2_448), -127.f), 127.f);
-      const float off0 = rowlive ? M + e0 : 0.f;
-      const float off1 = rowlive ? M + e1 : 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        cur[0][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[0][i], c, -off0));
-        cur[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[1][i], c, -off1));
-      }
-      float s0 = cur[0][0], s1 = cur[1][0];
-#pragma unroll
-      for (int i = 1; i < 16; i++) {
-        s0 += cur[0][i];
-        s1 += cur[1][i];
-      }
-      lsum += ldexpf(s0, (int)e0) + ldexpf(s1, (int)e1);
-      v8i pop;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        pop[j] = (int)pack4_e4m3(cur[0][4 * j], cur[0][4 * j + 1], cur[0][4 * j + 2], cur[0][4 * j + 3]);
-        pop[4 + j] = (int)pack4_e4m3(cur[1][4 * j], cur[1][4 * j + 1], cur[1][4 * j + 2], cur[1][4 * j + 3]);
-      }
-      const int psc = (int)(hh ? e1 : e0) + 127;
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int t = 0; t < D / 32; t++) {
-        const int ch = t * 32 + l32;
-        const v4i a = *reinterpret_cast<const v4i*>(&sm.v[st][(0 * D + ch) * 32 + (half_swz(ch, hh) << 4)]);
-        const v4i b = *reinterpret_cast<const v4i*>(&sm.v[st][(1 * D + ch) * 32 + (half_swz(ch, hh) << 4)]);
-        const int vsc = sm.vs[st][hh * D + ch];
-        oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), pop, oacc[t], 0, 0, 0, vsc, 0, psc);
-      }
+  // Key tile j (slot parity P = j % 2, a constant in each unrolled copy). Loads issued here
+  // land for tile j + 1: K tile j + 2 into K slot P (last read by the scores of tile j, during
+  // tile j - 1) and V tile j into V slot P (last read by P V of tile j - 2). The matrix-core
+  // work of the tile is the scores of tile j + 1 (K slot P ^ 1, into nxt) and P V of tile j - 1
+  // (V slot P ^ 1, codes pprev), both independent of this tile's softmax (on cur, codes into
+  // pcur). P V of a tile is thus accumulated one tile late, always before any rescale that a
+  // later tile's reference max causes (the rescale follows the barrier). Both products run
+  // unconditionally: past the last tile the scores are of a stale (finite) slot and unused, and
+  // a wave with no visible key in a tile gets zero P codes for it.
+  // kMask: diagonal and tail tiles, where the lane's key T*32 + 8(i>>2) + 4hh + (i&3) of the
+  // tile is visible when it is below vis_end. The tiles every lane sees whole come first (a
+  // causal row block's keys end at its diagonal, a sequence's at its ragged tail), so the two
+  // kinds run as two loops, each a straight-line block per tile.
+  auto tile = [&](auto par, auto masked, int j, v16f(&cur)[2], v16f(&nxt)[2], const v8i& pprev, int pscprev,
+                  v8i& pcur, int& psccur) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    constexpr bool kMask = decltype(masked)::value;
+    if (j + 2 < nkt) issue_k<D>(kvb, j + 2, wave, sm.k[P], sm.ks[P], kl, ksl);
+    issue_v<D>(kvb, j, wave, sm.v[P], sm.vs[P], vl, vsl);
+    float f;
+    if (kMask) {
+      pv<D>(sm, P ^ 1, pprev, pscprev, oacc);
+      scores<D>(sm, P ^ 1, qop, qsc, nxt);
+      f = softmax_tile<true, kLit, D>(cur, c, vis_end - j * kBlockN - 4 * hh, M, lsum, pcur, psccur);
+      interleave_tile();
+    } else {
+      f = whole_tile<D, kLit>(sm, P ^ 1, P ^ 1, qop, qsc, cur, nxt, pprev, pscprev, oacc, c, M, lsum, pcur, psccur);
     }
-    // publish K tile kt + 2 and V tile kt + 1
-    if (kt + 1 < nkt) {
-      wait_vmem();
-      wg_barrier();
+    // the tile's work stays ahead of the barrier: its results are used here (otherwise the
+    // compiler moves the arithmetic down to where the next tile first needs it)
+    pin_tile_results<D>(pcur, psccur, lsum, M, f, nxt, oacc);
+    // publish K tile j + 2 and V tile j
+    wait_vmem();
+    wg_barrier();
+    if (__builtin_amdgcn_ballot_w64(f != 1.f)) {
+#pragma unroll
+      for (int t = 0; t < D / 32; t++) oacc[t] *= f;
     }
   };
-  // two tiles per iteration, so the score registers alternate without copies
-  for (int kt = 0; kt < nkt; kt += 2) {
-    tile(std::integral_constant<int, 0>{}, kt, sa, sb);
-    if (kt + 1 < nkt) tile(std::integral_constant<int, 1>{}, kt + 1, sb, sa);
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  using Whole = std::false_type;
+  using Masked = std::true_type;
+  // tiles [0, jw) are seen whole by every lane of the workgroup
+  const int jw = min(nkt, p.causal ? (q0 + 1) / kBlockN : w.nk / kBlockN);
+  int j = 0;
+  // two tiles per iteration, so slots, score registers and code registers alternate without copies
+  for (; j + 1 < jw; j += 2) {
+    tile(Even{}, Whole{}, j, sa, sb, pb, psb, pa, psa);
+    tile(Odd{}, Whole{}, j + 1, sb, sa, pa, psa, pb, psb);
   }
+  if (j < jw) {
+    tile(Even{}, Whole{}, j, sa, sb, pb, psb, pa, psa);
+    j++;
+  }
+  if ((j & 1) && j < nkt) {
+    tile(Odd{}, Masked{}, j, sb, sa, pa, psa, pb, psb);
+    j++;
+  }
+  for (; j < nkt; j += 2) {
+    tile(Even{}, Masked{}, j, sa, sb, pb, psb, pa, psa);
+    if (j + 1 < nkt) tile(Odd{}, Masked{}, j + 1, sb, sa, pa, psa, pb, psb);
+  }
+  // P V of the last tile
+  if (nkt & 1) pv<D>(sm, 0, pa, psa, oacc);
+  else if (nkt > 0) pv<D>(sm, 1, pb, psb, oacc);
 
   // ---- epilogue: O = a / l, LSE = (M + log2 l) ln 2 ----
   const float l = lsum + swap32(lsum);
@@ -456,14 +655,23 @@ hipError_t launch_attn_fwd(const AttnParams& p, hipStream_t stream) {
     grid = dim3((unsigned)((g.max_seqlen + kBlockM - 1) / kBlockM), (unsigned)p.heads_q, (unsigned)g.n_docs);
   }
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+  // the default alpha = d^-1/2 takes the instance with alpha log2 e as a literal
+  const bool lit = p.head_dim == 128 ? p.scale * kLog2e == default_c<128>() && p.scale == 0.08838834764831845f
+                                     : p.scale == 0.125f;
   const int slot = profile_begin(kProfFwd, stream);
+#define MX_FWD_LAUNCH(DD, PK)                                                                            \
+  do {                                                                                                   \
+    if (lit) hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, true>), grid, dim3(256), 0, stream, p);       \
+    else hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, false>), grid, dim3(256), 0, stream, p);          \
+  } while (0)
   if (packed(g)) {
-    if (p.head_dim == 128) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, dim3(256), 0, stream, p);
+    if (p.head_dim == 128) MX_FWD_LAUNCH(128, true);
+    else MX_FWD_LAUNCH(64, true);
   } else {
-    if (p.head_dim == 128) hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, dim3(256), 0, stream, p);
+    if (p.head_dim == 128) MX_FWD_LAUNCH(128, false);
+    else MX_FWD_LAUNCH(64, false);
   }
+#undef MX_FWD_LAUNCH
   profile_end(slot, stream);
   return hipGetLastError();
 }

@@ -98,6 +98,30 @@ __device__ __forceinline__ float swap32(float x) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// v_max3_f32 without the compiler's NaN-quieting copies of each operand (IEEE-mode maxnum
+// of values that are not known to be canonical): the instruction itself ignores quiet NaN
+// operands and quiets signalling ones, which is the same result.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// max(x of this lane, x of lane ^ 32) in every lane: one v_permlane32_swap exchanges the upper
+// half of one copy with the lower half of the other, after which the two copies hold both
+// halves' values in every lane.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max3_raw(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+}
+
+// Largest of 16 values (three levels of v_max3_f32, seven instructions).
+__device__ __forceinline__ float max16_raw(const v16f& x) {
+  const float m0 = max3_raw(x[0], x[1], x[2]), m1 = max3_raw(x[3], x[4], x[5]), m2 = max3_raw(x[6], x[7], x[8]);
+  const float m3 = max3_raw(x[9], x[10], x[11]), m4 = max3_raw(x[12], x[13], x[14]);
+  const float n0 = max3_raw(m0, m1, m2), n1 = max3_raw(m3, m4, x[15]);
+  return max3_raw(n0, n1, n1);
+}
+
 // Maximum over all 64 lanes, without LDS: DPP within rows of 16, then the row pairs
 // (v_permlane16_swap) and the halves (v_permlane32_swap). Every lane gets the result.
 __device__ __forceinline__ float wave_max(float x) {
