@@ -13,6 +13,7 @@ Functions mirror the C entry points:
     mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, ...) -> (dq, dk, dv)
     mx_attn_varlen_fwd / mx_attn_varlen_bwd: the same with cu_seqlens (packed [T, H, d]).
     mx_attn_bwd_mx(...): mx_attn_bwd that also returns dK and dV as MX views (from FP32).
+    mx_attn_bwd_noalloc(...): mx_attn_bwd on the library's own scratch (for callers that cannot allocate).
     mx_attn_cross_fwd / mx_attn_cross_bwd: non-causal cross-attention, keys with their own
         lengths (batched, or packed with cu_seqlens_q and cu_seqlens_k).
     mx_rmsnorm_quantize(x, gamma, eps) -> (row QView, seq QView): RMSNorm written only as MX views.
@@ -24,7 +25,7 @@ from ._lib import (MX_VIEW_ROW, MX_VIEW_SEQ, MX_DQ_F32, MX_DQ_F16_BOOST, MXError
                    PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_DQ, mx_attn_cross_fwd, mx_attn_cross_bwd,
                    mx_attn_cross_workspace_size, mx_rmsnorm_quantize, PROFILE_RMSNORM, mx_gemm_quantize,
                    PROFILE_GEMM, mx_quantize_token_block,
-                   mx_attn_bwd_mx)
+                   mx_attn_bwd_mx, mx_attn_bwd_noalloc)
 
 __all__ = ["MX_VIEW_ROW", "MX_VIEW_SEQ", "MX_DQ_F32", "MX_DQ_F16_BOOST", "MXError", "QView", "lib_path", "load",
            "mx_abi_version", "mx_attn_bwd", "mx_attn_fwd", "mx_attn_varlen_bwd", "mx_attn_varlen_fwd", "mx_quantize",
@@ -32,4 +33,4 @@ __all__ = ["MX_VIEW_ROW", "MX_VIEW_SEQ", "MX_DQ_F32", "MX_DQ_F16_BOOST", "MXErro
            "PROFILE_QUANTIZE", "PROFILE_BWD_PREP", "PROFILE_BWD_DQ", "mx_attn_cross_fwd", "mx_attn_cross_bwd",
            "mx_attn_cross_workspace_size", "mx_rmsnorm_quantize", "PROFILE_RMSNORM", "mx_gemm_quantize",
            "PROFILE_GEMM", "mx_quantize_token_block",
-           "mx_attn_bwd_mx"]
+           "mx_attn_bwd_mx", "mx_attn_bwd_noalloc"]

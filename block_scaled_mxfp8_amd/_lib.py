@@ -78,7 +78,7 @@ def load():
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, P, P, P]
         f.restype = I32
-    for name in ("mx_attn_bwd", "mx_attn_varlen_bwd"):
+    for name in ("mx_attn_bwd", "mx_attn_varlen_bwd", "mx_attn_bwd_noalloc"):
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, _QView, _QView, P, P, P, I32, P, P, P, P]
         f.restype = I32
@@ -393,13 +393,16 @@ def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_sca
     need = lib.mx_attn_cross_workspace_size(ctypes.byref(desc), kseq_p, 1)
     if need == 0:
         raise ValueError("invalid geometry for the backward")
-    if workspace is None:
+    if name == "mx_attn_bwd_noalloc":
+        workspace = None          # the library's own scratch
+    elif workspace is None:
         size = lib.mx_attn_cross_workspace_size(ctypes.byref(desc), kseq_p, 2) if ds_store else need
         workspace = torch.empty(size, dtype=torch.uint8, device=dev)
     elif _nbytes(workspace) < need or not workspace.is_cuda:
         raise ValueError(f"workspace needs {need} bytes")
-    desc.workspace = workspace.data_ptr()
-    desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        desc.workspace = workspace.data_ptr()
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
     dq = torch.empty(qs, dtype=out_dtype, device=dev)
     dk = torch.empty(ks, dtype=out_dtype, device=dev)
     dv = torch.empty(ks, dtype=out_dtype, device=dev)
@@ -451,6 +454,16 @@ def mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal=True, softm
     the minimum. A given workspace selects the store by its size (mx_attn_workspace_size)."""
     return _bwd("mx_attn_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype,
                 dq_mode, cu_seqlens, max_seqlen, workspace, deterministic, ds_store)
+
+
+def mx_attn_bwd_noalloc(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal=True, softmax_scale=0.0,
+                        out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32, cu_seqlens=None, max_seqlen=None):
+    """mx_attn_bwd on the library's own scratch (no workspace argument; the call itself allocates
+    no device memory) -> (dq, dk, dv). Equal bit for bit to mx_attn_bwd with the minimal
+    workspace; calls that overlap on one device race (they share its scratch)."""
+    dq, dk, dv, _ = _bwd("mx_attn_bwd_noalloc", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale,
+                         out_dtype, dq_mode, cu_seqlens, max_seqlen, None, False, False)
+    return dq, dk, dv
 
 
 def mx_attn_bwd_mx(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, views=MX_VIEW_ROW | MX_VIEW_SEQ, causal=True,

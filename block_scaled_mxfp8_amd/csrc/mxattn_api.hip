@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mxattn.h"
 #include "mx_internal.h"
 #include "mx_gemm.h"
@@ -208,6 +210,31 @@ mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
   return mx::launch_attn_bwd(p, (hipStream_t)stream) == hipSuccess ? MX_OK : MX_E_DEVICE;
 }
 
+// Library-owned scratch of mx_attn_bwd_noalloc: the minimal backward workspace (G views, -D,
+// LSE log2 e, the status word) for callers that cannot allocate. One copy per device, alive
+// until the process ends. Host code never uses the array's name as an address: it is a
+// host-side stand-in; the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[MX_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device (null: not yet looked up)
+
+// Device address of the current device's scratch (looked up on the first call on a device,
+// with that device current).
+mx_status current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MX_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MX_E_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MX_OK;
+}
+
 }  // namespace
 
 namespace mx {
@@ -353,6 +380,24 @@ mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
                              mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                              mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream) {
   return bwd_impl(desc, nullptr, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, true);
+}
+
+mx_status mx_attn_bwd_noalloc(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
+                              mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
+                              mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream) {
+  mx::Geom geo, gk;
+  mx_status st = check_desc(desc, &geo);
+  if (st != MX_OK) return st;
+  gk = geo;
+  // the minimal workspace of this call must fit the scratch (checked before any device call)
+  const size_t need = bwd_layout(geo, gk, desc).total;
+  if (need > (size_t)MX_NOALLOC_SCRATCH_BYTES) return MX_E_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = current_scratch(&ws)) != MX_OK) return st;
+  mx_attn_desc d = *desc;
+  d.workspace = ws;
+  d.workspace_bytes = need;   // exactly the minimum: dQ rebuilds dS (no dS code store)
+  return bwd_impl(&d, nullptr, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, false);
 }
 
 mx_status mx_attn_bwd_mx(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row, mx_qview k_seq,

@@ -194,6 +194,26 @@ mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
                              mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                              mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
 
+/* Bytes of the library's own backward scratch (64 MiB per device; see mx_attn_bwd_noalloc). */
+#define MX_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* mx_attn_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation and results, bit
+ * for bit, as mx_attn_bwd given the minimal workspace (mx_attn_workspace_size(desc, 1): the dQ
+ * pass rebuilds dS), but the workspace is a library-owned device array of
+ * MX_NOALLOC_SCRATCH_BYTES per device, held until the process ends; desc->workspace and
+ * desc->workspace_bytes are ignored. Batched or packed (desc->seq.cu_seqlens), self-attention.
+ * Allocates nothing: the array's device address is looked up once per device (on the first call
+ * with that device current). Errors as mx_attn_bwd; a call whose minimal workspace exceeds
+ * MX_NOALLOC_SCRATCH_BYTES returns MX_E_WORKSPACE before touching the device. Every call on a
+ * device shares that device's array (the previous call's contents remain; everything the call
+ * reads is written first), so calls that overlap on one device -- concurrent streams or
+ * threads -- race and must be serialised by the caller. The call's status word is not
+ * readable through mx_read_flags. */
+mx_status mx_attn_bwd_noalloc(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
+                              mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
+                              mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
+
 /* mx_attn_bwd (batched, or packed when desc->seq.cu_seqlens is set: one entry point for both)
  * that also hands out dK and dV as MX views, formed inside the dK/dV kernel from its FP32
  * results (dK = alpha * accumulator, dV = accumulator) before they are rounded to out_dtype:

@@ -292,3 +292,15 @@ def test_bwd_mx_validation(lib):
     assert f(ctypes.byref(d), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, ctypes.byref(bad), None, None,
              None, None) != _lib.MX_OK
     assert f(None, v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, None, None, None, None) == _lib.MX_E_ARG
+
+
+def test_noalloc_backward_rejects_calls_beyond_its_scratch(lib):
+    # the minimal workspace of B1 H32 L8192 d128 (~137 MiB) exceeds the 64 MiB scratch: rejected
+    # on the host, before any device call
+    v = _lib._QView(FAKE, FAKE)
+    d = _desc()
+    d.seq.batch, d.seq.seqlen, d.heads_q, d.heads_kv = 1, 8192, 32, 32
+    assert lib.mx_attn_workspace_size(ctypes.byref(d), 1) > 64 << 20
+    st = lib.mx_attn_bwd_noalloc(ctypes.byref(d), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None)
+    assert st == _lib.MX_E_WORKSPACE
+    assert lib.mx_attn_bwd_noalloc(None, v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None) == _lib.MX_E_ARG
