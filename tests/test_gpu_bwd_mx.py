@@ -1,16 +1,17 @@
-"""dK and dV as MX views from the backward (mx_attn_bwd_mx): each view must equal mx_quantize of
-the kernel's own FP32 dK / dV bit for bit (mx_quantize is itself bit-exact against the oracle,
-and dK / dV are held to the oracle by the backward parity tests), and dQ / dK / dV must be the
-same bits as mx_attn_bwd's. Batched (causal and not, GQA, d 64 and 128, partial key groups) and
-packed documents; single views."""
+"""dK and dV as MX views from the backward (mx_attn_bwd_mx): each view must equal the oracle's
+MX quantisation (oracle.mx_quantize_groups, ROW along d and SEQ along the sequence) of the
+kernel's own FP32 dK / dV bit for bit (dK / dV themselves are held to the oracle by the
+backward parity tests), and dQ / dK / dV must be the same bits as mx_attn_bwd's. Batched
+(causal and not, GQA, d 64 and 128, partial key groups) and packed documents; single views."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from block_scaled_mxfp8_amd import (MX_VIEW_ROW, MX_VIEW_SEQ, mx_attn_bwd, mx_attn_bwd_mx, mx_attn_fwd,
                                     mx_attn_varlen_fwd, mx_quantize)
-from tests.layouts import seq_view_doc, to_device
+from tests.layouts import as_f64, seq_view_batched, seq_view_doc, to_np, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -44,22 +45,32 @@ def _check(t, causal, cu=None, maxlen=None, ds_store=True):
     dq, dk, dv, _, dkv, dvv = got
     for name, a, b in (("dQ", ref[0], dq), ("dK", ref[1], dk), ("dV", ref[2], dv)):
         assert torch.equal(a, b), f"{name} differs from mx_attn_bwd"
-    kw = dict(cu_seqlens=cu, max_seqlen=maxlen)
     for name, x, (row, seqv) in (("dK", dk, dkv), ("dV", dv, dvv)):
-        r_row, r_seq = mx_quantize(x, **kw)
-        torch.cuda.synchronize()
-        _same(row, r_row, name + " ROW")
+        xf = as_f64(x)                                  # the kernel's FP32 values
         if cu is None:
-            _same(seqv, r_seq, name + " SEQ")
+            B, H, L, d = xf.shape
+            sc, ss = seq_view_batched(seqv.codes, seqv.scales, L)
+            for b in range(B):
+                for h in range(H):
+                    rc, _, rs = oracle.mx_quantize_groups(xf[b, h], axis=1)
+                    assert np.array_equal(to_np(row.codes[b, h]), rc), f"{name} ROW codes ({b}, {h})"
+                    assert np.array_equal(to_np(row.scales[b, h]).reshape(rs.shape), rs), f"{name} ROW scales"
+                    qc, _, qs = oracle.mx_quantize_groups(xf[b, h], axis=0)
+                    assert np.array_equal(sc[b, h], qc), f"{name} SEQ codes ({b}, {h})"
+                    assert np.array_equal(ss[b, h], qs), f"{name} SEQ scales ({b}, {h})"
         else:
-            # packed SEQ views: compare every document's rows (the rows between documents are
-            # padding that neither kernel writes)
+            # packed: every document's rows (the SEQ rows between documents are padding that the
+            # kernel does not write)
             cuh = cu.cpu().numpy()
             for j in range(len(cuh) - 1):
-                for h in range(x.shape[1]):
-                    a_c, a_s = seq_view_doc(seqv.codes, seqv.scales, cuh, j, h)
-                    b_c, b_s = seq_view_doc(r_seq.codes, r_seq.scales, cuh, j, h)
-                    assert np.array_equal(a_c, b_c) and np.array_equal(a_s, b_s), f"{name} SEQ doc {j} head {h}"
+                a, e = int(cuh[j]), int(cuh[j + 1])
+                for h in range(xf.shape[1]):
+                    rc, _, rs = oracle.mx_quantize_groups(xf[a:e, h], axis=1)
+                    assert np.array_equal(to_np(row.codes[a:e, h]), rc), f"{name} ROW doc {j} head {h}"
+                    assert np.array_equal(to_np(row.scales[a:e, h]).reshape(rs.shape), rs), f"{name} ROW scales"
+                    qc, _, qs = oracle.mx_quantize_groups(xf[a:e, h], axis=0)
+                    c_d, s_d = seq_view_doc(seqv.codes, seqv.scales, cuh, j, h)
+                    assert np.array_equal(c_d, qc) and np.array_equal(s_d, qs), f"{name} SEQ doc {j} head {h}"
     return got
 
 

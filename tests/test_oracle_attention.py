@@ -12,7 +12,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import (ArithModel, e4m3_round, head_backward, head_forward, head_reference, mx_fake_quant,
+from oracle import (e4m3_round, head_backward, head_forward, head_reference, mx_fake_quant,
                     mx_quantize_groups, round_to)
 from tests.metrics import cosine, rel_l2
 
