@@ -4,14 +4,18 @@
 One step = the whole hot path on one batch of the B4 H32 L4096 d128 causal bf16 workload:
 mx_quantize of Q, K and V (ROW + SEQ views), the forward (O, LSE) and the backward (G
 views + D, the dK/dV kernel, the dQ kernel). Inputs are resident in HBM before the timed region.
+The step is timed over 3 rounds of 20 (the value is the median round's rate); each line also
+records the GPU clocks, ROCm and hipcc versions and the identity of the built sources.
 
 FLOPs are causal-adjusted (FLAMIA notes section 6 visible-pair count): forward 4 d per
 visible pair, backward 10 d (five GEMMs). `value` is the step's fwd+bwd FLOPs over the
 step's wall time (quantisation included). The per-kernel lines come from HIP events that
 the library records immediately around each launch of the named kernel, on its stream.
 
-    python bench.py [--steps K] [--warmup W] [--dq f32|f16] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--rounds R] [--dq f32|f16] [--no-cpu-baseline] [--cpu-heads N]
     python bench.py --pmc-run      # one untimed step + a 1 GiB device copy, for counter runs
+    python bench.py --workload c4  # 128 packed documents (log-normal lengths 32..2048), H4 d128 causal
+    python bench.py --workload c5  # B1 H16 L16384 d128 non-causal (c5gqa: 16 query heads on 4 KV heads)
     python bench.py --workload x1  # cross-attention: 768 documents x 512 queries against
                                    # jagged keys/values (<= 14980), H3 d128, non-causal
     python bench.py --workload n1  # fused RMSNorm + quantise producer, x [262144, 512] bf16
@@ -70,6 +74,10 @@ def recorded_traffic(path=None, sources=None):
         return None
     return int(rec["fetch_kib"] * rec["fetch_scale"] * 1024 + rec["write_kib"] * rec["write_scale"] * 1024)
 
+# every source the library is built from (the identity recorded in each line)
+ALL_SOURCES = sorted(os.path.relpath(p, ROOT) for p in
+                     __import__("glob").glob(os.path.join(ROOT, "block_scaled_mxfp8_amd", "csrc", "*")))
+
 PEAK_MXFP8_TFLOPS = 5000.0      # MI355X dense MXFP8 MFMA, AMD's published figure
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
@@ -85,9 +93,13 @@ def parse():
     ap.add_argument("--pmc-run", action="store_true", help="one untimed step + a 1 GiB copy (counter collection)")
     ap.add_argument("--recompute-dq", action="store_true",
                     help="minimal workspace: the dQ pass rebuilds dS instead of reading the stored codes")
-    ap.add_argument("--workload", choices=["c3", "x1", "n1", "g1"], default="c3",
-                    help="c3: the headline causal self-attention step; x1: the jagged cross-attention step; "
-                         "n1: the fused RMSNorm + quantise producer; g1: the fused GEMM + quantise producer")
+    ap.add_argument("--rounds", type=int, default=3, help="timed rounds of --steps steps (value: the median)")
+    ap.add_argument("--cpu-heads", type=int, default=24,
+                    help="(batch, head) pairs the CPU baseline times (0: all of them, the full tensor)")
+    ap.add_argument("--workload", choices=["c3", "c4", "c5", "c5gqa", "x1", "n1", "g1"], default="c3",
+                    help="c3: the headline causal self-attention step; c4: 128 packed documents; c5/c5gqa: "
+                         "B1 H16 L16384 non-causal (MHA / 16 on 4 KV heads); x1: the jagged cross-attention "
+                         "step; n1: the fused RMSNorm + quantise producer; g1: the fused GEMM + quantise producer")
     return ap.parse_args()
 
 
@@ -106,6 +118,41 @@ def main():
     if args.workload == "g1":
         run_gemm(args)
         return
+    run_attention(args)
+
+
+def environment():
+    """GPU clock, toolchain and source identity recorded in every line."""
+    import subprocess
+    info = {"source_sha256": kernel_sources_sha256(ALL_SOURCES)[:16]}
+    try:
+        with open(os.path.join(ROOT, "block_scaled_mxfp8_amd", "build_info.json")) as f:
+            b = json.load(f)
+        info["build_git"] = b.get("git")
+        info["hipcc"] = b.get("hipcc")
+        info["build_source_sha256"] = b.get("source_sha256", "")[:16]
+    except (OSError, ValueError):
+        info["build_git"] = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        card = next(iter(json.loads(out.stdout).values()))
+        info["gpu_clocks"] = {k: v for k, v in card.items() if any(c in k.lower() for c in ("sclk", "mclk", "fclk"))}
+    except Exception:  # noqa: BLE001 - informational
+        info["gpu_clocks"] = None
+    return info
+
+
+def run_attention(args):
+    """c3 (headline), c5, c5gqa (batched) and c4 (packed documents): one step = mx_quantize of
+    Q, K, V (ROW + SEQ views) + the forward + the backward, inputs resident in HBM. The step is
+    timed over --rounds rounds of --steps steps each, with no measurement hook installed; the
+    value is the median round. One more round of --steps steps records HIP events around every
+    launch of the backward's dK/dV kernel (on the stream it is launched on) for the roofline."""
     import numpy as np
     import torch
 
@@ -116,28 +163,47 @@ def main():
     from block_scaled_mxfp8_amd.flops import attn_flops, visible_pairs
 
     load()
-    cfg = synth.CONFIGS["c3"]
-    B, H, L, d = cfg["batch"], cfg["heads"], cfg["seqlen"], cfg["head_dim"]
+    name = args.workload
+    cfg = synth.CONFIGS[name]
+    d = cfg["head_dim"]
+    causal = cfg["causal"]
     dq_mode = MX_DQ_F32 if args.dq == "f32" else MX_DQ_F16_BOOST
-    print(f"[bench] generating c3 inputs B{B} H{H} L{L} d{d}", file=sys.stderr, flush=True)
-    x = synth.make_inputs("c3")
+    print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
+    x = synth.make_inputs(name)
+    packed = "cu_seqlens" in x
+    if packed:
+        cu_np = x.pop("cu_seqlens")
+        lengths = np.diff(cu_np)
+        cu = torch.from_numpy(cu_np.astype(np.int32)).cuda()
+        maxlen = int(lengths.max())
+        H = cfg["heads"]
+        pairs = visible_pairs(1, H, causal=causal, lengths=lengths)
+        kw = dict(cu_seqlens=cu, max_seqlen=maxlen)
+        desc = (f"{name}: {len(lengths)} packed documents (log-normal lengths {int(lengths.min())}..{maxlen}, "
+                f"T {int(cu_np[-1])}), H{H} d{d} causal per document")
+        cfg_line = {"documents": int(len(lengths)), "tokens": int(cu_np[-1]), "max_seqlen": maxlen, "heads": H}
+    else:
+        B, H, L = cfg["batch"], cfg["heads"], cfg["seqlen"]
+        pairs = visible_pairs(B, H, L, causal=causal)
+        kw = {}
+        desc = (f"{name}: B{B} H{H}" + (f" Hkv{cfg['heads_kv']}" if cfg["heads_kv"] != H else "") +
+                f" L{L} d{d} {'causal' if causal else 'non-causal'}")
+        cfg_line = {"batch": B, "heads": H, "heads_kv": cfg["heads_kv"], "seqlen": L}
     t = {n: torch.from_numpy(x[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v", "g")}
     del x
-    pairs = visible_pairs(B, H, L, causal=True)
     f_fwd = attn_flops(pairs, d)
     f_bwd = attn_flops(pairs, d, backward=True)
     ws = {}
+    ds_store = not args.recompute_dq
 
     def quant():
-        return mx_quantize(t["q"]), mx_quantize(t["k"]), mx_quantize(t["v"])
-
-    ds_store = not args.recompute_dq
+        return mx_quantize(t["q"], **kw), mx_quantize(t["k"], **kw), mx_quantize(t["v"], **kw)
 
     def step(mode=dq_mode):
         (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
-        o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=True)
-        dq, dk, dv, w = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=True, dq_mode=mode,
-                                    workspace=ws.get(mode), ds_store=ds_store)
+        o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=causal, **kw)
+        dq, dk, dv, w = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=causal,
+                                    dq_mode=mode, workspace=ws.get(mode), ds_store=ds_store, **kw)
         ws[mode] = w
         return o, dq
 
@@ -154,8 +220,17 @@ def main():
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
-    # the timed region also feeds the roofline line: events around every launch of the
-    # backward dK/dV kernel (the step's dominant kernel)
+    rounds = []
+    for r in range(max(1, args.rounds)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        rounds.append((time.perf_counter() - t0) * 1e3 / args.steps)
+        print(f"[bench] round {r}: {args.steps} steps, {rounds[-1]:.3f} ms/step", file=sys.stderr, flush=True)
+    ms_step = float(np.median(rounds))
+    # roofline round: events around every launch of the dK/dV kernel (the step's dominant kernel)
     ev_main = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in ev_main:
         a.record()
@@ -166,11 +241,10 @@ def main():
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    ms_hooked = (time.perf_counter() - t0) * 1e3 / args.steps
     mx_profile_kernel(0, [])
-    ms_step = (t1 - t0) * 1e3 / args.steps
     ms_bwd_main = float(np.mean([a.elapsed_time(b) for a, b in ev_main]))
-    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+    print(f"[bench] roofline round: {ms_hooked:.3f} ms/step, dK/dV {ms_bwd_main:.3f} ms", file=sys.stderr, flush=True)
 
     # per-kernel averages outside the timed region
     def kernel_ms(kind, fn, n=args.profile_steps):
@@ -187,21 +261,22 @@ def main():
         return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
-    o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=True)
-    ms_fwd = kernel_ms(PROFILE_FWD, lambda: mx_attn_fwd(q_row, k_row, v_seq, causal=True))
-    ms_quant = kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize(t["q"]), n=3 * args.profile_steps)
-    # the token-block variant of the quantiser (same bytes; one exponent per 32 tokens x d)
-    ms_quant_tb = kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize_token_block(t["q"]), n=3 * args.profile_steps)
+    o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=causal, **kw)
+    ms_fwd = kernel_ms(PROFILE_FWD, lambda: mx_attn_fwd(q_row, k_row, v_seq, causal=causal, **kw))
+    ms_quant = kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize(t["q"], **kw), n=3 * args.profile_steps)
+    ms_quant_tb = None
+    if not packed:   # the token-block variant of the quantiser (same bytes; one exponent per 32 tokens x d)
+        ms_quant_tb = kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize_token_block(t["q"]), n=3 * args.profile_steps)
 
     def bwd(mode):
-        return lambda: mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=True, dq_mode=mode,
-                                   workspace=ws.get(mode), ds_store=ds_store)
+        return lambda: mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=causal, dq_mode=mode,
+                                   workspace=ws.get(mode), ds_store=ds_store, **kw)
 
     res_bwd = {}
-    for name, mode in (("f32", MX_DQ_F32), ("f16", MX_DQ_F16_BOOST)):
+    for nm, mode in (("f32", MX_DQ_F32), ("f16", MX_DQ_F16_BOOST)):
         if mode not in ws:
             _, _, _, ws[mode] = bwd(mode)()
-        main = kernel_ms(PROFILE_BWD_DKDV, bwd(mode))
+        main_ms = kernel_ms(PROFILE_BWD_DKDV, bwd(mode))
         prep = kernel_ms(PROFILE_BWD_PREP, bwd(mode))
         fin = kernel_ms(PROFILE_BWD_DQ, bwd(mode))
         # whole call, events around it on the current stream
@@ -213,28 +288,21 @@ def main():
         s1.record()
         torch.cuda.synchronize()
         call = s0.elapsed_time(s1) / args.profile_steps
-        res_bwd[name] = dict(dkdv_ms=main, prep_ms=prep, dq_ms=fin, call_ms=call)
+        res_bwd[nm] = dict(dkdv_ms=main_ms, prep_ms=prep, dq_ms=fin, call_ms=call)
 
-    q_elems = B * H * L * d
+    q_elems = int(t["q"].numel())
     quant_bytes = q_elems * (2 + 2 * (1 + 1 / 32))          # bf16 in, two views of codes + scales out
     tflops = lambda f, ms: f / (ms * 1e-3) / 1e12          # noqa: E731
     # algorithmic FLOPs per kernel: dK/dV kernel S, E, dV, dK (4 of the 5 products, 8 d per
     # visible pair); dQ kernel dQ (2 d; the recomputing variant also rebuilds S and E, 4 d more,
     # not counted in the step's FLOPs, which follow the method's 10 d per pair)
     f_dkdv = f_bwd * 4 // 5
-    # dQ from the store reads the stored 32 x 32 blocks once (1024 code bytes + 1 exponent each)
-    nb = (L + 31) // 32
-    ds_bytes = B * H * nb * (nb + 1) // 2 * 1025
-    kernels = {
-        "attn_fwd": dict(ms=ms_fwd, tflops=tflops(f_fwd, ms_fwd)),
-        "attn_bwd_dkdv": dict(ms=ms_bwd_main, tflops=tflops(f_dkdv, ms_bwd_main)),
-        "quantize": dict(ms=ms_quant, gbs=quant_bytes / (ms_quant * 1e-3) / 1e9),
-    }
-    bwd_f32 = res_bwd["f32"]
-    bwd_f16 = res_bwd["f16"]
+    bwd_f32, bwd_f16 = res_bwd["f32"], res_bwd["f16"]
+    value = tflops(f_fwd + f_bwd, ms_step)
     line = {
-        "metric": "MXFP8 attn fwd/bwd TFLOP/s (causal-adj) at B4 H32 L4096 d128, % of peak",
-        "value": round(tflops(f_fwd + f_bwd, ms_step), 2),
+        "metric": "MXFP8 attn fwd/bwd TFLOP/s (causal-adj) at B4 H32 L4096 d128, % of peak" if name == "c3"
+        else f"MXFP8 attn fwd/bwd TFLOP/s (causal-adj) on {name}",
+        "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -245,32 +313,35 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp8",
         "data": "synthetic",
-        "config": {"workload": "c3: B4 H32 L4096 d128 causal, bf16 N(0,1) inputs, step = quantise Q/K/V + fwd + bwd",
-                   "batch": B, "heads": H, "seqlen": L, "head_dim": d, "causal": True, "dq": args.dq,
-                   "dq_pass": "rebuilds dS" if args.recompute_dq else "reads stored dS codes"},
-        "pct_of_peak": round(100 * tflops(f_fwd + f_bwd, ms_step) / PEAK_MXFP8_TFLOPS, 2),
+        "config": dict({"workload": desc + ", bf16 N(0,1)-based synthetic inputs, step = quantise Q/K/V + fwd + bwd",
+                        "head_dim": d, "causal": causal, "dq": args.dq,
+                        "dq_pass": "rebuilds dS" if args.recompute_dq else "reads stored dS codes"}, **cfg_line),
+        "timing": {"rounds": args.rounds, "steps_per_round": args.steps, "ms_per_step_rounds": [round(r, 4) for r in rounds],
+                   "statistic": "median of rounds, wall clock, no measurement hook",
+                   "ms_per_step_roofline_round": round(ms_hooked, 4)},
+        "pct_of_peak": round(100 * value / PEAK_MXFP8_TFLOPS, 2),
         "fwd_tflops": round(tflops(f_fwd, ms_fwd), 2),
         "fwd_pct_of_peak": round(100 * tflops(f_fwd, ms_fwd) / PEAK_MXFP8_TFLOPS, 2),
         "bwd_tflops": round(tflops(f_bwd, bwd_f32["call_ms"]), 2),
         "bwd_pct_of_peak": round(100 * tflops(f_bwd, bwd_f32["call_ms"]) / PEAK_MXFP8_TFLOPS, 2),
         "bwd_f16dq_tflops": round(tflops(f_bwd, bwd_f16["call_ms"]), 2),
         "bwd_f16dq_pct_of_peak": round(100 * tflops(f_bwd, bwd_f16["call_ms"]) / PEAK_MXFP8_TFLOPS, 2),
-        "quantize_gbs": round(kernels["quantize"]["gbs"], 1),
-        "quantize_token_block_gbs": round(quant_bytes / (ms_quant_tb * 1e-3) / 1e9, 1),
-        "dq_store_read_gbs": None if args.recompute_dq else round(ds_bytes / (bwd_f32["dq_ms"] * 1e-3) / 1e9, 1),
+        "quantize_gbs": round(quant_bytes / (ms_quant * 1e-3) / 1e9, 1),
+        "quantize_token_block_gbs": None if ms_quant_tb is None else round(quant_bytes / (ms_quant_tb * 1e-3) / 1e9, 1),
         "kernels_ms": {"attn_fwd": round(ms_fwd, 4), "attn_bwd_dkdv": round(bwd_f32["dkdv_ms"], 4),
                        "attn_bwd_dq_f32": round(bwd_f32["dq_ms"], 4), "attn_bwd_dq_f16": round(bwd_f16["dq_ms"], 4),
                        "bwd_prep": round(bwd_f32["prep_ms"], 4), "quantize_one_tensor": round(ms_quant, 4)},
         "flops": {"fwd": f_fwd, "bwd": f_bwd, "visible_pairs": pairs},
         "pages_context": {"fa4_mx8_fwd_pflops_gb300": 2.85, "fa4_mx8_bwd_pflops_gb300_f16dq": 1.98,
                           "fa4_mx8_bwd_pflops_gb300_f32dq": 1.82},
-        "roofline": {"kernel": "attn_bwd_dkdv_kernel<128> (backward dK/dV)", "bound": "mfma",
-                     "achieved": round(kernels["attn_bwd_dkdv"]["tflops"], 2), "peak": PEAK_MXFP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(kernels["attn_bwd_dkdv"]["tflops"] / PEAK_MXFP8_TFLOPS, 4),
-                     "traffic": recorded_traffic()},
+        "roofline": {"kernel": f"attn_bwd_dkdv_kernel<{d}> (backward dK/dV)", "bound": "mfma",
+                     "achieved": round(tflops(f_dkdv, ms_bwd_main), 2), "peak": PEAK_MXFP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops(f_dkdv, ms_bwd_main) / PEAK_MXFP8_TFLOPS, 4),
+                     "traffic": recorded_traffic() if name == "c3" else None},
+        "env": environment(),
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(t)
+    if not args.no_cpu_baseline and name == "c3":
+        line["cpu_baseline"] = cpu_baseline(t, args.cpu_heads)
     print(json.dumps(line), flush=True)
 
 
@@ -580,30 +651,31 @@ def cpu_baseline_norm(x, gamma, eps, rows=32768):
             "sample": f"first {rows} of {x.shape[0]} rows (n {n}), float64 numpy, {sec:.1f} s"}
 
 
-def cpu_baseline(t):
-    """The float64 oracle (as it stands) on a bounded sample of the same workload: forward and
-    backward of one (batch, head) pair of the B4 H32 L4096 d128 causal step."""
+def cpu_baseline(t, heads=8):
+    """The C++ oracle (oracle/cpp, as it stands) on a bounded sample of the same workload:
+    forward and backward of the first `heads` (batch, head) pairs of the c3 step (every pair
+    is the same work), scaled to the metric's unit; heads=0 times every pair (the full tensor)."""
     import numpy as np
     import torch
 
-    import oracle
     from block_scaled_mxfp8_amd.flops import attn_flops
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001 - only used to report the thread count
-        cores = os.cpu_count()
-    q, k, v, g = (t[n][0, 0].to(torch.float64).cpu().numpy() for n in ("q", "k", "v", "g"))
-    L, d = q.shape
-    t0 = time.perf_counter()
-    f = oracle.head_forward(q, k, v, True)
-    oracle.head_backward(q, k, v, f["O_out"], f["lse"], g, True)
-    sec = time.perf_counter() - t0
-    pairs = L * (L + 1) // 2
-    fl = attn_flops(pairs, d) + attn_flops(pairs, d, backward=True)
-    return {"value": round(fl / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fwd+bwd of 1 of 128 (batch, head) pairs (b0 h0, L{L} d{d} causal), float64 numpy, "
-                      f"{sec:.1f} s"}
+    from oracle import fast
+    B, H, L, d = t["q"].shape
+    n_pairs = B * H if heads <= 0 else min(heads, B * H)
+    pairs = [(i // H, i % H) for i in range(n_pairs)]
+    sec = 0.0
+    for bh in pairs:
+        q, k, v, g = (t[n][bh].to(torch.float64).cpu().numpy() for n in ("q", "k", "v", "g"))
+        t0 = time.perf_counter()
+        f = fast.head_forward(q, k, v, True)
+        fast.head_backward(q, k, v, f["O_out"], f["lse"].astype(np.float32), g, True)
+        sec += time.perf_counter() - t0
+    fl = n_pairs * (attn_flops(L * (L + 1) // 2, d) + attn_flops(L * (L + 1) // 2, d, backward=True))
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return {"value": round(fl / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fwd+bwd of {n_pairs} of {B * H} (batch, head) pairs (L{L} d{d} causal; every pair is "
+                      f"the same work), C++17/OpenMP oracle with matrix-core-model scores, {sec:.1f} s; "
+                      f"full tensor at this rate: {sec * B * H / n_pairs:.0f} s"}
 
 
 if __name__ == "__main__":

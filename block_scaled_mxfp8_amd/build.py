@@ -47,7 +47,31 @@ def build(verbose=False, out=LIB, extra=()):
     if verbose and msgs.strip():
         print(msgs)
     os.replace(tmp, out)
+    write_build_info(os.path.join(HERE, "build_info.json"))
     return out
+
+
+def write_build_info(path):
+    """Identity of this build (read by the benchmark): git revision of the tree, hipcc version,
+    hash of the sources compiled."""
+    import hashlib
+    import json
+    h = hashlib.sha256()
+    for src in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        with open(src, "rb") as f:
+            h.update(os.path.relpath(src, ROOT).encode() + b"\0" + f.read())
+    def run(cmd):
+        try:
+            return subprocess.run(cmd, capture_output=True, text=True, cwd=ROOT, timeout=30).stdout.strip()
+        except Exception:  # noqa: BLE001 - informational
+            return None
+    git = run(["git", "rev-parse", "--short=12", "HEAD"])
+    if git and run(["git", "status", "--porcelain", "--", "block_scaled_mxfp8_amd", "include"]):
+        git += "+uncommitted"
+    hip = run([hipcc(), "--version"])
+    info = {"git": git, "hipcc": hip.splitlines()[0] if hip else None, "source_sha256": h.hexdigest()}
+    with open(path, "w") as f:
+        json.dump(info, f)
 
 
 if __name__ == "__main__":
