@@ -40,6 +40,7 @@
 #include "mx_internal.h"
 #include "mx_layout.h"
 #include "mx_profile.h"
+#include "mx_worklist.h"
 
 namespace mx {
 
@@ -50,6 +51,8 @@ constexpr int kBlockK = 32 * kWaves;   // keys per dK/dV workgroup
 constexpr int kStepQ = 64;             // queries per dK/dV step
 constexpr int kBlockQ = 32 * kWaves;   // queries per dQ workgroup
 constexpr int kStepK = 64;             // keys per dQ step
+constexpr int kDkvProducers = 2 * kWaves;  // dK/dV workgroup: producer waves, then kWaves accumulators
+constexpr int kDkvThreads = 64 * (kDkvProducers + kWaves);
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kBoost = 512.f;        // 2^9 (FP16 dQ partial sums)
 constexpr int kDkvChunk = 2;           // (sequence, head) pairs per longest-first chunk (mx_layout.h lpt_order)
@@ -155,11 +158,24 @@ struct KvWork {
 };
 
 template <bool kPacked>
-__device__ __forceinline__ KvWork decode_kv(const BwdParams& p) {
+__device__ __forceinline__ KvWork decode_kv(const BwdParams& p, int* smem) {
   const Geom& g = p.geom;
   KvWork w;
   w.valid = true;
-  if (!kPacked) {
+  if (kPacked && p.plan) {
+    // the work list: rank blockIdx / H_kv takes the rank-th key block in decreasing query-step count
+    static_assert(kPlanBlock == kBlockK, "work items are the workgroup's key blocks");
+    const PlanItem it = plan_item<kDkvThreads>(g, p.geom_k, kKeyItems, p.causal != 0,
+                                               (int)(blockIdx.x / p.heads_kv), smem);
+    w.hkv = (int)(blockIdx.x % p.heads_kv);
+    w.s = it.valid ? it.doc : 0;
+    w.kb = it.blk;
+    w.doc_start = g.cu[w.s];
+    w.n = g.cu[w.s + 1] - w.doc_start;
+    w.doc_k = p.geom_k.cu[w.s];
+    w.nk = p.geom_k.cu[w.s + 1] - w.doc_k;
+    w.valid = it.valid;
+  } else if (!kPacked) {
     const int nkb = (p.geom_k.seqlen + kBlockK - 1) / kBlockK;
     int bh, rank;
     lpt_order<kDkvChunk>(blockIdx.x, p.heads_kv * g.batch, nkb, bh, rank);
@@ -358,8 +374,6 @@ __device__ __forceinline__ int dkv_codes_tile(const DkvStage<D>& S, int qt, cons
 // apply the codes of step j - 1 (stage (j-1) % 3, buffer (j-1) % 2); one barrier ends the
 // iteration. The accumulators set the pace (eight products per step each, against four
 // per producer), so the dS stores sit with the producers.
-constexpr int kDkvProducers = 2 * kWaves;
-constexpr int kDkvThreads = 64 * (kDkvProducers + kWaves);
 constexpr int kCodeDw = 1280;               // exchange dwords per key group
 
 template <int D>
@@ -518,7 +532,7 @@ __device__ __forceinline__ void dkv_mx_views(const BwdParams& p, const KvWork& w
 template <int D, bool kPacked, bool kStore, bool kMxOut = false>
 __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __shared__ DkvShared<D> sm;
-  const KvWork w = decode_kv<kPacked>(p);
+  const KvWork w = decode_kv<kPacked>(p, reinterpret_cast<int*>(&sm));
   if (!w.valid) return;
   const Geom& gk = p.geom_k;              // keys, values, dK, dV
   const int lane = threadIdx.x & 63;
@@ -735,11 +749,23 @@ struct QWork {
   bool valid;
 };
 
-__device__ __forceinline__ QWork decode_q(const BwdParams& p) {
+__device__ __forceinline__ QWork decode_q(const BwdParams& p, int* smem) {
   const Geom& g = p.geom;
   QWork w;
   w.valid = true;
-  if (!packed(g)) {
+  if (packed(g) && p.plan) {
+    // the work list: rank blockIdx / H takes the rank-th query block in decreasing key-tile count
+    static_assert(kPlanBlock == kBlockQ, "work items are the workgroup's query blocks");
+    const PlanItem it = plan_item<256>(g, p.geom_k, kQueryItems, p.causal != 0, (int)(blockIdx.x / p.heads_q), smem);
+    w.h = (int)(blockIdx.x % p.heads_q);
+    w.s = it.valid ? it.doc : 0;
+    w.qb = it.blk;
+    w.doc_start = g.cu[w.s];
+    w.n = g.cu[w.s + 1] - w.doc_start;
+    w.doc_k = p.geom_k.cu[w.s];
+    w.nk = p.geom_k.cu[w.s + 1] - w.doc_k;
+    w.valid = it.valid;
+  } else if (!packed(g)) {
     const int nqb = (g.seqlen + kBlockQ - 1) / kBlockQ;
     int bh, rank;
     lpt_order<4>(blockIdx.x, p.heads_q * g.batch, nqb, bh, rank);
@@ -814,7 +840,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 template <int D, bool kF16>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   __shared__ DqStage<D> sm[2];
-  const QWork w = decode_q(p);
+  const QWork w = decode_q(p, reinterpret_cast<int*>(&sm[0]));
   if (!w.valid) return;
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
@@ -1073,7 +1099,7 @@ __device__ __forceinline__ void dqds_tile(const BwdParams& p, const QWork& w, co
 template <int D, bool kF16, bool kPacked>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(BwdParams p) {
   __shared__ DqdsStage<D> sm[3];
-  const QWork w = decode_q(p);
+  const QWork w = decode_q(p, reinterpret_cast<int*>(&sm[0]));
   if (!w.valid) return;
   const Geom& g = p.geom;
   constexpr int NCT = D / 32;
@@ -1187,6 +1213,9 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
   if (!packed(g)) {
     gkv = dim3((unsigned)((long long)((p.geom_k.seqlen + kBlockK - 1) / kBlockK) * p.heads_kv * g.batch), 1, 1);
     gq = dim3((unsigned)((long long)((g.seqlen + kBlockQ - 1) / kBlockQ) * p.heads_q * g.batch), 1, 1);
+  } else if (p.plan) {
+    gkv = dim3((unsigned)(plan_items_bound(p.geom_k) * p.heads_kv), 1, 1);
+    gq = dim3((unsigned)(plan_items_bound(g) * p.heads_q), 1, 1);
   } else {
     gkv = dim3((unsigned)((p.geom_k.max_seqlen + kBlockK - 1) / kBlockK), (unsigned)p.heads_kv, (unsigned)g.n_docs);
     gq = dim3((unsigned)((g.max_seqlen + kBlockQ - 1) / kBlockQ), (unsigned)p.heads_q, (unsigned)g.n_docs);

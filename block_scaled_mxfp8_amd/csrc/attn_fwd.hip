@@ -40,6 +40,7 @@
 #include "mx_internal.h"
 #include "mx_layout.h"
 #include "mx_profile.h"
+#include "mx_worklist.h"
 
 #include <type_traits>
 
@@ -86,11 +87,23 @@ struct Work {
 };
 
 template <bool kPacked>
-__device__ __forceinline__ Work decode_work(const AttnParams& p) {
+__device__ __forceinline__ Work decode_work(const AttnParams& p, int* smem) {
   const Geom& g = p.geom;
   Work w;
   w.valid = true;
-  if (!kPacked) {
+  if (kPacked && p.plan) {
+    // the work list: rank blockIdx / H takes the rank-th query block in decreasing key-tile count
+    static_assert(kPlanBlock == kBlockM, "work items are the workgroup's query blocks");
+    const PlanItem it = plan_item<256>(g, p.geom_k, kQueryItems, p.causal != 0, (int)(blockIdx.x / p.heads_q), smem);
+    w.h = (int)(blockIdx.x % p.heads_q);
+    w.s = it.valid ? it.doc : 0;
+    w.qt = it.blk;
+    w.doc_start = g.cu[w.s];
+    w.n = g.cu[w.s + 1] - w.doc_start;
+    w.doc_k = p.geom_k.cu[w.s];
+    w.nk = p.geom_k.cu[w.s + 1] - w.doc_k;
+    w.valid = it.valid;
+  } else if (!kPacked) {
     const int nqt = (g.seqlen + kBlockM - 1) / kBlockM;
     int bh, rank;
     lpt_order<4>(blockIdx.x, p.heads_q * g.batch, nqt, bh, rank);
@@ -487,7 +500,7 @@ __device__ __forceinline__ void pin_tile_results(const v8i& pcur, int psc, float
 template <int D, bool kPacked, bool kLit>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<D> sm;
-  const Work w = decode_work<kPacked>(p);
+  const Work w = decode_work<kPacked>(p, reinterpret_cast<int*>(&sm));
   if (!w.valid) return;
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
@@ -651,6 +664,8 @@ hipError_t launch_attn_fwd(const AttnParams& p, hipStream_t stream) {
   if (!packed(g)) {
     const int nqt = (g.seqlen + kBlockM - 1) / kBlockM;
     grid = dim3((unsigned)((long long)nqt * p.heads_q * g.batch), 1, 1);
+  } else if (p.plan) {
+    grid = dim3((unsigned)(plan_items_bound(g) * p.heads_q), 1, 1);
   } else {
     grid = dim3((unsigned)((g.max_seqlen + kBlockM - 1) / kBlockM), (unsigned)p.heads_q, (unsigned)g.n_docs);
   }

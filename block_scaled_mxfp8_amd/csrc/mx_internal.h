@@ -35,6 +35,7 @@ struct AttnParams {
   int causal;
   float scale;           // alpha
   bool out_f32;          // O / dQ / dK / dV storage type (else bf16)
+  int plan;              // packed: 1D grid over the device-built work list (mx_worklist.h)
   // forward operands
   const uint8_t* q_codes; const uint8_t* q_scales;    // ROW view of Q
   const uint8_t* k_codes; const uint8_t* k_scales;    // ROW view of K
@@ -50,6 +51,7 @@ struct BwdParams {
   int causal;
   float scale;
   bool out_f32;
+  int plan;              // packed: 1D grids over the device-built work lists (mx_worklist.h)
   int dq_mode;
   const uint8_t* q_codes; const uint8_t* q_scales;      // ROW Q
   const uint8_t* qs_codes; const uint8_t* qs_scales;    // SEQ Q

@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "../../include/mxattn.h"
+#include "mx_worklist.h"
 #include "mx_internal.h"
 #include "mx_gemm.h"
 #include "mx_norm.h"
@@ -138,6 +139,7 @@ mx_status fwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
   p.causal = desc->causal ? 1 : 0;
   p.scale = desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0f / sqrtf((float)desc->head_dim);
   p.out_f32 = desc->out_dtype == MX_F32;
+  p.plan = mx::plan_eligible(g, gk) ? 1 : 0;
   p.q_codes = q_row.codes; p.q_scales = q_row.scales;
   p.k_codes = k_row.codes; p.k_scales = k_row.scales;
   p.v_codes = v_seq.codes; p.v_scales = v_seq.scales;
@@ -173,6 +175,7 @@ mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
   p.causal = desc->causal ? 1 : 0;
   p.scale = desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0f / sqrtf((float)desc->head_dim);
   p.out_f32 = desc->out_dtype == MX_F32;
+  p.plan = mx::plan_eligible(g, gk) ? 1 : 0;
   p.dq_mode = desc->dq_mode;
   p.q_codes = q_row.codes; p.q_scales = q_row.scales;
   p.qs_codes = q_seq.codes; p.qs_scales = q_seq.scales;
