@@ -60,9 +60,10 @@ sum to FP16 (half an FP16 ulp of each, from the signed running sums).
 import math
 import numpy as np
 
-from .codec import (GROUP, e4m3_decode, e4m3_encode, e4m3_round, mx_dequantize_groups, mx_quantize_groups,
-                    mx_quantize_token_blocks, mx_scale_exponent)
-from .mfma import GROUP_TRUNC, KSTEP, dot_rows, exp_magnitude, f32, group_max_bound, model_slack, ulp32
+from .codec import (GROUP, e4m3_decode, e4m3_encode, e4m3_round, mx4_dequantize_groups, mx4_quantize_groups,
+                    mx_dequantize_groups, mx_quantize_groups, mx_quantize_token_blocks, mx_scale_exponent)
+from .mfma import (GROUP_TRUNC, KSTEP, dot_rows, dot_rows_e2m1, exp_magnitude, f32, group_max_bound, model_slack,
+                   ulp32)
 
 LN2 = math.log(2.0)
 LOG2E = 1.0 / LN2
@@ -82,11 +83,17 @@ class _View:
 
     kind: "row" (groups of 32 channels of a token), "seq" (groups of 32 tokens of a channel),
     "token_block" (one exponent per 32-token block for every channel: the codes serve both
-    contraction axes)."""
+    contraction axes), "row_fp4" (the ROW groups with E2M1 codes: MXFP4)."""
 
     def __init__(self, x, kind):
         n, d = x.shape
-        if kind == "token_block":
+        self.fp4 = kind == "row_fp4"
+        if kind == "row_fp4":
+            codes, e, _ = mx4_quantize_groups(x, axis=1)
+            self.x = mx4_dequantize_groups(codes, e, axis=1)
+            self.blk_exp = e
+            self.elem_exp = np.repeat(e, GROUP, axis=1)[:, :d]
+        elif kind == "token_block":
             codes, eb, _ = mx_quantize_token_blocks(x)
             e_tok = np.repeat(eb, GROUP)[:n]
             self.x = np.ldexp(e4m3_decode(codes), e_tok[:, None])
@@ -109,6 +116,26 @@ class _View:
     def mag(self, idx=slice(None)):
         """exp_magnitude of the elements (rows idx)."""
         return exp_magnitude(self.x[idx], self.elem_exp[idx])
+
+
+def _scores(A, ai, B, bi, c0=0.0):
+    """The matrix-core product of rows ai of view A with rows bi of view B (both ROW-type
+    views of the same element format): the E4M3 model, or the E2M1 one for MXFP4 views."""
+    assert A.fp4 == B.fp4
+    f = dot_rows_e2m1 if A.fp4 else dot_rows
+    return f(A.codes[ai], A.blk_exp[ai], B.codes[bi], B.blk_exp[bi], c0)
+
+
+def _score_views(q, k, scales, score_format):
+    """The views of Q and K that form S: ROW (or token-block) views in E4M3, or MXFP4 ROW views
+    (FLAMIA notes, sections 2 and 3: the mixed route scores with 4-bit Q and K and keeps the
+    other products in 8 bits; here with the matrix core's E8M0 scale per 32 channels)."""
+    assert score_format in ("mxfp8", "mxfp4"), score_format
+    if score_format == "mxfp4":
+        assert scales == "axis", "4-bit scores use per-axis groups"
+        return _View(q, "row_fp4"), _View(k, "row_fp4")
+    kind = "token_block" if scales == "token_block" else "row"
+    return _View(q, kind), _View(k, kind)
 
 
 def _c32(alpha):
@@ -197,7 +224,8 @@ def _mx_dev(y, e, dy_rel, group_axis, exp_amb=False):
 
 
 def head_forward(q, k, v, causal, softmax_scale=None, quantized=True, out_dtype="bf16",
-                 bounds=False, perturb=None, rows=None, scales="axis", score_precision="kernel"):
+                 bounds=False, perturb=None, rows=None, scales="axis", score_precision="kernel",
+                 score_format="mxfp8"):
     """Forward pass for one head: returns dict(O (float64, unrounded), O_out (rounded), lse,
     ell, and when bounds=True: B (ambiguity bound on O), eta (accumulation allowance),
     drel_max (relative budget of l)).
@@ -218,7 +246,11 @@ def head_forward(q, k, v, causal, softmax_scale=None, quantized=True, out_dtype=
     ``score_precision="float64"`` forms the scores of the quantised operands in float64
     instead of the matrix-core model (faster on long sequences; then the P decisions are not
     the kernels' and no bounds are given). It serves only to make a saved O and LSE as inputs
-    of a backward check, which hands the same values to both sides."""
+    of a backward check, which hands the same values to both sides.
+
+    ``score_format="mxfp4"``: Q and K enter the score product as MXFP4 ROW views (E2M1 codes,
+    one E8M0 exponent per 32 channels; the E2M1 instruction model of oracle/mfma.py); V and P
+    stay E4M3."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -230,8 +262,7 @@ def head_forward(q, k, v, causal, softmax_scale=None, quantized=True, out_dtype=
     if quantized:
         assert scales in ("axis", "token_block"), scales
         tb = scales == "token_block"
-        Qv = _View(q, "token_block" if tb else "row")
-        Kv = _View(k, "token_block" if tb else "row")
+        Qv, Kv = _score_views(q, k, scales, score_format)
         Vv = _View(v, "token_block" if tb else "seq")
         Qt, Kt, Vt = Qv.x, Kv.x, Vv.x
         c = _c32(alpha)
@@ -254,7 +285,7 @@ def head_forward(q, k, v, causal, softmax_scale=None, quantized=True, out_dtype=
         qi = sel[r0:r1]
         mask = (np.arange(nk)[None, :] <= qi[:, None]) if causal else np.ones((r1 - r0, nk), dtype=bool)
         if quantized and score_precision == "kernel":
-            Sraw = dot_rows(Qv.codes[qi], Qv.blk_exp[qi], Kv.codes, Kv.blk_exp)
+            Sraw = _scores(Qv, qi, Kv, slice(None))
         else:
             Sraw = Qt[qi] @ Kt.T
         Sp = np.where(mask, Sraw * c, -np.inf)            # base-2 logits S' = S alpha log2 e
@@ -348,7 +379,7 @@ def _quant_blocks2d(U):
 
 def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantized=True,
                   out_dtype="bf16", bounds=False, fwd=None, dq_mode="f32", perturb=None,
-                  dq_blocks=None, dk_blocks=None, scales="axis"):
+                  dq_blocks=None, dk_blocks=None, scales="axis", score_format="mxfp8"):
     """Backward pass for one head (Algorithm 1 steps 09-16 of the FLAMIA notes).
 
     o_saved: O as stored by the forward (output dtype); lse: the forward's row LSE (natural
@@ -373,6 +404,10 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
     ``scales``: the geometry of Q's, K's and V's scales, as in head_forward ("token_block":
     one exponent per 32-token block, so each tensor's ROW and SEQ views hold the same values).
     G is quantised inside the backward with per-axis groups either way.
+
+    ``score_format="mxfp4"`` rebuilds S from the same MXFP4 Q and K views as head_forward
+    (FLAMIA notes, section 3: the backward recomputes the scores with the original 4-bit Q/K
+    and takes E4M3 views for dQ and dK); every other product is unchanged.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -387,9 +422,8 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
     if quantized:
         assert scales in ("axis", "token_block"), scales
         tb = scales == "token_block"
-        Qr = _View(q, "token_block" if tb else "row")
+        Qr, Kr = _score_views(q, k, scales, score_format)
         Qs = Qr if tb else _View(q, "seq")
-        Kr = _View(k, "token_block" if tb else "row")
         Ks = Kr if tb else _View(k, "seq")
         Vr = _View(v, "token_block" if tb else "row")
         Gr, Gs = _View(g, "row"), _View(g, "seq")
@@ -450,7 +484,7 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
         mask = visible(rows, nk, causal, r0)[:, kc]
         live = mask & np.isfinite(lse[r0:r1])[:, None]
         if quantized:
-            Sraw = dot_rows(Qr.codes[r0:r1], Qr.blk_exp[r0:r1], Kr.codes[kc], Kr.blk_exp[kc])
+            Sraw = _scores(Qr, slice(r0, r1), Kr, kc)
             EmD = dot_rows(Gr.codes[r0:r1], Gr.blk_exp[r0:r1], Vr.codes[kc], Vr.blk_exp[kc], c0=-D32[r0:r1])
         else:
             Sraw = Qrx[r0:r1] @ Krx[kc].T

@@ -198,3 +198,121 @@ def mx_fake_quant_token_blocks(x):
     """decode(quantise(x)) with token-block scales (mx_quantize_token_blocks)."""
     codes, e, _ = mx_quantize_token_blocks(x)
     return np.ldexp(e4m3_decode(codes), np.repeat(e, GROUP)[: codes.shape[0], None])
+
+
+# ---------------------------------------------------------------------------------------------
+# MXFP4: E2M1 element codes with the same E8M0 scale per 32 elements.
+#
+# FLAMIA reading notes, section 2 ("two hardware formats"): the 4-bit element code is E2M1;
+# NVFP4 pairs it with an E4M3 scale per 16 elements (and an optional FP32 tensor scale).
+# The matrix core this library targets takes only E8M0 scales, one per 32 contraction
+# elements, so the 4-bit score operands here are MXFP4: E2M1 codes, one E8M0 scale per 32.
+# Readings (listed in DESIGN.md), chosen to mirror the E4M3 ones above:
+#   * E2M1: sign | 2-bit exponent (bias 1) | 1-bit mantissa; exponent field 0 is subnormal
+#     (0 or 0.5); largest magnitude 6; no infinities and no NaN.
+#   * group exponent: the smallest integer e with amax * 2^-e <= 6 (6 in place of 448);
+#   * conversion rounds to nearest, ties to the even code, keeps the sign (a negative value
+#     that rounds to zero encodes as 0x8), and saturates to +-6;
+#   * a group holding a NaN or an infinity gets scale byte 0xFF (E8M0 NaN) and codes 0x7.
+# ---------------------------------------------------------------------------------------------
+
+E2M1_MAX = 6.0
+E2M1_NAN_GROUP_CODE = 0x7
+
+
+def e2m1_decode(codes):
+    """Value of each E2M1 code (low 4 bits): sign | 2-bit exponent (bias 1) | 1-bit mantissa.
+
+    exponent field 0 -> subnormal m * 0.5; otherwise (1 + m/2) * 2^(E - 1)."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    efield = (c >> 1) & 0x3
+    mfield = c & 0x1
+    sub = mfield * 0.5
+    nrm = (1.0 + mfield / 2.0) * np.exp2(efield - 1.0)
+    return sign * np.where(efield == 0, sub, nrm)
+
+
+def e2m1_round(y):
+    """Round float64 values onto the E2M1 value grid (RNE, saturating to +-6). Returns values.
+
+    Grid spacing: 2^(E - 1) for |y| in [2^E, 2^(E+1)) with E >= 0, and 0.5 below 1 (the
+    subnormal step). Division by the power-of-two spacing is exact, so np.rint (half to even)
+    rounds a tie to the even multiple of the spacing, which is the code with mantissa 0."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    with np.errstate(invalid="ignore", over="ignore"):
+        _, ex = np.frexp(a)                 # a = f * 2^ex with f in [0.5, 1)
+        binade = np.maximum(ex - 1, 0)
+        step = np.ldexp(1.0, binade - 1)
+        q = np.rint(a / step) * step
+        q = np.where(q > E2M1_MAX, E2M1_MAX, q)
+    q = np.where(np.isnan(a), np.nan, q)
+    return np.copysign(q, y)
+
+
+def e2m1_encode(y):
+    """E2M1 code (0..15) of each float64 value: RNE onto the grid, then pack the bit fields."""
+    y = np.asarray(y, dtype=np.float64)
+    q = np.abs(e2m1_round(y))
+    q = np.where(np.isnan(q), 0.0, q)
+    _, ex = np.frexp(q)
+    e_unb = ex - 1
+    normal = q >= 1.0
+    efield = np.where(normal, e_unb + 1, 0)
+    mfield = np.where(normal, (q / np.ldexp(1.0, np.where(normal, e_unb, 0)) - 1.0) * 2.0, q / 0.5)
+    code = (efield.astype(np.int64) << 1) | np.rint(mfield).astype(np.int64)
+    code = code | (np.signbit(y).astype(np.int64) << 3)
+    return code.astype(np.uint8)
+
+
+def mx4_scale_exponent(amax):
+    """E8M0 exponent of an MXFP4 group: the smallest integer e with amax * 2^-e <= 6.
+
+    Written as the definition, like mx_scale_exponent: start below the answer and step up
+    while the inequality fails. amax == 0 gives -127; results are clamped to [-127, 127]."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))        # a in [2^(ex-1), 2^ex)
+    e = (ex - 1) - 3                                 # a * 2^-e in [8, 16): too big
+    for _ in range(3):
+        e = np.where(np.ldexp(a, -e) > E2M1_MAX, e + 1, e)
+    assert np.all((np.ldexp(a, -e) <= E2M1_MAX) | (a == 0))
+    assert np.all((np.ldexp(a, -(e - 1)) > E2M1_MAX) | (a == 0))
+    e = np.where(a > 0, e, E8M0_MIN_EXP)
+    return np.clip(e, E8M0_MIN_EXP, E8M0_MAX_EXP).astype(np.int64)
+
+
+def mx4_quantize_groups(x, axis):
+    """MXFP4 quantisation in groups of 32 consecutive elements along ``axis`` (as
+    mx_quantize_groups, with E2M1 codes and the E2M1 group rule). Returns (codes uint8 0..15
+    with the shape of x, exponents int64 per group, scale bytes uint8 per group)."""
+    x = np.asarray(x, dtype=np.float64)
+    xm = np.moveaxis(x, axis, -1)
+    n = xm.shape[-1]
+    ng = -(-n // GROUP)
+    pad = ng * GROUP - n
+    xp = np.concatenate([xm, np.zeros(xm.shape[:-1] + (pad,))], axis=-1) if pad else xm
+    blocks = xp.reshape(xm.shape[:-1] + (ng, GROUP))
+    finite = np.all(np.isfinite(blocks), axis=-1)
+    amax = np.max(np.abs(np.where(np.isfinite(blocks), blocks, 0.0)), axis=-1)
+    e = mx4_scale_exponent(amax)
+    codes = e2m1_encode(np.ldexp(np.where(np.isfinite(blocks), blocks, 0.0), -e[..., None]))
+    codes = np.where(finite[..., None], codes, E2M1_NAN_GROUP_CODE).astype(np.uint8)
+    sbytes = np.where(finite, e + E8M0_BIAS, E8M0_NAN).astype(np.uint8)
+    codes = codes.reshape(xp.shape)[..., :n]
+    return np.moveaxis(codes, -1, axis), np.moveaxis(e, -1, axis), np.moveaxis(sbytes, -1, axis)
+
+
+def mx4_dequantize_groups(codes, exps, axis):
+    """Inverse of mx4_quantize_groups: decode(code) * 2^e of the element's group."""
+    v = np.moveaxis(e2m1_decode(codes), axis, -1)
+    ee = np.repeat(np.moveaxis(np.asarray(exps), axis, -1), GROUP, axis=-1)[..., : v.shape[-1]]
+    return np.moveaxis(np.ldexp(v, ee), -1, axis)
+
+
+def mx4_pack_row(codes):
+    """Byte layout of an MXFP4 ROW view: two codes per byte along the last axis, the even
+    element in the low nibble."""
+    c = np.asarray(codes).astype(np.uint8)
+    assert c.shape[-1] % 2 == 0
+    return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
