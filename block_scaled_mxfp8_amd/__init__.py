@@ -8,6 +8,8 @@ not load the library; the first call does, and raises if it has not been built
 
 Functions mirror the C entry points:
     mx_quantize(x, views=ROW|SEQ, cu_seqlens=None, max_seqlen=None) -> (row QView, seq QView)
+        (views with MX_VIEW_ROW_FP4 in place of MX_VIEW_ROW: the row view in MXFP4, the 4-bit
+        score operands; attention calls given ROW_FP4 q_row / k_row score in MXFP4)
     mx_quantize_token_block(...): the same with one exponent per 32-token block (shared codes).
     mx_attn_fwd(q_row, k_row, v_seq, ...) -> (o, lse)
     mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, ...) -> (dq, dk, dv)
@@ -19,7 +21,7 @@ Functions mirror the C entry points:
     mx_rmsnorm_quantize(x, gamma, eps) -> (row QView, seq QView): RMSNorm written only as MX views.
     mx_gemm_quantize(a_row, b_row) -> (row QView, seq QView): C = A B^T written only as MX views.
 """
-from ._lib import (MX_VIEW_ROW, MX_VIEW_SEQ, MX_DQ_F32, MX_DQ_F16_BOOST, MXError, QView, lib_path, load,
+from ._lib import (MX_VIEW_ROW, MX_VIEW_SEQ, MX_VIEW_ROW_FP4, MX_SCORE_MXFP8, MX_SCORE_MXFP4, MX_DQ_F32, MX_DQ_F16_BOOST, MXError, QView, lib_path, load,
                    mx_abi_version, mx_attn_bwd, mx_attn_fwd, mx_attn_varlen_bwd, mx_attn_varlen_fwd, mx_quantize,
                    mx_attn_workspace_size, mx_read_flags, mx_profile_kernel, PROFILE_FWD, PROFILE_BWD_DKDV,
                    PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_DQ, mx_attn_cross_fwd, mx_attn_cross_bwd,
@@ -27,7 +29,7 @@ from ._lib import (MX_VIEW_ROW, MX_VIEW_SEQ, MX_DQ_F32, MX_DQ_F16_BOOST, MXError
                    PROFILE_GEMM, mx_quantize_token_block,
                    mx_attn_bwd_mx, mx_attn_bwd_noalloc)
 
-__all__ = ["MX_VIEW_ROW", "MX_VIEW_SEQ", "MX_DQ_F32", "MX_DQ_F16_BOOST", "MXError", "QView", "lib_path", "load",
+__all__ = ["MX_VIEW_ROW", "MX_VIEW_SEQ", "MX_VIEW_ROW_FP4", "MX_SCORE_MXFP8", "MX_SCORE_MXFP4", "MX_DQ_F32", "MX_DQ_F16_BOOST", "MXError", "QView", "lib_path", "load",
            "mx_abi_version", "mx_attn_bwd", "mx_attn_fwd", "mx_attn_varlen_bwd", "mx_attn_varlen_fwd", "mx_quantize",
            "mx_attn_workspace_size", "mx_read_flags", "mx_profile_kernel", "PROFILE_FWD", "PROFILE_BWD_DKDV",
            "PROFILE_QUANTIZE", "PROFILE_BWD_PREP", "PROFILE_BWD_DQ", "mx_attn_cross_fwd", "mx_attn_cross_bwd",

@@ -14,8 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 MX_OK, MX_E_ARG, MX_E_UNSUPPORTED, MX_E_WORKSPACE, MX_E_DEVICE = range(5)
 MX_F32, MX_BF16 = 0, 1
-MX_VIEW_ROW, MX_VIEW_SEQ = 1, 2
+MX_VIEW_ROW, MX_VIEW_SEQ, MX_VIEW_ROW_FP4 = 1, 2, 4
 MX_DQ_F32, MX_DQ_F16_BOOST = 0, 1
+MX_SCORE_MXFP8, MX_SCORE_MXFP4 = 0, 1
 
 
 class MXError(RuntimeError):
@@ -37,13 +38,32 @@ class _Desc(ctypes.Structure):
     _fields_ = [("seq", _Seq), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("out_dtype", ctypes.c_int32), ("dq_mode", ctypes.c_int32), ("deterministic", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("score_format", ctypes.c_int32)]
 
 
 class QView(NamedTuple):
     """One quantised view: uint8 codes and E8M0 scale bytes (layouts in include/mxattn.h)."""
     codes: torch.Tensor
     scales: torch.Tensor
+
+
+def _row_is_fp4(v):
+    """A ROW-type view is MXFP4 (ROW_FP4) when its codes hold 16 bytes per scale byte (E4M3: 32)."""
+    return v.codes.shape[-1] * 2 == v.scales.shape[-1] * 32
+
+
+def _elem_shape(v):
+    """Element shape of the tensor a ROW or ROW_FP4 view encodes."""
+    shape = tuple(v.codes.shape)
+    return shape[:-1] + (shape[-1] * 2,) if _row_is_fp4(v) else shape
+
+
+def _score_format(q_row, k_row):
+    fp4 = _row_is_fp4(q_row)
+    if _row_is_fp4(k_row) != fp4:
+        raise ValueError("q_row and k_row must both be ROW (E4M3) or both ROW_FP4 (MXFP4) views")
+    return MX_SCORE_MXFP4 if fp4 else MX_SCORE_MXFP8
 
 
 _LIB = None
@@ -209,7 +229,9 @@ def _seq_view_shapes(shape, seq, cu_seqlens):
 
 
 def mx_quantize(x, views=MX_VIEW_ROW | MX_VIEW_SEQ, cu_seqlens=None, max_seqlen=None):
-    """Quantise x ([B,H,L,d] or packed [T,H,d], fp32/bf16) -> (row QView or None, seq QView or None)."""
+    """Quantise x ([B,H,L,d] or packed [T,H,d], fp32/bf16) -> (row QView or None, seq QView or None).
+    views may hold MX_VIEW_ROW_FP4 instead of MX_VIEW_ROW: the row QView is then MXFP4 (codes
+    [..., d/2], two E2M1 codes per byte), the score operands of the mixed 4-bit path."""
     return _quantize(x, views, cu_seqlens, max_seqlen, "mx_quantize")
 
 
@@ -229,8 +251,10 @@ def _quantize(x, views, cu_seqlens, max_seqlen, name):
     row = seqv = None
     rv = _QView()
     sv = _QView()
-    if views & MX_VIEW_ROW:
-        row = QView(torch.empty(shape, dtype=torch.uint8, device=x.device),
+    row_view = MX_VIEW_ROW_FP4 if views & MX_VIEW_ROW_FP4 else MX_VIEW_ROW
+    if views & (MX_VIEW_ROW | MX_VIEW_ROW_FP4):
+        cshape = shape[:-1] + (d // 2,) if row_view == MX_VIEW_ROW_FP4 else shape
+        row = QView(torch.empty(cshape, dtype=torch.uint8, device=x.device),
                     torch.empty(shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device))
         rv = _qv(row)
     if views & MX_VIEW_SEQ:
@@ -238,7 +262,7 @@ def _quantize(x, views, cu_seqlens, max_seqlen, name):
         seqv = QView(torch.empty(cs, dtype=torch.uint8, device=x.device),
                      torch.empty(ss, dtype=torch.uint8, device=x.device))
         sv = _qv(seqv)
-    for v, view, what in ((row, MX_VIEW_ROW, "row view"), (seqv, MX_VIEW_SEQ, "seq view")):
+    for v, view, what in ((row, row_view, "row view"), (seqv, MX_VIEW_SEQ, "seq view")):
         if v is not None:
             _check_view(lib, v, seq, heads, d, view, what)
     st = getattr(lib, name)(ctypes.byref(seq), heads, d, x.data_ptr(), _dtype_code(x.dtype), views, ctypes.byref(rv),
@@ -310,7 +334,7 @@ def mx_gemm_quantize(a_row, b_row, views=MX_VIEW_ROW | MX_VIEW_SEQ):
 
 
 def _desc(q_shape, k_shape, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode=MX_DQ_F32,
-          deterministic=False, cross=None):
+          deterministic=False, cross=None, score_format=MX_SCORE_MXFP8):
     """cross = (cu_seqlens_k, max_seqlen_k) for cross-attention (k/v with their own lengths)."""
     d = _Desc()
     d.seq = _seq(q_shape, cu_seqlens, max_seqlen)
@@ -326,6 +350,7 @@ def _desc(q_shape, k_shape, cu_seqlens, max_seqlen, causal, softmax_scale, out_d
     d.out_dtype = _dtype_code(out_dtype)
     d.dq_mode = int(dq_mode)
     d.deterministic = 1 if deterministic else 0
+    d.score_format = int(score_format)
     return d
 
 
@@ -339,14 +364,16 @@ def _key_seq(k_shape, cross):
 
 def _fwd(name, q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen, cross=None):
     lib = load()
-    qs, ks = tuple(q_row.codes.shape), tuple(k_row.codes.shape)
-    desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, cross=cross)
+    qs, ks = _elem_shape(q_row), _elem_shape(k_row)
+    fmt = _score_format(q_row, k_row)
+    row_view = MX_VIEW_ROW_FP4 if fmt == MX_SCORE_MXFP4 else MX_VIEW_ROW
+    desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, cross=cross, score_format=fmt)
     dev = q_row.codes.device
     seq = desc.seq
     seq_k = _key_seq(ks, cross)
     kseq = seq if seq_k is None else seq_k
-    _check_view(lib, q_row, seq, desc.heads_q, desc.head_dim, MX_VIEW_ROW, "q_row")
-    _check_view(lib, k_row, kseq, desc.heads_kv, desc.head_dim, MX_VIEW_ROW, "k_row")
+    _check_view(lib, q_row, seq, desc.heads_q, desc.head_dim, row_view, "q_row")
+    _check_view(lib, k_row, kseq, desc.heads_kv, desc.head_dim, row_view, "k_row")
     _check_view(lib, v_seq, kseq, desc.heads_kv, desc.head_dim, MX_VIEW_SEQ, "v_seq")
     o = torch.empty(qs, dtype=out_dtype, device=dev)
     lse = torch.empty(qs[:-1], dtype=torch.float32, device=dev)
@@ -362,7 +389,9 @@ def _fwd(name, q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens
 
 def mx_attn_fwd(q_row, k_row, v_seq, causal=True, softmax_scale=0.0, out_dtype=torch.bfloat16, cu_seqlens=None,
                 max_seqlen=None):
-    """Forward attention from quantised views -> (o [like q], lse float32 [B,H,L] / [T,H])."""
+    """Forward attention from quantised views -> (o [like q], lse float32 [B,H,L] / [T,H]).
+    q_row and k_row are ROW views (E4M3 scores) or both ROW_FP4 views (MXFP4 scores, the mixed
+    path); the score format follows from the views."""
     return _fwd("mx_attn_fwd", q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen)
 
 
@@ -372,21 +401,26 @@ def mx_attn_varlen_fwd(q_row, k_row, v_seq, cu_seqlens, max_seqlen=None, causal=
 
 
 def mx_attn_workspace_size(q_shape, cu_seqlens=None, max_seqlen=None, heads_kv=None, dq_mode=MX_DQ_F32,
-                           causal=True, ds_store=True):
-    """Backward workspace bytes; ds_store=True includes the dS code store (O(L^2) bytes)."""
+                           causal=True, ds_store=True, score_format=MX_SCORE_MXFP8):
+    """Backward workspace bytes; ds_store=True includes the dS code store (O(L^2) bytes; always
+    included for MXFP4 scores, which need it)."""
     lib = load()
     k_shape = list(q_shape)
     if heads_kv is not None:
         k_shape[-3 if cu_seqlens is None else -2] = heads_kv
-    desc = _desc(tuple(q_shape), tuple(k_shape), cu_seqlens, max_seqlen, causal, 0.0, torch.bfloat16, dq_mode)
+    desc = _desc(tuple(q_shape), tuple(k_shape), cu_seqlens, max_seqlen, causal, 0.0, torch.bfloat16, dq_mode,
+                 score_format=score_format)
     return lib.mx_attn_workspace_size(ctypes.byref(desc), 2 if ds_store else 1)
 
 
 def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype, dq_mode, cu_seqlens,
          max_seqlen, workspace, deterministic=False, ds_store=True, cross=None, mx_views=0):
     lib = load()
-    qs, ks = tuple(q_row.codes.shape), tuple(k_row.codes.shape)
-    desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode, deterministic, cross)
+    qs, ks = _elem_shape(q_row), _elem_shape(k_row)
+    fmt = _score_format(q_row, k_row)
+    row_view = MX_VIEW_ROW_FP4 if fmt == MX_SCORE_MXFP4 else MX_VIEW_ROW
+    desc = _desc(qs, ks, cu_seqlens, max_seqlen, causal, softmax_scale, out_dtype, dq_mode, deterministic, cross,
+                 score_format=fmt)
     seq_k = _key_seq(ks, cross)
     kseq_p = None if seq_k is None else ctypes.byref(seq_k)
     dev = q_row.codes.device
@@ -408,13 +442,13 @@ def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_sca
     dv = torch.empty(ks, dtype=out_dtype, device=dev)
     seq = desc.seq
     kseq = seq if seq_k is None else seq_k
-    for v, sq, h, view, what in ((q_row, seq, desc.heads_q, MX_VIEW_ROW, "q_row"),
+    for v, sq, h, view, what in ((q_row, seq, desc.heads_q, row_view, "q_row"),
                                  (q_seq, seq, desc.heads_q, MX_VIEW_SEQ, "q_seq"),
-                                 (k_row, kseq, desc.heads_kv, MX_VIEW_ROW, "k_row"),
+                                 (k_row, kseq, desc.heads_kv, row_view, "k_row"),
                                  (k_seq, kseq, desc.heads_kv, MX_VIEW_SEQ, "k_seq"),
                                  (v_row, kseq, desc.heads_kv, MX_VIEW_ROW, "v_row")):
         _check_view(lib, v, sq, h, desc.head_dim, view, what)
-    nq = q_row.codes.numel()
+    nq = int(torch.Size(qs).numel())
     _check_tensor(o, nq, "o")
     _check_tensor(g, nq, "g")
     _check_tensor(lse, nq // desc.head_dim, "lse")

@@ -34,6 +34,11 @@
 //     the lane's 16 + 16 key values of its query are the B operand of dQ^T += K_seq^T dS^T,
 //     contracting over the 64 keys of the tile.
 // The SEQ views store each 32-token group in that contraction order (mx_layout.h seq_pos).
+// 4-bit scores (kF4; FLAMIA notes, section 3: the backward rebuilds S from the forward's 4-bit
+// Q and K and takes E4M3 views for dQ and dK): Q and K ROW views are MXFP4, and the dK/dV pass
+// forms S with E2M1 operands (cbsz = blgp = 4: 16 bytes per lane, lane half h holding
+// contraction indices 32h .. 32h + 31; a Q ROW tile row is d/2 bytes). Only that pass rebuilds
+// S: the dQ pass then reads the stored dS codes, so this mode requires the store.
 // E8M0 group exponents are exact functions of the group max-abs bits; codes come from
 // v_cvt_scalef32_pk_fp8_f32 (x / 2^e, RNE). Group maxima use DPP and lane permutes, no LDS.
 #include "mx_device.h"
@@ -136,7 +141,7 @@ __device__ __forceinline__ void dma_seq_tile(const uint8_t* codes, long long row
 // One 64-query step in LDS, written entirely by LDS-DMA.
 template <int D>
 struct DkvStage {
-  alignas(16) uint8_t qr[kStepQ * D];   // Q ROW codes [query][d], row_swz chunks
+  alignas(16) uint8_t qr[kStepQ * D];   // Q ROW codes [query][d] (E2M1: [query][d/2]), row_swz chunks
   alignas(16) uint8_t gr[kStepQ * D];   // G ROW codes
   alignas(16) uint8_t qs[2 * D * 32];   // Q SEQ codes [group][channel][32], half_swz halves
   alignas(16) uint8_t gs[2 * D * 32];   // G SEQ codes
@@ -207,11 +212,12 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p, int* smem) {
 // 4 the Q SEQ scales, 5 the G SEQ scales (dword lane % (d/2) of the step's two groups, the
 // second clamped to the last group). Rows past the end are clamped to the last row (finite
 // codes and values); the masked tile code gives them P = 0 and U = 0.
-template <int D, bool kPacked, int NL>
+template <int D, bool kPacked, int NL, bool kF4>
 __device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
                                               int lw) {
   static_assert(NL >= 6, "six small-item loaders");
   constexpr int NCH = D / 16, RPI = 64 / NCH;
+  constexpr int NCHQ = kF4 ? NCH / 2 : NCH, RPIQ = 64 / NCHQ;   // Q ROW tile (E2M1: d/2 bytes a row)
   const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
   const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
@@ -242,8 +248,19 @@ __device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& 
     if (NCH % NL == 0 || j < NCH) {
       const int row = j * RPI + lrow;
       const int vo = (full ? row : min(row, rmax)) * ts + row_swz(row, lane % NCH, NCH) * 16;
-      lds_dma(p.q_codes + off0 + (uint32_t)vo, st.qr + j * 1024, 16);
+      if (!kF4) lds_dma(p.q_codes + off0 + (uint32_t)vo, st.qr + j * 1024, 16);
       lds_dma(p.gr_codes + off0 + (uint32_t)vo, st.gr + j * 1024, 16);
+    }
+  }
+  if (kF4) {
+#pragma unroll
+    for (int j0 = 0; j0 < NCHQ; j0 += NL) {
+      const int j = j0 + lw;
+      if (NCHQ % NL == 0 || j < NCHQ) {
+        const int row = j * RPIQ + lane / NCHQ;
+        const int vo = (full ? row : min(row, rmax)) * (ts >> 1) + row_swz(row, lane % NCHQ, NCHQ) * 16;
+        lds_dma(p.q_codes + (off0 >> 1) + (uint32_t)vo, st.qr + j * 1024, 16);
+      }
     }
   }
 }
@@ -294,10 +311,11 @@ __device__ __forceinline__ int p_scale_exp(float amax) {
 //
 // `mid` runs after the S and E products are issued, while the matrix cores work on them (the
 // producers issue the next step's loads there).
-template <int D, bool kMask, class Mid>
+template <int D, bool kMask, bool kF4, class Mid>
 __device__ __forceinline__ int dkv_codes_tile(const DkvStage<D>& S, int qt, const v8i* kop, const v8i* vop,
-                                               uint32_t kvsc, const int* roff_ab, int fidx, float c, int rel, int lim,
-                                               bool kvalid, bool causal, uint32_t* cx, int slot_off, Mid&& mid) {
+                                               uint32_t kvsc, const int* roff_ab, const int* roff_q, int fidx, float c,
+                                               int rel, int lim, bool kvalid, bool causal, uint32_t* cx, int slot_off,
+                                               Mid&& mid) {
   constexpr int NS = D / 64;
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
@@ -315,10 +333,11 @@ __device__ __forceinline__ int dkv_codes_tile(const DkvStage<D>& S, int qt, cons
 #pragma unroll
   for (int s = 0; s < NS; s++) {
     const int o0 = qt * 32 * D + roff_ab[2 * s], o1 = qt * 32 * D + roff_ab[2 * s + 1];
-    const v8i qa = cat(*reinterpret_cast<const v4i*>(&S.qr[o0]), *reinterpret_cast<const v4i*>(&S.qr[o1]));
+    const v8i qa = kF4 ? cat(*reinterpret_cast<const v4i*>(&S.qr[qt * 16 * D + roff_q[s]]), v4i{})
+                       : cat(*reinterpret_cast<const v4i*>(&S.qr[o0]), *reinterpret_cast<const v4i*>(&S.qr[o1]));
     const v8i ga = cat(*reinterpret_cast<const v4i*>(&S.gr[o0]), *reinterpret_cast<const v4i*>(&S.gr[o1]));
-    sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kop[s], sacc, 0, 0, 0, (int)(qsw >> (16 * s)), 0,
-                                                           (int)(kvsc >> (8 * s)));
+    sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kop[s], sacc, kF4 ? 4 : 0, kF4 ? 4 : 0, 0,
+                                                           (int)(qsw >> (16 * s)), 0, (int)(kvsc >> (8 * s)));
     eacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ga, vop[s], eacc, 0, 0, 0, (int)(gsw >> (16 * s)), 0,
                                                            (int)(kvsc >> (16 + 8 * s)));
   }
@@ -529,8 +548,9 @@ __device__ __forceinline__ void dkv_mx_views(const BwdParams& p, const KvWork& w
   }
 }
 
-template <int D, bool kPacked, bool kStore, bool kMxOut = false>
+template <int D, bool kPacked, bool kStore, bool kMxOut = false, bool kF4 = false>
 __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+  static_assert(!kF4 || kStore, "the 4-bit score path needs the dS store");
   __shared__ DkvShared<D> sm;
   const KvWork w = decode_kv<kPacked>(p, reinterpret_cast<int*>(&sm));
   if (!w.valid) return;
@@ -564,25 +584,30 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
 #pragma unroll
     for (int s = 0; s < NS; s++) {
       const long long off = elem_offset_k<kPacked>(gk, p.heads_kv, D, sbase_k, w.hkv, min(key, w.nk - 1), 64 * s);
-      kop[s] = cat(*reinterpret_cast<const v4i*>(p.k_codes + off + 16 * hh),
-                   *reinterpret_cast<const v4i*>(p.k_codes + off + 32 + 16 * hh));
+      if (kF4)   // channels 64s + 32h .. + 31: 16 bytes at element offset / 2
+        kop[s] = cat(*reinterpret_cast<const v4i*>(p.k_codes + (off >> 1) + 16 * hh), v4i{});
+      else
+        kop[s] = cat(*reinterpret_cast<const v4i*>(p.k_codes + off + 16 * hh),
+                     *reinterpret_cast<const v4i*>(p.k_codes + off + 32 + 16 * hh));
       vop[s] = cat(*reinterpret_cast<const v4i*>(p.vr_codes + off + 16 * hh),
                    *reinterpret_cast<const v4i*>(p.vr_codes + off + 32 + 16 * hh));
       kvsc |= ((uint32_t)p.k_scales[(off >> 5) + hh] << (8 * s)) |
               ((uint32_t)p.vr_scales[(off >> 5) + hh] << (16 + 8 * s));
     }
     int roff_ab[2 * NS];                  // ROW tile, row l32: chunks 4s + hh and 4s + 2 + hh
+    int roff_q[NS];                       // E2M1 Q ROW tile (d/2 bytes a row), row l32: chunk 2s + hh
 #pragma unroll
     for (int s = 0; s < NS; s++) {
       roff_ab[2 * s] = l32 * D + (row_swz(l32, 4 * s + hh, D / 16) << 4);
       roff_ab[2 * s + 1] = l32 * D + (row_swz(l32, 4 * s + 2 + hh, D / 16) << 4);
+      roff_q[s] = kF4 ? l32 * (D / 2) + (row_swz(l32, 2 * s + hh, D / 32) << 4) : 0;
     }
     const int fidx = 4 * hh;              // LSE / D index of the lane's rows
     const int slot_off = ds_slot_off(lane);
     const int kb = kw >> 5;               // key group of the dS blocks
     int hq = w.hkv * group;               // head of step j
     int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
-    dkv_issue_row<D, kPacked, kDkvProducers>(p, w, hq_l, q0_l, sm.st[0], lw);
+    dkv_issue_row<D, kPacked, kDkvProducers, kF4>(p, w, hq_l, q0_l, sm.st[0], lw);
     wait_vmem();
     wg_barrier();                         // stage 0 loaded
     int q0 = qfirst;                      // step whose codes are computed (j)
@@ -594,8 +619,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
       // the last step they reload the first step, whose addresses are valid, into stage
       // (j + 1) % 3, which nobody reads then.
       auto issue = [&]() __attribute__((always_inline)) {
-        dkv_issue_row<D, kPacked, kDkvProducers>(p, w, load ? hq_l : w.hkv * group, load ? q0_l : qfirst,
-                                                 sm.st[(j + 1) % 3], lw);
+        dkv_issue_row<D, kPacked, kDkvProducers, kF4>(p, w, load ? hq_l : w.hkv * group, load ? q0_l : qfirst,
+                                                      sm.st[(j + 1) % 3], lw);
       };
       bool stored = false;
       if (j < nsteps && active(q0)) {
@@ -604,11 +629,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.nk;
         int dse;
         if (need_mask)
-          dse = dkv_codes_tile<D, true>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, q0 + 4 * hh - key,
-                                        w.n - q0 - 4 * hh, kvalid, p.causal, cx, slot_off, issue);
+          dse = dkv_codes_tile<D, true, kF4>(S, qt, kop, vop, kvsc, roff_ab, roff_q, fidx, c, q0 + 4 * hh - key,
+                                             w.n - q0 - 4 * hh, kvalid, p.causal, cx, slot_off, issue);
         else
-          dse = dkv_codes_tile<D, false>(S, qt, kop, vop, kvsc, roff_ab, fidx, c, 0, 0, true, false, cx, slot_off,
-                                         issue);
+          dse = dkv_codes_tile<D, false, kF4>(S, qt, kop, vop, kvsc, roff_ab, roff_q, fidx, c, 0, 0, true, false, cx,
+                                              slot_off, issue);
         // kStore: this wave's dS block (query group qb, key group kb; under causal only kb <= qb),
         // read back transposed from the exchange buffer (the wave's own LDS writes, in order)
         const int qb = (q0 >> 5) + qt;
@@ -1223,7 +1248,15 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
   const bool store = p.ds_codes != nullptr;
   const bool mx = p.dkr_codes || p.dks_codes || p.dvr_codes || p.dvs_codes;
   int slot = profile_begin(kProfBwdKV, stream);
-  if (mx) {
+  if (p.score_fp4) {   // (the host rejects this mode without the store)
+    if (packed(g)) {
+      if (mx) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, true, true, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, true, false, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+    } else {
+      if (mx) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, true, true, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+      else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, true, false, true>), gkv, dim3(kDkvThreads), 0, stream, p);
+    }
+  } else if (mx) {
     if (packed(g)) {
       if (store) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, true, true>), gkv, dim3(kDkvThreads), 0, stream, p);
       else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, false, true>), gkv, dim3(kDkvThreads), 0, stream, p);

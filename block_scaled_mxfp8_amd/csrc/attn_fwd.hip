@@ -36,6 +36,11 @@
 //    accumulator splits keys between l and l^32 -- no cross-lane data movement. The V SEQ view
 //    stores each 32-token group in that order (mx_layout.h seq_pos), so V^T operands are
 //    contiguous 16-byte LDS reads; the E8M0 scale of contraction block b comes from lane r+32b.
+//  * 4-bit scores (kF4; FLAMIA notes, sections 2 and 3, the mixed route: Q and K as MXFP4, V and
+//    P as E4M3): the same instruction with E2M1 operands (cbsz = blgp = 4). An E2M1 operand is
+//    16 bytes per lane, lane half h holding contraction indices 32h .. 32h + 31 in order (two
+//    codes per byte, low nibble first; the instruction reads 4 registers), so a K ROW tile row
+//    is d/2 bytes and each product reads one 16-byte chunk per lane.
 #include "mx_device.h"
 #include "mx_internal.h"
 #include "mx_layout.h"
@@ -57,8 +62,9 @@ constexpr float kLog2_448 = 8.807354922057604f;
 constexpr float kTau = 8.f;           // largest lag of the reference max behind the running max
 
 // LDS tiles, written by LDS-DMA loads (lane i of a load lands at base + i * size).
-//  k:  K ROW codes [64 keys][d]; 16-byte chunks swizzled by row (mx_device.h row_swz) so
-//      the rows an operand read touches spread over all banks.
+//  k:  K ROW codes [64 keys][d] (E2M1: [64 keys][d/2], the first half of the slot); 16-byte
+//      chunks swizzled by row (mx_device.h row_swz) so the rows an operand read touches spread
+//      over all banks.
 //  v:  V SEQ codes [2 groups][d channels][32 tokens]; the two 16-byte halves of channel ch
 //      are swapped when (ch >> 3) & 1 (half_swz), for the same reason.
 //  ks: K ROW scales, one dword per key (its d/32 bytes; at d = 64 the upper half is unused);
@@ -138,12 +144,17 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // parity of j, which is the wave's), and so is its part of a V-code address (channel lane / 2,
 // logical half (lane & 1) ^ bit 4 of the lane); each is computed once (kl, vl) and added to a
 // wave-uniform base.
-template <int D, bool kPacked>
+// Bytes of one K ROW code row: d (E4M3) or d/2 (E2M1).
+template <int D, bool kF4>
+constexpr int kRowBytes = kF4 ? D / 2 : D;
+
+template <int D, bool kPacked, bool kF4>
 __device__ __forceinline__ uint32_t k_lane_off(const AttnParams& p, int wave) {
-  constexpr int NCH = D / 16, RPI = 64 / NCH;
+  constexpr int NCH = kRowBytes<D, kF4> / 16, RPI = 64 / NCH;
   const int lane = threadIdx.x & 63;
   const int row = (wave & 1) * RPI + lane / NCH;   // row of instruction j = wave, mod the swizzle period
-  return (uint32_t)((lane / NCH) * (int)token_stride_k<kPacked>(p.heads_kv, D) + row_swz(row, lane % NCH, NCH) * 16);
+  const int tsb = (int)token_stride_k<kPacked>(p.heads_kv, D) / (kF4 ? 2 : 1);
+  return (uint32_t)((lane / NCH) * tsb + row_swz(row, lane % NCH, NCH) * 16);
 }
 __device__ __forceinline__ uint32_t v_lane_off() {
   const int lane = threadIdx.x & 63;
@@ -156,62 +167,69 @@ struct KvBase {
   const uint8_t* ks;   // K ROW scales of key 0
   const uint8_t* v;    // V SEQ codes of group 0 (the groups of a sequence are consecutive rows)
   const uint8_t* vs;   // V SEQ scales of group 0
-  int ts;              // token stride of K, in elements (= bytes of codes)
+  int ts;              // token stride of K, in elements
+  int tsb;             // token stride of the K codes, in bytes (ts, or ts / 2 for E2M1)
   int n;               // tokens
 };
 
-template <int D, bool kPacked>
+template <int D, bool kPacked, bool kF4>
 __device__ __forceinline__ KvBase kv_base(const AttnParams& p, const Work& w, int hkv) {
   const Geom& g = p.geom_k;
   const long long sbase = kPacked ? (long long)w.doc_k : (long long)w.s;
   const long long k0 = elem_offset_k<kPacked>(g, p.heads_kv, D, sbase, hkv, 0, 0);
   const long long row0 = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, hkv, w.doc_k, 0);
   KvBase b;
-  b.k = p.k_codes + k0;
+  b.k = p.k_codes + (kF4 ? k0 >> 1 : k0);
   b.ks = p.k_scales + (k0 >> 5);
   b.v = p.v_codes + row0 * (D * 32);
   b.vs = p.v_scales + row0 * D;
   b.ts = (int)token_stride_k<kPacked>(p.heads_kv, D);
+  b.tsb = kF4 ? b.ts >> 1 : b.ts;
   b.n = w.nk;
   return b;
 }
 
-// Issue the LDS-DMA loads of K tile kt into `kt_lds` / `ks_lds`: kNj code instructions per
-// wave, and on wave 0 the scales (one key per lane; at d = 64 a 2-byte DMA, which lands in
-// the low half of the key's dword). Rows past the end of the sequence / document are clamped
-// to its last row: they are finite, and their scores are masked, so their P is 0.
-template <int D>
-constexpr int kNj = D / 16 / kWaves;
-
-template <int D>
+// Issue the LDS-DMA loads of K tile kt into `kt_lds` / `ks_lds`: the tile's code instructions
+// j = wave, wave + 4, ... (64/NCH rows of NCH 16-byte chunks each; NI = 8 or 4 instructions for
+// E4M3 rows of d = 128 or 64, 4 or 2 for E2M1 rows), and on wave 0 the scales (one key per
+// lane; at d = 64 a 2-byte DMA, which lands in the low half of the key's dword). Rows past the
+// end of the sequence / document are clamped to its last row: they are finite, and their scores
+// are masked, so their P is 0.
+template <int D, bool kF4>
 __device__ __forceinline__ void issue_k(const KvBase& b, int kt, int wave, uint8_t* kt_lds, uint32_t* ks_lds,
                                         uint32_t kl, uint32_t ksl) {
-  constexpr int NCH = D / 16, RPI = 64 / NCH;
+  constexpr int NCH = kRowBytes<D, kF4> / 16, RPI = 64 / NCH, NI = NCH;
+  constexpr int NJ = (NI + kWaves - 1) / kWaves;
   const int k0 = kt * kBlockN;
   const int rmax = b.n - 1 - k0;            // last row of the tile inside the sequence
-  const uint8_t* kb = b.k + (long long)k0 * b.ts;
+  const uint8_t* kb = b.k + (long long)k0 * b.tsb;
   const uint8_t* ksb = b.ks + (((long long)k0 * b.ts) >> 5);
   if (rmax >= kBlockN - 1) {
 #pragma unroll
-    for (int jj = 0; jj < kNj<D>; jj++) {
+    for (int jj = 0; jj < NJ; jj++) {
       const int j = wave + jj * kWaves;
-      lds_dma_so(kb + (long long)j * RPI * b.ts, kl, kt_lds + j * 1024, 16);
+      if (NI % kWaves == 0 || j < NI) lds_dma_so(kb + (long long)j * RPI * b.tsb, kl, kt_lds + j * 1024, 16);
     }
     if (wave == 0) lds_dma_so(ksb, ksl, ks_lds, D / 32);
     asm volatile("" ::: "memory");        // keeps the clamped path's loads separate
   } else {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int jj = 0; jj < kNj<D>; jj++) {
+    for (int jj = 0; jj < NJ; jj++) {
       const int j = wave + jj * kWaves;
+      if (NI % kWaves != 0 && j >= NI) continue;
       const int r = j * RPI + lane / NCH;
-      const int o = min(r, rmax) * b.ts + row_swz(r, lane % NCH, NCH) * 16;
+      const int o = min(r, rmax) * b.tsb + row_swz(r, lane % NCH, NCH) * 16;
       lds_dma(kb + (uint32_t)o, kt_lds + j * 1024, 16);
     }
     if (wave == 0) lds_dma(ksb + ((uint32_t)(min(lane, rmax) * b.ts) >> 5), ks_lds, D / 32);
     asm volatile("" ::: "memory");
   }
 }
+
+// V-code DMA instructions per wave and tile (64 x 16 bytes each; 2 d x 32 bytes per tile).
+template <int D>
+constexpr int kNj = D / 16 / kWaves;
 
 // Issue the LDS-DMA loads of V tile kt (SEQ groups 2kt and 2kt + 1, the second clamped to the
 // last group) into `vt_lds` / `vs_lds`: kNj code instructions per wave (64 x 16 bytes of the
@@ -235,13 +253,30 @@ __device__ __forceinline__ void issue_v(const KvBase& b, int kt, int wave, uint8
     lds_dma_so(b.vs + (long long)(2 * kt) * D, two ? vsl : vsl % D, vs_lds, 4);
 }
 
+// The A operand of score product (half tile T, channel step s) from K slot `k` (the lane's key
+// row T * 32 + l32): E4M3 chunks 4s + h and 4s + 2 + h, or the E2M1 chunk 2s + h.
+template <int D, bool kF4>
+__device__ __forceinline__ v8i k_operand(const uint8_t* k, int T, int s, int hh, int l32) {
+  constexpr int KR = kRowBytes<D, kF4>, NCH = KR / 16;
+  const int row = T * 32 + l32;
+  if (kF4) return cat(*reinterpret_cast<const v4i*>(&k[row * KR + (row_swz(row, 2 * s + hh, NCH) << 4)]), v4i{});
+  const v4i a = *reinterpret_cast<const v4i*>(&k[row * KR + (row_swz(row, 4 * s + hh, NCH) << 4)]);
+  const v4i b = *reinterpret_cast<const v4i*>(&k[row * KR + (row_swz(row, 4 * s + 2 + hh, NCH) << 4)]);
+  return cat(a, b);
+}
+
+// One score product: E4M3 or (kF4) E2M1 operands on both sides.
+template <bool kF4>
+__device__ __forceinline__ v16f score_mfma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kF4 ? 4 : 0, kF4 ? 4 : 0, 0, sa, 0, sb);
+}
+
 // S^T for the two 32-key half tiles of K slot st: keys are MFMA rows, the wave's 32 queries columns.
-template <int D>
+template <int D, bool kF4>
 __device__ __forceinline__ void scores(const FwdSmem<D>& sm, int st, const v8i* qop, const int* qsc, v16f* sacc) {
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5, l32 = lane & 31;
   constexpr int NS = D / 64;
-  constexpr int NCH = D / 16;
   uint32_t ksw[2];
 #pragma unroll
   for (int T = 0; T < 2; T++) {
@@ -253,11 +288,8 @@ __device__ __forceinline__ void scores(const FwdSmem<D>& sm, int st, const v8i* 
   for (int s = 0; s < NS; s++) {
 #pragma unroll
     for (int T = 0; T < 2; T++) {
-      const int row = T * 32 + l32;
-      const v4i a = *reinterpret_cast<const v4i*>(&sm.k[st][row * D + (row_swz(row, 4 * s + hh, NCH) << 4)]);
-      const v4i b = *reinterpret_cast<const v4i*>(&sm.k[st][row * D + (row_swz(row, 4 * s + 2 + hh, NCH) << 4)]);
       const int ksc = (ksw[T] >> (8 * (2 * s + hh))) & 0xFF;
-      sacc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), qop[s], sacc[T], 0, 0, 0, ksc, 0, qsc[s]);
+      sacc[T] = score_mfma<kF4>(k_operand<D, kF4>(sm.k[st], T, s, hh, l32), qop[s], sacc[T], ksc, qsc[s]);
     }
   }
 }
@@ -368,14 +400,13 @@ __device__ __forceinline__ float softmax_tile(v16f (&cur)[2], float c_rt, int li
 // issued right after the previous product, a chunk ahead of their use.
 // Chunks: 0 the two groups' max trees; 1 the lane exchange, reference max, rescale factor;
 // 2-5 eight exponent arguments and exp2 each; 6 the sums and the group exponents; 7 the codes.
-template <int D, bool kLit>
+template <int D, bool kLit, bool kF4>
 __device__ __forceinline__ float whole_tile(const FwdSmem<D>& sm, int kst, int vst, const v8i* qop, const int* qsc,
                                             v16f (&cur)[2], v16f (&nxt)[2], const v8i& pprev, int pscprev, v16f* oacc,
                                             float c_rt, float& M, float& lsum, v8i& pop, int& psc) {
   constexpr int NPV = D / 32, NS = D / 64, NP = NPV + 2 * NS;
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5, l32 = lane & 31;
-  constexpr int NCH = D / 16;
   const float c = kLit ? default_c<D>() : c_rt;
   // operands of product i: P V of channel block i (i < NPV), else the scores of half tile
   // T = (i - NPV) % 2 over channel step s = (i - NPV) / 2
@@ -393,10 +424,7 @@ __device__ __forceinline__ float whole_tile(const FwdSmem<D>& sm, int kst, int v
         ksw0 = sm.ks[kst][l32];
         ksw1 = sm.ks[kst][32 + l32];
       }
-      const int row = T * 32 + l32;
-      const v4i a = *reinterpret_cast<const v4i*>(&sm.k[kst][row * D + (row_swz(row, 4 * s + hh, NCH) << 4)]);
-      const v4i b = *reinterpret_cast<const v4i*>(&sm.k[kst][row * D + (row_swz(row, 4 * s + 2 + hh, NCH) << 4)]);
-      A = cat(a, b);
+      A = k_operand<D, kF4>(sm.k[kst], T, s, hh, l32);
       sc = (int)(((T ? ksw1 : ksw0) >> (8 * (2 * s + hh))) & 0xFF);
     }
   };
@@ -405,8 +433,7 @@ __device__ __forceinline__ float whole_tile(const FwdSmem<D>& sm, int kst, int v
       oacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, pprev, oacc[i], 0, 0, 0, sc, 0, pscprev);
     } else {
       const int T = (i - NPV) & 1, s = (i - NPV) >> 1;
-      nxt[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, qop[s], s == 0 ? v16f{} : nxt[T], 0, 0, 0, sc, 0,
-                                                               qsc[s]);
+      nxt[T] = score_mfma<kF4>(A, qop[s], s == 0 ? v16f{} : nxt[T], sc, qsc[s]);
     }
   };
   v8i opa[2];
@@ -497,7 +524,7 @@ __device__ __forceinline__ void pin_tile_results(const v8i& pcur, int psc, float
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool kPacked, bool kLit>
+template <int D, bool kPacked, bool kLit, bool kF4>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<D> sm;
   const Work w = decode_work<kPacked>(p, reinterpret_cast<int*>(&sm));
@@ -515,13 +542,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   const bool qvalid = qi < w.n;
   const int kend = p.causal ? min(w.n, q0 + kBlockM) : w.nk;  // keys this workgroup needs (may be 0)
   const int nkt = (kend + kBlockN - 1) / kBlockN;
-  const uint32_t kl = k_lane_off<D, kPacked>(p, wave), vl = v_lane_off();
+  const uint32_t kl = k_lane_off<D, kPacked, kF4>(p, wave), vl = v_lane_off();
   const uint32_t ksl = (uint32_t)(lane * (int)token_stride_k<kPacked>(p.heads_kv, D)) >> 5;   // K scales of key `lane`
   const uint32_t vsl = (uint32_t)(lane * 4);
 
-  const KvBase kvb = kv_base<D, kPacked>(p, w, hkv);
-  if (nkt > 0) issue_k<D>(kvb, 0, wave, sm.k[0], sm.ks[0], kl, ksl);
-  if (nkt > 1) issue_k<D>(kvb, 1, wave, sm.k[1], sm.ks[1], kl, ksl);
+  const KvBase kvb = kv_base<D, kPacked, kF4>(p, w, hkv);
+  if (nkt > 0) issue_k<D, kF4>(kvb, 0, wave, sm.k[0], sm.ks[0], kl, ksl);
+  if (nkt > 1) issue_k<D, kF4>(kvb, 1, wave, sm.k[1], sm.ks[1], kl, ksl);
 
   // ---- Q operand (B of S^T = K Q^T), kept in registers ----
   constexpr int NS = D / 64;  // contraction steps of 64 over d
@@ -531,8 +558,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   for (int s = 0; s < NS; s++) {
     if (qvalid) {
       const long long off = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, w.h, qi, 64 * s);
-      qop[s] = cat(*reinterpret_cast<const v4i*>(p.q_codes + off + 16 * hh),
-                   *reinterpret_cast<const v4i*>(p.q_codes + off + 32 + 16 * hh));
+      if (kF4)   // channels 64s + 32h .. + 31: 16 bytes at element offset / 2
+        qop[s] = cat(*reinterpret_cast<const v4i*>(p.q_codes + (off >> 1) + 16 * hh), v4i{});
+      else
+        qop[s] = cat(*reinterpret_cast<const v4i*>(p.q_codes + off + 16 * hh),
+                     *reinterpret_cast<const v4i*>(p.q_codes + off + 32 + 16 * hh));
       qsc[s] = p.q_scales[(off >> 5) + hh];
     } else {
       qop[s] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -556,7 +586,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   wait_vmem();
   __syncthreads();
   v16f sa[2], sb[2];
-  scores<D>(sm, 0, qop, qsc, sa);
+  scores<D, kF4>(sm, 0, qop, qsc, sa);
   wg_barrier();   // every wave has read K slot 0 before the first tile loads K(2) into it
   v8i pa = v8i{0, 0, 0, 0, 0, 0, 0, 0}, pb = v8i{0, 0, 0, 0, 0, 0, 0, 0};   // P codes of even / odd tiles
   int psa = 127, psb = 127;
@@ -578,16 +608,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
                   v8i& pcur, int& psccur) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
     constexpr bool kMask = decltype(masked)::value;
-    if (j + 2 < nkt) issue_k<D>(kvb, j + 2, wave, sm.k[P], sm.ks[P], kl, ksl);
+    if (j + 2 < nkt) issue_k<D, kF4>(kvb, j + 2, wave, sm.k[P], sm.ks[P], kl, ksl);
     issue_v<D>(kvb, j, wave, sm.v[P], sm.vs[P], vl, vsl);
     float f;
     if (kMask) {
       pv<D>(sm, P ^ 1, pprev, pscprev, oacc);
-      scores<D>(sm, P ^ 1, qop, qsc, nxt);
+      scores<D, kF4>(sm, P ^ 1, qop, qsc, nxt);
       f = softmax_tile<true, kLit, D>(cur, c, vis_end - j * kBlockN - 4 * hh, M, lsum, pcur, psccur);
       interleave_tile();
     } else {
-      f = whole_tile<D, kLit>(sm, P ^ 1, P ^ 1, qop, qsc, cur, nxt, pprev, pscprev, oacc, c, M, lsum, pcur, psccur);
+      f = whole_tile<D, kLit, kF4>(sm, P ^ 1, P ^ 1, qop, qsc, cur, nxt, pprev, pscprev, oacc, c, M, lsum, pcur,
+                                   psccur);
     }
     // the tile's work stays ahead of the barrier: its results are used here (otherwise the
     // compiler moves the arithmetic down to where the next tile first needs it)
@@ -676,8 +707,13 @@ hipError_t launch_attn_fwd(const AttnParams& p, hipStream_t stream) {
   const int slot = profile_begin(kProfFwd, stream);
 #define MX_FWD_LAUNCH(DD, PK)                                                                            \
   do {                                                                                                   \
-    if (lit) hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, true>), grid, dim3(256), 0, stream, p);       \
-    else hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, false>), grid, dim3(256), 0, stream, p);          \
+    if (p.score_fp4) {                                                                                   \
+      if (lit) hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, true, true>), grid, dim3(256), 0, stream, p); \
+      else hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, false, true>), grid, dim3(256), 0, stream, p);    \
+    } else {                                                                                             \
+      if (lit) hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, true, false>), grid, dim3(256), 0, stream, p);\
+      else hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, false, false>), grid, dim3(256), 0, stream, p);   \
+    }                                                                                                    \
   } while (0)
   if (packed(g)) {
     if (p.head_dim == 128) MX_FWD_LAUNCH(128, true);

@@ -40,6 +40,36 @@ __device__ __forceinline__ int scale_exp_from_bits(uint32_t abits) {
   return e < kExpMin ? kExpMin : (e > kExpMax ? kExpMax : e);
 }
 
+// E8M0 exponent of an MXFP4 group (E2M1 codes, largest magnitude 6 = 1.5 * 2^2): the smallest
+// e with amax / 2^e <= 6, i.e. e = E - 2 + [m > 1.5] for amax = m * 2^E, m in [1, 2).
+__device__ __forceinline__ int scale_exp4_from_bits(uint32_t abits) {
+  if (abits == 0) return kExpMin;
+  int E;
+  uint32_t frac;
+  if (abits >= 0x00800000u) {
+    E = (int)(abits >> 23) - 127;
+    frac = abits & 0x7FFFFFu;
+  } else {  // subnormal amax = abits * 2^-149
+    int msb = 31 - __builtin_clz(abits);
+    E = msb - 149;
+    frac = (abits << (23 - msb)) & 0x7FFFFFu;
+  }
+  int e = E - 2 + (frac > 0x400000u ? 1 : 0);
+  return e < kExpMin ? kExpMin : (e > kExpMax ? kExpMax : e);
+}
+
+// Eight E2M1 codes of x[i] * 2^-e (RNE, sign kept; v_cvt_scalef32_pk_fp4_f32 with scale 1 on
+// the exactly scaled values), two per byte with x[2j] in the low nibble of byte j. Callers pass
+// e from scale_exp4_from_bits of the group, so |x| * 2^-e <= 6.
+__device__ __forceinline__ uint32_t pack8_e2m1(const float* x, int e) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, ldexpf(x[0], -e), ldexpf(x[1], -e), 1.f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, ldexpf(x[2], -e), ldexpf(x[3], -e), 1.f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, ldexpf(x[4], -e), ldexpf(x[5], -e), 1.f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, ldexpf(x[6], -e), ldexpf(x[7], -e), 1.f, 3);
+  return w;
+}
+
 // Four E4M3 codes (RNE) packed little-endian into one dword. Each conversion writes one half
 // of its destination and keeps the other; the first starts from a's own bits (its other half
 // is overwritten by the second), so no register has to be cleared first.
@@ -168,12 +198,13 @@ __device__ __forceinline__ v8i cat(v4i a, v4i b) { return v8i{a[0], a[1], a[2], 
 // LDS tile swizzles. A 16-byte-per-lane LDS read is served 16 lanes (256 bytes, every bank
 // once) at a time, so the 16 rows (channels) such a group touches must land on distinct
 // 16-byte bank groups.
-//  Row-major code tiles ([rows][d], nchunk = d/16 chunks of 16 bytes per row; 16/nchunk rows
-//  fill the 256 bytes): chunk c of row r sits at c ^ ((r / (16/nchunk)) mod nchunk).
+//  Row-major code tiles ([rows][bytes per row], nchunk = 8, 4 or 2 chunks of 16 bytes per row:
+//  E4M3 rows of d = 128 or 64, E2M1 rows of d = 128 or 64; 16/nchunk rows fill the 256 bytes):
+//  chunk c of row r sits at c ^ ((r / (16/nchunk)) mod nchunk).
 //  SEQ-view tiles ([group][channel][32]): the two 16-byte halves of channel ch swap when
 //  (ch >> 3) & 1.
 __device__ __forceinline__ int row_swz(int row, int chunk, int nchunk) {
-  return chunk ^ ((nchunk == 8 ? row >> 1 : row >> 2) & (nchunk - 1));
+  return chunk ^ ((nchunk == 8 ? row >> 1 : nchunk == 4 ? row >> 2 : row >> 3) & (nchunk - 1));
 }
 __device__ __forceinline__ int half_swz(int c, int half) { return half ^ ((c >> 3) & 1); }
 

@@ -16,6 +16,7 @@ struct QuantizeParams {
   const void* x;
   uint8_t* row_codes;    // nullptr: ROW view not wanted
   uint8_t* row_scales;
+  bool row_fp4;          // the ROW view in MXFP4 (E2M1 codes, two per byte) instead of E4M3
   uint8_t* seq_codes;    // nullptr: SEQ view not wanted
   uint8_t* seq_scales;
   // backward preprocessing (all nullptr for a plain quantise): with `o` set, the kernel also
@@ -36,6 +37,7 @@ struct AttnParams {
   float scale;           // alpha
   bool out_f32;          // O / dQ / dK / dV storage type (else bf16)
   int plan;              // packed: 1D grid over the device-built work list (mx_worklist.h)
+  bool score_fp4;        // Q and K ROW views are MXFP4 (E2M1 codes, d/2 bytes per token)
   // forward operands
   const uint8_t* q_codes; const uint8_t* q_scales;    // ROW view of Q
   const uint8_t* k_codes; const uint8_t* k_scales;    // ROW view of K
@@ -52,6 +54,7 @@ struct BwdParams {
   float scale;
   bool out_f32;
   int plan;              // packed: 1D grids over the device-built work lists (mx_worklist.h)
+  bool score_fp4;        // Q and K ROW views (the score operands) are MXFP4; needs the dS store
   int dq_mode;
   const uint8_t* q_codes; const uint8_t* q_scales;      // ROW Q
   const uint8_t* qs_codes; const uint8_t* qs_scales;    // SEQ Q

@@ -53,6 +53,8 @@ size_t seq_codes_bytes(const mx::Geom& g, int heads, int d) {
 
 bool valid_dim(int d) { return d == 64 || d == 128; }
 
+bool score_fp4(const mx_attn_desc* d) { return d->score_format == MX_SCORE_MXFP4; }
+
 mx_status check_view(const mx_qview& v) {
   if (!v.codes || !v.scales) return MX_E_ARG;
   if (!aligned(v.codes, 16) || !aligned(v.scales, 4)) return MX_E_ARG;
@@ -68,6 +70,7 @@ mx_status check_desc(const mx_attn_desc* d, mx::Geom* g) {
   if (d->dq_mode != MX_DQ_F32 && d->dq_mode != MX_DQ_F16_BOOST) return MX_E_ARG;
   if (!valid_dim(d->head_dim)) return MX_E_UNSUPPORTED;
   if (d->deterministic != 0 && d->deterministic != 1) return MX_E_ARG;
+  if (d->score_format != MX_SCORE_MXFP8 && d->score_format != MX_SCORE_MXFP4) return MX_E_ARG;
   return MX_OK;
 }
 
@@ -140,6 +143,7 @@ mx_status fwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
   p.scale = desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0f / sqrtf((float)desc->head_dim);
   p.out_f32 = desc->out_dtype == MX_F32;
   p.plan = mx::plan_eligible(g, gk) ? 1 : 0;
+  p.score_fp4 = score_fp4(desc);
   p.q_codes = q_row.codes; p.q_scales = q_row.scales;
   p.k_codes = k_row.codes; p.k_scales = k_row.scales;
   p.v_codes = v_seq.codes; p.v_scales = v_seq.scales;
@@ -176,6 +180,7 @@ mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
   p.scale = desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0f / sqrtf((float)desc->head_dim);
   p.out_f32 = desc->out_dtype == MX_F32;
   p.plan = mx::plan_eligible(g, gk) ? 1 : 0;
+  p.score_fp4 = score_fp4(desc);
   p.dq_mode = desc->dq_mode;
   p.q_codes = q_row.codes; p.q_scales = q_row.scales;
   p.qs_codes = q_seq.codes; p.qs_scales = q_seq.scales;
@@ -196,6 +201,9 @@ mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
     p.ds_codes = ws + w.ds_codes;
     p.ds_exps = ws + w.ds_exps;
     p.ds = w.ds;
+  } else if (p.score_fp4) {
+    // the 4-bit score path has only the dK/dV kernel rebuild S: dQ reads the stored dS codes
+    return w.store_ok ? MX_E_WORKSPACE : MX_E_UNSUPPORTED;
   }
   if (mx_out) {   // dK ROW, dK SEQ, dV ROW, dV SEQ; a view with null codes is not wanted
     const mx_qview& a = mx_out[0];
@@ -254,8 +262,10 @@ static mx_status quantize_impl(const mx_seq* seq, int32_t heads, int32_t head_di
   mx::Geom g;
   if (!make_geom(seq, &g) || heads < 1 || !x) return MX_E_ARG;
   if (dtype != MX_F32 && dtype != MX_BF16) return MX_E_ARG;
-  if (views < 1 || views > 3) return MX_E_ARG;
+  if (views < 1 || views > (MX_VIEW_SEQ | MX_VIEW_ROW_FP4)) return MX_E_ARG;
+  if ((views & MX_VIEW_ROW) && (views & MX_VIEW_ROW_FP4)) return MX_E_ARG;   // one row_out
   if (!valid_dim(head_dim)) return MX_E_UNSUPPORTED;
+  if (token_block && (views & MX_VIEW_ROW_FP4)) return MX_E_UNSUPPORTED;
   if (!aligned(x, 16)) return MX_E_ARG;
   mx::QuantizeParams p = {};
   p.geom = g;
@@ -264,10 +274,11 @@ static mx_status quantize_impl(const mx_seq* seq, int32_t heads, int32_t head_di
   p.f32 = dtype == MX_F32;
   p.token_block = token_block;
   p.x = x;
-  if (views & MX_VIEW_ROW) {
+  if (views & (MX_VIEW_ROW | MX_VIEW_ROW_FP4)) {
     if (!row_out || check_view(*row_out) != MX_OK) return MX_E_ARG;
     p.row_codes = row_out->codes;
     p.row_scales = row_out->scales;
+    p.row_fp4 = (views & MX_VIEW_ROW_FP4) != 0;
   }
   if (views & MX_VIEW_SEQ) {
     if (!seq_out || check_view(*seq_out) != MX_OK) return MX_E_ARG;
@@ -391,6 +402,7 @@ mx_status mx_attn_bwd_noalloc(const mx_attn_desc* desc, mx_qview q_row, mx_qview
   mx::Geom geo, gk;
   mx_status st = check_desc(desc, &geo);
   if (st != MX_OK) return st;
+  if (score_fp4(desc)) return MX_E_UNSUPPORTED;   // needs the dS code store, which the scratch lacks
   gk = geo;
   // the minimal workspace of this call must fit the scratch (checked before any device call)
   const size_t need = bwd_layout(geo, gk, desc).total;
@@ -427,6 +439,7 @@ size_t mx_attn_cross_workspace_size(const mx_attn_desc* desc, const mx_seq* seq_
   if (!desc || !make_geom(&desc->seq, &g) || desc->heads_q < 1 || !valid_dim(desc->head_dim)) return 0;
   if (key_geom(desc, g, seq_k, &gk) != MX_OK) return 0;
   const BwdWorkspace w = bwd_layout(g, gk, desc);
+  if (score_fp4(desc)) return w.store_ok ? w.total_store : 0;   // the store is required
   return for_bwd == 2 ? w.total_store : w.total;
 }
 
@@ -439,11 +452,14 @@ size_t mx_view_codes_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, i
   if (!make_geom(seq, &g) || heads < 1 || !valid_dim(head_dim)) return 0;
   if (view == MX_VIEW_ROW) return row_codes_bytes(g, heads, head_dim);
   if (view == MX_VIEW_SEQ) return seq_codes_bytes(g, heads, head_dim);
+  if (view == MX_VIEW_ROW_FP4) return row_codes_bytes(g, heads, head_dim) / 2;
   return 0;
 }
 
 size_t mx_view_scales_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view) {
-  return mx_view_codes_bytes(seq, heads, head_dim, view) / 32;
+  // one scale byte per 32 elements in every view
+  const int32_t elem_view = view == MX_VIEW_ROW_FP4 ? MX_VIEW_ROW : view;
+  return mx_view_codes_bytes(seq, heads, head_dim, elem_view) / 32;
 }
 
 mx_status mx_read_flags(const void* workspace, uint32_t* flags) {

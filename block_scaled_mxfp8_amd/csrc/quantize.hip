@@ -11,6 +11,9 @@
 // 32 tokens of a channel) after a transpose through LDS. The kernel is HBM-bound:
 // 2 B read + 2 x (1 + 1/32) B written per bf16 element.
 //
+// MXFP4 ROW view (row_fp4; FLAMIA notes, sections 2 and 3, the 4-bit score operands of the mixed
+// route): the same ROW groups with E2M1 codes, two per byte, written instead of the E4M3 ones.
+//
 // Token-block scales (kBlock; FLAMIA notes, section 3): the workgroup's tile IS one token
 // block (32 consecutive tokens of a sequence or document x all d channels of a head), so its
 // single exponent comes from a workgroup max-abs (a wave max, then the waves' maxima through
@@ -99,7 +102,21 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
   }
 
   // ---- ROW view: 32 channels of one token = this thread's 16 + the neighbour's 16 ----
-  if (p.row_codes) {
+  if (p.row_codes && !kBlock && p.row_fp4) {
+    // MXFP4 (the 4-bit score operands): E2M1 codes, 8 bytes for the thread's 16 channels
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) am = max(am, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+    const bool nonfinite = am >= kInfBits;
+    const int e = scale_exp4_from_bits(nonfinite ? 0u : am);
+    const uint32_t w0 = nonfinite ? 0x77777777u : pack8_e2m1(v, e);
+    const uint32_t w1 = nonfinite ? 0x77777777u : pack8_e2m1(v + 8, e);
+    if (valid) {
+      *reinterpret_cast<v2i*>(p.row_codes + (e0 >> 1)) = v2i{(int)w0, (int)w1};
+      if ((cb & 1) == 0) p.row_scales[e0 >> 5] = nonfinite ? 0xFF : (uint8_t)(e + 127);
+    }
+  } else if (p.row_codes) {
     uint32_t am = 0;
     if (kBlock) {
       am = blk_am;

@@ -42,6 +42,13 @@
  *                 Inside each 32-byte group the token at offset t (0..31) is stored at byte
  *                 position MX_SEQ_POS(t) = 16*((t>>2)&1) + 4*(t>>3) + (t&3); padding tokens
  *                 of a partial group hold code 0.
+ *       ROW_FP4 view (MXFP4, the 4-bit score operands; FLAMIA notes, sections 2 and 3: the
+ *                 mixed route scores with 4-bit Q and K and keeps the other products in 8 bits;
+ *                 the matrix core takes only E8M0 scales, one per 32 contraction elements, so
+ *                 the 4-bit format here is MXFP4 rather than NVFP4's E4M3 scale per 16):
+ *                 the ROW groups with E2M1 codes (sign | 2-bit exponent, bias 1 | 1-bit
+ *                 mantissa: 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte, channel 2i in the low
+ *                 nibble of byte i: codes [B,H,L,d/2] / [T,H,d/2]; scales as the ROW view.
  */
 #ifndef MXATTN_H
 #define MXATTN_H
@@ -53,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXATTN_ABI_VERSION 1
+#define MXATTN_ABI_VERSION 2
 
 #define MX_SEQ_POS(t) (16 * (((t) >> 2) & 1) + 4 * ((t) >> 3) + ((t) & 3))
 
@@ -67,7 +74,8 @@ typedef enum {
 
 typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
 
-enum { MX_VIEW_ROW = 1, MX_VIEW_SEQ = 2 };
+enum { MX_VIEW_ROW = 1, MX_VIEW_SEQ = 2, MX_VIEW_ROW_FP4 = 4 };
+enum { MX_SCORE_MXFP8 = 0, MX_SCORE_MXFP4 = 1 };
 enum { MX_DQ_F32 = 0, MX_DQ_F16_BOOST = 1 };
 
 /* Bits of the device status word (see mx_read_flags). */
@@ -107,13 +115,21 @@ typedef struct {
   void* workspace;        /* device scratch for mx_attn_bwd (see mx_attn_workspace_size); with at
                              least the for_bwd = 2 size the backward keeps the dS codes there */
   size_t workspace_bytes;
+  int32_t score_format;   /* format of q_row and k_row, the score operands: MX_SCORE_MXFP8 (ROW
+                             views, E4M3) or MX_SCORE_MXFP4 (ROW_FP4 views; the mixed route: V,
+                             P, G, dS and the SEQ views of Q and K stay E4M3); other values:
+                             MX_E_ARG */
 } mx_attn_desc;
 
 /* Quantise one tensor x (layout above, dtype MX_F32 or MX_BF16) into the ROW and/or SEQ view
  * in a single pass over x. views = MX_VIEW_ROW | MX_VIEW_SEQ; the unused output may be NULL.
  * Group exponent: the smallest e with amax * 2^-e <= 448 (amax 0 -> -127), clamped to
  * [-127, 127]; codes = E4M3 round-to-nearest-even of x * 2^-e. A group holding a NaN or an
- * infinity gets scale 0xFF and codes 0x7F. */
+ * infinity gets scale 0xFF and codes 0x7F.
+ * views may hold MX_VIEW_ROW_FP4 in place of MX_VIEW_ROW (both: MX_E_ARG): row_out then
+ * receives the ROW_FP4 view, with the group exponent the smallest e with amax * 2^-e <= 6 and
+ * codes = E2M1 round-to-nearest-even of x * 2^-e (sign kept); a group holding a NaN or an
+ * infinity gets scale 0xFF and codes 0x7. Head dims 64 and 128, as for the other views. */
 mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x, mx_dtype dtype,
                       int32_t views, mx_qview* row_out, mx_qview* seq_out, void* stream);
 
@@ -173,7 +189,8 @@ mx_status mx_gemm_quantize(mx_qview a_row, mx_qview b_row, int64_t m, int32_t n,
 
 /* Forward: O [layout above, out_dtype] and LSE float32 [B,H,L] / [T,H] (natural log,
  * +inf for a row without visible keys). q_row / k_row: ROW views of Q and K (heads_q and
- * heads_kv heads); v_seq: SEQ view of V. */
+ * heads_kv heads), or ROW_FP4 views when desc->score_format = MX_SCORE_MXFP4; v_seq: SEQ view
+ * of V. */
 mx_status mx_attn_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o,
                       float* lse, void* stream);
 
@@ -181,7 +198,13 @@ mx_status mx_attn_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, 
  * Q, K, V, writes dQ [like Q], dK and dV [like K] in out_dtype. G is quantised internally
  * (ROW and SEQ views) into the workspace and D = rowsum(G_row o O) is formed there. dQ is
  * accumulated in FP32, or (dq_mode = MX_DQ_F16_BOOST) as FP16 sums of FP32 partials over
- * 128-key blocks, each multiplied by 2^9 before rounding; the boost is removed at the end. */
+ * 128-key blocks, each multiplied by 2^9 before rounding; the boost is removed at the end.
+ * With desc->score_format = MX_SCORE_MXFP4, q_row and k_row are the forward's ROW_FP4 views (S
+ * and P are rebuilt from them) while q_seq, k_seq and v_row stay E4M3 (FLAMIA notes, section 3:
+ * the backward recomputes the scores with the same 4-bit Q/K and uses 8-bit views for dQ and
+ * dK); this mode needs the dS code store: a workspace of at least mx_attn_workspace_size(desc,
+ * 1), which includes it (MX_E_WORKSPACE below that; MX_E_UNSUPPORTED for a geometry too large
+ * to have a store). */
 mx_status mx_attn_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
                       mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                       mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
@@ -209,7 +232,8 @@ mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
  * device shares that device's array (the previous call's contents remain; everything the call
  * reads is written first), so calls that overlap on one device -- concurrent streams or
  * threads -- race and must be serialised by the caller. The call's status word is not
- * readable through mx_read_flags. */
+ * readable through mx_read_flags. desc->score_format = MX_SCORE_MXFP4 returns MX_E_UNSUPPORTED
+ * (that mode needs the dS code store, which the scratch does not hold). */
 mx_status mx_attn_bwd_noalloc(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
                               mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                               mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
@@ -260,10 +284,13 @@ size_t mx_attn_cross_workspace_size(const mx_attn_desc* desc, const mx_seq* seq_
  * mx_attn_bwd uses the store whenever desc->workspace_bytes >= the for_bwd = 2 size. A geometry
  * whose store would hold 2^32 or more blocks or exponent bytes has none: for_bwd = 2 then
  * returns the for_bwd = 1 size.
+ * With desc->score_format = MX_SCORE_MXFP4 the store is required, so for_bwd = 1 and 2 both
+ * return the size with the store (0 for a geometry without one).
  * Other for_bwd values (0 = forward, which needs none) return 0. */
 size_t mx_attn_workspace_size(const mx_attn_desc* desc, int32_t for_bwd);
 
-/* Byte sizes of the quantised views of a tensor with `heads` heads (codes, scales). */
+/* Byte sizes of the quantised views of a tensor with `heads` heads (codes, scales); view is
+ * MX_VIEW_ROW, MX_VIEW_SEQ or MX_VIEW_ROW_FP4 (other values: 0). */
 size_t mx_view_codes_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view);
 size_t mx_view_scales_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view);
 

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mx_abi_version() == 1
+    assert lib.mx_abi_version() == 2
     assert lib.mx_strerror(0) == b"ok"
 
 
@@ -279,7 +279,9 @@ def test_token_block_quantize_validation(lib):
     assert f(ctypes.byref(s), 1, 128, FAKE, 7, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
     assert f(ctypes.byref(s), 1, 128, FAKE + 2, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
     assert f(ctypes.byref(s), 1, 96, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_UNSUPPORTED
-    assert f(ctypes.byref(s), 1, 128, FAKE, 1, 4, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(s), 1, 128, FAKE, 1, 8, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    # the MXFP4 ROW view has no token-block form
+    assert f(ctypes.byref(s), 1, 128, FAKE, 1, 4, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_UNSUPPORTED
     assert f(ctypes.byref(s), 1, 128, FAKE, 1, 1, None, ctypes.byref(v), None) == _lib.MX_E_ARG
 
 
@@ -304,3 +306,47 @@ def test_noalloc_backward_rejects_calls_beyond_its_scratch(lib):
     st = lib.mx_attn_bwd_noalloc(ctypes.byref(d), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None)
     assert st == _lib.MX_E_WORKSPACE
     assert lib.mx_attn_bwd_noalloc(None, v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None) == _lib.MX_E_ARG
+
+
+def test_mxfp4_view_and_score_format_validation(lib):
+    s = _seq()
+    v = _lib._QView(FAKE, FAKE)
+    q = lib.mx_quantize
+    # ROW and ROW_FP4 both write row_out: asking for both is an argument error
+    assert q(ctypes.byref(s), 1, 128, FAKE, 1, 1 | 4, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert q(ctypes.byref(s), 1, 128, FAKE, 1, 8, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    # no 4-bit token-block view
+    assert lib.mx_quantize_token_block(ctypes.byref(s), 1, 128, FAKE, 1, 4, ctypes.byref(v), ctypes.byref(v),
+                                       None) == _lib.MX_E_UNSUPPORTED
+    # ROW_FP4 sizes: half the ROW codes, the same scales
+    s2 = _seq(batch=2, seqlen=70)
+    assert lib.mx_view_codes_bytes(ctypes.byref(s2), 3, 128, 4) == 2 * 3 * 70 * 64
+    assert lib.mx_view_scales_bytes(ctypes.byref(s2), 3, 128, 4) == 2 * 3 * 70 * 4
+    assert lib.mx_view_codes_bytes(ctypes.byref(s2), 3, 128, 3) == 0
+    # score_format outside {MXFP8, MXFP4}
+    assert lib.mx_attn_fwd(ctypes.byref(_desc(score_format=2)), v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    # MXFP4 scores need the dS store: both workspace sizes include it, a smaller workspace is refused
+    d8 = _desc()
+    d4 = _desc(score_format=_lib.MX_SCORE_MXFP4)
+    with_store = lib.mx_attn_workspace_size(ctypes.byref(d8), 2)
+    assert with_store > lib.mx_attn_workspace_size(ctypes.byref(d8), 1)
+    assert lib.mx_attn_workspace_size(ctypes.byref(d4), 1) == with_store
+    assert lib.mx_attn_workspace_size(ctypes.byref(d4), 2) == with_store
+    d4.workspace, d4.workspace_bytes = FAKE, with_store - 1
+    b = lib.mx_attn_bwd
+    assert b(ctypes.byref(d4), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None) == _lib.MX_E_WORKSPACE
+    # the library-owned scratch has no store: refused before any device call
+    assert lib.mx_attn_bwd_noalloc(ctypes.byref(_desc(score_format=1)), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE,
+                                   FAKE, FAKE, None) == _lib.MX_E_UNSUPPORTED
+
+
+def test_binding_reads_the_score_format_from_the_views():
+    import torch
+    fp8 = _lib.QView(torch.empty((2, 3, 70, 128), dtype=torch.uint8), torch.empty((2, 3, 70, 4), dtype=torch.uint8))
+    fp4 = _lib.QView(torch.empty((2, 3, 70, 64), dtype=torch.uint8), torch.empty((2, 3, 70, 4), dtype=torch.uint8))
+    assert not _lib._row_is_fp4(fp8) and _lib._row_is_fp4(fp4)
+    assert _lib._elem_shape(fp4) == (2, 3, 70, 128) == _lib._elem_shape(fp8)
+    assert _lib._score_format(fp4, fp4) == _lib.MX_SCORE_MXFP4
+    assert _lib._score_format(fp8, fp8) == _lib.MX_SCORE_MXFP8
+    with pytest.raises(ValueError):
+        _lib._score_format(fp8, fp4)
