@@ -20,6 +20,8 @@ the library records immediately around each launch of the named kernel, on its s
                                    # jagged keys/values (<= 14980), H3 d128, non-causal
     python bench.py --workload n1  # fused RMSNorm + quantise producer, x [262144, 512] bf16
     python bench.py --workload g1  # fused MXFP8 GEMM + quantise producer, 16384 x 12288 x 4096
+    python bench.py --score mxfp4  # the mixed route: Q and K scored as MXFP4 (E2M1), everything else
+                                   # MXFP8 (any attention workload; default c3)
 
 `roofline.traffic` is the roofline kernel's HBM bytes per launch from rocprofv3 counters
 (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for the 1 GiB copy of --pmc-run),
@@ -79,6 +81,13 @@ ALL_SOURCES = sorted(os.path.relpath(p, ROOT) for p in
                      __import__("glob").glob(os.path.join(ROOT, "block_scaled_mxfp8_amd", "csrc", "*")))
 
 PEAK_MXFP8_TFLOPS = 5000.0      # MI355X dense MXFP8 MFMA, AMD's published figure
+PEAK_MXFP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
+
+
+def mixed_peak(fp4_share):
+    """Peak of work whose FLOPs are fp4_share MXFP4 products and the rest MXFP8 ones (each at its
+    own peak): the harmonic mix, FLOPs over the time the two parts need at their peaks."""
+    return 1.0 / (fp4_share / PEAK_MXFP4_TFLOPS + (1.0 - fp4_share) / PEAK_MXFP8_TFLOPS)
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
 
@@ -96,6 +105,8 @@ def parse():
     ap.add_argument("--rounds", type=int, default=3, help="timed rounds of --steps steps (value: the median)")
     ap.add_argument("--cpu-heads", type=int, default=24,
                     help="(batch, head) pairs the CPU baseline times (0: all of them, the full tensor)")
+    ap.add_argument("--score", choices=["mxfp8", "mxfp4"], default="mxfp8",
+                    help="score operands of the attention workloads: MXFP8 (E4M3), or MXFP4 (E2M1; the mixed route)")
     ap.add_argument("--workload", choices=["c3", "c4", "c5", "c5gqa", "x1", "n1", "g1"], default="c3",
                     help="c3: the headline causal self-attention step; c4: 128 packed documents; c5/c5gqa: "
                          "B1 H16 L16384 non-causal (MHA / 16 on 4 KV heads); x1: the jagged cross-attention "
@@ -157,9 +168,10 @@ def run_attention(args):
     import torch
 
     import synth
-    from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F32, PROFILE_BWD_DKDV, PROFILE_BWD_DQ,
-                                        PROFILE_BWD_PREP, PROFILE_FWD, PROFILE_QUANTIZE, load, mx_attn_bwd,
-                                        mx_attn_fwd, mx_profile_kernel, mx_quantize, mx_quantize_token_block)
+    from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F32, MX_VIEW_ROW_FP4, MX_VIEW_SEQ, PROFILE_BWD_DKDV,
+                                        PROFILE_BWD_DQ, PROFILE_BWD_PREP, PROFILE_FWD, PROFILE_QUANTIZE, load,
+                                        mx_attn_bwd, mx_attn_fwd, mx_profile_kernel, mx_quantize,
+                                        mx_quantize_token_block)
     from block_scaled_mxfp8_amd.flops import attn_flops, visible_pairs
 
     load()
@@ -196,8 +208,12 @@ def run_attention(args):
     ws = {}
     ds_store = not args.recompute_dq
 
+    fp4 = args.score == "mxfp4"
+    qk_views = (MX_VIEW_ROW_FP4 | MX_VIEW_SEQ) if fp4 else 3
+
     def quant():
-        return mx_quantize(t["q"], **kw), mx_quantize(t["k"], **kw), mx_quantize(t["v"], **kw)
+        return (mx_quantize(t["q"], views=qk_views, **kw), mx_quantize(t["k"], views=qk_views, **kw),
+                mx_quantize(t["v"], **kw))
 
     def step(mode=dq_mode):
         (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
@@ -265,7 +281,7 @@ def run_attention(args):
     ms_fwd = kernel_ms(PROFILE_FWD, lambda: mx_attn_fwd(q_row, k_row, v_seq, causal=causal, **kw))
     ms_quant = kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize(t["q"], **kw), n=3 * args.profile_steps)
     ms_quant_tb = None
-    if not packed:   # the token-block variant of the quantiser (same bytes; one exponent per 32 tokens x d)
+    if not packed and not fp4:   # the token-block variant of the quantiser (same bytes; one exponent per 32 tokens x d)
         ms_quant_tb = kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize_token_block(t["q"]), n=3 * args.profile_steps)
 
     def bwd(mode):
@@ -299,9 +315,21 @@ def run_attention(args):
     f_dkdv = f_bwd * 4 // 5
     bwd_f32, bwd_f16 = res_bwd["f32"], res_bwd["f16"]
     value = tflops(f_fwd + f_bwd, ms_step)
+    # peaks: MXFP8 everywhere, or (MXFP4 scores) the mix of the FP4 score products' FLOP share
+    # (forward 1 of 2 products, backward 1 of 5, dK/dV kernel 1 of 4, whole step 2 of 7) with MXFP8
+    pk_step = mixed_peak(2 / 7) if fp4 else PEAK_MXFP8_TFLOPS
+    pk_fwd = mixed_peak(1 / 2) if fp4 else PEAK_MXFP8_TFLOPS
+    pk_bwd = mixed_peak(1 / 5) if fp4 else PEAK_MXFP8_TFLOPS
+    pk_dkdv = mixed_peak(1 / 4) if fp4 else PEAK_MXFP8_TFLOPS
+    if fp4:
+        metric = f"mixed MXFP4-score / MXFP8 attn fwd/bwd TFLOP/s (causal-adj) on {name}" + (
+            " (B4 H32 L4096 d128)" if name == "c3" else "")
+    elif name == "c3":
+        metric = "MXFP8 attn fwd/bwd TFLOP/s (causal-adj) at B4 H32 L4096 d128, % of peak"
+    else:
+        metric = f"MXFP8 attn fwd/bwd TFLOP/s (causal-adj) on {name}"
     line = {
-        "metric": "MXFP8 attn fwd/bwd TFLOP/s (causal-adj) at B4 H32 L4096 d128, % of peak" if name == "c3"
-        else f"MXFP8 attn fwd/bwd TFLOP/s (causal-adj) on {name}",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -311,21 +339,23 @@ def run_attention(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8",
+        "dtype": "mxfp4 scores + mxfp8" if fp4 else "mxfp8",
         "data": "synthetic",
-        "config": dict({"workload": desc + ", bf16 N(0,1)-based synthetic inputs, step = quantise Q/K/V + fwd + bwd",
-                        "head_dim": d, "causal": causal, "dq": args.dq,
+        "config": dict({"workload": desc + ", bf16 N(0,1)-based synthetic inputs, step = quantise Q/K/V + fwd + bwd"
+                        + (" with Q and K scored as MXFP4" if fp4 else ""),
+                        "head_dim": d, "causal": causal, "dq": args.dq, "score": args.score,
                         "dq_pass": "rebuilds dS" if args.recompute_dq else "reads stored dS codes"}, **cfg_line),
         "timing": {"rounds": args.rounds, "steps_per_round": args.steps, "ms_per_step_rounds": [round(r, 4) for r in rounds],
                    "statistic": "median of rounds, wall clock, no measurement hook",
                    "ms_per_step_roofline_round": round(ms_hooked, 4)},
-        "pct_of_peak": round(100 * value / PEAK_MXFP8_TFLOPS, 2),
+        "pct_of_peak": round(100 * value / pk_step, 2),
         "fwd_tflops": round(tflops(f_fwd, ms_fwd), 2),
-        "fwd_pct_of_peak": round(100 * tflops(f_fwd, ms_fwd) / PEAK_MXFP8_TFLOPS, 2),
+        "fwd_pct_of_peak": round(100 * tflops(f_fwd, ms_fwd) / pk_fwd, 2),
         "bwd_tflops": round(tflops(f_bwd, bwd_f32["call_ms"]), 2),
-        "bwd_pct_of_peak": round(100 * tflops(f_bwd, bwd_f32["call_ms"]) / PEAK_MXFP8_TFLOPS, 2),
+        "bwd_pct_of_peak": round(100 * tflops(f_bwd, bwd_f32["call_ms"]) / pk_bwd, 2),
         "bwd_f16dq_tflops": round(tflops(f_bwd, bwd_f16["call_ms"]), 2),
-        "bwd_f16dq_pct_of_peak": round(100 * tflops(f_bwd, bwd_f16["call_ms"]) / PEAK_MXFP8_TFLOPS, 2),
+        "bwd_f16dq_pct_of_peak": round(100 * tflops(f_bwd, bwd_f16["call_ms"]) / pk_bwd, 2),
+        "peaks_tflops": {"step": round(pk_step, 1), "fwd": round(pk_fwd, 1), "bwd": round(pk_bwd, 1)},
         "quantize_gbs": round(quant_bytes / (ms_quant * 1e-3) / 1e9, 1),
         "quantize_token_block_gbs": None if ms_quant_tb is None else round(quant_bytes / (ms_quant_tb * 1e-3) / 1e9, 1),
         "kernels_ms": {"attn_fwd": round(ms_fwd, 4), "attn_bwd_dkdv": round(bwd_f32["dkdv_ms"], 4),
@@ -335,12 +365,12 @@ def run_attention(args):
         "pages_context": {"fa4_mx8_fwd_pflops_gb300": 2.85, "fa4_mx8_bwd_pflops_gb300_f16dq": 1.98,
                           "fa4_mx8_bwd_pflops_gb300_f32dq": 1.82},
         "roofline": {"kernel": f"attn_bwd_dkdv_kernel<{d}> (backward dK/dV)", "bound": "mfma",
-                     "achieved": round(tflops(f_dkdv, ms_bwd_main), 2), "peak": PEAK_MXFP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops(f_dkdv, ms_bwd_main) / PEAK_MXFP8_TFLOPS, 4),
-                     "traffic": recorded_traffic() if name == "c3" else None},
+                     "achieved": round(tflops(f_dkdv, ms_bwd_main), 2), "peak": round(pk_dkdv, 1),
+                     "unit": "TFLOP/s", "frac": round(tflops(f_dkdv, ms_bwd_main) / pk_dkdv, 4),
+                     "traffic": recorded_traffic() if name == "c3" and not fp4 else None},
         "env": environment(),
     }
-    if not args.no_cpu_baseline and name == "c3":
+    if not args.no_cpu_baseline and name == "c3" and not fp4:
         line["cpu_baseline"] = cpu_baseline(t, args.cpu_heads)
     print(json.dumps(line), flush=True)
 

@@ -338,3 +338,56 @@ def test_mixed_chain_cosine_tracks_the_oracle(causal):
             assert cs >= ref_cos[n] - 0.05 * (1 - ref_cos[n]) - 2e-3, (n, cs, ref_cos[n])
         # and the 4-bit scores are measurably coarser than the 8-bit ones (O)
         assert ref_cos["O"] < cosine(f8["O"], r["O"])
+
+
+def test_mixed_c3_full_shape_sampled_heads():
+    # The mixed path at the benchmark's launch configuration (B4 H32 L4096 d128 causal, bf16, the
+    # c3 inputs): the device runs the whole call; for 3 seeded (b, h) pairs the oracle checks
+    # sampled 32-row query blocks of the forward, then supplies those heads' saved O and LSE
+    # (written into the device's O and LSE) so their backward is checked in isolation: dQ on the
+    # sampled query blocks, dK and dV on sampled key blocks, and the stored dS blocks.
+    print("[c3 full fp4] quantise + forward", flush=True)
+    x = synth.make_inputs("c3")
+    t = {n: to_device(x[n], torch.bfloat16) for n in "qkvg"}
+    del x
+    B, H, L, d = t["q"].shape
+    q4, q_seq, k4, k_seq, v_row, v_seq = _views(t)
+    o, lse = mx_attn_fwd(q4, k4, v_seq, causal=True)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(404)
+    heads = [(int(i) // H, int(i) % H) for i in sorted(r.choice(B * H, size=3, replace=False))]
+    print(f"  sampled (b, h): {heads}", flush=True)
+    qblocks, kblocks = [0, 37, 80, 127], [0, 61, 126, 127]
+    rows = np.concatenate([np.arange(32 * b, 32 * b + 32) for b in qblocks])
+    krows = np.concatenate([np.arange(32 * b, 32 * b + 32) for b in kblocks])
+    o2, lse2 = o.clone(), lse.clone()
+    saved = {}
+    for bh in heads:
+        q, k, v = (as_f64(t[n][bh]) for n in "qkv")
+        f = oracle.head_forward(q, k, v, True, bounds=True, rows=rows, score_format="mxfp4")
+        assert gate("O", as_f64(o[bh])[rows], f["O"], f["B"], f["eta"]).ok
+        assert np.all(np.abs(as_f64(lse[bh])[rows] - f["lse"]) <= 2e-5 + 4 * f["drel_max"] + 1e-6 * np.abs(f["lse"]))
+        full = oracle.head_forward(q, k, v, True, score_format="mxfp4")
+        saved[bh] = (full["O_out"], full["lse"].astype(np.float32))
+        o2[bh] = torch.from_numpy(saved[bh][0]).to(torch.bfloat16).cuda()
+        lse2[bh] = torch.from_numpy(saved[bh][1]).cuda()
+        print(f"  oracle forward {bh} done", flush=True)
+    dq, dk, dv, ws = mx_attn_bwd(q4, q_seq, k4, k_seq, v_row, o2, lse2, t["g"], causal=True)
+    torch.cuda.synchronize()
+    store = DsStore(ws, tuple(t["q"].shape), True)
+    tot = [0, 0, 0, 0, 0]
+    for bh in heads:
+        q, k, v, g = (as_f64(t[n][bh]) for n in "qkvg")
+        O_s, L_s = saved[bh]
+        rq = oracle.head_backward(q, k, v, O_s, L_s, g, True, bounds=True, dq_blocks=qblocks, score_format="mxfp4")
+        assert gate("dQ", as_f64(dq[bh])[rows], rq["dQ"][rows], rq["B_dQ"][rows], rq["eta_dQ"][rows]).ok
+        rk = oracle.head_backward(q, k, v, O_s, L_s, g, True, bounds=True, dk_blocks=kblocks, score_format="mxfp4")
+        for n, dev in (("dK", dk), ("dV", dv)):
+            assert gate(n, as_f64(dev[bh])[krows], rk[n][krows], rk["B_" + n][krows], rk["eta_" + n][krows]).ok, n
+        codes, exps = store.head(bh[0], bh[1], L, L, True)
+        for rr in (rq, rk):
+            tot = [a + b for a, b in zip(tot, compare_ds(codes, exps, rr, L, L))]
+        print(f"  oracle backward {bh} done", flush=True)
+    print(f"  dS store: {tot[0]} blocks, exponents differing {tot[1]}; {tot[2]} codes, differing unflagged "
+          f"{tot[3]}, differing flagged {tot[4]}", flush=True)
+    assert tot[0] > 0 and tot[1] == 0 and tot[3] == 0, tot
