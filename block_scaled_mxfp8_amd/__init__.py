@@ -21,7 +21,7 @@ Functions mirror the C entry points:
     mx_rmsnorm_quantize(x, gamma, eps) -> (row QView, seq QView): RMSNorm written only as MX views.
     mx_gemm_quantize(a_row, b_row) -> (row QView, seq QView): C = A B^T written only as MX views.
 """
-from ._lib import (MX_VIEW_ROW, MX_VIEW_SEQ, MX_VIEW_ROW_FP4, MX_SCORE_MXFP8, MX_SCORE_MXFP4, MX_DQ_F32, MX_DQ_F16_BOOST, MXError, QView, lib_path, load,
+from ._lib import (MX_VIEW_ROW, MX_VIEW_SEQ, MX_VIEW_ROW_FP4, MX_SCORE_MXFP8, MX_SCORE_MXFP4, MX_DQ_F32, MX_DQ_F16_PREFIX, MX_DQ_F16_BOOST, MXError, QView, lib_path, load,
                    mx_abi_version, mx_attn_bwd, mx_attn_fwd, mx_attn_varlen_bwd, mx_attn_varlen_fwd, mx_quantize,
                    mx_attn_workspace_size, mx_read_flags, mx_profile_kernel, PROFILE_FWD, PROFILE_BWD_DKDV,
                    PROFILE_QUANTIZE, PROFILE_BWD_PREP, PROFILE_BWD_DQ, mx_attn_cross_fwd, mx_attn_cross_bwd,
@@ -29,7 +29,7 @@ from ._lib import (MX_VIEW_ROW, MX_VIEW_SEQ, MX_VIEW_ROW_FP4, MX_SCORE_MXFP8, MX
                    PROFILE_GEMM, mx_quantize_token_block,
                    mx_attn_bwd_mx, mx_attn_bwd_noalloc)
 
-__all__ = ["MX_VIEW_ROW", "MX_VIEW_SEQ", "MX_VIEW_ROW_FP4", "MX_SCORE_MXFP8", "MX_SCORE_MXFP4", "MX_DQ_F32", "MX_DQ_F16_BOOST", "MXError", "QView", "lib_path", "load",
+__all__ = ["MX_VIEW_ROW", "MX_VIEW_SEQ", "MX_VIEW_ROW_FP4", "MX_SCORE_MXFP8", "MX_SCORE_MXFP4", "MX_DQ_F32", "MX_DQ_F16_PREFIX", "MX_DQ_F16_BOOST", "MXError", "QView", "lib_path", "load",
            "mx_abi_version", "mx_attn_bwd", "mx_attn_fwd", "mx_attn_varlen_bwd", "mx_attn_varlen_fwd", "mx_quantize",
            "mx_attn_workspace_size", "mx_read_flags", "mx_profile_kernel", "PROFILE_FWD", "PROFILE_BWD_DKDV",
            "PROFILE_QUANTIZE", "PROFILE_BWD_PREP", "PROFILE_BWD_DQ", "mx_attn_cross_fwd", "mx_attn_cross_bwd",

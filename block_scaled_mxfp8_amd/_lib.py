@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 MX_OK, MX_E_ARG, MX_E_UNSUPPORTED, MX_E_WORKSPACE, MX_E_DEVICE = range(5)
 MX_F32, MX_BF16 = 0, 1
 MX_VIEW_ROW, MX_VIEW_SEQ, MX_VIEW_ROW_FP4 = 1, 2, 4
-MX_DQ_F32, MX_DQ_F16_BOOST = 0, 1
+MX_DQ_F32, MX_DQ_F16_BOOST, MX_DQ_F16_PREFIX = 0, 1, 2
 MX_SCORE_MXFP8, MX_SCORE_MXFP4 = 0, 1
 
 

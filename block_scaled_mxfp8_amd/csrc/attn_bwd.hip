@@ -59,7 +59,6 @@ constexpr int kStepK = 64;             // keys per dQ step
 constexpr int kDkvProducers = 2 * kWaves;  // dK/dV workgroup: producer waves, then kWaves accumulators
 constexpr int kDkvThreads = 64 * (kDkvProducers + kWaves);
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kBoost = 512.f;        // 2^9 (FP16 dQ partial sums)
 constexpr int kDkvChunk = 2;           // (sequence, head) pairs per longest-first chunk (mx_layout.h lpt_order)
 
 __device__ __forceinline__ float max_abs16(const float* x) {
@@ -204,40 +203,36 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p, int* smem) {
   return w;
 }
 
-// Issue the producers' loads of the step (query head hq, queries q0..q0+63) into stage `st`, as
-// loader `lw` of NL (NL >= 6), all LDS-DMA: ROW-tile instructions j = lw, lw + NL, ... (each
-// moves 64 x 16 bytes: 64/NCH rows of NCH = d/16 chunks) and, for lw < 6, one per-query item
-// (64 lanes x 4 bytes; the ROW scale words are 2 bytes at d = 64, landing in the low half of
-// the lane's dword): 0 the Q ROW scale words, 1 the G ROW scale words, 2 LSE * log2 e, 3 -D,
-// 4 the Q SEQ scales, 5 the G SEQ scales (dword lane % (d/2) of the step's two groups, the
-// second clamped to the last group). Rows past the end are clamped to the last row (finite
-// codes and values); the masked tile code gives them P = 0 and U = 0.
+// Issue the producers' loads of step c into stage `st`, as loader `lw` of NL (NL >= 6), all
+// LDS-DMA: ROW-tile instructions j = lw, lw + NL, ... (each moves 64 x 16 bytes: 64/NCH rows of
+// NCH 16-byte chunks) and, for lw < 6, one per-query item (64 lanes x 4 bytes; the ROW scale
+// words are 2 bytes at d = 64, landing in the low half of the lane's dword): 0 the Q ROW scale
+// words, 1 the G ROW scale words, 2 LSE * log2 e, 3 -D, 4 the Q SEQ scales, 5 the G SEQ scales
+// (dword lane % (d/2) of the step's two groups, the second clamped to the last group). Rows past
+// the end are clamped to the last row (finite codes and values); the masked tile code gives them
+// P = 0 and U = 0. Every address is a base plus c's offsets plus a lane part.
 template <int D, bool kPacked, int NL, bool kF4>
-__device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
+__device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& w, const StepPos& c, DkvStage<D>& st,
                                               int lw) {
   static_assert(NL >= 6, "six small-item loaders");
   constexpr int NCH = D / 16, RPI = 64 / NCH;
   constexpr int NCHQ = kF4 ? NCH / 2 : NCH, RPIQ = 64 / NCHQ;   // Q ROW tile (E2M1: d/2 bytes a row)
-  const Geom& g = p.geom;
   const int lane = threadIdx.x & 63;
-  const long long sbase = kPacked ? (long long)w.doc_start : (long long)w.s;
   const int ts = (int)token_stride_k<kPacked>(p.heads_q, D);
-  const long long off0 = elem_offset_k<kPacked>(g, p.heads_q, D, sbase, hq, q0, 0);
-  const int rmax = w.n - 1 - q0;
+  const int rmax = w.n - 1 - c.q0;
   const int r = min(lane, rmax);
   if (lw == 0 || lw == 1) {
-    lds_dma((lw == 0 ? p.q_scales : p.gr_scales) + (off0 >> 5) + ((uint32_t)(r * ts) >> 5), lw == 0 ? st.qrs : st.grs,
+    lds_dma((lw == 0 ? p.q_scales : p.gr_scales) + (c.elem >> 5) + ((uint32_t)(r * ts) >> 5), lw == 0 ? st.qrs : st.grs,
             D / 32);
   } else if (lw == 2 || lw == 3) {
-    const float* src = (lw == 2 ? p.lse2 : p.ndelta) + token_index_k<kPacked>(g, p.heads_q, w.s, w.doc_start, hq, q0) +
-                       (uint32_t)(r * (kPacked ? p.heads_q : 1));
-    lds_dma(src, lw == 2 ? st.lse2 : st.ndlt, 4);
+    lds_dma((lw == 2 ? p.lse2 : p.ndelta) + c.tok + (uint32_t)(r * (kPacked ? p.heads_q : 1)), lw == 2 ? st.lse2 : st.ndlt,
+            4);
   } else if (lw == 4 || lw == 5) {
-    const int glast = ((w.n + 31) >> 5) - 1;
     const int word = lane % (D / 2);       // lanes >= d/2 repeat a dword of the lower half
-    const int gi = min((q0 >> 5) + (word * 4) / D, glast);
-    const long long row = seq_group_row_k<kPacked>(g, p.heads_q, w.s, hq, w.doc_start, gi);
-    lds_dma((lw == 4 ? p.qs_scales : p.gs_scales) + row * D + (word * 4) % D, lw == 4 ? st.qss : st.gss, 4);
+    const int gl = ((w.n + 31) >> 5) - 1 - (c.q0 >> 5);   // the last group, relative to q0's
+    const int gi = min((word * 4) / D, gl);
+    lds_dma((lw == 4 ? p.qs_scales : p.gs_scales) + c.srow * D + (uint32_t)(gi * D + (word * 4) % D),
+            lw == 4 ? st.qss : st.gss, 4);
   }
   // ROW tiles (Q, G)
   const int lrow = lane / NCH;
@@ -248,8 +243,8 @@ __device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& 
     if (NCH % NL == 0 || j < NCH) {
       const int row = j * RPI + lrow;
       const int vo = (full ? row : min(row, rmax)) * ts + row_swz(row, lane % NCH, NCH) * 16;
-      if (!kF4) lds_dma(p.q_codes + off0 + (uint32_t)vo, st.qr + j * 1024, 16);
-      lds_dma(p.gr_codes + off0 + (uint32_t)vo, st.gr + j * 1024, 16);
+      if (!kF4) lds_dma(p.q_codes + c.elem + (uint32_t)vo, st.qr + j * 1024, 16);
+      lds_dma(p.gr_codes + c.elem + (uint32_t)vo, st.gr + j * 1024, 16);
     }
   }
   if (kF4) {
@@ -259,7 +254,7 @@ __device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& 
       if (NCHQ % NL == 0 || j < NCHQ) {
         const int row = j * RPIQ + lane / NCHQ;
         const int vo = (full ? row : min(row, rmax)) * (ts >> 1) + row_swz(row, lane % NCHQ, NCHQ) * 16;
-        lds_dma(p.q_codes + (off0 >> 1) + (uint32_t)vo, st.qr + j * 1024, 16);
+        lds_dma(p.q_codes + (c.elem >> 1) + (uint32_t)vo, st.qr + j * 1024, 16);
       }
     }
   }
@@ -419,6 +414,19 @@ __device__ __forceinline__ void ds_block(const BwdParams& p, int s, int h, int d
   const Geom& g = p.geom;
   const uint32_t row = kPacked ? (uint32_t)h * g.gseq + (uint32_t)((doc_start >> 5) + s + qb)
                                : ((uint32_t)s * p.heads_q + h) * g.gseq + qb;
+  exp_idx = row * (uint32_t)p.ds.ecols + kb;
+  if (!kPacked && p.ds.tri)
+    code_blk = ((uint32_t)s * p.heads_q + h) * (uint32_t)p.ds.head_blocks + (uint32_t)(qb * (qb + 1) / 2 + kb);
+  else
+    code_blk = row * (uint32_t)p.ds.cols + kb;
+}
+
+// The same indices given the block row (seq_group_row of query group qb), which the producers
+// carry in their step position: exponent row * ecols + kb; code block row * cols + kb, or under
+// batched causal (b H + h) head_blocks + qb (qb + 1) / 2 + kb.
+template <bool kPacked>
+__device__ __forceinline__ void ds_block_at(const BwdParams& p, int s, int h, uint32_t row, int qb, int kb,
+                                            uint32_t& code_blk, uint32_t& exp_idx) {
   exp_idx = row * (uint32_t)p.ds.ecols + kb;
   if (!kPacked && p.ds.tri)
     code_blk = ((uint32_t)s * p.heads_q + h) * (uint32_t)p.ds.head_blocks + (uint32_t)(qb * (qb + 1) / 2 + kb);
@@ -605,26 +613,48 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     const int fidx = 4 * hh;              // LSE / D index of the lane's rows
     const int slot_off = ds_slot_off(lane);
     const int kb = kw >> 5;               // key group of the dS blocks
-    int hq = w.hkv * group;               // head of step j
-    int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
-    dkv_issue_row<D, kPacked, kDkvProducers, kF4>(p, w, hq_l, q0_l, sm.st[0], lw);
+    const StepWalk sw = step_walk<kPacked>(p.geom, p.heads_q, D, w.s, w.doc_start, w.n, w.hkv * group, qfirst,
+                                           kStepQ);
+    StepPos cur = sw.first;               // step whose codes are computed (j)
+    StepPos ld = sw.first;                // step being loaded (j + 1)
+    dkv_issue_row<D, kPacked, kDkvProducers, kF4>(p, w, ld, sm.st[0], lw);
     wait_vmem();
     wg_barrier();                         // stage 0 loaded
-    int q0 = qfirst;                      // step whose codes are computed (j)
+    // kStore: the dS block of step j is written to the store during step j + 1, right after that
+    // step's loads are issued, while its S and E products run (the block stays in exchange
+    // buffer j % 2 until the end of step j + 1: the accumulators only read it then). pend_* hold
+    // the block's code-block index, exponent index and exponent, pend_buf its buffer.
+    bool pend = false;
+    uint32_t pend_blk = 0, pend_ei = 0;
+    int pend_dse = 0, pend_buf = 0;
+    int stc = 0, stn = 1;                 // stages j % 3 and (j + 1) % 3
     for (int j = 0; j <= nsteps; j++) {
-      next_step(hq_l, q0_l, qfirst, w.n);  // step j + 1
+      step_next(ld, sw, kStepQ);          // step j + 1
       const bool load = j + 1 < nsteps;
+      bool stored = false;
       // the next step's loads are issued while this step's S and E products run. They are
       // issued on every iteration (no branch for the compiler to sink the products past): past
       // the last step they reload the first step, whose addresses are valid, into stage
-      // (j + 1) % 3, which nobody reads then.
+      // (j + 1) % 3, which nobody reads then. Then the previous step's dS block is stored (two
+      // stores, younger than the loads).
       auto issue = [&]() __attribute__((always_inline)) {
-        dkv_issue_row<D, kPacked, kDkvProducers, kF4>(p, w, load ? hq_l : w.hkv * group, load ? q0_l : qfirst,
-                                                      sm.st[(j + 1) % 3], lw);
+        dkv_issue_row<D, kPacked, kDkvProducers, kF4>(p, w, load ? ld : sw.first, sm.st[stn], lw);
+        if (kStore && pend) {
+          asm volatile("" ::: "memory");   // the stores stay behind the loads (counted waits below)
+          const uint8_t* cxp = reinterpret_cast<const uint8_t*>(sm.cx[pend_buf][kg]);
+          const v4i x = ds_read_tr8_pair(cxp + (2 + qt) * 1024 + ds_tr_offset(fresh_lane()));
+          uint32_t lo = (uint32_t)(lane * 16);
+          asm volatile("" : "+v"(lo));     // keeps the scalar-base + 32-bit-offset store form
+          __builtin_nontemporal_store(
+              x, reinterpret_cast<__attribute__((address_space(1))) v4i*>(
+                     scalar_ptr(p.ds_codes + ((uint64_t)pend_blk << 10)) + lo));
+          if (lane == 0) p.ds_exps[pend_ei] = (uint8_t)(pend_dse + 127);
+          stored = true;
+        }
       };
-      bool stored = false;
+      const int q0 = cur.q0;
       if (j < nsteps && active(q0)) {
-        const DkvStage<D>& S = sm.st[j % 3];
+        const DkvStage<D>& S = sm.st[stc];
         uint32_t* cx = sm.cx[j & 1][kg];
         const bool need_mask = (p.causal && kw + 31 > q0) || q0 + kStepQ > w.n || kw + 32 > w.nk;
         int dse;
@@ -634,29 +664,21 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         else
           dse = dkv_codes_tile<D, false, kF4>(S, qt, kop, vop, kvsc, roff_ab, roff_q, fidx, c, 0, 0, true, false, cx,
                                               slot_off, issue);
-        // kStore: this wave's dS block (query group qb, key group kb; under causal only kb <= qb),
-        // read back transposed from the exchange buffer (the wave's own LDS writes, in order)
+        // this wave's dS block (query group qb, key group kb; under causal only kb <= qb)
         const int qb = (q0 >> 5) + qt;
-        if (kStore && (qb << 5) < w.n && (!p.causal || kb <= qb)) {
-          const v4i x = ds_read_tr8_pair(reinterpret_cast<const uint8_t*>(cx) + (2 + qt) * 1024 + ds_tr_offset(fresh_lane()));
-          uint32_t blk, ei;
-          ds_block<kPacked>(p, w.s, hq, w.doc_start, qb, kb, blk, ei);
-          uint32_t lo = (uint32_t)(lane * 16);
-          asm volatile("" : "+v"(lo));     // keeps the scalar-base + 32-bit-offset store form
-          __builtin_nontemporal_store(
-              x, reinterpret_cast<__attribute__((address_space(1))) v4i*>(
-                     scalar_ptr(p.ds_codes + ((uint64_t)blk << 10)) + lo));
-          if (lane == 0) p.ds_exps[ei] = (uint8_t)(dse + 127);
-          stored = true;
+        pend = kStore && (qb << 5) < w.n && (!p.causal || kb <= qb);
+        if (pend) {
+          ds_block_at<kPacked>(p, w.s, cur.hq, (uint32_t)cur.srow + qt, qb, kb, pend_blk, pend_ei);
+          pend_dse = dse;
+          pend_buf = j & 1;
         }
       } else {
         issue();
+        pend = false;
       }
-      q0 += kStepQ;
-      if (q0 >= w.n) {
-        q0 = qfirst;
-        hq++;
-      }
+      step_next(cur, sw, kStepQ);
+      stc = stn;
+      stn = stn == 2 ? 0 : stn + 1;
       // this step's loads have landed once at most the two younger stores are outstanding
       if (stored) wait_vmem_n<2>();
       else wait_vmem();
@@ -753,6 +775,120 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     dkv_mx_views<D, kPacked>(p, w, kw, dk, p.scale, T, p.dkr_codes, p.dkr_scales, p.dks_codes, p.dks_scales);
     dkv_mx_views<D, kPacked>(p, w, kw, dv, 1.f, T, p.dvr_codes, p.dvr_scales, p.dvs_codes, p.dvs_scales);
   }
+}
+
+// ====================== prefix dQ boost (dq_mode 2) ======================
+// FLAMIA notes, section 4 (the last paragraphs): the FP16 dQ sums carry a power-of-two boost per
+// row chosen from that row's own |G_i| and prefix maxima of V and K over the keys it sees, so
+// that no later position changes an earlier row's rounding. a_i = 2 alpha |G~_i| max |V~_j|
+// max_c |K~_jc| (over the visible keys) bounds |dQ_ic| and every partial or running sum of it
+// (|U_ij| <= P_ij (|E_ij| + |D_i|) <= 2 P_ij |G_i| max |V_j|, sum_j P_ij = 1); the boost
+// 2^(14 - ceil(log2 a_i)) keeps the boosted sums below 2^14, under FP16's largest value.
+
+// Boost exponent from the row's |G~| and the prefix maxima at its last visible key (FP32,
+// left to right); [-64, 64]; 64 for a_i = 0 (the row's dQ is 0), 0 for a non-finite a_i.
+__device__ __forceinline__ int dq_boost_exp(float alpha, float gn, float vp, float kp) {
+  const float a = ((2.f * alpha) * gn) * vp * kp;
+  const uint32_t u = __float_as_uint(a);
+  if ((u & kInfBits) == kInfBits) return 0;                 // inf or NaN
+  if (a == 0.f) return 64;
+  int cl;                                                    // ceil(log2 a)
+  if (u >= 0x00800000u) cl = (int)(u >> 23) - 127 + ((u & 0x7FFFFFu) != 0);
+  else {                                                     // subnormal a = u 2^-149
+    const int msb = 31 - __builtin_clz(u);
+    cl = msb - 149 + ((u & ((1u << msb) - 1)) != 0);
+  }
+  return min(64, max(-64, 14 - cl));
+}
+
+// Max of x over the workgroup's threads up to this one (inclusive scan), 256 threads;
+// wmax: 4 floats of shared memory.
+__device__ __forceinline__ float block_scan_max(float x, float* wmax) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(x, o, 64);
+    if (lane >= o) x = fmaxf(x, y);
+  }
+  if (lane == 63) wmax[wave] = x;
+  __syncthreads();
+  for (int w = 0; w < wave; w++) x = fmaxf(x, wmax[w]);
+  __syncthreads();
+  return x;
+}
+
+// vpre[j] = max_{j' <= j} |V~_row,j'|_2 and kpre[j] = max_{j' <= j} max_c |K~_seq,j'c| for the keys of
+// one (KV head, sequence or document): blockIdx.x = KV head, blockIdx.y = sequence or document.
+// The keys go 256 at a time (one per thread), decoded from the views the backward's products read;
+// a workgroup max-scan joins them, carried from one group of 256 to the next.
+template <int D, bool kPacked>
+__global__ __launch_bounds__(256) void bwd_kv_prefix_kernel(BwdParams p) {
+  __shared__ float wm[2][4];
+  __shared__ float last[2];
+  const Geom& gk = p.geom_k;
+  const int hkv = blockIdx.x, s = blockIdx.y;
+  const int doc_k = kPacked ? gk.cu[s] : 0;
+  const int nk = kPacked ? gk.cu[s + 1] - doc_k : gk.seqlen;
+  const long long sbase = kPacked ? (long long)doc_k : (long long)s;
+  float vc = 0.f, kc = 0.f;                 // maxima of the keys before this group of 256
+  for (int j0 = 0; j0 < nk; j0 += 256) {
+    const int j = j0 + (int)threadIdx.x;
+    float vn = 0.f, km = 0.f;
+    if (j < nk) {
+      const long long off = elem_offset_k<kPacked>(gk, p.heads_kv, D, sbase, hkv, j, 0);
+      float ss = 0.f;
+#pragma unroll
+      for (int c16 = 0; c16 < D / 16; c16++) {
+        const v4i w = *reinterpret_cast<const v4i*>(p.vr_codes + off + 16 * c16);
+        const int e = (int)p.vr_scales[(off >> 5) + c16 / 2] - 127;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          float x4[4];
+          unpack4_e4m3((uint32_t)w[q], x4);
+#pragma unroll
+          for (int u = 0; u < 4; u++) {
+            const float x = ldexpf(x4[u], e);
+            ss = __builtin_fmaf(x, x, ss);
+          }
+        }
+      }
+      vn = __builtin_sqrtf(ss);
+      const long long grow = seq_group_row_k<kPacked>(gk, p.heads_kv, s, hkv, doc_k, j >> 5);
+      const uint8_t* kcod = p.ks_codes + grow * (D * 32) + seq_pos(j & 31);
+      const uint8_t* ksc = p.ks_scales + grow * D;
+#pragma unroll 8
+      for (int c = 0; c < D; c++)
+        km = fmaxf(km, fabsf(ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)kcod[c * 32], 0), (int)ksc[c] - 127)));
+    }
+    const float vs = fmaxf(block_scan_max(vn, wm[0]), vc);
+    const float ks = fmaxf(block_scan_max(km, wm[1]), kc);
+    if (j < nk) {
+      const long long idx = token_index_k<kPacked>(gk, p.heads_kv, s, doc_k, hkv, j);
+      p.vpre[idx] = vs;
+      p.kpre[idx] = ks;
+    }
+    if (threadIdx.x == 255) {                // the group's maxima (held by its last thread)
+      last[0] = vs;
+      last[1] = ks;
+    }
+    __syncthreads();
+    vc = last[0];
+    kc = last[1];
+    __syncthreads();
+  }
+}
+
+// Boost exponent of query qi of work item w (dq_mode 2), or 9 (the fixed 2^9 of dq_mode 1).
+template <bool kPacked>
+__device__ __forceinline__ int row_boost_exp(const BwdParams& p, int s, int doc_start, int doc_k, int nk, int h,
+                                             int hkv, int qi, bool qvalid) {
+  if (p.dq_mode != 2) return 9;
+  if (!qvalid) return 0;
+  const int jl = p.causal ? min(qi, nk - 1) : nk - 1;
+  if (jl < 0) return 64;                    // no keys: dQ = 0
+  const float gn = p.gnorm[token_index_k<kPacked>(p.geom, p.heads_q, s, doc_start, h, qi)];
+  const long long kj = token_index_k<kPacked>(p.geom_k, p.heads_kv, s, doc_k, hkv, jl);
+  return dq_boost_exp(p.scale, gn, p.vpre[kj], p.kpre[kj]);
 }
 
 // ================================ dQ pass =================================
@@ -915,7 +1051,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 8; i++) acc16[t][i] = h2{(_Float16)0.f, (_Float16)0.f};
   }
-  const float fmul = p.scale * kBoost;
+  // FP16 modes: partial sums x alpha 2^be (be = 9, or the row's own boost exponent)
+  const int be = kF16 ? (packed(g) ? row_boost_exp<true>(p, w.s, w.doc_start, w.doc_k, w.nk, w.h, hkv, qi, qvalid)
+                                   : row_boost_exp<false>(p, w.s, w.doc_start, w.doc_k, w.nk, w.h, hkv, qi, qvalid))
+                      : 0;
+  const float fmul = ldexpf(p.scale, be);
   auto fold = [&]() {
 #pragma unroll
     for (int t = 0; t < NCT; t++) {
@@ -999,7 +1139,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
     }
   }
 
-  // ---- epilogue: dQ = alpha * acc (FP32) or acc16 * 2^-9; lane writes 4 channels at a time ----
+  // ---- epilogue: dQ = alpha * acc (FP32) or acc16 * 2^-be; lane writes 4 channels at a time ----
   uint32_t bad = 0;
   if (qvalid) {
     const long long obase = elem_offset(g, p.heads_q, D, sbase, w.h, qi, 0);
@@ -1015,7 +1155,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
           const float a = kF16 ? (float)acc16[t][i >> 1][i & 1] : dq[t][i];
           if (__builtin_isnan(a)) bad |= 2u;
           else if (__builtin_isinf(a)) bad |= kF16 ? 1u : 2u;
-          o[u] = kF16 ? a * (1.f / kBoost) : a * p.scale;
+          o[u] = kF16 ? ldexpf(a, -be) : a * p.scale;
         }
         if (p.out_f32) {
           *reinterpret_cast<v4f*>(static_cast<float*>(p.dq) + obase + ch) = v4f{o[0], o[1], o[2], o[3]};
@@ -1162,7 +1302,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 8; i++) acc16[t][i] = h2{(_Float16)0.f, (_Float16)0.f};
   }
-  const float fmul = p.scale * kBoost;
+  // FP16 modes: partial sums x alpha 2^be (be = 9, or the boost exponent of the lane's query
+  // qw + sigma(l32)); its loads complete before the counted waits of the tile ring begin
+  const int qi_l = qw + sigma_q(l32);
+  const int be = kF16 ? row_boost_exp<kPacked>(p, w.s, w.doc_start, w.doc_k, w.nk, w.h, c.hkv, qi_l, qi_l < w.n) : 0;
+  const float fmul = ldexpf(p.scale, be);
+  if (kF16 && p.dq_mode == 2) wait_vmem();
 
   // Ring slot of tile kt: kt mod kPre. Tiles 0 .. P-3 load here; iterations kt = -2, -1 only
   // issue (K 0, dS P-2, K 1, dS P-1), giving the steady-state order from the first real tile.
@@ -1215,7 +1360,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(BwdParams p) {
           const float a = kF16 ? (float)acc16[t][i >> 1][i & 1] : dq[t][i];
           if (__builtin_isnan(a)) bad |= 2u;
           else if (__builtin_isinf(a)) bad |= kF16 ? 1u : 2u;
-          o[u] = kF16 ? a * (1.f / kBoost) : a * p.scale;
+          o[u] = kF16 ? ldexpf(a, -be) : a * p.scale;
         }
         if (p.out_f32) {
           *reinterpret_cast<v4f*>(static_cast<float*>(p.dq) + obase + ch) = v4f{o[0], o[1], o[2], o[3]};
@@ -1310,11 +1455,23 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
   qp.ndelta = p.ndelta;
   qp.lse = p.lse;
   qp.lse2 = p.lse2;
+  qp.gnorm = p.gnorm;
   hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(1), 0, stream, p.flags);
   const int slot = profile_begin(kProfBwdPrep, stream);
   hipError_t err = launch_quantize(qp, stream);
   profile_end(slot, stream);
   if (err != hipSuccess) return err;
+  if (p.dq_mode == 2) {   // prefix maxima of the per-key statistics of the prefix dQ boost
+    const dim3 grid((unsigned)p.heads_kv, (unsigned)(packed(p.geom_k) ? p.geom_k.n_docs : p.geom_k.batch));
+    if (p.head_dim == 128) {
+      if (packed(p.geom_k)) hipLaunchKernelGGL((bwd_kv_prefix_kernel<128, true>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((bwd_kv_prefix_kernel<128, false>), grid, dim3(256), 0, stream, p);
+    } else {
+      if (packed(p.geom_k)) hipLaunchKernelGGL((bwd_kv_prefix_kernel<64, true>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((bwd_kv_prefix_kernel<64, false>), grid, dim3(256), 0, stream, p);
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   // 2. dK / dV, 3. dQ
   return p.head_dim == 128 ? launch_main<128>(p, stream) : launch_main<64>(p, stream);
 }

@@ -27,6 +27,7 @@ struct QuantizeParams {
   float* ndelta;
   const float* lse;
   float* lse2;
+  float* gnorm;          // nullptr, or |G~_row|_2 per (token, head) (the prefix dQ boost)
 };
 
 struct AttnParams {
@@ -72,6 +73,9 @@ struct BwdParams {
   float* ndelta;                                        // -D per (row, head)
   float* lse2;                                          // LSE * log2 e per (row, head)
   uint32_t* flags;
+  // prefix dQ boost (dq_mode 2): |G~_row| per (row, head); prefix maxima of |V~_row,j|_2 and of
+  // max_c |K~_seq,jc| per (key, KV head)
+  float* gnorm; float* vpre; float* kpre;
   // dS code store (nullptr: dQ recomputes dS instead); layout in mx_layout.h DsStore
   uint8_t* ds_codes; uint8_t* ds_exps;
   DsStore ds;

@@ -64,6 +64,61 @@ __host__ __device__ inline long long token_index_k(const Geom& g, int heads, int
   return kPacked ? ((long long)(doc_start + t) * heads + h) : (((long long)s * heads + h) * g.seqlen + t);
 }
 
+// Position of one step (a block of `step` queries of one head) of a loop that visits the steps
+// of consecutive query heads in order: its head and first query, and where its rows start in
+// each stream -- the element offset of (q0, channel 0) in a [B,H,L,d] / [T,H,d] tensor, the
+// index of (q0, head) in a per-row array, and the SEQ-view group row of q0's group. step_next
+// moves it by additions (the next `step` queries); only a change of head multiplies. The
+// backward's producers keep their loop positions this way.
+struct StepPos {
+  int hq, q0;
+  long long elem, tok, srow;
+};
+
+// The increments of StepPos and the position of the first step (head hq0, query qfirst) of
+// sequence or document s (index b or j, first token doc_start when packed) of n queries.
+struct StepWalk {
+  long long elem_step, tok_step, elem_head, tok_head, srow_head;
+  int n;
+  StepPos first;
+};
+
+template <bool kPacked>
+__host__ __device__ inline StepWalk step_walk(const Geom& g, int heads, int d, int s, int doc_start, int n, int hq0,
+                                              int qfirst, int step) {
+  StepWalk sw;
+  const long long sbase = kPacked ? (long long)doc_start : (long long)s;
+  sw.first.hq = hq0;
+  sw.first.q0 = qfirst;
+  sw.first.elem = elem_offset_k<kPacked>(g, heads, d, sbase, hq0, qfirst, 0);
+  sw.first.tok = token_index_k<kPacked>(g, heads, s, doc_start, hq0, qfirst);
+  sw.first.srow = seq_group_row_k<kPacked>(g, heads, s, hq0, doc_start, qfirst >> 5);
+  sw.elem_step = (long long)step * token_stride_k<kPacked>(heads, d);
+  sw.tok_step = kPacked ? (long long)step * heads : step;
+  sw.elem_head = kPacked ? (long long)d : (long long)g.seqlen * d;
+  sw.tok_head = kPacked ? 1 : g.seqlen;
+  sw.srow_head = g.gseq;
+  sw.n = n;
+  return sw;
+}
+
+// The step after c: the next `step` queries of its head, or the first step of the next head.
+// (step a multiple of 32, so the group row moves by step / 32.)
+__host__ __device__ inline void step_next(StepPos& c, const StepWalk& sw, int step) {
+  c.q0 += step;
+  c.elem += sw.elem_step;
+  c.tok += sw.tok_step;
+  c.srow += step >> 5;
+  if (c.q0 >= sw.n) {
+    const int k = c.hq + 1 - sw.first.hq;
+    c = sw.first;
+    c.hq += k;
+    c.elem += k * sw.elem_head;
+    c.tok += k * sw.tok_head;
+    c.srow += k * sw.srow_head;
+  }
+}
+
 // Work order of a batched launch over nbh (sequence, head) pairs x nt tiles per pair, one
 // workgroup per (pair, tile); rank 0 is the most expensive tile of a pair. Workgroups go
 // round-robin to the 8 XCDs (each with its own L2), so XCD x receives workgroups x, x + 8, ...

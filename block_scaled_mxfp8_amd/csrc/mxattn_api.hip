@@ -67,7 +67,7 @@ mx_status check_desc(const mx_attn_desc* d, mx::Geom* g) {
   if (d->heads_q < 1 || d->heads_kv < 1 || d->heads_q % d->heads_kv != 0) return MX_E_ARG;
   if (d->out_dtype != MX_F32 && d->out_dtype != MX_BF16) return MX_E_ARG;
   if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale)) return MX_E_ARG;
-  if (d->dq_mode != MX_DQ_F32 && d->dq_mode != MX_DQ_F16_BOOST) return MX_E_ARG;
+  if (d->dq_mode != MX_DQ_F32 && d->dq_mode != MX_DQ_F16_BOOST && d->dq_mode != MX_DQ_F16_PREFIX) return MX_E_ARG;
   if (!valid_dim(d->head_dim)) return MX_E_UNSUPPORTED;
   if (d->deterministic != 0 && d->deterministic != 1) return MX_E_ARG;
   if (d->score_format != MX_SCORE_MXFP8 && d->score_format != MX_SCORE_MXFP4) return MX_E_ARG;
@@ -80,6 +80,7 @@ mx_status check_desc(const mx_attn_desc* d, mx::Geom* g) {
 // store would need more has no store (store_ok false, total_store = total).
 struct BwdWorkspace {
   size_t gr_codes, gr_scales, gs_codes, gs_scales, ndelta, lse2, flags, total;
+  size_t gnorm, vpre, kpre;   // prefix dQ boost only (0 otherwise)
   size_t ds_codes, ds_exps, total_store;
   bool store_ok;
   mx::DsStore ds;
@@ -96,6 +97,12 @@ BwdWorkspace bwd_layout(const mx::Geom& g, const mx::Geom& gk, const mx_attn_des
   w.gs_scales = off; off += align_up(seq_codes_bytes(g, hq, dim) / 32);
   w.ndelta = off; off += align_up((size_t)g.total * hq * sizeof(float));
   w.lse2 = off; off += align_up((size_t)g.total * hq * sizeof(float));
+  w.gnorm = w.vpre = w.kpre = 0;
+  if (d->dq_mode == MX_DQ_F16_PREFIX) {   // |G~| per (row, head), prefix maxima per (key, KV head)
+    w.gnorm = off; off += align_up((size_t)g.total * hq * sizeof(float));
+    w.vpre = off; off += align_up((size_t)gk.total * d->heads_kv * sizeof(float));
+    w.kpre = off; off += align_up((size_t)gk.total * d->heads_kv * sizeof(float));
+  }
   w.total = off;
   w.ds = mx::ds_store_geom(g, gk, d->causal != 0);
   const size_t rows = (size_t)g.gseq * hq * (mx::packed(g) ? 1 : (size_t)g.batch);   // query groups
@@ -197,6 +204,11 @@ mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
   p.ndelta = reinterpret_cast<float*>(ws + w.ndelta);
   p.lse2 = reinterpret_cast<float*>(ws + w.lse2);
   p.flags = reinterpret_cast<uint32_t*>(ws + w.flags);
+  if (desc->dq_mode == MX_DQ_F16_PREFIX) {
+    p.gnorm = reinterpret_cast<float*>(ws + w.gnorm);
+    p.vpre = reinterpret_cast<float*>(ws + w.vpre);
+    p.kpre = reinterpret_cast<float*>(ws + w.kpre);
+  }
   if (w.store_ok && desc->workspace_bytes >= w.total_store) {
     p.ds_codes = ws + w.ds_codes;
     p.ds_exps = ws + w.ds_exps;

@@ -140,8 +140,9 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
     }
     if (!kBlock && p.o != nullptr) {
       // Backward preprocessing (FLAMIA notes section 5, Algorithm 1 step 09; the same G view
-      // feeds D and dP): D = sum_c G_row~ * O with O as saved, in fp32.
-      float part = 0.f;
+      // feeds D and dP): D = sum_c G_row~ * O with O as saved, in fp32; with gnorm set, also
+      // |G_row~|_2 (the prefix dQ boost's row statistic).
+      float part = 0.f, sq = 0.f;
       float ov[16];
       if (valid) {
         if (p.o_f32) {
@@ -168,16 +169,25 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
           float dq4[4];
           unpack4_e4m3(w[i], dq4);
 #pragma unroll
-          for (int j = 0; j < 4; j++) part = __builtin_fmaf(ldexpf(dq4[j], e), ov[4 * i + j], part);
+          for (int j = 0; j < 4; j++) {
+            const float gq = ldexpf(dq4[j], e);
+            part = __builtin_fmaf(gq, ov[4 * i + j], part);
+            sq = __builtin_fmaf(gq, gq, sq);
+          }
         }
       }
 #pragma unroll
       for (int m = 1; m < TPT; m <<= 1) part += __shfl_xor(part, m);
+      if (p.gnorm) {
+#pragma unroll
+        for (int m = 1; m < TPT; m <<= 1) sq += __shfl_xor(sq, m);
+      }
       if (valid && cb == 0) {
         const long long ti = packed(g) ? ((long long)(doc_start + tok0 + tk) * p.heads + h)
                                        : (((long long)s * p.heads + h) * g.seqlen + tok0 + tk);
         p.ndelta[ti] = -part;
         p.lse2[ti] = p.lse[ti] * 1.4426950408889634f;
+        if (p.gnorm) p.gnorm[ti] = __builtin_sqrtf(sq);
       }
     }
   }

@@ -76,7 +76,7 @@ typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
 
 enum { MX_VIEW_ROW = 1, MX_VIEW_SEQ = 2, MX_VIEW_ROW_FP4 = 4 };
 enum { MX_SCORE_MXFP8 = 0, MX_SCORE_MXFP4 = 1 };
-enum { MX_DQ_F32 = 0, MX_DQ_F16_BOOST = 1 };
+enum { MX_DQ_F32 = 0, MX_DQ_F16_BOOST = 1, MX_DQ_F16_PREFIX = 2 };
 
 /* Bits of the device status word (see mx_read_flags). */
 enum { MX_FLAG_DQ_OVERFLOW = 1u, MX_FLAG_NONFINITE = 2u };
@@ -109,7 +109,9 @@ typedef struct {
   int32_t causal;         /* 1: key j visible to query i iff j <= i inside the sequence/document */
   float softmax_scale;    /* alpha; 0 -> head_dim^-1/2 */
   mx_dtype out_dtype;     /* storage type of O, dQ, dK, dV */
-  int32_t dq_mode;        /* MX_DQ_F32 or MX_DQ_F16_BOOST (FP16 partial sums x 2^9) */
+  int32_t dq_mode;        /* MX_DQ_F32, MX_DQ_F16_BOOST (FP16 partial sums x 2^9) or MX_DQ_F16_PREFIX
+                             (FP16 partial sums x a per-row boost from prefix statistics; see
+                             mx_attn_bwd) */
   int32_t deterministic;  /* 0 or 1; every call is bitwise reproducible (fixed reduction order, no
                              atomics), so 1 costs nothing; other values: MX_E_ARG */
   void* workspace;        /* device scratch for mx_attn_bwd (see mx_attn_workspace_size); with at
@@ -199,6 +201,17 @@ mx_status mx_attn_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, 
  * (ROW and SEQ views) into the workspace and D = rowsum(G_row o O) is formed there. dQ is
  * accumulated in FP32, or (dq_mode = MX_DQ_F16_BOOST) as FP16 sums of FP32 partials over
  * 128-key blocks, each multiplied by 2^9 before rounding; the boost is removed at the end.
+ * dq_mode = MX_DQ_F16_PREFIX (FLAMIA notes, section 4: a data-dependent power-of-two boost per
+ * row, from the row's own |G_i| and prefix maxima of V and K over the keys it sees, so that no
+ * later position changes an earlier row's rounding): the same FP16 sums with the boost
+ * b_i = 2^(14 - ceil(log2 a_i)) of query row i, where
+ *   a_i = 2 alpha |G~_row,i|_2 * max_j |V~_row,j|_2 * max_j max_c |K~_seq,jc|
+ * over the keys j visible to row i (j <= i under causal; every key otherwise), computed in FP32
+ * from the quantised views the products read. a_i bounds |dQ_ic| and every partial or running
+ * sum of it, so the boosted sums stay below 2^14 and cannot overflow FP16 (65504), whatever
+ * the magnitudes. (Exponent clamped to [-64, 64]; 64 for a row with a_i = 0, 0 for a
+ * non-finite a_i.) The workspace then also holds |G~_i| per (row, head) and the prefix maxima
+ * per (key, KV head), written by the backward's prep.
  * With desc->score_format = MX_SCORE_MXFP4, q_row and k_row are the forward's ROW_FP4 views (S
  * and P are rebuilt from them) while q_seq, k_seq and v_row stay E4M3 (FLAMIA notes, section 3:
  * the backward recomputes the scores with the same 4-bit Q/K and uses 8-bit views for dQ and

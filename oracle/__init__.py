@@ -40,7 +40,8 @@ from .codec import (E4M3_MAX, GROUP, e4m3_decode, e4m3_encode, e4m3_round, mx_sc
                     mx_quantize_groups, mx_dequantize_groups, mx_fake_quant, mx_fake_quant_blocks2d,
                     mx_quantize_token_blocks, mx_fake_quant_token_blocks, E2M1_MAX, e2m1_decode, e2m1_encode,
                     e2m1_round, mx4_scale_exponent, mx4_quantize_groups, mx4_dequantize_groups, mx4_pack_row)
-from .attention import (DS_UNSET, head_forward, head_backward, head_reference, visible, round_to, ulp_of)
+from .attention import (DS_UNSET, dq_boost_exponents, head_forward, head_backward, head_reference, visible, round_to,
+                        ulp_of)
 from .norm import rmsnorm, rmsnorm_quantize, fp32_rel_bound, admissible
 from .gemm import gemm_quantize, accumulation_bound, dequant_rows
 from .mfma import (f32, fma32, ulp32, mfma_e4m3, dot_rows as mfma_dot_rows, dot_rows_e2m1 as mfma_dot_rows_e2m1,
@@ -51,7 +52,7 @@ __all__ = [
     "mx_quantize_groups", "mx_dequantize_groups", "mx_fake_quant", "mx_fake_quant_blocks2d",
     "mx_quantize_token_blocks", "mx_fake_quant_token_blocks", "E2M1_MAX", "e2m1_decode", "e2m1_encode",
     "e2m1_round", "mx4_scale_exponent", "mx4_quantize_groups", "mx4_dequantize_groups", "mx4_pack_row",
-    "DS_UNSET", "head_forward", "head_backward", "head_reference", "visible", "round_to", "ulp_of",
+    "DS_UNSET", "dq_boost_exponents", "head_forward", "head_backward", "head_reference", "visible", "round_to", "ulp_of",
     "rmsnorm", "rmsnorm_quantize", "fp32_rel_bound", "admissible", "gemm_quantize", "accumulation_bound", "dequant_rows",
     "f32", "fma32", "ulp32", "mfma_e4m3", "mfma_dot_rows", "mfma_dot_rows_e2m1", "group_max_bound", "exp_magnitude", "model_slack",
 ]

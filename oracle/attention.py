@@ -72,6 +72,9 @@ ROW_CHUNK = 512          # query rows per step (a multiple of 32, so groups neve
 EXP2_REL = 2.0 ** -23    # the hardware exp2: relative error at most one FP32 ulp
 FP32_MIN_NORMAL = 2.0 ** -126
 FP16_BOOST = 512.0       # the FP16 dQ mode's partial sums carry alpha 2^9
+DQ_BOOST_TARGET_EXP = 14  # the per-row boost keeps every boosted dQ sum below 2^14 (FP16 max 65504)
+DQ_BOOST_EXP_CLAMP = 64
+DQ_BOOST_AMBIGUITY = 2.0 ** -20   # relative FP32 error of the device's a_i (norms, products)
 DQ_F16_KEYS = 128        # keys per FP16 dQ partial sum (two 64-key tiles)
 LOG2_448 = math.log2(448.0)
 
@@ -405,6 +408,11 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
     one exponent per 32-token block, so each tensor's ROW and SEQ views hold the same values).
     G is quantised inside the backward with per-axis groups either way.
 
+    ``dq_mode``: "f32", "f16" (FP16 sums of 128-key partials x alpha 2^9) or "f16prefix" (the
+    same with each row's own power-of-two boost from dq_boost_exponents; returned as
+    dq_boost_exp / dq_boost_amb). The values are those of the exact products either way; the
+    mode sets the accumulation allowance.
+
     ``score_format="mxfp4"`` rebuilds S from the same MXFP4 Q and K views as head_forward
     (FLAMIA notes, section 3: the backward recomputes the scores with the original 4-bit Q/K
     and takes E4M3 views for dQ and dK); every other product is unchanged.
@@ -456,6 +464,13 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
         if perturb is not None:
             D = perturb("D", D, dD)
     D32 = f32(D) if quantized else D
+    boost_exp = boost_amb = None
+    if dq_mode == "f16prefix":
+        assert quantized, "the prefix boost is a mode of the quantised path"
+        be_nom, be_lo, boost_amb = dq_boost_exponents(Grx, Vrx, Ksx, alpha, causal)
+        boost_exp = be_lo                  # the smaller boost: the larger FP16 rounding
+    else:
+        assert dq_mode in ("f32", "f16"), dq_mode
     if dq_blocks is not None:
         chunks = [(32 * int(b), min(n, 32 * int(b) + 32)) for b in sorted(set(dq_blocks))]
     else:
@@ -535,21 +550,22 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
             ds_exp_amb[qb0:qb0 + ue.shape[0], kblk] = eamb[::GROUP, ::GROUP][:, :len(kblk)] if rows else False
             # product allowances at the largest admissible codes (value + dev, group exponent at
             # most one above the nominal one)
+            bx = None if boost_exp is None else boost_exp[r0:r1]
             up = _product_allowances(np.abs(Pb) + devPb, pe_elem + (devPb > 0), Uh, devU, ue_elem + (devU > 0),
                                      Gsx[r0:r1], Gsm[r0:r1], Qsx[r0:r1], Qsm[r0:r1], Ksx[kc], Ksm, alpha, n,
-                                     dq_mode)
+                                     dq_mode, bx)
             edV[kc] += up[0]
             edK[kc] += up[1]
             edQ[r0:r1] = up[2]
             if perturb is not None:
                 # a device whose codes are this run's: the allowances of its own products
                 own = _product_allowances(np.abs(Pb), pe_elem, Uh, np.zeros_like(Uh), ue_elem, Gsx[r0:r1],
-                                          Gsm[r0:r1], Qsx[r0:r1], Qsm[r0:r1], Ksx[kc], Ksm, alpha, n, dq_mode)
+                                          Gsm[r0:r1], Qsx[r0:r1], Qsm[r0:r1], Ksx[kc], Ksm, alpha, n, dq_mode, bx)
                 pdV[kc] += own[0]
                 pdK[kc] += own[1]
                 pdQ[r0:r1] = own[2]
     if need:
-        edQ += U32 * (np.abs(dQ) + BdQ)        # the final multiply by alpha (FP32 mode) or 2^-9
+        edQ += U32 * (np.abs(dQ) + BdQ)        # the final multiply by alpha (FP32 mode) or 1/b
         edK += U32 * (np.abs(dK) + BdK)
         if perturb is not None:
             dQ = perturb("dQ", dQ, pdQ + U32 * np.abs(dQ))
@@ -567,6 +583,8 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
     out = dict(dQ=dQ, dK=dK, dV=dV, D=D, dQ_out=round_to(dQ, out_dtype), dK_out=round_to(dK, out_dtype),
                dV_out=round_to(dV, out_dtype), dS_codes=ds_codes, dS_exp=ds_exp, dS_amb=ds_amb,
                dS_exp_amb=ds_exp_amb)
+    if boost_exp is not None:
+        out.update(dq_boost_exp=be_nom, dq_boost_amb=boost_amb)
     if bounds and need:
         out.update(B_dQ=BdQ, B_dK=BdK, B_dV=BdV, eta_dQ=edQ, eta_dK=edK, eta_dV=edV)
     elif bounds:
@@ -579,7 +597,7 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
 DS_UNSET = -1000          # dS_exp of a block the call did not evaluate
 
 
-def _product_allowances(Pb_abs, pb_exp, Uh, devU, u_exp, Gs, Gsm, Qs, Qsm, Ks, Ksm, alpha, n, dq_mode):
+def _product_allowances(Pb_abs, pb_exp, Uh, devU, u_exp, Gs, Gsm, Qs, Qsm, Ks, Ksm, alpha, n, dq_mode, boost_exp=None):
     """Accumulation allowances of one query chunk's contributions to dV = P_b^T G_seq,
     dK = alpha U^T Q_seq and dQ = alpha U K_seq (the chunk's rows). Pb_abs: |P_b| values (or an
     upper bound); Uh: dS values, devU: how far each may move (|Uh| + devU bounds it); *_exp:
@@ -595,19 +613,20 @@ def _product_allowances(Pb_abs, pb_exp, Uh, devU, u_exp, Gs, Gsm, Qs, Qsm, Ks, K
         nkc = Uh.shape[1]
         pdQ = alpha * (GROUP_TRUNC * group_max_bound(Um, Ksm, nkc) + 4 * (_ins(nkc) + 1) * U32 * (Ua @ np.abs(Ks)))
     else:
-        pdQ = _f16_dq_allowance(Uh, devU, Um, Ks, Ksm, alpha)
+        pdQ = _f16_dq_allowance(Uh, devU, Um, Ks, Ksm, alpha, boost_exp)
     return pdV, pdK, pdQ
 
 
-def _f16_dq_allowance(Uh, devU, Um, Ks, Ksm, alpha):
-    """Accumulation allowance of dQ in the FP16 mode: the partial sum of every 128 keys (FP32
-    matrix-core chain) is multiplied by alpha 2^9 in FP32, rounded to FP16 and added to an FP16
-    running sum; the result is scaled by 2^-9. Per partial t: its product allowance, one FP32
-    rounding of the multiply, half an FP16 ulp of the partial and half an FP16 ulp of the
-    signed running sum R_t (its magnitude, plus what alternative codes (devU) and the
-    allowance so far can add)."""
+def _f16_dq_allowance(Uh, devU, Um, Ks, Ksm, alpha, boost_exp=None):
+    """Accumulation allowance of dQ in the FP16 modes: the partial sum of every 128 keys (FP32
+    matrix-core chain) is multiplied by alpha b in FP32 (b = 2^9, or the row's own boost 2^e
+    in the prefix mode: boost_exp per row), rounded to FP16 and added to an FP16 running sum;
+    the result is scaled by 1/b. Per partial t: its product allowance, one FP32 rounding of the
+    multiply, half an FP16 ulp of the partial and half an FP16 ulp of the signed running sum
+    R_t (its magnitude, plus what alternative codes (devU) and the allowance so far can add)."""
     rows, nkc = Uh.shape
-    boost = alpha * FP16_BOOST
+    bval = FP16_BOOST if boost_exp is None else np.ldexp(1.0, np.asarray(boost_exp))[:, None]
+    boost = alpha * bval
     err = np.zeros((rows, Ks.shape[1]))
     run = np.zeros_like(err)
     alt = np.zeros_like(err)
@@ -622,7 +641,50 @@ def _f16_dq_allowance(Uh, devU, Um, Ks, Ksm, alpha):
         run = run + boost * part
         alt = alt + boost * dpart
         err = err + boost * pe + U32 * y + _half_ulp16(y) + _half_ulp16(np.abs(run) + alt + err + y)
-    return err / FP16_BOOST
+    return err / bval
+
+
+def dq_boost_exponents(G_row, V_row, K_seq, alpha, causal, n_keys=None):
+    """Per-row FP16 dQ boost of the prefix mode (FLAMIA notes, section 4, the last paragraphs:
+    a data-dependent power-of-two boost b_i = 2^floor(log2(h / a_i)) before the FP16 reduction,
+    with the strict option taking each row's own |G_i| and prefix maxima of V and K over the keys
+    the row sees, so that no later position changes an earlier row's boost).
+
+    a_i = 2 alpha |G~_row,i|_2 max_{j visible} |V~_row,j|_2 max_{j visible} max_c |K~_seq,jc| bounds
+    |dQ_ic| and each partial or running sum of it (|U_ij| <= P_ij (|E_ij| + |D_i|) with |E_ij| <=
+    |G_i| |V_j| and |D_i| <= |G_i| |O_i| <= |G_i| max_j |V_j|, and sum_j P_ij = 1); the visible keys
+    are j <= i under causal, else all. With h = 2^14: b_i = 2^(14 - ceil(log2 a_i)), so b_i a_i <=
+    2^14; the exponent is clamped to [-64, 64] (64 when a_i = 0: the row's dQ is 0), and is 0
+    for a non-finite a_i.
+
+    Returns (exponent per row, the smallest exponent a device whose FP32 a_i is within
+    DQ_BOOST_AMBIGUITY of it can choose, whether the two differ)."""
+    G_row, V_row, K_seq = (np.asarray(a, np.float64) for a in (G_row, V_row, K_seq))
+    n = G_row.shape[0]
+    nk = V_row.shape[0] if n_keys is None else n_keys
+    vn = np.sqrt(np.sum(V_row[:nk] ** 2, axis=1))
+    km = np.max(np.abs(K_seq[:nk]), axis=1) if nk else np.zeros(0)
+    if causal:
+        idx = np.minimum(np.arange(n), nk - 1)
+        vp = np.maximum.accumulate(vn)[idx] if nk else np.zeros(n)
+        kp = np.maximum.accumulate(km)[idx] if nk else np.zeros(n)
+    else:
+        vp = np.full(n, vn.max() if nk else 0.0)
+        kp = np.full(n, km.max() if nk else 0.0)
+    a = 2.0 * alpha * np.sqrt(np.sum(G_row ** 2, axis=1)) * vp * kp
+
+    def expo(x):
+        with np.errstate(divide="ignore", invalid="ignore"):
+            m, ex = np.frexp(np.where(x > 0, x, 1.0))          # x = m 2^ex, m in [0.5, 1)
+            ceil_log2 = np.where(m == 0.5, ex - 1, ex)
+        e = np.clip(DQ_BOOST_TARGET_EXP - ceil_log2, -DQ_BOOST_EXP_CLAMP, DQ_BOOST_EXP_CLAMP)
+        e = np.where(x > 0, e, DQ_BOOST_EXP_CLAMP)
+        return np.where(np.isfinite(x), e, 0).astype(np.int64)
+
+    e = expo(a)
+    e_lo = np.minimum(e, expo(a * (1 + DQ_BOOST_AMBIGUITY)))
+    e_lo = np.minimum(e_lo, expo(a * (1 - DQ_BOOST_AMBIGUITY)))
+    return e, e_lo, e_lo != e
 
 
 def _dev_cols(P, drel):

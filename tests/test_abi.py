@@ -350,3 +350,19 @@ def test_binding_reads_the_score_format_from_the_views():
     assert _lib._score_format(fp8, fp8) == _lib.MX_SCORE_MXFP8
     with pytest.raises(ValueError):
         _lib._score_format(fp8, fp4)
+
+
+def test_prefix_boost_workspace_and_mode_validation(lib):
+    # dq_mode 2 (per-row prefix boost) adds |G~| per (row, head) and two prefix-maximum arrays per
+    # (key, KV head) before the dS store; dq_mode 3 is an argument error
+    B, H, L, d = 2, 3, 100, 128
+    base = _bwd_desc(_seq(batch=B, seqlen=L), H, d, 1)
+    pre = _bwd_desc(_seq(batch=B, seqlen=L), H, d, 1)
+    pre.dq_mode = 2
+    extra = 3 * _up(B * H * L * 4)
+    assert lib.mx_attn_workspace_size(ctypes.byref(pre), 1) == lib.mx_attn_workspace_size(ctypes.byref(base), 1) + extra
+    assert lib.mx_attn_workspace_size(ctypes.byref(pre), 2) == lib.mx_attn_workspace_size(ctypes.byref(base), 2) + extra
+    v = _lib._QView(FAKE, FAKE)
+    bad = _desc(dq_mode=3)
+    bad.workspace, bad.workspace_bytes = FAKE, 1 << 30
+    assert lib.mx_attn_bwd(ctypes.byref(bad), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None) == _lib.MX_E_ARG

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import synth
-from block_scaled_mxfp8_amd import MX_DQ_F16_BOOST, MX_DQ_F32, mx_attn_bwd, mx_attn_fwd, mx_quantize
+from block_scaled_mxfp8_amd import MX_DQ_F16_BOOST, MX_DQ_F16_PREFIX, MX_DQ_F32, mx_attn_bwd, mx_attn_fwd, mx_quantize
 from tests.layouts import DsStore, as_f64, compare_ds, to_device
 from tests.metrics import REL, cosine, gate, rms
 
@@ -52,6 +52,11 @@ def _bwd_dev(t, o, lse, causal, out_dtype, dq_mode, ds_store=True):
 
 def _odt(dtype):
     return "f32" if dtype == torch.float32 else "bf16"
+
+
+def _omode(dq_mode):
+    """The oracle's name of a dQ accumulation mode."""
+    return {MX_DQ_F32: "f32", MX_DQ_F16_BOOST: "f16", MX_DQ_F16_PREFIX: "f16prefix"}[dq_mode]
 
 
 def _check_ds_store(ws, q_shape, causal, ors, L, dq_mode, cu=None, max_seqlen=None, heads_kv=None):
@@ -111,6 +116,10 @@ BWD_CASES = [
     ("c3", 1, 2, 2, 97, 128, torch.bfloat16, False, MX_DQ_F32),
     ("c3", 2, 1, 1, 130, 64, torch.bfloat16, True, MX_DQ_F16_BOOST),
     ("c5", 1, 4, 2, 160, 128, torch.bfloat16, False, MX_DQ_F32),
+    # the per-row prefix boost of the FP16 sums
+    ("c2", 1, 2, 2, 200, 128, torch.bfloat16, True, MX_DQ_F16_PREFIX),
+    ("c3", 2, 1, 1, 130, 64, torch.bfloat16, True, MX_DQ_F16_PREFIX),
+    ("c5", 1, 4, 2, 160, 128, torch.bfloat16, False, MX_DQ_F16_PREFIX),
 ]
 
 
@@ -140,7 +149,7 @@ def test_backward_matches_oracle(case):
         for h in range(H):
             hk = h // (H // Hkv)
             r = oracle.head_backward(q[b, h], k[b, hk], v[b, hk], O_saved[b, h], LSE[b, h].astype(np.float64),
-                                     g[b, h], causal, out_dtype=odt, bounds=True, dq_mode="f32" if dq_mode == 0 else "f16")
+                                     g[b, h], causal, out_dtype=odt, bounds=True, dq_mode=_omode(dq_mode))
             ors[b, h] = r
             ref["dQ"][b, h] = r["dQ"]
             Bb["dQ"][b, h] = r["B_dQ"]
@@ -161,7 +170,7 @@ def test_backward_matches_oracle(case):
             key = "dQ16" if (n == "dQ" and dq_mode != 0) else n
             assert gate(n, dev[n], ref[n], Bb[n], eta[n], odt, key=key).ok, n
         if ds_store:
-            _check_ds_store(ws, t["q"].shape, causal, ors, L, dq_mode)
+            _check_ds_store(ws, t["q"].shape, causal, ors, L, dq_mode, heads_kv=Hkv)
     # the two variants quantise the same dS blocks the same way
     for n, a, b in zip(("dQ", "dK", "dV"), outs[True], outs[False]):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)) if a.dtype == torch.bfloat16 \
@@ -241,3 +250,30 @@ def test_fp16_dq_overflow_sets_the_flag():
                               True, torch.bfloat16, MX_DQ_F32)
     torch.cuda.synchronize()
     assert mx_read_flags(ws) == 0
+
+
+def test_prefix_boost_keeps_the_fp16_sums_in_range():
+    # The same x50-outlier inputs where the fixed 2^9 boost overflows (max |dQ| ~ 266): the
+    # per-row prefix boost bounds every boosted sum by 2^14, so no overflow, and dQ passes the
+    # FP16 gate against the oracle's prefix mode.
+    from block_scaled_mxfp8_amd import mx_read_flags
+    t = _inputs("c2", 1, 2, 2, 64, 128, torch.bfloat16)
+    q, k, v, g = (as_f64(t[n]) for n in ("q", "k", "v", "g"))
+    O_saved = np.zeros(q.shape)
+    LSE = np.zeros(q.shape[:-1], np.float32)
+    refs = []
+    for h in range(2):
+        f = oracle.head_forward(q[0, h], k[0, h], v[0, h], True)
+        O_saved[0, h], LSE[0, h] = f["O_out"], f["lse"]
+        refs.append(oracle.head_backward(q[0, h], k[0, h], v[0, h], f["O_out"], f["lse"].astype(np.float32).astype(np.float64),
+                                         g[0, h], True, bounds=True, dq_mode="f16prefix"))
+    print(f"  boost exponents (oracle): {sorted(set(np.concatenate([r['dq_boost_exp'] for r in refs]).tolist()))}",
+          flush=True)
+    for ds_store in (True, False):
+        dq, dk, dv, ws = _bwd_dev(t, torch.from_numpy(O_saved).to(torch.bfloat16).cuda(), torch.from_numpy(LSE).cuda(),
+                                  True, torch.bfloat16, MX_DQ_F16_PREFIX, ds_store=ds_store)
+        torch.cuda.synchronize()
+        assert mx_read_flags(ws) == 0, ds_store
+        dev = as_f64(dq)[0]
+        assert gate("dQ", dev, np.stack([r["dQ"] for r in refs]), np.stack([r["B_dQ"] for r in refs]),
+                    np.stack([r["eta_dQ"] for r in refs]), key="dQ16").ok, ds_store

@@ -11,13 +11,16 @@ section 9 on the tests it proposes): two inputs that differ only from token p on
   group, while rows before 96 stay identical; a suffix value below the group's maximum leaves
   every row before p identical. This is the scale-geometry dependency the pages describe.
 dK and dV accumulate later queries by definition and are not probed.
+The dQ probe runs in the FP32 mode and in the FP16 mode with the per-row prefix boost (FLAMIA
+notes, section 4: each row's boost from its own |G_i| and prefix maxima over the keys it sees, so
+a later position cannot change it; a boost from whole-sequence statistics could).
 """
 import numpy as np
 import pytest
 import torch
 
 import synth
-from block_scaled_mxfp8_amd import mx_attn_bwd, mx_attn_fwd, mx_quantize
+from block_scaled_mxfp8_amd import MX_DQ_F16_PREFIX, MX_DQ_F32, mx_attn_bwd, mx_attn_fwd, mx_quantize
 from tests.layouts import to_device
 
 pytestmark = pytest.mark.gpu
@@ -29,7 +32,7 @@ def _base():
     return {n: np.ascontiguousarray(x[n][..., :d]) for n in ("q", "k", "v", "g")}
 
 
-def _fwd_bwd(x, backward=True, out_dtype=torch.bfloat16):
+def _fwd_bwd(x, backward=True, out_dtype=torch.bfloat16, dq_mode=MX_DQ_F32):
     t = {n: to_device(x[n], torch.bfloat16) for n in x}
     q_row, q_seq = mx_quantize(t["q"])
     k_row, k_seq = mx_quantize(t["k"])
@@ -37,21 +40,23 @@ def _fwd_bwd(x, backward=True, out_dtype=torch.bfloat16):
     o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=True, out_dtype=out_dtype)
     out = {"o": o, "lse": lse}
     if backward:
-        out["dq"] = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=True, out_dtype=out_dtype)[0]
+        out["dq"] = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=True, out_dtype=out_dtype,
+                                dq_mode=dq_mode)[0]
     torch.cuda.synchronize()
     return {n: v.view(torch.int16) if v.dtype == torch.bfloat16 else v.view(torch.int32) for n, v in out.items()}
 
 
+@pytest.mark.parametrize("dq_mode", [MX_DQ_F32, MX_DQ_F16_PREFIX])
 @pytest.mark.parametrize("p", [32, 96, 224])
 @pytest.mark.parametrize("factor", [2.0 ** 12, 2.0 ** -24])
-def test_aligned_suffix_leaves_the_prefix_bit_identical(p, factor):
-    print(f"[suffix] p={p} factor={factor}", flush=True)
+def test_aligned_suffix_leaves_the_prefix_bit_identical(p, factor, dq_mode):
+    print(f"[suffix] p={p} factor={factor} dq_mode={dq_mode}", flush=True)
     x0 = _base()
     x1 = {n: a.copy() for n, a in x0.items()}
     rng = np.random.default_rng(p)
     for n in ("q", "k", "v", "g"):
         x1[n][:, :, p:] = (rng.standard_normal(x1[n][:, :, p:].shape) * factor).astype(np.float32)
-    a, b = _fwd_bwd(x0), _fwd_bwd(x1)
+    a, b = _fwd_bwd(x0, dq_mode=dq_mode), _fwd_bwd(x1, dq_mode=dq_mode)
     assert torch.equal(a["o"][:, :, :p], b["o"][:, :, :p]), "O prefix changed"
     assert torch.equal(a["lse"][:, :, :p], b["lse"][:, :, :p]), "LSE prefix changed"
     assert torch.equal(a["dq"][:, :, :p], b["dq"][:, :, :p]), "dQ prefix changed"

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from block_scaled_mxfp8_amd import (MX_DQ_F32, mx_attn_varlen_bwd, mx_attn_varlen_fwd, mx_quantize)
+from block_scaled_mxfp8_amd import (MX_DQ_F16_PREFIX, MX_DQ_F32, mx_attn_varlen_bwd, mx_attn_varlen_fwd, mx_quantize)
 from tests.layouts import DsStore, as_f64, compare_ds, to_device
 from tests.metrics import cosine, gate
 
@@ -45,9 +45,9 @@ def _bwd(t, o, lse, cud, maxlen, causal=True, dq_mode=MX_DQ_F32, ds_store=True):
 LENGTHS = [1, 31, 32, 33, 100, 7, 300, 129, 64]
 
 
-def _check_ds(ws, q_shape, cu, maxlen, Hkv, ors):
+def _check_ds(ws, q_shape, cu, maxlen, Hkv, ors, dq_mode=MX_DQ_F32):
     """Stored dS blocks of the documents in ors[(j, h)] against the oracle's decisions."""
-    store = DsStore(ws, tuple(q_shape), True, torch.from_numpy(np.asarray(cu, np.int32)).cuda(), maxlen, Hkv)
+    store = DsStore(ws, tuple(q_shape), True, torch.from_numpy(np.asarray(cu, np.int32)).cuda(), maxlen, Hkv, dq_mode)
     tot = [0, 0, 0, 0, 0]
     for (j, h), r in ors.items():
         n = int(cu[j + 1] - cu[j])
@@ -81,9 +81,9 @@ def test_varlen_forward_matches_oracle(H, Hkv, d):
     assert gate("O", np.concatenate(devs), np.concatenate(refs), np.concatenate(Bs), np.concatenate(etas)).ok
 
 
-@pytest.mark.parametrize("H,Hkv,d", [(2, 2, 128), (4, 2, 64)])
-def test_varlen_backward_matches_oracle(H, Hkv, d):
-    print(f"[varlen bwd] H{H} kv{Hkv} d{d}", flush=True)
+@pytest.mark.parametrize("H,Hkv,d,dq_mode", [(2, 2, 128, MX_DQ_F32), (4, 2, 64, MX_DQ_F32), (4, 2, 128, MX_DQ_F16_PREFIX)])
+def test_varlen_backward_matches_oracle(H, Hkv, d, dq_mode):
+    print(f"[varlen bwd] H{H} kv{Hkv} d{d} dq_mode {dq_mode}", flush=True)
     x, cu = _packed(LENGTHS, H, Hkv, d)
     t, cud = _dev(x, cu)
     q, k, v, g = (as_f64(t[n]) for n in ("q", "k", "v", "g"))
@@ -105,7 +105,8 @@ def test_varlen_backward_matches_oracle(H, Hkv, d):
         for h in range(H):
             hk = h // (H // Hkv)
             r = oracle.head_backward(q[a:b, h], k[a:b, hk], v[a:b, hk], O[a:b, h], LSE[a:b, h].astype(np.float64),
-                                     g[a:b, h], True, bounds=True)
+                                     g[a:b, h], True, bounds=True,
+                                     dq_mode="f16prefix" if dq_mode == MX_DQ_F16_PREFIX else "f32")
             ors[j, h] = r
             ref["dQ"][a:b, h] = r["dQ"]
             Bb["dQ"][a:b, h] = r["B_dQ"]
@@ -118,14 +119,15 @@ def test_varlen_backward_matches_oracle(H, Hkv, d):
     outs = {}
     for ds_store in (True, False):
         print(f"  ds_store={ds_store}", flush=True)
-        dq, dk, dv, ws = _bwd(t, o_dev, lse_dev, cud, max(LENGTHS), ds_store=ds_store)
+        dq, dk, dv, ws = _bwd(t, o_dev, lse_dev, cud, max(LENGTHS), dq_mode=dq_mode, ds_store=ds_store)
         torch.cuda.synchronize()
         outs[ds_store] = (dq, dk, dv)
         dev = {"dQ": as_f64(dq), "dK": as_f64(dk), "dV": as_f64(dv)}
         for n in ("dQ", "dK", "dV"):
-            assert gate(n, dev[n], ref[n], Bb[n], eta[n]).ok, n
+            key = "dQ16" if (n == "dQ" and dq_mode != MX_DQ_F32) else n
+            assert gate(n, dev[n], ref[n], Bb[n], eta[n], key=key).ok, n
         if ds_store:
-            _check_ds(ws, q.shape, cu, max(LENGTHS), Hkv, ors)
+            _check_ds(ws, q.shape, cu, max(LENGTHS), Hkv, ors, dq_mode)
     for n, a, b in zip(("dQ", "dK", "dV"), outs[True], outs[False]):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), n
 

@@ -49,3 +49,24 @@ def test_generator_magnitude_is_per_token():
     # u ~ U(0.5, 4) is shared by all heads and channels of a token
     r = np.abs(x).mean(axis=(1, 3))[0]
     assert r.min() > 0.2 and r.max() < 4.0
+
+
+def test_backward_step_cursor_matches_the_layout_formulas(tmp_path):
+    # The backward producers walk their (head, 64-query step) positions by additions
+    # (mx_layout.h step_walk / step_next); a host build of that header checks every step of many
+    # batched and packed geometries against the closed address formulas.
+    import os
+    import shutil
+    import subprocess
+    import pytest
+    hipcc = shutil.which("hipcc") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else None)
+    if hipcc is None:
+        pytest.skip("hipcc not available")
+    here = os.path.dirname(os.path.abspath(__file__))
+    exe = str(tmp_path / "step_walk_check")
+    subprocess.run([hipcc, "-O1", "-std=c++17", os.path.join(here, "host_cpp", "step_walk_check.cpp"), "-o", exe],
+                   check=True, capture_output=True)
+    out = subprocess.run([exe], capture_output=True, text=True)
+    print(out.stdout)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "0 mismatches" in out.stdout
