@@ -38,7 +38,7 @@ in integers) agreeing; its agreement with the hardware is a GPU test.
 """
 from .codec import (E4M3_MAX, GROUP, e4m3_decode, e4m3_encode, e4m3_round, mx_scale_exponent,
                     mx_quantize_groups, mx_dequantize_groups, mx_fake_quant, mx_fake_quant_blocks2d,
-                    mx_quantize_token_blocks, mx_fake_quant_token_blocks, E2M1_MAX, e2m1_decode, e2m1_encode,
+                    mx_quantize_token_blocks, mx_fake_quant_token_blocks, mx_quantize_per_token, E2M1_MAX, e2m1_decode, e2m1_encode,
                     e2m1_round, mx4_scale_exponent, mx4_quantize_groups, mx4_dequantize_groups, mx4_pack_row)
 from .attention import (DS_UNSET, dq_boost_exponents, head_forward, head_backward, head_reference, visible, round_to,
                         ulp_of)
@@ -50,7 +50,7 @@ from .mfma import (f32, fma32, ulp32, mfma_e4m3, dot_rows as mfma_dot_rows, dot_
 __all__ = [
     "E4M3_MAX", "GROUP", "e4m3_decode", "e4m3_encode", "e4m3_round", "mx_scale_exponent",
     "mx_quantize_groups", "mx_dequantize_groups", "mx_fake_quant", "mx_fake_quant_blocks2d",
-    "mx_quantize_token_blocks", "mx_fake_quant_token_blocks", "E2M1_MAX", "e2m1_decode", "e2m1_encode",
+    "mx_quantize_token_blocks", "mx_fake_quant_token_blocks", "mx_quantize_per_token", "E2M1_MAX", "e2m1_decode", "e2m1_encode",
     "e2m1_round", "mx4_scale_exponent", "mx4_quantize_groups", "mx4_dequantize_groups", "mx4_pack_row",
     "DS_UNSET", "dq_boost_exponents", "head_forward", "head_backward", "head_reference", "visible", "round_to", "ulp_of",
     "rmsnorm", "rmsnorm_quantize", "fp32_rel_bound", "admissible", "gemm_quantize", "accumulation_bound", "dequant_rows",

@@ -316,3 +316,20 @@ def mx4_pack_row(codes):
     c = np.asarray(codes).astype(np.uint8)
     assert c.shape[-1] % 2 == 0
     return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
+
+
+def mx_quantize_per_token(x):
+    """One E8M0 exponent per token for all of its channels (the per-key scale of FLAMIA's strict
+    option on diagonal tiles, notes section 4: P_ij (s_j v_j) = (P_ij s_j) v_j, so each term's
+    scale depends on its own key only). x: [n, d]; the exponent is the group rule
+    (mx_scale_exponent) on the token's largest |x|; a token holding a NaN or an infinity gets
+    scale byte 0xFF and codes 0x7F. Returns (codes uint8 [n, d], exponents int64 [n], scale
+    bytes uint8 [n])."""
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.all(np.isfinite(x), axis=1)
+    amax = np.max(np.abs(np.where(np.isfinite(x), x, 0.0)), axis=1) if x.shape[1] else np.zeros(x.shape[0])
+    e = mx_scale_exponent(amax)
+    codes = e4m3_encode(np.ldexp(x, -e[:, None]))
+    codes = np.where(finite[:, None], codes, E4M3_NAN).astype(np.uint8)
+    sbytes = np.where(finite, e + E8M0_BIAS, E8M0_NAN).astype(np.uint8)
+    return codes, e, sbytes
