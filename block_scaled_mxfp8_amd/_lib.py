@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 MX_OK, MX_E_ARG, MX_E_UNSUPPORTED, MX_E_WORKSPACE, MX_E_DEVICE = range(5)
 MX_F32, MX_BF16 = 0, 1
-MX_VIEW_ROW, MX_VIEW_SEQ, MX_VIEW_ROW_FP4 = 1, 2, 4
+MX_VIEW_ROW, MX_VIEW_SEQ, MX_VIEW_ROW_FP4, MX_VIEW_SEQ_TOKEN = 1, 2, 4, 8
 MX_DQ_F32, MX_DQ_F16_BOOST, MX_DQ_F16_PREFIX = 0, 1, 2
 MX_SCORE_MXFP8, MX_SCORE_MXFP4 = 0, 1
 
@@ -98,6 +98,8 @@ def load():
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, P, P, P]
         f.restype = I32
+    lib.mx_attn_fwd_strict.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, _QView, P, P, P]
+    lib.mx_attn_fwd_strict.restype = I32
     for name in ("mx_attn_bwd", "mx_attn_varlen_bwd", "mx_attn_bwd_noalloc"):
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, _QView, _QView, P, P, P, I32, P, P, P, P]
@@ -217,21 +219,26 @@ def _view_bytes(lib, seq, heads, d, view):
             lib.mx_view_scales_bytes(ctypes.byref(seq), heads, d, view))
 
 
-def _seq_view_shapes(shape, seq, cu_seqlens):
+def _seq_view_shapes(shape, seq, cu_seqlens, per_token=False):
+    """Codes and scales shapes of the SEQ view (per_token: the SEQ_TOKEN view, one scale byte
+    per token slot of each group row)."""
     d = shape[-1]
+    sd = 32 if per_token else d
     if cu_seqlens is None:
         B, H, L, _ = shape
         G = (L + 31) // 32
-        return (B, H, G, d, 32), (B, H, G, d)
+        return (B, H, G, d, 32), (B, H, G, sd)
     T, H, _ = shape
     Gc = T // 32 + (cu_seqlens.numel() - 1)
-    return (H, Gc, d, 32), (H, Gc, d)
+    return (H, Gc, d, 32), (H, Gc, sd)
 
 
 def mx_quantize(x, views=MX_VIEW_ROW | MX_VIEW_SEQ, cu_seqlens=None, max_seqlen=None):
     """Quantise x ([B,H,L,d] or packed [T,H,d], fp32/bf16) -> (row QView or None, seq QView or None).
     views may hold MX_VIEW_ROW_FP4 instead of MX_VIEW_ROW: the row QView is then MXFP4 (codes
-    [..., d/2], two E2M1 codes per byte), the score operands of the mixed 4-bit path."""
+    [..., d/2], two E2M1 codes per byte), the score operands of the mixed 4-bit path; and
+    MX_VIEW_SEQ_TOKEN instead of MX_VIEW_SEQ: the seq QView then has one exponent per token
+    (scales [..., G, 32]), the V operand of mx_attn_fwd_strict."""
     return _quantize(x, views, cu_seqlens, max_seqlen, "mx_quantize")
 
 
@@ -257,12 +264,13 @@ def _quantize(x, views, cu_seqlens, max_seqlen, name):
         row = QView(torch.empty(cshape, dtype=torch.uint8, device=x.device),
                     torch.empty(shape[:-1] + (d // 32,), dtype=torch.uint8, device=x.device))
         rv = _qv(row)
-    if views & MX_VIEW_SEQ:
-        cs, ss = _seq_view_shapes(shape, seq, cu_seqlens)
+    seq_view = MX_VIEW_SEQ_TOKEN if views & MX_VIEW_SEQ_TOKEN else MX_VIEW_SEQ
+    if views & (MX_VIEW_SEQ | MX_VIEW_SEQ_TOKEN):
+        cs, ss = _seq_view_shapes(shape, seq, cu_seqlens, seq_view == MX_VIEW_SEQ_TOKEN)
         seqv = QView(torch.empty(cs, dtype=torch.uint8, device=x.device),
                      torch.empty(ss, dtype=torch.uint8, device=x.device))
         sv = _qv(seqv)
-    for v, view, what in ((row, row_view, "row view"), (seqv, MX_VIEW_SEQ, "seq view")):
+    for v, view, what in ((row, row_view, "row view"), (seqv, seq_view, "seq view")):
         if v is not None:
             _check_view(lib, v, seq, heads, d, view, what)
     st = getattr(lib, name)(ctypes.byref(seq), heads, d, x.data_ptr(), _dtype_code(x.dtype), views, ctypes.byref(rv),
@@ -362,7 +370,7 @@ def _key_seq(k_shape, cross):
     return _seq(k_shape, cu_k, max_k)
 
 
-def _fwd(name, q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen, cross=None):
+def _fwd(name, q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen, cross=None, v_tok=None):
     lib = load()
     qs, ks = _elem_shape(q_row), _elem_shape(k_row)
     fmt = _score_format(q_row, k_row)
@@ -375,9 +383,14 @@ def _fwd(name, q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens
     _check_view(lib, q_row, seq, desc.heads_q, desc.head_dim, row_view, "q_row")
     _check_view(lib, k_row, kseq, desc.heads_kv, desc.head_dim, row_view, "k_row")
     _check_view(lib, v_seq, kseq, desc.heads_kv, desc.head_dim, MX_VIEW_SEQ, "v_seq")
+    if v_tok is not None:
+        _check_view(lib, v_tok, kseq, desc.heads_kv, desc.head_dim, MX_VIEW_SEQ_TOKEN, "v_tok")
     o = torch.empty(qs, dtype=out_dtype, device=dev)
     lse = torch.empty(qs[:-1], dtype=torch.float32, device=dev)
-    if seq_k is None:
+    if v_tok is not None:
+        st = lib.mx_attn_fwd_strict(ctypes.byref(desc), _qv(q_row), _qv(k_row), _qv(v_seq), _qv(v_tok), o.data_ptr(),
+                                    lse.data_ptr(), _stream())
+    elif seq_k is None:
         st = getattr(lib, name)(ctypes.byref(desc), _qv(q_row), _qv(k_row), _qv(v_seq), o.data_ptr(),
                                 lse.data_ptr(), _stream())
     else:
@@ -398,6 +411,15 @@ def mx_attn_fwd(q_row, k_row, v_seq, causal=True, softmax_scale=0.0, out_dtype=t
 def mx_attn_varlen_fwd(q_row, k_row, v_seq, cu_seqlens, max_seqlen=None, causal=True, softmax_scale=0.0,
                        out_dtype=torch.bfloat16):
     return _fwd("mx_attn_varlen_fwd", q_row, k_row, v_seq, causal, softmax_scale, out_dtype, cu_seqlens, max_seqlen)
+
+
+def mx_attn_fwd_strict(q_row, k_row, v_seq, v_tok, softmax_scale=0.0, out_dtype=torch.bfloat16, cu_seqlens=None,
+                       max_seqlen=None):
+    """Causal forward with the strict per-key V fold on the diagonal tiles -> (o, lse). v_seq:
+    the SEQ view of V, v_tok: its SEQ_TOKEN view (mx_quantize(v, MX_VIEW_SEQ_TOKEN)); batched,
+    or packed with cu_seqlens."""
+    return _fwd("mx_attn_fwd_strict", q_row, k_row, v_seq, True, softmax_scale, out_dtype, cu_seqlens, max_seqlen,
+                v_tok=v_tok)
 
 
 def mx_attn_workspace_size(q_shape, cu_seqlens=None, max_seqlen=None, heads_kv=None, dq_mode=MX_DQ_F32,

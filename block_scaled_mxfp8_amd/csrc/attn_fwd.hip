@@ -41,6 +41,16 @@
 //    16 bytes per lane, lane half h holding contraction indices 32h .. 32h + 31 in order (two
 //    codes per byte, low nibble first; the instruction reads 4 registers), so a K ROW tile row
 //    is d/2 bytes and each product reads one 16-byte chunk per lane.
+//  * Strict per-key V fold (kStrict, causal; FLAMIA notes, section 4, the strict option: move the
+//    scale to the probability side on the diagonal tiles): a workgroup's diagonal tiles are the
+//    keys of its own 128 queries. There V comes from a per-token view (one exponent e_j per key
+//    over all channels, the SEQ code layout) whose scale enters the MFMA as 1, and the key's 2^e_j
+//    is folded into its probability: the P codes are those of P' = P 2^e_j in the same groups of
+//    32 keys, so no scale that a query's output uses depends on a later key. The group exponent
+//    is the E8M0 rule on max P' taken exactly: with R = max_j (e_j + exponent of p_j) over the
+//    group's nonzero p, P' / 2^R = p_j 2^(e_j - R) lies in (0, 1) and is exact, and the codes
+//    are those of P' / 2^e = (P' / 2^R) / 2^(e - R). l still sums the unfolded p. The 128 token
+//    exponent bytes of the diagonal keys are loaded into LDS with the first K tiles.
 #include "mx_device.h"
 #include "mx_internal.h"
 #include "mx_layout.h"
@@ -69,6 +79,8 @@ constexpr float kTau = 8.f;           // largest lag of the reference max behind
 //      are swapped when (ch >> 3) & 1 (half_swz), for the same reason.
 //  ks: K ROW scales, one dword per key (its d/32 bytes; at d = 64 the upper half is unused);
 //  vs: V SEQ scales [2 groups][d].
+//  vt: (kStrict) exponent bytes of the per-token V scales of the workgroup's diagonal keys
+//      q0 .. q0 + 127, in key order.
 // K and V tiles have two slots each: K(j) sits in slot j % 2 and is loaded during tile j - 2
 // (its scores are computed during tile j - 1), V(j) in slot j % 2, loaded during tile j (P V
 // of tile j runs during tile j + 1).
@@ -78,6 +90,7 @@ struct FwdSmem {
   alignas(16) uint8_t v[2][2 * D * 32];
   alignas(16) uint32_t ks[2][kBlockN];
   alignas(16) uint8_t vs[2][2 * D];
+  alignas(16) uint8_t vt[kBlockM];
 };
 
 // Work decode: which (sequence, head, query tile) this workgroup computes.
@@ -167,6 +180,8 @@ struct KvBase {
   const uint8_t* ks;   // K ROW scales of key 0
   const uint8_t* v;    // V SEQ codes of group 0 (the groups of a sequence are consecutive rows)
   const uint8_t* vs;   // V SEQ scales of group 0
+  const uint8_t* vtc;  // (strict) per-token V view: codes of group 0 (SEQ code layout)
+  const uint8_t* vts;  // (strict) per-token V view: scale bytes of token 0
   int ts;              // token stride of K, in elements
   int tsb;             // token stride of the K codes, in bytes (ts, or ts / 2 for E2M1)
   int n;               // tokens
@@ -183,6 +198,8 @@ __device__ __forceinline__ KvBase kv_base(const AttnParams& p, const Work& w, in
   b.ks = p.k_scales + (k0 >> 5);
   b.v = p.v_codes + row0 * (D * 32);
   b.vs = p.v_scales + row0 * D;
+  b.vtc = p.vt_codes ? p.vt_codes + row0 * (D * 32) : nullptr;
+  b.vts = p.vt_scales ? p.vt_scales + row0 * 32 : nullptr;
   b.ts = (int)token_stride_k<kPacked>(p.heads_kv, D);
   b.tsb = kF4 ? b.ts >> 1 : b.ts;
   b.n = w.nk;
@@ -235,12 +252,14 @@ constexpr int kNj = D / 16 / kWaves;
 // last group) into `vt_lds` / `vs_lds`: kNj code instructions per wave (64 x 16 bytes of the
 // [group][channel][32] tile each: at d = 128 instruction jj of wave w covers group jj,
 // channels 32w.., at d = 64 group w / 2, channels 32(w % 2)..), and on wave 1 the scales (the
-// lane's dword of the two groups' [2][d] bytes; vsl = 4 lane for lanes < d/2).
+// lane's dword of the two groups' [2][d] bytes; vsl = 4 lane for lanes < d/2). tok: the codes
+// of the per-token view instead (a diagonal tile of the strict fold; its V scale is 1 and no
+// scale bytes are loaded).
 template <int D>
 __device__ __forceinline__ void issue_v(const KvBase& b, int kt, int wave, uint8_t* vt_lds, uint8_t* vs_lds,
-                                        uint32_t vl, uint32_t vsl) {
+                                        uint32_t vl, uint32_t vsl, bool tok = false) {
   const bool two = 2 * kt + 1 <= ((b.n + 31) >> 5) - 1;   // the tile's second group exists
-  const uint8_t* g0 = b.v + (long long)(2 * kt) * (D * 32);
+  const uint8_t* g0 = (tok ? b.vtc : b.v) + (long long)(2 * kt) * (D * 32);
   const uint8_t* g1 = two ? g0 + D * 32 : g0;
 #pragma unroll
   for (int jj = 0; jj < kNj<D>; jj++) {
@@ -249,7 +268,7 @@ __device__ __forceinline__ void issue_v(const KvBase& b, int kt, int wave, uint8
     const int cw = D == 128 ? wave : (wave & 1);           // 32-channel block (x 1024 bytes)
     lds_dma_so(gb + cw * 1024, vl, vt_lds + j * 1024, 16);
   }
-  if (wave == 1 && (threadIdx.x & 63) < D / 2)
+  if (!tok && wave == 1 && (threadIdx.x & 63) < D / 2)
     lds_dma_so(b.vs + (long long)(2 * kt) * D, two ? vsl : vsl % D, vs_lds, 4);
 }
 
@@ -325,9 +344,10 @@ __device__ __forceinline__ float vsum16(const v16f& x) {
 
 // O^T += V^T P^T for the V tile in slot st: channels are MFMA rows, the wave's 32 queries
 // columns, the 64 keys of the tile the contraction (pop: the lane's 32 P codes, psc: their
-// E8M0 byte).
+// E8M0 byte). tok: the tile holds per-token codes whose scales are folded into P (V scale 1).
 template <int D>
-__device__ __forceinline__ void pv(const FwdSmem<D>& sm, int st, const v8i& pop, int psc, v16f* oacc) {
+__device__ __forceinline__ void pv(const FwdSmem<D>& sm, int st, const v8i& pop, int psc, v16f* oacc,
+                                   bool tok = false) {
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5, l32 = lane & 31;
 #pragma unroll
@@ -335,7 +355,7 @@ __device__ __forceinline__ void pv(const FwdSmem<D>& sm, int st, const v8i& pop,
     const int ch = t * 32 + l32;
     const v4i a = *reinterpret_cast<const v4i*>(&sm.v[st][(0 * D + ch) * 32 + (half_swz(ch, hh) << 4)]);
     const v4i b = *reinterpret_cast<const v4i*>(&sm.v[st][(1 * D + ch) * 32 + (half_swz(ch, hh) << 4)]);
-    const int vsc = sm.vs[st][hh * D + ch];
+    const int vsc = tok ? 127 : sm.vs[st][hh * D + ch];
     oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(a, b), pop, oacc[t], 0, 0, 0, vsc, 0, psc);
   }
 }
@@ -388,6 +408,80 @@ __device__ __forceinline__ float softmax_tile(v16f (&cur)[2], float c_rt, int li
     pop[4 + j] = (int)pack4_e4m3_scaled(cur[1][4 * j], cur[1][4 * j + 1], cur[1][4 * j + 2], cur[1][4 * j + 3], s1);
   }
   psc = ((threadIdx.x & 32) ? i1 : i0) + 127;
+  return f;
+}
+
+// The P codes of one 32-key group of a diagonal tile under the strict fold: the codes of
+// P'_j = p_j 2^e_j (x: the lane's 16 p of the group, eb: their keys' token scale bytes, four
+// per dword in key order). Returns the group's E8M0 exponent e, the E8M0 rule on max P'
+// (amax 0 -> -127; clamped to [-127, 127]).
+//  * R = max (e_j + frexp exponent of p_j) over the group's nonzero p (both lane halves), so
+//    y_j = p_j 2^(e_j - R) < 1 and the largest is >= 1/2: exact, no overflow; a y_j that leaves
+//    the normal range is below 2^-125 of the group maximum, so its code is 0 either way.
+//  * e = R + rule(max y) (the rule commutes with powers of two), codes RNE(y_j / 2^(e - R)).
+__device__ __forceinline__ int fold_group(v16f& x, uint32_t (&eb)[4], v8i& pop, int half) {
+  // (the exponents are re-read from eb in each pass -- the empty asm keeps the compiler from
+  // holding the 16 values of the first pass -- and y overwrites x: no extra arrays live)
+  auto ej = [&](int i) __attribute__((always_inline)) { return (int)((eb[i >> 2] >> (8 * (i & 3))) & 0xFFu) - 127; };
+  int R = -(1 << 20);
+#pragma unroll
+  for (int i = 0; i < 16; i++)
+    if (x[i] > 0.f) R = max(R, ej(i) + __builtin_amdgcn_frexp_expf(x[i]));
+  R = max(R, __float_as_int(swap32(__int_as_float(R))));
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int b = 0; b < 4; b++) asm volatile("" : "+v"(eb[b]));
+#endif
+  float ym = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    x[i] = __builtin_ldexpf(x[i], max(ej(i) - R, -160));   // p = 0 stays 0; R may be -2^20
+    ym = fmaxf(ym, x[i]);
+  }
+  ym = fmaxf(ym, swap32(ym));
+  int e = kExpMin;
+  float sc = 1.f;
+  if (ym > 0.f) {
+    e = min(max(R + scale_exp_from_bits(__float_as_uint(ym)), kExpMin), kExpMax);
+    sc = exp2_scale(e - R);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+    pop[4 * half + j] = (int)pack4_e4m3_scaled(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3], sc);
+  return e;
+}
+
+// Online softmax of a diagonal tile under the strict fold: softmax_tile<true, ...> with the P
+// codes of P' = P 2^e_j (fold_group); vt: the tile's 64 token scale bytes in key order.
+template <bool kLit, int D>
+__device__ __forceinline__ float softmax_tile_fold(v16f (&cur)[2], float c_rt, int lim, const uint8_t* vt, float& M,
+                                                   float& lsum, v8i& pop, int& psc) {
+  const float c = kLit ? default_c<D>() : c_rt;
+  mask_tile<0>(cur[0], lim, std::make_integer_sequence<int, 16>{});
+  mask_tile<32>(cur[1], lim, std::make_integer_sequence<int, 16>{});
+  const float gm0 = max_halves(max16_raw(cur[0])), gm1 = max_halves(max16_raw(cur[1]));
+  const float mt = ceilf(fmaxf(gm0, gm1) * c);
+  const bool up = mt > M + kTau;
+  const float f = up ? __builtin_amdgcn_exp2f(M - mt) : 1.f;
+  M = up ? mt : M;
+  const float nm = M > -INFINITY ? -M : 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    cur[0][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[0][i], c, nm));
+    cur[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[1][i], c, nm));
+  }
+  lsum = __builtin_fmaf(lsum, f, vsum16(cur[0]) + vsum16(cur[1]));
+  // value i of half tile T is key T*32 + 8(i >> 2) + 4hh + (i & 3): bytes 4hh.. of dword 2(i>>2)
+  const int hh = (threadIdx.x >> 5) & 1;
+  int eg[2];
+#pragma unroll
+  for (int T = 0; T < 2; T++) {
+    uint32_t eb[4];
+#pragma unroll
+    for (int b4 = 0; b4 < 4; b4++) eb[b4] = *reinterpret_cast<const uint32_t*>(vt + T * 32 + 8 * b4 + 4 * hh);
+    eg[T] = fold_group(cur[T], eb, pop, T);
+  }
+  psc = (hh ? eg[1] : eg[0]) + 127;
   return f;
 }
 
@@ -524,7 +618,7 @@ __device__ __forceinline__ void pin_tile_results(const v8i& pcur, int psc, float
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool kPacked, bool kLit, bool kF4>
+template <int D, bool kPacked, bool kLit, bool kF4, bool kStrict>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   __shared__ FwdSmem<D> sm;
   const Work w = decode_work<kPacked>(p, reinterpret_cast<int*>(&sm));
@@ -549,6 +643,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   const KvBase kvb = kv_base<D, kPacked, kF4>(p, w, hkv);
   if (nkt > 0) issue_k<D, kF4>(kvb, 0, wave, sm.k[0], sm.ks[0], kl, ksl);
   if (nkt > 1) issue_k<D, kF4>(kvb, 1, wave, sm.k[1], sm.ks[1], kl, ksl);
+  if (kStrict && nkt > 0 && wave == 2 && lane < kBlockM / 4) {
+    // token scale bytes of the diagonal keys q0 .. q0 + 127 (groups q0/32 + lane/8, clamped to
+    // the sequence's last group: keys past its end are masked)
+    const int grp = min(q0 / 32 + lane / 8, ((w.nk + 31) >> 5) - 1);
+    lds_dma(kvb.vts + grp * 32 + 4 * (lane & 7), sm.vt, 4);
+  }
 
   // ---- Q operand (B of S^T = K Q^T), kept in registers ----
   constexpr int NS = D / 64;  // contraction steps of 64 over d
@@ -604,18 +704,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   // tile is visible when it is below vis_end. The tiles every lane sees whole come first (a
   // causal row block's keys end at its diagonal, a sequence's at its ragged tail), so the two
   // kinds run as two loops, each a straight-line block per tile.
+  // tiles [0, jw) are seen whole by every lane of the workgroup
+  const int jw = min(nkt, p.causal ? (q0 + 1) / kBlockN : w.nk / kBlockN);
   auto tile = [&](auto par, auto masked, int j, v16f(&cur)[2], v16f(&nxt)[2], const v8i& pprev, int pscprev,
                   v8i& pcur, int& psccur) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
     constexpr bool kMask = decltype(masked)::value;
     if (j + 2 < nkt) issue_k<D, kF4>(kvb, j + 2, wave, sm.k[P], sm.ks[P], kl, ksl);
-    issue_v<D>(kvb, j, wave, sm.v[P], sm.vs[P], vl, vsl);
+    // under the strict fold the masked tiles are exactly the diagonal ones (causal: j >= jw)
+    issue_v<D>(kvb, j, wave, sm.v[P], sm.vs[P], vl, vsl, kStrict && kMask);
     float f;
     if (kMask) {
-      pv<D>(sm, P ^ 1, pprev, pscprev, oacc);
+      pv<D>(sm, P ^ 1, pprev, pscprev, oacc, kStrict && j - 1 >= jw);
       scores<D, kF4>(sm, P ^ 1, qop, qsc, nxt);
-      f = softmax_tile<true, kLit, D>(cur, c, vis_end - j * kBlockN - 4 * hh, M, lsum, pcur, psccur);
-      interleave_tile();
+      if (kStrict) {
+        f = softmax_tile_fold<kLit, D>(cur, c, vis_end - j * kBlockN - 4 * hh, sm.vt + (j - jw) * kBlockN, M, lsum,
+                                       pcur, psccur);
+      } else {
+        f = softmax_tile<true, kLit, D>(cur, c, vis_end - j * kBlockN - 4 * hh, M, lsum, pcur, psccur);
+        interleave_tile();
+      }
     } else {
       f = whole_tile<D, kLit, kF4>(sm, P ^ 1, P ^ 1, qop, qsc, cur, nxt, pprev, pscprev, oacc, c, M, lsum, pcur,
                                    psccur);
@@ -635,8 +743,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
   using Odd = std::integral_constant<int, 1>;
   using Whole = std::false_type;
   using Masked = std::true_type;
-  // tiles [0, jw) are seen whole by every lane of the workgroup
-  const int jw = min(nkt, p.causal ? (q0 + 1) / kBlockN : w.nk / kBlockN);
   int j = 0;
   // two tiles per iteration, so slots, score registers and code registers alternate without copies
   for (; j + 1 < jw; j += 2) {
@@ -655,9 +761,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
     tile(Even{}, Masked{}, j, sa, sb, pb, psb, pa, psa);
     if (j + 1 < nkt) tile(Odd{}, Masked{}, j + 1, sb, sa, pa, psa, pb, psb);
   }
-  // P V of the last tile
-  if (nkt & 1) pv<D>(sm, 0, pa, psa, oacc);
-  else if (nkt > 0) pv<D>(sm, 1, pb, psb, oacc);
+  // P V of the last tile (a diagonal one under the strict fold)
+  if (nkt & 1) pv<D>(sm, 0, pa, psa, oacc, kStrict);
+  else if (nkt > 0) pv<D>(sm, 1, pb, psb, oacc, kStrict);
 
   // ---- epilogue: O = a / l, LSE = (M + log2 l) ln 2 ----
   const float l = lsum + swap32(lsum);
@@ -705,15 +811,20 @@ hipError_t launch_attn_fwd(const AttnParams& p, hipStream_t stream) {
   const bool lit = p.head_dim == 128 ? p.scale * kLog2e == default_c<128>() && p.scale == 0.08838834764831845f
                                      : p.scale == 0.125f;
   const int slot = profile_begin(kProfFwd, stream);
-#define MX_FWD_LAUNCH(DD, PK)                                                                            \
-  do {                                                                                                   \
-    if (p.score_fp4) {                                                                                   \
-      if (lit) hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, true, true>), grid, dim3(256), 0, stream, p); \
-      else hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, false, true>), grid, dim3(256), 0, stream, p);    \
-    } else {                                                                                             \
-      if (lit) hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, true, false>), grid, dim3(256), 0, stream, p);\
-      else hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, false, false>), grid, dim3(256), 0, stream, p);   \
-    }                                                                                                    \
+  // the strict fold (causal, E4M3 scores only; checked by the caller) has its own instances
+  const bool strict = p.vt_codes != nullptr;
+#define MX_FWD_LAUNCH(DD, PK)                                                                                   \
+  do {                                                                                                          \
+    if (strict) {                                                                                               \
+      if (lit) hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, true, false, true>), grid, dim3(256), 0, stream, p); \
+      else hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, false, false, true>), grid, dim3(256), 0, stream, p);    \
+    } else if (p.score_fp4) {                                                                                   \
+      if (lit) hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, true, true, false>), grid, dim3(256), 0, stream, p); \
+      else hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, false, true, false>), grid, dim3(256), 0, stream, p);    \
+    } else {                                                                                                    \
+      if (lit) hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, true, false, false>), grid, dim3(256), 0, stream, p);\
+      else hipLaunchKernelGGL((attn_fwd_kernel<DD, PK, false, false, false>), grid, dim3(256), 0, stream, p);   \
+    }                                                                                                           \
   } while (0)
   if (packed(g)) {
     if (p.head_dim == 128) MX_FWD_LAUNCH(128, true);

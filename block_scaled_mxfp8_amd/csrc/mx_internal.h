@@ -19,6 +19,8 @@ struct QuantizeParams {
   bool row_fp4;          // the ROW view in MXFP4 (E2M1 codes, two per byte) instead of E4M3
   uint8_t* seq_codes;    // nullptr: SEQ view not wanted
   uint8_t* seq_scales;
+  bool seq_token;        // the SEQ codes with one exponent per token (all channels); seq_scales
+                         // then holds one byte per token, [group row][32]
   // backward preprocessing (all nullptr for a plain quantise): with `o` set, the kernel also
   // writes ndelta[token, head] = -sum_c dequant(ROW code) * O (that is -D) and
   // lse2[token, head] = lse * log2 e, the forms the backward kernels consume.
@@ -43,6 +45,9 @@ struct AttnParams {
   const uint8_t* q_codes; const uint8_t* q_scales;    // ROW view of Q
   const uint8_t* k_codes; const uint8_t* k_scales;    // ROW view of K
   const uint8_t* v_codes; const uint8_t* v_scales;    // SEQ view of V
+  // strict per-key V fold (causal): the per-token view of V (SEQ code layout, one scale byte per
+  // token); nullptr: the plain forward
+  const uint8_t* vt_codes; const uint8_t* vt_scales;
   void* o;
   float* lse;
 };

@@ -131,7 +131,7 @@ mx_status key_geom(const mx_attn_desc* d, const mx::Geom& g, const mx_seq* seq_k
 }
 
 mx_status fwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview k_row, mx_qview v_seq,
-                   void* o, float* lse, void* stream, bool need_packed) {
+                   void* o, float* lse, void* stream, bool need_packed, const mx_qview* v_tok = nullptr) {
   mx::Geom g, gk;
   mx_status st = check_desc(desc, &g);
   if (st != MX_OK) return st;
@@ -140,6 +140,11 @@ mx_status fwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
   if ((st = check_view(q_row)) != MX_OK || (st = check_view(k_row)) != MX_OK || (st = check_view(v_seq)) != MX_OK)
     return st;
   if (!o || !lse || !aligned(o, 16) || !aligned(lse, 4)) return MX_E_ARG;
+  if (v_tok) {   // the strict per-key V fold: causal self-attention with E4M3 scores
+    if ((st = check_view(*v_tok)) != MX_OK) return st;
+    if (!desc->causal || seq_k) return MX_E_ARG;
+    if (score_fp4(desc)) return MX_E_UNSUPPORTED;
+  }
   mx::AttnParams p = {};
   p.geom = g;
   p.geom_k = gk;
@@ -154,6 +159,10 @@ mx_status fwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
   p.q_codes = q_row.codes; p.q_scales = q_row.scales;
   p.k_codes = k_row.codes; p.k_scales = k_row.scales;
   p.v_codes = v_seq.codes; p.v_scales = v_seq.scales;
+  if (v_tok) {
+    p.vt_codes = v_tok->codes;
+    p.vt_scales = v_tok->scales;
+  }
   p.o = o;
   p.lse = lse;
   if (g.total == 0) return MX_OK;
@@ -274,10 +283,11 @@ static mx_status quantize_impl(const mx_seq* seq, int32_t heads, int32_t head_di
   mx::Geom g;
   if (!make_geom(seq, &g) || heads < 1 || !x) return MX_E_ARG;
   if (dtype != MX_F32 && dtype != MX_BF16) return MX_E_ARG;
-  if (views < 1 || views > (MX_VIEW_SEQ | MX_VIEW_ROW_FP4)) return MX_E_ARG;
-  if ((views & MX_VIEW_ROW) && (views & MX_VIEW_ROW_FP4)) return MX_E_ARG;   // one row_out
+  if (views < 1 || views > (MX_VIEW_SEQ | MX_VIEW_ROW_FP4 | MX_VIEW_SEQ_TOKEN)) return MX_E_ARG;
+  if ((views & MX_VIEW_ROW) && (views & MX_VIEW_ROW_FP4)) return MX_E_ARG;        // one row_out
+  if ((views & MX_VIEW_SEQ) && (views & MX_VIEW_SEQ_TOKEN)) return MX_E_ARG;      // one seq_out
   if (!valid_dim(head_dim)) return MX_E_UNSUPPORTED;
-  if (token_block && (views & MX_VIEW_ROW_FP4)) return MX_E_UNSUPPORTED;
+  if (token_block && (views & (MX_VIEW_ROW_FP4 | MX_VIEW_SEQ_TOKEN))) return MX_E_UNSUPPORTED;
   if (!aligned(x, 16)) return MX_E_ARG;
   mx::QuantizeParams p = {};
   p.geom = g;
@@ -292,10 +302,11 @@ static mx_status quantize_impl(const mx_seq* seq, int32_t heads, int32_t head_di
     p.row_scales = row_out->scales;
     p.row_fp4 = (views & MX_VIEW_ROW_FP4) != 0;
   }
-  if (views & MX_VIEW_SEQ) {
+  if (views & (MX_VIEW_SEQ | MX_VIEW_SEQ_TOKEN)) {
     if (!seq_out || check_view(*seq_out) != MX_OK) return MX_E_ARG;
     p.seq_codes = seq_out->codes;
     p.seq_scales = seq_out->scales;
+    p.seq_token = (views & MX_VIEW_SEQ_TOKEN) != 0;
   }
   if (g.total == 0) return MX_OK;
   const int slot = mx::profile_begin(mx::kProfQuantize, (hipStream_t)stream);
@@ -390,6 +401,11 @@ mx_status mx_attn_varlen_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
   return fwd_impl(desc, nullptr, q_row, k_row, v_seq, o, lse, stream, true);
 }
 
+mx_status mx_attn_fwd_strict(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq,
+                             mx_qview v_tok, void* o, float* lse, void* stream) {
+  return fwd_impl(desc, nullptr, q_row, k_row, v_seq, o, lse, stream, false, &v_tok);
+}
+
 mx_status mx_attn_cross_fwd(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview k_row,
                             mx_qview v_seq, void* o, float* lse, void* stream) {
   if (!seq_k) return MX_E_ARG;
@@ -465,11 +481,13 @@ size_t mx_view_codes_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, i
   if (view == MX_VIEW_ROW) return row_codes_bytes(g, heads, head_dim);
   if (view == MX_VIEW_SEQ) return seq_codes_bytes(g, heads, head_dim);
   if (view == MX_VIEW_ROW_FP4) return row_codes_bytes(g, heads, head_dim) / 2;
+  if (view == MX_VIEW_SEQ_TOKEN) return seq_codes_bytes(g, heads, head_dim);
   return 0;
 }
 
 size_t mx_view_scales_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view) {
-  // one scale byte per 32 elements in every view
+  // one scale byte per 32 elements in every view but the per-token one (one per token slot)
+  if (view == MX_VIEW_SEQ_TOKEN) return valid_dim(head_dim) ? mx_view_codes_bytes(seq, heads, head_dim, view) / head_dim : 0;
   const int32_t elem_view = view == MX_VIEW_ROW_FP4 ? MX_VIEW_ROW : view;
   return mx_view_codes_bytes(seq, heads, head_dim, elem_view) / 32;
 }

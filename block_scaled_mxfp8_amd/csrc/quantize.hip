@@ -14,6 +14,12 @@
 // MXFP4 ROW view (row_fp4; FLAMIA notes, sections 2 and 3, the 4-bit score operands of the mixed
 // route): the same ROW groups with E2M1 codes, two per byte, written instead of the E4M3 ones.
 //
+// Per-token SEQ view (seq_token; FLAMIA notes, section 4, the strict option's per-key scale on
+// the diagonal tiles): the SEQ code layout with one exponent per token over all d channels, so a
+// code depends on its own token only; the token's maximum comes from its TPT threads (lane
+// exchanges), and the transpose reads each of its tokens' exponents from LDS. One scale byte
+// per token, [group row][32] in token order; the padding tokens of a partial group get byte 0.
+//
 // Token-block scales (kBlock; FLAMIA notes, section 3): the workgroup's tile IS one token
 // block (32 consecutive tokens of a sequence or document x all d channels of a head), so its
 // single exponent comes from a workgroup max-abs (a wave max, then the waves' maxima through
@@ -195,11 +201,51 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
 
   // ---- SEQ view: 32 tokens of one channel, through LDS ----
   __shared__ float tile[kGroup][D + 1];
+  __shared__ uint32_t tok_am[kGroup];   // seq_token: the token's largest magnitude bits
 #pragma unroll
   for (int i = 0; i < 16; i++) tile[tk][cb * 16 + i] = v[i];
+  if (!kBlock && p.seq_token) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) am = max(am, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+#pragma unroll
+    for (int m = 1; m < TPT; m <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, m));
+    if (cb == 0) tok_am[tk] = am;
+  }
   __syncthreads();
   const int c = tid >> 1;   // channel (2 threads per channel, 16 tokens each)
   const int hf = tid & 1;   // token half
+  const long long grow = seq_group_row(g, p.heads, s, h, doc_start, grp);
+  uint8_t* dst = p.seq_codes + (grow * D + c) * kGroup;
+  if (!kBlock && p.seq_token) {
+    // token t of the thread's runs: A holds tokens 16hf + {0..3, 8..11}, B 16hf + {4..7, 12..15}
+    uint32_t w[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int t = 16 * hf + 8 * (r & 1) + 4 * (r >> 1) + i;
+        const uint32_t am = tok_am[t];
+        const float val = tile[t][c];
+        x[i] = am >= kInfBits ? 0.f : ldexpf(val, -scale_exp_from_bits(am));
+      }
+      w[r] = pack4_e4m3(x[0], x[1], x[2], x[3]);
+      // every code of a non-finite token is 0x7F
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int t = 16 * hf + 8 * (r & 1) + 4 * (r >> 1) + i;
+        if (tok_am[t] >= kInfBits) w[r] = (w[r] & ~(0xFFu << (8 * i))) | (0x7Fu << (8 * i));
+      }
+    }
+    *reinterpret_cast<v2i*>(dst + 8 * hf) = v2i{(int)w[0], (int)w[1]};
+    *reinterpret_cast<v2i*>(dst + 16 + 8 * hf) = v2i{(int)w[2], (int)w[3]};
+    if (tid < kGroup) {
+      const uint32_t am = tok_am[tid];
+      p.seq_scales[grow * kGroup + tid] = am >= kInfBits ? 0xFF : (uint8_t)(scale_exp_from_bits(am) + 127);
+    }
+    return;
+  }
   // run A (bytes 8hf..8hf+7) holds tokens 16hf + {0..3, 8..11}; run B (bytes 16+8hf..) tokens 16hf + {4..7, 12..15}
   float a[8], b[8];
 #pragma unroll
@@ -229,8 +275,6 @@ __global__ __launch_bounds__(2 * D) void quantize_kernel(QuantizeParams p) {
     wb1 = pack4_e4m3(ldexpf(b[4], -e), ldexpf(b[5], -e), ldexpf(b[6], -e), ldexpf(b[7], -e));
     // padding tokens of a partial group are exact zeros -> code 0
   }
-  const long long grow = seq_group_row(g, p.heads, s, h, doc_start, grp);
-  uint8_t* dst = p.seq_codes + (grow * D + c) * kGroup;
   *reinterpret_cast<v2i*>(dst + 8 * hf) = v2i{(int)wa0, (int)wa1};
   *reinterpret_cast<v2i*>(dst + 16 + 8 * hf) = v2i{(int)wb0, (int)wb1};
   if (hf == 0) p.seq_scales[grow * D + c] = nonfinite ? 0xFF : (uint8_t)(e + 127);

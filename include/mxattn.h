@@ -49,6 +49,12 @@
  *                 the ROW groups with E2M1 codes (sign | 2-bit exponent, bias 1 | 1-bit
  *                 mantissa: 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte, channel 2i in the low
  *                 nibble of byte i: codes [B,H,L,d/2] / [T,H,d/2]; scales as the ROW view.
+ *       SEQ_TOKEN view (per-token scales, the V operand of the strict fold; FLAMIA notes,
+ *                 section 4, the strict option's per-key scale on the diagonal tiles): codes in
+ *                 the SEQ layout above, but each token has ONE exponent for all d channels (the
+ *                 smallest e with max_c |x_tc| * 2^-e <= 448); scales: one byte per token slot,
+ *                 [B, H, G, 32] / [H, Gc, 32] in token order (the group rows of the SEQ view;
+ *                 padding tokens hold byte 0 and codes 0).
  */
 #ifndef MXATTN_H
 #define MXATTN_H
@@ -74,7 +80,7 @@ typedef enum {
 
 typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
 
-enum { MX_VIEW_ROW = 1, MX_VIEW_SEQ = 2, MX_VIEW_ROW_FP4 = 4 };
+enum { MX_VIEW_ROW = 1, MX_VIEW_SEQ = 2, MX_VIEW_ROW_FP4 = 4, MX_VIEW_SEQ_TOKEN = 8 };
 enum { MX_SCORE_MXFP8 = 0, MX_SCORE_MXFP4 = 1 };
 enum { MX_DQ_F32 = 0, MX_DQ_F16_BOOST = 1, MX_DQ_F16_PREFIX = 2 };
 
@@ -131,7 +137,10 @@ typedef struct {
  * views may hold MX_VIEW_ROW_FP4 in place of MX_VIEW_ROW (both: MX_E_ARG): row_out then
  * receives the ROW_FP4 view, with the group exponent the smallest e with amax * 2^-e <= 6 and
  * codes = E2M1 round-to-nearest-even of x * 2^-e (sign kept); a group holding a NaN or an
- * infinity gets scale 0xFF and codes 0x7. Head dims 64 and 128, as for the other views. */
+ * infinity gets scale 0xFF and codes 0x7. Head dims 64 and 128, as for the other views.
+ * views may hold MX_VIEW_SEQ_TOKEN in place of MX_VIEW_SEQ (both: MX_E_ARG): seq_out then
+ * receives the SEQ_TOKEN view (one exponent per token; a token holding a NaN or an infinity
+ * gets scale 0xFF and codes 0x7F in every channel). */
 mx_status mx_quantize(const mx_seq* seq, int32_t heads, int32_t head_dim, const void* x, mx_dtype dtype,
                       int32_t views, mx_qview* row_out, mx_qview* seq_out, void* stream);
 
@@ -195,6 +204,21 @@ mx_status mx_gemm_quantize(mx_qview a_row, mx_qview b_row, int64_t m, int32_t n,
  * of V. */
 mx_status mx_attn_fwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq, void* o,
                       float* lse, void* stream);
+
+/* Forward with the strict per-key V fold (FLAMIA notes, section 4, the strict option: on the
+ * diagonal tiles the V scale moves to the probability side, P_ij (s_j v_j) = (P_ij s_j) v_j, so
+ * that no scale an output row uses depends on a later key). Causal self-attention only
+ * (desc->causal = 0: MX_E_ARG), E4M3 scores (MX_SCORE_MXFP4: MX_E_UNSUPPORTED); batched or
+ * packed. For query i, the keys j < 128 floor(i / 128) (128: the query block, relative to the
+ * sequence or document start) are read through v_seq as in mx_attn_fwd; the keys
+ * 128 floor(i / 128) <= j <= i through v_tok, the SEQ_TOKEN view of the same V, whose exponent
+ * e_j is folded into P: the P codes of those keys are the MX codes of P_ij 2^e_j in the same
+ * groups of 32 keys (exponent: the group rule on max P_ij 2^e_j), and they multiply the key's
+ * codes with V scale 1. LSE and the normaliser sum the unfolded P. Other arguments, layouts and
+ * errors as mx_attn_fwd. Inputs must be finite (a non-finite V token makes the rows that fold it
+ * NaN); V tokens whose largest |v| reaches 2^126 may saturate P' codes. */
+mx_status mx_attn_fwd_strict(const mx_attn_desc* desc, mx_qview q_row, mx_qview k_row, mx_qview v_seq,
+                             mx_qview v_tok, void* o, float* lse, void* stream);
 
 /* Backward: given G = dL/dO (g_dtype), the saved O and LSE of the forward, and the views of
  * Q, K, V, writes dQ [like Q], dK and dV [like K] in out_dtype. G is quantised internally
@@ -303,7 +327,7 @@ size_t mx_attn_cross_workspace_size(const mx_attn_desc* desc, const mx_seq* seq_
 size_t mx_attn_workspace_size(const mx_attn_desc* desc, int32_t for_bwd);
 
 /* Byte sizes of the quantised views of a tensor with `heads` heads (codes, scales); view is
- * MX_VIEW_ROW, MX_VIEW_SEQ or MX_VIEW_ROW_FP4 (other values: 0). */
+ * MX_VIEW_ROW, MX_VIEW_SEQ, MX_VIEW_ROW_FP4 or MX_VIEW_SEQ_TOKEN (other values: 0). */
 size_t mx_view_codes_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view);
 size_t mx_view_scales_bytes(const mx_seq* seq, int32_t heads, int32_t head_dim, int32_t view);
 

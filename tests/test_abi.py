@@ -279,7 +279,7 @@ def test_token_block_quantize_validation(lib):
     assert f(ctypes.byref(s), 1, 128, FAKE, 7, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
     assert f(ctypes.byref(s), 1, 128, FAKE + 2, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
     assert f(ctypes.byref(s), 1, 96, FAKE, 1, 3, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_UNSUPPORTED
-    assert f(ctypes.byref(s), 1, 128, FAKE, 1, 8, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(s), 1, 128, FAKE, 1, 16, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
     # the MXFP4 ROW view has no token-block form
     assert f(ctypes.byref(s), 1, 128, FAKE, 1, 4, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_UNSUPPORTED
     assert f(ctypes.byref(s), 1, 128, FAKE, 1, 1, None, ctypes.byref(v), None) == _lib.MX_E_ARG
@@ -314,7 +314,7 @@ def test_mxfp4_view_and_score_format_validation(lib):
     q = lib.mx_quantize
     # ROW and ROW_FP4 both write row_out: asking for both is an argument error
     assert q(ctypes.byref(s), 1, 128, FAKE, 1, 1 | 4, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
-    assert q(ctypes.byref(s), 1, 128, FAKE, 1, 8, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    assert q(ctypes.byref(s), 1, 128, FAKE, 1, 16, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
     # no 4-bit token-block view
     assert lib.mx_quantize_token_block(ctypes.byref(s), 1, 128, FAKE, 1, 4, ctypes.byref(v), ctypes.byref(v),
                                        None) == _lib.MX_E_UNSUPPORTED
@@ -366,3 +366,26 @@ def test_prefix_boost_workspace_and_mode_validation(lib):
     bad = _desc(dq_mode=3)
     bad.workspace, bad.workspace_bytes = FAKE, 1 << 30
     assert lib.mx_attn_bwd(ctypes.byref(bad), v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None) == _lib.MX_E_ARG
+
+
+def test_strict_fold_view_and_entry_validation(lib):
+    s = _seq()
+    v = _lib._QView(FAKE, FAKE)
+    q = lib.mx_quantize
+    # SEQ and SEQ_TOKEN both write seq_out
+    assert q(ctypes.byref(s), 1, 128, FAKE, 1, 2 | 8, ctypes.byref(v), ctypes.byref(v), None) == _lib.MX_E_ARG
+    # no per-token view with token-block scales
+    assert lib.mx_quantize_token_block(ctypes.byref(s), 1, 128, FAKE, 1, 8, ctypes.byref(v), ctypes.byref(v),
+                                       None) == _lib.MX_E_UNSUPPORTED
+    # SEQ_TOKEN sizes: the SEQ codes, one scale byte per token slot of each group row
+    s2 = _seq(batch=2, seqlen=70)
+    assert lib.mx_view_codes_bytes(ctypes.byref(s2), 3, 128, 8) == 2 * 3 * 3 * 128 * 32
+    assert lib.mx_view_scales_bytes(ctypes.byref(s2), 3, 128, 8) == 2 * 3 * 3 * 32
+    assert lib.mx_view_scales_bytes(ctypes.byref(s2), 3, 96, 8) == 0
+    f = lib.mx_attn_fwd_strict
+    # causal self-attention with E4M3 scores only; the token view is checked like the others
+    assert f(ctypes.byref(_desc(causal=0)), v, v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(_desc(score_format=1)), v, v, v, v, FAKE, FAKE, None) == _lib.MX_E_UNSUPPORTED
+    assert f(ctypes.byref(_desc()), v, v, v, _lib._QView(0, FAKE), FAKE, FAKE, None) == _lib.MX_E_ARG
+    assert f(ctypes.byref(_desc()), v, v, v, _lib._QView(FAKE, FAKE + 1), FAKE, FAKE, None) == _lib.MX_E_ARG
+    assert f(None, v, v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
