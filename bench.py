@@ -22,6 +22,8 @@ the library records immediately around each launch of the named kernel, on its s
     python bench.py --workload g1  # fused MXFP8 GEMM + quantise producer, 16384 x 12288 x 4096
     python bench.py --score mxfp4  # the mixed route: Q and K scored as MXFP4 (E2M1), everything else
                                    # MXFP8 (any attention workload; default c3)
+    python bench.py --fwd strict   # the forward with the strict per-key V fold on the diagonal tiles
+                                   # (causal workloads; V also quantised to its per-token view)
 
 `roofline.traffic` is the roofline kernel's HBM bytes per launch from rocprofv3 counters
 (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for the 1 GiB copy of --pmc-run),
@@ -107,6 +109,8 @@ def parse():
                     help="(batch, head) pairs the CPU baseline times (0: all of them, the full tensor)")
     ap.add_argument("--score", choices=["mxfp8", "mxfp4"], default="mxfp8",
                     help="score operands of the attention workloads: MXFP8 (E4M3), or MXFP4 (E2M1; the mixed route)")
+    ap.add_argument("--fwd", choices=["plain", "strict"], default="plain",
+                    help="forward of the step: plain, or with the strict per-key V fold (causal only)")
     ap.add_argument("--workload", choices=["c3", "c4", "c5", "c5gqa", "x1", "n1", "g1"], default="c3",
                     help="c3: the headline causal self-attention step; c4: 128 packed documents; c5/c5gqa: "
                          "B1 H16 L16384 non-causal (MHA / 16 on 4 KV heads); x1: the jagged cross-attention "
@@ -168,10 +172,10 @@ def run_attention(args):
     import torch
 
     import synth
-    from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F32, MX_VIEW_ROW_FP4, MX_VIEW_SEQ, PROFILE_BWD_DKDV,
-                                        PROFILE_BWD_DQ, PROFILE_BWD_PREP, PROFILE_FWD, PROFILE_QUANTIZE, load,
-                                        mx_attn_bwd, mx_attn_fwd, mx_profile_kernel, mx_quantize,
-                                        mx_quantize_token_block)
+    from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F32, MX_VIEW_ROW_FP4, MX_VIEW_SEQ, MX_VIEW_SEQ_TOKEN,
+                                        PROFILE_BWD_DKDV, PROFILE_BWD_DQ, PROFILE_BWD_PREP, PROFILE_FWD,
+                                        PROFILE_QUANTIZE, load, mx_attn_bwd, mx_attn_fwd, mx_attn_fwd_strict,
+                                        mx_profile_kernel, mx_quantize, mx_quantize_token_block)
     from block_scaled_mxfp8_amd.flops import attn_flops, visible_pairs
 
     load()
@@ -209,15 +213,26 @@ def run_attention(args):
     ds_store = not args.recompute_dq
 
     fp4 = args.score == "mxfp4"
+    strict = args.fwd == "strict"
+    if strict and (fp4 or not causal):
+        sys.exit("--fwd strict needs a causal workload with MXFP8 scores")
     qk_views = (MX_VIEW_ROW_FP4 | MX_VIEW_SEQ) if fp4 else 3
+    v_tok = [None]
 
     def quant():
+        if strict:   # the per-token V view of the diagonal tiles: a second pass over V
+            v_tok[0] = mx_quantize(t["v"], views=MX_VIEW_SEQ_TOKEN, **kw)[1]
         return (mx_quantize(t["q"], views=qk_views, **kw), mx_quantize(t["k"], views=qk_views, **kw),
                 mx_quantize(t["v"], **kw))
 
+    def fwd(q_row, k_row, v_seq):
+        if strict:
+            return mx_attn_fwd_strict(q_row, k_row, v_seq, v_tok[0], **kw)
+        return mx_attn_fwd(q_row, k_row, v_seq, causal=causal, **kw)
+
     def step(mode=dq_mode):
         (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
-        o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=causal, **kw)
+        o, lse = fwd(q_row, k_row, v_seq)
         dq, dk, dv, w = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=causal,
                                     dq_mode=mode, workspace=ws.get(mode), ds_store=ds_store, **kw)
         ws[mode] = w
@@ -277,8 +292,9 @@ def run_attention(args):
         return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
-    o, lse = mx_attn_fwd(q_row, k_row, v_seq, causal=causal, **kw)
-    ms_fwd = kernel_ms(PROFILE_FWD, lambda: mx_attn_fwd(q_row, k_row, v_seq, causal=causal, **kw))
+    o, lse = fwd(q_row, k_row, v_seq)
+    ms_fwd = kernel_ms(PROFILE_FWD, lambda: fwd(q_row, k_row, v_seq))
+    ms_fwd_plain = kernel_ms(PROFILE_FWD, lambda: mx_attn_fwd(q_row, k_row, v_seq, causal=causal, **kw)) if strict else None
     ms_quant = kernel_ms(PROFILE_QUANTIZE, lambda: mx_quantize(t["q"], **kw), n=3 * args.profile_steps)
     ms_quant_tb = None
     if not packed and not fp4:   # the token-block variant of the quantiser (same bytes; one exponent per 32 tokens x d)
@@ -324,6 +340,8 @@ def run_attention(args):
     if fp4:
         metric = f"mixed MXFP4-score / MXFP8 attn fwd/bwd TFLOP/s (causal-adj) on {name}" + (
             " (B4 H32 L4096 d128)" if name == "c3" else "")
+    elif strict:
+        metric = f"MXFP8 attn fwd/bwd TFLOP/s (causal-adj) on {name}, forward with the strict per-key V fold"
     elif name == "c3":
         metric = "MXFP8 attn fwd/bwd TFLOP/s (causal-adj) at B4 H32 L4096 d128, % of peak"
     else:
@@ -342,8 +360,9 @@ def run_attention(args):
         "dtype": "mxfp4 scores + mxfp8" if fp4 else "mxfp8",
         "data": "synthetic",
         "config": dict({"workload": desc + ", bf16 N(0,1)-based synthetic inputs, step = quantise Q/K/V + fwd + bwd"
-                        + (" with Q and K scored as MXFP4" if fp4 else ""),
-                        "head_dim": d, "causal": causal, "dq": args.dq, "score": args.score,
+                        + (" with Q and K scored as MXFP4" if fp4 else "")
+                        + (", the forward with the strict per-key V fold (V also quantised per token)" if strict else ""),
+                        "head_dim": d, "causal": causal, "dq": args.dq, "score": args.score, "fwd": args.fwd,
                         "dq_pass": "rebuilds dS" if args.recompute_dq else "reads stored dS codes"}, **cfg_line),
         "timing": {"rounds": args.rounds, "steps_per_round": args.steps, "ms_per_step_rounds": [round(r, 4) for r in rounds],
                    "statistic": "median of rounds, wall clock, no measurement hook",
@@ -358,7 +377,9 @@ def run_attention(args):
         "peaks_tflops": {"step": round(pk_step, 1), "fwd": round(pk_fwd, 1), "bwd": round(pk_bwd, 1)},
         "quantize_gbs": round(quant_bytes / (ms_quant * 1e-3) / 1e9, 1),
         "quantize_token_block_gbs": None if ms_quant_tb is None else round(quant_bytes / (ms_quant_tb * 1e-3) / 1e9, 1),
-        "kernels_ms": {"attn_fwd": round(ms_fwd, 4), "attn_bwd_dkdv": round(bwd_f32["dkdv_ms"], 4),
+        "kernels_ms": {"attn_fwd": round(ms_fwd, 4),
+                       **({"attn_fwd_plain": round(ms_fwd_plain, 4)} if strict else {}),
+                       "attn_bwd_dkdv": round(bwd_f32["dkdv_ms"], 4),
                        "attn_bwd_dq_f32": round(bwd_f32["dq_ms"], 4), "attn_bwd_dq_f16": round(bwd_f16["dq_ms"], 4),
                        "bwd_prep": round(bwd_f32["prep_ms"], 4), "quantize_one_tensor": round(ms_quant, 4)},
         "flops": {"fwd": f_fwd, "bwd": f_bwd, "visible_pairs": pairs},
@@ -367,10 +388,10 @@ def run_attention(args):
         "roofline": {"kernel": f"attn_bwd_dkdv_kernel<{d}> (backward dK/dV)", "bound": "mfma",
                      "achieved": round(tflops(f_dkdv, ms_bwd_main), 2), "peak": round(pk_dkdv, 1),
                      "unit": "TFLOP/s", "frac": round(tflops(f_dkdv, ms_bwd_main) / pk_dkdv, 4),
-                     "traffic": recorded_traffic() if name == "c3" and not fp4 else None},
+                     "traffic": recorded_traffic() if name == "c3" and not fp4 and not strict else None},
         "env": environment(),
     }
-    if not args.no_cpu_baseline and name == "c3" and not fp4:
+    if not args.no_cpu_baseline and name == "c3" and not fp4 and not strict:
         line["cpu_baseline"] = cpu_baseline(t, args.cpu_heads)
     print(json.dumps(line), flush=True)
 

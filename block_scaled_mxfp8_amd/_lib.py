@@ -4,6 +4,7 @@ Torch supplies device memory (outputs are allocated here with torch.empty) and t
 HIP stream; the library does all the work. Nothing here falls back to another
 implementation: a missing library or a non-zero status raises.
 """
+import contextlib
 import ctypes
 import os
 from typing import NamedTuple
@@ -81,7 +82,40 @@ def load():
     path = lib_path()
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m block_scaled_mxfp8_amd.build`")
-    lib = ctypes.CDLL(path)
+    _LIB = _bind(ctypes.CDLL(path))
+    return _LIB
+
+
+_VARIANT_LIBS = {}
+
+
+def load_variant(name):
+    """A build of the same sources under another scheduler (build.VARIANTS; for tests), loaded
+    beside the library; raises if it was not built."""
+    from .build import VARIANTS
+    if name not in _VARIANT_LIBS:
+        path = os.path.join(HERE, VARIANTS[name][0])
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m block_scaled_mxfp8_amd.build "
+                               f"--variant {name}`")
+        _VARIANT_LIBS[name] = _bind(ctypes.CDLL(path))
+    return _VARIANT_LIBS[name]
+
+
+@contextlib.contextmanager
+def using(lib):
+    """Route the binding's calls to `lib` (a load_variant handle) inside the block."""
+    global _LIB
+    saved = load()
+    _LIB = lib
+    try:
+        yield lib
+    finally:
+        _LIB = saved
+
+
+def _bind(lib):
+    """Argument and result types of every entry point."""
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.mx_quantize.argtypes = [ctypes.POINTER(_Seq), I32, I32, P, I32, I32, ctypes.POINTER(_QView),
                                 ctypes.POINTER(_QView), P]
@@ -129,7 +163,6 @@ def load():
     lib.mx_profile_kernel.restype = I32
     lib.mx_abi_version.argtypes = []
     lib.mx_abi_version.restype = I32
-    _LIB = lib
     return lib
 
 

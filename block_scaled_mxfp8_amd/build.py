@@ -1,6 +1,6 @@
 """Build libmxattn.so in-tree with hipcc for gfx950.
 
-    python -m block_scaled_mxfp8_amd.build [--verbose]
+    python -m block_scaled_mxfp8_amd.build [--verbose] [--variant max-ilp]
 
 All HIP sources under csrc/ are compiled into one shared library next to this file. Packed
 FP32 instructions are disabled for the device code (-packed-fp32-ops); the host pass of
@@ -19,6 +19,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmxattn.so")
 
+# Builds of the same sources under another instruction scheduler, loaded only by tests: the
+# kernels' counted memory waits must not depend on the order a scheduler picks (LLVM's max-ilp
+# scheduler once hoisted the dQ-from-store kernel's dS loads above its K-tile LDS-DMA).
+VARIANTS = {"max-ilp": ("libmxattn_maxilp.so", ("-mllvm", "-amdgpu-sched-strategy=max-ilp"))}
+
 
 def hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -31,7 +36,7 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose=False, out=LIB, extra=()):
+def build(verbose=False, out=LIB, extra=(), info=True):
     tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
@@ -47,8 +52,15 @@ def build(verbose=False, out=LIB, extra=()):
     if verbose and msgs.strip():
         print(msgs)
     os.replace(tmp, out)
-    write_build_info(os.path.join(HERE, "build_info.json"))
+    if info:
+        write_build_info(os.path.join(HERE, "build_info.json"))
     return out
+
+
+def build_variant(name, verbose=False):
+    """Build one of VARIANTS next to the library (its own file; build_info.json is untouched)."""
+    fname, extra = VARIANTS[name]
+    return build(verbose, os.path.join(HERE, fname), extra, info=False)
 
 
 def write_build_info(path):
@@ -75,4 +87,7 @@ def write_build_info(path):
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    if "--variant" in sys.argv:
+        print(build_variant(sys.argv[sys.argv.index("--variant") + 1], verbose="--verbose" in sys.argv))
+    else:
+        print(build(verbose="--verbose" in sys.argv))
