@@ -98,7 +98,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--dq", choices=["f32", "f16"], default="f32", help="dQ accumulation of the timed step")
+    ap.add_argument("--dq", choices=["f32", "f16", "f16prefix"], default="f32",
+                    help="dQ accumulation of the timed step (f16prefix: FP16 sums with the per-row prefix boost; "
+                         "attention workloads without cross keys)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=10, help="launches averaged per kernel line")
     ap.add_argument("--pmc-run", action="store_true", help="one untimed step + a 1 GiB copy (counter collection)")
@@ -172,7 +174,8 @@ def run_attention(args):
     import torch
 
     import synth
-    from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F32, MX_VIEW_ROW_FP4, MX_VIEW_SEQ, MX_VIEW_SEQ_TOKEN,
+    from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F16_PREFIX, MX_DQ_F32, MX_VIEW_ROW_FP4, MX_VIEW_SEQ,
+                                        MX_VIEW_SEQ_TOKEN,
                                         PROFILE_BWD_DKDV, PROFILE_BWD_DQ, PROFILE_BWD_PREP, PROFILE_FWD,
                                         PROFILE_QUANTIZE, load, mx_attn_bwd, mx_attn_fwd, mx_attn_fwd_strict,
                                         mx_profile_kernel, mx_quantize, mx_quantize_token_block)
@@ -183,7 +186,7 @@ def run_attention(args):
     cfg = synth.CONFIGS[name]
     d = cfg["head_dim"]
     causal = cfg["causal"]
-    dq_mode = MX_DQ_F32 if args.dq == "f32" else MX_DQ_F16_BOOST
+    dq_mode = {"f32": MX_DQ_F32, "f16": MX_DQ_F16_BOOST, "f16prefix": MX_DQ_F16_PREFIX}[args.dq]
     print(f"[bench] generating {name} inputs", file=sys.stderr, flush=True)
     x = synth.make_inputs(name)
     packed = "cu_seqlens" in x
@@ -305,7 +308,10 @@ def run_attention(args):
                                    workspace=ws.get(mode), ds_store=ds_store, **kw)
 
     res_bwd = {}
-    for nm, mode in (("f32", MX_DQ_F32), ("f16", MX_DQ_F16_BOOST)):
+    modes = [("f32", MX_DQ_F32), ("f16", MX_DQ_F16_BOOST)]
+    if args.dq == "f16prefix":
+        modes.append(("f16prefix", MX_DQ_F16_PREFIX))
+    for nm, mode in modes:
         if mode not in ws:
             _, _, _, ws[mode] = bwd(mode)()
         main_ms = kernel_ms(PROFILE_BWD_DKDV, bwd(mode))
@@ -374,6 +380,10 @@ def run_attention(args):
         "bwd_pct_of_peak": round(100 * tflops(f_bwd, bwd_f32["call_ms"]) / pk_bwd, 2),
         "bwd_f16dq_tflops": round(tflops(f_bwd, bwd_f16["call_ms"]), 2),
         "bwd_f16dq_pct_of_peak": round(100 * tflops(f_bwd, bwd_f16["call_ms"]) / pk_bwd, 2),
+        **({"bwd_f16prefix_tflops": round(tflops(f_bwd, res_bwd["f16prefix"]["call_ms"]), 2),
+            "bwd_f16prefix_call_ms": round(res_bwd["f16prefix"]["call_ms"], 4),
+            "bwd_f16prefix_prep_ms": round(res_bwd["f16prefix"]["prep_ms"], 4),
+            "attn_bwd_dq_f16prefix_ms": round(res_bwd["f16prefix"]["dq_ms"], 4)} if "f16prefix" in res_bwd else {}),
         "peaks_tflops": {"step": round(pk_step, 1), "fwd": round(pk_fwd, 1), "bwd": round(pk_bwd, 1)},
         "quantize_gbs": round(quant_bytes / (ms_quant * 1e-3) / 1e9, 1),
         "quantize_token_block_gbs": None if ms_quant_tb is None else round(quant_bytes / (ms_quant_tb * 1e-3) / 1e9, 1),
@@ -412,6 +422,8 @@ def run_cross(args):
     load()
     cfg = synth.CONFIGS["x1"]
     H, d = cfg["heads"], cfg["head_dim"]
+    if args.dq == "f16prefix":
+        sys.exit("--dq f16prefix is measured on the self-attention workloads")
     dq_mode = MX_DQ_F32 if args.dq == "f32" else MX_DQ_F16_BOOST
     print("[bench] generating x1 inputs on the device", file=sys.stderr, flush=True)
     x = synth.make_cross_inputs_device()
