@@ -818,62 +818,102 @@ __device__ __forceinline__ float block_scan_max(float x, float* wmax) {
 }
 
 // vpre[j] = max_{j' <= j} |V~_row,j'|_2 and kpre[j] = max_{j' <= j} max_c |K~_seq,j'c| for the keys of
-// one (KV head, sequence or document): blockIdx.x = KV head, blockIdx.y = sequence or document.
-// The keys go 256 at a time (one per thread), decoded from the views the backward's products read;
-// a workgroup max-scan joins them, carried from one group of 256 to the next.
+// one (KV head, sequence or document), in two passes. This one: blockIdx = (KV head, sequence or
+// document, chunk of 256 keys); one key per thread, decoded from the views the backward's
+// products read, then a workgroup max-scan: the maxima inside the chunk.
 template <int D, bool kPacked>
 __global__ __launch_bounds__(256) void bwd_kv_prefix_kernel(BwdParams p) {
   __shared__ float wm[2][4];
-  __shared__ float last[2];
   const Geom& gk = p.geom_k;
   const int hkv = blockIdx.x, s = blockIdx.y;
   const int doc_k = kPacked ? gk.cu[s] : 0;
   const int nk = kPacked ? gk.cu[s + 1] - doc_k : gk.seqlen;
+  const int j0 = (int)blockIdx.z * 256;
+  if (j0 >= nk) return;                      // (uniform over the workgroup)
   const long long sbase = kPacked ? (long long)doc_k : (long long)s;
-  float vc = 0.f, kc = 0.f;                 // maxima of the keys before this group of 256
-  for (int j0 = 0; j0 < nk; j0 += 256) {
-    const int j = j0 + (int)threadIdx.x;
-    float vn = 0.f, km = 0.f;
-    if (j < nk) {
-      const long long off = elem_offset_k<kPacked>(gk, p.heads_kv, D, sbase, hkv, j, 0);
-      float ss = 0.f;
+  const int j = j0 + (int)threadIdx.x;
+  float vn = 0.f, km = 0.f;
+  if (j < nk) {
+    const long long off = elem_offset_k<kPacked>(gk, p.heads_kv, D, sbase, hkv, j, 0);
+    float ss = 0.f;
 #pragma unroll
-      for (int c16 = 0; c16 < D / 16; c16++) {
-        const v4i w = *reinterpret_cast<const v4i*>(p.vr_codes + off + 16 * c16);
-        const int e = (int)p.vr_scales[(off >> 5) + c16 / 2] - 127;
+    for (int c16 = 0; c16 < D / 16; c16++) {
+      const v4i w = *reinterpret_cast<const v4i*>(p.vr_codes + off + 16 * c16);
+      const int e = (int)p.vr_scales[(off >> 5) + c16 / 2] - 127;
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-          float x4[4];
-          unpack4_e4m3((uint32_t)w[q], x4);
+      for (int q = 0; q < 4; q++) {
+        float x4[4];
+        unpack4_e4m3((uint32_t)w[q], x4);
 #pragma unroll
-          for (int u = 0; u < 4; u++) {
-            const float x = ldexpf(x4[u], e);
-            ss = __builtin_fmaf(x, x, ss);
-          }
+        for (int u = 0; u < 4; u++) {
+          const float x = ldexpf(x4[u], e);
+          ss = __builtin_fmaf(x, x, ss);
         }
       }
-      vn = __builtin_sqrtf(ss);
-      const long long grow = seq_group_row_k<kPacked>(gk, p.heads_kv, s, hkv, doc_k, j >> 5);
-      const uint8_t* kcod = p.ks_codes + grow * (D * 32) + seq_pos(j & 31);
-      const uint8_t* ksc = p.ks_scales + grow * D;
+    }
+    vn = __builtin_sqrtf(ss);
+    const long long grow = seq_group_row_k<kPacked>(gk, p.heads_kv, s, hkv, doc_k, j >> 5);
+    const uint8_t* kcod = p.ks_codes + grow * (D * 32) + seq_pos(j & 31);
+    const uint8_t* ksc = p.ks_scales + grow * D;
 #pragma unroll 8
-      for (int c = 0; c < D; c++)
-        km = fmaxf(km, fabsf(ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)kcod[c * 32], 0), (int)ksc[c] - 127)));
+    for (int c = 0; c < D; c++)
+      km = fmaxf(km, fabsf(ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)kcod[c * 32], 0), (int)ksc[c] - 127)));
+  }
+  const float vs = block_scan_max(vn, wm[0]);
+  const float ks = block_scan_max(km, wm[1]);
+  if (j < nk) {
+    const long long idx = token_index_k<kPacked>(gk, p.heads_kv, s, doc_k, hkv, j);
+    p.vpre[idx] = vs;
+    p.kpre[idx] = ks;
+  }
+}
+
+// Second pass: blockIdx = (KV head, sequence or document). Each chunk's maxima are its last
+// key's values from the first pass; every key of chunk c then takes the maximum with those of
+// the chunks before c (an exclusive max-scan over chunks, held in LDS). All reads of the chunk
+// maxima come before the first write.
+template <bool kPacked>
+__global__ __launch_bounds__(256) void bwd_kv_prefix_carry_kernel(BwdParams p) {
+  constexpr int kMaxChunks = 256;            // chunks per window: one per thread (64 Ki keys)
+  __shared__ float cv[kMaxChunks], ck[kMaxChunks];
+  __shared__ float wm[2][4];
+  const Geom& gk = p.geom_k;
+  const int hkv = blockIdx.x, s = blockIdx.y;
+  const int doc_k = kPacked ? gk.cu[s] : 0;
+  const int nk = kPacked ? gk.cu[s + 1] - doc_k : gk.seqlen;
+  const int nch = (nk + 255) / 256;
+  float vc = 0.f, kc = 0.f;                  // maxima of the chunks before the current window
+  for (int c0 = 0; c0 < nch; c0 += kMaxChunks) {
+    // window of chunks [c0, c0 + kMaxChunks): thread t reads chunk c0 + t's maxima (its last key)
+    const int c = c0 + (int)threadIdx.x;
+    float v = 0.f, k = 0.f;
+    if (threadIdx.x < kMaxChunks && c < nch) {
+      const int jl = min(c * 256 + 255, nk - 1);
+      const long long idx = token_index_k<kPacked>(gk, p.heads_kv, s, doc_k, hkv, jl);
+      v = p.vpre[idx];
+      k = p.kpre[idx];
     }
-    const float vs = fmaxf(block_scan_max(vn, wm[0]), vc);
-    const float ks = fmaxf(block_scan_max(km, wm[1]), kc);
-    if (j < nk) {
-      const long long idx = token_index_k<kPacked>(gk, p.heads_kv, s, doc_k, hkv, j);
-      p.vpre[idx] = vs;
-      p.kpre[idx] = ks;
-    }
-    if (threadIdx.x == 255) {                // the group's maxima (held by its last thread)
-      last[0] = vs;
-      last[1] = ks;
+    // inclusive max-scan over the window (joined with the earlier windows' vc, kc): entry t is
+    // the maximum of every chunk up to c0 + t, i.e. the carry into chunk c0 + t + 1
+    const float vi = fmaxf(block_scan_max(v, wm[0]), vc);
+    const float ki = fmaxf(block_scan_max(k, wm[1]), kc);
+    if (threadIdx.x < kMaxChunks) {
+      cv[threadIdx.x] = vi;
+      ck[threadIdx.x] = ki;
     }
     __syncthreads();
-    vc = last[0];
-    kc = last[1];
+    const int wend = min(nch, c0 + kMaxChunks);
+    // keys of chunk c0 take vc, kc (chunk 0 needs nothing); those of chunk c > c0 cv, ck[c - c0 - 1]
+    for (int jj = (c0 == 0 ? 256 : c0 * 256) + (int)threadIdx.x; jj < min(nk, wend * 256); jj += 256) {
+      const int cj = jj >> 8;
+      const float av = cj == c0 ? vc : cv[cj - c0 - 1];
+      const float ak = cj == c0 ? kc : ck[cj - c0 - 1];
+      const long long idx = token_index_k<kPacked>(gk, p.heads_kv, s, doc_k, hkv, jj);
+      p.vpre[idx] = fmaxf(p.vpre[idx], av);
+      p.kpre[idx] = fmaxf(p.kpre[idx], ak);
+    }
+    vc = cv[min(kMaxChunks, wend - c0) - 1];
+    kc = ck[min(kMaxChunks, wend - c0) - 1];
     __syncthreads();
   }
 }
@@ -1462,14 +1502,19 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
   profile_end(slot, stream);
   if (err != hipSuccess) return err;
   if (p.dq_mode == 2) {   // prefix maxima of the per-key statistics of the prefix dQ boost
-    const dim3 grid((unsigned)p.heads_kv, (unsigned)(packed(p.geom_k) ? p.geom_k.n_docs : p.geom_k.batch));
+    const bool pk = packed(p.geom_k);
+    const unsigned nseq = (unsigned)(pk ? p.geom_k.n_docs : p.geom_k.batch);
+    const unsigned nch = (unsigned)(((pk ? p.geom_k.max_seqlen : p.geom_k.seqlen) + 255) / 256);
+    const dim3 grid((unsigned)p.heads_kv, nseq, nch), grid2((unsigned)p.heads_kv, nseq);
     if (p.head_dim == 128) {
-      if (packed(p.geom_k)) hipLaunchKernelGGL((bwd_kv_prefix_kernel<128, true>), grid, dim3(256), 0, stream, p);
+      if (pk) hipLaunchKernelGGL((bwd_kv_prefix_kernel<128, true>), grid, dim3(256), 0, stream, p);
       else hipLaunchKernelGGL((bwd_kv_prefix_kernel<128, false>), grid, dim3(256), 0, stream, p);
     } else {
-      if (packed(p.geom_k)) hipLaunchKernelGGL((bwd_kv_prefix_kernel<64, true>), grid, dim3(256), 0, stream, p);
+      if (pk) hipLaunchKernelGGL((bwd_kv_prefix_kernel<64, true>), grid, dim3(256), 0, stream, p);
       else hipLaunchKernelGGL((bwd_kv_prefix_kernel<64, false>), grid, dim3(256), 0, stream, p);
     }
+    if (pk) hipLaunchKernelGGL((bwd_kv_prefix_carry_kernel<true>), grid2, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((bwd_kv_prefix_carry_kernel<false>), grid2, dim3(256), 0, stream, p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // 2. dK / dV, 3. dQ
