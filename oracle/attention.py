@@ -416,7 +416,7 @@ def _quant_blocks2d(U):
 
 def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantized=True,
                   out_dtype="bf16", bounds=False, fwd=None, dq_mode="f32", perturb=None,
-                  dq_blocks=None, dk_blocks=None, scales="axis", score_format="mxfp8"):
+                  dq_blocks=None, dk_blocks=None, scales="axis", score_format="mxfp8", strict=False):
     """Backward pass for one head (Algorithm 1 steps 09-16 of the FLAMIA notes).
 
     o_saved: O as stored by the forward (output dtype); lse: the forward's row LSE (natural
@@ -450,6 +450,18 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
     ``score_format="mxfp4"`` rebuilds S from the same MXFP4 Q and K views as head_forward
     (FLAMIA notes, section 3: the backward recomputes the scores with the original 4-bit Q/K
     and takes E4M3 views for dQ and dK); every other product is unchanged.
+
+    ``strict=True`` (causal, FP32 dQ): dQ by FLAMIA's strict option (notes, section 4: per-key
+    K scales folded into dS -- the K fold -- and per-query dS scales), so that dQ_i depends on no
+    position after i. dQ's dS operand is U quantised per query in groups of 32 keys (one E8M0
+    exponent per (query, 32-key group), the MX rule on the group's largest |value|) instead of in
+    32 x 32 blocks shared with later queries; for the keys of the query's own 32-key group
+    (32 floor(i/32) <= j <= i), whose K SEQ group reaches past i, K enters through the per-token
+    view (mx_quantize_per_token: one exponent e_j per key over all channels) and its 2^e_j is
+    folded into U before that quantisation: U'_ij = U_ij 2^e_j multiplies the key's codes.
+    Earlier keys keep the K SEQ view. dK, dV and the dS blocks (dS_codes, dS_exp) are the plain
+    ones. Returns dQ_dS_exp, the per-query exponents [rows, ceil(n_k/32)] (DS_UNSET where a
+    group is not evaluated).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -481,6 +493,13 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
         c = alpha * LOG2E
         lse2 = lse * LOG2E
     need = quantized and (bounds or perturb is not None)
+    if strict:
+        assert quantized and causal and dq_mode == "f32" and scales == "axis" and perturb is None, \
+            "the strict dQ is a causal, per-axis, FP32-dQ mode"
+        kcodes_t, ke_t, _ = mx_quantize_per_token(k)
+        Kcode = e4m3_decode(kcodes_t)                 # the key's codes (its scale is folded into dS)
+        Kcode_mag = exp_magnitude(Kcode, np.zeros((nk, 1), np.int64))
+        dq_dse = np.full((n, -(-nk // GROUP)), DS_UNSET, np.int64)
     D = np.sum(Grx * o_saved, axis=1)
     lse2f = np.where(np.isfinite(lse2), lse2, 0.0)
     if need:
@@ -568,7 +587,17 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
             Pb, Uh = P, U
         dV[kc] += Pb.T @ Gsx[r0:r1]
         dK[kc] += alpha * (Uh.T @ Qsx[r0:r1])
-        dQ[r0:r1] += alpha * (Uh @ Ksx[kc])
+        if strict:
+            assert nkc == nk, "the strict dQ evaluates whole rows"
+            ri = np.arange(r0, r1)
+            fold = (np.arange(nk)[None, :] // GROUP) == (ri // GROUP)[:, None]   # the query's own key group
+            Uf = np.where(fold, np.ldexp(U, np.broadcast_to(ke_t[None, :], U.shape)), U)
+            e_q = _group_exp_rows(np.abs(Uf))                 # one exponent per (query, 32 keys)
+            Uq = np.ldexp(e4m3_round(np.ldexp(Uf, -e_q)), e_q)
+            dQ[r0:r1] += alpha * (np.where(fold, 0.0, Uq) @ Ksx + np.where(fold, Uq, 0.0) @ Kcode)
+            dq_dse[r0:r1] = e_q[:, ::GROUP]
+        else:
+            dQ[r0:r1] += alpha * (Uh @ Ksx[kc])
         if need:
             drel = np.where(mask, LN2 * dx, 0.0)
             devPb = _dev_cols(P, drel)
@@ -576,7 +605,12 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
             dU = np.where(mask, P * dE + np.abs(U) * (drel + U32), 0.0)
             devU, eamb = _dev_blocks(U, dU, exp_amb=True)
             BdK[kc] += alpha * (devU.T @ np.abs(Qsx[r0:r1]))
-            BdQ[r0:r1] += alpha * (devU @ np.abs(Ksx[kc]))
+            if strict:
+                dUf = np.where(fold, np.ldexp(dU, np.broadcast_to(ke_t[None, :], U.shape)), dU)
+                devQ = _dev_rows(Uf, dUf)
+                BdQ[r0:r1] += alpha * (np.where(fold, 0.0, devQ) @ np.abs(Ksx) + np.where(fold, devQ, 0.0) @ np.abs(Kcode))
+            else:
+                BdQ[r0:r1] += alpha * (devU @ np.abs(Ksx[kc]))
             amb = (devU > 0) | np.where(U == 0, dU > 0, False)
             sub = np.zeros((-(-rows // GROUP) * GROUP, len(kblk) * GROUP), bool)
             sub[:rows, pos] = amb
@@ -591,6 +625,13 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
             edV[kc] += up[0]
             edK[kc] += up[1]
             edQ[r0:r1] = up[2]
+            if strict:   # dQ's own products: per-query codes, folded keys against their token codes
+                Ua = np.abs(Uq) + devQ
+                Um = exp_magnitude(Ua, e_q + (devQ > 0))
+                edQ[r0:r1] = alpha * (GROUP_TRUNC * (group_max_bound(np.where(fold, 0.0, Um), Ksm, nk)
+                                                     + group_max_bound(np.where(fold, Um, 0.0), Kcode_mag, nk))
+                                      + 4 * (_ins(nk) + 1) * U32 * (np.where(fold, 0.0, Ua) @ np.abs(Ksx)
+                                                                    + np.where(fold, Ua, 0.0) @ np.abs(Kcode)))
             if perturb is not None:
                 # a device whose codes are this run's: the allowances of its own products
                 own = _product_allowances(np.abs(Pb), pe_elem, Uh, np.zeros_like(Uh), ue_elem, Gsx[r0:r1],
@@ -619,6 +660,8 @@ def head_backward(q, k, v, o_saved, lse, g, causal, softmax_scale=None, quantize
                dS_exp_amb=ds_exp_amb)
     if boost_exp is not None:
         out.update(dq_boost_exp=be_nom, dq_boost_amb=boost_amb)
+    if strict:
+        out.update(dQ_dS_exp=dq_dse)
     if bounds and need:
         out.update(B_dQ=BdQ, B_dK=BdK, B_dV=BdV, eta_dQ=edQ, eta_dK=edK, eta_dV=edV)
     elif bounds:
@@ -761,6 +804,22 @@ def _dev_blocks(U, dU, exp_amb=False):
         eamb = np.asarray(eamb).reshape(R // GROUP, C // GROUP, GROUP, GROUP).transpose(0, 2, 1, 3).reshape(R, C)
         return dev[:rows, :nk], eamb
     return dev[:rows, :nk]
+
+
+def _dev_rows(U, dU):
+    """_mx_dev for the strict dQ's dS: groups of 32 consecutive keys (columns) of each query row,
+    absolute budgets dU."""
+    rows, nk = U.shape
+    y0 = _pad_groups(U)
+    d0 = _pad_groups(dU)
+    e = mx_scale_exponent(np.max(np.abs(y0), axis=2))[:, :, None]
+    e = np.broadcast_to(e, y0.shape)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(y0 != 0, d0 / np.abs(y0), 0.0)
+    dev = _mx_dev(np.ldexp(y0, -e), e, rel, 2)
+    # an element whose value is 0 but whose budget is not: it may quantise away from 0
+    dev = np.maximum(dev, np.where(y0 == 0, np.ldexp(e4m3_round(np.ldexp(d0, -e)), e), 0.0))
+    return dev.reshape(rows, -1)[:, :nk]
 
 
 def _round_spread(x, allowance, dtype):
