@@ -1460,7 +1460,7 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   slot = profile_begin(kProfBwdQ, stream);
-  const bool f16 = p.dq_mode == 1;
+  const bool f16 = p.dq_mode != 0;        // FP16 sums: the fixed 2^9 boost (1) or the per-row prefix boost (2)
   if (!store) {
     if (f16) hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), gq, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), gq, dim3(256), 0, stream, p);

@@ -277,3 +277,26 @@ def test_prefix_boost_keeps_the_fp16_sums_in_range():
         dev = as_f64(dq)[0]
         assert gate("dQ", dev, np.stack([r["dQ"] for r in refs]), np.stack([r["B_dQ"] for r in refs]),
                     np.stack([r["eta_dQ"] for r in refs]), key="dQ16").ok, ds_store
+
+
+def test_prefix_mode_accumulates_in_fp16_with_a_row_scaled_boost():
+    # The prefix mode runs the FP16 dQ kernels (its dQ differs from the FP32 mode's bits) with a
+    # boost that follows each row's statistics: G -> 2^-20 G scales U, and so every row's a_i, by
+    # 2^-20, the boost by 2^20, and the FP16 sums are the same numbers, so dQ scales by exactly
+    # 2^-20. The fixed 2^9 boost of the other FP16 mode leaves such sums in FP16's subnormal
+    # range, where they lose bits. Both dQ routes (stored and rebuilt dS).
+    print("[prefix fp16] c3 B1 H2 L200 d128", flush=True)
+    t = _inputs("c3", 1, 2, 2, 200, 128, torch.bfloat16)
+    o, lse = _fwd_dev(t, True, torch.bfloat16)
+    o = o.float().contiguous()             # FP32 outputs (the backward takes O in the output type)
+    small = dict(t, g=(t["g"].float() * 2.0 ** -20).to(torch.bfloat16))
+    for ds_store in (True, False):
+        def run(x, mode):
+            dq = _bwd_dev(x, o, lse, True, torch.float32, mode, ds_store=ds_store)[0]
+            torch.cuda.synchronize()
+            return dq.clone()
+        p1, p2 = run(t, MX_DQ_F16_PREFIX), run(small, MX_DQ_F16_PREFIX)
+        assert not torch.equal(p1, run(t, MX_DQ_F32)), ds_store
+        assert torch.equal(p2, p1 * 2.0 ** -20), ds_store
+        f1, f2 = run(t, MX_DQ_F16_BOOST), run(small, MX_DQ_F16_BOOST)
+        assert not torch.equal(f2, f1 * 2.0 ** -20), ds_store
