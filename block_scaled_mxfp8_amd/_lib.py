@@ -134,6 +134,9 @@ def _bind(lib):
         f.restype = I32
     lib.mx_attn_fwd_strict.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, _QView, P, P, P]
     lib.mx_attn_fwd_strict.restype = I32
+    lib.mx_attn_bwd_strict.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, _QView, _QView, _QView, P, P, P,
+                                       I32, P, P, P, P]
+    lib.mx_attn_bwd_strict.restype = I32
     for name in ("mx_attn_bwd", "mx_attn_varlen_bwd", "mx_attn_bwd_noalloc"):
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(_Desc), _QView, _QView, _QView, _QView, _QView, P, P, P, I32, P, P, P, P]
@@ -469,7 +472,7 @@ def mx_attn_workspace_size(q_shape, cu_seqlens=None, max_seqlen=None, heads_kv=N
 
 
 def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype, dq_mode, cu_seqlens,
-         max_seqlen, workspace, deterministic=False, ds_store=True, cross=None, mx_views=0):
+         max_seqlen, workspace, deterministic=False, ds_store=True, cross=None, mx_views=0, k_tok=None):
     lib = load()
     qs, ks = _elem_shape(q_row), _elem_shape(k_row)
     fmt = _score_format(q_row, k_row)
@@ -503,6 +506,8 @@ def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_sca
                                  (k_seq, kseq, desc.heads_kv, MX_VIEW_SEQ, "k_seq"),
                                  (v_row, kseq, desc.heads_kv, MX_VIEW_ROW, "v_row")):
         _check_view(lib, v, sq, h, desc.head_dim, view, what)
+    if k_tok is not None:
+        _check_view(lib, k_tok, kseq, desc.heads_kv, desc.head_dim, MX_VIEW_SEQ_TOKEN, "k_tok")
     nq = int(torch.Size(qs).numel())
     _check_tensor(o, nq, "o")
     _check_tensor(g, nq, "g")
@@ -526,7 +531,9 @@ def _bwd(name, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_sca
         st = lib.mx_attn_bwd_mx(ctypes.byref(desc), *args[:-1], *ptrs, args[-1])
         _check(st, name)
         return dq, dk, dv, workspace, (views[0], views[1]), (views[2], views[3])
-    if seq_k is None:
+    if k_tok is not None:
+        st = lib.mx_attn_bwd_strict(ctypes.byref(desc), *args[:4], _qv(k_tok), *args[4:])
+    elif seq_k is None:
         st = getattr(lib, name)(ctypes.byref(desc), *args)
     else:
         st = lib.mx_attn_cross_bwd(ctypes.byref(desc), ctypes.byref(seq_k), *args)
@@ -543,6 +550,15 @@ def mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal=True, softm
     the minimum. A given workspace selects the store by its size (mx_attn_workspace_size)."""
     return _bwd("mx_attn_bwd", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal, softmax_scale, out_dtype,
                 dq_mode, cu_seqlens, max_seqlen, workspace, deterministic, ds_store)
+
+
+def mx_attn_bwd_strict(q_row, q_seq, k_row, k_seq, k_tok, v_row, o, lse, g, softmax_scale=0.0,
+                       out_dtype=torch.bfloat16, cu_seqlens=None, max_seqlen=None, workspace=None):
+    """Causal backward with the strict dQ (per-query dS scales and the K fold on each query's own
+    key group) -> (dq, dk, dv, workspace); k_tok: mx_quantize(k, MX_VIEW_SEQ_TOKEN)[1]. FP32 dQ;
+    batched, or packed with cu_seqlens. dK and dV are mx_attn_bwd's."""
+    return _bwd("mx_attn_bwd_strict", q_row, q_seq, k_row, k_seq, v_row, o, lse, g, True, softmax_scale, out_dtype,
+                MX_DQ_F32, cu_seqlens, max_seqlen, workspace, ds_store=False, k_tok=k_tok)
 
 
 def mx_attn_bwd_noalloc(q_row, q_seq, k_row, k_seq, v_row, o, lse, g, causal=True, softmax_scale=0.0,

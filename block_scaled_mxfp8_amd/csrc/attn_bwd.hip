@@ -933,8 +933,9 @@ __device__ __forceinline__ int row_boost_exp(const BwdParams& p, int s, int doc_
 
 // ================================ dQ pass =================================
 
-// One 64-key tile in LDS (code tiles by LDS-DMA, small items by ordinary loads).
-template <int D>
+// One 64-key tile in LDS (code tiles by LDS-DMA, small items by ordinary loads). kS (strict dQ):
+// also the tile's per-token K codes (SEQ layout) and their scale bytes.
+template <int D, bool kS = false>
 struct DqStage {
   alignas(16) uint8_t kr[kStepK * D];   // K ROW codes [key][d], row_swz chunks
   alignas(16) uint8_t vr[kStepK * D];   // V ROW codes
@@ -942,6 +943,8 @@ struct DqStage {
   alignas(16) uint32_t krs[kStepK];     // K ROW scale word per key
   alignas(16) uint32_t vrs[kStepK];     // V ROW scale word per key
   alignas(16) uint8_t kss[2 * D];       // K SEQ scales [group][channel]
+  alignas(16) uint8_t kt[kS ? 2 * D * 32 : 16];   // (kS) per-token K codes, the SEQ tile's layout
+  alignas(16) uint8_t kte[kS ? kStepK : 16];      // (kS) per-token K scale bytes, key order
 };
 
 // doc_start / n: the queries of the sequence or document; doc_k / nk: its keys.
@@ -993,8 +996,8 @@ __device__ __forceinline__ QWork decode_q(const BwdParams& p, int* smem) {
 }
 
 // Issue the loads of key tile kt (keys 64kt..64kt+63 of KV head hkv) into stage `st`.
-template <int D>
-__device__ __forceinline__ void dq_issue(const BwdParams& p, const QWork& w, int hkv, int kt, DqStage<D>& st,
+template <int D, bool kS>
+__device__ __forceinline__ void dq_issue(const BwdParams& p, const QWork& w, int hkv, int kt, DqStage<D, kS>& st,
                                          uint32_t& sv, const int (&roff)[2], int soff) {
   const Geom& g = p.geom_k;
   const int lane = threadIdx.x & 63;
@@ -1012,6 +1015,7 @@ __device__ __forceinline__ void dq_issue(const BwdParams& p, const QWork& w, int
     const long long row0 = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_k, min(g0, glast));
     const long long row1 = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_k, min(g0 + 1, glast));
     dma_seq_tile<D>(p.ks_codes, row0, row1, soff, st.ks, wave - 2, 2);
+    if (kS) dma_seq_tile<D>(p.kt_codes, row0, row1, soff, st.kt, wave - 2, 2);
   }
   sv = 0;
   if (wave < 2) {                                     // ROW scale words (wave 0: K, wave 1: V)
@@ -1023,24 +1027,37 @@ __device__ __forceinline__ void dq_issue(const BwdParams& p, const QWork& w, int
     const int gi = min((k0 >> 5) + (lane * 4) / D, glast);
     const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_k, gi);
     sv = *reinterpret_cast<const uint32_t*>(p.ks_scales + row * D + (lane * 4) % D);
+  } else if (kS && wave == 3 && lane < kStepK / 4) {  // per-token K scale bytes, a dword per lane
+    const int gi = min((k0 >> 5) + lane / 8, glast);
+    const long long row = seq_group_row(g, p.heads_kv, w.s, hkv, w.doc_k, gi);
+    sv = *reinterpret_cast<const uint32_t*>(p.kt_scales + row * 32 + 4 * (lane & 7));
   }
 }
 
-template <int D>
-__device__ __forceinline__ void dq_put(DqStage<D>& st, uint32_t sv) {
+template <int D, bool kS>
+__device__ __forceinline__ void dq_put(DqStage<D, kS>& st, uint32_t sv) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   if (wave < 2) (wave == 0 ? st.krs : st.vrs)[lane] = sv;
   else if (wave == 2 && lane < D / 2) reinterpret_cast<uint32_t*>(st.kss)[lane] = sv;
+  else if (kS && wave == 3 && lane < kStepK / 4) reinterpret_cast<uint32_t*>(st.kte)[lane] = sv;
 }
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // kF16: dQ partial sums of 128 keys (two tiles) are multiplied by alpha 2^9, rounded to FP16
 // and summed in FP16; the result is scaled by 2^-9.
-template <int D, bool kF16>
+// kS: the strict dQ (FLAMIA notes, section 4: per-query dS scales and the K fold), so that dQ_i
+// depends on no later position. dS is quantised per query in groups of 32 keys -- the lane's 16
+// values and lane ^ 32's, one exponent per (query, key group), which is exactly the B operand's
+// scale granularity -- instead of in 32 x 32 blocks shared with the wave's other queries; on the
+// wave's own key group (keys 32 floor(i/32) .. , the diagonal one, whose K SEQ group reaches past
+// i) each key's per-token K exponent is folded into dS (fold_codes16) and K enters through the
+// per-token codes with scale 1.
+template <int D, bool kF16, bool kS = false>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
-  __shared__ DqStage<D> sm[2];
+  static_assert(!(kF16 && kS), "the strict dQ accumulates in FP32");
+  __shared__ DqStage<D, kS> sm[2];
   const QWork w = decode_q(p, reinterpret_cast<int*>(&sm[0]));
   if (!w.valid) return;
   const Geom& g = p.geom;
@@ -1063,7 +1080,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const int roff[2] = {row_tile_lane_off<D>(lane, 0), row_tile_lane_off<D>(lane, 1)};
   const int soff = seq_tile_lane_off(lane);
   uint32_t sv = 0;
-  if (nkt > 0) dq_issue<D>(p, w, hkv, 0, sm[0], sv, roff, soff);
+  if (nkt > 0) dq_issue<D, kS>(p, w, hkv, 0, sm[0], sv, roff, soff);
 
   // Q and G of the lane's query: B operands of S^T and E^T, kept in registers
   v8i qop[NS], gop[NS];
@@ -1113,14 +1130,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   }
   const int soff_c = l32 * 32 + (half_swz(l32, hh) << 4);   // SEQ tile, channel l32 of group 0
   const int scoff = hh * D + l32;                            // SEQ scale of channel l32, group hh
-  if (nkt > 0) dq_put<D>(sm[0], sv);
+  if (nkt > 0) dq_put<D, kS>(sm[0], sv);
   wait_vmem();
   __syncthreads();
 
   for (int kt = 0; kt < nkt; kt++) {
     const int buf = kt & 1;
-    if (kt + 1 < nkt) dq_issue<D>(p, w, hkv, kt + 1, sm[buf ^ 1], sv, roff, soff);
-    const DqStage<D>& S = sm[buf];
+    if (kt + 1 < nkt) dq_issue<D, kS>(p, w, hkv, kt + 1, sm[buf ^ 1], sv, roff, soff);
+    const DqStage<D, kS>& S = sm[buf];
     const int kbase = kt * kStepK;
     if (qw < w.n && !(p.causal && kbase > qw + 31)) {
       const bool need_mask = (p.causal && kbase + kStepK - 1 > qw) || kbase + kStepK > w.nk || qw + 32 > w.n;
@@ -1155,25 +1172,43 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
           }
           U[i] = __builtin_amdgcn_exp2f(x) * eacc[i];
         }
-        const float um = wave_max(max_abs16(U));
-        dse[T] = scale_exp_from_bits(__float_as_uint(um));
-        const float usc = exp2_scale(dse[T]);
+        if (kS && (kbase >> 5) + T == (qw >> 5)) {   // the wave's own key group: the K fold
+          uint32_t eb[4];
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-          dsop[4 * T + j] = (int)pack4_e4m3_scaled(U[4 * j], U[4 * j + 1], U[4 * j + 2], U[4 * j + 3], usc);
+          for (int b4 = 0; b4 < 4; b4++) eb[b4] = *reinterpret_cast<const uint32_t*>(S.kte + T * 32 + 8 * b4 + 4 * hh);
+          v16f uv;
+#pragma unroll
+          for (int i = 0; i < 16; i++) uv[i] = U[i];
+          dse[T] = fold_codes16(uv, eb, dsop, T);
+        } else {
+          // one exponent per (query, 32 keys) (kS), or per 32 x 32 block (the wave's queries)
+          const float ul = max_abs16(U);
+          const float um = kS ? fmaxf(ul, swap32(ul)) : wave_max(ul);
+          dse[T] = scale_exp_from_bits(__float_as_uint(um));
+          const float usc = exp2_scale(dse[T]);
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            dsop[4 * T + j] = (int)pack4_e4m3_scaled(U[4 * j], U[4 * j + 1], U[4 * j + 2], U[4 * j + 3], usc);
+        }
       }
       const int dssc = (hh ? dse[1] : dse[0]) + 127;
+      // (kS) the key groups of this tile that are the wave's own: their K codes are per-token
+      const bool dg0 = kS && (kbase >> 5) == (qw >> 5), dg1 = kS && (kbase >> 5) + 1 == (qw >> 5);
+      const uint8_t* ksrc0 = dg0 ? S.kt : S.ks;
+      const uint8_t* ksrc1 = dg1 ? S.kt : S.ks;
+      const bool dgh = hh ? dg1 : dg0;                         // the group whose scale this lane supplies
       // dQ^T += K_seq^T dS^T (rows = channels, columns = the wave's queries)
 #pragma unroll
       for (int t = 0; t < NCT; t++) {
-        const v8i ka = cat(*reinterpret_cast<const v4i*>(&S.ks[t * 1024 + soff_c]),
-                           *reinterpret_cast<const v4i*>(&S.ks[D * 32 + t * 1024 + soff_c]));
-        dq[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, dsop, dq[t], 0, 0, 0, S.kss[scoff + t * 32], 0, dssc);
+        const v8i ka = cat(*reinterpret_cast<const v4i*>(&ksrc0[t * 1024 + soff_c]),
+                           *reinterpret_cast<const v4i*>(&ksrc1[D * 32 + t * 1024 + soff_c]));
+        const int ksc = dgh ? 127 : S.kss[scoff + t * 32];
+        dq[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, dsop, dq[t], 0, 0, 0, ksc, 0, dssc);
       }
     }
     if (kF16 && ((kt & 1) || kt + 1 == nkt)) fold();
     if (kt + 1 < nkt) {
-      dq_put<D>(sm[buf ^ 1], sv);
+      dq_put<D, kS>(sm[buf ^ 1], sv);
       wait_vmem();
       __syncthreads();
     }
@@ -1461,7 +1496,9 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
   if (err != hipSuccess) return err;
   slot = profile_begin(kProfBwdQ, stream);
   const bool f16 = p.dq_mode != 0;        // FP16 sums: the fixed 2^9 boost (1) or the per-row prefix boost (2)
-  if (!store) {
+  if (p.kt_codes) {                        // the strict dQ (FP32; the host checks the mode)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false, true>), gq, dim3(256), 0, stream, p);
+  } else if (!store) {
     if (f16) hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), gq, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), gq, dim3(256), 0, stream, p);
   } else if (packed(g)) {

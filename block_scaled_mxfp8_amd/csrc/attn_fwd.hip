@@ -411,48 +411,8 @@ __device__ __forceinline__ float softmax_tile(v16f (&cur)[2], float c_rt, int li
   return f;
 }
 
-// The P codes of one 32-key group of a diagonal tile under the strict fold: the codes of
-// P'_j = p_j 2^e_j (x: the lane's 16 p of the group, eb: their keys' token scale bytes, four
-// per dword in key order). Returns the group's E8M0 exponent e, the E8M0 rule on max P'
-// (amax 0 -> -127; clamped to [-127, 127]).
-//  * R = max (e_j + frexp exponent of p_j) over the group's nonzero p (both lane halves), so
-//    y_j = p_j 2^(e_j - R) < 1 and the largest is >= 1/2: exact, no overflow; a y_j that leaves
-//    the normal range is below 2^-125 of the group maximum, so its code is 0 either way.
-//  * e = R + rule(max y) (the rule commutes with powers of two), codes RNE(y_j / 2^(e - R)).
-__device__ __forceinline__ int fold_group(v16f& x, uint32_t (&eb)[4], v8i& pop, int half) {
-  // (the exponents are re-read from eb in each pass -- the empty asm keeps the compiler from
-  // holding the 16 values of the first pass -- and y overwrites x: no extra arrays live)
-  auto ej = [&](int i) __attribute__((always_inline)) { return (int)((eb[i >> 2] >> (8 * (i & 3))) & 0xFFu) - 127; };
-  int R = -(1 << 20);
-#pragma unroll
-  for (int i = 0; i < 16; i++)
-    if (x[i] > 0.f) R = max(R, ej(i) + __builtin_amdgcn_frexp_expf(x[i]));
-  R = max(R, __float_as_int(swap32(__int_as_float(R))));
-#if defined(__HIP_DEVICE_COMPILE__)
-#pragma unroll
-  for (int b = 0; b < 4; b++) asm volatile("" : "+v"(eb[b]));
-#endif
-  float ym = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    x[i] = __builtin_ldexpf(x[i], max(ej(i) - R, -160));   // p = 0 stays 0; R may be -2^20
-    ym = fmaxf(ym, x[i]);
-  }
-  ym = fmaxf(ym, swap32(ym));
-  int e = kExpMin;
-  float sc = 1.f;
-  if (ym > 0.f) {
-    e = min(max(R + scale_exp_from_bits(__float_as_uint(ym)), kExpMin), kExpMax);
-    sc = exp2_scale(e - R);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; j++)
-    pop[4 * half + j] = (int)pack4_e4m3_scaled(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3], sc);
-  return e;
-}
-
 // Online softmax of a diagonal tile under the strict fold: softmax_tile<true, ...> with the P
-// codes of P' = P 2^e_j (fold_group); vt: the tile's 64 token scale bytes in key order.
+// codes of P' = P 2^e_j (fold_codes16); vt: the tile's 64 token scale bytes in key order.
 template <bool kLit, int D>
 __device__ __forceinline__ float softmax_tile_fold(v16f (&cur)[2], float c_rt, int lim, const uint8_t* vt, float& M,
                                                    float& lsum, v8i& pop, int& psc) {
@@ -479,7 +439,7 @@ __device__ __forceinline__ float softmax_tile_fold(v16f (&cur)[2], float c_rt, i
     uint32_t eb[4];
 #pragma unroll
     for (int b4 = 0; b4 < 4; b4++) eb[b4] = *reinterpret_cast<const uint32_t*>(vt + T * 32 + 8 * b4 + 4 * hh);
-    eg[T] = fold_group(cur[T], eb, pop, T);
+    eg[T] = fold_codes16(cur[T], eb, pop, T);   // P' = P 2^e_j of the group's keys
   }
   psc = (hh ? eg[1] : eg[0]) + 127;
   return f;

@@ -272,6 +272,49 @@ __device__ __forceinline__ void wait_vmem_n() {
   asm volatile("" ::: "memory");
 }
 
+// MX codes of x_j 2^e_j for one 32-element group held by a lane and its partner lane ^ 32 (16
+// values each; x signed or not): the power of two 2^e_j of element j is folded into the value
+// before quantising (FLAMIA notes, section 4, the strict option's per-key scales: P_ij (s_j v_j)
+// = (P_ij s_j) v_j in the forward, dS_ij (s_j k_j) = (dS_ij s_j) k_j for dQ). eb: the elements'
+// scale bytes (e_j + 127), four per dword in element order. Writes the 16 codes into pop
+// registers 4 half .. 4 half + 3 and returns the group's E8M0 exponent e, the group rule on
+// max |x_j 2^e_j| (amax 0 -> -127; clamped to [-127, 127]).
+//  * R = max (e_j + frexp exponent of x_j) over the group's nonzero x, so y_j = x_j 2^(e_j - R)
+//    has |y_j| < 1 with the largest >= 1/2: exact, no overflow; a y_j that leaves the normal
+//    range is below 2^-125 of the group maximum, so its code is 0 either way.
+//  * e = R + rule(max |y|) (the rule commutes with powers of two), codes RNE(y_j / 2^(e - R)).
+// x is overwritten by y; the exponents are re-read from eb in each pass (the empty asm keeps the
+// compiler from holding the 16 values of the first pass).
+__device__ __forceinline__ int fold_codes16(v16f& x, uint32_t (&eb)[4], v8i& pop, int half) {
+  auto ej = [&](int i) __attribute__((always_inline)) { return (int)((eb[i >> 2] >> (8 * (i & 3))) & 0xFFu) - 127; };
+  int R = -(1 << 20);
+#pragma unroll
+  for (int i = 0; i < 16; i++)
+    if (x[i] != 0.f) R = max(R, ej(i) + __builtin_amdgcn_frexp_expf(x[i]));
+  R = max(R, __float_as_int(swap32(__int_as_float(R))));
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int b = 0; b < 4; b++) asm volatile("" : "+v"(eb[b]));
+#endif
+  float ym = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    x[i] = __builtin_ldexpf(x[i], max(ej(i) - R, -160));   // 0 stays 0; R may be -2^20
+    ym = fmaxf(ym, fabsf(x[i]));
+  }
+  ym = fmaxf(ym, swap32(ym));
+  int e = kExpMin;
+  float sc = 1.f;
+  if (ym > 0.f) {
+    e = min(max(R + scale_exp_from_bits(__float_as_uint(ym)), kExpMin), kExpMax);
+    sc = exp2_scale(e - R);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+    pop[4 * half + j] = (int)pack4_e4m3_scaled(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3], sc);
+  return e;
+}
+
 // Workgroup barrier that completes this wave's LDS operations first (so its LDS writes are
 // visible after the barrier) but does not wait for global loads, stores or LDS-DMA: the
 // caller orders its LDS-DMA with wait_vmem / wait_vmem_n, and global stores drain on their

@@ -67,6 +67,9 @@ struct BwdParams {
   const uint8_t* k_codes; const uint8_t* k_scales;      // ROW K
   const uint8_t* ks_codes; const uint8_t* ks_scales;    // SEQ K
   const uint8_t* vr_codes; const uint8_t* vr_scales;    // ROW V
+  // strict dQ (causal, FP32 dQ): the per-token view of K (SEQ code layout, one scale byte per
+  // token); nullptr: the plain backward
+  const uint8_t* kt_codes; const uint8_t* kt_scales;
   const void* o;
   const float* lse;
   const void* g;

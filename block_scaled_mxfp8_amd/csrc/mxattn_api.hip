@@ -171,7 +171,8 @@ mx_status fwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
 
 mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
                    mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* gptr, mx_dtype g_dtype,
-                   void* dq, void* dk, void* dv, void* stream, bool need_packed, const mx_qview* mx_out = nullptr) {
+                   void* dq, void* dk, void* dv, void* stream, bool need_packed, const mx_qview* mx_out = nullptr,
+                   const mx_qview* k_tok = nullptr) {
   mx::Geom g, gk;
   mx_status st = check_desc(desc, &g);
   if (st != MX_OK) return st;
@@ -183,6 +184,11 @@ mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
   if (!o || !lse || !gptr || !dq || !dk || !dv) return MX_E_ARG;
   if (!aligned(o, 16) || !aligned(gptr, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16)) return MX_E_ARG;
   if (g_dtype != MX_F32 && g_dtype != MX_BF16) return MX_E_ARG;
+  if (k_tok) {   // the strict dQ: causal self-attention, FP32 dQ, E4M3 scores
+    if ((st = check_view(*k_tok)) != MX_OK) return st;
+    if (!desc->causal || seq_k) return MX_E_ARG;
+    if (desc->dq_mode != MX_DQ_F32 || score_fp4(desc)) return MX_E_UNSUPPORTED;
+  }
   const BwdWorkspace w = bwd_layout(g, gk, desc);
   if (!desc->workspace || desc->workspace_bytes < w.total || !aligned(desc->workspace, kAlign)) return MX_E_WORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(desc->workspace);
@@ -218,7 +224,10 @@ mx_status bwd_impl(const mx_attn_desc* desc, const mx_seq* seq_k, mx_qview q_row
     p.vpre = reinterpret_cast<float*>(ws + w.vpre);
     p.kpre = reinterpret_cast<float*>(ws + w.kpre);
   }
-  if (w.store_ok && desc->workspace_bytes >= w.total_store) {
+  if (k_tok) {   // (dQ rebuilds its own per-query dS, so the code store is not used)
+    p.kt_codes = k_tok->codes;
+    p.kt_scales = k_tok->scales;
+  } else if (w.store_ok && desc->workspace_bytes >= w.total_store) {
     p.ds_codes = ws + w.ds_codes;
     p.ds_exps = ws + w.ds_exps;
     p.ds = w.ds;
@@ -416,6 +425,13 @@ mx_status mx_attn_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, 
                       mx_qview v_row, const void* o, const float* lse, const void* g, mx_dtype g_dtype, void* dq,
                       void* dk, void* dv, void* stream) {
   return bwd_impl(desc, nullptr, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, false);
+}
+
+mx_status mx_attn_bwd_strict(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
+                             mx_qview k_seq, mx_qview k_tok, mx_qview v_row, const void* o, const float* lse,
+                             const void* g, mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream) {
+  return bwd_impl(desc, nullptr, q_row, q_seq, k_row, k_seq, v_row, o, lse, g, g_dtype, dq, dk, dv, stream, false,
+                  nullptr, &k_tok);
 }
 
 mx_status mx_attn_varlen_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,

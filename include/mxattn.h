@@ -49,9 +49,9 @@
  *                 the ROW groups with E2M1 codes (sign | 2-bit exponent, bias 1 | 1-bit
  *                 mantissa: 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte, channel 2i in the low
  *                 nibble of byte i: codes [B,H,L,d/2] / [T,H,d/2]; scales as the ROW view.
- *       SEQ_TOKEN view (per-token scales, the V operand of the strict fold; FLAMIA notes,
- *                 section 4, the strict option's per-key scale on the diagonal tiles): codes in
- *                 the SEQ layout above, but each token has ONE exponent for all d channels (the
+ *       SEQ_TOKEN view (per-token scales: the V operand of the strict forward and the K operand
+ *                 of the strict dQ; FLAMIA notes, section 4, the strict option's per-key scales
+ *                 on the diagonal tiles): codes in the SEQ layout above, but each token has ONE exponent for all d channels (the
  *                 smallest e with max_c |x_tc| * 2^-e <= 448); scales: one byte per token slot,
  *                 [B, H, G, 32] / [H, Gc, 32] in token order (the group rows of the SEQ view;
  *                 padding tokens hold byte 0 and codes 0).
@@ -245,6 +245,23 @@ mx_status mx_attn_fwd_strict(const mx_attn_desc* desc, mx_qview q_row, mx_qview 
 mx_status mx_attn_bwd(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
                       mx_qview k_seq, mx_qview v_row, const void* o, const float* lse, const void* g,
                       mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
+
+/* Backward with the strict dQ (FLAMIA notes, section 4, the strict option: per-key K scales
+ * folded into dS -- the K fold -- and per-query dS scales), so that dQ of row i depends on no
+ * position after i. Causal self-attention only (desc->causal = 0: MX_E_ARG), dq_mode MX_DQ_F32 and
+ * E4M3 scores (otherwise MX_E_UNSUPPORTED); batched or packed. dK, dV are mx_attn_bwd's (from
+ * the 32 x 32 dS blocks; they accumulate later queries by definition). dQ's dS operand is U
+ * quantised per query in groups of 32 keys (one E8M0 exponent per (query, key group), the group
+ * rule on its largest |value|) instead of in 32 x 32 blocks; for the keys of the query's own
+ * group, 32 floor(i / 32) <= j <= i (relative to the sequence or document start), whose K SEQ
+ * group reaches past i, K enters through k_tok -- the SEQ_TOKEN view of K (mx_quantize with
+ * MX_VIEW_SEQ_TOKEN) -- and each key's exponent e_j is folded into dS before that quantisation:
+ * the dS codes of those keys are those of U_ij 2^e_j, multiplying the key's codes with K scale 1.
+ * dQ rebuilds S, P and U itself (the minimal workspace, mx_attn_workspace_size(desc, 1),
+ * suffices; the dS code store is not used). Other arguments, layouts and errors as mx_attn_bwd. */
+mx_status mx_attn_bwd_strict(const mx_attn_desc* desc, mx_qview q_row, mx_qview q_seq, mx_qview k_row,
+                             mx_qview k_seq, mx_qview k_tok, mx_qview v_row, const void* o, const float* lse,
+                             const void* g, mx_dtype g_dtype, void* dq, void* dk, void* dv, void* stream);
 
 /* Packed (jagged) entry points: identical to mx_attn_fwd / mx_attn_bwd and the same kernels,
  * but desc->seq.cu_seqlens is required (MX_E_ARG otherwise). */

@@ -389,3 +389,19 @@ def test_strict_fold_view_and_entry_validation(lib):
     assert f(ctypes.byref(_desc()), v, v, v, _lib._QView(0, FAKE), FAKE, FAKE, None) == _lib.MX_E_ARG
     assert f(ctypes.byref(_desc()), v, v, v, _lib._QView(FAKE, FAKE + 1), FAKE, FAKE, None) == _lib.MX_E_ARG
     assert f(None, v, v, v, v, FAKE, FAKE, None) == _lib.MX_E_ARG
+
+
+def test_strict_backward_validation(lib):
+    v = _lib._QView(FAKE, FAKE)
+    b = lib.mx_attn_bwd_strict
+    args = (v, v, v, v, v, v, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None)
+    # causal self-attention, FP32 dQ, E4M3 scores; the token view is checked like the others
+    assert b(ctypes.byref(_desc(causal=0)), *args) == _lib.MX_E_ARG
+    assert b(ctypes.byref(_desc(dq_mode=1)), *args) == _lib.MX_E_UNSUPPORTED
+    assert b(ctypes.byref(_desc(dq_mode=2)), *args) == _lib.MX_E_UNSUPPORTED
+    assert b(ctypes.byref(_desc(score_format=1)), *args) == _lib.MX_E_UNSUPPORTED
+    bad = (v, v, v, v, _lib._QView(0, FAKE)) + args[5:]
+    assert b(ctypes.byref(_desc()), *bad) == _lib.MX_E_ARG
+    assert b(None, *args) == _lib.MX_E_ARG
+    # then the workspace, as mx_attn_bwd (the minimal one suffices)
+    assert b(ctypes.byref(_desc()), *args) == _lib.MX_E_WORKSPACE
