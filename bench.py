@@ -24,6 +24,8 @@ the library records immediately around each launch of the named kernel, on its s
                                    # MXFP8 (any attention workload; default c3)
     python bench.py --fwd strict   # the forward with the strict per-key V fold on the diagonal tiles
                                    # (causal workloads; V also quantised to its per-token view)
+    python bench.py --bwd strict   # the backward with the strict dQ (per-query dS scales, K fold;
+                                   # FP32 dQ; K also quantised to its per-token view)
 
 `roofline.traffic` is the roofline kernel's HBM bytes per launch from rocprofv3 counters
 (FETCH_SIZE and WRITE_SIZE, each scaled by its reading for the 1 GiB copy of --pmc-run),
@@ -113,6 +115,8 @@ def parse():
                     help="score operands of the attention workloads: MXFP8 (E4M3), or MXFP4 (E2M1; the mixed route)")
     ap.add_argument("--fwd", choices=["plain", "strict"], default="plain",
                     help="forward of the step: plain, or with the strict per-key V fold (causal only)")
+    ap.add_argument("--bwd", choices=["plain", "strict"], default="plain",
+                    help="backward of the step: plain, or with the strict dQ (causal, FP32 dQ)")
     ap.add_argument("--workload", choices=["c3", "c4", "c5", "c5gqa", "x1", "n1", "g1"], default="c3",
                     help="c3: the headline causal self-attention step; c4: 128 packed documents; c5/c5gqa: "
                          "B1 H16 L16384 non-causal (MHA / 16 on 4 KV heads); x1: the jagged cross-attention "
@@ -177,7 +181,8 @@ def run_attention(args):
     from block_scaled_mxfp8_amd import (MX_DQ_F16_BOOST, MX_DQ_F16_PREFIX, MX_DQ_F32, MX_VIEW_ROW_FP4, MX_VIEW_SEQ,
                                         MX_VIEW_SEQ_TOKEN,
                                         PROFILE_BWD_DKDV, PROFILE_BWD_DQ, PROFILE_BWD_PREP, PROFILE_FWD,
-                                        PROFILE_QUANTIZE, load, mx_attn_bwd, mx_attn_fwd, mx_attn_fwd_strict,
+                                        PROFILE_QUANTIZE, load, mx_attn_bwd, mx_attn_bwd_strict, mx_attn_fwd,
+                                        mx_attn_fwd_strict,
                                         mx_profile_kernel, mx_quantize, mx_quantize_token_block)
     from block_scaled_mxfp8_amd.flops import attn_flops, visible_pairs
 
@@ -217,14 +222,20 @@ def run_attention(args):
 
     fp4 = args.score == "mxfp4"
     strict = args.fwd == "strict"
-    if strict and (fp4 or not causal):
-        sys.exit("--fwd strict needs a causal workload with MXFP8 scores")
+    bstrict = args.bwd == "strict"
+    if (strict or bstrict) and (fp4 or not causal):
+        sys.exit("--fwd/--bwd strict need a causal workload with MXFP8 scores")
+    if bstrict and args.dq != "f32":
+        sys.exit("--bwd strict accumulates dQ in FP32")
     qk_views = (MX_VIEW_ROW_FP4 | MX_VIEW_SEQ) if fp4 else 3
     v_tok = [None]
+    k_tok = [None]
 
     def quant():
         if strict:   # the per-token V view of the diagonal tiles: a second pass over V
             v_tok[0] = mx_quantize(t["v"], views=MX_VIEW_SEQ_TOKEN, **kw)[1]
+        if bstrict:  # the per-token K view of the strict dQ: a second pass over K
+            k_tok[0] = mx_quantize(t["k"], views=MX_VIEW_SEQ_TOKEN, **kw)[1]
         return (mx_quantize(t["q"], views=qk_views, **kw), mx_quantize(t["k"], views=qk_views, **kw),
                 mx_quantize(t["v"], **kw))
 
@@ -236,9 +247,14 @@ def run_attention(args):
     def step(mode=dq_mode):
         (q_row, q_seq), (k_row, k_seq), (v_row, v_seq) = quant()
         o, lse = fwd(q_row, k_row, v_seq)
-        dq, dk, dv, w = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=causal,
-                                    dq_mode=mode, workspace=ws.get(mode), ds_store=ds_store, **kw)
-        ws[mode] = w
+        key = "strict" if bstrict else mode    # (the strict call's workspace is the minimal one)
+        if bstrict:
+            dq, dk, dv, w = mx_attn_bwd_strict(q_row, q_seq, k_row, k_seq, k_tok[0], v_row, o, lse, t["g"],
+                                               workspace=ws.get(key), **kw)
+        else:
+            dq, dk, dv, w = mx_attn_bwd(q_row, q_seq, k_row, k_seq, v_row, o, lse, t["g"], causal=causal,
+                                        dq_mode=mode, workspace=ws.get(key), ds_store=ds_store, **kw)
+        ws[key] = w
         return o, dq
 
     if args.pmc_run:
@@ -308,6 +324,21 @@ def run_attention(args):
                                    workspace=ws.get(mode), ds_store=ds_store, **kw)
 
     res_bwd = {}
+    if bstrict:   # the strict backward's own call (its workspace is the minimal one)
+        def sbwd():
+            r = mx_attn_bwd_strict(q_row, q_seq, k_row, k_seq, k_tok[0], v_row, o, lse, t["g"],
+                                   workspace=ws.get("strict"), **kw)
+            ws["strict"] = r[3]
+        sbwd()
+        s_dq = kernel_ms(PROFILE_BWD_DQ, sbwd)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        for _ in range(args.profile_steps):
+            sbwd()
+        s1.record()
+        torch.cuda.synchronize()
+        res_bwd["strict"] = dict(dq_ms=s_dq, call_ms=s0.elapsed_time(s1) / args.profile_steps)
     modes = [("f32", MX_DQ_F32), ("f16", MX_DQ_F16_BOOST)]
     if args.dq == "f16prefix":
         modes.append(("f16prefix", MX_DQ_F16_PREFIX))
@@ -346,8 +377,10 @@ def run_attention(args):
     if fp4:
         metric = f"mixed MXFP4-score / MXFP8 attn fwd/bwd TFLOP/s (causal-adj) on {name}" + (
             " (B4 H32 L4096 d128)" if name == "c3" else "")
-    elif strict:
-        metric = f"MXFP8 attn fwd/bwd TFLOP/s (causal-adj) on {name}, forward with the strict per-key V fold"
+    elif strict or bstrict:
+        metric = (f"MXFP8 attn fwd/bwd TFLOP/s (causal-adj) on {name}, strict option ("
+                  + " and ".join(x for x, on in (("forward V fold", strict), ("dQ K fold + per-query dS scales", bstrict))
+                                 if on) + ")")
     elif name == "c3":
         metric = "MXFP8 attn fwd/bwd TFLOP/s (causal-adj) at B4 H32 L4096 d128, % of peak"
     else:
@@ -367,8 +400,9 @@ def run_attention(args):
         "data": "synthetic",
         "config": dict({"workload": desc + ", bf16 N(0,1)-based synthetic inputs, step = quantise Q/K/V + fwd + bwd"
                         + (" with Q and K scored as MXFP4" if fp4 else "")
-                        + (", the forward with the strict per-key V fold (V also quantised per token)" if strict else ""),
-                        "head_dim": d, "causal": causal, "dq": args.dq, "score": args.score, "fwd": args.fwd,
+                        + (", the forward with the strict per-key V fold (V also quantised per token)" if strict else "")
+                        + (", the backward with the strict dQ (K also quantised per token)" if bstrict else ""),
+                        "head_dim": d, "causal": causal, "dq": args.dq, "score": args.score, "fwd": args.fwd, "bwd": args.bwd,
                         "dq_pass": "rebuilds dS" if args.recompute_dq else "reads stored dS codes"}, **cfg_line),
         "timing": {"rounds": args.rounds, "steps_per_round": args.steps, "ms_per_step_rounds": [round(r, 4) for r in rounds],
                    "statistic": "median of rounds, wall clock, no measurement hook",
@@ -380,6 +414,9 @@ def run_attention(args):
         "bwd_pct_of_peak": round(100 * tflops(f_bwd, bwd_f32["call_ms"]) / pk_bwd, 2),
         "bwd_f16dq_tflops": round(tflops(f_bwd, bwd_f16["call_ms"]), 2),
         "bwd_f16dq_pct_of_peak": round(100 * tflops(f_bwd, bwd_f16["call_ms"]) / pk_bwd, 2),
+        **({"bwd_strict_tflops": round(tflops(f_bwd, res_bwd["strict"]["call_ms"]), 2),
+            "bwd_strict_call_ms": round(res_bwd["strict"]["call_ms"], 4),
+            "attn_bwd_dq_strict_ms": round(res_bwd["strict"]["dq_ms"], 4)} if "strict" in res_bwd else {}),
         **({"bwd_f16prefix_tflops": round(tflops(f_bwd, res_bwd["f16prefix"]["call_ms"]), 2),
             "bwd_f16prefix_call_ms": round(res_bwd["f16prefix"]["call_ms"], 4),
             "bwd_f16prefix_prep_ms": round(res_bwd["f16prefix"]["prep_ms"], 4),
@@ -398,10 +435,10 @@ def run_attention(args):
         "roofline": {"kernel": f"attn_bwd_dkdv_kernel<{d}> (backward dK/dV)", "bound": "mfma",
                      "achieved": round(tflops(f_dkdv, ms_bwd_main), 2), "peak": round(pk_dkdv, 1),
                      "unit": "TFLOP/s", "frac": round(tflops(f_dkdv, ms_bwd_main) / pk_dkdv, 4),
-                     "traffic": recorded_traffic() if name == "c3" and not fp4 and not strict else None},
+                     "traffic": recorded_traffic() if name == "c3" and not fp4 and not strict and not bstrict else None},
         "env": environment(),
     }
-    if not args.no_cpu_baseline and name == "c3" and not fp4 and not strict:
+    if not args.no_cpu_baseline and name == "c3" and not fp4 and not strict and not bstrict:
         line["cpu_baseline"] = cpu_baseline(t, args.cpu_heads)
     print(json.dumps(line), flush=True)
 
