@@ -203,36 +203,39 @@ __device__ __forceinline__ KvWork decode_kv(const BwdParams& p, int* smem) {
   return w;
 }
 
-// Issue the producers' loads of step c into stage `st`, as loader `lw` of NL (NL >= 6), all
+// Issue the ROW-tile and per-query loads of step c into stage `st`, as loader `lw` of NL, all
 // LDS-DMA: ROW-tile instructions j = lw, lw + NL, ... (each moves 64 x 16 bytes: 64/NCH rows of
-// NCH 16-byte chunks) and, for lw < 6, one per-query item (64 lanes x 4 bytes; the ROW scale
-// words are 2 bytes at d = 64, landing in the low half of the lane's dword): 0 the Q ROW scale
-// words, 1 the G ROW scale words, 2 LSE * log2 e, 3 -D, 4 the Q SEQ scales, 5 the G SEQ scales
-// (dword lane % (d/2) of the step's two groups, the second clamped to the last group). Rows past
-// the end are clamped to the last row (finite codes and values); the masked tile code gives them
-// P = 0 and U = 0. Every address is a base plus c's offsets plus a lane part.
+// NCH 16-byte chunks) and the per-query items i = lw, lw + NL, ... < 6 (64 lanes x 4 bytes; the
+// ROW scale words are 2 bytes at d = 64, landing in the low half of the lane's dword): 0 the Q
+// ROW scale words, 1 the G ROW scale words, 2 LSE * log2 e, 3 -D, 4 the Q SEQ scales, 5 the G
+// SEQ scales (dword lane % (d/2) of the step's two groups, the second clamped to the last
+// group). Rows past the end are clamped to the last row (finite codes and values); the masked
+// tile code gives them P = 0 and U = 0. Every address is a base plus c's offsets plus a lane part.
 template <int D, bool kPacked, int NL, bool kF4>
 __device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& w, const StepPos& c, DkvStage<D>& st,
                                               int lw) {
-  static_assert(NL >= 6, "six small-item loaders");
   constexpr int NCH = D / 16, RPI = 64 / NCH;
   constexpr int NCHQ = kF4 ? NCH / 2 : NCH, RPIQ = 64 / NCHQ;   // Q ROW tile (E2M1: d/2 bytes a row)
   const int lane = threadIdx.x & 63;
   const int ts = (int)token_stride_k<kPacked>(p.heads_q, D);
   const int rmax = w.n - 1 - c.q0;
   const int r = min(lane, rmax);
-  if (lw == 0 || lw == 1) {
-    lds_dma((lw == 0 ? p.q_scales : p.gr_scales) + (c.elem >> 5) + ((uint32_t)(r * ts) >> 5), lw == 0 ? st.qrs : st.grs,
-            D / 32);
-  } else if (lw == 2 || lw == 3) {
-    lds_dma((lw == 2 ? p.lse2 : p.ndelta) + c.tok + (uint32_t)(r * (kPacked ? p.heads_q : 1)), lw == 2 ? st.lse2 : st.ndlt,
-            4);
-  } else if (lw == 4 || lw == 5) {
-    const int word = lane % (D / 2);       // lanes >= d/2 repeat a dword of the lower half
-    const int gl = ((w.n + 31) >> 5) - 1 - (c.q0 >> 5);   // the last group, relative to q0's
-    const int gi = min((word * 4) / D, gl);
-    lds_dma((lw == 4 ? p.qs_scales : p.gs_scales) + c.srow * D + (uint32_t)(gi * D + (word * 4) % D),
-            lw == 4 ? st.qss : st.gss, 4);
+#pragma unroll
+  for (int i0 = 0; i0 < 6; i0 += NL) {
+    const int it = i0 + lw;               // (wave-uniform)
+    if (it == 0 || it == 1) {
+      lds_dma((it == 0 ? p.q_scales : p.gr_scales) + (c.elem >> 5) + ((uint32_t)(r * ts) >> 5),
+              it == 0 ? st.qrs : st.grs, D / 32);
+    } else if (it == 2 || it == 3) {
+      lds_dma((it == 2 ? p.lse2 : p.ndelta) + c.tok + (uint32_t)(r * (kPacked ? p.heads_q : 1)),
+              it == 2 ? st.lse2 : st.ndlt, 4);
+    } else if (it == 4 || it == 5) {
+      const int word = lane % (D / 2);     // lanes >= d/2 repeat a dword of the lower half
+      const int gl = ((w.n + 31) >> 5) - 1 - (c.q0 >> 5);   // the last group, relative to q0's
+      const int gi = min((word * 4) / D, gl);
+      lds_dma((it == 4 ? p.qs_scales : p.gs_scales) + c.srow * D + (uint32_t)(gi * D + (word * 4) % D),
+              it == 4 ? st.qss : st.gss, 4);
+    }
   }
   // ROW tiles (Q, G)
   const int lrow = lane / NCH;
@@ -375,19 +378,21 @@ __device__ __forceinline__ int dkv_codes_tile(const DkvStage<D>& S, int qt, cons
 
 // Producer / accumulator split, 12 waves. Waves 0-7 are producers: wave w computes the codes
 // of query tile w >> 2 for key group w & 3 (VALU-heavy, holding the group's K and V
-// operands), loads stages and (kStore) writes its 32 x 32 dS block to the code store; waves
-// 8-11 are accumulators: wave 8 + k holds key group k's dK and dV and applies the codes one
-// step later (codes pass through an LDS exchange buffer). The waves of a workgroup go
-// round-robin to the four SIMDs, so each SIMD runs two producers and one accumulator of the
+// operands) and (kStore) writes its 32 x 32 dS block to the code store; waves 8-11 are
+// accumulators: wave 8 + k holds key group k's dK and dV, applies the codes one step later
+// (codes pass through an LDS exchange buffer) and loads the stages. The waves of a workgroup
+// go round-robin to the four SIMDs, so each SIMD runs two producers and one accumulator of the
 // same key group: the producers' VALU work overlaps each other's latencies and the
 // accumulator's MFMAs, and each role fits three waves per SIMD.
 //
-// Iteration j (j = 0..nsteps): producers issue the S and E products of step j, then the
-// ROW-tile and small-item loads of step j + 1 into stage (j+1) % 3, then turn stage j % 3
-// into codes in exchange buffer j % 2; accumulators issue the SEQ-tile loads of step j + 1 and
-// apply the codes of step j - 1 (stage (j-1) % 3, buffer (j-1) % 2); one barrier ends the
-// iteration. The accumulators set the pace (eight products per step each, against four
-// per producer), so the dS stores sit with the producers.
+// Iteration j (j = 0..nsteps): producers issue the S and E products of step j, store the dS
+// block of step j - 1, then turn stage j % 3 into codes in exchange buffer j % 2; accumulators
+// issue every load of step j + 1 into stage (j+1) % 3 (ROW tiles, per-query items, SEQ tiles,
+// all LDS-DMA) and apply the codes of step j - 1 (stage (j-1) % 3, buffer (j-1) % 2), then wait
+// for their loads; one barrier ends the iteration. With no loads of their own the producers
+// never wait for vector memory, so their dS stores drain while later steps run (a producer
+// that also loaded had to wait each step for its loads, and with them for its previous step's
+// stores, which the in-order count ties together: 0.13 ms of the c3 dK/dV kernel).
 constexpr int kCodeDw = 1280;               // exchange dwords per key group
 
 template <int D>
@@ -581,10 +586,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   auto active = [&](int q0) { return kw < w.nk && !(p.causal && kw > q0 + kStepQ - 1); };
 
   if (wave < kDkvProducers) {
-    // ---------------- producer + loader ----------------
+    // ---------------- producer ----------------
     if (nsteps == 0) return;              // (uniform: no wave of the workgroup reaches a barrier)
     const int qt = wave >> 2;
-    const int lw = wave;                  // loader index
     const bool kvalid = key < w.nk;
     const float c = p.scale * kLog2e;
     v8i kop[NS], vop[NS];
@@ -616,31 +620,20 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     const StepWalk sw = step_walk<kPacked>(p.geom, p.heads_q, D, w.s, w.doc_start, w.n, w.hkv * group, qfirst,
                                            kStepQ);
     StepPos cur = sw.first;               // step whose codes are computed (j)
-    StepPos ld = sw.first;                // step being loaded (j + 1)
-    dkv_issue_row<D, kPacked, kDkvProducers, kF4>(p, w, ld, sm.st[0], lw);
-    wait_vmem();
-    wg_barrier();                         // stage 0 loaded
-    // kStore: the dS block of step j is written to the store during step j + 1, right after that
-    // step's loads are issued, while its S and E products run (the block stays in exchange
-    // buffer j % 2 until the end of step j + 1: the accumulators only read it then). pend_* hold
-    // the block's code-block index, exponent index and exponent, pend_buf its buffer.
+    wg_barrier();                         // stage 0 loaded (by the accumulators)
+    // kStore: the dS block of step j is written to the store during step j + 1, while its S and
+    // E products run (the block stays in exchange buffer j % 2 until the end of step j + 1: the
+    // accumulators only read it then). pend_* hold the block's code-block index, exponent index
+    // and exponent, pend_buf its buffer. The producers issue no loads, so they never wait for
+    // vector memory and their stores drain on their own while later steps run.
     bool pend = false;
     uint32_t pend_blk = 0, pend_ei = 0;
     int pend_dse = 0, pend_buf = 0;
-    int stc = 0, stn = 1;                 // stages j % 3 and (j + 1) % 3
+    int stc = 0;                          // stage j % 3
     for (int j = 0; j <= nsteps; j++) {
-      step_next(ld, sw, kStepQ);          // step j + 1
-      const bool load = j + 1 < nsteps;
-      bool stored = false;
-      // the next step's loads are issued while this step's S and E products run. They are
-      // issued on every iteration (no branch for the compiler to sink the products past): past
-      // the last step they reload the first step, whose addresses are valid, into stage
-      // (j + 1) % 3, which nobody reads then. Then the previous step's dS block is stored (two
-      // stores, younger than the loads).
+      // the previous step's dS block is stored while this step's S and E products run
       auto issue = [&]() __attribute__((always_inline)) {
-        dkv_issue_row<D, kPacked, kDkvProducers, kF4>(p, w, load ? ld : sw.first, sm.st[stn], lw);
         if (kStore && pend) {
-          asm volatile("" ::: "memory");   // the stores stay behind the loads (counted waits below)
           const uint8_t* cxp = reinterpret_cast<const uint8_t*>(sm.cx[pend_buf][kg]);
           const v4i x = ds_read_tr8_pair(cxp + (2 + qt) * 1024 + ds_tr_offset(fresh_lane()));
           uint32_t lo = (uint32_t)(lane * 16);
@@ -649,7 +642,6 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
               x, reinterpret_cast<__attribute__((address_space(1))) v4i*>(
                      scalar_ptr(p.ds_codes + ((uint64_t)pend_blk << 10)) + lo));
           if (lane == 0) p.ds_exps[pend_ei] = (uint8_t)(pend_dse + 127);
-          stored = true;
         }
       };
       const int q0 = cur.q0;
@@ -677,11 +669,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         pend = false;
       }
       step_next(cur, sw, kStepQ);
-      stc = stn;
-      stn = stn == 2 ? 0 : stn + 1;
-      // this step's loads have landed once at most the two younger stores are outstanding
-      if (stored) wait_vmem_n<2>();
-      else wait_vmem();
+      stc = stc == 2 ? 0 : stc + 1;
       wg_barrier();
     }
     return;
@@ -697,9 +685,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     dk[t] = v16f{};
     dv[t] = v16f{};
   }
-  const int lw = wave - kDkvProducers;    // SEQ-tile loader index
+  const int lw = wave - kDkvProducers;    // loader index (every load of the workgroup)
   int hq_l = w.hkv * group, q0_l = qfirst;   // step being loaded
+  const StepWalk sw = step_walk<kPacked>(p.geom, p.heads_q, D, w.s, w.doc_start, w.n, w.hkv * group, qfirst, kStepQ);
+  StepPos ld = sw.first;                  // the same step, for the ROW tiles and per-query items
   if (nsteps > 0) {
+    dkv_issue_row<D, kPacked, kWaves, kF4>(p, w, ld, sm.st[0], lw);
     dkv_issue_seq<D, kPacked, kWaves>(p, w, hq_l, q0_l, sm.st[0], lw);
     wait_vmem();
     wg_barrier();                         // stage 0 loaded
@@ -707,8 +698,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   int q0_a = qfirst;                      // step whose codes are applied (j - 1)
   for (int j = 0; nsteps > 0 && j <= nsteps; j++) {
     next_step(hq_l, q0_l, qfirst, w.n);  // step j + 1
+    step_next(ld, sw, kStepQ);
     const bool load = j + 1 < nsteps;
-    if (load) dkv_issue_seq<D, kPacked, kWaves>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], lw);
+    if (load) {
+      dkv_issue_row<D, kPacked, kWaves, kF4>(p, w, ld, sm.st[(j + 1) % 3], lw);
+      dkv_issue_seq<D, kPacked, kWaves>(p, w, hq_l, q0_l, sm.st[(j + 1) % 3], lw);
+    }
     if (j >= 1) {
       if (active(q0_a)) {
         // per-lane offsets, recomputed here (registers are short in this role)
