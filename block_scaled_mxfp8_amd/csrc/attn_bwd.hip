@@ -263,6 +263,11 @@ __device__ __forceinline__ void dkv_issue_row(const BwdParams& p, const KvWork& 
   }
 }
 
+// DMA instructions dkv_issue_seq issues per accumulator wave (kWaves loaders): two (Q, G) per
+// 64 x 16-byte instruction slot.
+template <int D>
+constexpr int kSeqDmas = 2 * (4 * D / 64) / kWaves;
+
 // Issue the accumulators' loads of the step into stage `st`: the SEQ tiles of Q and G (groups
 // q0/32 and q0/32 + 1, the latter clamped to the last group), instructions j = lw, lw + NL, ...
 // (each moves the 32 channels of one group). The lane offset is recomputed here (registers are
@@ -271,6 +276,7 @@ template <int D, bool kPacked, int NL>
 __device__ __forceinline__ void dkv_issue_seq(const BwdParams& p, const KvWork& w, int hq, int q0, DkvStage<D>& st,
                                               int lw) {
   constexpr int PER = D / 32, NSEQ = 4 * D / 64;
+  static_assert(NL != kWaves || NSEQ % NL == 0, "kSeqDmas counts whole slots");
   const Geom& g = p.geom;
   const int glast = ((w.n + 31) >> 5) - 1;
   const int soff = seq_tile_lane_off(fresh_lane());
@@ -733,7 +739,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
       q0_a += kStepQ;
       if (q0_a >= w.n) q0_a = qfirst;
     }
-    wait_vmem();
+    // step j + 1's ROW tiles and per-query items are read by the producers in iteration j + 1,
+    // its SEQ tiles only by this wave in iteration j + 2: the SEQ DMAs, issued last, may stay in
+    // flight across the barrier (the next iteration's wait covers them, as they are older than
+    // its loads). Past the last load everything is waited for (no DMA may be in flight when the
+    // wave ends, and the last SEQ tiles are still to be applied).
+    if (load) wait_vmem_n<kSeqDmas<D>>();
+    else wait_vmem();
     wg_barrier();
   }
 
