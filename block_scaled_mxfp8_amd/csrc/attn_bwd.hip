@@ -1242,9 +1242,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
         if (p.out_f32) {
           *reinterpret_cast<v4f*>(static_cast<float*>(p.dq) + obase + ch) = v4f{o[0], o[1], o[2], o[3]};
         } else {
-          const uint32_t w0 = float_to_bf16_bits(o[0]) | (float_to_bf16_bits(o[1]) << 16);
-          const uint32_t w1 = float_to_bf16_bits(o[2]) | (float_to_bf16_bits(o[3]) << 16);
-          *reinterpret_cast<v2i*>(static_cast<uint16_t*>(p.dq) + obase + ch) = v2i{(int)w0, (int)w1};
+          *reinterpret_cast<v2i*>(static_cast<uint16_t*>(p.dq) + obase + ch) =
+              v2i{(int)pack2_bf16(o[0], o[1]), (int)pack2_bf16(o[2], o[3])};
         }
       }
     }

@@ -741,9 +741,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p) {
       if (p.out_f32) {
         *reinterpret_cast<v4f*>(static_cast<float*>(p.o) + obase + ch) = v4f{o0, o1, o2, o3};
       } else {
-        const uint32_t w0 = float_to_bf16_bits(o0) | (float_to_bf16_bits(o1) << 16);
-        const uint32_t w1 = float_to_bf16_bits(o2) | (float_to_bf16_bits(o3) << 16);
-        *reinterpret_cast<v2i*>(static_cast<uint16_t*>(p.o) + obase + ch) = v2i{(int)w0, (int)w1};
+        *reinterpret_cast<v2i*>(static_cast<uint16_t*>(p.o) + obase + ch) = v2i{(int)pack2_bf16(o0, o1), (int)pack2_bf16(o2, o3)};
       }
     }
   }

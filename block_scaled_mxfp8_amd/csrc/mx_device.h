@@ -88,13 +88,6 @@ __device__ __forceinline__ void unpack4_e4m3(uint32_t w, float* out) {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Round-to-nearest-even float -> bf16 bits (NaN stays NaN).
-__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // 2^e for an E8M0 exponent e in [-127, 127] as an fp32 scale operand (2^-127 is the
 // subnormal 0x00400000; the kernels run with IEEE denormals).
 __device__ __forceinline__ float exp2_scale(int e) {
@@ -113,7 +106,8 @@ __device__ __forceinline__ uint32_t pack4_e4m3_scaled(float a, float b, float c,
   return __builtin_bit_cast(uint32_t, w);
 }
 
-// Two floats -> packed bf16 pair (low half = a), RNE (v_cvt_pk_bf16_f32).
+// Two floats -> packed bf16 pair (low half = a), RNE (v_cvt_pk_bf16_f32; NaN stays NaN with
+// the quiet bit set, as the integer RNE conversion (u + 0x7FFF + lsb) >> 16 with quieting).
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   typedef float f2 __attribute__((ext_vector_type(2)));
