@@ -127,7 +127,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU; multi-GPU runs are not part of it (use --gpus 1)",
+        print("bench.py: measures one GPU; multi-GPU runs are not supported (use --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     if args.workload == "x1":
@@ -751,7 +751,7 @@ def cpu_baseline_norm(x, gamma, eps, rows=32768):
             "sample": f"first {rows} of {x.shape[0]} rows (n {n}), float64 numpy, {sec:.1f} s"}
 
 
-def cpu_baseline(t, heads=8):
+def cpu_baseline(t, heads=24):
     """The C++ oracle (oracle/cpp, as it stands) on a bounded sample of the same workload:
     forward and backward of the first `heads` (batch, head) pairs of the c3 step (every pair
     is the same work), scaled to the metric's unit; heads=0 times every pair (the full tensor)."""
