@@ -64,7 +64,7 @@ def build_variant(name, verbose=False):
 
 
 def write_build_info(path):
-    """Identity of the built library (read by the benchmark): git revision of the tree, hipcc version,
+    """Identity of this build (read by the benchmark): git revision of the tree, hipcc version,
     hash of the sources compiled."""
     import hashlib
     import json
