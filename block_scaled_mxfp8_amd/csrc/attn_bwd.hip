@@ -1455,6 +1455,161 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(BwdParams p) {
   if (bad) __hip_atomic_fetch_or(p.flags, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The same pass with two 32-query blocks per wave (batched calls, FP32 sums): workgroup =
+// (sequence, query head, 256 queries), wave w owns the query blocks qb and qb + 1 of queries
+// [64w, 64w + 64). Each K SEQ tile in LDS and each K operand read from it then serve twice the
+// dS bytes (the tile's DMA per dS byte halves, and one A operand feeds two products); a block's
+// products, tiles and operands are those of the one-block kernel in the same order, so dQ is
+// bit-identical. Under causal both blocks of a wave end in the same 64-key tile (qb is even):
+// block qb's second key group there is beyond its diagonal and enters as zero codes. FP16 sums
+// would need a second set of partial sums that the registers do not hold; those modes, and
+// packed calls (whose work list has 128-query items), use the one-block kernel.
+constexpr int kBlockQ2 = 64 * kWaves;       // queries per two-block dQ workgroup
+constexpr int kPre2 = 3;                    // dS tiles in flight per wave (register ring)
+
+// dS blocks kb = 2kt, 2kt + 1 of both query blocks (r[0..1] block A, r[2..3] block B) and the
+// exponents of block 2kt + hh of each; absent blocks load block 0 of the store (never used).
+__device__ __forceinline__ void dqds2_load_ds(const BwdParams& p, const DqdsCtx& c, int kt, uint32_t blkb,
+                                              uint32_t exb, int kb_end_b, v4i (&r)[4], int (&e)[2]) {
+  const int g0 = 2 * kt;
+#pragma unroll
+  for (int b = 0; b < 4; b++) {
+    const int ke = b < 2 ? c.kb_end : kb_end_b;
+    const uint32_t blk = g0 + (b & 1) < ke ? (b < 2 ? c.blk0 : blkb) + g0 + (b & 1) : 0;
+    r[b] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) v4i*>(
+        scalar_ptr(p.ds_codes + ((uint64_t)blk << 10)) + (uint32_t)(c.lane * 16)));
+  }
+  e[0] = p.ds_exps[g0 + c.hh < c.kb_end ? c.ex0 + g0 + c.hh : 0];
+  e[1] = p.ds_exps[g0 + c.hh < kb_end_b ? exb + g0 + c.hh : 0];
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds2_kernel(BwdParams p) {
+  __shared__ DqdsStage<D> sm[3];
+  const Geom& g = p.geom;
+  QWork w;
+  {
+    const int nqb = (g.seqlen + kBlockQ2 - 1) / kBlockQ2;
+    int bh, rank;
+    lpt_order<4>(blockIdx.x, p.heads_q * g.batch, nqb, bh, rank);
+    w.qb = p.causal ? nqb - 1 - rank : rank;   // causal: the last query block sees the most keys
+    w.s = bh / p.heads_q;
+    w.h = bh % p.heads_q;
+    w.doc_start = 0;
+    w.n = g.seqlen;
+    w.doc_k = 0;
+    w.nk = p.geom_k.seqlen;
+    w.valid = true;
+  }
+  constexpr int NCT = D / 32;
+  constexpr int NK = 2 * (D / 32) / kWaves + 1;   // K-tile instructions per wave and tile
+  // Vector-memory instructions per wave and tile: NK (K tile, LDS-DMA) then 6 (four dS blocks, two
+  // exponent bytes). At the top of iteration kt, K tile kt and dS tile kt have landed once at
+  // most [dS kt-2+P] [K kt+1] [dS kt-1+P] = NK + 12 younger instructions remain.
+  constexpr int NW = NK + 12;
+  static_assert(kPre2 >= 3, "dS tile kt must be issued before K tile kt");
+  DqdsCtx c;
+  c.lane = threadIdx.x & 63;
+  c.wave = wave_id();
+  c.hh = c.lane >> 5;
+  const int l32 = c.lane & 31;
+  c.hkv = w.h / (p.heads_q / p.heads_kv);
+  const int q0 = w.qb * kBlockQ2;
+  const int qw = q0 + c.wave * 64;            // first query of this wave = 32 qb
+  const int qb = qw >> 5;
+  const int kend = p.causal ? min(w.n, q0 + kBlockQ2) : w.nk;
+  const int nkt = (kend + kStepK - 1) / kStepK;   // 0: no keys (dQ = 0; nothing is loaded)
+  c.glast = ((w.nk + 31) >> 5) - 1;            // last key group
+  c.kb_end = qw >= w.n ? 0 : (p.causal ? qb + 1 : c.glast + 1);             // block A = qb
+  const int kb_end_b = qw + 32 >= w.n ? 0 : (p.causal ? qb + 2 : c.glast + 1);   // block B = qb + 1
+  const int kb_end = max(c.kb_end, kb_end_b);
+  c.blk0 = 0;
+  c.ex0 = 0;
+  uint32_t blkb = 0, exb = 0;
+  if (c.kb_end > 0) ds_block<false>(p, w.s, w.h, 0, qb, 0, c.blk0, c.ex0);
+  if (kb_end_b > 0) ds_block<false>(p, w.s, w.h, 0, qb + 1, 0, blkb, exb);
+  c.soff = seq_tile_lane_off(c.lane);
+  c.soff_c = l32 * 32 + (half_swz(l32, c.hh) << 4);   // SEQ tile, channel l32 of group 0
+  c.scoff = c.hh * D + l32;                            // SEQ scale of channel l32, group hh
+
+  v16f dqa[NCT], dqb[NCT];
+#pragma unroll
+  for (int t = 0; t < NCT; t++) {
+    dqa[t] = v16f{};
+    dqb[t] = v16f{};
+  }
+  // ring slot of tile kt: kt mod kPre2; as in the one-block kernel, iterations kt = -2, -1 only
+  // issue, giving the steady-state order from the first real tile
+  v4i dsr[kPre2][4];
+  int exr[kPre2][2];
+  if (nkt > 0) {
+#pragma unroll
+    for (int u = 0; u < kPre2 - 2; u++) dqds2_load_ds(p, c, u, blkb, exb, kb_end_b, dsr[u], exr[u]);
+  }
+  for (int kt0 = -2; nkt > 0 && kt0 < nkt; kt0 += kPre2) {
+#pragma unroll
+    for (int u = 0; u < kPre2; u++) {
+      const int kt = kt0 + u;
+      const int slot = (u + kPre2 - 2) % kPre2;
+      wait_vmem_n<NW>();
+      wg_barrier();                        // K tile kt visible; every wave is done with tile kt - 1
+      const DqdsStage<D>* __restrict__ cur = &sm[(kt + 3) % 3];
+      dqds_issue_k<D, false>(p, w, c, kt + 2, &sm[(kt + 2) % 3]);
+      // (the vmcnt count relies on this order: the K tile's DMA before this tile's dS loads)
+      asm volatile("" ::: "memory");
+      const int g0 = 2 * kt;
+      if (kt >= 0 && g0 < kb_end) {
+        const bool a1 = g0 < c.kb_end;
+        const v8i opa = cat(dsr[slot][0], g0 + 1 < c.kb_end ? dsr[slot][1] : v4i{0, 0, 0, 0});
+        const v8i opb = cat(dsr[slot][2], g0 + 1 < kb_end_b ? dsr[slot][3] : v4i{0, 0, 0, 0});
+        const int sca = g0 + c.hh < c.kb_end ? exr[slot][0] : 127;
+        const int scb = g0 + c.hh < kb_end_b ? exr[slot][1] : 127;
+#pragma unroll
+        for (int t = 0; t < NCT; t++) {
+          const v8i ka = cat(*reinterpret_cast<const v4i*>(&cur->ks[t * 1024 + c.soff_c]),
+                             *reinterpret_cast<const v4i*>(&cur->ks[D * 32 + t * 1024 + c.soff_c]));
+          const int ksc = cur->kss[c.wave][c.scoff + t * 32];
+          if (a1) dqa[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, opa, dqa[t], 0, 0, 0, ksc, 0, sca);
+          dqb[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, opb, dqb[t], 0, 0, 0, ksc, 0, scb);
+        }
+      }
+      dqds2_load_ds(p, c, kt + kPre2, blkb, exb, kb_end_b, dsr[slot], exr[slot]);
+    }
+  }
+  wait_vmem();                             // no LDS-DMA may be in flight when the wave ends
+
+  // ---- epilogue: column l32 of block x = query qw + 32x + sigma(l32); 4 channels per store ----
+  uint32_t bad = 0;
+#pragma unroll
+  for (int x = 0; x < 2; x++) {
+    const int qi = qw + 32 * x + sigma_q(l32);
+    if (qi < w.n) {
+      const long long obase = elem_offset_k<false>(g, p.heads_q, D, (long long)w.s, w.h, qi, 0);
+#pragma unroll
+      for (int t = 0; t < NCT; t++) {
+#pragma unroll
+        for (int b4 = 0; b4 < 4; b4++) {
+          const int ch = t * 32 + 8 * b4 + 4 * c.hh;
+          float o[4];
+#pragma unroll
+          for (int u = 0; u < 4; u++) {
+            const float a = x ? dqb[t][4 * b4 + u] : dqa[t][4 * b4 + u];
+            if (!__builtin_isfinite(a)) bad |= 2u;
+            o[u] = a * p.scale;
+          }
+          if (p.out_f32) {
+            *reinterpret_cast<v4f*>(static_cast<float*>(p.dq) + obase + ch) = v4f{o[0], o[1], o[2], o[3]};
+          } else {
+            *reinterpret_cast<v2i*>(static_cast<uint16_t*>(p.dq) + obase + ch) =
+                v2i{(int)pack2_bf16(o[0], o[1]), (int)pack2_bf16(o[2], o[3])};
+          }
+        }
+      }
+    }
+  }
+  if (bad) __hip_atomic_fetch_or(p.flags, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ void clear_flags_kernel(uint32_t* flags) { *flags = 0u; }
 
 template <int D>
@@ -1510,9 +1665,11 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
   } else if (packed(g)) {
     if (f16) hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D, true, true>), gq, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D, false, true>), gq, dim3(256), 0, stream, p);
-  } else {
-    if (f16) hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D, true, false>), gq, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D, false, false>), gq, dim3(256), 0, stream, p);
+  } else if (f16) {
+    hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D, true, false>), gq, dim3(256), 0, stream, p);
+  } else {   // batched, FP32 sums: two query blocks per wave
+    const dim3 gq2((unsigned)((long long)((g.seqlen + kBlockQ2 - 1) / kBlockQ2) * p.heads_q * g.batch), 1, 1);
+    hipLaunchKernelGGL((attn_bwd_dq_ds2_kernel<D>), gq2, dim3(256), 0, stream, p);
   }
   profile_end(slot, stream);
   return hipGetLastError();
