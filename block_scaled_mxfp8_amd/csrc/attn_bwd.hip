@@ -1261,10 +1261,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 // straight into registers, kPre tiles ahead; the K SEQ tile (shared by the four waves) goes
 // through LDS by DMA, two tiles ahead. The pass reads 1 byte per visible (query, key) pair
 // from HBM and moves no other per-pair data: it is bound by HBM bandwidth.
-template <int D>
+template <int D, int NW = kWaves>
 struct DqdsStage {
   alignas(16) uint8_t ks[2 * D * 32];       // K SEQ codes [group][channel][32], half_swz halves
-  alignas(16) uint8_t kss[kWaves][256];     // K SEQ scales [group][channel], one copy per wave
+  alignas(16) uint8_t kss[NW][256];         // K SEQ scales [group][channel], one copy per wave
 };
 
 constexpr int kPre = 4;                     // dS tiles in flight per wave (register ring)
@@ -1277,16 +1277,17 @@ struct DqdsCtx {
   int soff, soff_c, scoff;    // K SEQ DMA lane offset, operand offset, scale offset
 };
 
-// K SEQ tile kt into stage st; tiles past the end reload the last groups (never read).
-template <int D, bool kPacked>
+// K SEQ tile kt into stage st, by NW waves; tiles past the end reload the last groups (never read).
+template <int D, bool kPacked, int NW = kWaves>
 __device__ __forceinline__ void dqds_issue_k(const BwdParams& p, const QWork& w, const DqdsCtx& c, int kt,
-                                             DqdsStage<D>* __restrict__ st) {
+                                             DqdsStage<D, NW>* __restrict__ st) {
   constexpr int PER = D / 32, NSEQ = 2 * PER;
+  static_assert(NSEQ % NW == 0, "the tile's 1 KB slots split evenly over the waves");
   const Geom& g = p.geom_k;
   const int g0 = 2 * kt;
 #pragma unroll
-  for (int jj = 0; jj < NSEQ / kWaves; jj++) {
-    const int j = c.wave + kWaves * jj;
+  for (int jj = 0; jj < NSEQ / NW; jj++) {
+    const int j = c.wave + NW * jj;
     const int grp = min(g0 + j / PER, c.glast);
     const long long row = seq_group_row_k<kPacked>(g, p.heads_kv, w.s, c.hkv, w.doc_k, grp);
     lds_dma(p.ks_codes + row * (D * 32) + (j % PER) * 1024 + c.soff, st->ks + j * 1024, 16);
@@ -1456,16 +1457,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(BwdParams p) {
 }
 
 // The same pass with two 32-query blocks per wave (batched calls, FP32 sums): workgroup =
-// (sequence, query head, 256 queries), wave w owns the query blocks qb and qb + 1 of queries
-// [64w, 64w + 64). Each K SEQ tile in LDS and each K operand read from it then serve twice the
-// dS bytes (the tile's DMA per dS byte halves, and one A operand feeds two products); a block's
-// products, tiles and operands are those of the one-block kernel in the same order, so dQ is
-// bit-identical. Under causal both blocks of a wave end in the same 64-key tile (qb is even):
+// (sequence, query head, 64 NW queries), wave w of NW owns the query blocks qb and qb + 1 of
+// queries [64w, 64w + 64). Each K SEQ tile in LDS then serves 2 NW query blocks instead of four
+// (its DMA per dS byte falls by that factor) and each K operand read from it two products; a
+// block's products, tiles and operands are those of the one-block kernel in the same order, so
+// dQ is bit-identical. Under causal both blocks of a wave end in the same 64-key tile (qb is even):
 // block qb's second key group there is beyond its diagonal and enters as zero codes. FP16 sums
 // would need a second set of partial sums that the registers do not hold; those modes, and
 // packed calls (whose work list has 128-query items), use the one-block kernel.
-constexpr int kBlockQ2 = 64 * kWaves;       // queries per two-block dQ workgroup
 constexpr int kPre2 = 3;                    // dS tiles in flight per wave (register ring)
+// waves of a two-block dQ workgroup: eight where the K tile's 1 KB slots split over eight
+template <int D>
+constexpr int kDq2Waves = (2 * D / 32) % 8 == 0 ? 8 : kWaves;
 
 // dS blocks kb = 2kt, 2kt + 1 of both query blocks (r[0..1] block A, r[2..3] block B) and the
 // exponents of block 2kt + hh of each; absent blocks load block 0 of the store (never used).
@@ -1483,9 +1486,10 @@ __device__ __forceinline__ void dqds2_load_ds(const BwdParams& p, const DqdsCtx&
   e[1] = p.ds_exps[g0 + c.hh < kb_end_b ? exb + g0 + c.hh : 0];
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds2_kernel(BwdParams p) {
-  __shared__ DqdsStage<D> sm[3];
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bwd_dq_ds2_kernel(BwdParams p) {
+  constexpr int kBlockQ2 = 64 * NW;         // queries per workgroup
+  __shared__ DqdsStage<D, NW> sm[3];
   const Geom& g = p.geom;
   QWork w;
   {
@@ -1502,11 +1506,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds2_kernel(BwdParams p) {
     w.valid = true;
   }
   constexpr int NCT = D / 32;
-  constexpr int NK = 2 * (D / 32) / kWaves + 1;   // K-tile instructions per wave and tile
+  constexpr int NK = 2 * (D / 32) / NW + 1;   // K-tile instructions per wave and tile
   // Vector-memory instructions per wave and tile: NK (K tile, LDS-DMA) then 6 (four dS blocks, two
   // exponent bytes). At the top of iteration kt, K tile kt and dS tile kt have landed once at
   // most [dS kt-2+P] [K kt+1] [dS kt-1+P] = NK + 12 younger instructions remain.
-  constexpr int NW = NK + 12;
+  constexpr int NWT = NK + 12;
   static_assert(kPre2 >= 3, "dS tile kt must be issued before K tile kt");
   DqdsCtx c;
   c.lane = threadIdx.x & 63;
@@ -1551,10 +1555,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds2_kernel(BwdParams p) {
     for (int u = 0; u < kPre2; u++) {
       const int kt = kt0 + u;
       const int slot = (u + kPre2 - 2) % kPre2;
-      wait_vmem_n<NW>();
+      wait_vmem_n<NWT>();
       wg_barrier();                        // K tile kt visible; every wave is done with tile kt - 1
-      const DqdsStage<D>* __restrict__ cur = &sm[(kt + 3) % 3];
-      dqds_issue_k<D, false>(p, w, c, kt + 2, &sm[(kt + 2) % 3]);
+      const DqdsStage<D, NW>* __restrict__ cur = &sm[(kt + 3) % 3];
+      dqds_issue_k<D, false, NW>(p, w, c, kt + 2, &sm[(kt + 2) % 3]);
       // (the vmcnt count relies on this order: the K tile's DMA before this tile's dS loads)
       asm volatile("" ::: "memory");
       const int g0 = 2 * kt;
@@ -1668,8 +1672,9 @@ hipError_t launch_main(const BwdParams& p, hipStream_t stream) {
   } else if (f16) {
     hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<D, true, false>), gq, dim3(256), 0, stream, p);
   } else {   // batched, FP32 sums: two query blocks per wave
-    const dim3 gq2((unsigned)((long long)((g.seqlen + kBlockQ2 - 1) / kBlockQ2) * p.heads_q * g.batch), 1, 1);
-    hipLaunchKernelGGL((attn_bwd_dq_ds2_kernel<D>), gq2, dim3(256), 0, stream, p);
+    constexpr int NW = kDq2Waves<D>;
+    const dim3 gq2((unsigned)((long long)((g.seqlen + 64 * NW - 1) / (64 * NW)) * p.heads_q * g.batch), 1, 1);
+    hipLaunchKernelGGL((attn_bwd_dq_ds2_kernel<D, NW>), gq2, dim3(64 * NW), 0, stream, p);
   }
   profile_end(slot, stream);
   return hipGetLastError();
